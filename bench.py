@@ -1,0 +1,275 @@
+"""Benchmark of the fused low-bit dequantize-matmul path on one MI355X.
+
+One step = one decode pass (M = 1) over the four phi4-14B-shaped 2-bit
+MatMulNBits layers (qkv 5120x7680, gate_up 5120x35840, down 17920x5120,
+lm_head 5120x100352; block 64, fp16 scales, uniform zero point 1.5, fp32 A and
+C).  Weights are resident in HBM and rotated through enough copies (>= 1 GiB,
+four times the 256 MB last-level cache) that every step reads them cold.
+`value` is the weight bytes streamed per step divided by the step time.
+
+Extra legs in the same JSON line: the fused MoE decode (GPT-OSS-20B shape and
+the 128-expert top-8 shape, fresh routing per call) and the prefill matmul when
+built.  Each kernel launch is bracketed by HIP events on the stream it runs on.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2516.6
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--legs", default="decode,qmoe", help="comma list of decode,qmoe,prefill")
+    return ap.parse_args()
+
+
+def to_dev(x):
+    import torch
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.uint16:
+        return torch.from_numpy(x.view(np.int16)).cuda()
+    return torch.from_numpy(x).cuda()
+
+
+def weight_bytes_nbits(K, N, bits=2, block=64):
+    nblk = (K + block - 1) // block
+    return N * nblk * block * bits // 8 + N * nblk * 2   # packed codes + fp16 scales
+
+
+# ---------------------------------------------------------------------------
+# decode leg: phi4 2-bit M = 1
+# ---------------------------------------------------------------------------
+
+def decode_leg(args):
+    import torch
+    from gemm_qmm_nbits_amd import inputs as gen
+    from gemm_qmm_nbits_amd import qmm as Q
+
+    shapes = list(gen.PHI4_SHAPES.items())
+    step_bytes = sum(weight_bytes_nbits(K, N) for _, (K, N) in shapes)
+    copies = max(2, int(np.ceil(1.0 * (1 << 30) / step_bytes)) + 1)
+    log(f"[decode] {len(shapes)} shapes, {step_bytes / 1e6:.1f} MB weights/step, {copies} copies")
+    sets = []
+    for ci in range(copies):
+        layer = []
+        for si, (name, (K, N)) in enumerate(shapes):
+            p = gen.nbits_problem(1, K, N, 2, 64, seed=gen.config_seed(1, si) + 100 * ci,
+                                  zp="none", scale_range=(0.01, 0.05))
+            layer.append({"name": name, "K": K, "N": N, "A": to_dev(p["A"]), "W": to_dev(p["W"]),
+                          "scales": to_dev(p["scales"]),
+                          "C": torch.empty((1, N), dtype=torch.float32, device="cuda")})
+        sets.append(layer)
+    stream = torch.cuda.current_stream()
+
+    def run_step(i, events=None):
+        layer = sets[i % copies]
+        for j, L in enumerate(layer):
+            Q.qmm_nbits(L["A"], L["W"], L["scales"], L["K"], 2, 64, None, Q.QMM_ZP_UNIFORM, 1.5,
+                        out=L["C"], stream=stream)
+            if events is not None:
+                events[j + 1].record(stream)
+
+    for i in range(args.warmup):
+        run_step(i)
+    torch.cuda.synchronize()
+    nshape = len(shapes)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nshape + 1)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        run_step(i, ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_shape_ms = np.zeros(nshape)
+    for i in range(args.steps):
+        for j in range(nshape):
+            per_shape_ms[j] += ev[i][j].elapsed_time(ev[i][j + 1])
+    per_shape_ms /= args.steps
+    step_ms = float(per_shape_ms.sum())
+    shapes_out = {}
+    for j, (name, (K, N)) in enumerate(shapes):
+        b = weight_bytes_nbits(K, N)
+        shapes_out[name] = {"K": K, "N": N, "weight_MB": round(b / 1e6, 3),
+                            "us": round(per_shape_ms[j] * 1e3, 2),
+                            "GBps": round(b / (per_shape_ms[j] * 1e-3) / 1e9, 1),
+                            "frac_hbm": round(b / (per_shape_ms[j] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    return {"step_bytes": step_bytes, "step_ms": step_ms, "wall_s": wall, "shapes": shapes_out,
+            "copies": copies}
+
+
+# ---------------------------------------------------------------------------
+# MoE decode leg
+# ---------------------------------------------------------------------------
+
+def qmoe_bytes(H, I, block, zp, bias, n_experts):
+    def per(nout, kin):
+        nblk = (kin + block - 1) // block
+        b = nout * nblk * block // 2 + nout * nblk * 2
+        if zp:
+            b += nout * ((nblk + 1) // 2)
+        if bias:
+            b += nout * 2
+        return b
+    return n_experts * (per(2 * I, H) + per(H, I))
+
+
+def qmoe_leg(args, name, T, H, I, E, k, block, zp, bias, mode, calls=40):
+    import torch
+    from gemm_qmm_nbits_amd import inputs as gen
+    from gemm_qmm_nbits_amd import qmm as Q
+
+    # whole-layer copies so that the rotation exceeds the last-level cache
+    layer_bytes = qmoe_bytes(H, I, block, zp, bias, E)
+    copies = max(2, int(np.ceil((1 << 30) / layer_bytes)))
+    p = gen.qmoe_problem(T, H, I, E, k, block, seed=gen.config_seed(3 if E == 32 else 4, T),
+                         zp=zp, bias=bias)
+    fcs = []
+    for c in range(copies):
+        d = {}
+        for fc in ("fc1", "fc2"):
+            src = p[fc]
+            d[fc] = {"W": to_dev(src["W"]), "scales": to_dev(src["scales"]),
+                     "zp": to_dev(src["zp"]) if src["zp"] is not None else None,
+                     "bias": to_dev(src["bias"]) if src["bias"] is not None else None}
+        fcs.append(d)
+    X = to_dev(p["X"]).view(torch.float16)
+    rng = np.random.default_rng(7)
+    routes = []
+    n_unique = []
+    for i in range(calls + args.warmup):
+        ids, w = gen.routing(rng, T, E, k)
+        routes.append((to_dev(ids), to_dev(w)))
+        n_unique.append(len(np.unique(ids)))
+    Y = torch.empty((T, H), dtype=torch.float16, device="cuda")
+    scratch = torch.empty(Q.qmoe_decode_scratch_bytes(T, H, I, k, mode), dtype=torch.uint8,
+                          device="cuda")
+    stream = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        d = fcs[i % copies]
+        Q.qmoe_decode_fused(X, routes[i][0], routes[i][1], d["fc1"], d["fc2"], H, I, E, block,
+                            mode=mode, out=Y, scratch=scratch, stream=stream)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(calls)]
+    for i in range(calls):
+        d = fcs[i % copies]
+        ids, w = routes[args.warmup + i]
+        ev[i][0].record(stream)
+        Q.qmoe_decode_fused(X, ids, w, d["fc1"], d["fc2"], H, I, E, block, mode=mode, out=Y,
+                            scratch=scratch, stream=stream)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    us = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+    uniq = np.array(n_unique[args.warmup:])
+    per_expert = qmoe_bytes(H, I, block, zp, bias, 1)
+    gbps = float(np.mean(uniq * per_expert / (us * 1e-6)) / 1e9)
+    del fcs
+    torch.cuda.empty_cache()
+    return {"name": name, "T": T, "H": H, "I": I, "E": E, "k": k, "block": block, "zp": zp,
+            "bias": bias, "mode": "int8" if mode == Q.QMOE_INT8_ACT else "fp",
+            "us_mean": round(float(us.mean()), 2), "us_median": round(float(np.median(us)), 2),
+            "tok_per_s": round(T / (float(us.mean()) * 1e-6), 1),
+            "weight_GBps": round(gbps, 1), "frac_hbm": round(gbps / HBM_PEAK_GBS, 4),
+            "unique_experts_mean": float(uniq.mean())}
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle on a bounded sample of the decode workload
+# ---------------------------------------------------------------------------
+
+def cpu_baseline():
+    """The oracle, as it stands, on one full decode step (the four phi4 layers at M = 1)."""
+    from threadpoolctl import threadpool_limits
+
+    from gemm_qmm_nbits_amd import inputs as gen
+    from oracle import qmm_oracle as O
+
+    total_b = 0
+    total_s = 0.0
+    with threadpool_limits(limits=1):
+        for si, (name, (K, N)) in enumerate(gen.PHI4_SHAPES.items()):
+            p = gen.nbits_problem(1, K, N, 2, 64, seed=gen.config_seed(1, si), zp="none",
+                                  scale_range=(0.01, 0.05))
+            t0 = time.perf_counter()
+            O.qmm_nbits(p["A"], "f32", p["W"], 2, K, 64, p["scales"], None, O.ZP_UNIFORM,
+                        uniform_zp=1.5)
+            total_s += time.perf_counter() - t0
+            total_b += weight_bytes_nbits(K, N)
+            del p
+    return {"value": round(total_b / total_s / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"one full decode step (qkv, gate_up, down, lm_head at M=1): "
+                      f"{total_b / 1e6:.1f} MB of weights in {total_s:.1f} s, numpy fp64, 1 thread"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
+                                   "(the per-GPU shard of a multi-GPU run is the same kernel at N/G)"}))
+        sys.exit(2)
+    import torch
+    from gemm_qmm_nbits_amd import qmm as Q
+
+    torch.cuda.set_device(0)
+    Q.lib()
+    legs = set(args.legs.split(","))
+    dec = decode_leg(args)
+    value = dec["step_bytes"] / (dec["step_ms"] * 1e-3) / 1e9
+    out = {
+        "metric": "weight GB/s & % HBM peak at M=1..64; prefill TFLOP/s; QMoE decode tok/s",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dec["step_ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u2 weights x fp32 activations, fp32 accumulate",
+        "data": "synthetic (seeded random codes, scales and activations of the phi4-14B 2-bit shapes)",
+        "config": {"workload": "phi4-14B-shaped 2-bit MatMulNBits decode, M=1, block 64, uniform zp 1.5, "
+                               "fp32 A/C: qkv 5120x7680, gate_up 5120x35840, down 17920x5120, "
+                               "lm_head 5120x100352",
+                   "M": 1, "bits": 2, "block": 64, "weight_copies_rotated": dec["copies"]},
+        "roofline": {"bound": "hbm", "kernel": "gemv_kernel<affine,u2,f32,M=1> (4 phi4 shapes)",
+                     "achieved": round(value, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(value / HBM_PEAK_GBS, 4), "traffic": None},
+        "decode_shapes": dec["shapes"],
+    }
+    if "qmoe" in legs:
+        q = []
+        q.append(qmoe_leg(args, "gpt-oss-20b", 1, 2880, 2880, 32, 4, 64, False, False, Q.QMOE_FP))
+        q.append(qmoe_leg(args, "gpt-oss-20b", 1, 2880, 2880, 32, 4, 64, False, False, Q.QMOE_INT8_ACT))
+        for T in (1, 4, 8):
+            q.append(qmoe_leg(args, "128x768 top-8", T, 2048, 768, 128, 8, 64, True, False, Q.QMOE_FP))
+        out["qmoe"] = q
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,820 @@
+// Host runtime of the qmm library: argument checks, path dispatch, the up-front
+// tiling tuner and the extern "C" entry points declared in include/qmm.h.
+//
+// Error state ([P2] hip-ep PR 1328, "What": clear the HIP error state before the
+// launches): every compute entry point calls hipGetLastError() once on entry and
+// returns hipGetLastError() after its launches.
+//
+// Tuning ([P1] hip-ep PR 1318, "What", commit 1: GEMV autotune timed on rotated
+// cold weights, median of cold bursts; [P2] "What": the first call of a shape
+// times every candidate up front -- one discarded round then timed rounds, least
+// total time wins -- writing only scratch, never while the stream is captured,
+// under a mutex).  Every candidate computes the same bits, so the choice only
+// affects speed.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <tuple>
+#include <vector>
+
+#include "qmm.h"
+#include "qmm_internal.h"
+
+using namespace qmm;
+
+namespace {
+
+constexpr int kMaxGemvM = 8;  // M above this takes the prefill (matrix-core) path
+
+bool is_pow2_block(int b) { return b >= 16 && b <= 256 && (b & (b - 1)) == 0; }
+bool valid_dtype(int t) { return t == QMM_F32 || t == QMM_F16 || t == QMM_BF16; }
+size_t dtype_size(int t) { return t == QMM_F32 ? 4 : 2; }
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  if (cus[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) {
+      (void)hipGetLastError();
+      v = 256;
+    }
+    cus[dev] = v;
+  }
+  return cus[dev];
+}
+
+bool env_flag(const char* name) {
+  const char* v = std::getenv(name);
+  return v && v[0] && std::strcmp(v, "0") != 0;
+}
+
+// ---------------------------------------------------------------------------
+// Tuner state
+// ---------------------------------------------------------------------------
+enum { ENTRY_NBITS = 0, ENTRY_CODEBOOK = 1, ENTRY_QMOE_FC1 = 2, ENTRY_QMOE_FC2 = 3, ENTRY_COUNT = 4 };
+
+// GEMV candidates: rows of W per lane.
+constexpr int kGemvCandidates[] = {1, 2, 4};
+constexpr int kNumGemvCandidates = 3;
+
+struct TunerState {
+  std::mutex mu;
+  int mode = -1;  // -1: not yet read from the environment
+  int forced = 0;
+  std::map<std::tuple<int, int64_t, int64_t, int64_t, int, int, int, int>, int> choice;
+  int last_choice[ENTRY_COUNT] = {-1, -1, -1, -1};
+  // cold-rotation pool (library-owned device memory, allocated on first tuning)
+  uint8_t* pool = nullptr;
+  size_t pool_bytes = 0;
+  size_t pool_cursor = 0;
+  void* out_scratch = nullptr;
+  size_t out_scratch_bytes = 0;
+};
+
+TunerState& tuner() {
+  static TunerState* t = new TunerState();  // lives until process end
+  return *t;
+}
+
+int tuning_mode_locked(TunerState& t) {
+  if (t.mode < 0) {
+    t.mode = env_flag("QMM_NO_TUNE") ? 1 : 0;
+    if (const char* f = std::getenv("QMM_FORCE_TILE")) {
+      t.mode = 2;
+      t.forced = std::atoi(f);
+    }
+  }
+  return t.mode;
+}
+
+bool stream_capturing(hipStream_t st) {
+  hipStreamCaptureStatus s = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(st, &s) != hipSuccess) {
+    (void)hipGetLastError();
+    return true;  // be conservative: do not time
+  }
+  return s != hipStreamCaptureStatusNone;
+}
+
+// Winner of an up-front timing: round 0 is discarded, the least total of the
+// remaining rounds wins, ties go to the lower index.
+int pick_winner(const double* t, int rounds, int ncand) {
+  int best = 0;
+  double best_total = 0;
+  for (int c = 0; c < ncand; ++c) {
+    double tot = 0;
+    for (int r = 1; r < rounds; ++r) tot += t[r * ncand + c];
+    if (c == 0 || tot < best_total) {
+      best = c;
+      best_total = tot;
+    }
+  }
+  return best;
+}
+
+// Ensure the rotation pool holds at least 4x the last-level cache (256 MB) and at
+// least 4 copies of `unit` bytes.  Returns false when memory is not available.
+bool ensure_pool(TunerState& t, size_t unit, size_t out_bytes) {
+  const size_t want = std::max<size_t>(size_t(1) << 30, unit * 4);
+  if (t.pool_bytes < want) {
+    if (t.pool) (void)hipFree(t.pool);
+    t.pool = nullptr;
+    t.pool_bytes = 0;
+    if (hipMalloc((void**)&t.pool, want) != hipSuccess) {
+      (void)hipGetLastError();
+      return false;
+    }
+    // deterministic content: every byte 0x5a (codes in range, scales finite)
+    if (hipMemset(t.pool, 0x5a, want) != hipSuccess) {
+      (void)hipGetLastError();
+      return false;
+    }
+    t.pool_bytes = want;
+    t.pool_cursor = 0;
+  }
+  if (t.out_scratch_bytes < out_bytes) {
+    if (t.out_scratch) (void)hipFree(t.out_scratch);
+    t.out_scratch = nullptr;
+    t.out_scratch_bytes = 0;
+    if (hipMalloc(&t.out_scratch, out_bytes) != hipSuccess) {
+      (void)hipGetLastError();
+      return false;
+    }
+    t.out_scratch_bytes = out_bytes;
+  }
+  return true;
+}
+
+// Next cold region of `unit` bytes in the pool (256-byte aligned).
+uint8_t* next_region(TunerState& t, size_t unit) {
+  const size_t u = (unit + 255) & ~size_t(255);
+  if (t.pool_cursor + u > t.pool_bytes) t.pool_cursor = 0;
+  uint8_t* p = t.pool + t.pool_cursor;
+  t.pool_cursor += u;
+  return p;
+}
+
+// Choose rows-per-lane for a GEMV shape, timing candidates on the first call.
+int gemv_choice(int entry, const GemvArgs& g, hipStream_t st) {
+  TunerState& t = tuner();
+  std::lock_guard<std::mutex> lock(t.mu);
+  const int mode = tuning_mode_locked(t);
+  // default: the largest R that still gives >= 2 work-groups per compute unit
+  auto default_idx = [&]() {
+    const int subs = 64 >> g.lpr_log2;
+    for (int i = kNumGemvCandidates - 1; i > 0; --i) {
+      const int64_t wgs = ceil_div(g.N, 4LL * subs * kGemvCandidates[i]);
+      if (wgs >= 512) return i;
+    }
+    return 0;
+  };
+  if (mode == 2) {
+    int f = t.forced;
+    if (f < 0 || f >= kNumGemvCandidates) f = 0;
+    t.last_choice[entry] = f;
+    return kGemvCandidates[f];
+  }
+  if (mode == 1 || !g.chunked) {
+    const int d = default_idx();
+    t.last_choice[entry] = d;
+    return kGemvCandidates[d];
+  }
+  const int64_t mb = g.M;  // M <= 8: one bucket per M
+  auto key = std::make_tuple(entry, mb, g.K, g.N, g.bits, g.block, g.a_type, g.fmt);
+  auto it = t.choice.find(key);
+  if (it != t.choice.end()) {
+    t.last_choice[entry] = it->second;
+    return kGemvCandidates[it->second];
+  }
+  if (stream_capturing(st)) {  // no timing under capture: default now, decide later
+    const int d = default_idx();
+    t.last_choice[entry] = d;
+    return kGemvCandidates[d];
+  }
+  // --- up-front cold timing -------------------------------------------------
+  const size_t wbytes = (size_t)(g.N * g.row_bytes);
+  const size_t sbytes = (size_t)(g.N * g.nblk) * (g.fmt == GEMV_CODEBOOK ? 4 : 2);
+  const size_t zbytes = (g.zp_kind == QMM_ZP_PACKED) ? (size_t)(g.N * g.zp_row_bytes)
+                        : (g.zp_kind == QMM_ZP_F16)  ? (size_t)(g.N * g.nblk * 2)
+                                                     : 0;
+  const size_t unit = ((wbytes + 255) & ~size_t(255)) + ((sbytes + 255) & ~size_t(255)) +
+                      ((zbytes + 255) & ~size_t(255));
+  const size_t obytes = (size_t)(g.M * g.N * 4);
+  int chosen = default_idx();
+  if (ensure_pool(t, unit, obytes)) {
+    constexpr int kRounds = 9;
+    constexpr int kBurst = 4;
+    std::vector<double> times(kRounds * kNumGemvCandidates, 0.0);
+    hipEvent_t e0, e1;
+    bool ok = hipEventCreate(&e0) == hipSuccess && hipEventCreate(&e1) == hipSuccess;
+    for (int r = 0; ok && r < kRounds; ++r) {
+      for (int c = 0; ok && c < kNumGemvCandidates; ++c) {
+        ok = hipEventRecord(e0, st) == hipSuccess;
+        for (int b = 0; ok && b < kBurst; ++b) {
+          GemvArgs tg = g;
+          uint8_t* reg = next_region(t, unit);
+          tg.W = reg;
+          uint8_t* sp = reg + ((wbytes + 255) & ~size_t(255));
+          if (g.fmt == GEMV_CODEBOOK) tg.absmax = (const float*)sp;
+          else tg.scales = (const uint16_t*)sp;
+          if (zbytes) tg.zp = sp + ((sbytes + 255) & ~size_t(255));
+          tg.C = t.out_scratch;
+          tg.c_type = QMM_F32;
+          tg.bias = nullptr;
+          ok = launch_gemv(tg, kGemvCandidates[c], st) == hipSuccess &&
+               hipPeekAtLastError() == hipSuccess;
+        }
+        ok = ok && hipEventRecord(e1, st) == hipSuccess && hipEventSynchronize(e1) == hipSuccess;
+        float ms = 0;
+        ok = ok && hipEventElapsedTime(&ms, e0, e1) == hipSuccess;
+        times[r * kNumGemvCandidates + c] = ms * 1000.0;
+      }
+    }
+    if (ok) {
+      chosen = pick_winner(times.data(), kRounds, kNumGemvCandidates);
+      if (env_flag("QMM_LOG")) {
+        std::fprintf(stderr, "[qmm] tune entry=%d M=%lld K=%lld N=%lld bits=%d block=%d ->", entry,
+                     (long long)g.M, (long long)g.K, (long long)g.N, g.bits, g.block);
+        for (int c = 0; c < kNumGemvCandidates; ++c) {
+          double tot = 0;
+          for (int r = 1; r < kRounds; ++r) tot += times[r * kNumGemvCandidates + c];
+          std::fprintf(stderr, " R=%d:%.2fus", kGemvCandidates[c], tot / ((kRounds - 1) * kBurst));
+        }
+        std::fprintf(stderr, " pick R=%d\n", kGemvCandidates[chosen]);
+      }
+      t.choice[key] = chosen;
+    } else {
+      (void)hipGetLastError();  // timing failed: default tiling, decide again later
+    }
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+  }
+  t.last_choice[entry] = chosen;
+  return kGemvCandidates[chosen];
+}
+
+// MoE decode candidates: rows per lane of the fc1 kernel (each row = a g row and
+// its u row) and of the fc2 kernel.
+constexpr int kQmoeCandidates[] = {1, 2};
+constexpr int kNumQmoeCandidates = 2;
+
+struct QmoeTimingBufs {
+  int32_t* ids = nullptr;  // timing expert ids, [kSets][T][k]
+  size_t ids_count = 0;
+  uint16_t* y = nullptr;   // timing output [T][H]
+  size_t y_bytes = 0;
+};
+
+QmoeTimingBufs& qmoe_bufs() {
+  static QmoeTimingBufs* b = new QmoeTimingBufs();
+  return *b;
+}
+
+// Choose (fc1, fc2) rows-per-lane for a MoE shape.  The first uncaptured call of
+// a shape times each candidate of each kernel: one discarded round, then 8 timed
+// rounds, every timed launch on a different set of k experts (so the weights are
+// read cold), writing only the call's scratch and a library-owned output.
+void qmoe_choice(const QmoeArgs& a, hipStream_t st, int* r1, int* r2) {
+  TunerState& t = tuner();
+  std::lock_guard<std::mutex> lock(t.mu);
+  const int mode = tuning_mode_locked(t);
+  auto finish = [&](int c1, int c2) {
+    t.last_choice[ENTRY_QMOE_FC1] = c1;
+    t.last_choice[ENTRY_QMOE_FC2] = c2;
+    *r1 = kQmoeCandidates[c1];
+    *r2 = kQmoeCandidates[c2];
+  };
+  if (mode == 2) {
+    int f = t.forced;
+    if (f < 0 || f >= kNumQmoeCandidates * kNumQmoeCandidates) f = 0;
+    finish(f % kNumQmoeCandidates, f / kNumQmoeCandidates);
+    return;
+  }
+  if (mode == 1) {
+    finish(0, 0);
+    return;
+  }
+  auto key1 = std::make_tuple((int)ENTRY_QMOE_FC1, a.T * 1000 + a.k, a.H, a.I, a.block, a.mode,
+                              (int)a.E, a.fc1.zp != nullptr);
+  auto key2 = std::make_tuple((int)ENTRY_QMOE_FC2, a.T * 1000 + a.k, a.H, a.I, a.block, a.mode,
+                              (int)a.E, a.fc2.zp != nullptr);
+  auto i1 = t.choice.find(key1), i2 = t.choice.find(key2);
+  if (i1 != t.choice.end() && i2 != t.choice.end()) {
+    finish(i1->second, i2->second);
+    return;
+  }
+  if (stream_capturing(st)) {
+    finish(0, 0);
+    return;
+  }
+  QmoeTimingBufs& b = qmoe_bufs();
+  constexpr int kRounds = 9;
+  const int sets = kRounds * kNumQmoeCandidates * 2;
+  const size_t ids_count = (size_t)sets * a.T * a.k;
+  const size_t y_bytes = (size_t)a.T * a.H * 2;
+  bool ok = true;
+  if (b.ids_count < ids_count) {
+    if (b.ids) (void)hipFree(b.ids);
+    b.ids = nullptr;
+    b.ids_count = 0;
+    ok = hipMalloc((void**)&b.ids, ids_count * 4) == hipSuccess;
+    if (ok) b.ids_count = ids_count;
+  }
+  if (ok && b.y_bytes < y_bytes) {
+    if (b.y) (void)hipFree(b.y);
+    b.y = nullptr;
+    b.y_bytes = 0;
+    ok = hipMalloc((void**)&b.y, y_bytes) == hipSuccess;
+    if (ok) b.y_bytes = y_bytes;
+  }
+  int c1 = 0, c2 = 0;
+  if (ok) {
+    // timing expert sets: launch s of token tt uses experts (s*k*T + tt*k + j) mod E,
+    // so consecutive launches touch different experts
+    std::vector<int32_t> hid(ids_count);
+    for (int s = 0; s < sets; ++s)
+      for (int64_t tt = 0; tt < a.T; ++tt)
+        for (int j = 0; j < a.k; ++j)
+          hid[((size_t)s * a.T + tt) * a.k + j] =
+              (int32_t)(((int64_t)s * a.k * a.T + tt * a.k + j) % a.E);
+    ok = hipMemcpy(b.ids, hid.data(), ids_count * 4, hipMemcpyHostToDevice) == hipSuccess;
+  }
+  if (ok) {
+    hipEvent_t e0, e1;
+    ok = hipEventCreate(&e0) == hipSuccess && hipEventCreate(&e1) == hipSuccess;
+    std::vector<double> t1(kRounds * kNumQmoeCandidates), t2(kRounds * kNumQmoeCandidates);
+    int set = 0;
+    for (int r = 0; ok && r < kRounds; ++r) {
+      for (int which = 0; ok && which < 2; ++which) {
+        for (int c = 0; ok && c < kNumQmoeCandidates; ++c) {
+          QmoeArgs ta = a;
+          ta.ids = b.ids + (size_t)(set++) * a.T * a.k;
+          ta.Y = b.y;
+          ok = hipEventRecord(e0, st) == hipSuccess;
+          if (which == 0) ok = ok && launch_qmoe_fc1(ta, kQmoeCandidates[c], st) == hipSuccess;
+          else ok = ok && launch_qmoe_fc2(ta, kQmoeCandidates[c], st) == hipSuccess;
+          ok = ok && hipPeekAtLastError() == hipSuccess;
+          ok = ok && hipEventRecord(e1, st) == hipSuccess && hipEventSynchronize(e1) == hipSuccess;
+          float ms = 0;
+          ok = ok && hipEventElapsedTime(&ms, e0, e1) == hipSuccess;
+          (which == 0 ? t1 : t2)[r * kNumQmoeCandidates + c] = ms * 1000.0;
+        }
+      }
+    }
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    if (ok) {
+      c1 = pick_winner(t1.data(), kRounds, kNumQmoeCandidates);
+      c2 = pick_winner(t2.data(), kRounds, kNumQmoeCandidates);
+      t.choice[key1] = c1;
+      t.choice[key2] = c2;
+      if (env_flag("QMM_LOG")) {
+        for (int which = 0; which < 2; ++which) {
+          const std::vector<double>& tv = which == 0 ? t1 : t2;
+          std::fprintf(stderr, "[qmm] tune qmoe fc%d T=%lld H=%lld I=%lld E=%lld k=%d block=%d mode=%d ->",
+                       which + 1, (long long)a.T, (long long)a.H, (long long)a.I, (long long)a.E,
+                       a.k, a.block, a.mode);
+          for (int c = 0; c < kNumQmoeCandidates; ++c) {
+            double tot = 0;
+            for (int r = 1; r < kRounds; ++r) tot += tv[r * kNumQmoeCandidates + c];
+            std::fprintf(stderr, " R=%d:%.2fus", kQmoeCandidates[c], tot / (kRounds - 1));
+          }
+          std::fprintf(stderr, " pick R=%d\n", kQmoeCandidates[which == 0 ? c1 : c2]);
+        }
+      }
+    }
+  }
+  if (!ok) {
+    (void)hipGetLastError();
+    c1 = c2 = 0;
+  }
+  finish(c1, c2);
+}
+
+// ---------------------------------------------------------------------------
+// argument checks
+// ---------------------------------------------------------------------------
+qmm_status check_nbits(const void* A, int a_type, int64_t M, int64_t K, int64_t N, const uint8_t* W,
+                       int bits, int block, const uint16_t* scales, const void* zp, int zp_kind,
+                       const void* bias, const void* C, int c_type, const void* workspace,
+                       size_t workspace_bytes) {
+  (void)bias;
+  if (!valid_dtype(a_type) || !valid_dtype(c_type)) return QMM_E_DTYPE;
+  if (bits != 2 && bits != 4) return QMM_E_BITS;
+  if (!is_pow2_block(block)) return QMM_E_BLOCK;
+  if (M < 0 || K < 0 || N < 0 || M > (1LL << 30) || K > (1LL << 30) || N > (1LL << 30))
+    return QMM_E_SHAPE;
+  if (zp_kind < QMM_ZP_NONE || zp_kind > QMM_ZP_UNIFORM) return QMM_E_MODE;
+  if (M == 0 || N == 0) return QMM_OK;
+  if (!C) return QMM_E_NULL;
+  if (K > 0 && (!A || !W || !scales)) return QMM_E_NULL;
+  if ((zp_kind == QMM_ZP_PACKED || zp_kind == QMM_ZP_F16) && K > 0 && !zp) return QMM_E_NULL;
+  if (!aligned(A, dtype_size(a_type)) || !aligned(C, dtype_size(c_type)) || !aligned(scales, 2))
+    return QMM_E_ALIGN;
+  if (bias && !aligned(bias, dtype_size(c_type))) return QMM_E_ALIGN;
+  if (zp_kind == QMM_ZP_F16 && !aligned(zp, 2)) return QMM_E_ALIGN;
+  const size_t need = qmm_nbits_workspace_bytes(M, K, a_type);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return QMM_E_WORKSPACE;
+  return QMM_OK;
+}
+
+qmm_status check_codebook(const void* A, int a_type, int64_t M, int64_t K, int64_t N,
+                          const uint8_t* W, int block, const float* absmax, const float* codebook,
+                          const void* bias, const void* C, int c_type, const void* workspace,
+                          size_t workspace_bytes) {
+  if (!valid_dtype(a_type) || !valid_dtype(c_type)) return QMM_E_DTYPE;
+  if (!is_pow2_block(block)) return QMM_E_BLOCK;
+  if (M < 0 || K < 0 || N < 0 || M > (1LL << 30) || K > (1LL << 30) || N > (1LL << 30))
+    return QMM_E_SHAPE;
+  if (M == 0 || N == 0) return QMM_OK;
+  if (!C) return QMM_E_NULL;
+  if (K > 0 && (!A || !W || !absmax || !codebook)) return QMM_E_NULL;
+  if (!aligned(A, dtype_size(a_type)) || !aligned(C, dtype_size(c_type)) || !aligned(absmax, 4) ||
+      !aligned(codebook, 4))
+    return QMM_E_ALIGN;
+  if (bias && !aligned(bias, dtype_size(c_type))) return QMM_E_ALIGN;
+  const size_t need = qmm_codebook4_workspace_bytes(M, K, a_type);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return QMM_E_WORKSPACE;
+  return QMM_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct QmoeLayout {
+  size_t h = 0, xq = 0, xs = 0, hq = 0, hs = 0, total = 0;
+};
+
+QmoeLayout qmoe_layout(int64_t T, int64_t H, int64_t I, int k, int mode) {
+  QmoeLayout L;
+  size_t off = 0;
+  L.h = off;
+  off += align256((size_t)(T * k * I) * 2);
+  if (mode == QMOE_INT8_ACT) {
+    L.xq = off;
+    off += align256((size_t)(T * H));
+    L.xs = off;
+    off += align256((size_t)(T * (H / 32)) * 4);
+    L.hq = off;
+    off += align256((size_t)(T * k * I));
+    L.hs = off;
+    off += align256((size_t)(T * k * (I / 32)) * 4);
+  }
+  L.total = off;
+  return L;
+}
+
+constexpr size_t kMaxLds = 64 * 1024;
+
+qmm_status check_qmoe(const uint16_t* X, int64_t T, int64_t H, int64_t I, int64_t E, int k,
+                      const int32_t* ids, const float* w, qmoe_weights fc1, qmoe_weights fc2,
+                      int bits, int block, int mode, const uint16_t* Y, const void* scratch,
+                      size_t scratch_bytes) {
+  if (bits != 4) return QMM_E_BITS;
+  if (!is_pow2_block(block) || block < 32) return QMM_E_BLOCK;
+  if (mode != QMOE_FP && mode != QMOE_INT8_ACT) return QMM_E_MODE;
+  if (T < 0 || T > 4096 || H <= 0 || I <= 0 || H > (1LL << 24) || I > (1LL << 24)) return QMM_E_SHAPE;
+  if (E < 1 || E > (1LL << 20) || k < 1 || k > 64 || k > E) return QMM_E_SHAPE;
+  if (H % 8 != 0 || I % 8 != 0) return QMM_E_SHAPE;
+  if (mode == QMOE_INT8_ACT) {
+    if (H % 32 != 0 || I % 32 != 0) return QMM_E_SHAPE;
+    if ((size_t)H + (size_t)(H / 32) * 8 > kMaxLds) return QMM_E_SHAPE;
+    if ((size_t)(k * I) + (size_t)(k * I / 32) * 8 > kMaxLds) return QMM_E_SHAPE;
+  }
+  if (T == 0) return QMM_OK;
+  if (!X || !ids || !w || !Y) return QMM_E_NULL;
+  if (!fc1.W || !fc1.scales || !fc2.W || !fc2.scales) return QMM_E_NULL;
+  if (!aligned(X, 16) || !aligned(Y, 2) || !aligned(ids, 4) || !aligned(w, 4)) return QMM_E_ALIGN;
+  if (!aligned(fc1.W, 16) || !aligned(fc2.W, 16) || !aligned(fc1.scales, 2) ||
+      !aligned(fc2.scales, 2) || !aligned(fc1.bias, 2) || !aligned(fc2.bias, 2))
+    return QMM_E_ALIGN;
+  const size_t need = qmoe_layout(T, H, I, k, mode).total;
+  if (!scratch || scratch_bytes < need) return QMM_E_WORKSPACE;
+  if (!aligned(scratch, 256)) return QMM_E_ALIGN;
+  return QMM_OK;
+}
+
+GemvArgs make_gemv(const void* A, int a_type, int64_t M, int64_t K, int64_t N, const uint8_t* W,
+                   int bits, int block, const void* bias, void* C, int c_type) {
+  GemvArgs g{};
+  g.A = A;
+  g.a_type = a_type;
+  g.M = M;
+  g.K = K;
+  g.N = N;
+  g.W = W;
+  g.bits = bits;
+  g.block = block;
+  g.block_log2 = __builtin_ctz((unsigned)block);
+  g.nblk = ceil_div(K, block);
+  g.row_bytes = g.nblk * block * bits / 8;
+  g.nchunks = g.row_bytes / 16;
+  g.bias = bias;
+  g.C = C;
+  g.c_type = c_type;
+  g.chunked = (g.row_bytes % 16 == 0) && aligned(W, 16);
+  g.lpr_log2 = gemv_lanes_per_row_log2(g.nchunks);
+  g.a_vec = aligned(A, 16) && (K % 4 == 0);
+  return g;
+}
+
+// Run a GEMV over all M rows, at most kMaxGemvM rows of A per launch.
+hipError_t run_gemv_rows(int entry, GemvArgs g, hipStream_t st) {
+  const size_t a_es = dtype_size(g.a_type), c_es = dtype_size(g.c_type);
+  for (int64_t m0 = 0; m0 < g.M; m0 += kMaxGemvM) {
+    GemvArgs s = g;
+    s.M = std::min<int64_t>(kMaxGemvM, g.M - m0);
+    s.A = (const uint8_t*)g.A + m0 * g.K * (int64_t)a_es;
+    s.C = (uint8_t*)g.C + m0 * g.N * (int64_t)c_es;
+    s.a_vec = g.a_vec && aligned(s.A, 16);
+    gemv_plan(s, device_cus());
+    const int R = gemv_choice(entry, s, st);
+    hipError_t e = launch_gemv(s, R, st);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace
+
+// ===========================================================================
+// extern "C" entry points
+// ===========================================================================
+extern "C" {
+
+size_t qmm_nbits_workspace_bytes(int64_t M, int64_t K, int a_type) {
+  (void)M; (void)K; (void)a_type;
+  return 0;  // the prefill cast workspace is added with the matrix-core path
+}
+
+size_t qmm_codebook4_workspace_bytes(int64_t M, int64_t K, int a_type) {
+  (void)M; (void)K; (void)a_type;
+  return 0;
+}
+
+qmm_status qmm_validate_nbits(const void* A, int a_type, int64_t M, int64_t K, int64_t N,
+                              const uint8_t* W, int bits, int block, const uint16_t* scales,
+                              const void* zp, int zp_kind, const void* bias, const void* C,
+                              int c_type, const void* workspace, size_t workspace_bytes) {
+  return check_nbits(A, a_type, M, K, N, W, bits, block, scales, zp, zp_kind, bias, C, c_type,
+                     workspace, workspace_bytes);
+}
+
+qmm_status qmm_validate_codebook4(const void* A, int a_type, int64_t M, int64_t K, int64_t N,
+                                  const uint8_t* W, int block, const float* absmax,
+                                  const float* codebook, const void* bias, const void* C,
+                                  int c_type, const void* workspace, size_t workspace_bytes) {
+  return check_codebook(A, a_type, M, K, N, W, block, absmax, codebook, bias, C, c_type,
+                        workspace, workspace_bytes);
+}
+
+qmm_status qmm_nbits(const void* A, int a_type, int64_t M, int64_t K, int64_t N, const uint8_t* W,
+                     int bits, int block, const uint16_t* scales, const void* zp, int zp_kind,
+                     float uniform_zp, const void* bias, void* C, int c_type, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  (void)hipGetLastError();
+  const qmm_status s = check_nbits(A, a_type, M, K, N, W, bits, block, scales, zp, zp_kind, bias, C,
+                                   c_type, workspace, workspace_bytes);
+  if (s != QMM_OK) return s;
+  if (M == 0 || N == 0) return QMM_OK;
+  hipStream_t st = (hipStream_t)stream;
+  GemvArgs g = make_gemv(A, a_type, M, K, N, W, bits, block, bias, C, c_type);
+  g.fmt = GEMV_AFFINE;
+  g.scales = scales;
+  g.zp = zp;
+  g.zp_kind = zp_kind;
+  g.uniform_zp = uniform_zp;
+  g.zp_row_bytes = ceil_div(g.nblk * bits, 8);
+  hipError_t e = run_gemv_rows(ENTRY_NBITS, g, st);
+  if (e != hipSuccess) return (qmm_status)e;
+  return (qmm_status)hipGetLastError();
+}
+
+qmm_status qmm_codebook4(const void* A, int a_type, int64_t M, int64_t K, int64_t N,
+                         const uint8_t* W, int block, const float* absmax, const float* codebook,
+                         const void* bias, void* C, int c_type, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  (void)hipGetLastError();
+  const qmm_status s = check_codebook(A, a_type, M, K, N, W, block, absmax, codebook, bias, C,
+                                      c_type, workspace, workspace_bytes);
+  if (s != QMM_OK) return s;
+  if (M == 0 || N == 0) return QMM_OK;
+  hipStream_t st = (hipStream_t)stream;
+  GemvArgs g = make_gemv(A, a_type, M, K, N, W, 4, block, bias, C, c_type);
+  g.fmt = GEMV_CODEBOOK;
+  g.absmax = absmax;
+  g.codebook = codebook;
+  hipError_t e = run_gemv_rows(ENTRY_CODEBOOK, g, st);
+  if (e != hipSuccess) return (qmm_status)e;
+  return (qmm_status)hipGetLastError();
+}
+
+size_t qmm_uniform_scratch_bytes(void) { return (2 + kUniformPartials) * sizeof(uint32_t); }
+
+qmm_status qmm_fp16_uniform_value(const uint16_t* zp, int64_t count, void* scratch,
+                                  size_t scratch_bytes, int* is_uniform, float* value,
+                                  void* stream) {
+  (void)hipGetLastError();
+  if (!is_uniform || !value) return QMM_E_NULL;
+  *is_uniform = 0;
+  *value = 0.0f;
+  if (count < 0) return QMM_E_SHAPE;
+  if (count == 0) return QMM_OK;
+  if (!zp || !scratch) return QMM_E_NULL;
+  if (scratch_bytes < qmm_uniform_scratch_bytes()) return QMM_E_WORKSPACE;
+  if (!aligned(zp, 2) || !aligned(scratch, 4)) return QMM_E_ALIGN;
+  hipStream_t st = (hipStream_t)stream;
+  launch_uniform_check(zp, count, (uint32_t*)scratch, st);
+  uint32_t res[2] = {0, 0};
+  hipError_t e = hipMemcpyAsync(res, scratch, sizeof(res), hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return (qmm_status)e;
+  *is_uniform = res[0] ? 1 : 0;
+  std::memcpy(value, &res[1], 4);
+  return (qmm_status)hipGetLastError();
+}
+
+qmm_status qmm_dequantize_nbits(const uint8_t* W, int bits, int block, const uint16_t* scales,
+                                const void* zp, int zp_kind, float uniform_zp, int64_t N, int64_t K,
+                                void* out, int out_type, void* stream) {
+  (void)hipGetLastError();
+  if (bits != 2 && bits != 4) return QMM_E_BITS;
+  if (!is_pow2_block(block)) return QMM_E_BLOCK;
+  if (N < 0 || K < 0) return QMM_E_SHAPE;
+  if (out_type != QMM_F32 && out_type != QMM_F16) return QMM_E_DTYPE;
+  if (zp_kind < QMM_ZP_NONE || zp_kind > QMM_ZP_UNIFORM) return QMM_E_MODE;
+  if (N == 0 || K == 0) return QMM_OK;
+  if (!W || !scales || !out) return QMM_E_NULL;
+  if ((zp_kind == QMM_ZP_PACKED || zp_kind == QMM_ZP_F16) && !zp) return QMM_E_NULL;
+  DequantArgs d{};
+  d.W = W;
+  d.fmt = GEMV_AFFINE;
+  d.bits = bits;
+  d.block = block;
+  d.N = N;
+  d.K = K;
+  d.nblk = ceil_div(K, block);
+  d.row_bytes = d.nblk * block * bits / 8;
+  d.scales = scales;
+  d.zp = zp;
+  d.zp_kind = zp_kind;
+  d.uniform_zp = uniform_zp;
+  d.zp_row_bytes = ceil_div(d.nblk * bits, 8);
+  d.out = out;
+  d.out_type = out_type;
+  launch_dequant(d, (hipStream_t)stream);
+  return (qmm_status)hipGetLastError();
+}
+
+qmm_status qmm_dequantize_codebook4(const uint8_t* W, int block, const float* absmax,
+                                    const float* codebook, int64_t N, int64_t K, void* out,
+                                    int out_type, void* stream) {
+  (void)hipGetLastError();
+  if (!is_pow2_block(block)) return QMM_E_BLOCK;
+  if (N < 0 || K < 0) return QMM_E_SHAPE;
+  if (out_type != QMM_F32 && out_type != QMM_F16) return QMM_E_DTYPE;
+  if (N == 0 || K == 0) return QMM_OK;
+  if (!W || !absmax || !codebook || !out) return QMM_E_NULL;
+  DequantArgs d{};
+  d.W = W;
+  d.fmt = GEMV_CODEBOOK;
+  d.bits = 4;
+  d.block = block;
+  d.N = N;
+  d.K = K;
+  d.nblk = ceil_div(K, block);
+  d.row_bytes = d.nblk * block / 2;
+  d.absmax = absmax;
+  d.codebook = codebook;
+  d.out = out;
+  d.out_type = out_type;
+  launch_dequant(d, (hipStream_t)stream);
+  return (qmm_status)hipGetLastError();
+}
+
+size_t qmoe_decode_scratch_bytes(int64_t T, int64_t H, int64_t I, int k, int mode) {
+  if (T < 0 || H < 0 || I < 0 || k < 0) return 0;
+  return qmoe_layout(T, H, I, k, mode).total;
+}
+
+qmm_status qmm_validate_qmoe(const uint16_t* X, int64_t T, int64_t H, int64_t I, int64_t E, int k,
+                             const int32_t* expert_ids, const float* expert_w, qmoe_weights fc1,
+                             qmoe_weights fc2, int bits, int block, int mode, const uint16_t* Y,
+                             const void* scratch, size_t scratch_bytes) {
+  return check_qmoe(X, T, H, I, E, k, expert_ids, expert_w, fc1, fc2, bits, block, mode, Y, scratch,
+                    scratch_bytes);
+}
+
+qmm_status qmoe_decode_fused(const uint16_t* X, int64_t T, int64_t H, int64_t I, int64_t E, int k,
+                             const int32_t* expert_ids, const float* expert_w, qmoe_weights fc1,
+                             qmoe_weights fc2, int bits, int block, int mode, uint16_t* Y,
+                             void* scratch, size_t scratch_bytes, void* stream) {
+  (void)hipGetLastError();
+  const qmm_status s = check_qmoe(X, T, H, I, E, k, expert_ids, expert_w, fc1, fc2, bits, block,
+                                  mode, Y, scratch, scratch_bytes);
+  if (s != QMM_OK) return s;
+  if (T == 0) return QMM_OK;
+  hipStream_t st = (hipStream_t)stream;
+  QmoeArgs a{};
+  a.X = X;
+  a.T = T;
+  a.H = H;
+  a.I = I;
+  a.E = E;
+  a.k = k;
+  a.ids = expert_ids;
+  a.rw = expert_w;
+  a.fc1 = fc1;
+  a.fc2 = fc2;
+  a.block = block;
+  a.mode = mode;
+  a.fc1_nblk = ceil_div(H, block);
+  a.fc1_row_bytes = a.fc1_nblk * block / 2;
+  a.fc1_zp_row_bytes = ceil_div(a.fc1_nblk, 2);
+  a.fc1_chunks = ceil_div(H, 32);
+  a.fc1_lpr_log2 = gemv_lanes_per_row_log2(a.fc1_chunks);
+  a.fc2_nblk = ceil_div(I, block);
+  a.fc2_row_bytes = a.fc2_nblk * block / 2;
+  a.fc2_zp_row_bytes = ceil_div(a.fc2_nblk, 2);
+  a.fc2_chunks = ceil_div(I, 32);
+  a.fc2_lpr_log2 = gemv_lanes_per_row_log2(a.fc2_chunks);
+  const QmoeLayout L = qmoe_layout(T, H, I, k, mode);
+  uint8_t* sc = (uint8_t*)scratch;
+  a.h = (uint16_t*)(sc + L.h);
+  if (mode == QMOE_INT8_ACT) {
+    a.xq_out = (int8_t*)(sc + L.xq);
+    a.xs_out = (float*)(sc + L.xs);
+    a.hq_out = (int8_t*)(sc + L.hq);
+    a.hs_out = (float*)(sc + L.hs);
+  }
+  a.Y = Y;
+  int r1 = 1, r2 = 1;
+  qmoe_choice(a, st, &r1, &r2);
+  hipError_t e = launch_qmoe_fc1(a, r1, st);
+  if (e == hipSuccess) e = launch_qmoe_fc2(a, r2, st);
+  if (e != hipSuccess) return (qmm_status)e;
+  return (qmm_status)hipGetLastError();
+}
+
+qmm_status qmm_set_tuning(int mode, int forced_index) {
+  if (mode < 0 || mode > 2) return QMM_E_MODE;
+  TunerState& t = tuner();
+  std::lock_guard<std::mutex> lock(t.mu);
+  t.mode = mode;
+  t.forced = forced_index;
+  return QMM_OK;
+}
+
+int qmm_num_candidates(int entry) {
+  if (entry == ENTRY_NBITS || entry == ENTRY_CODEBOOK) return kNumGemvCandidates;
+  if (entry == ENTRY_QMOE_FC1 || entry == ENTRY_QMOE_FC2) return kNumQmoeCandidates;
+  return 0;
+}
+
+int qmm_tuned_choice(int entry) {
+  if (entry < 0 || entry >= ENTRY_COUNT) return -1;
+  TunerState& t = tuner();
+  std::lock_guard<std::mutex> lock(t.mu);
+  return t.last_choice[entry];
+}
+
+void qmm_clear_tuning(void) {
+  TunerState& t = tuner();
+  std::lock_guard<std::mutex> lock(t.mu);
+  t.choice.clear();
+  for (int i = 0; i < ENTRY_COUNT; ++i) t.last_choice[i] = -1;
+}
+
+int qmm_tuner_pick(const double* times_us, int rounds, int ncand) {
+  if (!times_us || rounds < 2 || ncand < 1) return -1;
+  return pick_winner(times_us, rounds, ncand);
+}
+
+const char* qmm_status_string(qmm_status s) {
+  switch (s) {
+    case QMM_OK: return "ok";
+    case QMM_E_NULL: return "null pointer";
+    case QMM_E_DTYPE: return "unsupported element type";
+    case QMM_E_BITS: return "unsupported bit width";
+    case QMM_E_BLOCK: return "unsupported block size";
+    case QMM_E_SHAPE: return "bad shape";
+    case QMM_E_ALIGN: return "misaligned pointer";
+    case QMM_E_WORKSPACE: return "workspace missing or too small";
+    case QMM_E_MODE: return "unknown mode or zero-point kind";
+    case QMM_E_DEVICE: return "no usable device";
+    default: return s > 0 ? hipGetErrorString((hipError_t)s) : "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,105 @@
+// Device-side helpers shared by the gfx950 kernels of the qmm library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "qmm.h"
+
+namespace qmm {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+// ---- scalar conversions (all round to nearest even) -------------------------
+
+__device__ __forceinline__ float f16_to_f32(uint16_t h) {
+  _Float16 v;
+  __builtin_memcpy(&v, &h, 2);
+  return (float)v;
+}
+
+__device__ __forceinline__ uint16_t f32_to_f16(float f) {
+  _Float16 v = (_Float16)f;  // v_cvt_f16_f32, round to nearest even
+  uint16_t h;
+  __builtin_memcpy(&h, &v, 2);
+  return h;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+template <int T>
+__device__ __forceinline__ float load_elem(const void* p, int64_t i) {
+  if constexpr (T == QMM_F32) return ((const float*)p)[i];
+  else if constexpr (T == QMM_F16) return f16_to_f32(((const uint16_t*)p)[i]);
+  else return bf16_to_f32(((const uint16_t*)p)[i]);
+}
+
+__device__ __forceinline__ float load_elem_rt(const void* p, int t, int64_t i) {
+  if (t == QMM_F32) return ((const float*)p)[i];
+  if (t == QMM_F16) return f16_to_f32(((const uint16_t*)p)[i]);
+  return bf16_to_f32(((const uint16_t*)p)[i]);
+}
+
+__device__ __forceinline__ void store_elem_rt(void* p, int t, int64_t i, float v) {
+  if (t == QMM_F32) ((float*)p)[i] = v;
+  else if (t == QMM_F16) ((uint16_t*)p)[i] = f32_to_f16(v);
+  else ((uint16_t*)p)[i] = f32_to_bf16(v);
+}
+
+// ---- code extraction -------------------------------------------------------
+
+// Unsigned `bits`-wide code of element j (0-based) of a packed block.
+__device__ __forceinline__ uint32_t code_at(const uint8_t* blk, int j, int bits) {
+  const int bit = j * bits;
+  return (blk[bit >> 3] >> (bit & 7)) & ((1u << bits) - 1u);
+}
+
+// Zero point of (row n, block b) as fp32 for each zero-point kind.
+__device__ __forceinline__ float zero_point(const void* zp, int zp_kind, float uniform_zp,
+                                            int bits, int64_t n, int b, int64_t zp_row_bytes,
+                                            int64_t nblk) {
+  switch (zp_kind) {
+    case QMM_ZP_PACKED: {
+      const uint8_t* row = (const uint8_t*)zp + n * zp_row_bytes;
+      const int bit = b * bits;
+      return (float)((row[bit >> 3] >> (bit & 7)) & ((1u << bits) - 1u));
+    }
+    case QMM_ZP_F16:
+      return f16_to_f32(((const uint16_t*)zp)[n * nblk + b]);
+    case QMM_ZP_UNIFORM:
+      return uniform_zp;
+    default:
+      return (float)(1 << (bits - 1));
+  }
+}
+
+// Bit-exact affine dequant: fp32(fp32(q - zp) * s), two separate roundings.
+__device__ __forceinline__ float dequant_affine(uint32_t q, float zp, float s) {
+  float d = __fsub_rn((float)q, zp);
+  return __fmul_rn(d, s);
+}
+
+// ---- wave-level helpers ------------------------------------------------------
+
+// Butterfly sum over groups of `width` consecutive lanes (power of two <= 64).
+// Every lane of the group ends with the same, order-fixed result.
+__device__ __forceinline__ float group_sum(float v, int width) {
+  for (int off = 1; off < width; off <<= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+}  // namespace qmm

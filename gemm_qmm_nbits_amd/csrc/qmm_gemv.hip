@@ -1,0 +1,111 @@
+// Dispatch of the weight-streaming GEMV kernels (instantiated in qmm_gemv_*.hip).
+#include "qmm_device.h"
+#include "qmm_internal.h"
+
+namespace qmm {
+
+template <int FMT, int BITS, int AT>
+hipError_t launch_at_type(const GemvArgs& g, int R, hipStream_t st);
+
+template <int FMT, int BITS>
+static hipError_t launch_at(const GemvArgs& g, int R, hipStream_t st) {
+  switch (g.a_type) {
+    case QMM_F32: return launch_at_type<FMT, BITS, QMM_F32>(g, R, st);
+    case QMM_F16: return launch_at_type<FMT, BITS, QMM_F16>(g, R, st);
+    default: return launch_at_type<FMT, BITS, QMM_BF16>(g, R, st);
+  }
+}
+
+// Generic path for layouts the chunked kernel cannot read (row length not a
+// multiple of 16 bytes, or unaligned pointers): one wave per output column n,
+// lane l handles codes k = l, l+64, ..., each dequantized exactly as defined.
+__global__ __launch_bounds__(256) void gemv_generic_kernel(GemvArgs g) {
+  const int lane = threadIdx.x & 63;
+  const int64_t n = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (n >= g.N) return;
+  float acc[8];
+#pragma unroll
+  for (int m = 0; m < 8; ++m) acc[m] = 0.0f;
+  const int bits = g.fmt == GEMV_CODEBOOK ? 4 : g.bits;
+  const int blob = g.block * bits / 8;
+  for (int64_t k = lane; k < g.K; k += 64) {
+    const int b = (int)(k / g.block);
+    const int j = (int)(k % g.block);
+    const uint32_t q = code_at(g.W + n * g.row_bytes + (int64_t)b * blob, j, bits);
+    float w;
+    if (g.fmt == GEMV_CODEBOOK) {
+      w = __fmul_rn(g.codebook[q], g.absmax[n * g.nblk + b]);
+    } else {
+      const float s = f16_to_f32(g.scales[n * g.nblk + b]);
+      const float z = zero_point(g.zp, g.zp_kind, g.uniform_zp, bits, n, b, g.zp_row_bytes, g.nblk);
+      w = dequant_affine(q, z, s);
+    }
+    for (int m = 0; m < 8; ++m)
+      if (m < g.M) acc[m] = fmaf(load_elem_rt(g.A, g.a_type, (int64_t)m * g.K + k), w, acc[m]);
+  }
+  for (int m = 0; m < 8; ++m) acc[m] = group_sum(acc[m], 64);
+  if (lane == 0) {
+    const float bv = g.bias ? load_elem_rt(g.bias, g.c_type, n) : 0.0f;
+    for (int m = 0; m < 8; ++m)
+      if (m < g.M) store_elem_rt(g.C, g.c_type, (int64_t)m * g.N + n, acc[m] + bv);
+  }
+}
+
+
+int gemv_lanes_per_row_log2(int64_t nchunks) {
+  // Widest row group (fewest sequential chunks per lane) that keeps at least 80%
+  // of the lane slots busy; otherwise the group with the fewest idle slots
+  // (ties to the wider one).  Depends on the chunk count only.
+  for (int l = 6; l >= 3; --l) {
+    const int64_t lpr = 1LL << l;
+    const int64_t slots = ((nchunks + lpr - 1) / lpr) * lpr;
+    if (nchunks * 5 >= slots * 4) return l;
+  }
+  int best = 6;
+  int64_t best_slots = ((nchunks + 63) / 64) * 64;
+  for (int l = 5; l >= 3; --l) {
+    const int64_t lpr = 1LL << l;
+    const int64_t slots = ((nchunks + lpr - 1) / lpr) * lpr;
+    if (slots < best_slots) {
+      best_slots = slots;
+      best = l;
+    }
+  }
+  return best;
+}
+
+void gemv_plan(GemvArgs& g, int num_cus) {
+  g.mt = g.M <= 1 ? 1 : g.M <= 2 ? 2 : g.M <= 4 ? 4 : 8;
+  g.num_cus = num_cus > 0 ? num_cus : 256;
+  const int bits = g.fmt == GEMV_CODEBOOK ? 4 : g.bits;
+  const int64_t cs_bytes = (int64_t)(128 / bits + 4) * 4;  // LDS bytes per chunk slot per A row
+  const int64_t lpr = 1LL << g.lpr_log2;
+  const int64_t per_iter = (int64_t)g.mt * lpr * cs_bytes;  // one chunk per lane, all A rows
+  const int64_t iters_all = (g.nchunks + lpr - 1) / lpr;
+  int64_t iters = (int64_t)kGemvLdsBudget / per_iter;
+  if (iters < 1) iters = 1;
+  if (iters > iters_all) iters = iters_all > 0 ? iters_all : 1;
+  g.slice_chunks = (int)(iters * lpr);
+  g.lds_bytes = (size_t)(iters * per_iter) + 16 * sizeof(float);
+  if (g.lds_bytes > kMaxGemvLds) {
+    g.chunked = 0;  // no slice fits: generic kernel
+    g.lds_bytes = 0;
+  }
+  int per_cu = g.lds_bytes ? (int)(kMaxGemvLds / g.lds_bytes) : 8;
+  if (per_cu > 4) per_cu = 4;
+  if (per_cu < 1) per_cu = 1;
+  g.wg_per_cu = per_cu;
+}
+
+hipError_t launch_gemv(GemvArgs g, int rows_per_lane, hipStream_t st) {
+  if (!g.chunked) {
+    const dim3 grid((unsigned)((g.N + 3) / 4));
+    hipLaunchKernelGGL(gemv_generic_kernel, grid, dim3(256), 0, st, g);
+    return hipSuccess;
+  }
+  if (g.fmt == GEMV_CODEBOOK) return launch_at<GEMV_CODEBOOK, 4>(g, rows_per_lane, st);
+  if (g.bits == 2) return launch_at<GEMV_AFFINE, 2>(g, rows_per_lane, st);
+  return launch_at<GEMV_AFFINE, 4>(g, rows_per_lane, st);
+}
+
+}  // namespace qmm

@@ -1,0 +1,420 @@
+// Weight-streaming GEMV / skinny GEMM for M <= 8 on gfx950.
+//
+// Affine MatMulNBits weights ([P1] hip-ep PR 1318, "What", commit 1: GEMV that reads
+// fp32 A and writes fp32 C directly; uniform zero point as a scalar) and 16-entry
+// codebook 4-bit weights ([P3] bitsandbytes PR 1979, "Technical details": centroids
+// staged in LDS, scale applied once per chunk, next chunk prefetched into registers).
+//
+// Work decomposition (fixed by K, block and bits only, so every tiling gives the
+// same bits):
+//   * a weight row is read as 16-byte chunks; chunk c holds WPC = 128/bits codes;
+//   * each row is owned by a group of LPR lanes (LPR in {8,16,32,64}, chosen from
+//     the chunk count); lane p of the group handles chunks p, p+LPR, ... in order;
+//   * inside a chunk the codes are decoded four bytes at a time and multiplied into
+//     a per-group partial sum in index order; the group's scale (and zero point,
+//     folded as s * (sum a*q - zp * sum a)) is applied once per block group;
+//   * the LPR lane partials are combined by a fixed xor butterfly.
+// A tile of R rows per lane (the tunable part) only changes which wave owns a row.
+#pragma once
+#include "qmm_device.h"
+#include "qmm_internal.h"
+
+namespace qmm {
+
+// --- decoding four bytes (one dword) of codes into fp32 ------------------------
+//
+// 2-bit codes: masking with 0x33333333 leaves codes 4b and 4b+2 of byte b as the
+// two nibbles of that byte, each in 0..3; as e2m1 (fp4) nibbles 0..3 decode to
+// 0, 0.5, 1, 1.5, i.e. exactly q/2, two at a time with one conversion.
+// 4-bit codes: masking with 0x0f0f0f0f leaves one code per byte; as e4m3 (fp8)
+// bytes 0..15 decode to exactly q * 2^-9, two at a time.
+template <int B>
+__device__ __forceinline__ void fp4_pair(uint32_t ev, uint32_t od, float (&q)[16]) {
+  f32x2 e = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(ev, 1.0f, B);
+  f32x2 o = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(od, 1.0f, B);
+  q[4 * B + 0] = e.x;
+  q[4 * B + 2] = e.y;
+  q[4 * B + 1] = o.x;
+  q[4 * B + 3] = o.y;
+}
+
+template <int BITS>
+__device__ __forceinline__ void decode_dword_affine(uint32_t x, float (&q)[32 / BITS]) {
+  if constexpr (BITS == 2) {
+    const uint32_t ev = x & 0x33333333u;
+    const uint32_t od = (x >> 2) & 0x33333333u;
+    fp4_pair<0>(ev, od, q);
+    fp4_pair<1>(ev, od, q);
+    fp4_pair<2>(ev, od, q);
+    fp4_pair<3>(ev, od, q);
+  } else {
+    const uint32_t lo = x & 0x0f0f0f0fu;
+    const uint32_t hi = (x >> 4) & 0x0f0f0f0fu;
+    f32x2 l0 = __builtin_amdgcn_cvt_pk_f32_fp8(lo, false);
+    f32x2 l1 = __builtin_amdgcn_cvt_pk_f32_fp8(lo, true);
+    f32x2 h0 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
+    f32x2 h1 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
+    q[0] = l0.x; q[2] = l0.y; q[4] = l1.x; q[6] = l1.y;
+    q[1] = h0.x; q[3] = h0.y; q[5] = h1.x; q[7] = h1.y;
+  }
+}
+
+// Factor that turns the decoded values above into the codes themselves.
+template <int BITS>
+__device__ __forceinline__ constexpr float affine_decode_factor() {
+  return BITS == 2 ? 2.0f : 512.0f;
+}
+
+// Codebook lookup of the eight 4-bit codes of a dword from the LDS table.
+__device__ __forceinline__ void decode_dword_codebook(uint32_t x, const float* cb, float (&q)[8]) {
+  const uint32_t lo4 = (x << 2) & 0x3c3c3c3cu;  // byte b = 4 * code(2b)
+  const uint32_t hi4 = (x >> 2) & 0x3c3c3c3cu;  // byte b = 4 * code(2b+1)
+  const char* base = (const char*)cb;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    q[2 * b + 0] = *(const float*)(base + __builtin_amdgcn_ubfe(lo4, 8 * b, 8));
+    q[2 * b + 1] = *(const float*)(base + __builtin_amdgcn_ubfe(hi4, 8 * b, 8));
+  }
+}
+
+// Stage the activations of chunks [c0, c0 + SC) of every A row into LDS as fp32:
+// chunk slot `slot` of row m occupies lds[(m * SC + slot) * CS .. + WPC); codes past
+// K read 0.  The CS - WPC = 4 floats after each slot hold the sums of A over the
+// slot's (up to four) scale groups, for the zero-point fold; that padding also
+// spreads the lanes of a wave over distinct LDS banks.
+template <int AT, int WPC, int CS>
+__device__ __forceinline__ void stage_a(const GemvArgs& g, float* lds, int c0, int SC, int G) {
+  const int per_row = SC * (WPC / 4);  // float4 pieces per A row in the slice
+  const int total = (int)g.M * per_row;
+  const int K = (int)g.K;
+  for (int idx = threadIdx.x; idx < total; idx += blockDim.x) {
+    const int m = idx / per_row;
+    const int rem = idx - m * per_row;
+    const int slot = rem / (WPC / 4);
+    const int j4 = rem - slot * (WPC / 4);
+    const int k = (c0 + slot) * WPC + 4 * j4;
+    const int64_t base = (int64_t)m * K + k;
+    f32x4 v;
+    if (g.a_vec && k + 3 < K) {
+      if constexpr (AT == QMM_F32) {
+        v = *(const f32x4*)((const float*)g.A + base);
+      } else {
+        const uint2 u = *(const uint2*)((const uint16_t*)g.A + base);
+        if constexpr (AT == QMM_F16) {
+          v.x = f16_to_f32((uint16_t)(u.x & 0xffffu));
+          v.y = f16_to_f32((uint16_t)(u.x >> 16));
+          v.z = f16_to_f32((uint16_t)(u.y & 0xffffu));
+          v.w = f16_to_f32((uint16_t)(u.y >> 16));
+        } else {
+          v.x = __uint_as_float(u.x << 16);
+          v.y = __uint_as_float(u.x & 0xffff0000u);
+          v.z = __uint_as_float(u.y << 16);
+          v.w = __uint_as_float(u.y & 0xffff0000u);
+        }
+      }
+    } else {
+      v.x = (k + 0 < K) ? load_elem<AT>(g.A, base + 0) : 0.0f;
+      v.y = (k + 1 < K) ? load_elem<AT>(g.A, base + 1) : 0.0f;
+      v.z = (k + 2 < K) ? load_elem<AT>(g.A, base + 2) : 0.0f;
+      v.w = (k + 3 < K) ? load_elem<AT>(g.A, base + 3) : 0.0f;
+    }
+    *(f32x4*)(lds + (m * SC + slot) * CS + 4 * j4) = v;
+  }
+  __syncthreads();
+  // group sums, each summed in index order
+  const int gpc = WPC / G;
+  const int ng = (int)g.M * SC * gpc;
+  for (int idx = threadIdx.x; idx < ng; idx += blockDim.x) {
+    const int ms = idx / gpc;  // m * SC + slot
+    const int gi = idx - ms * gpc;
+    const float* src = lds + ms * CS + gi * G;
+    float sum = 0.0f;
+    for (int i = 0; i < G; ++i) sum += src[i];
+    lds[ms * CS + WPC + gi] = sum;
+  }
+}
+
+// Weights and scale data of one work item of one lane: R rows x one 16-byte chunk,
+// plus NS = 1 (or 4 when a chunk spans several blocks) scales and zero points per row.
+template <int R, int NS>
+struct ItemBuf {
+  uint4 w[R];
+  float s[R][NS];
+  float z[R][NS];
+};
+
+// Persistent weight-streaming kernel.  A work-group owns tiles of 4*SUBS*R rows
+// (tile = blockIdx.x, blockIdx.x + gridDim.x, ...); each lane walks the sequence
+// (tile, K-slice, chunk iteration) with the next item's weights and scales in
+// flight in a second register set (the loop is unrolled twice so the two sets
+// swap roles without copies; every fetch issues the same loads, with clamped
+// addresses past the end, so the compiler's wait counts stay exact).  A is staged
+// in LDS one K-slice of SC chunks at a time (once for all tiles when one slice
+// covers K).  ZK: 0 = zero point is a constant (none / uniform), 1 = packed codes,
+// 2 = fp16 tensor.  MULTI: a chunk spans several blocks (block < codes per chunk).
+template <int FMT, int BITS, int AT, int MT, int R, int MULTI, int ZK>
+__global__ __launch_bounds__(256) void gemv_kernel(GemvArgs g) {
+  constexpr int WPC = 128 / BITS;  // codes per 16-byte chunk
+  constexpr int WPD = 32 / BITS;   // codes per dword
+  constexpr int CS = WPC + 4;      // LDS floats per chunk slot
+  constexpr int NS = MULTI ? 4 : 1;
+  extern __shared__ float lds[];
+  const int SC = g.slice_chunks;
+  float* cb_lds = lds + MT * SC * CS;
+  if constexpr (FMT == GEMV_CODEBOOK) {
+    if (threadIdx.x < 16) cb_lds[threadIdx.x] = g.codebook[threadIdx.x];
+  }
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int lpr_log2 = g.lpr_log2;
+  const int LPR = 1 << lpr_log2;
+  const int lp = lane & (LPR - 1);
+  const int sub = lane >> lpr_log2;
+  const int SUBS = 64 >> lpr_log2;
+  const int rows_per_wave = SUBS * R;
+  const int rows_per_tile = (int)(blockDim.x >> 6) * rows_per_wave;
+  const int N = (int)g.N;
+  const int ntiles = (N + rows_per_tile - 1) / rows_per_tile;
+  const int nchunks = (int)g.nchunks;
+  const int nslices = (nchunks + SC - 1) / SC;
+  const int iters = SC >> lpr_log2;  // chunk iterations per slice
+  const int nblk = (int)g.nblk;
+  const int blog = g.block_log2;
+  const int G = g.block < WPC ? g.block : WPC;  // codes per scale group inside a chunk
+  const int GPC = WPC / G;                       // groups per chunk: 1, 2 or 4
+  const int DPG = G / WPD;                       // dwords per group: 1, 2 or 4
+  const int64_t row_bytes = g.row_bytes;
+  constexpr float FAC = (FMT == GEMV_AFFINE) ? affine_decode_factor<BITS>() : 1.0f;
+  const float zconst = g.zp_kind == QMM_ZP_UNIFORM ? g.uniform_zp : (float)(1 << (BITS - 1));
+  const int zrow_bytes = (int)g.zp_row_bytes;
+
+  int tile = blockIdx.x, s = 0, it = 0;
+  if (tile >= ntiles) return;
+
+  // loads of item (tl, chunk c) into b: always the same instructions; rows or chunks
+  // past the end read row N-1 / chunk nchunks-1 instead (results unused)
+  auto fetch = [&](int tl, int c, ItemBuf<R, NS>& b) {
+    const int cc = c < nchunks ? c : nchunks - 1;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      int row = tl * rows_per_tile + wave * rows_per_wave + r * SUBS + sub;
+      row = row < N ? row : N - 1;
+      b.w[r] = *(const uint4*)(g.W + (int64_t)row * row_bytes + cc * 16);
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        const int gi = i < GPC ? i : GPC - 1;
+        const int bidx = (cc * WPC + gi * G) >> blog;
+        const int64_t si = (int64_t)row * nblk + bidx;
+        if constexpr (FMT == GEMV_AFFINE) {
+          b.s[r][i] = f16_to_f32(g.scales[si]);
+          if constexpr (ZK == 1) {
+            const uint8_t* zr = (const uint8_t*)g.zp + (int64_t)row * zrow_bytes;
+            const int bit = bidx * BITS;
+            b.z[r][i] = (float)((zr[bit >> 3] >> (bit & 7)) & ((1u << BITS) - 1u));
+          } else if constexpr (ZK == 2) {
+            b.z[r][i] = f16_to_f32(((const uint16_t*)g.zp)[si]);
+          } else {
+            b.z[r][i] = zconst;
+          }
+        } else {
+          b.s[r][i] = g.absmax[si];
+          b.z[r][i] = 0.0f;
+        }
+      }
+    }
+  };
+
+  float acc[R][MT];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[r][m] = 0.0f;
+
+  bool staged = false;
+  bool done = false;
+  // One step: stage A if this item starts a slice, prefetch the next item into
+  // `nxt`, compute the current item from `cur`, finish the tile if it ends here.
+  auto step = [&](ItemBuf<R, NS>& cur, ItemBuf<R, NS>& nxt) {
+    int tn = tile, sn = s, itn = it + 1;
+    if (itn == iters) {
+      itn = 0;
+      if (++sn == nslices) {
+        sn = 0;
+        tn = tile + gridDim.x;
+      }
+    }
+    const bool has_next = tn < ntiles;
+    if (it == 0 && (nslices > 1 || !staged)) {
+      __syncthreads();
+      stage_a<AT, WPC, CS>(g, lds, s * SC, SC, G);
+      __syncthreads();
+      staged = true;
+    }
+    fetch(has_next ? tn : tile, has_next ? sn * SC + itn * LPR + lp : nchunks, nxt);
+
+    const int c = s * SC + it * LPR + lp;
+    if (c < nchunks) {
+      const float* abase = lds + (it * LPR + lp) * CS;
+      float P[R][MT];
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) P[r][m] = 0.0f;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        float a[MT][WPD];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          const int mm = m < g.M ? m : 0;
+          const f32x4* ap = (const f32x4*)(abase + mm * SC * CS + d * WPD);
+#pragma unroll
+          for (int i = 0; i < WPD / 4; ++i) {
+            const f32x4 v = ap[i];
+            a[m][4 * i + 0] = v.x; a[m][4 * i + 1] = v.y; a[m][4 * i + 2] = v.z; a[m][4 * i + 3] = v.w;
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const uint32_t x = d == 0 ? cur.w[r].x : d == 1 ? cur.w[r].y : d == 2 ? cur.w[r].z : cur.w[r].w;
+          float q[WPD];
+          if constexpr (FMT == GEMV_AFFINE) decode_dword_affine<BITS>(x, q);
+          else decode_dword_codebook(x, cb_lds, q);
+#pragma unroll
+          for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int i = 0; i < WPD; ++i) P[r][m] = fmaf(a[m][i], q[i], P[r][m]);
+        }
+        if (!MULTI ? d == 3 : (((d + 1) % DPG) == 0)) {
+          // scale group gi of the chunk complete
+          const int gi = MULTI ? d / DPG : 0;
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            float scv, z;
+            if constexpr (MULTI) {
+              scv = gi == 0 ? cur.s[r][0] : gi == 1 ? cur.s[r][NS > 1 ? 1 : 0]
+                  : gi == 2 ? cur.s[r][NS > 2 ? 2 : 0] : cur.s[r][NS > 3 ? 3 : 0];
+              z = gi == 0 ? cur.z[r][0] : gi == 1 ? cur.z[r][NS > 1 ? 1 : 0]
+                  : gi == 2 ? cur.z[r][NS > 2 ? 2 : 0] : cur.z[r][NS > 3 ? 3 : 0];
+            } else {
+              scv = cur.s[r][0];
+              z = cur.z[r][0];
+            }
+            if constexpr (FMT == GEMV_AFFINE) {
+#pragma unroll
+              for (int m = 0; m < MT; ++m) {
+                const int mm = m < g.M ? m : 0;
+                const float sa = abase[mm * SC * CS + WPC + gi];
+                acc[r][m] = fmaf(scv, fmaf(-z, sa, FAC * P[r][m]), acc[r][m]);
+                P[r][m] = 0.0f;
+              }
+            } else {
+#pragma unroll
+              for (int m = 0; m < MT; ++m) {
+                acc[r][m] = fmaf(scv, P[r][m], acc[r][m]);
+                P[r][m] = 0.0f;
+              }
+            }
+          }
+        }
+      }
+    }
+
+    if (s == nslices - 1 && it == iters - 1) {
+      // tile complete: fixed-order combination of the LPR lane partials of each row
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) acc[r][m] = group_sum(acc[r][m], LPR);
+      if (lp == 0) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const int row = tile * rows_per_tile + wave * rows_per_wave + r * SUBS + sub;
+          if (row >= N) continue;
+          const float bv = g.bias ? load_elem_rt(g.bias, g.c_type, row) : 0.0f;
+#pragma unroll
+          for (int m = 0; m < MT; ++m)
+            if (m < g.M) store_elem_rt(g.C, g.c_type, (int64_t)m * N + row, acc[r][m] + bv);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) acc[r][m] = 0.0f;
+    }
+    done = !has_next;
+    tile = tn;
+    s = sn;
+    it = itn;
+  };
+
+  ItemBuf<R, NS> b0, b1;
+  fetch(tile, lp, b0);
+  while (true) {
+    step(b0, b1);
+    if (done) break;
+    step(b1, b0);
+    if (done) break;
+  }
+}
+
+// ---- launch ------------------------------------------------------------------
+
+template <typename K>
+static void allow_large_lds(K kernel, size_t lds) {
+  if (lds > 64 * 1024)
+    (void)hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)kMaxGemvLds);
+}
+
+template <int FMT, int BITS, int AT, int MT, int R, int MULTI, int ZK>
+static hipError_t launch_one(const GemvArgs& g, hipStream_t st) {
+  const int subs = 64 >> g.lpr_log2;
+  const int64_t rows_per_tile = 4LL * subs * R;
+  const int64_t ntiles = (g.N + rows_per_tile - 1) / rows_per_tile;
+  int64_t grid = (int64_t)g.num_cus * g.wg_per_cu;
+  if (grid > ntiles) grid = ntiles;
+  if (grid < 1) grid = 1;
+  auto kern = gemv_kernel<FMT, BITS, AT, MT, R, MULTI, ZK>;
+  allow_large_lds(kern, g.lds_bytes);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), g.lds_bytes, st, g);
+  return hipSuccess;
+}
+
+template <int FMT, int BITS, int AT, int MULTI, int ZK>
+static hipError_t launch_mr(const GemvArgs& g, int R, hipStream_t st) {
+  switch (g.mt) {
+    case 1:
+      if (R == 1) return launch_one<FMT, BITS, AT, 1, 1, MULTI, ZK>(g, st);
+      if (R == 2) return launch_one<FMT, BITS, AT, 1, 2, MULTI, ZK>(g, st);
+      return launch_one<FMT, BITS, AT, 1, 4, MULTI, ZK>(g, st);
+    case 2:
+      if (R == 1) return launch_one<FMT, BITS, AT, 2, 1, MULTI, ZK>(g, st);
+      return launch_one<FMT, BITS, AT, 2, 2, MULTI, ZK>(g, st);
+    case 4:
+      if (R == 1) return launch_one<FMT, BITS, AT, 4, 1, MULTI, ZK>(g, st);
+      return launch_one<FMT, BITS, AT, 4, 2, MULTI, ZK>(g, st);
+    default:
+      return launch_one<FMT, BITS, AT, 8, 1, MULTI, ZK>(g, st);
+  }
+}
+
+template <int FMT, int BITS, int AT>
+hipError_t launch_at_type(const GemvArgs& g, int R, hipStream_t st) {
+  constexpr int WPC = 128 / BITS;
+  const bool multi = g.block < WPC;
+  if constexpr (FMT == GEMV_CODEBOOK) {
+    return multi ? launch_mr<FMT, BITS, AT, 1, 0>(g, R, st) : launch_mr<FMT, BITS, AT, 0, 0>(g, R, st);
+  } else {
+    const int zk = g.zp_kind == QMM_ZP_PACKED ? 1 : g.zp_kind == QMM_ZP_F16 ? 2 : 0;
+    if (multi) {
+      if (zk == 1) return launch_mr<FMT, BITS, AT, 1, 1>(g, R, st);
+      if (zk == 2) return launch_mr<FMT, BITS, AT, 1, 2>(g, R, st);
+      return launch_mr<FMT, BITS, AT, 1, 0>(g, R, st);
+    }
+    if (zk == 1) return launch_mr<FMT, BITS, AT, 0, 1>(g, R, st);
+    if (zk == 2) return launch_mr<FMT, BITS, AT, 0, 2>(g, R, st);
+    return launch_mr<FMT, BITS, AT, 0, 0>(g, R, st);
+  }
+}
+
+}  // namespace qmm

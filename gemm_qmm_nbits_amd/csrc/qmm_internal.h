@@ -1,0 +1,105 @@
+// Internal interfaces between the host runtime (qmm_api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "qmm.h"
+
+namespace qmm {
+
+enum { GEMV_AFFINE = 0, GEMV_CODEBOOK = 1 };
+
+struct GemvArgs {
+  const void* A;
+  int a_type;
+  int64_t M, K, N;
+  const uint8_t* W;
+  int64_t row_bytes;  // bytes per weight row = nblk * block * bits / 8
+  int64_t nchunks;    // row_bytes / 16 (chunked kernel)
+  int fmt;            // GEMV_AFFINE or GEMV_CODEBOOK
+  int bits;
+  int block;
+  int block_log2;
+  int64_t nblk;
+  const uint16_t* scales;  // affine: fp16 [N][nblk]
+  const float* absmax;     // codebook: fp32 [N][nblk]
+  const float* codebook;   // codebook: fp32 [16]
+  const void* zp;
+  int zp_kind;
+  float uniform_zp;
+  int64_t zp_row_bytes;
+  const void* bias;
+  void* C;
+  int c_type;
+  int lpr_log2;  // lanes per row = 1 << lpr_log2 (fixed by K, block, bits)
+  int a_vec;     // A rows allow 4-element vector loads (16-byte aligned base, K % 4 == 0)
+  int chunked;   // use the chunked kernel (row_bytes % 16 == 0 and W 16-byte aligned)
+  int mt;        // rows of A handled per kernel instance: 1, 2, 4 or 8 (>= M)
+  int slice_chunks;  // chunks of A staged in LDS per K-slice (a multiple of 1 << lpr_log2)
+  size_t lds_bytes;  // dynamic LDS of the chunked kernel
+  int num_cus;       // compute units of the device
+  int wg_per_cu;     // resident work-groups per compute unit used to size the grid
+};
+
+constexpr size_t kMaxGemvLds = 160 * 1024;   // LDS per work-group on gfx950
+constexpr size_t kGemvLdsBudget = 80 * 1024; // preferred A staging size per work-group
+
+// Fill mt, slice_chunks, lds_bytes, wg_per_cu (and clear `chunked` when no slice fits).
+void gemv_plan(GemvArgs& g, int num_cus);
+
+int gemv_lanes_per_row_log2(int64_t nchunks);
+hipError_t launch_gemv(GemvArgs g, int rows_per_lane, hipStream_t st);
+
+struct DequantArgs {
+  const uint8_t* W;
+  int fmt;
+  int bits;
+  int block;
+  int64_t N, K, nblk, row_bytes;
+  const uint16_t* scales;
+  const float* absmax;
+  const float* codebook;
+  const void* zp;
+  int zp_kind;
+  float uniform_zp;
+  int64_t zp_row_bytes;
+  void* out;
+  int out_type;
+};
+hipError_t launch_dequant(const DequantArgs& d, hipStream_t st);
+
+hipError_t launch_uniform_check(const uint16_t* zp, int64_t count, uint32_t* scratch,
+                                hipStream_t st);
+constexpr int kUniformPartials = 256;
+
+// A (fp32 / bf16) -> fp16, round to nearest even, count elements.
+hipError_t launch_cast_to_f16(const void* src, int src_type, uint16_t* dst, int64_t count,
+                              hipStream_t st);
+
+struct QmoeArgs {
+  const uint16_t* X;
+  int64_t T, H, I, E;
+  int k;
+  const int32_t* ids;
+  const float* rw;
+  qmoe_weights fc1, fc2;
+  int block;
+  int mode;
+  int64_t fc1_row_bytes, fc1_nblk, fc1_zp_row_bytes, fc1_chunks;
+  int fc1_lpr_log2;
+  int64_t fc2_row_bytes, fc2_nblk, fc2_zp_row_bytes, fc2_chunks;
+  int fc2_lpr_log2;
+  uint16_t* h;      // scratch: fp16 [T][k][I]
+  int8_t* xq_out;   // int8 mode: [T][H] codes of x (natural order)
+  float* xs_out;    // int8 mode: [T][H/32] scales of x
+  int8_t* hq_out;   // int8 mode: [T][k][I] codes of h
+  float* hs_out;    // int8 mode: [T][k][I/32] scales of h
+  uint16_t* Y;
+};
+size_t qmoe_fc1_lds_bytes(const QmoeArgs& a);
+size_t qmoe_fc2_lds_bytes(const QmoeArgs& a);
+hipError_t launch_qmoe_fc1(const QmoeArgs& a, int rows_per_lane, hipStream_t st);
+hipError_t launch_qmoe_fc2(const QmoeArgs& a, int rows_per_lane, hipStream_t st);
+
+}  // namespace qmm

@@ -1,0 +1,117 @@
+// Small kernels: bit-exact dequantization, uniform zero-point detection, A cast.
+#include "qmm_device.h"
+#include "qmm_internal.h"
+
+namespace qmm {
+
+// ---- dense dequantization --------------------------------------------------
+// out[n][k] = fp32(fp32(q - zp) * s)  (affine, [P1] "What", commit 1)
+//           = fp32(codebook[q] * absmax) (codebook, [P3] "Summary")
+// fp16 output is the round-to-nearest-even of that fp32 value.
+__global__ __launch_bounds__(256) void dequant_kernel(DequantArgs d) {
+  const int64_t total = d.N * d.K;
+  const int blob = d.block * d.bits / 8;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t n = i / d.K;
+    const int64_t k = i - n * d.K;
+    const int b = (int)(k / d.block);
+    const int j = (int)(k - (int64_t)b * d.block);
+    const uint32_t q = code_at(d.W + n * d.row_bytes + (int64_t)b * blob, j, d.bits);
+    float w;
+    if (d.fmt == GEMV_CODEBOOK) {
+      w = __fmul_rn(d.codebook[q], d.absmax[n * d.nblk + b]);
+    } else {
+      const float s = f16_to_f32(d.scales[n * d.nblk + b]);
+      const float z = zero_point(d.zp, d.zp_kind, d.uniform_zp, d.bits, n, b, d.zp_row_bytes, d.nblk);
+      w = dequant_affine(q, z, s);
+    }
+    if (d.out_type == QMM_F16) ((uint16_t*)d.out)[i] = f32_to_f16(w);
+    else ((float*)d.out)[i] = w;
+  }
+}
+
+hipError_t launch_dequant(const DequantArgs& d, hipStream_t st) {
+  const int64_t total = d.N * d.K;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(dequant_kernel, dim3((unsigned)blocks), dim3(256), 0, st, d);
+  return hipSuccess;
+}
+
+// ---- uniform zero point ([P1] "What", commit 1) ------------------------------
+// Pass 1: partial p of kUniformPartials records whether its slice holds any fp16
+// bit pattern different from zp[0].  Pass 2: one work-group folds the partials
+// and writes {is_uniform, value bits}.  No atomics; deterministic.
+__global__ __launch_bounds__(256) void uniform_partial_kernel(const uint16_t* zp, int64_t count,
+                                                              uint32_t* partial) {
+  const uint16_t first = zp[0];
+  int diff = 0;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count;
+       i += (int64_t)gridDim.x * blockDim.x)
+    diff |= (zp[i] != first);
+  diff = __syncthreads_or(diff);
+  if (threadIdx.x == 0) partial[blockIdx.x] = (uint32_t)diff;
+}
+
+__global__ __launch_bounds__(256) void uniform_final_kernel(const uint16_t* zp, const uint32_t* partial,
+                                                            uint32_t* result) {
+  int diff = 0;
+  for (int i = threadIdx.x; i < kUniformPartials; i += blockDim.x) diff |= (partial[i] != 0u);
+  diff = __syncthreads_or(diff);
+  if (threadIdx.x == 0) {
+    const uint16_t first = zp[0];
+    const bool is_nan = ((first & 0x7c00u) == 0x7c00u) && ((first & 0x03ffu) != 0u);
+    const float v = f16_to_f32(first);
+    result[0] = (!diff && !is_nan) ? 1u : 0u;
+    result[1] = __float_as_uint(v);
+  }
+}
+
+hipError_t launch_uniform_check(const uint16_t* zp, int64_t count, uint32_t* scratch,
+                                hipStream_t st) {
+  hipLaunchKernelGGL(uniform_partial_kernel, dim3(kUniformPartials), dim3(256), 0, st, zp, count,
+                     scratch + 2);
+  hipLaunchKernelGGL(uniform_final_kernel, dim3(1), dim3(256), 0, st, zp, scratch + 2, scratch);
+  return hipSuccess;
+}
+
+// ---- A cast to fp16 (prefill path; [P1] "What", commit 1: cast A once) --------
+__global__ __launch_bounds__(256) void cast_f16_kernel(const void* src, int src_type, uint16_t* dst,
+                                                       int64_t count) {
+  const int64_t n4 = count / 4;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    float v[4];
+    if (src_type == QMM_F32) {
+      const f32x4 x = ((const f32x4*)src)[i];
+      v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+    } else {
+      const uint2 x = ((const uint2*)src)[i];
+      v[0] = bf16_to_f32((uint16_t)(x.x & 0xffffu));
+      v[1] = bf16_to_f32((uint16_t)(x.x >> 16));
+      v[2] = bf16_to_f32((uint16_t)(x.y & 0xffffu));
+      v[3] = bf16_to_f32((uint16_t)(x.y >> 16));
+    }
+    uint2 o;
+    o.x = (uint32_t)f32_to_f16(v[0]) | ((uint32_t)f32_to_f16(v[1]) << 16);
+    o.y = (uint32_t)f32_to_f16(v[2]) | ((uint32_t)f32_to_f16(v[3]) << 16);
+    ((uint2*)dst)[i] = o;
+  }
+  // tail
+  const int64_t t = n4 * 4 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t < count && t >= n4 * 4) dst[t] = f32_to_f16(load_elem_rt(src, src_type, t));
+}
+
+hipError_t launch_cast_to_f16(const void* src, int src_type, uint16_t* dst, int64_t count,
+                              hipStream_t st) {
+  int64_t blocks = (count / 4 + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(cast_f16_kernel, dim3((unsigned)blocks), dim3(256), 0, st, src, src_type, dst,
+                     count);
+  return hipSuccess;
+}
+
+}  // namespace qmm

@@ -1,0 +1,276 @@
+"""Thin ctypes binding of libqmm.so (include/qmm.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI.  Tensors are torch tensors on the GPU; their
+data_ptr() and the current torch stream are passed through.  If the library is
+missing the binding raises: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, Structure, c_double, c_float, c_int, c_int64, c_size_t, c_void_p
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libqmm.so")
+
+QMM_F32, QMM_F16, QMM_BF16 = 0, 1, 2
+QMM_ZP_NONE, QMM_ZP_PACKED, QMM_ZP_F16, QMM_ZP_UNIFORM = 0, 1, 2, 3
+QMOE_FP, QMOE_INT8_ACT = 0, 1
+STATUS = {0: "QMM_OK", -1: "QMM_E_NULL", -2: "QMM_E_DTYPE", -3: "QMM_E_BITS", -4: "QMM_E_BLOCK",
+          -5: "QMM_E_SHAPE", -6: "QMM_E_ALIGN", -7: "QMM_E_WORKSPACE", -8: "QMM_E_MODE",
+          -9: "QMM_E_DEVICE"}
+ENTRY_NBITS, ENTRY_CODEBOOK, ENTRY_QMOE_FC1, ENTRY_QMOE_FC2 = 0, 1, 2, 3
+
+
+class QmmError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        name = STATUS.get(status, f"hipError {status}")
+        super().__init__(f"{fn} failed: {name} ({status})")
+
+
+class qmoe_weights(Structure):
+    _fields_ = [("W", c_void_p), ("scales", c_void_p), ("zp", c_void_p), ("bias", c_void_p)]
+
+
+_lib = None
+
+_SIGS = {
+    "qmm_nbits": (c_int, [c_void_p, c_int, c_int64, c_int64, c_int64, c_void_p, c_int, c_int,
+                          c_void_p, c_void_p, c_int, c_float, c_void_p, c_void_p, c_int,
+                          c_void_p, c_size_t, c_void_p]),
+    "qmm_nbits_workspace_bytes": (c_size_t, [c_int64, c_int64, c_int]),
+    "qmm_validate_nbits": (c_int, [c_void_p, c_int, c_int64, c_int64, c_int64, c_void_p, c_int,
+                                   c_int, c_void_p, c_void_p, c_int, c_void_p, c_void_p, c_int,
+                                   c_void_p, c_size_t]),
+    "qmm_codebook4": (c_int, [c_void_p, c_int, c_int64, c_int64, c_int64, c_void_p, c_int,
+                              c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_void_p, c_size_t,
+                              c_void_p]),
+    "qmm_codebook4_workspace_bytes": (c_size_t, [c_int64, c_int64, c_int]),
+    "qmm_validate_codebook4": (c_int, [c_void_p, c_int, c_int64, c_int64, c_int64, c_void_p, c_int,
+                                       c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_void_p,
+                                       c_size_t]),
+    "qmm_fp16_uniform_value": (c_int, [c_void_p, c_int64, c_void_p, c_size_t, POINTER(c_int),
+                                       POINTER(c_float), c_void_p]),
+    "qmm_uniform_scratch_bytes": (c_size_t, []),
+    "qmm_dequantize_nbits": (c_int, [c_void_p, c_int, c_int, c_void_p, c_void_p, c_int, c_float,
+                                     c_int64, c_int64, c_void_p, c_int, c_void_p]),
+    "qmm_dequantize_codebook4": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_int64, c_int64,
+                                         c_void_p, c_int, c_void_p]),
+    "qmoe_decode_fused": (c_int, [c_void_p, c_int64, c_int64, c_int64, c_int64, c_int, c_void_p,
+                                  c_void_p, qmoe_weights, qmoe_weights, c_int, c_int, c_int,
+                                  c_void_p, c_void_p, c_size_t, c_void_p]),
+    "qmoe_decode_scratch_bytes": (c_size_t, [c_int64, c_int64, c_int64, c_int, c_int]),
+    "qmm_validate_qmoe": (c_int, [c_void_p, c_int64, c_int64, c_int64, c_int64, c_int, c_void_p,
+                                  c_void_p, qmoe_weights, qmoe_weights, c_int, c_int, c_int,
+                                  c_void_p, c_void_p, c_size_t]),
+    "qmm_set_tuning": (c_int, [c_int, c_int]),
+    "qmm_num_candidates": (c_int, [c_int]),
+    "qmm_tuned_choice": (c_int, [c_int]),
+    "qmm_clear_tuning": (None, []),
+    "qmm_tuner_pick": (c_int, [POINTER(c_double), c_int, c_int]),
+    "qmm_status_string": (ctypes.c_char_p, [c_int]),
+}
+
+
+def lib():
+    """Load libqmm.so once (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: run __graft_entry__.build() first")
+        # torch ships its own HIP runtime with the same soname as ROCm's; importing
+        # torch first makes libqmm.so bind to that one runtime instead of a second copy
+        import torch  # noqa: F401
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name, None)
+            if fn is None:  # reported by the export test; calling it raises AttributeError
+                continue
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(fn, status):
+    if status != 0:
+        raise QmmError(fn, status)
+
+
+# ---------------------------------------------------------------------------
+# torch marshalling
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def dtype_code(t) -> int:
+    torch = _torch()
+    m = {torch.float32: QMM_F32, torch.float16: QMM_F16, torch.bfloat16: QMM_BF16}
+    if t.dtype not in m:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return m[t.dtype]
+
+
+def torch_dtype(code: int):
+    torch = _torch()
+    return {QMM_F32: torch.float32, QMM_F16: torch.float16, QMM_BF16: torch.bfloat16}[code]
+
+
+def _ptr(t):
+    return None if t is None else c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return c_void_p(s.cuda_stream)
+
+
+def _contig(t, name):
+    if t is not None and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def nblocks(K, block):
+    return (K + block - 1) // block
+
+
+def qmm_nbits(A, W, scales, K, bits, block, zp=None, zp_kind=QMM_ZP_NONE, uniform_zp=0.0,
+              bias=None, out=None, out_dtype=None, workspace=None, stream=None):
+    """C[M,N] = A[M,K] . dequant(W)^T (+ bias) through the C ABI."""
+    torch = _torch()
+    A = _contig(A, "A")
+    M = A.shape[0]
+    N = W.shape[0]
+    ctype = dtype_code(A) if out_dtype is None else dtype_code(torch.empty(0, dtype=out_dtype))
+    if out is None:
+        out = torch.empty((M, N), dtype=torch_dtype(ctype), device=A.device)
+    ws_bytes = lib().qmm_nbits_workspace_bytes(M, K, dtype_code(A))
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=A.device)
+    st = lib().qmm_nbits(_ptr(A), dtype_code(A), M, K, N, _ptr(W), bits, block, _ptr(scales),
+                         _ptr(zp), zp_kind, float(uniform_zp), _ptr(bias), _ptr(out),
+                         dtype_code(out), _ptr(workspace),
+                         0 if workspace is None else workspace.numel() * workspace.element_size(),
+                         _stream(stream))
+    _check("qmm_nbits", st)
+    return out
+
+
+def qmm_codebook4(A, W, absmax, codebook, K, block=64, bias=None, out=None, out_dtype=None,
+                  workspace=None, stream=None):
+    torch = _torch()
+    A = _contig(A, "A")
+    M = A.shape[0]
+    N = W.shape[0]
+    ctype = dtype_code(A) if out_dtype is None else dtype_code(torch.empty(0, dtype=out_dtype))
+    if out is None:
+        out = torch.empty((M, N), dtype=torch_dtype(ctype), device=A.device)
+    ws_bytes = lib().qmm_codebook4_workspace_bytes(M, K, dtype_code(A))
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=A.device)
+    st = lib().qmm_codebook4(_ptr(A), dtype_code(A), M, K, N, _ptr(W), block, _ptr(absmax),
+                             _ptr(codebook), _ptr(bias), _ptr(out), dtype_code(out),
+                             _ptr(workspace),
+                             0 if workspace is None else workspace.numel() * workspace.element_size(),
+                             _stream(stream))
+    _check("qmm_codebook4", st)
+    return out
+
+
+def qmm_fp16_uniform_value(zp, scratch=None, stream=None):
+    """(is_uniform, value) of an fp16 zero-point tensor (synchronizes the stream)."""
+    torch = _torch()
+    if scratch is None:
+        scratch = torch.empty(lib().qmm_uniform_scratch_bytes(), dtype=torch.uint8, device=zp.device)
+    flag = c_int(0)
+    val = c_float(0.0)
+    st = lib().qmm_fp16_uniform_value(_ptr(zp), zp.numel(), _ptr(scratch), scratch.numel(),
+                                      ctypes.byref(flag), ctypes.byref(val), _stream(stream))
+    _check("qmm_fp16_uniform_value", st)
+    return bool(flag.value), float(val.value)
+
+
+def qmm_dequantize_nbits(W, scales, K, bits, block, zp=None, zp_kind=QMM_ZP_NONE, uniform_zp=0.0,
+                         out_dtype=None, stream=None):
+    torch = _torch()
+    out_dtype = out_dtype or torch.float32
+    N = W.shape[0]
+    out = torch.empty((N, K), dtype=out_dtype, device=W.device)
+    st = lib().qmm_dequantize_nbits(_ptr(W), bits, block, _ptr(scales), _ptr(zp), zp_kind,
+                                    float(uniform_zp), N, K, _ptr(out), dtype_code(out),
+                                    _stream(stream))
+    _check("qmm_dequantize_nbits", st)
+    return out
+
+
+def qmm_dequantize_codebook4(W, absmax, codebook, K, block=64, out_dtype=None, stream=None):
+    torch = _torch()
+    out_dtype = out_dtype or torch.float32
+    N = W.shape[0]
+    out = torch.empty((N, K), dtype=out_dtype, device=W.device)
+    st = lib().qmm_dequantize_codebook4(_ptr(W), block, _ptr(absmax), _ptr(codebook), N, K,
+                                        _ptr(out), dtype_code(out), _stream(stream))
+    _check("qmm_dequantize_codebook4", st)
+    return out
+
+
+def _qw(d):
+    if d is None:
+        return qmoe_weights(None, None, None, None)
+    return qmoe_weights(d["W"].data_ptr(), d["scales"].data_ptr(),
+                        None if d.get("zp") is None else d["zp"].data_ptr(),
+                        None if d.get("bias") is None else d["bias"].data_ptr())
+
+
+def qmoe_decode_scratch_bytes(T, H, I, k, mode=QMOE_FP):
+    return lib().qmoe_decode_scratch_bytes(T, H, I, k, mode)
+
+
+def qmoe_decode_fused(X, expert_ids, expert_w, fc1, fc2, H, I, E, block, mode=QMOE_FP, bits=4,
+                      out=None, scratch=None, stream=None):
+    """Y[T,H] fp16 = top-k MoE decode (fc1 -> SwiGLU -> fc2) through the C ABI.
+
+    fc1 / fc2: dicts of device tensors {"W", "scales", "zp" (or None), "bias" (or None)}.
+    """
+    torch = _torch()
+    X = _contig(X, "X")
+    T = X.shape[0]
+    k = expert_ids.shape[1]
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.float16, device=X.device)
+    sb = lib().qmoe_decode_scratch_bytes(T, H, I, k, mode)
+    if scratch is None:
+        scratch = torch.empty(max(sb, 1), dtype=torch.uint8, device=X.device)
+    st = lib().qmoe_decode_fused(_ptr(X), T, H, I, E, k, _ptr(expert_ids), _ptr(expert_w), _qw(fc1),
+                                 _qw(fc2), bits, block, mode, _ptr(out), _ptr(scratch),
+                                 scratch.numel() * scratch.element_size(), _stream(stream))
+    _check("qmoe_decode_fused", st)
+    return out
+
+
+def set_tuning(mode: int, forced_index: int = 0):
+    _check("qmm_set_tuning", lib().qmm_set_tuning(mode, forced_index))
+
+
+def num_candidates(entry: int) -> int:
+    return lib().qmm_num_candidates(entry)
+
+
+def tuned_choice(entry: int) -> int:
+    return lib().qmm_tuned_choice(entry)
+
+
+def clear_tuning():
+    lib().qmm_clear_tuning()
+
+
+def tuner_pick(times_us, rounds, ncand):
+    arr = (c_double * len(times_us))(*times_us)
+    return lib().qmm_tuner_pick(arr, rounds, ncand)

@@ -1,0 +1,241 @@
+/*
+ * qmm.h -- C ABI of the fused low-bit dequantize-matmul library for MI355X (gfx950).
+ *
+ * The operations follow three public pages:
+ *   [P1] hip-ep pull request 1318, "bits=2 MatMulNBits" (2-bit phi4-14B): sections
+ *        "Why" and "What", commit 1 -- MatMulNBits with per-block fp16 scales and
+ *        a zero point that is a tensor or, when all equal, a scalar; a GEMV that
+ *        reads fp32 A and writes fp32 C; prefill tiles that cast A to fp16 once.
+ *   [P2] hip-ep pull request 1328, "fused QMoE decode picks tiling up front":
+ *        sections "Summary", "Why", "What", "Notes for reviewers" -- the top-k MoE
+ *        decode fc1 -> SwiGLU -> fc2 with an int8-activation variant, tiling chosen
+ *        before the first call computes, HIP error state cleared on entry,
+ *        num_experts argument, scratch-only timing, capture fallback.
+ *   [P3] bitsandbytes pull request 1979, "[ROCm] Fused 4-bit SIMT GEMM":
+ *        sections "Summary" and "Technical details" -- 16-entry codebook (NF4/FP4)
+ *        4-bit weights with per-block absmax, decoded inside the GEMM; A must be
+ *        contiguous row-major.
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *     keeps no reference to them after the call returns.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Compute entry points only enqueue work on it and return without waiting,
+ *     except the first call of a new shape, which times tiling candidates first
+ *     (synchronizing the stream; never while the stream is being captured).
+ *   - On entry the sticky HIP error state is cleared (hipGetLastError), so an
+ *     error left by unrelated earlier work is not reported as this call's.
+ *   - Return value (qmm_status): 0 on success; a negative QMM_E_* code if the
+ *     arguments were refused before anything was launched; a positive value is
+ *     the hipError_t reported after the launches.
+ *   - Matrices are dense and row-major: A[M][K] (row stride K), C[M][N].
+ *   - Packed weights: W[N][nblk][block*bits/8] bytes, nblk = ceil(K/block).
+ *     Element k of row n lives in block b = k/block at position j = k%block, as
+ *     the `bits`-wide field starting at bit (j*bits)%8 of byte (j*bits)/8 of that
+ *     block (least significant field first). Codes past K in the last block are
+ *     padding and are never read.
+ *   - Dequantized weight (affine): w = fp32(fp32(q - zp) * fp32(scale)).
+ *     Dequantized weight (codebook): w = fp32(codebook[q] * absmax).
+ *   - Outputs are accumulated in fp32 and rounded once to the output dtype.
+ *     Repeated calls with the same inputs give bit-identical outputs; the
+ *     summation order depends only on (M-path, K, block, bits), never on the
+ *     tiling chosen by the tuner.
+ */
+#ifndef QMM_H
+#define QMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int qmm_status;
+
+/* element types */
+enum { QMM_F32 = 0, QMM_F16 = 1, QMM_BF16 = 2 };
+
+/* zero-point kinds ([P1] "What", commit 1) */
+enum {
+  QMM_ZP_NONE = 0,     /* zp = 2^(bits-1) for every block                             */
+  QMM_ZP_PACKED = 1,   /* uint8 [N][ceil(nblk*bits/8)]: unsigned codes, same field order as W */
+  QMM_ZP_F16 = 2,      /* fp16 [N][nblk]                                              */
+  QMM_ZP_UNIFORM = 3   /* the scalar `uniform_zp`; the zp pointer is never read       */
+};
+
+/* MoE decode modes ([P2] "Summary": fp decode and its dp4a variant) */
+enum { QMOE_FP = 0, QMOE_INT8_ACT = 1 };
+
+/* refusal codes (negative): nothing was launched */
+enum {
+  QMM_OK = 0,
+  QMM_E_NULL = -1,       /* a required pointer is NULL                                  */
+  QMM_E_DTYPE = -2,      /* unsupported element type                                    */
+  QMM_E_BITS = -3,       /* bits not in {2, 4} (MoE: 4)                                 */
+  QMM_E_BLOCK = -4,      /* block not a power of two in [16, 256] (int8 MoE: >= 32)     */
+  QMM_E_SHAPE = -5,      /* a size is negative or out of range                          */
+  QMM_E_ALIGN = -6,      /* a pointer is not aligned as the kernels require             */
+  QMM_E_WORKSPACE = -7,  /* workspace/scratch missing or smaller than the query says    */
+  QMM_E_MODE = -8,       /* unknown zero-point kind or MoE mode                         */
+  QMM_E_DEVICE = -9      /* no usable gfx950 device / library not initialised           */
+};
+
+/* ---------------------------------------------------------------------------
+ * qmm_nbits -- C[M][N] = A[M][K] . dequant(W)^T (+ bias)       ([P1] "What", commit 1)
+ *
+ *   A        [M][K] of a_type (QMM_F32, QMM_F16, QMM_BF16), contiguous, 16-byte aligned.
+ *   W        packed codes, bits in {2, 4}, block in {16, 32, 64, 128, 256}.
+ *   scales   fp16 [N][nblk].
+ *   zp       per zp_kind (see above); uniform_zp used only for QMM_ZP_UNIFORM.
+ *   bias     [N] of c_type, or NULL.
+ *   C        [M][N] of c_type.
+ *   workspace, workspace_bytes: device scratch of at least
+ *            qmm_nbits_workspace_bytes(M, K, a_type) bytes (may be NULL when that is 0).
+ * Paths: M <= 8 runs the weight-streaming GEMV, which reads A in its own type
+ * and accumulates in fp32.  M > 8 runs the prefill path: A is rounded to fp16
+ * once into the workspace (skipped when A is already fp16), W tiles are
+ * dequantized to fp16 and multiplied on the fp16 matrix cores with fp32
+ * accumulation.
+ * ------------------------------------------------------------------------- */
+qmm_status qmm_nbits(const void* A, int a_type, int64_t M, int64_t K, int64_t N,
+                     const uint8_t* W, int bits, int block, const uint16_t* scales,
+                     const void* zp, int zp_kind, float uniform_zp, const void* bias,
+                     void* C, int c_type, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+size_t qmm_nbits_workspace_bytes(int64_t M, int64_t K, int a_type);
+
+/* Host-only check of qmm_nbits arguments: returns the status qmm_nbits would
+ * refuse with (or QMM_OK).  Never dereferences a pointer, needs no GPU. */
+qmm_status qmm_validate_nbits(const void* A, int a_type, int64_t M, int64_t K, int64_t N,
+                              const uint8_t* W, int bits, int block, const uint16_t* scales,
+                              const void* zp, int zp_kind, const void* bias, const void* C,
+                              int c_type, const void* workspace, size_t workspace_bytes);
+
+/* ---------------------------------------------------------------------------
+ * qmm_codebook4 -- C[M][N] = A . (codebook[q] * absmax)^T (+ bias)
+ *                                     ([P3] "Summary", "Technical details")
+ *   A        [M][K] of a_type (QMM_F16 or QMM_BF16; QMM_F32 also accepted).
+ *   W        packed 4-bit codes [N][nblk][block/2], block in {16..256}, power of two.
+ *   absmax   fp32 [N][nblk].
+ *   codebook fp32 [16] (any values; NF4/FP4 tables are sorted in [-1, 1]).
+ *   bias     [N] of c_type, or NULL.   C [M][N] of c_type.
+ * Paths: M <= 8 weight-streaming GEMV (fp32 FMA, codebook staged in LDS);
+ * larger M uses the matrix cores with weights rounded to fp16.
+ * ------------------------------------------------------------------------- */
+qmm_status qmm_codebook4(const void* A, int a_type, int64_t M, int64_t K, int64_t N,
+                         const uint8_t* W, int block, const float* absmax,
+                         const float* codebook, const void* bias, void* C, int c_type,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+size_t qmm_codebook4_workspace_bytes(int64_t M, int64_t K, int a_type);
+
+qmm_status qmm_validate_codebook4(const void* A, int a_type, int64_t M, int64_t K, int64_t N,
+                                  const uint8_t* W, int block, const float* absmax,
+                                  const float* codebook, const void* bias, const void* C,
+                                  int c_type, const void* workspace, size_t workspace_bytes);
+
+/* ---------------------------------------------------------------------------
+ * qmm_fp16_uniform_value -- is every fp16 zero point bitwise equal?
+ *                                     ([P1] "What", commit 1: detected once per buffer)
+ *   zp       fp16 [count] (device).
+ *   scratch  device buffer of at least qmm_uniform_scratch_bytes() bytes.
+ *   is_uniform, value: HOST pointers receiving the flag and the fp32 value.
+ * A NaN first element is never uniform; count == 0 is not uniform.
+ * Synchronizes `stream` (call once per weight buffer, not per matmul).
+ * ------------------------------------------------------------------------- */
+qmm_status qmm_fp16_uniform_value(const uint16_t* zp, int64_t count, void* scratch,
+                                  size_t scratch_bytes, int* is_uniform, float* value,
+                                  void* stream);
+size_t qmm_uniform_scratch_bytes(void);
+
+/* ---------------------------------------------------------------------------
+ * Dequantize to a dense matrix out[N][K] (out_type QMM_F32 or QMM_F16).
+ * Bit-exact with the definitions above (fp16 output is the RNE rounding of the
+ * fp32 weight, i.e. the operand the matrix-core paths use).
+ * ------------------------------------------------------------------------- */
+qmm_status qmm_dequantize_nbits(const uint8_t* W, int bits, int block, const uint16_t* scales,
+                                const void* zp, int zp_kind, float uniform_zp, int64_t N,
+                                int64_t K, void* out, int out_type, void* stream);
+
+qmm_status qmm_dequantize_codebook4(const uint8_t* W, int block, const float* absmax,
+                                    const float* codebook, int64_t N, int64_t K, void* out,
+                                    int out_type, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * qmoe_decode_fused -- top-k MoE decode with u4 expert weights.
+ *                                     ([P2] "Summary", "Why", "What")
+ * For token t in [0,T) and slot j in [0,k) with expert e = expert_ids[t][j]:
+ *   [g ; u] = W1_e . x'_t + b1_e     (fc1: 2I outputs, g = rows [0,I), u = rows [I,2I))
+ *   h       = fp16(g * sigmoid(g) * u)
+ *   z       = W2_e . h' + b2_e       (fc2: H outputs)
+ *   Y[t]    = fp16( sum over j = 0..k-1 in order of expert_w[t][j] * z )
+ * QMOE_FP: x' = x, h' = h.  QMOE_INT8_ACT: x' and h' are symmetric int8 per 32
+ * consecutive values (scale fp32(amax/127), codes rint(fp32(v*fp32(127/amax))))
+ * and the products with (q - zp) are summed exactly in int32 per 32 values.
+ *
+ *   X          fp16 [T][H]            Y fp16 [T][H]
+ *   expert_ids int32 [T][k], each in [0, E)  (precondition, not checked on device)
+ *   expert_w   fp32 [T][k]
+ *   fc1.W      uint8 [E][2I][nblk(H)][block/2]   fc1.scales fp16 [E][2I][nblk(H)]
+ *   fc1.zp     uint8 [E][2I][ceil(nblk(H)/2)] packed u4, or NULL (zp = 8)
+ *   fc1.bias   fp16 [E][2I] or NULL
+ *   fc2.*      the same with [E][H][..] over K = I
+ *   bits       4.  block in {32, 64, 128, 256} (int8 mode additionally needs
+ *              H % 32 == 0 and I % 32 == 0).
+ *   scratch    device buffer of at least qmoe_decode_scratch_bytes(T, H, I, k, mode).
+ *              Layout: fp16 h [T][k][I] at offset 0; in int8 mode followed (at the
+ *              next 256-byte boundary) by int8 x codes [T][H], fp32 x scales
+ *              [T][H/32], int8 h codes [T][k][I], fp32 h scales [T][k][I/32].
+ *   E          num_experts: the first call of a shape times tiling candidates on
+ *              other expert sets, writing only scratch.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  const uint8_t* W;
+  const uint16_t* scales;
+  const uint8_t* zp;    /* packed u4 or NULL */
+  const uint16_t* bias; /* fp16 or NULL */
+} qmoe_weights;
+
+qmm_status qmoe_decode_fused(const uint16_t* X, int64_t T, int64_t H, int64_t I, int64_t E,
+                             int k, const int32_t* expert_ids, const float* expert_w,
+                             qmoe_weights fc1, qmoe_weights fc2, int bits, int block,
+                             int mode, uint16_t* Y, void* scratch, size_t scratch_bytes,
+                             void* stream);
+
+size_t qmoe_decode_scratch_bytes(int64_t T, int64_t H, int64_t I, int k, int mode);
+
+qmm_status qmm_validate_qmoe(const uint16_t* X, int64_t T, int64_t H, int64_t I, int64_t E,
+                             int k, const int32_t* expert_ids, const float* expert_w,
+                             qmoe_weights fc1, qmoe_weights fc2, int bits, int block, int mode,
+                             const uint16_t* Y, const void* scratch, size_t scratch_bytes);
+
+/* ---------------------------------------------------------------------------
+ * Tuning control and introspection.
+ * qmm_tuning_mode: 0 = time candidates on the first call of a shape (default),
+ *   1 = never time, always use the default tiling, 2 = force candidate
+ *   `forced_index` (for tests: every candidate must give identical bits).
+ * qmm_tuned_choice: the candidate index chosen for the last call of the given
+ *   entry (0 = qmm_nbits GEMV, 1 = qmm_codebook4 GEMV, 2 = qmoe fc1, 3 = qmoe fc2),
+ *   or -1 if none; qmm_num_candidates gives the candidate count per entry.
+ * qmm_clear_tuning forgets every cached choice.
+ * ------------------------------------------------------------------------- */
+qmm_status qmm_set_tuning(int mode, int forced_index);
+int qmm_num_candidates(int entry);
+int qmm_tuned_choice(int entry);
+void qmm_clear_tuning(void);
+
+/* The selection rule of the up-front timing, exposed for host-only checks:
+ * times_us[r * ncand + c] is round r of candidate c; round 0 is discarded, the
+ * least total over rounds 1..rounds-1 wins, ties go to the lower index.
+ * Returns -1 for bad arguments. */
+int qmm_tuner_pick(const double* times_us, int rounds, int ncand);
+
+/* Human-readable name of a status code (static storage). */
+const char* qmm_status_string(qmm_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QMM_H */

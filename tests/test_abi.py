@@ -1,0 +1,151 @@
+"""CPU tests of the C ABI: the library loads, exports every declared symbol, and the
+host-only argument checks and tuner selection rule behave as documented."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gemm_qmm_nbits_amd import qmm as Q
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "qmm.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert "qmm_nbits" in names and "qmoe_decode_fused" in names and "qmm_codebook4" in names
+    L = Q.lib()
+    missing = [n for n in names if not hasattr(L, n)]
+    assert not missing, f"declared in include/qmm.h but not exported: {missing}"
+
+
+def test_status_strings():
+    L = Q.lib()
+    for code in range(-9, 1):
+        assert L.qmm_status_string(code)
+
+
+FAKE = 0x1000  # an aligned non-null address, never dereferenced by the validators
+
+
+def _v_nbits(**kw):
+    a = dict(A=FAKE, a_type=Q.QMM_F32, M=1, K=256, N=128, W=FAKE, bits=4, block=64, scales=FAKE,
+             zp=FAKE, zp_kind=Q.QMM_ZP_PACKED, bias=None, C=FAKE, c_type=Q.QMM_F32, ws=None, wsb=0)
+    a.update(kw)
+    return Q.lib().qmm_validate_nbits(a["A"], a["a_type"], a["M"], a["K"], a["N"], a["W"], a["bits"],
+                                      a["block"], a["scales"], a["zp"], a["zp_kind"], a["bias"],
+                                      a["C"], a["c_type"], a["ws"], a["wsb"])
+
+
+def test_validate_nbits_codes():
+    assert _v_nbits() == 0
+    assert _v_nbits(bits=3) == -3
+    assert _v_nbits(bits=8) == -3
+    for b in (8, 48, 96, 512, 0, -64):
+        assert _v_nbits(block=b) == -4, b
+    for b in (16, 32, 64, 128, 256):
+        assert _v_nbits(block=b) == 0
+    assert _v_nbits(a_type=7) == -2
+    assert _v_nbits(c_type=-1) == -2
+    assert _v_nbits(M=-1) == -5
+    assert _v_nbits(zp_kind=9) == -8
+    assert _v_nbits(zp=None) == -1
+    assert _v_nbits(zp=None, zp_kind=Q.QMM_ZP_UNIFORM) == 0
+    assert _v_nbits(zp=None, zp_kind=Q.QMM_ZP_NONE) == 0
+    assert _v_nbits(W=None) == -1
+    assert _v_nbits(C=None) == -1
+    assert _v_nbits(A=FAKE + 2) == -6           # fp32 A must be 4-byte aligned
+    assert _v_nbits(A=FAKE + 2, a_type=Q.QMM_F16) == 0
+    assert _v_nbits(M=0, A=None, W=None, C=None) == 0   # empty problem: nothing to do
+    # the prefill path needs its workspace
+    need = Q.lib().qmm_nbits_workspace_bytes(2048, 5120, Q.QMM_F32)
+    if need:
+        assert _v_nbits(M=2048, K=5120) == -7
+        assert _v_nbits(M=2048, K=5120, ws=FAKE, wsb=need - 1) == -7
+        assert _v_nbits(M=2048, K=5120, ws=FAKE, wsb=need) == 0
+
+
+def _v_cb(**kw):
+    a = dict(A=FAKE, a_type=Q.QMM_BF16, M=1, K=4096, N=1024, W=FAKE, block=64, absmax=FAKE,
+             cb=FAKE, bias=None, C=FAKE, c_type=Q.QMM_BF16, ws=None, wsb=0)
+    a.update(kw)
+    return Q.lib().qmm_validate_codebook4(a["A"], a["a_type"], a["M"], a["K"], a["N"], a["W"],
+                                          a["block"], a["absmax"], a["cb"], a["bias"], a["C"],
+                                          a["c_type"], a["ws"], a["wsb"])
+
+
+def test_validate_codebook_codes():
+    assert _v_cb() == 0
+    assert _v_cb(block=24) == -4
+    assert _v_cb(cb=None) == -1
+    assert _v_cb(absmax=FAKE + 2) == -6
+    assert _v_cb(a_type=5) == -2
+    assert _v_cb(N=-3) == -5
+
+
+def _v_moe(**kw):
+    a = dict(X=FAKE, T=1, H=2880, I=2880, E=32, k=4, ids=FAKE, w=FAKE, bits=4, block=64,
+             mode=Q.QMOE_FP, Y=FAKE, scratch=FAKE, sb=None)
+    a.update(kw)
+    if a["sb"] is None:
+        a["sb"] = Q.lib().qmoe_decode_scratch_bytes(a["T"], a["H"], a["I"], a["k"], a["mode"])
+    fc = Q.qmoe_weights(FAKE, FAKE, None, None)
+    fc1 = kw.get("fc1", fc)
+    return Q.lib().qmm_validate_qmoe(a["X"], a["T"], a["H"], a["I"], a["E"], a["k"], a["ids"],
+                                     a["w"], fc1, fc, a["bits"], a["block"], a["mode"], a["Y"],
+                                     a["scratch"], a["sb"])
+
+
+def test_validate_qmoe_codes():
+    assert _v_moe() == 0
+    assert _v_moe(bits=2) == -3
+    assert _v_moe(block=16) == -4              # the decode needs block >= 32
+    assert _v_moe(block=48) == -4
+    assert _v_moe(mode=3) == -8
+    assert _v_moe(k=0) == -5
+    assert _v_moe(k=33) == -5                  # k <= num_experts
+    assert _v_moe(E=0) == -5
+    assert _v_moe(T=-1) == -5
+    assert _v_moe(ids=None) == -1
+    assert _v_moe(fc1=Q.qmoe_weights(None, FAKE, None, None)) == -1
+    assert _v_moe(sb=16) == -7
+    assert _v_moe(mode=Q.QMOE_INT8_ACT, H=2880, I=2880, block=32) == 0
+    assert _v_moe(mode=Q.QMOE_INT8_ACT, H=2890, I=2880, block=32) == -5   # H % 32 != 0
+    assert _v_moe(scratch=None) == -7
+
+
+def test_tuner_selection_rule():
+    # 3 rounds x 3 candidates; round 0 is discarded (cold start outlier for candidate 0)
+    t = [100.0, 5.0, 6.0,
+         1.0, 5.0, 6.0,
+         1.0, 5.0, 6.0]
+    assert Q.tuner_pick(t, 3, 3) == 0
+    # ties go to the lower index
+    t = [9.0, 9.0, 9.0,
+         4.0, 3.0, 3.0,
+         4.0, 3.0, 3.0]
+    assert Q.tuner_pick(t, 3, 3) == 1
+    # the total decides, not one fast round
+    t = [0, 0, 0,
+         1.0, 0.1, 2.0,
+         1.0, 5.0, 2.0]
+    assert Q.tuner_pick(t, 3, 3) == 0
+    assert Q.tuner_pick([1.0], 1, 1) == -1
+
+
+def test_scratch_queries():
+    L = Q.lib()
+    assert L.qmm_uniform_scratch_bytes() >= 8
+    fp = L.qmoe_decode_scratch_bytes(1, 2880, 2880, 4, Q.QMOE_FP)
+    i8 = L.qmoe_decode_scratch_bytes(1, 2880, 2880, 4, Q.QMOE_INT8_ACT)
+    assert fp >= 4 * 2880 * 2
+    assert i8 > fp
+    assert L.qmoe_decode_scratch_bytes(8, 2048, 768, 8, Q.QMOE_FP) >= 8 * 8 * 768 * 2

@@ -1,0 +1,85 @@
+"""GPU parity of qmm_codebook4 / qmm_dequantize_codebook4 against the oracle."""
+import numpy as np
+import pytest
+
+from gemm_qmm_nbits_amd import inputs as gen
+from gemm_qmm_nbits_amd import qmm as Q
+from oracle import qmm_oracle as O
+
+from gpu_util import TOL, dev, dev_act, host_bits, host_f64, sample_rows, say, torch
+
+pytestmark = pytest.mark.gpu
+
+
+class CbDev:
+    def __init__(self, p):
+        t = torch()
+        self.p = p
+        self.A = dev_act(p["A"], p["a_dtype"])
+        self.W = dev(p["W"])
+        self.absmax = dev(p["absmax"])
+        self.cb = dev(p["codebook"])
+        td = {"f32": t.float32, "f16": t.float16, "bf16": t.bfloat16}[p["a_dtype"]]
+        self.bias = (t.from_numpy(np.asarray(p["bias"], dtype=np.uint16).view(np.int16)).cuda().view(td)
+                     if p["bias"] is not None else None)
+
+    def run(self, out=None):
+        p = self.p
+        return Q.qmm_codebook4(self.A, self.W, self.absmax, self.cb, p["K"], p["block"], self.bias,
+                               out=out)
+
+    def oracle(self, rows=None, w_round=None):
+        p = self.p
+        return O.qmm_codebook4(p["A"], p["a_dtype"], p["W"], p["K"], p["block"], p["absmax"],
+                               p["codebook"], bias=p["bias"], rows=rows, w_round=w_round)
+
+
+@pytest.mark.parametrize("out", ["f32", "f16"])
+@pytest.mark.parametrize("K,block", [(4096, 64), (1536, 64), (200, 32), (300, 256)])
+def test_dequant_codebook_bit_exact(K, block, out):
+    t = torch()
+    p = gen.codebook_problem(1, K, 77, seed=K + block, block=block)
+    d = CbDev(p)
+    got = Q.qmm_dequantize_codebook4(d.W, d.absmax, d.cb, K, block,
+                                     out_dtype=t.float32 if out == "f32" else t.float16)
+    w = O.dequant_codebook4(p["W"], K, block, p["absmax"], p["codebook"])
+    if out == "f32":
+        assert np.array_equal(host_bits(got).view(np.uint32), w.view(np.uint32))
+    else:
+        assert np.array_equal(host_bits(got).view(np.uint16), O.to_f16(w).view(np.uint16))
+
+
+@pytest.mark.parametrize("a_dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("M", gen.CODEBOOK_M)
+@pytest.mark.parametrize("name", list(gen.CODEBOOK_SHAPES))
+def test_codebook_config_shapes(name, M, a_dtype):
+    """16-entry codebook skinny GEMM at the four shapes, M in {1, 4, 16, 64}, bf16/fp16."""
+    K, N = gen.CODEBOOK_SHAPES[name]
+    say(f"codebook {name} K={K} N={N} M={M} {a_dtype}")
+    idx = list(gen.CODEBOOK_SHAPES).index(name)
+    p = gen.codebook_problem(M, K, N, seed=gen.config_seed(2, 10 * idx + M), a_dtype=a_dtype)
+    d = CbDev(p)
+    y = d.run()
+    rows = sample_rows(N, 2048, seed=N + M)
+    ref = d.oracle(rows=rows)
+    err = O.rel_l2(host_f64(y)[:, rows], ref)
+    say(f"  relL2={err:.3e}")
+    assert err <= TOL[a_dtype], err
+
+
+@pytest.mark.parametrize("M", [1, 3, 8])
+def test_codebook_ragged_bias(M):
+    p = gen.codebook_problem(M, 1000, 300, seed=55 + M, a_dtype="bf16", block=32, bias=True)
+    d = CbDev(p)
+    err = O.rel_l2(host_f64(d.run()), d.oracle())
+    assert err <= TOL["bf16"], err
+
+
+def test_codebook_repeat_bit_identical():
+    p = gen.codebook_problem(4, 4096, 4096, seed=56, a_dtype="f16")
+    d = CbDev(p)
+    first = host_bits(d.run()).copy()
+    out = torch().empty_like(d.run())
+    for i in range(128):
+        d.run(out=out)
+        assert np.array_equal(host_bits(out), first), i

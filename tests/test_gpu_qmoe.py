@@ -1,0 +1,167 @@
+"""GPU parity of the fused MoE decode (qmoe_decode_fused) against the oracle."""
+import numpy as np
+import pytest
+
+from gemm_qmm_nbits_amd import inputs as gen
+from gemm_qmm_nbits_amd import qmm as Q
+from oracle import qmm_oracle as O
+
+from gpu_util import TOL, dev, host_bits, host_f64, say, torch
+
+pytestmark = pytest.mark.gpu
+
+
+class MoeDev:
+    def __init__(self, p):
+        t = torch()
+        self.p = p
+        self.X = dev(p["X"]).view(t.float16)
+        self.ids = dev(p["ids"])
+        self.rw = dev(p["rw"])
+        self.fc = {}
+        for name in ("fc1", "fc2"):
+            d = p[name]
+            self.fc[name] = {"W": dev(d["W"]), "scales": dev(d["scales"]),
+                             "zp": dev(d["zp"]) if d["zp"] is not None else None,
+                             "bias": dev(d["bias"]) if d["bias"] is not None else None}
+
+    def run(self, mode, X=None, ids=None, rw=None, out=None, scratch=None):
+        p = self.p
+        return Q.qmoe_decode_fused(self.X if X is None else X, self.ids if ids is None else ids,
+                                   self.rw if rw is None else rw, self.fc["fc1"], self.fc["fc2"],
+                                   p["H"], p["I"], p["E"], p["block"], mode=mode, out=out,
+                                   scratch=scratch)
+
+    def oracle(self, mode):
+        p = self.p
+        return O.qmoe_decode(p["X"], p["ids"], p["rw"], p["fc1"], p["fc2"], p["H"], p["I"],
+                             p["block"], mode="int8" if mode == Q.QMOE_INT8_ACT else "fp")
+
+
+def _check(d, mode, label):
+    y = d.run(mode)
+    ref = d.oracle(mode)
+    err = O.rel_l2(host_f64(y), ref)
+    say(f"  {label} relL2={err:.3e}")
+    assert err <= TOL["f16"], (label, err)
+    return y
+
+
+MODES = [Q.QMOE_FP, Q.QMOE_INT8_ACT]
+
+
+@pytest.mark.parametrize("mode", MODES, ids=["fp", "int8"])
+@pytest.mark.parametrize("block", [32, 64, 128])
+@pytest.mark.parametrize("zp,bias", [(False, False), (True, False), (False, True), (True, True)])
+def test_gpt_oss_shape(mode, block, zp, bias):
+    """GPT-OSS-20B-shaped layer: 32 experts, top-4, hidden = intermediate = 2880, one token."""
+    c = gen.QMOE_GPT_OSS
+    say(f"qmoe gpt-oss mode={mode} block={block} zp={zp} bias={bias}")
+    p = gen.qmoe_problem(1, c["H"], c["I"], c["E"], c["k"], block,
+                         seed=gen.config_seed(3, block + 2 * zp + bias), zp=zp, bias=bias)
+    _check(MoeDev(p), mode, f"B={block} zp={zp} bias={bias}")
+
+
+@pytest.mark.parametrize("mode", MODES, ids=["fp", "int8"])
+@pytest.mark.parametrize("T", [1, 4, 8])
+def test_128_experts_top8(mode, T):
+    """128 experts, top-8, hidden 2048, intermediate 768, block 64, zero points, T tokens."""
+    c = gen.QMOE_128
+    say(f"qmoe 128/8 mode={mode} T={T}")
+    p = gen.qmoe_problem(T, c["H"], c["I"], c["E"], c["k"], c["block"],
+                         seed=gen.config_seed(4, T), zp=True, bias=False)
+    _check(MoeDev(p), mode, f"T={T}")
+
+
+@pytest.mark.parametrize("mode", MODES, ids=["fp", "int8"])
+def test_batched_equals_single_calls(mode):
+    """T tokens in one call give the bits of T separate single-token calls."""
+    t = torch()
+    p = gen.qmoe_problem(4, 1024, 512, 16, 4, 64, seed=901, zp=True, bias=True)
+    d = MoeDev(p)
+    yb = host_bits(d.run(mode)).copy()
+    for i in range(4):
+        yi = d.run(mode, X=d.X[i:i + 1].contiguous(), ids=d.ids[i:i + 1].contiguous(),
+                   rw=d.rw[i:i + 1].contiguous())
+        assert np.array_equal(host_bits(yi)[0], yb[i]), i
+    t.cuda.synchronize()
+
+
+def test_repeat_calls_bit_identical_int8():
+    """129 calls of the int8-activation decode on one input give identical bits
+    (a shape no other test uses, so the first call also runs the up-front timing)."""
+    p = gen.qmoe_problem(1, 1408, 704, 24, 6, 32, seed=902, zp=True, bias=True)
+    d = MoeDev(p)
+    first = host_bits(d.run(Q.QMOE_INT8_ACT)).copy()
+    out = torch().empty_like(d.X[:, :1408])
+    for i in range(128):
+        d.run(Q.QMOE_INT8_ACT, out=out)
+        assert np.array_equal(host_bits(out), first), i
+    assert O.rel_l2(first.view(np.float16).astype(np.float64), d.oracle(Q.QMOE_INT8_ACT)) <= TOL["f16"]
+
+
+@pytest.mark.parametrize("mode", MODES, ids=["fp", "int8"])
+def test_every_tiling_candidate_same_bits(mode):
+    p = gen.qmoe_problem(2, 2880, 2880, 32, 4, 64, seed=903, zp=True, bias=True)
+    d = MoeDev(p)
+    n1 = Q.num_candidates(Q.ENTRY_QMOE_FC1)
+    n2 = Q.num_candidates(Q.ENTRY_QMOE_FC2)
+    outs = []
+    try:
+        for c in range(n1 * n2):
+            Q.set_tuning(2, c)
+            outs.append(host_bits(d.run(mode)).copy())
+    finally:
+        Q.set_tuning(0, 0)
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+
+
+def test_int8_activation_codes_bit_exact():
+    """The int8 codes and scales of x and h the kernels use (kept in scratch) equal the
+    oracle quantizer applied to x and to the kernels' own fp16 h."""
+    t = torch()
+    p = gen.qmoe_problem(2, 2048, 768, 16, 4, 64, seed=904, zp=True)
+    d = MoeDev(p)
+    T, H, I, k = 2, 2048, 768, 4
+    nbytes = Q.qmoe_decode_scratch_bytes(T, H, I, k, Q.QMOE_INT8_ACT)
+    scratch = t.zeros(nbytes, dtype=t.uint8, device="cuda")
+    d.run(Q.QMOE_INT8_ACT, scratch=scratch)
+    t.cuda.synchronize()
+    raw = scratch.cpu().numpy()
+
+    def a256(x):
+        return (x + 255) // 256 * 256
+    off_h = 0
+    off_xq = a256(T * k * I * 2)
+    off_xs = off_xq + a256(T * H)
+    off_hq = off_xs + a256(T * (H // 32) * 4)
+    off_hs = off_hq + a256(T * k * I)
+    h = raw[off_h:off_h + T * k * I * 2].view(np.uint16).reshape(T, k, I)
+    xq = raw[off_xq:off_xq + T * H].view(np.int8).reshape(T, H)
+    xs = raw[off_xs:off_xs + T * (H // 32) * 4].view(np.float32).reshape(T, H // 32)
+    hq = raw[off_hq:off_hq + T * k * I].view(np.int8).reshape(T, k, I)
+    hs = raw[off_hs:off_hs + T * k * (I // 32) * 4].view(np.float32).reshape(T, k, I // 32)
+    qx, sx = O.quantize_int8_groups(O.f16_bits_to_f64(p["X"]))
+    assert np.array_equal(xq, qx) and np.array_equal(xs.view(np.uint32), sx.view(np.uint32))
+    qh, sh = O.quantize_int8_groups(O.f16_bits_to_f64(h))
+    assert np.array_equal(hq, qh) and np.array_equal(hs.view(np.uint32), sh.view(np.uint32))
+
+
+def test_zero_tokens_and_refusals():
+    t = torch()
+    p = gen.qmoe_problem(1, 512, 256, 8, 2, 64, seed=905)
+    d = MoeDev(p)
+    # T = 0: nothing to do
+    y = Q.qmoe_decode_fused(d.X[:0], d.ids[:0], d.rw[:0], d.fc["fc1"], d.fc["fc2"], 512, 256, 8, 64)
+    assert y.shape == (0, 512)
+    with pytest.raises(Q.QmmError) as e:
+        Q.qmoe_decode_fused(d.X, d.ids, d.rw, d.fc["fc1"], d.fc["fc2"], 512, 256, 8, 16)
+    assert e.value.status == -4
+    with pytest.raises(Q.QmmError) as e:
+        Q.qmoe_decode_fused(d.X, d.ids, d.rw, d.fc["fc1"], d.fc["fc2"], 512, 256, 8, 64, bits=2)
+    assert e.value.status == -3
+    small = t.empty(16, dtype=t.uint8, device="cuda")
+    with pytest.raises(Q.QmmError) as e:
+        Q.qmoe_decode_fused(d.X, d.ids, d.rw, d.fc["fc1"], d.fc["fc2"], 512, 256, 8, 64, scratch=small)
+    assert e.value.status == -7
