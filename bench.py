@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--legs", default="decode,qmoe", help="comma list of decode,qmoe,prefill")
+    ap.add_argument("--legs", default="decode,prefill,qmoe", help="comma list of decode,prefill,qmoe")
     return ap.parse_args()
 
 
@@ -116,6 +116,54 @@ def decode_leg(args):
                             "frac_hbm": round(b / (per_shape_ms[j] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     return {"step_bytes": step_bytes, "step_ms": step_ms, "wall_s": wall, "shapes": shapes_out,
             "copies": copies}
+
+
+# ---------------------------------------------------------------------------
+# prefill leg: phi4 2-bit M = 2048 on the matrix cores
+# ---------------------------------------------------------------------------
+
+def prefill_leg(args, M=2048, calls=5):
+    import torch
+    from gemm_qmm_nbits_amd import inputs as gen
+    from gemm_qmm_nbits_amd import qmm as Q
+
+    out = {}
+    tot_flop = 0.0
+    tot_ms = 0.0
+    for si, (name, (K, N)) in enumerate(gen.PHI4_SHAPES.items()):
+        p = gen.nbits_problem(1, K, N, 2, 64, seed=gen.config_seed(1, 20 + si), zp="none",
+                              scale_range=(0.01, 0.05))
+        W, S = to_dev(p["W"]), to_dev(p["scales"])
+        A = torch.randn((M, K), dtype=torch.float32, device="cuda",
+                        generator=torch.Generator(device="cuda").manual_seed(si))
+        C = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        ws = torch.empty(Q.lib().qmm_nbits_workspace_bytes(M, K, Q.QMM_F32), dtype=torch.uint8,
+                         device="cuda")
+        stream = torch.cuda.current_stream()
+        for _ in range(2):
+            Q.qmm_nbits(A, W, S, K, 2, 64, None, Q.QMM_ZP_UNIFORM, 1.5, out=C, workspace=ws,
+                        stream=stream)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(calls):
+            Q.qmm_nbits(A, W, S, K, 2, 64, None, Q.QMM_ZP_UNIFORM, 1.5, out=C, workspace=ws,
+                        stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / calls
+        flop = 2.0 * M * N * K
+        tot_flop += flop
+        tot_ms += ms
+        out[name] = {"K": K, "N": N, "M": M, "us": round(ms * 1e3, 1),
+                     "TFLOPs": round(flop / (ms * 1e-3) / 1e12, 1),
+                     "frac_mfma_f16": round(flop / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)}
+        del A, C, ws, W, S
+        torch.cuda.empty_cache()
+    tf = tot_flop / (tot_ms * 1e-3) / 1e12
+    return {"shapes": out, "TFLOPs": round(tf, 1), "frac_mfma_f16": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
+            "note": "cast of fp32 A to fp16 included in each call"}
 
 
 # ---------------------------------------------------------------------------
@@ -259,6 +307,8 @@ def main():
                      "frac": round(value / HBM_PEAK_GBS, 4), "traffic": None},
         "decode_shapes": dec["shapes"],
     }
+    if "prefill" in legs:
+        out["prefill"] = prefill_leg(args)
     if "qmoe" in legs:
         q = []
         q.append(qmoe_leg(args, "gpt-oss-20b", 1, 2880, 2880, 32, 4, 64, False, False, Q.QMOE_FP))

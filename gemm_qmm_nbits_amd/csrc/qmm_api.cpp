@@ -175,8 +175,8 @@ int gemv_choice(int entry, const GemvArgs& g, hipStream_t st) {
   auto default_idx = [&]() {
     const int subs = 64 >> g.lpr_log2;
     for (int i = kNumGemvCandidates - 1; i > 0; --i) {
-      const int64_t wgs = ceil_div(g.N, 4LL * subs * kGemvCandidates[i]);
-      if (wgs >= 512) return i;
+      const int64_t tiles = ceil_div(g.N, 8LL * subs * kGemvCandidates[i]);
+      if (tiles >= 2LL * g.num_cus) return i;
     }
     return 0;
   };
@@ -427,6 +427,7 @@ qmm_status check_nbits(const void* A, int a_type, int64_t M, int64_t K, int64_t 
   if (zp_kind == QMM_ZP_F16 && !aligned(zp, 2)) return QMM_E_ALIGN;
   const size_t need = qmm_nbits_workspace_bytes(M, K, a_type);
   if (need > 0 && (!workspace || workspace_bytes < need)) return QMM_E_WORKSPACE;
+  if (need > 0 && !aligned(workspace, 16)) return QMM_E_ALIGN;
   return QMM_OK;
 }
 
@@ -554,8 +555,9 @@ hipError_t run_gemv_rows(int entry, GemvArgs g, hipStream_t st) {
 extern "C" {
 
 size_t qmm_nbits_workspace_bytes(int64_t M, int64_t K, int a_type) {
-  (void)M; (void)K; (void)a_type;
-  return 0;  // the prefill cast workspace is added with the matrix-core path
+  // the prefill path (M > 8) casts A to fp16 once into the workspace
+  if (M <= kMaxGemvM || a_type == QMM_F16 || M <= 0 || K <= 0) return 0;
+  return ((size_t)M * (size_t)K * 2 + 255) & ~size_t(255);
 }
 
 size_t qmm_codebook4_workspace_bytes(int64_t M, int64_t K, int a_type) {
@@ -589,6 +591,39 @@ qmm_status qmm_nbits(const void* A, int a_type, int64_t M, int64_t K, int64_t N,
   if (s != QMM_OK) return s;
   if (M == 0 || N == 0) return QMM_OK;
   hipStream_t st = (hipStream_t)stream;
+  if (M > kMaxGemvM && K > 0) {
+    // prefill: A -> fp16 once, then the matrix-core tile kernel
+    PrefillArgs p{};
+    if (a_type == QMM_F16) {
+      p.A16 = (const uint16_t*)A;
+    } else {
+      hipError_t e = launch_cast_to_f16(A, a_type, (uint16_t*)workspace, M * K, st);
+      if (e != hipSuccess) return (qmm_status)e;
+      p.A16 = (const uint16_t*)workspace;
+    }
+    p.M = M;
+    p.N = N;
+    p.K = K;
+    p.W = W;
+    p.bits = bits;
+    p.block = block;
+    p.block_log2 = __builtin_ctz((unsigned)block);
+    p.nblk = ceil_div(K, block);
+    p.row_bytes = p.nblk * block * bits / 8;
+    p.scales = scales;
+    p.zp = zp;
+    p.zp_kind = zp_kind;
+    p.zconst = zp_kind == QMM_ZP_UNIFORM ? uniform_zp : (float)(1 << (bits - 1));
+    p.zp_row_bytes = ceil_div(p.nblk * bits, 8);
+    p.bias = bias;
+    p.C = C;
+    p.c_type = c_type;
+    p.a_vec = aligned(p.A16, 16) && (K % 8 == 0);
+    p.w_vec = aligned(W, 16) && (p.row_bytes % 16 == 0);
+    hipError_t e = launch_prefill(p, st);
+    if (e != hipSuccess) return (qmm_status)e;
+    return (qmm_status)hipGetLastError();
+  }
   GemvArgs g = make_gemv(A, a_type, M, K, N, W, bits, block, bias, C, c_type);
   g.fmt = GEMV_AFFINE;
   g.scales = scales;

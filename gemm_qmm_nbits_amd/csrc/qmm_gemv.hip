@@ -86,13 +86,16 @@ void gemv_plan(GemvArgs& g, int num_cus) {
   if (iters < 1) iters = 1;
   if (iters > iters_all) iters = iters_all > 0 ? iters_all : 1;
   g.slice_chunks = (int)(iters * lpr);
-  g.lds_bytes = (size_t)(iters * per_iter) + 16 * sizeof(float);
-  if (g.lds_bytes > kMaxGemvLds) {
+  // A slice + group sums + codebook; the kernel adds its output buffer
+  g.lds_bytes = (size_t)(iters * per_iter) + (size_t)g.mt * 4 * iters * lpr * sizeof(float) +
+                16 * sizeof(float);
+  const size_t total = g.lds_bytes + 4096 * sizeof(float);
+  if (total > kMaxGemvLds) {
     g.chunked = 0;  // no slice fits: generic kernel
     g.lds_bytes = 0;
   }
-  int per_cu = g.lds_bytes ? (int)(kMaxGemvLds / g.lds_bytes) : 8;
-  if (per_cu > 4) per_cu = 4;
+  int per_cu = g.lds_bytes ? (int)(kMaxGemvLds / total) : 2;
+  if (per_cu > 3) per_cu = 3;
   if (per_cu < 1) per_cu = 1;
   g.wg_per_cu = per_cu;
 }

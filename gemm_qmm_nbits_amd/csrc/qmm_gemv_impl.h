@@ -79,58 +79,56 @@ __device__ __forceinline__ void decode_dword_codebook(uint32_t x, const float* c
 
 // Stage the activations of chunks [c0, c0 + SC) of every A row into LDS as fp32:
 // chunk slot `slot` of row m occupies lds[(m * SC + slot) * CS .. + WPC); codes past
-// K read 0.  The CS - WPC = 4 floats after each slot hold the sums of A over the
-// slot's (up to four) scale groups, for the zero-point fold; that padding also
-// spreads the lanes of a wave over distinct LDS banks.
+// K read 0 (the 4 padding floats per slot spread the lanes of a wave over distinct
+// LDS banks).  The sums of A over each scale group of G codes, used by the zero
+// point fold, go to sums[(m * 4 + gi) * SC + slot]; each is reduced over the G/4
+// threads that staged it by a fixed xor butterfly.
 template <int AT, int WPC, int CS>
-__device__ __forceinline__ void stage_a(const GemvArgs& g, float* lds, int c0, int SC, int G) {
+__device__ __forceinline__ void stage_a(const GemvArgs& g, float* lds, float* sums, int c0, int SC,
+                                        int G) {
   const int per_row = SC * (WPC / 4);  // float4 pieces per A row in the slice
   const int total = (int)g.M * per_row;
   const int K = (int)g.K;
-  for (int idx = threadIdx.x; idx < total; idx += blockDim.x) {
-    const int m = idx / per_row;
+  const int gw = G / 4;  // threads per scale group (4, 8 or 16; aligned groups of lanes)
+  for (int base_idx = 0; base_idx < total; base_idx += blockDim.x) {
+    const int idx = base_idx + threadIdx.x;
+    const bool ok = idx < total;
+    const int m = ok ? idx / per_row : 0;
     const int rem = idx - m * per_row;
     const int slot = rem / (WPC / 4);
     const int j4 = rem - slot * (WPC / 4);
     const int k = (c0 + slot) * WPC + 4 * j4;
     const int64_t base = (int64_t)m * K + k;
-    f32x4 v;
-    if (g.a_vec && k + 3 < K) {
-      if constexpr (AT == QMM_F32) {
-        v = *(const f32x4*)((const float*)g.A + base);
-      } else {
-        const uint2 u = *(const uint2*)((const uint16_t*)g.A + base);
-        if constexpr (AT == QMM_F16) {
-          v.x = f16_to_f32((uint16_t)(u.x & 0xffffu));
-          v.y = f16_to_f32((uint16_t)(u.x >> 16));
-          v.z = f16_to_f32((uint16_t)(u.y & 0xffffu));
-          v.w = f16_to_f32((uint16_t)(u.y >> 16));
+    f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (ok) {
+      if (g.a_vec && k + 3 < K) {
+        if constexpr (AT == QMM_F32) {
+          v = *(const f32x4*)((const float*)g.A + base);
         } else {
-          v.x = __uint_as_float(u.x << 16);
-          v.y = __uint_as_float(u.x & 0xffff0000u);
-          v.z = __uint_as_float(u.y << 16);
-          v.w = __uint_as_float(u.y & 0xffff0000u);
+          const uint2 u = *(const uint2*)((const uint16_t*)g.A + base);
+          if constexpr (AT == QMM_F16) {
+            v.x = f16_to_f32((uint16_t)(u.x & 0xffffu));
+            v.y = f16_to_f32((uint16_t)(u.x >> 16));
+            v.z = f16_to_f32((uint16_t)(u.y & 0xffffu));
+            v.w = f16_to_f32((uint16_t)(u.y >> 16));
+          } else {
+            v.x = __uint_as_float(u.x << 16);
+            v.y = __uint_as_float(u.x & 0xffff0000u);
+            v.z = __uint_as_float(u.y << 16);
+            v.w = __uint_as_float(u.y & 0xffff0000u);
+          }
         }
+      } else {
+        v.x = (k + 0 < K) ? load_elem<AT>(g.A, base + 0) : 0.0f;
+        v.y = (k + 1 < K) ? load_elem<AT>(g.A, base + 1) : 0.0f;
+        v.z = (k + 2 < K) ? load_elem<AT>(g.A, base + 2) : 0.0f;
+        v.w = (k + 3 < K) ? load_elem<AT>(g.A, base + 3) : 0.0f;
       }
-    } else {
-      v.x = (k + 0 < K) ? load_elem<AT>(g.A, base + 0) : 0.0f;
-      v.y = (k + 1 < K) ? load_elem<AT>(g.A, base + 1) : 0.0f;
-      v.z = (k + 2 < K) ? load_elem<AT>(g.A, base + 2) : 0.0f;
-      v.w = (k + 3 < K) ? load_elem<AT>(g.A, base + 3) : 0.0f;
+      *(f32x4*)(lds + (m * SC + slot) * CS + 4 * j4) = v;
     }
-    *(f32x4*)(lds + (m * SC + slot) * CS + 4 * j4) = v;
-  }
-  __syncthreads();
-  // group sums, each summed in index order
-  const int gpc = WPC / G;
-  const int ng = (int)g.M * SC * gpc;
-  for (int idx = threadIdx.x; idx < ng; idx += blockDim.x) {
-    const int ms = idx / gpc;  // m * SC + slot
-    const int gi = idx - ms * gpc;
-    const float* src = lds + ms * CS + gi * G;
-    float sum = 0.0f;
-    for (int i = 0; i < G; ++i) sum += src[i];
-    lds[ms * CS + WPC + gi] = sum;
+    float part = ((v.x + v.y) + v.z) + v.w;
+    for (int off = 1; off < gw; off <<= 1) part += __shfl_xor(part, off, 64);
+    if (ok && (j4 % gw) == 0) sums[(m * 4 + j4 / gw) * SC + slot] = part;
   }
 }
 
@@ -143,24 +141,40 @@ struct ItemBuf {
   float z[R][NS];
 };
 
-// Persistent weight-streaming kernel.  A work-group owns tiles of 4*SUBS*R rows
-// (tile = blockIdx.x, blockIdx.x + gridDim.x, ...); each lane walks the sequence
-// (tile, K-slice, chunk iteration) with the next item's weights and scales in
-// flight in a second register set (the loop is unrolled twice so the two sets
-// swap roles without copies; every fetch issues the same loads, with clamped
-// addresses past the end, so the compiler's wait counts stay exact).  A is staged
-// in LDS one K-slice of SC chunks at a time (once for all tiles when one slice
-// covers K).  ZK: 0 = zero point is a constant (none / uniform), 1 = packed codes,
-// 2 = fp16 tensor.  MULTI: a chunk spans several blocks (block < codes per chunk).
+constexpr int kGemvThreads = 512;     // 8 waves per work-group
+constexpr int kGemvDepth = 3;         // items per lane whose loads are in flight
+constexpr int kGemvOutFloats = 4096;  // LDS output buffer (flushed when full)
+
+// Position of a lane in the item sequence of its work-group.
+struct ItemPos {
+  int tile, s, it;
+};
+
+// Persistent weight-streaming kernel.  Work-group g owns the contiguous tiles
+// [t_begin, t_end) of 8*SUBS*R rows each; every lane walks the sequence (tile,
+// K-slice, chunk iteration) with the loads of the next kGemvDepth-1 items in
+// flight in a ring of register sets (the loop is unrolled kGemvDepth times so
+// the sets rotate without copies; every fetch issues the same loads, with
+// clamped addresses past the end, so the compiler's wait counts stay exact).
+// Finished row sums go to an LDS buffer that is written out with coalesced
+// stores only when full and at the end, so no store or bias load sits between a
+// prefetch and its use.  A is staged in LDS one K-slice of SC chunks at a time
+// (once per work-group when one slice covers K).
+// ZK: 0 = zero point is a constant (none / uniform), 1 = packed codes, 2 = fp16
+// tensor.  MULTI: a chunk spans several blocks (block < codes per chunk).
 template <int FMT, int BITS, int AT, int MT, int R, int MULTI, int ZK>
-__global__ __launch_bounds__(256) void gemv_kernel(GemvArgs g) {
+__global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs g) {
   constexpr int WPC = 128 / BITS;  // codes per 16-byte chunk
   constexpr int WPD = 32 / BITS;   // codes per dword
   constexpr int CS = WPC + 4;      // LDS floats per chunk slot
   constexpr int NS = MULTI ? 4 : 1;
+  constexpr int D = kGemvDepth;
+  constexpr int NWAVES = kGemvThreads / 64;
   extern __shared__ float lds[];
   const int SC = g.slice_chunks;
-  float* cb_lds = lds + MT * SC * CS;
+  float* sums_lds = lds + MT * SC * CS;
+  float* cb_lds = sums_lds + MT * 4 * SC;
+  float* out_lds = cb_lds + 16;
   if constexpr (FMT == GEMV_CODEBOOK) {
     if (threadIdx.x < 16) cb_lds[threadIdx.x] = g.codebook[threadIdx.x];
   }
@@ -172,9 +186,15 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs g) {
   const int sub = lane >> lpr_log2;
   const int SUBS = 64 >> lpr_log2;
   const int rows_per_wave = SUBS * R;
-  const int rows_per_tile = (int)(blockDim.x >> 6) * rows_per_wave;
+  const int rows_per_tile = NWAVES * rows_per_wave;
   const int N = (int)g.N;
+  const int M = (int)g.M;
   const int ntiles = (N + rows_per_tile - 1) / rows_per_tile;
+  // contiguous tile range of this work-group
+  const int tiles_lo = ntiles / gridDim.x, extra = ntiles % gridDim.x;
+  const int t_begin = blockIdx.x * tiles_lo + (blockIdx.x < extra ? blockIdx.x : extra);
+  const int t_end = t_begin + tiles_lo + (blockIdx.x < extra ? 1 : 0);
+  if (t_begin >= t_end) return;
   const int nchunks = (int)g.nchunks;
   const int nslices = (nchunks + SC - 1) / SC;
   const int iters = SC >> lpr_log2;  // chunk iterations per slice
@@ -187,41 +207,92 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs g) {
   constexpr float FAC = (FMT == GEMV_AFFINE) ? affine_decode_factor<BITS>() : 1.0f;
   const float zconst = g.zp_kind == QMM_ZP_UNIFORM ? g.uniform_zp : (float)(1 << (BITS - 1));
   const int zrow_bytes = (int)g.zp_row_bytes;
+  // output buffer: tiles per flush
+  int out_tiles = kGemvOutFloats / (rows_per_tile * MT);
+  if (out_tiles < 1) out_tiles = 1;
 
-  int tile = blockIdx.x, s = 0, it = 0;
-  if (tile >= ntiles) return;
-
-  // loads of item (tl, chunk c) into b: always the same instructions; rows or chunks
-  // past the end read row N-1 / chunk nchunks-1 instead (results unused)
-  auto fetch = [&](int tl, int c, ItemBuf<R, NS>& b) {
-    const int cc = c < nchunks ? c : nchunks - 1;
+  auto advance = [&](ItemPos& p) {
+    if (++p.it == iters) {
+      p.it = 0;
+      if (++p.s == nslices) {
+        p.s = 0;
+        ++p.tile;
+      }
+    }
+  };
+  // fetch cursor: the next item to load, its chunk, and the row bases of its tile
+  ItemPos fpos{t_begin, 0, 0};
+  int fchunk = lp;  // chunk of this lane in the item at fpos
+  const uint8_t* fw[R];
+  const uint16_t* fsa[R];    // affine scales row
+  const float* fab[R];       // codebook absmax row
+  const uint8_t* fzp[R];     // packed zero-point row
+  const uint16_t* fzh[R];    // fp16 zero-point row
+  auto set_bases = [&](int tl) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       int row = tl * rows_per_tile + wave * rows_per_wave + r * SUBS + sub;
-      row = row < N ? row : N - 1;
-      b.w[r] = *(const uint4*)(g.W + (int64_t)row * row_bytes + cc * 16);
+      row = (tl < t_end && row < N) ? row : N - 1;
+      fw[r] = g.W + (int64_t)row * row_bytes;
+      if constexpr (FMT == GEMV_AFFINE) fsa[r] = g.scales + (int64_t)row * nblk;
+      else fab[r] = g.absmax + (int64_t)row * nblk;
+      if constexpr (ZK == 1) fzp[r] = (const uint8_t*)g.zp + (int64_t)row * zrow_bytes;
+      if constexpr (ZK == 2) fzh[r] = (const uint16_t*)g.zp + (int64_t)row * nblk;
+    }
+  };
+  set_bases(t_begin);
+  // load the item at the fetch cursor into b and advance the cursor: always the same
+  // loads; past the end of the work the last row / chunk is read (results unused)
+  auto fetch_next = [&](ItemBuf<R, NS>& b) {
+    const int cc = (fpos.tile < t_end && fchunk < nchunks) ? fchunk : nchunks - 1;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      b.w[r] = *(const uint4*)(fw[r] + cc * 16);
 #pragma unroll
       for (int i = 0; i < NS; ++i) {
         const int gi = i < GPC ? i : GPC - 1;
         const int bidx = (cc * WPC + gi * G) >> blog;
-        const int64_t si = (int64_t)row * nblk + bidx;
         if constexpr (FMT == GEMV_AFFINE) {
-          b.s[r][i] = f16_to_f32(g.scales[si]);
+          b.s[r][i] = f16_to_f32(fsa[r][bidx]);
           if constexpr (ZK == 1) {
-            const uint8_t* zr = (const uint8_t*)g.zp + (int64_t)row * zrow_bytes;
             const int bit = bidx * BITS;
-            b.z[r][i] = (float)((zr[bit >> 3] >> (bit & 7)) & ((1u << BITS) - 1u));
+            b.z[r][i] = (float)((fzp[r][bit >> 3] >> (bit & 7)) & ((1u << BITS) - 1u));
           } else if constexpr (ZK == 2) {
-            b.z[r][i] = f16_to_f32(((const uint16_t*)g.zp)[si]);
+            b.z[r][i] = f16_to_f32(fzh[r][bidx]);
           } else {
             b.z[r][i] = zconst;
           }
         } else {
-          b.s[r][i] = g.absmax[si];
+          b.s[r][i] = fab[r][bidx];
           b.z[r][i] = 0.0f;
         }
       }
     }
+    const int old_tile = fpos.tile;
+    advance(fpos);
+    if (fpos.tile != old_tile) {
+      fchunk = lp;
+      set_bases(fpos.tile);
+    } else {
+      fchunk = fpos.s * SC + fpos.it * LPR + lp;
+    }
+  };
+  // write the buffered row sums of tiles [tf, tl) (+ bias) to C
+  auto flush = [&](int tf, int tl) {
+    __syncthreads();
+    const int nrows = (tl - tf) * rows_per_tile;
+    const int row0 = tf * rows_per_tile;
+    for (int i = threadIdx.x; i < nrows * M; i += blockDim.x) {
+      const int m = i / nrows;
+      const int lr = i - m * nrows;
+      const int row = row0 + lr;
+      if (row < N) {
+        float v = out_lds[lr * MT + m];
+        if (g.bias) v += load_elem_rt(g.bias, g.c_type, row);
+        store_elem_rt(g.C, g.c_type, (int64_t)m * N + row, v);
+      }
+    }
+    __syncthreads();
   };
 
   float acc[R][MT];
@@ -230,31 +301,26 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs g) {
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[r][m] = 0.0f;
 
+  ItemPos cur{t_begin, 0, 0};   // item being computed
   bool staged = false;
+  int flush_from = t_begin;
   bool done = false;
-  // One step: stage A if this item starts a slice, prefetch the next item into
-  // `nxt`, compute the current item from `cur`, finish the tile if it ends here.
-  auto step = [&](ItemBuf<R, NS>& cur, ItemBuf<R, NS>& nxt) {
-    int tn = tile, sn = s, itn = it + 1;
-    if (itn == iters) {
-      itn = 0;
-      if (++sn == nslices) {
-        sn = 0;
-        tn = tile + gridDim.x;
-      }
-    }
-    const bool has_next = tn < ntiles;
-    if (it == 0 && (nslices > 1 || !staged)) {
+
+  // One step: stage A if this item starts a slice, fetch the item D-1 ahead into
+  // `nxt` (the set that held the previous item), compute the current item from
+  // `cb`, and finish the tile if it ends here.
+  auto step = [&](ItemBuf<R, NS>& cbuf, ItemBuf<R, NS>& nxt) {
+    if (cur.it == 0 && (nslices > 1 || !staged)) {
       __syncthreads();
-      stage_a<AT, WPC, CS>(g, lds, s * SC, SC, G);
+      stage_a<AT, WPC, CS>(g, lds, sums_lds, cur.s * SC, SC, G);
       __syncthreads();
       staged = true;
     }
-    fetch(has_next ? tn : tile, has_next ? sn * SC + itn * LPR + lp : nchunks, nxt);
+    fetch_next(nxt);
 
-    const int c = s * SC + it * LPR + lp;
+    const int c = cur.s * SC + cur.it * LPR + lp;
     if (c < nchunks) {
-      const float* abase = lds + (it * LPR + lp) * CS;
+      const float* abase = lds + (cur.it * LPR + lp) * CS;
       float P[R][MT];
 #pragma unroll
       for (int r = 0; r < R; ++r)
@@ -265,7 +331,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs g) {
         float a[MT][WPD];
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
-          const int mm = m < g.M ? m : 0;
+          const int mm = m < M ? m : 0;
           const f32x4* ap = (const f32x4*)(abase + mm * SC * CS + d * WPD);
 #pragma unroll
           for (int i = 0; i < WPD / 4; ++i) {
@@ -275,7 +341,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs g) {
         }
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-          const uint32_t x = d == 0 ? cur.w[r].x : d == 1 ? cur.w[r].y : d == 2 ? cur.w[r].z : cur.w[r].w;
+          const uint32_t x = d == 0 ? cbuf.w[r].x : d == 1 ? cbuf.w[r].y : d == 2 ? cbuf.w[r].z : cbuf.w[r].w;
           float q[WPD];
           if constexpr (FMT == GEMV_AFFINE) decode_dword_affine<BITS>(x, q);
           else decode_dword_codebook(x, cb_lds, q);
@@ -291,19 +357,19 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs g) {
           for (int r = 0; r < R; ++r) {
             float scv, z;
             if constexpr (MULTI) {
-              scv = gi == 0 ? cur.s[r][0] : gi == 1 ? cur.s[r][NS > 1 ? 1 : 0]
-                  : gi == 2 ? cur.s[r][NS > 2 ? 2 : 0] : cur.s[r][NS > 3 ? 3 : 0];
-              z = gi == 0 ? cur.z[r][0] : gi == 1 ? cur.z[r][NS > 1 ? 1 : 0]
-                  : gi == 2 ? cur.z[r][NS > 2 ? 2 : 0] : cur.z[r][NS > 3 ? 3 : 0];
+              scv = gi == 0 ? cbuf.s[r][0] : gi == 1 ? cbuf.s[r][NS > 1 ? 1 : 0]
+                  : gi == 2 ? cbuf.s[r][NS > 2 ? 2 : 0] : cbuf.s[r][NS > 3 ? 3 : 0];
+              z = gi == 0 ? cbuf.z[r][0] : gi == 1 ? cbuf.z[r][NS > 1 ? 1 : 0]
+                  : gi == 2 ? cbuf.z[r][NS > 2 ? 2 : 0] : cbuf.z[r][NS > 3 ? 3 : 0];
             } else {
-              scv = cur.s[r][0];
-              z = cur.z[r][0];
+              scv = cbuf.s[r][0];
+              z = cbuf.z[r][0];
             }
             if constexpr (FMT == GEMV_AFFINE) {
 #pragma unroll
               for (int m = 0; m < MT; ++m) {
-                const int mm = m < g.M ? m : 0;
-                const float sa = abase[mm * SC * CS + WPC + gi];
+                const int mm = m < M ? m : 0;
+                const float sa = sums_lds[(mm * 4 + gi) * SC + cur.it * LPR + lp];
                 acc[r][m] = fmaf(scv, fmaf(-z, sa, FAC * P[r][m]), acc[r][m]);
                 P[r][m] = 0.0f;
               }
@@ -319,40 +385,44 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs g) {
       }
     }
 
-    if (s == nslices - 1 && it == iters - 1) {
+    if (cur.s == nslices - 1 && cur.it == iters - 1) {
       // tile complete: fixed-order combination of the LPR lane partials of each row
 #pragma unroll
       for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int m = 0; m < MT; ++m) acc[r][m] = group_sum(acc[r][m], LPR);
       if (lp == 0) {
+        const int lt = cur.tile - flush_from;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-          const int row = tile * rows_per_tile + wave * rows_per_wave + r * SUBS + sub;
-          if (row >= N) continue;
-          const float bv = g.bias ? load_elem_rt(g.bias, g.c_type, row) : 0.0f;
+          const int lr = lt * rows_per_tile + wave * rows_per_wave + r * SUBS + sub;
 #pragma unroll
-          for (int m = 0; m < MT; ++m)
-            if (m < g.M) store_elem_rt(g.C, g.c_type, (int64_t)m * N + row, acc[r][m] + bv);
+          for (int m = 0; m < MT; ++m) out_lds[lr * MT + m] = acc[r][m];
         }
       }
 #pragma unroll
       for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int m = 0; m < MT; ++m) acc[r][m] = 0.0f;
+      if (cur.tile + 1 == t_end || cur.tile + 1 - flush_from == out_tiles) {
+        flush(flush_from, cur.tile + 1);
+        flush_from = cur.tile + 1;
+      }
+      done = cur.tile + 1 == t_end;
     }
-    done = !has_next;
-    tile = tn;
-    s = sn;
-    it = itn;
+    advance(cur);
   };
 
-  ItemBuf<R, NS> b0, b1;
-  fetch(tile, lp, b0);
+  ItemBuf<R, NS> b0, b1, b2;
+  static_assert(D == 3, "the unrolled loop below rotates three register sets");
+  fetch_next(b0);
+  fetch_next(b1);
   while (true) {
-    step(b0, b1);
+    step(b0, b2);
     if (done) break;
     step(b1, b0);
+    if (done) break;
+    step(b2, b1);
     if (done) break;
   }
 }
@@ -369,14 +439,15 @@ static void allow_large_lds(K kernel, size_t lds) {
 template <int FMT, int BITS, int AT, int MT, int R, int MULTI, int ZK>
 static hipError_t launch_one(const GemvArgs& g, hipStream_t st) {
   const int subs = 64 >> g.lpr_log2;
-  const int64_t rows_per_tile = 4LL * subs * R;
+  const int64_t rows_per_tile = (int64_t)(kGemvThreads / 64) * subs * R;
   const int64_t ntiles = (g.N + rows_per_tile - 1) / rows_per_tile;
   int64_t grid = (int64_t)g.num_cus * g.wg_per_cu;
   if (grid > ntiles) grid = ntiles;
   if (grid < 1) grid = 1;
+  const size_t lds = g.lds_bytes + kGemvOutFloats * sizeof(float);
   auto kern = gemv_kernel<FMT, BITS, AT, MT, R, MULTI, ZK>;
-  allow_large_lds(kern, g.lds_bytes);
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), g.lds_bytes, st, g);
+  allow_large_lds(kern, lds);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kGemvThreads), lds, st, g);
   return hipSuccess;
 }
 

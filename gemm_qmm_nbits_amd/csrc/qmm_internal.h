@@ -43,7 +43,7 @@ struct GemvArgs {
 };
 
 constexpr size_t kMaxGemvLds = 160 * 1024;   // LDS per work-group on gfx950
-constexpr size_t kGemvLdsBudget = 80 * 1024; // preferred A staging size per work-group
+constexpr size_t kGemvLdsBudget = 96 * 1024; // preferred A staging size per work-group
 
 // Fill mt, slice_chunks, lds_bytes, wg_per_cu (and clear `chunked` when no slice fits).
 void gemv_plan(GemvArgs& g, int num_cus);
@@ -76,6 +76,26 @@ constexpr int kUniformPartials = 256;
 // A (fp32 / bf16) -> fp16, round to nearest even, count elements.
 hipError_t launch_cast_to_f16(const void* src, int src_type, uint16_t* dst, int64_t count,
                               hipStream_t st);
+
+struct PrefillArgs {
+  const uint16_t* A16;  // fp16 [M][K]
+  int64_t M, N, K;
+  const uint8_t* W;
+  int bits, block, block_log2;
+  int64_t nblk, row_bytes;
+  const uint16_t* scales;
+  const void* zp;
+  int zp_kind;
+  float zconst;  // zero point for QMM_ZP_NONE / QMM_ZP_UNIFORM
+  int64_t zp_row_bytes;
+  const void* bias;
+  void* C;
+  int c_type;
+  int a_vec;  // A16 rows allow 16-byte loads
+  int w_vec;  // W rows allow 8/16-byte loads of 32 codes
+  int ntiles, mtiles;
+};
+hipError_t launch_prefill(PrefillArgs p, hipStream_t st);
 
 struct QmoeArgs {
   const uint16_t* X;

@@ -123,7 +123,10 @@ def test_gemv_small_shapes(M, bits, block, K, N, zp, a, c):
     say(f"gemv M={M} bits={bits} block={block} K={K} N={N} zp={zp} a={a} c={c}")
     p = gen.nbits_problem(M, K, N, bits, block, seed=7 * M + K, zp=zp, a_dtype=a, bias=(M % 2 == 1))
     d = NbitsDev(p, c_dtype=c)
-    _check(d, d.run(), label=f"M={M}")
+    if M > 8:  # prefill path: operands rounded to fp16 by declaration
+        _check_prefill(d, d.run(), label=f"M={M}")
+    else:
+        _check(d, d.run(), label=f"M={M}")
 
 
 def test_repeat_calls_bit_identical():
@@ -199,4 +202,101 @@ def test_refused_arguments_on_device():
     with pytest.raises(Q.QmmError) as e:
         Q.qmm_nbits(d.A, d.W, d.scales, 256, 4, 64, None, Q.QMM_ZP_PACKED)
     assert e.value.status == -1
+    t.cuda.synchronize()
+
+
+# --- prefill path (M > 8): A rounded to fp16 once, fp16 weights, fp32 accumulation ---
+
+def _check_prefill(d, got, rows=None, label=""):
+    """Gate against the oracle with the path's declared operand roundings (A and W
+    to fp16); the error against the unrounded oracle is printed for information."""
+    y = host_f64(got)
+    if rows is not None:
+        y = y[:, rows]
+    ref = d.oracle(O, rows=rows, a_round="f16", w_round="f16")
+    err = O.rel_l2(y, ref)
+    raw = O.rel_l2(y, d.oracle(O, rows=rows))
+    say(f"  {label} relL2(mirrored)={err:.3e} relL2(unrounded)={raw:.3e}")
+    assert err <= TOL[d.c_dtype], (label, err)
+    return err
+
+
+@pytest.mark.parametrize("name", list(gen.PHI4_SHAPES))
+def test_phi4_u2_prefill_full_size(name):
+    """phi4-14B 2-bit shapes at M = 2048 (full size; oracle on sampled output columns)."""
+    K, N = gen.PHI4_SHAPES[name]
+    say(f"phi4 prefill {name} K={K} N={N}")
+    p = gen.nbits_problem(2048, K, N, 2, 64, seed=gen.config_seed(1, 10 + list(gen.PHI4_SHAPES).index(name)),
+                          zp="f16_uniform", uniform_zp=1.5, scale_range=(0.01, 0.05))
+    d = NbitsDev(p)
+    got = d.run(uniform=True)
+    torch().cuda.synchronize()
+    rows = sample_rows(N, 192, seed=N + 1)
+    _check_prefill(d, got, rows=rows, label=name)
+    # the fp16 zero-point tensor path gives the same bits as the scalar path
+    got_t = d.run(uniform=False)
+    assert np.array_equal(host_bits(got), host_bits(got_t))
+
+
+@pytest.mark.parametrize("M,K,N,bits,block,zp,a,c", [
+    (9, 256, 130, 4, 64, "packed8", "f32", "f32"),
+    (16, 100, 300, 2, 16, "packed", "f32", "f32"),
+    (100, 5120, 257, 2, 64, "f16_uniform", "f32", "f32"),
+    (300, 2880, 520, 4, 128, "packed", "f16", "f16"),
+    (257, 1000, 64, 4, 32, "none", "bf16", "bf16"),
+    (64, 70, 33, 2, 16, "f16", "f32", "f16"),
+    (513, 4096, 300, 4, 256, "f16", "bf16", "f32"),
+])
+def test_prefill_small_shapes(M, K, N, bits, block, zp, a, c):
+    say(f"prefill M={M} K={K} N={N} bits={bits} block={block} zp={zp} a={a} c={c}")
+    p = gen.nbits_problem(M, K, N, bits, block, seed=11 * M + K, zp=zp, a_dtype=a, bias=(M % 2 == 1))
+    d = NbitsDev(p, c_dtype=c)
+    _check_prefill(d, d.run(), label=f"M={M}")
+
+
+def test_prefill_exact_arithmetic_bitwise():
+    """Small-integer activations and power-of-two scales make every partial sum exact,
+    so the matrix-core path and the GEMV path agree bit for bit with the oracle."""
+    t = torch()
+    M, K, N, bits, block = 32, 512, 96, 4, 64
+    p = gen.nbits_problem(M, K, N, bits, block, seed=5, zp="packed")
+    rng = np.random.default_rng(6)
+    p["A"] = rng.integers(-8, 9, size=(M, K)).astype(np.float32)
+    p["scales"] = (2.0 ** rng.integers(-6, -2, size=p["scales"].shape)).astype(np.float16).view(np.uint16)
+    d = NbitsDev(p)
+    got = host_f64(d.run())
+    ref = d.oracle(O)
+    assert np.array_equal(got, ref)
+    got1 = np.concatenate([host_f64(d.run(A=d.A[i:i + 1].contiguous())) for i in range(4)])
+    assert np.array_equal(got1, ref[:4])
+    t.cuda.synchronize()
+
+
+def test_prefill_repeat_bit_identical():
+    p = gen.nbits_problem(512, 5120, 1024, 2, 64, seed=79, zp="f16_uniform", scale_range=(0.01, 0.05))
+    d = NbitsDev(p)
+    first = host_bits(d.run(uniform=True)).copy()
+    out = torch().empty_like(d.run(uniform=True))
+    for i in range(16):
+        d.run(uniform=True, out=out)
+        assert np.array_equal(host_bits(out), first), i
+
+
+def test_empty_and_degenerate():
+    t = torch()
+    p = gen.nbits_problem(3, 256, 8, 4, 64, seed=9, zp="packed8", bias=True)
+    d = NbitsDev(p)
+    # M = 0 and N = 0: nothing to compute
+    y = Q.qmm_nbits(d.A[:0], d.W, d.scales, 256, 4, 64, d.zp, Q.QMM_ZP_PACKED)
+    assert y.shape == (0, 8)
+    y = Q.qmm_nbits(d.A, d.W[:0], d.scales[:0], 256, 4, 64, d.zp[:0], Q.QMM_ZP_PACKED)
+    assert y.shape == (3, 0)
+    # K = 1: one code of a ragged block; every weight row is (q - 8) * s
+    p1 = gen.nbits_problem(2, 1, 8, 4, 64, seed=10, zp="packed8", bias=True)
+    d1 = NbitsDev(p1)
+    assert O.rel_l2(host_f64(d1.run()), d1.oracle(O)) <= TOL["f32"]
+    # M = 20 with K = 1 on the prefill path
+    p2 = gen.nbits_problem(20, 1, 8, 2, 16, seed=11, zp="packed")
+    d2 = NbitsDev(p2)
+    assert O.rel_l2(host_f64(d2.run()), d2.oracle(O, a_round="f16", w_round="f16")) <= TOL["f32"]
     t.cuda.synchronize()
