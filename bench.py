@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--legs", default="decode,prefill,qmoe", help="comma list of decode,prefill,qmoe")
+    ap.add_argument("--decode-shapes", default="qkv,gate_up,down,lm_head",
+                    help="subset of the phi4 layers in the decode step (profiling runs)")
     return ap.parse_args()
 
 
@@ -62,60 +64,96 @@ def weight_bytes_nbits(K, N, bits=2, block=64):
 # ---------------------------------------------------------------------------
 
 def decode_leg(args):
+    """Decode step = the four phi4 layers at M = 1, captured as one HIP graph per
+    weight copy and replayed back to back (launch gaps of the host excluded)."""
     import torch
     from gemm_qmm_nbits_amd import inputs as gen
     from gemm_qmm_nbits_amd import qmm as Q
 
-    shapes = list(gen.PHI4_SHAPES.items())
+    want = args.decode_shapes.split(",")
+    shapes = [(n, kn) for n, kn in gen.PHI4_SHAPES.items() if n in want]
     step_bytes = sum(weight_bytes_nbits(K, N) for _, (K, N) in shapes)
     copies = max(2, int(np.ceil(1.0 * (1 << 30) / step_bytes)) + 1)
     log(f"[decode] {len(shapes)} shapes, {step_bytes / 1e6:.1f} MB weights/step, {copies} copies")
     sets = []
     for ci in range(copies):
         layer = []
-        for si, (name, (K, N)) in enumerate(shapes):
+        for name, (K, N) in shapes:
+            si = list(gen.PHI4_SHAPES).index(name)
             p = gen.nbits_problem(1, K, N, 2, 64, seed=gen.config_seed(1, si) + 100 * ci,
                                   zp="none", scale_range=(0.01, 0.05))
             layer.append({"name": name, "K": K, "N": N, "A": to_dev(p["A"]), "W": to_dev(p["W"]),
                           "scales": to_dev(p["scales"]),
                           "C": torch.empty((1, N), dtype=torch.float32, device="cuda")})
         sets.append(layer)
-    stream = torch.cuda.current_stream()
 
-    def run_step(i, events=None):
-        layer = sets[i % copies]
-        for j, L in enumerate(layer):
-            Q.qmm_nbits(L["A"], L["W"], L["scales"], L["K"], 2, 64, None, Q.QMM_ZP_UNIFORM, 1.5,
-                        out=L["C"], stream=stream)
-            if events is not None:
-                events[j + 1].record(stream)
+    def launch(L):
+        Q.qmm_nbits(L["A"], L["W"], L["scales"], L["K"], 2, 64, None, Q.QMM_ZP_UNIFORM, 1.5,
+                    out=L["C"])
 
-    for i in range(args.warmup):
-        run_step(i)
+    # eager warm-up: the first call of each shape runs the up-front tiling choice
+    for layer in sets:
+        for L in layer:
+            launch(L)
     torch.cuda.synchronize()
-    nshape = len(shapes)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nshape + 1)] for _ in range(args.steps)]
+    eager_ref = [L["C"].clone() for L in sets[0]]
+    cap = torch.cuda.Stream()
+    step_graphs = []
+    with torch.cuda.stream(cap):
+        for layer in sets:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                for L in layer:
+                    launch(L)
+            step_graphs.append(g)
+        # one graph per shape: that layer of every copy, back to back (cold rotation)
+        shape_graphs = []
+        for j in range(len(shapes)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                for layer in sets:
+                    launch(layer[j])
+            shape_graphs.append(g)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        step_graphs[i % copies].replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    e0.record(stream)
     for i in range(args.steps):
-        ev[i][0].record(stream)
-        run_step(i, ev[i])
+        step_graphs[i % copies].replay()
+    e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per_shape_ms = np.zeros(nshape)
-    for i in range(args.steps):
-        for j in range(nshape):
-            per_shape_ms[j] += ev[i][j].elapsed_time(ev[i][j + 1])
-    per_shape_ms /= args.steps
-    step_ms = float(per_shape_ms.sum())
+    step_ms = e0.elapsed_time(e1) / args.steps
     shapes_out = {}
+    reps = 5
     for j, (name, (K, N)) in enumerate(shapes):
+        shape_graphs[j].replay()
+        torch.cuda.synchronize()
+        a0 = torch.cuda.Event(enable_timing=True)
+        a1 = torch.cuda.Event(enable_timing=True)
+        a0.record(stream)
+        for _ in range(reps):
+            shape_graphs[j].replay()
+        a1.record(stream)
+        torch.cuda.synchronize()
+        us = a0.elapsed_time(a1) * 1e3 / (reps * copies)
         b = weight_bytes_nbits(K, N)
-        shapes_out[name] = {"K": K, "N": N, "weight_MB": round(b / 1e6, 3),
-                            "us": round(per_shape_ms[j] * 1e3, 2),
-                            "GBps": round(b / (per_shape_ms[j] * 1e-3) / 1e9, 1),
-                            "frac_hbm": round(b / (per_shape_ms[j] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        shapes_out[name] = {"K": K, "N": N, "weight_MB": round(b / 1e6, 3), "us": round(us, 2),
+                            "GBps": round(b / (us * 1e-6) / 1e9, 1),
+                            "frac_hbm": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    # the decode outputs of the graph replays equal the eager ones
+    for L in sets[0]:
+        L["C"].zero_()
+    step_graphs[0].replay()
+    torch.cuda.synchronize()
+    same = all(torch.equal(r, L["C"]) for r, L in zip(eager_ref, sets[0]))
     return {"step_bytes": step_bytes, "step_ms": step_ms, "wall_s": wall, "shapes": shapes_out,
-            "copies": copies}
+            "copies": copies, "graph_replay_matches_eager": bool(same)}
 
 
 # ---------------------------------------------------------------------------
@@ -182,12 +220,13 @@ def qmoe_bytes(H, I, block, zp, bias, n_experts):
     return n_experts * (per(2 * I, H) + per(H, I))
 
 
-def qmoe_leg(args, name, T, H, I, E, k, block, zp, bias, mode, calls=40):
+def qmoe_leg(args, name, T, H, I, E, k, block, zp, bias, mode, calls=48):
+    """Fused MoE decode: `calls` calls with fresh routing each and whole-layer weight
+    copies rotated (>= 1 GiB), captured in one HIP graph and replayed; mean per call."""
     import torch
     from gemm_qmm_nbits_amd import inputs as gen
     from gemm_qmm_nbits_amd import qmm as Q
 
-    # whole-layer copies so that the rotation exceeds the last-level cache
     layer_bytes = qmoe_bytes(H, I, block, zp, bias, E)
     copies = max(2, int(np.ceil((1 << 30) / layer_bytes)))
     p = gen.qmoe_problem(T, H, I, E, k, block, seed=gen.config_seed(3 if E == 32 else 4, T),
@@ -205,41 +244,52 @@ def qmoe_leg(args, name, T, H, I, E, k, block, zp, bias, mode, calls=40):
     rng = np.random.default_rng(7)
     routes = []
     n_unique = []
-    for i in range(calls + args.warmup):
+    for i in range(calls):
         ids, w = gen.routing(rng, T, E, k)
         routes.append((to_dev(ids), to_dev(w)))
         n_unique.append(len(np.unique(ids)))
     Y = torch.empty((T, H), dtype=torch.float16, device="cuda")
     scratch = torch.empty(Q.qmoe_decode_scratch_bytes(T, H, I, k, mode), dtype=torch.uint8,
                           device="cuda")
-    stream = torch.cuda.current_stream()
-    for i in range(args.warmup):
+
+    def call(i):
         d = fcs[i % copies]
         Q.qmoe_decode_fused(X, routes[i][0], routes[i][1], d["fc1"], d["fc2"], H, I, E, block,
-                            mode=mode, out=Y, scratch=scratch, stream=stream)
+                            mode=mode, out=Y, scratch=scratch)
+
+    for i in range(min(calls, 4)):   # eager: the first call times the tiling candidates
+        call(i)
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(calls)]
-    for i in range(calls):
-        d = fcs[i % copies]
-        ids, w = routes[args.warmup + i]
-        ev[i][0].record(stream)
-        Q.qmoe_decode_fused(X, ids, w, d["fc1"], d["fc2"], H, I, E, block, mode=mode, out=Y,
-                            scratch=scratch, stream=stream)
-        ev[i][1].record(stream)
+    cap = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            for i in range(calls):
+                call(i)
     torch.cuda.synchronize()
-    us = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
-    uniq = np.array(n_unique[args.warmup:])
+    g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    reps = 3
+    e0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (reps * calls)
+    uniq = float(np.mean(n_unique))
     per_expert = qmoe_bytes(H, I, block, zp, bias, 1)
-    gbps = float(np.mean(uniq * per_expert / (us * 1e-6)) / 1e9)
-    del fcs
+    gbps = uniq * per_expert / (us * 1e-6) / 1e9
+    del fcs, g
     torch.cuda.empty_cache()
     return {"name": name, "T": T, "H": H, "I": I, "E": E, "k": k, "block": block, "zp": zp,
             "bias": bias, "mode": "int8" if mode == Q.QMOE_INT8_ACT else "fp",
-            "us_mean": round(float(us.mean()), 2), "us_median": round(float(np.median(us)), 2),
-            "tok_per_s": round(T / (float(us.mean()) * 1e-6), 1),
+            "us_per_call": round(us, 2), "tok_per_s": round(T / (us * 1e-6), 1),
+            "weight_MB_per_call": round(uniq * per_expert / 1e6, 2),
             "weight_GBps": round(gbps, 1), "frac_hbm": round(gbps / HBM_PEAK_GBS, 4),
-            "unique_experts_mean": float(uniq.mean())}
+            "unique_experts_mean": uniq}
 
 
 # ---------------------------------------------------------------------------
@@ -269,6 +319,51 @@ def cpu_baseline():
             "kind": "oracle",
             "sample": f"one full decode step (qkv, gate_up, down, lm_head at M=1): "
                       f"{total_b / 1e6:.1f} MB of weights in {total_s:.1f} s, numpy fp64, 1 thread"}
+
+
+def copy_calibration(nbytes=256 << 20, calls=5):
+    """A plain device copy of known size, for scaling the HBM byte counters."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(calls):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    return {"bytes_per_copy": nbytes, "calls": calls}
+
+
+def roofline_entry(dec):
+    """Dominant kernel of the decode step: the lm_head GEMV (62% of the step's bytes)."""
+    if "lm_head" not in dec["shapes"]:
+        return None
+    lm = dec["shapes"]["lm_head"]
+    achieved = lm["GBps"]
+    r = {"bound": "hbm", "kernel": "gemv_kernel<affine, u2, fp32 A, M=1> on lm_head 5120x100352",
+         "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+         "algorithmic_bytes_per_launch": int(weight_bytes_nbits(5120, 100352)),
+         "avg_launch_us": lm["us"]}
+    r["traffic"] = measured_traffic("gemv_lm_head")
+    return r
+
+
+def measured_traffic(key):
+    """HBM bytes per launch from the committed counter summary, if it was taken on the
+    current kernel sources (FETCH_SIZE x its copy-kernel factor + WRITE_SIZE)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    h = hashlib.sha256()
+    for rel in t.get("sources", []):
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    if h.hexdigest() != t.get("sources_sha256"):
+        return None
+    e = t.get("kernels", {}).get(key)
+    return None if e is None else e.get("bytes_per_launch")
 
 
 def main():
@@ -302,13 +397,13 @@ def main():
                                "fp32 A/C: qkv 5120x7680, gate_up 5120x35840, down 17920x5120, "
                                "lm_head 5120x100352",
                    "M": 1, "bits": 2, "block": 64, "weight_copies_rotated": dec["copies"]},
-        "roofline": {"bound": "hbm", "kernel": "gemv_kernel<affine,u2,f32,M=1> (4 phi4 shapes)",
-                     "achieved": round(value, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(value / HBM_PEAK_GBS, 4), "traffic": None},
+        "roofline": roofline_entry(dec),
         "decode_shapes": dec["shapes"],
     }
     if "prefill" in legs:
         out["prefill"] = prefill_leg(args)
+    if "copycal" in legs:
+        out["copy_calibration"] = copy_calibration()
     if "qmoe" in legs:
         q = []
         q.append(qmoe_leg(args, "gpt-oss-20b", 1, 2880, 2880, 32, 4, 64, False, False, Q.QMOE_FP))
