@@ -95,10 +95,22 @@ __device__ __forceinline__ float dequant_affine(uint32_t q, float zp, float s) {
 
 // ---- wave-level helpers ------------------------------------------------------
 
+// xor-swizzle inside groups of 32 lanes (ds_swizzle bit mode: and 0x1f, xor k)
+template <int K>
+__device__ __forceinline__ float swz_xor(float v) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x1f | (K << 10)));
+}
+
 // Butterfly sum over groups of `width` consecutive lanes (power of two <= 64).
-// Every lane of the group ends with the same, order-fixed result.
+// Every lane of the group ends with the same, order-fixed result: at each step a
+// lane adds its partner's value (a + b == b + a bitwise, so partners agree).
 __device__ __forceinline__ float group_sum(float v, int width) {
-  for (int off = 1; off < width; off <<= 1) v += __shfl_xor(v, off, 64);
+  if (width > 1) v += swz_xor<1>(v);
+  if (width > 2) v += swz_xor<2>(v);
+  if (width > 4) v += swz_xor<4>(v);
+  if (width > 8) v += swz_xor<8>(v);
+  if (width > 16) v += swz_xor<16>(v);
+  if (width > 32) v += __shfl_xor(v, 32, 64);
   return v;
 }
 

@@ -6,13 +6,25 @@ namespace qmm {
 
 template <int FMT, int BITS, int AT>
 hipError_t launch_at_type(const GemvArgs& g, int R, hipStream_t st);
+template <int BITS, int AT>
+hipError_t launch_ip_at_type(const GemvArgs& g, int R, hipStream_t st);
 
-template <int FMT, int BITS>
-static hipError_t launch_at(const GemvArgs& g, int R, hipStream_t st) {
+// codebook weights: fp32 kernel with the LDS centroid table
+static hipError_t launch_codebook(const GemvArgs& g, int R, hipStream_t st) {
   switch (g.a_type) {
-    case QMM_F32: return launch_at_type<FMT, BITS, QMM_F32>(g, R, st);
-    case QMM_F16: return launch_at_type<FMT, BITS, QMM_F16>(g, R, st);
-    default: return launch_at_type<FMT, BITS, QMM_BF16>(g, R, st);
+    case QMM_F32: return launch_at_type<GEMV_CODEBOOK, 4, QMM_F32>(g, R, st);
+    case QMM_F16: return launch_at_type<GEMV_CODEBOOK, 4, QMM_F16>(g, R, st);
+    default: return launch_at_type<GEMV_CODEBOOK, 4, QMM_BF16>(g, R, st);
+  }
+}
+
+// affine weights: integer-plane kernel
+template <int BITS>
+static hipError_t launch_affine(const GemvArgs& g, int R, hipStream_t st) {
+  switch (g.a_type) {
+    case QMM_F32: return launch_ip_at_type<BITS, QMM_F32>(g, R, st);
+    case QMM_F16: return launch_ip_at_type<BITS, QMM_F16>(g, R, st);
+    default: return launch_ip_at_type<BITS, QMM_BF16>(g, R, st);
   }
 }
 
@@ -77,8 +89,13 @@ int gemv_lanes_per_row_log2(int64_t nchunks) {
 void gemv_plan(GemvArgs& g, int num_cus) {
   g.mt = g.M <= 1 ? 1 : g.M <= 2 ? 2 : g.M <= 4 ? 4 : 8;
   g.num_cus = num_cus > 0 ? num_cus : 256;
-  const int bits = g.fmt == GEMV_CODEBOOK ? 4 : g.bits;
-  const int64_t cs_bytes = (int64_t)(128 / bits + 4) * 4;  // LDS bytes per chunk slot per A row
+  // LDS bytes per chunk slot per A row: codebook kernel = fp32 activations (WPC + 4
+  // floats) + 4 group sums; integer-plane kernel = the planes (12 or 6 words per
+  // weight dword, 4 words of padding) + 4 group records of two floats
+  int64_t cs_bytes;
+  if (g.fmt == GEMV_CODEBOOK) cs_bytes = (int64_t)(32 + 4) * 4 + 4 * 4;
+  else if (g.bits == 2) cs_bytes = (int64_t)(4 * 12 + 4) * 4 + 4 * 8;
+  else cs_bytes = (int64_t)(4 * 6 + 4) * 4 + 4 * 8;
   const int64_t lpr = 1LL << g.lpr_log2;
   const int64_t per_iter = (int64_t)g.mt * lpr * cs_bytes;  // one chunk per lane, all A rows
   const int64_t iters_all = (g.nchunks + lpr - 1) / lpr;
@@ -86,9 +103,8 @@ void gemv_plan(GemvArgs& g, int num_cus) {
   if (iters < 1) iters = 1;
   if (iters > iters_all) iters = iters_all > 0 ? iters_all : 1;
   g.slice_chunks = (int)(iters * lpr);
-  // A slice + group sums + codebook; the kernel adds its output buffer
-  g.lds_bytes = (size_t)(iters * per_iter) + (size_t)g.mt * 4 * iters * lpr * sizeof(float) +
-                16 * sizeof(float);
+  // A slice + group records + codebook; the kernel adds its output buffer
+  g.lds_bytes = (size_t)(iters * per_iter) + 16 * sizeof(float);
   const size_t total = g.lds_bytes + 4096 * sizeof(float);
   if (total > kMaxGemvLds) {
     g.chunked = 0;  // no slice fits: generic kernel
@@ -106,9 +122,9 @@ hipError_t launch_gemv(GemvArgs g, int rows_per_lane, hipStream_t st) {
     hipLaunchKernelGGL(gemv_generic_kernel, grid, dim3(256), 0, st, g);
     return hipSuccess;
   }
-  if (g.fmt == GEMV_CODEBOOK) return launch_at<GEMV_CODEBOOK, 4>(g, rows_per_lane, st);
-  if (g.bits == 2) return launch_at<GEMV_AFFINE, 2>(g, rows_per_lane, st);
-  return launch_at<GEMV_AFFINE, 4>(g, rows_per_lane, st);
+  if (g.fmt == GEMV_CODEBOOK) return launch_codebook(g, rows_per_lane, st);
+  if (g.bits == 2) return launch_affine<2>(g, rows_per_lane, st);
+  return launch_affine<4>(g, rows_per_lane, st);
 }
 
 }  // namespace qmm

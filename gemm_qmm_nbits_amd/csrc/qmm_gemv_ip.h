@@ -1,0 +1,442 @@
+// Weight-streaming GEMV for affine 2-bit / 4-bit MatMulNBits weights with exact
+// integer dot products ([P1] hip-ep PR 1318, "What", commit 1: a GEMV that reads
+// fp32 A directly; zero point folded so a uniform zero point costs nothing).
+//
+// Each scale group of G codes of A (G = min(block, codes per 16-byte chunk)) is
+// staged in LDS as a block fixed-point number: a_int = rint(a * 2^(22 - e)) with
+// 2^e > max |a| over the group (so |a_int| <= 2^22 and the rounding error is at most
+// 2^-23 of the group maximum), stored as six 4-bit planes.  The dot product of a
+// chunk of codes with one plane is then exact in int32 with v_dot8 (eight 4-bit
+// products per instruction):
+//   2-bit codes: masking the weight dword with 0x33333333 (and the dword shifted
+//     right by 2) leaves the even (odd) codes as nibbles in index order; the A
+//     planes hold the digits of the even / odd activations in the same order; the
+//     top plane is the signed top nibble of a_int (sdot8; codes 0..3 are also valid
+//     signed nibbles), the other five are unsigned (udot8).
+//   4-bit codes: the weight dword already holds eight codes as nibbles; the planes
+//     hold the digits of a_int + 2^23 (all unsigned), and the bias is removed
+//     exactly from the top plane's sum with sum(q) (udot8 against 0x11111111).
+// Per group and row:  P = sum_k a_int[k] q[k]  (planes combined in int32 and one
+// fp32 multiply-add), and the row partial gains  s * (P * 2^(e-22) - zp * sum_k a[k])
+// where sum_k a[k] is the fp32 group sum taken at staging.
+//
+// The work decomposition (lanes per row, lane -> chunk map, per-lane chunk order,
+// fixed xor butterfly, tiles, prefetch ring, LDS output buffer) is that of the
+// fp32 kernel in qmm_gemv_impl.h, so the summation order again depends only on
+// (K, block, bits).
+#pragma once
+#include "qmm_gemv_impl.h"
+
+namespace qmm {
+
+// LDS words of A planes per 16-byte chunk slot (padded so consecutive slots start
+// in different bank groups) and per dword of weights.
+template <int BITS>
+struct IpLayout {
+  static constexpr int WPD = 32 / BITS;                // codes per weight dword
+  static constexpr int PWD = BITS == 2 ? 12 : 6;       // plane words per weight dword
+  static constexpr int SLOT = 4 * PWD + 4;             // words per chunk slot (52 / 28)
+};
+
+// Stage chunks [c0, c0 + SC) of every A row as planes; meta[(m*4+gi)*SC + slot] =
+// {2^(e-22), sum a} for scale group gi of the slot.  A group whose largest |a| is
+// not finite gets a NaN step, so the rows it meets come out NaN.
+template <int BITS, int AT, int G>
+__device__ __forceinline__ void stage_planes(const GemvArgs& g, uint32_t* planes, f32x2* meta, int c0,
+                                             int SC) {
+  using L = IpLayout<BITS>;
+  constexpr int WPC = 128 / BITS;
+  const int per_row = SC * (WPC / 4);  // float4 pieces per A row in the slice
+  const int total = (int)g.M * per_row;
+  const int K = (int)g.K;
+  constexpr int gw = G / 4;  // threads per scale group (4, 8 or 16: aligned groups of lanes)
+  for (int base_idx = 0; base_idx < total; base_idx += blockDim.x) {
+    const int idx = base_idx + threadIdx.x;
+    const bool ok = idx < total;
+    const int m = ok ? idx / per_row : 0;
+    const int rem = idx - m * per_row;
+    const int slot = rem / (WPC / 4);
+    const int j4 = rem - slot * (WPC / 4);  // float4 piece inside the chunk
+    const int k = (c0 + slot) * WPC + 4 * j4;
+    const int64_t base = (int64_t)m * K + k;
+    float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (ok) {
+      if (g.a_vec && k + 3 < K) {
+        if constexpr (AT == QMM_F32) {
+          const f32x4 x = *(const f32x4*)((const float*)g.A + base);
+          v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+        } else {
+          const uint2 u = *(const uint2*)((const uint16_t*)g.A + base);
+          const uint32_t w[2] = {u.x, u.y};
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            if constexpr (AT == QMM_F16) {
+              v[2 * e] = f16_to_f32((uint16_t)(w[e] & 0xffffu));
+              v[2 * e + 1] = f16_to_f32((uint16_t)(w[e] >> 16));
+            } else {
+              v[2 * e] = __uint_as_float(w[e] << 16);
+              v[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+            }
+          }
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (k + e < K) ? load_elem<AT>(g.A, base + e) : 0.0f;
+      }
+    }
+    // group maximum and group sum (fixed xor butterfly over the gw threads)
+    float mx = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+    float sm = ((v[0] + v[1]) + v[2]) + v[3];
+    if (gw > 1) { mx = fmaxf(mx, swz_xor<1>(mx)); sm += swz_xor<1>(sm); }
+    if (gw > 2) { mx = fmaxf(mx, swz_xor<2>(mx)); sm += swz_xor<2>(sm); }
+    if (gw > 4) { mx = fmaxf(mx, swz_xor<4>(mx)); sm += swz_xor<4>(sm); }
+    if (gw > 8) { mx = fmaxf(mx, swz_xor<8>(mx)); sm += swz_xor<8>(sm); }
+    int e = 0;
+    (void)frexpf(mx, &e);  // mx < 2^e (mx = 0 gives e = 0)
+    if (!ok) continue;
+    int ai[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) ai[q] = (int)rintf(ldexpf(v[q], 22 - e));
+    uint32_t* slot_w = planes + (m * SC + slot) * L::SLOT;
+    if constexpr (BITS == 2) {
+      // elements j0..j0+3 of a 16-code dword: j0, j0+2 even (nibbles j0/2, j0/2+1 of
+      // the E word), j0+1, j0+3 odd (same nibbles of the O word)
+      const int d = (4 * j4) >> 4;
+      const int j0 = (4 * j4) & 15;
+      uint8_t* wb = (uint8_t*)(slot_w + d * L::PWD);
+#pragma unroll
+      for (int p = 0; p < 6; ++p) {
+        const uint32_t e0 = ((uint32_t)(ai[0] >> (4 * p))) & 15u;
+        const uint32_t o0 = ((uint32_t)(ai[1] >> (4 * p))) & 15u;
+        const uint32_t e1 = ((uint32_t)(ai[2] >> (4 * p))) & 15u;
+        const uint32_t o1 = ((uint32_t)(ai[3] >> (4 * p))) & 15u;
+        wb[(2 * p) * 4 + (j0 >> 2)] = (uint8_t)(e0 | (e1 << 4));
+        wb[(2 * p + 1) * 4 + (j0 >> 2)] = (uint8_t)(o0 | (o1 << 4));
+      }
+    } else {
+      // elements j0..j0+3 of an 8-code dword are nibbles j0..j0+3 of each plane word
+      const int d = (4 * j4) >> 3;
+      const int j0 = (4 * j4) & 7;
+      uint16_t* wh = (uint16_t*)(slot_w + d * L::PWD);
+#pragma unroll
+      for (int p = 0; p < 6; ++p) {
+        uint32_t h = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) h |= ((((uint32_t)(ai[q] + (1 << 23))) >> (4 * p)) & 15u) << (4 * q);
+        wh[p * 2 + (j0 >> 2)] = (uint16_t)h;
+      }
+    }
+    if ((j4 % gw) == 0) {
+      const int gi = j4 / gw;
+      f32x2 mt;
+      mt.x = mx <= 3.402823466e38f ? ldexpf(1.0f, e - 22) : __builtin_nanf("");
+      mt.y = sm;
+      meta[(m * 4 + gi) * SC + slot] = mt;
+    }
+  }
+}
+
+// DPG: weight dwords per scale group inside a chunk (4 = the chunk lies in one block).
+template <int BITS, int AT, int MT, int R, int DPG, int ZK>
+__global__ __launch_bounds__(kGemvThreads) void gemv_ip_kernel(GemvArgs g) {
+  using L = IpLayout<BITS>;
+  constexpr int WPC = 128 / BITS;
+  constexpr int G = DPG * L::WPD;  // codes per scale group inside a chunk
+  constexpr int NS = 4 / DPG;      // scale groups per chunk
+  constexpr int NWAVES = kGemvThreads / 64;
+  extern __shared__ float lds[];
+  const int SC = g.slice_chunks;
+  uint32_t* planes = (uint32_t*)lds;
+  f32x2* meta = (f32x2*)(planes + MT * SC * L::SLOT);
+  float* out_lds = (float*)(meta + MT * 4 * SC);
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int lpr_log2 = g.lpr_log2;
+  const int LPR = 1 << lpr_log2;
+  const int lp = lane & (LPR - 1);
+  const int sub = lane >> lpr_log2;
+  const int SUBS = 64 >> lpr_log2;
+  const int rows_per_wave = SUBS * R;
+  const int rows_per_tile = NWAVES * rows_per_wave;
+  const int N = (int)g.N;
+  const int M = (int)g.M;
+  const int ntiles = (N + rows_per_tile - 1) / rows_per_tile;
+  const int tiles_lo = ntiles / gridDim.x, extra = ntiles % gridDim.x;
+  const int t_begin = blockIdx.x * tiles_lo + (blockIdx.x < extra ? blockIdx.x : extra);
+  const int t_end = t_begin + tiles_lo + (blockIdx.x < extra ? 1 : 0);
+  if (t_begin >= t_end) return;
+  const int nchunks = (int)g.nchunks;
+  const int nslices = (nchunks + SC - 1) / SC;
+  const int iters = SC >> lpr_log2;
+  const int nblk = (int)g.nblk;
+  const int blog = g.block_log2;
+  const int64_t row_bytes = g.row_bytes;
+  const float zconst = g.zp_kind == QMM_ZP_UNIFORM ? g.uniform_zp : (float)(1 << (BITS - 1));
+  const int zrow_bytes = (int)g.zp_row_bytes;
+  int out_tiles = kGemvOutFloats / (rows_per_tile * MT);
+  if (out_tiles < 1) out_tiles = 1;
+
+  auto advance = [&](ItemPos& p) {
+    if (++p.it == iters) {
+      p.it = 0;
+      if (++p.s == nslices) {
+        p.s = 0;
+        ++p.tile;
+      }
+    }
+  };
+  ItemPos fpos{t_begin, 0, 0};
+  int fchunk = lp;
+  const uint8_t* fw[R];
+  const uint16_t* fsa[R];
+  const uint8_t* fzp[R];
+  const uint16_t* fzh[R];
+  auto set_bases = [&](int tl) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      int row = tl * rows_per_tile + wave * rows_per_wave + r * SUBS + sub;
+      row = (tl < t_end && row < N) ? row : N - 1;
+      fw[r] = g.W + (int64_t)row * row_bytes;
+      fsa[r] = g.scales + (int64_t)row * nblk;
+      if constexpr (ZK == 1) fzp[r] = (const uint8_t*)g.zp + (int64_t)row * zrow_bytes;
+      if constexpr (ZK == 2) fzh[r] = (const uint16_t*)g.zp + (int64_t)row * nblk;
+    }
+  };
+  set_bases(t_begin);
+  auto fetch_next = [&](ItemBuf<R, NS>& b) {
+    const int cc = (fpos.tile < t_end && fchunk < nchunks) ? fchunk : nchunks - 1;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      b.w[r] = *(const uint4*)(fw[r] + cc * 16);
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        const int bidx = (cc * WPC + i * G) >> blog;
+        b.s[r][i] = f16_to_f32(fsa[r][bidx]);
+        if constexpr (ZK == 1) {
+          const int bit = bidx * BITS;
+          b.z[r][i] = (float)((fzp[r][bit >> 3] >> (bit & 7)) & ((1u << BITS) - 1u));
+        } else if constexpr (ZK == 2) {
+          b.z[r][i] = f16_to_f32(fzh[r][bidx]);
+        } else {
+          b.z[r][i] = zconst;
+        }
+      }
+    }
+    const int old_tile = fpos.tile;
+    advance(fpos);
+    if (fpos.tile != old_tile) {
+      fchunk = lp;
+      set_bases(fpos.tile);
+    } else {
+      fchunk = fpos.s * SC + fpos.it * LPR + lp;
+    }
+  };
+  auto flush = [&](int tf, int tl) {
+    __syncthreads();
+    const int nrows = (tl - tf) * rows_per_tile;
+    const int row0 = tf * rows_per_tile;
+    for (int i = threadIdx.x; i < nrows * M; i += blockDim.x) {
+      const int m = i / nrows;
+      const int lr = i - m * nrows;
+      const int row = row0 + lr;
+      if (row < N) {
+        float v = out_lds[lr * MT + m];
+        if (g.bias) v += load_elem_rt(g.bias, g.c_type, row);
+        store_elem_rt(g.C, g.c_type, (int64_t)m * N + row, v);
+      }
+    }
+    __syncthreads();
+  };
+
+  float acc[R][MT];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[r][m] = 0.0f;
+
+  ItemPos cur{t_begin, 0, 0};
+  bool staged = false;
+  int flush_from = t_begin;
+  bool done = false;
+
+  auto step = [&](ItemBuf<R, NS>& cbuf, ItemBuf<R, NS>& nxt) {
+    if (cur.it == 0 && (nslices > 1 || !staged)) {
+      __syncthreads();
+      stage_planes<BITS, AT, G>(g, planes, meta, cur.s * SC, SC);
+      __syncthreads();
+      staged = true;
+    }
+    fetch_next(nxt);
+
+    const int slot = cur.it * LPR + lp;
+    if (cur.s * SC + slot < nchunks) {
+      const uint32_t* pb = planes + slot * L::SLOT;
+      int S[R][MT][6];
+      int Sq[R];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        if (d % DPG == 0) {
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            Sq[r] = 0;
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+              for (int p = 0; p < 6; ++p) S[r][m][p] = 0;
+          }
+        }
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          const int mm = m < M ? m : 0;
+          const uint32_t* pw = pb + mm * SC * L::SLOT + d * L::PWD;
+          uint32_t pl[L::PWD];
+          if constexpr (BITS == 2) {
+            const uint4 a0 = ((const uint4*)pw)[0], a1 = ((const uint4*)pw)[1], a2 = ((const uint4*)pw)[2];
+            pl[0] = a0.x; pl[1] = a0.y; pl[2] = a0.z; pl[3] = a0.w;
+            pl[4] = a1.x; pl[5] = a1.y; pl[6] = a1.z; pl[7] = a1.w;
+            pl[8] = a2.x; pl[9] = a2.y; pl[10] = a2.z; pl[11] = a2.w;
+          } else {
+            const uint4 a0 = *(const uint4*)pw;
+            const uint2 a1 = *(const uint2*)(pw + 4);
+            pl[0] = a0.x; pl[1] = a0.y; pl[2] = a0.z; pl[3] = a0.w;
+            pl[4] = a1.x; pl[5] = a1.y;
+          }
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            const uint32_t x = d == 0 ? cbuf.w[r].x : d == 1 ? cbuf.w[r].y : d == 2 ? cbuf.w[r].z : cbuf.w[r].w;
+            if constexpr (BITS == 2) {
+              const uint32_t ev = x & 0x33333333u;
+              const uint32_t od = (x >> 2) & 0x33333333u;
+#pragma unroll
+              for (int p = 0; p < 5; ++p) {
+                S[r][m][p] = (int)__builtin_amdgcn_udot8(ev, pl[2 * p], (uint32_t)S[r][m][p], false);
+                S[r][m][p] = (int)__builtin_amdgcn_udot8(od, pl[2 * p + 1], (uint32_t)S[r][m][p], false);
+              }
+              S[r][m][5] = __builtin_amdgcn_sdot8((int)ev, (int)pl[10], S[r][m][5], false);
+              S[r][m][5] = __builtin_amdgcn_sdot8((int)od, (int)pl[11], S[r][m][5], false);
+            } else {
+#pragma unroll
+              for (int p = 0; p < 6; ++p)
+                S[r][m][p] = (int)__builtin_amdgcn_udot8(x, pl[p], (uint32_t)S[r][m][p], false);
+              if (m == 0) Sq[r] = (int)__builtin_amdgcn_udot8(x, 0x11111111u, (uint32_t)Sq[r], false);
+            }
+          }
+        }
+        if ((d + 1) % DPG == 0) {
+          const int gi = d / DPG;
+#pragma unroll
+          for (int m = 0; m < MT; ++m) {
+            const int mm = m < M ? m : 0;
+            const f32x2 mt = meta[(mm * 4 + gi) * SC + slot];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+              int s5 = S[r][m][5];
+              if constexpr (BITS == 4) s5 -= 8 * Sq[r];  // remove the 2^23 bias of a_int
+              // both halves stay below 2^24 in magnitude, so P is rounded once
+              const int lo = S[r][m][0] + (S[r][m][1] << 4) + (S[r][m][2] << 8);
+              const int hi = S[r][m][3] + (S[r][m][4] << 4) + s5 * 256;
+              const float P = fmaf((float)hi, 4096.0f, (float)lo);
+              const float scv = cbuf.s[r][gi];
+              const float z = cbuf.z[r][gi];
+              // same expression for every zero-point kind, so a uniform scalar and
+              // a tensor holding that value give the same bits
+              acc[r][m] = fmaf(scv, fmaf(-z, mt.y, P * mt.x), acc[r][m]);
+            }
+          }
+        }
+      }
+    }
+
+    if (cur.s == nslices - 1 && cur.it == iters - 1) {
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) acc[r][m] = group_sum(acc[r][m], LPR);
+      if (lp == 0) {
+        const int lt = cur.tile - flush_from;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const int lr = lt * rows_per_tile + wave * rows_per_wave + r * SUBS + sub;
+#pragma unroll
+          for (int m = 0; m < MT; ++m) out_lds[lr * MT + m] = acc[r][m];
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) acc[r][m] = 0.0f;
+      if (cur.tile + 1 == t_end || cur.tile + 1 - flush_from == out_tiles) {
+        flush(flush_from, cur.tile + 1);
+        flush_from = cur.tile + 1;
+      }
+      done = cur.tile + 1 == t_end;
+    }
+    advance(cur);
+  };
+
+  ItemBuf<R, NS> b0, b1, b2;
+  fetch_next(b0);
+  fetch_next(b1);
+  while (true) {
+    step(b0, b2);
+    if (done) break;
+    step(b1, b0);
+    if (done) break;
+    step(b2, b1);
+    if (done) break;
+  }
+}
+
+template <int BITS, int AT, int MT, int R, int DPG, int ZK>
+static hipError_t launch_ip_one(const GemvArgs& g, hipStream_t st) {
+  const int subs = 64 >> g.lpr_log2;
+  const int64_t rows_per_tile = (int64_t)(kGemvThreads / 64) * subs * R;
+  const int64_t ntiles = (g.N + rows_per_tile - 1) / rows_per_tile;
+  int64_t grid = (int64_t)g.num_cus * g.wg_per_cu;
+  if (grid > ntiles) grid = ntiles;
+  if (grid < 1) grid = 1;
+  const size_t lds = g.lds_bytes + kGemvOutFloats * sizeof(float);
+  auto kern = gemv_ip_kernel<BITS, AT, MT, R, DPG, ZK>;
+  allow_large_lds(kern, lds);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kGemvThreads), lds, st, g);
+  return hipSuccess;
+}
+
+template <int BITS, int AT, int DPG, int ZK>
+static hipError_t launch_ip_mr(const GemvArgs& g, int R, hipStream_t st) {
+  switch (g.mt) {
+    case 1:
+      if (R == 1) return launch_ip_one<BITS, AT, 1, 1, DPG, ZK>(g, st);
+      if (R == 2) return launch_ip_one<BITS, AT, 1, 2, DPG, ZK>(g, st);
+      return launch_ip_one<BITS, AT, 1, 4, DPG, ZK>(g, st);
+    case 2:
+      if (R == 1) return launch_ip_one<BITS, AT, 2, 1, DPG, ZK>(g, st);
+      return launch_ip_one<BITS, AT, 2, 2, DPG, ZK>(g, st);
+    case 4:
+      if (R == 1) return launch_ip_one<BITS, AT, 4, 1, DPG, ZK>(g, st);
+      return launch_ip_one<BITS, AT, 4, 2, DPG, ZK>(g, st);
+    default:
+      return launch_ip_one<BITS, AT, 8, 1, DPG, ZK>(g, st);
+  }
+}
+
+template <int BITS, int AT, int DPG>
+static hipError_t launch_ip_zk(const GemvArgs& g, int R, hipStream_t st) {
+  if (g.zp_kind == QMM_ZP_PACKED) return launch_ip_mr<BITS, AT, DPG, 1>(g, R, st);
+  if (g.zp_kind == QMM_ZP_F16) return launch_ip_mr<BITS, AT, DPG, 2>(g, R, st);
+  return launch_ip_mr<BITS, AT, DPG, 0>(g, R, st);
+}
+
+template <int BITS, int AT>
+hipError_t launch_ip_at_type(const GemvArgs& g, int R, hipStream_t st) {
+  constexpr int WPD = 32 / BITS;
+  // dwords per scale group: min(block, codes per chunk) / codes per dword
+  const int dpg = g.block >= 4 * WPD ? 4 : g.block / WPD;
+  if constexpr (BITS == 2) {
+    if (dpg == 1) return launch_ip_zk<BITS, AT, 1>(g, R, st);
+  }
+  if (dpg == 2) return launch_ip_zk<BITS, AT, 2>(g, R, st);
+  return launch_ip_zk<BITS, AT, 4>(g, R, st);
+}
+
+}  // namespace qmm

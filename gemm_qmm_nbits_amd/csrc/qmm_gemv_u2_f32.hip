@@ -1,6 +1,6 @@
-// Instantiation of the GEMV kernels for one weight format and activation type.
-#include "qmm_gemv_impl.h"
+// Instantiation of the integer-plane GEMV for 2-bit affine weights and f32 activations.
+#include "qmm_gemv_ip.h"
 
 namespace qmm {
-template hipError_t launch_at_type<GEMV_AFFINE, 2, QMM_F32>(const GemvArgs& g, int R, hipStream_t st);
+template hipError_t launch_ip_at_type<2, QMM_F32>(const GemvArgs& g, int R, hipStream_t st);
 }  // namespace qmm

@@ -1,6 +1,6 @@
-// Instantiation of the GEMV kernels for one weight format and activation type.
-#include "qmm_gemv_impl.h"
+// Instantiation of the integer-plane GEMV for 4-bit affine weights and f16 activations.
+#include "qmm_gemv_ip.h"
 
 namespace qmm {
-template hipError_t launch_at_type<GEMV_AFFINE, 4, QMM_F16>(const GemvArgs& g, int R, hipStream_t st);
+template hipError_t launch_ip_at_type<4, QMM_F16>(const GemvArgs& g, int R, hipStream_t st);
 }  // namespace qmm
