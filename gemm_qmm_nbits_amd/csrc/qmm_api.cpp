@@ -525,7 +525,7 @@ GemvArgs make_gemv(const void* A, int a_type, int64_t M, int64_t K, int64_t N, c
   g.C = C;
   g.c_type = c_type;
   g.chunked = (g.row_bytes % 16 == 0) && aligned(W, 16);
-  g.lpr_log2 = gemv_lanes_per_row_log2(g.nchunks);
+  g.lpr_log2 = gemv_row_lanes_log2(g.nchunks, N);
   g.a_vec = aligned(A, 16) && (K % 4 == 0);
   return g;
 }

@@ -86,6 +86,30 @@ int gemv_lanes_per_row_log2(int64_t nchunks) {
   return best;
 }
 
+int gemv_row_lanes_log2(int64_t nchunks, int64_t N) {
+  // Lanes per row for the GEMV: the group width with the best product of lane
+  // efficiency (busy lane slots / all slots of a row) and parallelism (row tiles of
+  // one 8-wave work-group, relative to a fixed 512), ties to the wider group.  A
+  // function of the shape only, so every device and every tiling candidate use the
+  // same summation order.
+  int best = 6;
+  double best_score = -1.0;
+  for (int l = 6; l >= 3; --l) {
+    const int64_t lpr = 1LL << l;
+    const int64_t slots = ((nchunks + lpr - 1) / lpr) * lpr;
+    const double eff = slots > 0 ? (double)nchunks / (double)slots : 0.0;
+    const int64_t rows_per_tile = 8 * (64 / lpr);
+    const int64_t tiles = (N + rows_per_tile - 1) / rows_per_tile;
+    const double par = tiles >= 512 ? 1.0 : (double)tiles / 512.0;
+    const double score = eff * par;
+    if (score > best_score + 1e-12) {
+      best_score = score;
+      best = l;
+    }
+  }
+  return best;
+}
+
 void gemv_plan(GemvArgs& g, int num_cus) {
   g.mt = g.M <= 1 ? 1 : g.M <= 2 ? 2 : g.M <= 4 ? 4 : 8;
   g.num_cus = num_cus > 0 ? num_cus : 256;

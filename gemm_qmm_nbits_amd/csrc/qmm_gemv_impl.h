@@ -19,6 +19,10 @@
 #include "qmm_device.h"
 #include "qmm_internal.h"
 
+#include <map>
+#include <mutex>
+#include <utility>
+
 namespace qmm {
 
 // --- decoding four bytes (one dword) of codes into fp32 ------------------------
@@ -434,6 +438,29 @@ static void allow_large_lds(K kernel, size_t lds) {
   if (lds > 64 * 1024)
     (void)hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)kMaxGemvLds);
+}
+
+// Work-groups of `kern` (`threads` threads, `lds` bytes of dynamic LDS) that can be
+// resident on one compute unit; cached per (kernel, LDS size).
+template <typename K>
+static int resident_per_cu(K kern, int threads, size_t lds) {
+  static std::mutex mu;
+  static std::map<std::pair<const void*, size_t>, int> cache;
+  const auto key = std::make_pair((const void*)kern, lds);
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+  }
+  allow_large_lds(kern, lds);
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, threads, lds) != hipSuccess || n < 1) {
+    (void)hipGetLastError();
+    n = 1;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  cache[key] = n;
+  return n;
 }
 
 template <int FMT, int BITS, int AT, int MT, int R, int MULTI, int ZK>

@@ -29,6 +29,23 @@
 
 namespace qmm {
 
+#ifndef QMM_IP_DEPTH
+#define QMM_IP_DEPTH 2
+#endif
+constexpr int kIpDepth = QMM_IP_DEPTH;  // items per lane whose loads are in flight
+
+// Raw loads of one work item of one lane: R rows x one 16-byte chunk, NS scales and
+// zero points per row.  They are kept as loaded and decoded where they are used,
+// so nothing between a prefetch and its use has to wait for the load.
+template <int R, int NS>
+struct IpBuf {
+  uint4 w[R];
+  _Float16 s[R][NS];    // scale
+  _Float16 zh[R][NS];   // fp16 zero point
+  uint32_t z[R][NS];    // packed zero-point byte
+  uint32_t zsh[R][NS];  // bit offset of the code in the packed zero-point byte
+};
+
 // LDS words of A planes per 16-byte chunk slot (padded so consecutive slots start
 // in different bank groups) and per dword of weights.
 template <int BITS>
@@ -46,96 +63,113 @@ __device__ __forceinline__ void stage_planes(const GemvArgs& g, uint32_t* planes
                                              int SC) {
   using L = IpLayout<BITS>;
   constexpr int WPC = 128 / BITS;
+  constexpr int NB = 4;  // float4 pieces per thread whose loads are issued together
   const int per_row = SC * (WPC / 4);  // float4 pieces per A row in the slice
   const int total = (int)g.M * per_row;
   const int K = (int)g.K;
   constexpr int gw = G / 4;  // threads per scale group (4, 8 or 16: aligned groups of lanes)
-  for (int base_idx = 0; base_idx < total; base_idx += blockDim.x) {
-    const int idx = base_idx + threadIdx.x;
-    const bool ok = idx < total;
-    const int m = ok ? idx / per_row : 0;
+  auto load = [&](int idx, float (&v)[4]) {
+    v[0] = v[1] = v[2] = v[3] = 0.0f;
+    if (idx >= total) return;
+    const int m = idx / per_row;
     const int rem = idx - m * per_row;
-    const int slot = rem / (WPC / 4);
-    const int j4 = rem - slot * (WPC / 4);  // float4 piece inside the chunk
-    const int k = (c0 + slot) * WPC + 4 * j4;
+    const int k = (c0 * WPC) + 4 * rem;
     const int64_t base = (int64_t)m * K + k;
-    float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (ok) {
-      if (g.a_vec && k + 3 < K) {
-        if constexpr (AT == QMM_F32) {
-          const f32x4 x = *(const f32x4*)((const float*)g.A + base);
-          v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
-        } else {
-          const uint2 u = *(const uint2*)((const uint16_t*)g.A + base);
-          const uint32_t w[2] = {u.x, u.y};
+    if (g.a_vec && k + 3 < K) {
+      if constexpr (AT == QMM_F32) {
+        const f32x4 x = *(const f32x4*)((const float*)g.A + base);
+        v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+      } else {
+        const uint2 u = *(const uint2*)((const uint16_t*)g.A + base);
+        const uint32_t w[2] = {u.x, u.y};
 #pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            if constexpr (AT == QMM_F16) {
-              v[2 * e] = f16_to_f32((uint16_t)(w[e] & 0xffffu));
-              v[2 * e + 1] = f16_to_f32((uint16_t)(w[e] >> 16));
-            } else {
-              v[2 * e] = __uint_as_float(w[e] << 16);
-              v[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
-            }
+        for (int e = 0; e < 2; ++e) {
+          if constexpr (AT == QMM_F16) {
+            v[2 * e] = f16_to_f32((uint16_t)(w[e] & 0xffffu));
+            v[2 * e + 1] = f16_to_f32((uint16_t)(w[e] >> 16));
+          } else {
+            v[2 * e] = __uint_as_float(w[e] << 16);
+            v[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
           }
         }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = (k + e < K) ? load_elem<AT>(g.A, base + e) : 0.0f;
-      }
-    }
-    // group maximum and group sum (fixed xor butterfly over the gw threads)
-    float mx = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
-    float sm = ((v[0] + v[1]) + v[2]) + v[3];
-    if (gw > 1) { mx = fmaxf(mx, swz_xor<1>(mx)); sm += swz_xor<1>(sm); }
-    if (gw > 2) { mx = fmaxf(mx, swz_xor<2>(mx)); sm += swz_xor<2>(sm); }
-    if (gw > 4) { mx = fmaxf(mx, swz_xor<4>(mx)); sm += swz_xor<4>(sm); }
-    if (gw > 8) { mx = fmaxf(mx, swz_xor<8>(mx)); sm += swz_xor<8>(sm); }
-    int e = 0;
-    (void)frexpf(mx, &e);  // mx < 2^e (mx = 0 gives e = 0)
-    if (!ok) continue;
-    int ai[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) ai[q] = (int)rintf(ldexpf(v[q], 22 - e));
-    uint32_t* slot_w = planes + (m * SC + slot) * L::SLOT;
-    if constexpr (BITS == 2) {
-      // elements j0..j0+3 of a 16-code dword: j0, j0+2 even (nibbles j0/2, j0/2+1 of
-      // the E word), j0+1, j0+3 odd (same nibbles of the O word)
-      const int d = (4 * j4) >> 4;
-      const int j0 = (4 * j4) & 15;
-      uint8_t* wb = (uint8_t*)(slot_w + d * L::PWD);
-#pragma unroll
-      for (int p = 0; p < 6; ++p) {
-        const uint32_t e0 = ((uint32_t)(ai[0] >> (4 * p))) & 15u;
-        const uint32_t o0 = ((uint32_t)(ai[1] >> (4 * p))) & 15u;
-        const uint32_t e1 = ((uint32_t)(ai[2] >> (4 * p))) & 15u;
-        const uint32_t o1 = ((uint32_t)(ai[3] >> (4 * p))) & 15u;
-        wb[(2 * p) * 4 + (j0 >> 2)] = (uint8_t)(e0 | (e1 << 4));
-        wb[(2 * p + 1) * 4 + (j0 >> 2)] = (uint8_t)(o0 | (o1 << 4));
       }
     } else {
-      // elements j0..j0+3 of an 8-code dword are nibbles j0..j0+3 of each plane word
-      const int d = (4 * j4) >> 3;
-      const int j0 = (4 * j4) & 7;
-      uint16_t* wh = (uint16_t*)(slot_w + d * L::PWD);
 #pragma unroll
-      for (int p = 0; p < 6; ++p) {
-        uint32_t h = 0;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) h |= ((((uint32_t)(ai[q] + (1 << 23))) >> (4 * p)) & 15u) << (4 * q);
-        wh[p * 2 + (j0 >> 2)] = (uint16_t)h;
-      }
+      for (int e = 0; e < 4; ++e) v[e] = (k + e < K) ? load_elem<AT>(g.A, base + e) : 0.0f;
     }
-    if ((j4 % gw) == 0) {
-      const int gi = j4 / gw;
-      f32x2 mt;
-      mt.x = mx <= 3.402823466e38f ? ldexpf(1.0f, e - 22) : __builtin_nanf("");
-      mt.y = sm;
-      meta[(m * 4 + gi) * SC + slot] = mt;
+  };
+  // NB rounds of pieces at a time: all loads first (one memory latency per batch),
+  // then the conversion; every lane takes part in the group butterflies
+  for (int base_idx = 0; base_idx < total; base_idx += NB * (int)blockDim.x) {
+    float vb[NB][4];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) load(base_idx + j * (int)blockDim.x + (int)threadIdx.x, vb[j]);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      if (base_idx + j * (int)blockDim.x >= total) break;  // uniform over the work-group
+      const int idx = base_idx + j * (int)blockDim.x + (int)threadIdx.x;
+      const bool ok = idx < total;
+      const float* v = vb[j];
+      const int m = ok ? idx / per_row : 0;
+      const int rem = idx - m * per_row;
+      const int slot = rem / (WPC / 4);
+      const int j4 = rem - slot * (WPC / 4);  // float4 piece inside the chunk
+      // group maximum and group sum (fixed xor butterfly over the gw threads)
+      float mx = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+      float sm = ((v[0] + v[1]) + v[2]) + v[3];
+      if (gw > 1) { mx = fmaxf(mx, swz_xor<1>(mx)); sm += swz_xor<1>(sm); }
+      if (gw > 2) { mx = fmaxf(mx, swz_xor<2>(mx)); sm += swz_xor<2>(sm); }
+      if (gw > 4) { mx = fmaxf(mx, swz_xor<4>(mx)); sm += swz_xor<4>(sm); }
+      if (gw > 8) { mx = fmaxf(mx, swz_xor<8>(mx)); sm += swz_xor<8>(sm); }
+      int e = 0;
+      (void)frexpf(mx, &e);  // mx < 2^e (mx = 0 gives e = 0)
+      if (!ok) continue;
+      int ai[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) ai[q] = (int)rintf(ldexpf(v[q], 22 - e));
+      uint32_t* slot_w = planes + (m * SC + slot) * L::SLOT;
+      if constexpr (BITS == 2) {
+        // elements j0..j0+3 of a 16-code dword: j0, j0+2 even (nibbles j0/2, j0/2+1 of
+        // the E word), j0+1, j0+3 odd (same nibbles of the O word)
+        const int d = (4 * j4) >> 4;
+        const int j0 = (4 * j4) & 15;
+        uint8_t* wb = (uint8_t*)(slot_w + d * L::PWD);
+#pragma unroll
+        for (int p = 0; p < 6; ++p) {
+          const uint32_t e0 = ((uint32_t)(ai[0] >> (4 * p))) & 15u;
+          const uint32_t o0 = ((uint32_t)(ai[1] >> (4 * p))) & 15u;
+          const uint32_t e1 = ((uint32_t)(ai[2] >> (4 * p))) & 15u;
+          const uint32_t o1 = ((uint32_t)(ai[3] >> (4 * p))) & 15u;
+          wb[(2 * p) * 4 + (j0 >> 2)] = (uint8_t)(e0 | (e1 << 4));
+          wb[(2 * p + 1) * 4 + (j0 >> 2)] = (uint8_t)(o0 | (o1 << 4));
+        }
+      } else {
+        // elements j0..j0+3 of an 8-code dword are nibbles j0..j0+3 of each plane word
+        const int d = (4 * j4) >> 3;
+        const int j0 = (4 * j4) & 7;
+        uint16_t* wh = (uint16_t*)(slot_w + d * L::PWD);
+#pragma unroll
+        for (int p = 0; p < 6; ++p) {
+          uint32_t h = 0;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) h |= ((((uint32_t)(ai[q] + (1 << 23))) >> (4 * p)) & 15u) << (4 * q);
+          wh[p * 2 + (j0 >> 2)] = (uint16_t)h;
+        }
+      }
+      if ((j4 % gw) == 0) {
+        const int gi = j4 / gw;
+        f32x2 mt;
+        mt.x = mx <= 3.402823466e38f ? ldexpf(1.0f, e - 22) : __builtin_nanf("");
+        mt.y = sm;
+        meta[(m * 4 + gi) * SC + slot] = mt;
+      }
     }
   }
 }
 
+// General form (A staged one K-slice at a time inside the item loop, row sums
+// written out whenever the LDS buffer fills); qmm_gemv_stream.h holds the
+// streaming form for rows whose activations fit in LDS whole.
 // DPG: weight dwords per scale group inside a chunk (4 = the chunk lies in one block).
 template <int BITS, int AT, int MT, int R, int DPG, int ZK>
 __global__ __launch_bounds__(kGemvThreads) void gemv_ip_kernel(GemvArgs g) {
@@ -188,22 +222,22 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_ip_kernel(GemvArgs g) {
   ItemPos fpos{t_begin, 0, 0};
   int fchunk = lp;
   const uint8_t* fw[R];
-  const uint16_t* fsa[R];
+  const _Float16* fsa[R];
   const uint8_t* fzp[R];
-  const uint16_t* fzh[R];
+  const _Float16* fzh[R];
   auto set_bases = [&](int tl) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       int row = tl * rows_per_tile + wave * rows_per_wave + r * SUBS + sub;
       row = (tl < t_end && row < N) ? row : N - 1;
       fw[r] = g.W + (int64_t)row * row_bytes;
-      fsa[r] = g.scales + (int64_t)row * nblk;
+      fsa[r] = (const _Float16*)g.scales + (int64_t)row * nblk;
       if constexpr (ZK == 1) fzp[r] = (const uint8_t*)g.zp + (int64_t)row * zrow_bytes;
-      if constexpr (ZK == 2) fzh[r] = (const uint16_t*)g.zp + (int64_t)row * nblk;
+      if constexpr (ZK == 2) fzh[r] = (const _Float16*)g.zp + (int64_t)row * nblk;
     }
   };
   set_bases(t_begin);
-  auto fetch_next = [&](ItemBuf<R, NS>& b) {
+  auto fetch_next = [&](IpBuf<R, NS>& b) {
     const int cc = (fpos.tile < t_end && fchunk < nchunks) ? fchunk : nchunks - 1;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -211,14 +245,13 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_ip_kernel(GemvArgs g) {
 #pragma unroll
       for (int i = 0; i < NS; ++i) {
         const int bidx = (cc * WPC + i * G) >> blog;
-        b.s[r][i] = f16_to_f32(fsa[r][bidx]);
+        b.s[r][i] = fsa[r][bidx];
         if constexpr (ZK == 1) {
           const int bit = bidx * BITS;
-          b.z[r][i] = (float)((fzp[r][bit >> 3] >> (bit & 7)) & ((1u << BITS) - 1u));
+          b.z[r][i] = fzp[r][bit >> 3];
+          b.zsh[r][i] = bit & 7;
         } else if constexpr (ZK == 2) {
-          b.z[r][i] = f16_to_f32(fzh[r][bidx]);
-        } else {
-          b.z[r][i] = zconst;
+          b.zh[r][i] = fzh[r][bidx];
         }
       }
     }
@@ -257,10 +290,11 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_ip_kernel(GemvArgs g) {
   ItemPos cur{t_begin, 0, 0};
   bool staged = false;
   int flush_from = t_begin;
-  bool done = false;
+  // items of every lane of this work-group; `live` is uniform over the work-group
+  const int total_items = (t_end - t_begin) * nslices * iters;
 
-  auto step = [&](ItemBuf<R, NS>& cbuf, ItemBuf<R, NS>& nxt) {
-    if (cur.it == 0 && (nslices > 1 || !staged)) {
+  auto step = [&](IpBuf<R, NS>& cbuf, IpBuf<R, NS>& nxt, bool live) {
+    if (live && cur.it == 0 && (nslices > 1 || !staged)) {
       __syncthreads();
       stage_planes<BITS, AT, G>(g, planes, meta, cur.s * SC, SC);
       __syncthreads();
@@ -268,8 +302,11 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_ip_kernel(GemvArgs g) {
     }
     fetch_next(nxt);
 
+    // computed for every lane (no branch around it, so the register sets of the
+    // ring stay in flight on every path); chunks past the row end are discarded
     const int slot = cur.it * LPR + lp;
-    if (cur.s * SC + slot < nchunks) {
+    const bool valid = live && cur.s * SC + slot < nchunks;
+    {
       const uint32_t* pb = planes + slot * L::SLOT;
       int S[R][MT][6];
       int Sq[R];
@@ -336,18 +373,22 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_ip_kernel(GemvArgs g) {
               const int lo = S[r][m][0] + (S[r][m][1] << 4) + (S[r][m][2] << 8);
               const int hi = S[r][m][3] + (S[r][m][4] << 4) + s5 * 256;
               const float P = fmaf((float)hi, 4096.0f, (float)lo);
-              const float scv = cbuf.s[r][gi];
-              const float z = cbuf.z[r][gi];
+              const float scv = (float)cbuf.s[r][gi];
+              float z;
+              if constexpr (ZK == 1) z = (float)((cbuf.z[r][gi] >> cbuf.zsh[r][gi]) & ((1u << BITS) - 1u));
+              else if constexpr (ZK == 2) z = (float)cbuf.zh[r][gi];
+              else z = zconst;
               // same expression for every zero-point kind, so a uniform scalar and
               // a tensor holding that value give the same bits
-              acc[r][m] = fmaf(scv, fmaf(-z, mt.y, P * mt.x), acc[r][m]);
+              const float nv = fmaf(scv, fmaf(-z, mt.y, P * mt.x), acc[r][m]);
+              acc[r][m] = valid ? nv : acc[r][m];
             }
           }
         }
       }
     }
 
-    if (cur.s == nslices - 1 && cur.it == iters - 1) {
+    if (live && cur.s == nslices - 1 && cur.it == iters - 1) {
 #pragma unroll
       for (int r = 0; r < R; ++r)
 #pragma unroll
@@ -369,74 +410,21 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_ip_kernel(GemvArgs g) {
         flush(flush_from, cur.tile + 1);
         flush_from = cur.tile + 1;
       }
-      done = cur.tile + 1 == t_end;
     }
     advance(cur);
   };
 
-  ItemBuf<R, NS> b0, b1, b2;
-  fetch_next(b0);
-  fetch_next(b1);
-  while (true) {
-    step(b0, b2);
-    if (done) break;
-    step(b1, b0);
-    if (done) break;
-    step(b2, b1);
-    if (done) break;
+  // ring of kIpDepth register sets; the loop body is unrolled so that set indices
+  // are constants and the sets rotate without copies
+  IpBuf<R, NS> buf[kIpDepth];
+#pragma unroll
+  for (int i = 0; i < kIpDepth - 1; ++i) fetch_next(buf[i]);
+  // whole rounds of kIpDepth steps; steps past the last item only issue clamped
+  // loads and discard their results
+  for (int base = 0; base < total_items; base += kIpDepth) {
+#pragma unroll
+    for (int i = 0; i < kIpDepth; ++i) step(buf[i], buf[(i + kIpDepth - 1) % kIpDepth], base + i < total_items);
   }
-}
-
-template <int BITS, int AT, int MT, int R, int DPG, int ZK>
-static hipError_t launch_ip_one(const GemvArgs& g, hipStream_t st) {
-  const int subs = 64 >> g.lpr_log2;
-  const int64_t rows_per_tile = (int64_t)(kGemvThreads / 64) * subs * R;
-  const int64_t ntiles = (g.N + rows_per_tile - 1) / rows_per_tile;
-  int64_t grid = (int64_t)g.num_cus * g.wg_per_cu;
-  if (grid > ntiles) grid = ntiles;
-  if (grid < 1) grid = 1;
-  const size_t lds = g.lds_bytes + kGemvOutFloats * sizeof(float);
-  auto kern = gemv_ip_kernel<BITS, AT, MT, R, DPG, ZK>;
-  allow_large_lds(kern, lds);
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kGemvThreads), lds, st, g);
-  return hipSuccess;
-}
-
-template <int BITS, int AT, int DPG, int ZK>
-static hipError_t launch_ip_mr(const GemvArgs& g, int R, hipStream_t st) {
-  switch (g.mt) {
-    case 1:
-      if (R == 1) return launch_ip_one<BITS, AT, 1, 1, DPG, ZK>(g, st);
-      if (R == 2) return launch_ip_one<BITS, AT, 1, 2, DPG, ZK>(g, st);
-      return launch_ip_one<BITS, AT, 1, 4, DPG, ZK>(g, st);
-    case 2:
-      if (R == 1) return launch_ip_one<BITS, AT, 2, 1, DPG, ZK>(g, st);
-      return launch_ip_one<BITS, AT, 2, 2, DPG, ZK>(g, st);
-    case 4:
-      if (R == 1) return launch_ip_one<BITS, AT, 4, 1, DPG, ZK>(g, st);
-      return launch_ip_one<BITS, AT, 4, 2, DPG, ZK>(g, st);
-    default:
-      return launch_ip_one<BITS, AT, 8, 1, DPG, ZK>(g, st);
-  }
-}
-
-template <int BITS, int AT, int DPG>
-static hipError_t launch_ip_zk(const GemvArgs& g, int R, hipStream_t st) {
-  if (g.zp_kind == QMM_ZP_PACKED) return launch_ip_mr<BITS, AT, DPG, 1>(g, R, st);
-  if (g.zp_kind == QMM_ZP_F16) return launch_ip_mr<BITS, AT, DPG, 2>(g, R, st);
-  return launch_ip_mr<BITS, AT, DPG, 0>(g, R, st);
-}
-
-template <int BITS, int AT>
-hipError_t launch_ip_at_type(const GemvArgs& g, int R, hipStream_t st) {
-  constexpr int WPD = 32 / BITS;
-  // dwords per scale group: min(block, codes per chunk) / codes per dword
-  const int dpg = g.block >= 4 * WPD ? 4 : g.block / WPD;
-  if constexpr (BITS == 2) {
-    if (dpg == 1) return launch_ip_zk<BITS, AT, 1>(g, R, st);
-  }
-  if (dpg == 2) return launch_ip_zk<BITS, AT, 2>(g, R, st);
-  return launch_ip_zk<BITS, AT, 4>(g, R, st);
 }
 
 }  // namespace qmm

@@ -1,5 +1,5 @@
 // Instantiation of the integer-plane GEMV for 4-bit affine weights and bf16 activations.
-#include "qmm_gemv_ip.h"
+#include "qmm_gemv_stream.h"
 
 namespace qmm {
 template hipError_t launch_ip_at_type<4, QMM_BF16>(const GemvArgs& g, int R, hipStream_t st);

@@ -49,6 +49,7 @@ constexpr size_t kGemvLdsBudget = 96 * 1024; // preferred A staging size per wor
 void gemv_plan(GemvArgs& g, int num_cus);
 
 int gemv_lanes_per_row_log2(int64_t nchunks);
+int gemv_row_lanes_log2(int64_t nchunks, int64_t N);
 hipError_t launch_gemv(GemvArgs g, int rows_per_lane, hipStream_t st);
 
 struct DequantArgs {
