@@ -101,6 +101,19 @@ __device__ __forceinline__ float swz_xor(float v) {
   return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x1f | (K << 10)));
 }
 
+// Lane exchange inside rows of 16 lanes through DPP (no LDS traffic): xor 1 and
+// xor 2 inside quads, then the mirror of each half row (lane i <-> 7 - i) and of the
+// row (lane i <-> 15 - i).  Applied in that order with a commutative combine, every
+// lane of an aligned group of 4, 8 or 16 lanes ends with the same group result.
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141;  // row_half_mirror
+constexpr int kDppMirror = 0x140;      // row_mirror
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
 // Butterfly sum over groups of `width` consecutive lanes (power of two <= 64).
 // Every lane of the group ends with the same, order-fixed result: at each step a
 // lane adds its partner's value (a + b == b + a bitwise, so partners agree).

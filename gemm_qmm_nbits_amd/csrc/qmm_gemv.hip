@@ -100,7 +100,10 @@ int gemv_row_lanes_log2(int64_t nchunks, int64_t N) {
     const double eff = slots > 0 ? (double)nchunks / (double)slots : 0.0;
     const int64_t rows_per_tile = 8 * (64 / lpr);
     const int64_t tiles = (N + rows_per_tile - 1) / rows_per_tile;
-    const double par = tiles >= 512 ? 1.0 : (double)tiles / 512.0;
+#ifndef QMM_LPR_TARGET
+#define QMM_LPR_TARGET 512
+#endif
+    const double par = tiles >= QMM_LPR_TARGET ? 1.0 : (double)tiles / (double)QMM_LPR_TARGET;
     const double score = eff * par;
     if (score > best_score + 1e-12) {
       best_score = score;

@@ -63,7 +63,7 @@ __device__ __forceinline__ void stage_planes(const GemvArgs& g, uint32_t* planes
                                              int SC) {
   using L = IpLayout<BITS>;
   constexpr int WPC = 128 / BITS;
-  constexpr int NB = 4;  // float4 pieces per thread whose loads are issued together
+  constexpr int NB = 8;  // float4 pieces per thread whose loads are issued together
   const int per_row = SC * (WPC / 4);  // float4 pieces per A row in the slice
   const int total = (int)g.M * per_row;
   const int K = (int)g.K;
@@ -114,47 +114,70 @@ __device__ __forceinline__ void stage_planes(const GemvArgs& g, uint32_t* planes
       const int rem = idx - m * per_row;
       const int slot = rem / (WPC / 4);
       const int j4 = rem - slot * (WPC / 4);  // float4 piece inside the chunk
-      // group maximum and group sum (fixed xor butterfly over the gw threads)
+      // group maximum and group sum over the gw threads of the group (DPP exchanges)
       float mx = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
       float sm = ((v[0] + v[1]) + v[2]) + v[3];
-      if (gw > 1) { mx = fmaxf(mx, swz_xor<1>(mx)); sm += swz_xor<1>(sm); }
-      if (gw > 2) { mx = fmaxf(mx, swz_xor<2>(mx)); sm += swz_xor<2>(sm); }
-      if (gw > 4) { mx = fmaxf(mx, swz_xor<4>(mx)); sm += swz_xor<4>(sm); }
-      if (gw > 8) { mx = fmaxf(mx, swz_xor<8>(mx)); sm += swz_xor<8>(sm); }
+      mx = fmaxf(mx, dpp_f<kDppXor1>(mx));
+      sm += dpp_f<kDppXor1>(sm);
+      mx = fmaxf(mx, dpp_f<kDppXor2>(mx));
+      sm += dpp_f<kDppXor2>(sm);
+      if constexpr (gw >= 8) {
+        mx = fmaxf(mx, dpp_f<kDppHalfMirror>(mx));
+        sm += dpp_f<kDppHalfMirror>(sm);
+      }
+      if constexpr (gw >= 16) {
+        mx = fmaxf(mx, dpp_f<kDppMirror>(mx));
+        sm += dpp_f<kDppMirror>(sm);
+      }
       int e = 0;
       (void)frexpf(mx, &e);  // mx < 2^e (mx = 0 gives e = 0)
       if (!ok) continue;
-      int ai[4];
+      uint32_t u[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) ai[q] = (int)rintf(ldexpf(v[q], 22 - e));
+      for (int q = 0; q < 4; ++q) u[q] = (uint32_t)(int)rintf(ldexpf(v[q], 22 - e));
       uint32_t* slot_w = planes + (m * SC + slot) * L::SLOT;
       if constexpr (BITS == 2) {
         // elements j0..j0+3 of a 16-code dword: j0, j0+2 even (nibbles j0/2, j0/2+1 of
-        // the E word), j0+1, j0+3 odd (same nibbles of the O word)
+        // the E words), j0+1, j0+3 odd (same nibbles of the O words).  Digit p of two
+        // values goes to one byte: the low nibbles of bytes 0-2 of a value are its
+        // digits 0, 2, 4, the high nibbles its digits 1, 3, 5 (24-bit two's complement).
         const int d = (4 * j4) >> 4;
-        const int j0 = (4 * j4) & 15;
-        uint8_t* wb = (uint8_t*)(slot_w + d * L::PWD);
+        const int qb = ((4 * j4) & 15) >> 2;  // byte of each plane word
+        uint8_t* wb = (uint8_t*)(slot_w + d * L::PWD) + qb;
+        const uint32_t ee = (u[0] & 0x0F0F0Fu) | ((u[2] << 4) & 0xF0F0F0u);  // E digits 0, 2, 4
+        const uint32_t eo = ((u[0] >> 4) & 0x0F0F0Fu) | (u[2] & 0xF0F0F0u);  // E digits 1, 3, 5
+        const uint32_t oe = (u[1] & 0x0F0F0Fu) | ((u[3] << 4) & 0xF0F0F0u);
+        const uint32_t oo = ((u[1] >> 4) & 0x0F0F0Fu) | (u[3] & 0xF0F0F0u);
 #pragma unroll
-        for (int p = 0; p < 6; ++p) {
-          const uint32_t e0 = ((uint32_t)(ai[0] >> (4 * p))) & 15u;
-          const uint32_t o0 = ((uint32_t)(ai[1] >> (4 * p))) & 15u;
-          const uint32_t e1 = ((uint32_t)(ai[2] >> (4 * p))) & 15u;
-          const uint32_t o1 = ((uint32_t)(ai[3] >> (4 * p))) & 15u;
-          wb[(2 * p) * 4 + (j0 >> 2)] = (uint8_t)(e0 | (e1 << 4));
-          wb[(2 * p + 1) * 4 + (j0 >> 2)] = (uint8_t)(o0 | (o1 << 4));
+        for (int k = 0; k < 3; ++k) {
+          wb[(2 * (2 * k)) * 4] = (uint8_t)(ee >> (8 * k));
+          wb[(2 * (2 * k + 1)) * 4] = (uint8_t)(eo >> (8 * k));
+          wb[(2 * (2 * k) + 1) * 4] = (uint8_t)(oe >> (8 * k));
+          wb[(2 * (2 * k + 1) + 1) * 4] = (uint8_t)(oo >> (8 * k));
         }
       } else {
         // elements j0..j0+3 of an 8-code dword are nibbles j0..j0+3 of each plane word
+        // (digits of a + 2^23): pair the values, then join the two pairs' bytes
         const int d = (4 * j4) >> 3;
-        const int j0 = (4 * j4) & 7;
-        uint16_t* wh = (uint16_t*)(slot_w + d * L::PWD);
+        const int qh = ((4 * j4) & 7) >> 2;  // half-word of each plane word
+        uint16_t* wh = (uint16_t*)(slot_w + d * L::PWD) + qh;
 #pragma unroll
-        for (int p = 0; p < 6; ++p) {
-          uint32_t h = 0;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) h |= ((((uint32_t)(ai[q] + (1 << 23))) >> (4 * p)) & 15u) << (4 * q);
-          wh[p * 2 + (j0 >> 2)] = (uint16_t)h;
-        }
+        for (int q = 0; q < 4; ++q) u[q] += 1u << 23;
+        const uint32_t x01 = (u[0] & 0x0F0F0Fu) | ((u[1] << 4) & 0xF0F0F0u);  // digits 0, 2, 4
+        const uint32_t y01 = ((u[0] >> 4) & 0x0F0F0Fu) | (u[1] & 0xF0F0F0u);  // digits 1, 3, 5
+        const uint32_t x23 = (u[2] & 0x0F0F0Fu) | ((u[3] << 4) & 0xF0F0F0u);
+        const uint32_t y23 = ((u[2] >> 4) & 0x0F0F0Fu) | (u[3] & 0xF0F0F0u);
+        // byte k of a pair word + byte k of the other pair word = the plane's half-word
+        const uint32_t p02 = __builtin_amdgcn_perm(x23, x01, 0x05010400u);  // digits 0 | 2
+        const uint32_t p13 = __builtin_amdgcn_perm(y23, y01, 0x05010400u);  // digits 1 | 3
+        const uint32_t p45 = __builtin_amdgcn_perm(y23, y01, 0x06020000u) & 0xffff0000u;
+        const uint32_t p4 = __builtin_amdgcn_perm(x23, x01, 0x00000602u) & 0xffffu;
+        wh[0 * 2] = (uint16_t)p02;
+        wh[2 * 2] = (uint16_t)(p02 >> 16);
+        wh[1 * 2] = (uint16_t)p13;
+        wh[3 * 2] = (uint16_t)(p13 >> 16);
+        wh[4 * 2] = (uint16_t)p4;
+        wh[5 * 2] = (uint16_t)(p45 >> 16);
       }
       if ((j4 % gw) == 0) {
         const int gi = j4 / gw;
