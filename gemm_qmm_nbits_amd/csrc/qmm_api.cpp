@@ -555,9 +555,12 @@ hipError_t run_gemv_rows(int entry, GemvArgs g, hipStream_t st) {
 extern "C" {
 
 size_t qmm_nbits_workspace_bytes(int64_t M, int64_t K, int a_type) {
-  // the prefill path (M > 8) casts A to fp16 once into the workspace
-  if (M <= kMaxGemvM || a_type == QMM_F16 || M <= 0 || K <= 0) return 0;
-  return ((size_t)M * (size_t)K * 2 + 255) & ~size_t(255);
+  // the prefill path (M > 8) writes A once as fp16 rows of K rounded up to 64
+  // (zero padded) into the workspace, whatever the type of A
+  (void)a_type;
+  if (M <= kMaxGemvM || M <= 0 || K <= 0) return 0;
+  const size_t kp = (size_t)((K + 63) / 64) * 64;
+  return ((size_t)M * kp * 2 + 255) & ~size_t(255);
 }
 
 size_t qmm_codebook4_workspace_bytes(int64_t M, int64_t K, int a_type) {
@@ -594,16 +597,15 @@ qmm_status qmm_nbits(const void* A, int a_type, int64_t M, int64_t K, int64_t N,
   if (M > kMaxGemvM && K > 0) {
     // prefill: A -> fp16 once, then the matrix-core tile kernel
     PrefillArgs p{};
-    if (a_type == QMM_F16) {
-      p.A16 = (const uint16_t*)A;
-    } else {
-      hipError_t e = launch_cast_to_f16(A, a_type, (uint16_t*)workspace, M * K, st);
-      if (e != hipSuccess) return (qmm_status)e;
-      p.A16 = (const uint16_t*)workspace;
-    }
+    const int64_t Kp = (K + 63) / 64 * 64;
+    hipError_t ce = launch_cast_pad_f16(A, a_type, M, K, Kp, (uint16_t*)workspace, st);
+    if (ce != hipSuccess) return (qmm_status)ce;
+    p.A16 = (const uint16_t*)workspace;
     p.M = M;
     p.N = N;
     p.K = K;
+    p.Kp = Kp;
+    p.ldc = N;
     p.W = W;
     p.bits = bits;
     p.block = block;
@@ -618,8 +620,6 @@ qmm_status qmm_nbits(const void* A, int a_type, int64_t M, int64_t K, int64_t N,
     p.bias = bias;
     p.C = C;
     p.c_type = c_type;
-    p.a_vec = aligned(p.A16, 16) && (K % 8 == 0);
-    p.w_vec = aligned(W, 16) && (p.row_bytes % 16 == 0);
     hipError_t e = launch_prefill(p, st);
     if (e != hipSuccess) return (qmm_status)e;
     return (qmm_status)hipGetLastError();

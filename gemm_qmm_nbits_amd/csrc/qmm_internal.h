@@ -75,12 +75,15 @@ hipError_t launch_uniform_check(const uint16_t* zp, int64_t count, uint32_t* scr
 constexpr int kUniformPartials = 256;
 
 // A (fp32 / bf16) -> fp16, round to nearest even, count elements.
-hipError_t launch_cast_to_f16(const void* src, int src_type, uint16_t* dst, int64_t count,
-                              hipStream_t st);
+// dst[m][k] = fp16(src[m][k]) for k < K, 0 for K <= k < Kp (rows of Kp elements).
+hipError_t launch_cast_pad_f16(const void* src, int src_type, int64_t M, int64_t K, int64_t Kp,
+                               uint16_t* dst, hipStream_t st);
 
 struct PrefillArgs {
-  const uint16_t* A16;  // fp16 [M][K]
+  const uint16_t* A16;  // fp16 [M][Kp], k >= K zero
   int64_t M, N, K;
+  int64_t Kp;   // K rounded up to a multiple of 64
+  int64_t ldc;  // row stride of C (elements)
   const uint8_t* W;
   int bits, block, block_log2;
   int64_t nblk, row_bytes;
@@ -92,8 +95,6 @@ struct PrefillArgs {
   const void* bias;
   void* C;
   int c_type;
-  int a_vec;  // A16 rows allow 16-byte loads
-  int w_vec;  // W rows allow 8/16-byte loads of 32 codes
   int ntiles, mtiles;
 };
 hipError_t launch_prefill(PrefillArgs p, hipStream_t st);

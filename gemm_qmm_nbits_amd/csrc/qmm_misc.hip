@@ -78,39 +78,34 @@ hipError_t launch_uniform_check(const uint16_t* zp, int64_t count, uint32_t* scr
 }
 
 // ---- A cast to fp16 (prefill path; [P1] "What", commit 1: cast A once) --------
-__global__ __launch_bounds__(256) void cast_f16_kernel(const void* src, int src_type, uint16_t* dst,
-                                                       int64_t count) {
-  const int64_t n4 = count / 4;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4;
+// One thread per 8 consecutive elements of a destination row (one 16-byte store).
+__global__ __launch_bounds__(256) void cast_pad_f16_kernel(const void* src, int src_type, int64_t M,
+                                                           int64_t K, int64_t Kp, uint16_t* dst) {
+  const int64_t per_row = Kp / 8;
+  const int64_t total = M * per_row;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
        i += (int64_t)gridDim.x * blockDim.x) {
-    float v[4];
-    if (src_type == QMM_F32) {
-      const f32x4 x = ((const f32x4*)src)[i];
-      v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
-    } else {
-      const uint2 x = ((const uint2*)src)[i];
-      v[0] = bf16_to_f32((uint16_t)(x.x & 0xffffu));
-      v[1] = bf16_to_f32((uint16_t)(x.x >> 16));
-      v[2] = bf16_to_f32((uint16_t)(x.y & 0xffffu));
-      v[3] = bf16_to_f32((uint16_t)(x.y >> 16));
+    const int64_t m = i / per_row;
+    const int64_t k = (i - m * per_row) * 8;
+    const int64_t base = m * K + k;
+    uint32_t o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float v0 = (k + 2 * e < K) ? load_elem_rt(src, src_type, base + 2 * e) : 0.0f;
+      const float v1 = (k + 2 * e + 1 < K) ? load_elem_rt(src, src_type, base + 2 * e + 1) : 0.0f;
+      o[e] = (uint32_t)f32_to_f16(v0) | ((uint32_t)f32_to_f16(v1) << 16);
     }
-    uint2 o;
-    o.x = (uint32_t)f32_to_f16(v[0]) | ((uint32_t)f32_to_f16(v[1]) << 16);
-    o.y = (uint32_t)f32_to_f16(v[2]) | ((uint32_t)f32_to_f16(v[3]) << 16);
-    ((uint2*)dst)[i] = o;
+    ((uint4*)dst)[i] = make_uint4(o[0], o[1], o[2], o[3]);
   }
-  // tail
-  const int64_t t = n4 * 4 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t < count && t >= n4 * 4) dst[t] = f32_to_f16(load_elem_rt(src, src_type, t));
 }
 
-hipError_t launch_cast_to_f16(const void* src, int src_type, uint16_t* dst, int64_t count,
-                              hipStream_t st) {
-  int64_t blocks = (count / 4 + 255) / 256;
-  if (blocks > 8192) blocks = 8192;
+hipError_t launch_cast_pad_f16(const void* src, int src_type, int64_t M, int64_t K, int64_t Kp,
+                               uint16_t* dst, hipStream_t st) {
+  int64_t blocks = (M * (Kp / 8) + 255) / 256;
+  if (blocks > 16384) blocks = 16384;
   if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL(cast_f16_kernel, dim3((unsigned)blocks), dim3(256), 0, st, src, src_type, dst,
-                     count);
+  hipLaunchKernelGGL(cast_pad_f16_kernel, dim3((unsigned)blocks), dim3(256), 0, st, src, src_type, M,
+                     K, Kp, dst);
   return hipSuccess;
 }
 

@@ -4,23 +4,28 @@
 // "Performance"/Qwen study: prefill is compute bound).
 //
 // C[M][N] = A16 . W16^T (+ bias), with A16 = fp16(A) (cast once into the caller's
-// workspace by launch_cast_to_f16) and W16 = fp16(fp32(fp32(q - zp) * s)), the
-// round-to-nearest fp16 of the exact dequantized weight, built tile by tile in LDS.
-// Products are accumulated in fp32 by v_mfma_f32_32x32x16_f16 in increasing k order
-// (64 codes per stage), whatever the tile shape.
+// workspace by launch_cast_pad_f16, rows padded with zeros to a multiple of 64) and
+// W16 = fp16(fp32(fp32(q - zp) * s)), the round-to-nearest fp16 of the exact
+// dequantized weight, built tile by tile in LDS.  Products are accumulated in fp32
+// by v_mfma_f32_32x32x16_f16 in increasing k order (64 codes per stage), whatever
+// the tile shape.
 //
-// Work-group: 256 threads (4 waves), output tile BM x BN = 256 x 256, each wave a
-// 128 x 128 quarter held as 4 x 4 MFMA blocks of 32 x 32 (fp32 accumulators).  Each
-// stage stages A[256][64] (fp16) and W16[256][64] in LDS (rows padded to 72 halves
-// so the 16-byte operand reads of a wave hit distinct banks), double buffered with
-// one barrier per stage: the next stage's global loads are issued before the MFMAs
-// of the current one and written to the other buffer after them.
+// Work-group: 512 threads (8 waves, two per SIMD so that one wave's matrix-core
+// work overlaps the other's dequantization and LDS traffic), output tile
+// BM x BN = 256 x 256, each wave a 64 x 128 part held as 2 x 4 MFMA blocks of
+// 32 x 32 (fp32 accumulators).  Each stage stages A[256][64] (fp16) and W16[256][64]
+// in LDS (rows padded to 72 halves so the 16-byte operand reads of a wave hit
+// distinct banks), double buffered with one barrier per stage.  The global loads
+// of a stage are issued two stages ahead into one of two register sets (buffer
+// loads: rows past the end read 0, so no address is clamped).
 //
 // MFMA operand layout (32x32x16 f16): lane l holds row (or column) l % 32 and the 8
 // consecutive k at 8 * (l / 32); accumulator v of lane l is row 8*(v/4) + 4*(l/32)
 // + v%4, column l % 32.
 #include "qmm_device.h"
 #include "qmm_internal.h"
+
+#include <algorithm>
 
 namespace qmm {
 
@@ -30,82 +35,27 @@ constexpr int BM = 256;
 constexpr int BN = 256;
 constexpr int BK = 64;
 constexpr int LDA = BK + 8;  // padded LDS row (halves)
-constexpr int NT = 256;      // threads
+constexpr int NT = 512;      // threads
+constexpr uint32_t kWord3 = 0x00020000u;  // raw buffer descriptor, 32-bit data format
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, int64_t bytes) {
+  const uint32_t n = bytes >= 0x7fffffff ? 0x7fffffffu : (uint32_t)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)n, (int)kWord3);
+}
+
+// Global data of one stage for one thread: 32 halves of A (row t/2, k half t%2) and
+// 32 codes of W (row t/2, same k half) with the scale and zero point of each 16.
+template <int BITS>
+struct Stage {
+  uint32_t a[16];
+  uint32_t w[BITS];  // 32 codes: 2-bit -> 2 dwords, 4-bit -> 4 dwords
+  _Float16 sc[2];
+  _Float16 zh[2];
+  uint32_t zb[2];
+};
 
 __device__ __forceinline__ uint32_t pack_h2(float a, float b) {
   return (uint32_t)f32_to_f16(a) | ((uint32_t)f32_to_f16(b) << 16);
-}
-
-// Raw codes, scales and zero points of 64 codes of weight row n starting at k0.
-template <int BITS>
-struct BStage {
-  uint32_t raw[2 * BITS];  // 64 codes: 2-bit -> 4 dwords, 4-bit -> 8 dwords
-  float sc[4];             // per 16 codes (a block holds >= 16 codes)
-  float zz[4];
-};
-
-template <int BITS, int ZK>
-__device__ __forceinline__ void load_b(const PrefillArgs& p, int n, int k0, BStage<BITS>& b) {
-  const bool row_ok = n < p.N;
-  const int kpad = (int)(p.nblk * p.block);
-  const uint8_t* row = p.W + (int64_t)(row_ok ? n : 0) * p.row_bytes;
-  if (row_ok && k0 + BK <= kpad && p.w_vec) {
-    const uint4* src = (const uint4*)(row + ((k0 * BITS) >> 3));
-#pragma unroll
-    for (int q = 0; q < BITS / 2; ++q) {
-      const uint4 v = src[q];
-      b.raw[4 * q + 0] = v.x;
-      b.raw[4 * q + 1] = v.y;
-      b.raw[4 * q + 2] = v.z;
-      b.raw[4 * q + 3] = v.w;
-    }
-  } else {
-#pragma unroll
-    for (int d = 0; d < 2 * BITS; ++d) {
-      uint32_t x = 0;
-#pragma unroll
-      for (int by = 0; by < 4; ++by) {
-        const int kb = k0 + (d * 4 + by) * (8 / BITS);  // first code of this byte
-        if (row_ok && kb < kpad) x |= (uint32_t)row[(kb * BITS) >> 3] << (8 * by);
-      }
-      b.raw[d] = x;
-    }
-  }
-#pragma unroll
-  for (int h = 0; h < 4; ++h) {
-    int blk = (k0 + 16 * h) >> p.block_log2;
-    if (blk >= p.nblk) blk = (int)p.nblk - 1;
-    const int64_t si = (int64_t)(row_ok ? n : 0) * p.nblk + blk;
-    b.sc[h] = f16_to_f32(p.scales[si]);
-    if constexpr (ZK == 1) {
-      const uint8_t* zr = (const uint8_t*)p.zp + (int64_t)(row_ok ? n : 0) * p.zp_row_bytes;
-      const int bit = blk * BITS;
-      b.zz[h] = (float)((zr[bit >> 3] >> (bit & 7)) & ((1u << BITS) - 1u));
-    } else if constexpr (ZK == 2) {
-      b.zz[h] = f16_to_f32(((const uint16_t*)p.zp)[si]);
-    } else {
-      b.zz[h] = p.zconst;
-    }
-  }
-}
-
-// Dequantize 64 codes to fp16 in k order and store them as one padded LDS row.
-template <int BITS>
-__device__ __forceinline__ void store_b(const BStage<BITS>& b, uint16_t* dst_row) {
-  uint32_t o[32];
-#pragma unroll
-  for (int j = 0; j < 32; ++j) {
-    const int k = 2 * j;  // codes k, k+1 of the stage
-    const int h = k >> 4;
-    const uint32_t q0 = (b.raw[(k * BITS) >> 5] >> ((k * BITS) & 31)) & ((1u << BITS) - 1u);
-    const uint32_t q1 = (b.raw[((k + 1) * BITS) >> 5] >> (((k + 1) * BITS) & 31)) & ((1u << BITS) - 1u);
-    const float w0 = __fmul_rn(__fsub_rn((float)q0, b.zz[h]), b.sc[h]);
-    const float w1 = __fmul_rn(__fsub_rn((float)q1, b.zz[h]), b.sc[h]);
-    o[j] = pack_h2(w0, w1);
-  }
-  uint4* dst = (uint4*)dst_row;
-#pragma unroll
-  for (int q = 0; q < 8; ++q) dst[q] = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
 }
 
 template <int CT>
@@ -140,88 +90,130 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillArgs p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;  // 2 x 2 waves, 128 x 128 each
-  const int K = (int)p.K;
-  const int nsteps = (K + BK - 1) / BK;
+  const int wm = wave >> 1, wn = wave & 1;  // 4 x 2 waves, 64 x 128 each
+  const int Kp = (int)p.Kp;
+  const int nsteps = Kp / BK;
+  const int nblk = (int)p.nblk;
+  const int blog = p.block_log2;
 
-  // A stage: thread -> row m0 + tid, 64 halves (8 x 16 bytes)
-  const int a_row = m0 + tid;
-  const bool a_ok = a_row < p.M;
-  const uint16_t* arow = p.A16 + (int64_t)(a_ok ? a_row : 0) * K;
-  auto load_a = [&](int k0, uint4 (&v)[8]) {
+  // this thread's global rows: A row m0 + tid/2, W row n0 + tid/2, k half tid%2
+  const int r2 = tid >> 1, h = tid & 1;
+  const __amdgpu_buffer_rsrc_t rA = rsrc(p.A16, p.M * (int64_t)Kp * 2);
+  const __amdgpu_buffer_rsrc_t rW = rsrc(p.W, p.N * p.row_bytes);
+  const __amdgpu_buffer_rsrc_t rS = rsrc(p.scales, p.N * p.nblk * 2);
+  __amdgpu_buffer_rsrc_t rZ = rS;
+  if constexpr (ZK == 1) rZ = rsrc(p.zp, p.N * p.zp_row_bytes);
+  if constexpr (ZK == 2) rZ = rsrc(p.zp, p.N * p.nblk * 2);
+  const uint32_t a_off = (uint32_t)((int64_t)(m0 + r2) * Kp * 2) + (uint32_t)h * 64u;
+  const int wrow = n0 + r2;
+  const uint32_t w_off = (uint32_t)((int64_t)wrow * p.row_bytes) + (uint32_t)h * (32 * BITS / 8);
+  const uint32_t s_off = (uint32_t)((int64_t)wrow * nblk * 2);
+  const uint32_t z_off = (uint32_t)((int64_t)wrow * p.zp_row_bytes);
+  const int kmax_blk = nblk - 1;
+
+  auto load = [&](int s, Stage<BITS>& st) {
+    const int k0 = s * BK;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int k = k0 + 8 * q;
-      if (a_ok && p.a_vec && k + 8 <= K) {
-        v[q] = *(const uint4*)(arow + k);
-      } else {
-        uint32_t t[4];
+    for (int q = 0; q < 4; ++q) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rA, (int)(a_off + (uint32_t)k0 * 2u + 16u * q), 0, 0);
+      st.a[4 * q + 0] = v[0];
+      st.a[4 * q + 1] = v[1];
+      st.a[4 * q + 2] = v[2];
+      st.a[4 * q + 3] = v[3];
+    }
+    const uint32_t wo = w_off + (uint32_t)(k0 * BITS / 8);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t lo = (a_ok && k + 2 * e < K) ? arow[k + 2 * e] : 0u;
-          const uint32_t hi = (a_ok && k + 2 * e + 1 < K) ? arow[k + 2 * e + 1] : 0u;
-          t[e] = lo | (hi << 16);
-        }
-        v[q] = make_uint4(t[0], t[1], t[2], t[3]);
+    for (int d = 0; d < BITS; ++d) st.w[d] = __builtin_amdgcn_raw_buffer_load_b32(rW, (int)(wo + 4u * d), 0, 0);
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      int blk = (k0 + 32 * h + 16 * g) >> blog;
+      blk = blk < kmax_blk ? blk : kmax_blk;  // codes past the row end meet zero A
+      st.sc[g] = __builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(rS, (int)(s_off + 2u * blk), 0, 0));
+      if constexpr (ZK == 1) {
+        const int bit = blk * BITS;
+        st.zb[g] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rZ, (int)(z_off + (uint32_t)(bit >> 3)), 0, 0) >> (bit & 7);
+      } else if constexpr (ZK == 2) {
+        st.zh[g] = __builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(rZ, (int)(s_off + 2u * blk), 0, 0));
       }
     }
   };
-  auto store_a = [&](int buf, const uint4 (&v)[8]) {
-    uint4* dst = (uint4*)(As + buf * BM * LDA + tid * LDA);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) dst[q] = v[q];
-  };
-  const int b_row = n0 + tid;
 
-  f32x16 acc[4][4];
+  // dequantize this thread's 32 codes and write both halves of the stage to LDS
+  auto store = [&](const Stage<BITS>& st, int buf) {
+    uint4* ad = (uint4*)(As + buf * BM * LDA + r2 * LDA + 32 * h);
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+    for (int q = 0; q < 4; ++q) ad[q] = make_uint4(st.a[4 * q], st.a[4 * q + 1], st.a[4 * q + 2], st.a[4 * q + 3]);
+    uint32_t o[16];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const float sc = (float)st.sc[g];
+      float z;
+      if constexpr (ZK == 1) z = (float)(st.zb[g] & ((1u << BITS) - 1u));
+      else if constexpr (ZK == 2) z = (float)st.zh[g];
+      else z = p.zconst;
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const int k = 16 * g + 2 * jj;  // codes k, k+1 of the thread's 32
+        const uint32_t q0 = (st.w[(k * BITS) >> 5] >> ((k * BITS) & 31)) & ((1u << BITS) - 1u);
+        const uint32_t q1 = (st.w[((k + 1) * BITS) >> 5] >> (((k + 1) * BITS) & 31)) & ((1u << BITS) - 1u);
+        const float w0 = __fmul_rn(__fsub_rn((float)q0, z), sc);
+        const float w1 = __fmul_rn(__fsub_rn((float)q1, z), sc);
+        o[8 * g + jj] = pack_h2(w0, w1);
+      }
+    }
+    uint4* bd = (uint4*)(Bs + buf * BN * LDA + r2 * LDA + 32 * h);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) bd[q] = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
+  };
+
+  f32x16 acc[2][4];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = f32x16{};
 
-  {
-    uint4 av[8];
-    BStage<BITS> bs;
-    load_a(0, av);
-    load_b<BITS, ZK>(p, b_row, 0, bs);
-    store_a(0, av);
-    store_b<BITS>(bs, Bs + tid * LDA);
-  }
-  __syncthreads();
-
-  for (int s = 0; s < nsteps; ++s) {
-    const int buf = s & 1;
-    const bool more = s + 1 < nsteps;
-    uint4 av[8];
-    BStage<BITS> bs;
-    if (more) {
-      load_a((s + 1) * BK, av);
-      load_b<BITS, ZK>(p, b_row, (s + 1) * BK, bs);
-    }
+  auto compute = [&](int buf) {
     const uint16_t* Ab = As + buf * BM * LDA;
     const uint16_t* Bb = Bs + buf * BN * LDA;
 #pragma unroll
     for (int kk = 0; kk < BK; kk += 16) {
-      f16x8 af[4], bf[4];
+      f16x8 af[2], bf[4];
       const int koff = kk + 8 * (lane >> 5);
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
-        af[a] = *(const f16x8*)(Ab + (wm * 128 + a * 32 + (lane & 31)) * LDA + koff);
+      for (int a = 0; a < 2; ++a)
+        af[a] = *(const f16x8*)(Ab + (wm * 64 + a * 32 + (lane & 31)) * LDA + koff);
 #pragma unroll
       for (int b = 0; b < 4; ++b)
         bf[b] = *(const f16x8*)(Bb + (wn * 128 + b * 32 + (lane & 31)) * LDA + koff);
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+      for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int b = 0; b < 4; ++b)
           acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[a], bf[b], acc[a][b], 0, 0, 0);
     }
-    if (more) {
-      store_a(buf ^ 1, av);
-      store_b<BITS>(bs, Bs + (buf ^ 1) * BN * LDA + tid * LDA);
-    }
+  };
+
+  Stage<BITS> s0, s1;
+  load(0, s0);
+  load(1, s1);
+  store(s0, 0);
+  __syncthreads();
+  // stage s computes from LDS buffer s % 2 while stage s + 1 sits in a register set
+  // (in flight) and stage s + 2 is loaded into the set stage s had used
+  int s = 0;
+  for (; s + 2 <= nsteps; s += 2) {
+    load(s + 2, s0);
+    __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the matrix-core work
+    compute(0);
+    store(s1, 1);
+    __syncthreads();
+    load(s + 3, s1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(1);
+    if (s + 2 < nsteps) store(s0, 0);
     __syncthreads();
   }
+  if (s < nsteps) compute(0);  // odd number of stages: the last one is in buffer 0
 
   // epilogue: + bias, convert, store (rows/columns past the end are skipped)
 #pragma unroll
@@ -230,11 +222,11 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillArgs p) {
     const bool col_ok = col < p.N;
     const float bv = (p.bias && col_ok) ? load_bias<CT>(p.bias, col) : 0.0f;
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
+    for (int a = 0; a < 2; ++a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int row = m0 + wm * 128 + a * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if (col_ok && row < p.M) store_c<CT>(p.C, (int64_t)row * p.N + col, acc[a][b][v] + bv);
+        const int row = m0 + wm * 64 + a * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        if (col_ok && row < p.M) store_c<CT>(p.C, (int64_t)row * p.ldc + col, acc[a][b][v] + bv);
       }
     }
   }
@@ -264,19 +256,39 @@ void launch_ct(const PrefillArgs& p, dim3 grid, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_prefill(PrefillArgs p, hipStream_t st) {
-  p.ntiles = (int)((p.N + BN - 1) / BN);
-  p.mtiles = (int)((p.M + BM - 1) / BM);
-  const int64_t groups = (p.ntiles + 7) / 8;
-  const dim3 grid((unsigned)(groups * 8 * p.mtiles));
+  // buffer offsets are 32-bit: split M and N so that every operand slice stays
+  // below 2^31 bytes (one launch per slice)
+  const int64_t lim = (int64_t)1 << 30;
+  int64_t mstep = std::max<int64_t>(BM, (lim / (p.Kp * 2)) / BM * BM);
+  int64_t nstep = std::max<int64_t>(BN, (lim / std::max<int64_t>(p.row_bytes, p.nblk * 2)) / BN * BN);
   const int zk = p.zp_kind == QMM_ZP_PACKED ? 1 : p.zp_kind == QMM_ZP_F16 ? 2 : 0;
-  if (p.bits == 2) {
-    if (zk == 1) launch_ct<2, 1>(p, grid, st);
-    else if (zk == 2) launch_ct<2, 2>(p, grid, st);
-    else launch_ct<2, 0>(p, grid, st);
-  } else {
-    if (zk == 1) launch_ct<4, 1>(p, grid, st);
-    else if (zk == 2) launch_ct<4, 2>(p, grid, st);
-    else launch_ct<4, 0>(p, grid, st);
+  const size_t c_es = p.c_type == QMM_F32 ? 4 : 2;
+  for (int64_t m0 = 0; m0 < p.M; m0 += mstep) {
+    for (int64_t n0 = 0; n0 < p.N; n0 += nstep) {
+      PrefillArgs q = p;
+      q.M = std::min(mstep, p.M - m0);
+      q.N = std::min(nstep, p.N - n0);
+      q.A16 = p.A16 + m0 * p.Kp;
+      q.W = p.W + n0 * p.row_bytes;
+      q.scales = p.scales + n0 * p.nblk;
+      if (zk == 1) q.zp = (const uint8_t*)p.zp + n0 * p.zp_row_bytes;
+      if (zk == 2) q.zp = (const uint16_t*)p.zp + n0 * p.nblk;
+      if (p.bias) q.bias = (const uint8_t*)p.bias + n0 * (int64_t)c_es;
+      q.C = (uint8_t*)p.C + (m0 * p.ldc + n0) * (int64_t)c_es;
+      q.ntiles = (int)((q.N + BN - 1) / BN);
+      q.mtiles = (int)((q.M + BM - 1) / BM);
+      const int64_t groups = (q.ntiles + 7) / 8;
+      const dim3 grid((unsigned)(groups * 8 * q.mtiles));
+      if (q.bits == 2) {
+        if (zk == 1) launch_ct<2, 1>(q, grid, st);
+        else if (zk == 2) launch_ct<2, 2>(q, grid, st);
+        else launch_ct<2, 0>(q, grid, st);
+      } else {
+        if (zk == 1) launch_ct<4, 1>(q, grid, st);
+        else if (zk == 2) launch_ct<4, 2>(q, grid, st);
+        else launch_ct<4, 0>(q, grid, st);
+      }
+    }
   }
   return hipSuccess;
 }
