@@ -54,9 +54,6 @@ struct Stage {
   uint32_t zb[2];
 };
 
-__device__ __forceinline__ uint32_t pack_h2(float a, float b) {
-  return (uint32_t)f32_to_f16(a) | ((uint32_t)f32_to_f16(b) << 16);
-}
 
 template <int CT>
 __device__ __forceinline__ void store_c(void* C, int64_t i, float v) {
@@ -78,13 +75,21 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillArgs p) {
   uint16_t* As = smem_h;                  // [2][BM * LDA]
   uint16_t* Bs = smem_h + 2 * BM * LDA;   // [2][BN * LDA]
 
-  // tile order: the M tiles of one N tile run on one XCD (work-groups are dealt
-  // round-robin over 8 XCDs), so the packed weights of that N tile are read into
-  // one L2
+  // tile order (work-groups are dealt round-robin over the 8 XCDs): otherwise the
+  // M tiles of one N tile run on one XCD, so the packed weights of that N tile are
+  // read into one L2
   const int i = blockIdx.x;
   const int x = i & 7, j = i >> 3;
-  const int nt = (j / p.mtiles) * 8 + x;
-  const int mt = j % p.mtiles;
+  int nt, mt;
+  if (p.mtiles == 8) {
+    // one M tile per XCD: its A rows (256 x K fp16) stay in that XCD's L2 while the
+    // XCD walks every N tile; the packed weights are shared through the last-level cache
+    mt = x;
+    nt = j;
+  } else {
+    nt = (j / p.mtiles) * 8 + x;
+    mt = j % p.mtiles;
+  }
   if (nt >= p.ntiles) return;
   const int m0 = mt * BM, n0 = nt * BN;
 
@@ -138,32 +143,54 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillArgs p) {
     }
   };
 
-  // dequantize this thread's 32 codes and write both halves of the stage to LDS
-  auto store = [&](const Stage<BITS>& st, int buf) {
+  // dequantize part q (codes 8q .. 8q+7) of this thread's 32 codes and write that
+  // part of both halves of the stage to LDS
+  auto store_part = [&](const Stage<BITS>& st, int buf, int q) {
     uint4* ad = (uint4*)(As + buf * BM * LDA + r2 * LDA + 32 * h);
+    ad[q] = make_uint4(st.a[4 * q], st.a[4 * q + 1], st.a[4 * q + 2], st.a[4 * q + 3]);
+    const int g = q >> 1;
+    const float sc = (float)st.sc[g];
+    float z;
+    if constexpr (ZK == 1) z = (float)(st.zb[g] & ((1u << BITS) - 1u));
+    else if constexpr (ZK == 2) z = (float)st.zh[g];
+    else z = p.zconst;
+    // codes 8q .. 8q+7 as exact fp32 integers, two per conversion: 2-bit codes
+    // masked into e2m1 nibbles are q/2 (scaled by 2), 4-bit codes masked into e4m3
+    // bytes are q * 2^-9 (scaled by 2^9)
+    float qv[8];
+    if constexpr (BITS == 2) {
+      const uint32_t x = st.w[q >> 1] >> (16 * (q & 1));  // 8 codes in the low 16 bits
+      const uint32_t ev = x & 0x3333u, od = (x >> 2) & 0x3333u;
+      const f32x2 e0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(ev, 2.0f, 0);
+      const f32x2 o0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(od, 2.0f, 0);
+      const f32x2 e1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(ev, 2.0f, 1);
+      const f32x2 o1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(od, 2.0f, 1);
+      qv[0] = e0.x; qv[2] = e0.y; qv[1] = o0.x; qv[3] = o0.y;
+      qv[4] = e1.x; qv[6] = e1.y; qv[5] = o1.x; qv[7] = o1.y;
+    } else {
+      const uint32_t x = st.w[q];  // 8 codes
+      const uint32_t lo = x & 0x0F0F0F0Fu, hi = (x >> 4) & 0x0F0F0F0Fu;
+      const f32x2 l0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(lo, 512.0f, false);
+      const f32x2 h0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hi, 512.0f, false);
+      const f32x2 l1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(lo, 512.0f, true);
+      const f32x2 h1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hi, 512.0f, true);
+      qv[0] = l0.x; qv[2] = l0.y; qv[4] = l1.x; qv[6] = l1.y;
+      qv[1] = h0.x; qv[3] = h0.y; qv[5] = h1.x; qv[7] = h1.y;
+    }
+    uint32_t o[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) ad[q] = make_uint4(st.a[4 * q], st.a[4 * q + 1], st.a[4 * q + 2], st.a[4 * q + 3]);
-    uint32_t o[16];
-#pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      const float sc = (float)st.sc[g];
-      float z;
-      if constexpr (ZK == 1) z = (float)(st.zb[g] & ((1u << BITS) - 1u));
-      else if constexpr (ZK == 2) z = (float)st.zh[g];
-      else z = p.zconst;
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        const int k = 16 * g + 2 * jj;  // codes k, k+1 of the thread's 32
-        const uint32_t q0 = (st.w[(k * BITS) >> 5] >> ((k * BITS) & 31)) & ((1u << BITS) - 1u);
-        const uint32_t q1 = (st.w[((k + 1) * BITS) >> 5] >> (((k + 1) * BITS) & 31)) & ((1u << BITS) - 1u);
-        const float w0 = __fmul_rn(__fsub_rn((float)q0, z), sc);
-        const float w1 = __fmul_rn(__fsub_rn((float)q1, z), sc);
-        o[8 * g + jj] = pack_h2(w0, w1);
-      }
+    for (int jj = 0; jj < 4; ++jj) {
+      f32x2 w;
+      w.x = __fmul_rn(__fsub_rn(qv[2 * jj], z), sc);
+      w.y = __fmul_rn(__fsub_rn(qv[2 * jj + 1], z), sc);
+      o[jj] = __builtin_bit_cast(uint32_t, __builtin_convertvector(w, f16x2));  // round to nearest even
     }
     uint4* bd = (uint4*)(Bs + buf * BN * LDA + r2 * LDA + 32 * h);
+    bd[q] = make_uint4(o[0], o[1], o[2], o[3]);
+  };
+  auto store = [&](const Stage<BITS>& st, int buf) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) bd[q] = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
+    for (int q = 0; q < 4; ++q) store_part(st, buf, q);
   };
 
   f32x16 acc[2][4];
@@ -172,11 +199,15 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillArgs p) {
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = f32x16{};
 
-  auto compute = [&](int buf) {
+  // matrix-core work of LDS buffer `buf`; after each 16-deep k step, one part of the
+  // next stage (st, into buffer `sbuf`) is dequantized and stored, so that the
+  // dequantization of one stage runs under the MFMAs of the previous one
+  auto compute = [&](int buf, const Stage<BITS>& st, int sbuf, bool do_store) {
     const uint16_t* Ab = As + buf * BM * LDA;
     const uint16_t* Bb = Bs + buf * BN * LDA;
 #pragma unroll
-    for (int kk = 0; kk < BK; kk += 16) {
+    for (int q = 0; q < BK / 16; ++q) {
+      const int kk = 16 * q;
       f16x8 af[2], bf[4];
       const int koff = kk + 8 * (lane >> 5);
 #pragma unroll
@@ -190,6 +221,7 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillArgs p) {
 #pragma unroll
         for (int b = 0; b < 4; ++b)
           acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[a], bf[b], acc[a][b], 0, 0, 0);
+      if (do_store) store_part(st, sbuf, q);
     }
   };
 
@@ -204,16 +236,14 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillArgs p) {
   for (; s + 2 <= nsteps; s += 2) {
     load(s + 2, s0);
     __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the matrix-core work
-    compute(0);
-    store(s1, 1);
+    compute(0, s1, 1, true);
     __syncthreads();
     load(s + 3, s1);
     __builtin_amdgcn_sched_barrier(0);
-    compute(1);
-    if (s + 2 < nsteps) store(s0, 0);
+    compute(1, s0, 0, s + 2 < nsteps);
     __syncthreads();
   }
-  if (s < nsteps) compute(0);  // odd number of stages: the last one is in buffer 0
+  if (s < nsteps) compute(0, s0, 1, false);  // odd number of stages: the last one is in buffer 0
 
   // epilogue: + bias, convert, store (rows/columns past the end are skipped)
 #pragma unroll
