@@ -13,11 +13,10 @@
 // Work-group: 512 threads (8 waves, two per SIMD so that one wave's matrix-core
 // work overlaps the other's dequantization and LDS traffic), output tile
 // BM x BN = 256 x 256, each wave a 64 x 128 part held as 2 x 4 MFMA blocks of
-// 32 x 32 (fp32 accumulators).  Each stage stages A[256][64] (fp16) and W16[256][64]
-// in LDS (rows padded to 72 halves so the 16-byte operand reads of a wave hit
-// distinct banks), double buffered with one barrier per stage.  The global loads
-// of a stage are issued two stages ahead into one of two register sets (buffer
-// loads: rows past the end read 0, so no address is clamped).
+// 32 x 32 (fp32 accumulators).  Per 64-deep k stage, A[256][64] (fp16) comes into
+// LDS by direct global->LDS loads and W16[256][64] is dequantized into LDS, both
+// double buffered with one barrier per stage; the dequantization of the next stage
+// is interleaved with the MFMA k steps of the current one.
 //
 // MFMA operand layout (32x32x16 f16): lane l holds row (or column) l % 32 and the 8
 // consecutive k at 8 * (l / 32); accumulator v of lane l is row 8*(v/4) + 4*(l/32)
@@ -34,7 +33,6 @@ namespace {
 constexpr int BM = 256;
 constexpr int BN = 256;
 constexpr int BK = 64;
-constexpr int LDA = BK + 8;  // padded LDS row (halves)
 constexpr int NT = 512;      // threads
 constexpr uint32_t kWord3 = 0x00020000u;  // raw buffer descriptor, 32-bit data format
 
@@ -43,17 +41,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, int64_t by
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)n, (int)kWord3);
 }
 
-// Global data of one stage for one thread: 32 halves of A (row t/2, k half t%2) and
-// 32 codes of W (row t/2, same k half) with the scale and zero point of each 16.
+// Weight data of one stage for one thread: 32 codes of W row n0 + t/2 (k half t%2)
+// with the scale and zero point of each 16.
 template <int BITS>
 struct Stage {
-  uint32_t a[16];
   uint32_t w[BITS];  // 32 codes: 2-bit -> 2 dwords, 4-bit -> 4 dwords
   _Float16 sc[2];
   _Float16 zh[2];
   uint32_t zb[2];
 };
-
 
 template <int CT>
 __device__ __forceinline__ void store_c(void* C, int64_t i, float v) {
@@ -69,15 +65,21 @@ __device__ __forceinline__ float load_bias(const void* b, int64_t i) {
   else return bf16_to_f32(((const uint16_t*)b)[i]);
 }
 
+// LDS tiles: 256 rows of 64 fp16 (128 bytes, no padding); the 16-byte piece p of row
+// r sits at piece position p ^ (r % 8), so the 16-byte operand reads of 8 consecutive
+// rows at one k hit 8 different bank groups.  A is double buffered and filled by
+// direct global->LDS loads (no registers on the way); W16 is double buffered and
+// written by the dequantization.
+__shared__ __attribute__((aligned(16))) uint8_t pf_a0[BM * 128];
+__shared__ __attribute__((aligned(16))) uint8_t pf_a1[BM * 128];
+__shared__ __attribute__((aligned(16))) uint8_t pf_b0[BN * 128];
+__shared__ __attribute__((aligned(16))) uint8_t pf_b1[BN * 128];
+
+__device__ __forceinline__ uint32_t swz(int row, int piece) { return (uint32_t)row * 128u + (uint32_t)((piece ^ (row & 7)) << 4); }
+
 template <int BITS, int ZK, int CT>
 __global__ __launch_bounds__(NT) void prefill_kernel(PrefillArgs p) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t smem_h[];
-  uint16_t* As = smem_h;                  // [2][BM * LDA]
-  uint16_t* Bs = smem_h + 2 * BM * LDA;   // [2][BN * LDA]
-
-  // tile order (work-groups are dealt round-robin over the 8 XCDs): otherwise the
-  // M tiles of one N tile run on one XCD, so the packed weights of that N tile are
-  // read into one L2
+  // tile order (work-groups are dealt round-robin over the 8 XCDs)
   const int i = blockIdx.x;
   const int x = i & 7, j = i >> 3;
   int nt, mt;
@@ -87,6 +89,8 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillArgs p) {
     mt = x;
     nt = j;
   } else {
+    // the M tiles of one N tile on one XCD: the packed weights of that N tile are
+    // read into one L2
     nt = (j / p.mtiles) * 8 + x;
     mt = j % p.mtiles;
   }
@@ -101,31 +105,44 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillArgs p) {
   const int nblk = (int)p.nblk;
   const int blog = p.block_log2;
 
-  // this thread's global rows: A row m0 + tid/2, W row n0 + tid/2, k half tid%2
+  // A rows of this thread's direct loads: wave w fills rows 32w .. 32w + 31 with four
+  // 8-row loads; lane l takes row 32w + 8i + l/8 at piece position l % 8, i.e. global
+  // piece (l % 8) ^ (row % 8).  Rows past M read row M - 1 (results unused).
+  const uint8_t* a_src[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int row = wave * 32 + q * 8 + (lane >> 3);
+    int grow = m0 + row;
+    grow = grow < (int)p.M ? grow : (int)p.M - 1;
+    const int piece = (lane & 7) ^ (row & 7);
+    a_src[q] = (const uint8_t*)p.A16 + ((int64_t)grow * Kp) * 2 + piece * 16;
+  }
+  // plain global addresses (no range check): the stage index is clamped to the last
+  // stage, so no load ever leaves the A16 rows
+  auto load_a = [&](int s, uint8_t* dst) {
+    const int sc = s < nsteps ? s : nsteps - 1;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      __builtin_amdgcn_global_load_lds((const void*)(a_src[q] + (int64_t)sc * (BK * 2)),
+                                       (__attribute__((address_space(3))) void*)(dst + (wave * 32 + q * 8) * 128),
+                                       16, 0, 0);
+  };
+
+  // this thread's W row n0 + tid/2, k half tid%2 (32 codes per stage)
   const int r2 = tid >> 1, h = tid & 1;
-  const __amdgpu_buffer_rsrc_t rA = rsrc(p.A16, p.M * (int64_t)Kp * 2);
   const __amdgpu_buffer_rsrc_t rW = rsrc(p.W, p.N * p.row_bytes);
   const __amdgpu_buffer_rsrc_t rS = rsrc(p.scales, p.N * p.nblk * 2);
   __amdgpu_buffer_rsrc_t rZ = rS;
   if constexpr (ZK == 1) rZ = rsrc(p.zp, p.N * p.zp_row_bytes);
   if constexpr (ZK == 2) rZ = rsrc(p.zp, p.N * p.nblk * 2);
-  const uint32_t a_off = (uint32_t)((int64_t)(m0 + r2) * Kp * 2) + (uint32_t)h * 64u;
   const int wrow = n0 + r2;
   const uint32_t w_off = (uint32_t)((int64_t)wrow * p.row_bytes) + (uint32_t)h * (32 * BITS / 8);
   const uint32_t s_off = (uint32_t)((int64_t)wrow * nblk * 2);
   const uint32_t z_off = (uint32_t)((int64_t)wrow * p.zp_row_bytes);
   const int kmax_blk = nblk - 1;
 
-  auto load = [&](int s, Stage<BITS>& st) {
+  auto load_w = [&](int s, Stage<BITS>& st) {
     const int k0 = s * BK;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rA, (int)(a_off + (uint32_t)k0 * 2u + 16u * q), 0, 0);
-      st.a[4 * q + 0] = v[0];
-      st.a[4 * q + 1] = v[1];
-      st.a[4 * q + 2] = v[2];
-      st.a[4 * q + 3] = v[3];
-    }
     const uint32_t wo = w_off + (uint32_t)(k0 * BITS / 8);
 #pragma unroll
     for (int d = 0; d < BITS; ++d) st.w[d] = __builtin_amdgcn_raw_buffer_load_b32(rW, (int)(wo + 4u * d), 0, 0);
@@ -143,24 +160,21 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillArgs p) {
     }
   };
 
-  // dequantize part q (codes 8q .. 8q+7) of this thread's 32 codes and write that
-  // part of both halves of the stage to LDS
-  auto store_part = [&](const Stage<BITS>& st, int buf, int q) {
-    uint4* ad = (uint4*)(As + buf * BM * LDA + r2 * LDA + 32 * h);
-    ad[q] = make_uint4(st.a[4 * q], st.a[4 * q + 1], st.a[4 * q + 2], st.a[4 * q + 3]);
+  // dequantize part q (codes 8q .. 8q+7) of this thread's 32 codes into row r2 of dst
+  auto store_part = [&](const Stage<BITS>& st, uint8_t* dst, int q) {
     const int g = q >> 1;
     const float sc = (float)st.sc[g];
     float z;
     if constexpr (ZK == 1) z = (float)(st.zb[g] & ((1u << BITS) - 1u));
     else if constexpr (ZK == 2) z = (float)st.zh[g];
     else z = p.zconst;
-    // codes 8q .. 8q+7 as exact fp32 integers, two per conversion: 2-bit codes
-    // masked into e2m1 nibbles are q/2 (scaled by 2), 4-bit codes masked into e4m3
-    // bytes are q * 2^-9 (scaled by 2^9)
+    // codes as exact fp32 integers, two per conversion: 2-bit codes masked into e2m1
+    // nibbles are q/2 (scaled by 2), 4-bit codes masked into e4m3 bytes are q * 2^-9
+    // (scaled by 2^9)
     float qv[8];
     if constexpr (BITS == 2) {
-      const uint32_t x = st.w[q >> 1] >> (16 * (q & 1));  // 8 codes in the low 16 bits
-      const uint32_t ev = x & 0x3333u, od = (x >> 2) & 0x3333u;
+      const uint32_t xw = st.w[q >> 1] >> (16 * (q & 1));  // 8 codes in the low 16 bits
+      const uint32_t ev = xw & 0x3333u, od = (xw >> 2) & 0x3333u;
       const f32x2 e0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(ev, 2.0f, 0);
       const f32x2 o0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(od, 2.0f, 0);
       const f32x2 e1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(ev, 2.0f, 1);
@@ -168,8 +182,8 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillArgs p) {
       qv[0] = e0.x; qv[2] = e0.y; qv[1] = o0.x; qv[3] = o0.y;
       qv[4] = e1.x; qv[6] = e1.y; qv[5] = o1.x; qv[7] = o1.y;
     } else {
-      const uint32_t x = st.w[q];  // 8 codes
-      const uint32_t lo = x & 0x0F0F0F0Fu, hi = (x >> 4) & 0x0F0F0F0Fu;
+      const uint32_t xw = st.w[q];  // 8 codes
+      const uint32_t lo = xw & 0x0F0F0F0Fu, hi = (xw >> 4) & 0x0F0F0F0Fu;
       const f32x2 l0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(lo, 512.0f, false);
       const f32x2 h0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hi, 512.0f, false);
       const f32x2 l1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(lo, 512.0f, true);
@@ -185,12 +199,7 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillArgs p) {
       w.y = __fmul_rn(__fsub_rn(qv[2 * jj + 1], z), sc);
       o[jj] = __builtin_bit_cast(uint32_t, __builtin_convertvector(w, f16x2));  // round to nearest even
     }
-    uint4* bd = (uint4*)(Bs + buf * BN * LDA + r2 * LDA + 32 * h);
-    bd[q] = make_uint4(o[0], o[1], o[2], o[3]);
-  };
-  auto store = [&](const Stage<BITS>& st, int buf) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) store_part(st, buf, q);
+    *(uint4*)(dst + swz(r2, 4 * h + q)) = make_uint4(o[0], o[1], o[2], o[3]);
   };
 
   f32x16 acc[2][4];
@@ -199,51 +208,61 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillArgs p) {
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = f32x16{};
 
-  // matrix-core work of LDS buffer `buf`; after each 16-deep k step, one part of the
-  // next stage (st, into buffer `sbuf`) is dequantized and stored, so that the
-  // dequantization of one stage runs under the MFMAs of the previous one
-  auto compute = [&](int buf, const Stage<BITS>& st, int sbuf, bool do_store) {
-    const uint16_t* Ab = As + buf * BM * LDA;
-    const uint16_t* Bb = Bs + buf * BN * LDA;
+  // operand rows of this lane: A rows wm*64 + 32a + lane%32, W rows wn*128 + 32b + lane%32;
+  // all have row % 8 == lane % 8
+  const uint32_t a_row0 = (uint32_t)(wm * 64 + (lane & 31)) * 128u;
+  const uint32_t b_row0 = (uint32_t)(wn * 128 + (lane & 31)) * 128u;
+  const int hi = lane >> 5, l7 = lane & 7;
+
+  // matrix-core work of one stage (tiles ab, bb); after each 16-deep k step, one part
+  // of the next stage's weights (st) is dequantized into sdst
+  auto compute = [&](const uint8_t* ab, const uint8_t* bb, const Stage<BITS>& st, uint8_t* sdst,
+                     bool do_store) {
+    f16x8 af[2][2], bf[2][4];
+    auto frags = [&](int q, f16x8 (&fa)[2], f16x8 (&fb)[4]) {
+      const uint32_t pos = (uint32_t)(((2 * q + hi) ^ l7) << 4);
+#pragma unroll
+      for (int a = 0; a < 2; ++a) fa[a] = *(const f16x8*)(ab + a_row0 + a * 32 * 128 + pos);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) fb[b] = *(const f16x8*)(bb + b_row0 + b * 32 * 128 + pos);
+    };
+    frags(0, af[0], bf[0]);
 #pragma unroll
     for (int q = 0; q < BK / 16; ++q) {
-      const int kk = 16 * q;
-      f16x8 af[2], bf[4];
-      const int koff = kk + 8 * (lane >> 5);
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
-        af[a] = *(const f16x8*)(Ab + (wm * 64 + a * 32 + (lane & 31)) * LDA + koff);
-#pragma unroll
-      for (int b = 0; b < 4; ++b)
-        bf[b] = *(const f16x8*)(Bb + (wn * 128 + b * 32 + (lane & 31)) * LDA + koff);
+      if (q + 1 < BK / 16) frags(q + 1, af[(q + 1) & 1], bf[(q + 1) & 1]);
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int b = 0; b < 4; ++b)
-          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[a], bf[b], acc[a][b], 0, 0, 0);
-      if (do_store) store_part(st, sbuf, q);
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[q & 1][a], bf[q & 1][b], acc[a][b], 0, 0, 0);
+      if (do_store) store_part(st, sdst, q);
     }
   };
 
-  Stage<BITS> s0, s1;
-  load(0, s0);
-  load(1, s1);
-  store(s0, 0);
+  // stage s computes from (pf_a[s%2], pf_b[s%2]); during it, A of stage s + 1 is
+  // loaded into pf_a[(s+1)%2], the weights of stage s + 2 into register set s%2, and
+  // the weights of stage s + 1 (register set (s+1)%2) are dequantized into
+  // pf_b[(s+1)%2].  Every load issued in a stage is waited for at its closing barrier.
+  Stage<BITS> w0, w1;
+  load_a(0, pf_a0);
+  load_w(0, w0);
+  load_w(1, w1);
   __syncthreads();
-  // stage s computes from LDS buffer s % 2 while stage s + 1 sits in a register set
-  // (in flight) and stage s + 2 is loaded into the set stage s had used
+#pragma unroll
+  for (int q = 0; q < 4; ++q) store_part(w0, pf_b0, q);
+  __syncthreads();
   int s = 0;
   for (; s + 2 <= nsteps; s += 2) {
-    load(s + 2, s0);
-    __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the matrix-core work
-    compute(0, s1, 1, true);
+    load_a(s + 1, pf_a1);
+    load_w(s + 2, w0);
+    compute(pf_a0, pf_b0, w1, pf_b1, true);
     __syncthreads();
-    load(s + 3, s1);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(1, s0, 0, s + 2 < nsteps);
+    if (s + 2 < nsteps) load_a(s + 2, pf_a0);
+    load_w(s + 3, w1);
+    compute(pf_a1, pf_b1, w0, pf_b0, s + 2 < nsteps);
     __syncthreads();
   }
-  if (s < nsteps) compute(0, s0, 1, false);  // odd number of stages: the last one is in buffer 0
+  if (s < nsteps) compute(pf_a0, pf_b0, w1, pf_b1, false);  // odd number of stages
 
   // epilogue: + bias, convert, store (rows/columns past the end are skipped)
 #pragma unroll
@@ -262,18 +281,9 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillArgs p) {
   }
 }
 
-constexpr size_t kPrefillLds = (size_t)2 * (BM + BN) * LDA * sizeof(uint16_t);
-
 template <int BITS, int ZK, int CT>
 void launch_one(const PrefillArgs& p, dim3 grid, hipStream_t st) {
-  auto k = prefill_kernel<BITS, ZK, CT>;
-  static bool attr = false;  // per instantiation
-  if (!attr) {
-    (void)hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)kPrefillLds);
-    attr = true;
-  }
-  hipLaunchKernelGGL(k, grid, dim3(NT), kPrefillLds, st, p);
+  hipLaunchKernelGGL((prefill_kernel<BITS, ZK, CT>), grid, dim3(NT), 0, st, p);
 }
 
 template <int BITS, int ZK>
