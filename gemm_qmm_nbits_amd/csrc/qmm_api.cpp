@@ -564,8 +564,8 @@ size_t qmm_nbits_workspace_bytes(int64_t M, int64_t K, int a_type) {
 }
 
 size_t qmm_codebook4_workspace_bytes(int64_t M, int64_t K, int a_type) {
-  (void)M; (void)K; (void)a_type;
-  return 0;
+  // M > 8 runs the matrix-core path, which writes A once as padded fp16 rows
+  return qmm_nbits_workspace_bytes(M, K, a_type);
 }
 
 qmm_status qmm_validate_nbits(const void* A, int a_type, int64_t M, int64_t K, int64_t N,
@@ -646,6 +646,35 @@ qmm_status qmm_codebook4(const void* A, int a_type, int64_t M, int64_t K, int64_
   if (s != QMM_OK) return s;
   if (M == 0 || N == 0) return QMM_OK;
   hipStream_t st = (hipStream_t)stream;
+  if (M > kMaxGemvM && K > 0) {
+    // matrix-core path: A -> padded fp16 once, W16 = fp16(codebook[q] * absmax) per tile
+    PrefillArgs p{};
+    const int64_t Kp = (K + 63) / 64 * 64;
+    hipError_t ce = launch_cast_pad_f16(A, a_type, M, K, Kp, (uint16_t*)workspace, st);
+    if (ce != hipSuccess) return (qmm_status)ce;
+    p.A16 = (const uint16_t*)workspace;
+    p.M = M;
+    p.N = N;
+    p.K = K;
+    p.Kp = Kp;
+    p.ldc = N;
+    p.W = W;
+    p.bits = 4;
+    p.block = block;
+    p.block_log2 = __builtin_ctz((unsigned)block);
+    p.nblk = ceil_div(K, block);
+    p.row_bytes = p.nblk * block / 2;
+    p.fmt = GEMV_CODEBOOK;
+    p.absmax = absmax;
+    p.codebook = codebook;
+    p.zp_kind = QMM_ZP_NONE;
+    p.bias = bias;
+    p.C = C;
+    p.c_type = c_type;
+    hipError_t e = launch_prefill(p, st);
+    if (e != hipSuccess) return (qmm_status)e;
+    return (qmm_status)hipGetLastError();
+  }
   GemvArgs g = make_gemv(A, a_type, M, K, N, W, 4, block, bias, C, c_type);
   g.fmt = GEMV_CODEBOOK;
   g.absmax = absmax;

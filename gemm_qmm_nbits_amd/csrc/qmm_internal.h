@@ -87,7 +87,10 @@ struct PrefillArgs {
   const uint8_t* W;
   int bits, block, block_log2;
   int64_t nblk, row_bytes;
-  const uint16_t* scales;
+  int fmt;                 // GEMV_AFFINE or GEMV_CODEBOOK
+  const uint16_t* scales;  // affine: fp16 [N][nblk]
+  const float* absmax;     // codebook: fp32 [N][nblk]
+  const float* codebook;   // codebook: fp32 [16]
   const void* zp;
   int zp_kind;
   float zconst;  // zero point for QMM_ZP_NONE / QMM_ZP_UNIFORM

@@ -46,9 +46,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, int64_t by
 template <int BITS>
 struct Stage {
   uint32_t w[BITS];  // 32 codes: 2-bit -> 2 dwords, 4-bit -> 4 dwords
-  _Float16 sc[2];
+  _Float16 sc[2];    // affine scale
   _Float16 zh[2];
   uint32_t zb[2];
+  float am[2];       // codebook absmax
 };
 
 template <int CT>
@@ -74,11 +75,16 @@ __shared__ __attribute__((aligned(16))) uint8_t pf_a0[BM * 128];
 __shared__ __attribute__((aligned(16))) uint8_t pf_a1[BM * 128];
 __shared__ __attribute__((aligned(16))) uint8_t pf_b0[BN * 128];
 __shared__ __attribute__((aligned(16))) uint8_t pf_b1[BN * 128];
+__shared__ float pf_cb[16];  // codebook (16 entries, one per bank)
 
 __device__ __forceinline__ uint32_t swz(int row, int piece) { return (uint32_t)row * 128u + (uint32_t)((piece ^ (row & 7)) << 4); }
 
-template <int BITS, int ZK, int CT>
+// FMT: GEMV_AFFINE (w = (q - zp) * s) or GEMV_CODEBOOK (BITS = 4, w = codebook[q] * absmax).
+template <int FMT, int BITS, int ZK, int CT>
 __global__ __launch_bounds__(NT) void prefill_kernel(PrefillArgs p) {
+  if constexpr (FMT == GEMV_CODEBOOK) {
+    if (threadIdx.x < 16) pf_cb[threadIdx.x] = p.codebook[threadIdx.x];
+  }
   // tile order (work-groups are dealt round-robin over the 8 XCDs)
   const int i = blockIdx.x;
   const int x = i & 7, j = i >> 3;
@@ -131,7 +137,8 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillArgs p) {
   // this thread's W row n0 + tid/2, k half tid%2 (32 codes per stage)
   const int r2 = tid >> 1, h = tid & 1;
   const __amdgpu_buffer_rsrc_t rW = rsrc(p.W, p.N * p.row_bytes);
-  const __amdgpu_buffer_rsrc_t rS = rsrc(p.scales, p.N * p.nblk * 2);
+  const __amdgpu_buffer_rsrc_t rS = FMT == GEMV_CODEBOOK ? rsrc(p.absmax, p.N * p.nblk * 4)
+                                                          : rsrc(p.scales, p.N * p.nblk * 2);
   __amdgpu_buffer_rsrc_t rZ = rS;
   if constexpr (ZK == 1) rZ = rsrc(p.zp, p.N * p.zp_row_bytes);
   if constexpr (ZK == 2) rZ = rsrc(p.zp, p.N * p.nblk * 2);
@@ -150,6 +157,10 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillArgs p) {
     for (int g = 0; g < 2; ++g) {
       int blk = (k0 + 32 * h + 16 * g) >> blog;
       blk = blk < kmax_blk ? blk : kmax_blk;  // codes past the row end meet zero A
+      if constexpr (FMT == GEMV_CODEBOOK) {
+        st.am[g] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rS, (int)(2u * s_off + 4u * blk), 0, 0));
+        continue;
+      }
       st.sc[g] = __builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(rS, (int)(s_off + 2u * blk), 0, 0));
       if constexpr (ZK == 1) {
         const int bit = blk * BITS;
@@ -163,6 +174,21 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillArgs p) {
   // dequantize part q (codes 8q .. 8q+7) of this thread's 32 codes into row r2 of dst
   auto store_part = [&](const Stage<BITS>& st, uint8_t* dst, int q) {
     const int g = q >> 1;
+    if constexpr (FMT == GEMV_CODEBOOK) {
+      // w = fp32(codebook[q] * absmax), then fp16 (round to nearest even)
+      const uint32_t xw = st.w[q];  // 8 codes
+      const float am = st.am[g];
+      uint32_t o[4];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        f32x2 w;
+        w.x = __fmul_rn(pf_cb[(xw >> (8 * jj)) & 15u], am);
+        w.y = __fmul_rn(pf_cb[(xw >> (8 * jj + 4)) & 15u], am);
+        o[jj] = __builtin_bit_cast(uint32_t, __builtin_convertvector(w, f16x2));
+      }
+      *(uint4*)(dst + swz(r2, 4 * h + q)) = make_uint4(o[0], o[1], o[2], o[3]);
+      return;
+    }
     const float sc = (float)st.sc[g];
     float z;
     if constexpr (ZK == 1) z = (float)(st.zb[g] & ((1u << BITS) - 1u));
@@ -281,16 +307,16 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillArgs p) {
   }
 }
 
-template <int BITS, int ZK, int CT>
+template <int FMT, int BITS, int ZK, int CT>
 void launch_one(const PrefillArgs& p, dim3 grid, hipStream_t st) {
-  hipLaunchKernelGGL((prefill_kernel<BITS, ZK, CT>), grid, dim3(NT), 0, st, p);
+  hipLaunchKernelGGL((prefill_kernel<FMT, BITS, ZK, CT>), grid, dim3(NT), 0, st, p);
 }
 
-template <int BITS, int ZK>
+template <int FMT, int BITS, int ZK>
 void launch_ct(const PrefillArgs& p, dim3 grid, hipStream_t st) {
-  if (p.c_type == QMM_F32) launch_one<BITS, ZK, QMM_F32>(p, grid, st);
-  else if (p.c_type == QMM_F16) launch_one<BITS, ZK, QMM_F16>(p, grid, st);
-  else launch_one<BITS, ZK, QMM_BF16>(p, grid, st);
+  if (p.c_type == QMM_F32) launch_one<FMT, BITS, ZK, QMM_F32>(p, grid, st);
+  else if (p.c_type == QMM_F16) launch_one<FMT, BITS, ZK, QMM_F16>(p, grid, st);
+  else launch_one<FMT, BITS, ZK, QMM_BF16>(p, grid, st);
 }
 
 }  // namespace
@@ -300,7 +326,7 @@ hipError_t launch_prefill(PrefillArgs p, hipStream_t st) {
   // below 2^31 bytes (one launch per slice)
   const int64_t lim = (int64_t)1 << 30;
   int64_t mstep = std::max<int64_t>(BM, (lim / (p.Kp * 2)) / BM * BM);
-  int64_t nstep = std::max<int64_t>(BN, (lim / std::max<int64_t>(p.row_bytes, p.nblk * 2)) / BN * BN);
+  int64_t nstep = std::max<int64_t>(BN, (lim / std::max<int64_t>(p.row_bytes, p.nblk * 4)) / BN * BN);
   const int zk = p.zp_kind == QMM_ZP_PACKED ? 1 : p.zp_kind == QMM_ZP_F16 ? 2 : 0;
   const size_t c_es = p.c_type == QMM_F32 ? 4 : 2;
   for (int64_t m0 = 0; m0 < p.M; m0 += mstep) {
@@ -310,7 +336,8 @@ hipError_t launch_prefill(PrefillArgs p, hipStream_t st) {
       q.N = std::min(nstep, p.N - n0);
       q.A16 = p.A16 + m0 * p.Kp;
       q.W = p.W + n0 * p.row_bytes;
-      q.scales = p.scales + n0 * p.nblk;
+      if (p.scales) q.scales = p.scales + n0 * p.nblk;
+      if (p.absmax) q.absmax = p.absmax + n0 * p.nblk;
       if (zk == 1) q.zp = (const uint8_t*)p.zp + n0 * p.zp_row_bytes;
       if (zk == 2) q.zp = (const uint16_t*)p.zp + n0 * p.nblk;
       if (p.bias) q.bias = (const uint8_t*)p.bias + n0 * (int64_t)c_es;
@@ -319,14 +346,16 @@ hipError_t launch_prefill(PrefillArgs p, hipStream_t st) {
       q.mtiles = (int)((q.M + BM - 1) / BM);
       const int64_t groups = (q.ntiles + 7) / 8;
       const dim3 grid((unsigned)(groups * 8 * q.mtiles));
-      if (q.bits == 2) {
-        if (zk == 1) launch_ct<2, 1>(q, grid, st);
-        else if (zk == 2) launch_ct<2, 2>(q, grid, st);
-        else launch_ct<2, 0>(q, grid, st);
+      if (q.fmt == GEMV_CODEBOOK) {
+        launch_ct<GEMV_CODEBOOK, 4, 0>(q, grid, st);
+      } else if (q.bits == 2) {
+        if (zk == 1) launch_ct<GEMV_AFFINE, 2, 1>(q, grid, st);
+        else if (zk == 2) launch_ct<GEMV_AFFINE, 2, 2>(q, grid, st);
+        else launch_ct<GEMV_AFFINE, 2, 0>(q, grid, st);
       } else {
-        if (zk == 1) launch_ct<4, 1>(q, grid, st);
-        else if (zk == 2) launch_ct<4, 2>(q, grid, st);
-        else launch_ct<4, 0>(q, grid, st);
+        if (zk == 1) launch_ct<GEMV_AFFINE, 4, 1>(q, grid, st);
+        else if (zk == 2) launch_ct<GEMV_AFFINE, 4, 2>(q, grid, st);
+        else launch_ct<GEMV_AFFINE, 4, 0>(q, grid, st);
       }
     }
   }

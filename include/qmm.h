@@ -94,8 +94,9 @@ enum {
  *            qmm_nbits_workspace_bytes(M, K, a_type) bytes (may be NULL when that is 0).
  * Paths: M <= 8 runs the weight-streaming GEMV, which reads A in its own type
  * and accumulates in fp32.  M > 8 runs the prefill path: A is rounded to fp16
- * once into the workspace (skipped when A is already fp16), W tiles are
- * dequantized to fp16 and multiplied on the fp16 matrix cores with fp32
+ * once into the workspace (rows of K rounded up to a multiple of 64, padded with
+ * zeros; qmm_nbits_workspace_bytes = M * that * 2 bytes for any a_type), W tiles
+ * are dequantized to fp16 and multiplied on the fp16 matrix cores with fp32
  * accumulation.
  * ------------------------------------------------------------------------- */
 qmm_status qmm_nbits(const void* A, int a_type, int64_t M, int64_t K, int64_t N,
@@ -121,8 +122,11 @@ qmm_status qmm_validate_nbits(const void* A, int a_type, int64_t M, int64_t K, i
  *   absmax   fp32 [N][nblk].
  *   codebook fp32 [16] (any values; NF4/FP4 tables are sorted in [-1, 1]).
  *   bias     [N] of c_type, or NULL.   C [M][N] of c_type.
+ *   workspace, workspace_bytes: device scratch of at least
+ *            qmm_codebook4_workspace_bytes(M, K, a_type) bytes (NULL when that is 0).
  * Paths: M <= 8 weight-streaming GEMV (fp32 FMA, codebook staged in LDS);
- * larger M uses the matrix cores with weights rounded to fp16.
+ * larger M uses the matrix cores: A rounded to fp16 once into the workspace (as
+ * for qmm_nbits), weights fp16(fp32(codebook[q] * absmax)) built tile by tile.
  * ------------------------------------------------------------------------- */
 qmm_status qmm_codebook4(const void* A, int a_type, int64_t M, int64_t K, int64_t N,
                          const uint8_t* W, int block, const float* absmax,

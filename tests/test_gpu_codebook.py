@@ -28,10 +28,28 @@ class CbDev:
         return Q.qmm_codebook4(self.A, self.W, self.absmax, self.cb, p["K"], p["block"], self.bias,
                                out=out)
 
-    def oracle(self, rows=None, w_round=None):
+    def oracle(self, rows=None, w_round=None, a_round=None):
         p = self.p
         return O.qmm_codebook4(p["A"], p["a_dtype"], p["W"], p["K"], p["block"], p["absmax"],
-                               p["codebook"], bias=p["bias"], rows=rows, w_round=w_round)
+                               p["codebook"], bias=p["bias"], rows=rows, w_round=w_round,
+                               a_round=a_round)
+
+    def check(self, y, rows=None, label=""):
+        """M <= 8: the GEMV against the exact oracle.  M > 8: the matrix-core path against
+        the oracle with its declared operand roundings (A and W to fp16); the error against
+        the exact oracle is printed for information."""
+        got = host_f64(y)
+        if rows is not None:
+            got = got[:, rows]
+        tol = TOL[self.p["a_dtype"]]
+        if self.p["A"].shape[0] > 8:
+            err = O.rel_l2(got, self.oracle(rows=rows, a_round="f16", w_round="f16"))
+            raw = O.rel_l2(got, self.oracle(rows=rows))
+            say(f"  {label} relL2(mirrored)={err:.3e} relL2(exact)={raw:.3e}")
+        else:
+            err = O.rel_l2(got, self.oracle(rows=rows))
+            say(f"  {label} relL2={err:.3e}")
+        assert err <= tol, (label, err)
 
 
 @pytest.mark.parametrize("out", ["f32", "f16"])
@@ -61,10 +79,7 @@ def test_codebook_config_shapes(name, M, a_dtype):
     d = CbDev(p)
     y = d.run()
     rows = sample_rows(N, 2048, seed=N + M)
-    ref = d.oracle(rows=rows)
-    err = O.rel_l2(host_f64(y)[:, rows], ref)
-    say(f"  relL2={err:.3e}")
-    assert err <= TOL[a_dtype], err
+    d.check(y, rows=rows, label=f"{name} M={M}")
 
 
 @pytest.mark.parametrize("M", [1, 3, 8])
@@ -83,3 +98,15 @@ def test_codebook_repeat_bit_identical():
     for i in range(128):
         d.run(out=out)
         assert np.array_equal(host_bits(out), first), i
+
+
+@pytest.mark.parametrize("M,K,N,block,a_dtype", [
+    (9, 1000, 300, 32, "bf16"),     # ragged K (last stage half padding), ragged N tile
+    (33, 4096, 257, 64, "f16"),
+    (300, 200, 64, 256, "bf16"),    # one block longer than K, two M tiles
+])
+def test_codebook_matrix_core_ragged(M, K, N, block, a_dtype):
+    """M > 8 runs the matrix-core path; ragged M, N, K and a bias."""
+    p = gen.codebook_problem(M, K, N, seed=57 + M, a_dtype=a_dtype, block=block, bias=True)
+    d = CbDev(p)
+    d.check(d.run(), label=f"M={M} K={K} N={N}")
