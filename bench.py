@@ -40,7 +40,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--legs", default="decode,prefill,qmoe", help="comma list of decode,prefill,qmoe")
+    ap.add_argument("--legs", default="decode,prefill,qmoe,codebook",
+                    help="comma list of decode,prefill,qmoe,codebook (copycal: a plain copy for counter calibration)")
     ap.add_argument("--decode-shapes", default="qkv,gate_up,down,lm_head",
                     help="subset of the phi4 layers in the decode step (profiling runs)")
     return ap.parse_args()
@@ -157,6 +158,71 @@ def decode_leg(args):
 
 
 # ---------------------------------------------------------------------------
+# codebook leg: 16-entry codebook 4-bit weights, M in {1, 4, 16, 64}, bf16 A/C
+# ---------------------------------------------------------------------------
+
+def codebook_leg(args, reps=5):
+    """Weight GB/s of qmm_codebook4 at the four codebook shapes for M = 1, 4, 16, 64:
+    bf16 A and C, block 64, weights rotated over copies >= 1 GiB, each shape's calls
+    captured in one HIP graph (M <= 8: weight-streaming GEMV; M > 8: matrix cores)."""
+    import torch
+    from gemm_qmm_nbits_amd import inputs as gen
+    from gemm_qmm_nbits_amd import qmm as Q
+
+    out = {}
+    stream = torch.cuda.current_stream()
+    for name, (K, N) in gen.CODEBOOK_SHAPES.items():
+        nblk = (K + 63) // 64
+        wbytes = N * nblk * (32 + 4)  # packed codes + fp32 absmax
+        copies = max(2, int(np.ceil((1 << 30) / wbytes)) + 1)
+        base = gen.codebook_problem(1, K, N, seed=gen.config_seed(2, 1000 + list(gen.CODEBOOK_SHAPES).index(name)))
+        cb = to_dev(base["codebook"])
+        g = torch.Generator(device="cuda")
+        g.manual_seed(N)
+        Ws = [torch.randint(0, 256, (N, nblk * 32), dtype=torch.uint8, device="cuda", generator=g)
+              for _ in range(copies)]
+        ams = [(torch.rand((N, nblk), device="cuda", generator=g) * 0.09 + 0.01) for _ in range(copies)]
+        for M in gen.CODEBOOK_M:
+            A = torch.randn((M, K), device="cuda", generator=g).to(torch.bfloat16)
+            C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+            wsb = Q.lib().qmm_codebook4_workspace_bytes(M, K, N, Q.QMM_BF16)
+            ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+
+            def call(i):
+                Q.qmm_codebook4(A, Ws[i], ams[i], cb, K, 64, None, out=C, workspace=ws if wsb else None)
+
+            for i in range(copies):
+                call(i)
+            torch.cuda.synchronize()
+            cap = torch.cuda.Stream()
+            with torch.cuda.stream(cap):
+                gr = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(gr, stream=cap):
+                    for i in range(copies):
+                        call(i)
+            torch.cuda.synchronize()
+            gr.replay()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                gr.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / (reps * copies)
+            gbs = wbytes / (us * 1e-6) / 1e9
+            out[f"{name} M={M}"] = {"K": K, "N": N, "M": M, "us": round(us, 2), "weight_GBps": round(gbs, 1),
+                                    "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                                    "path": "gemv" if M <= 8 else "matrix cores"}
+            del gr
+        del Ws, ams
+        torch.cuda.empty_cache()
+    log(f"[codebook] {len(out)} cases")
+    return out
+
+
+# ---------------------------------------------------------------------------
 # prefill leg: phi4 2-bit M = 2048 on the matrix cores
 # ---------------------------------------------------------------------------
 
@@ -175,7 +241,7 @@ def prefill_leg(args, M=2048, calls=5):
         A = torch.randn((M, K), dtype=torch.float32, device="cuda",
                         generator=torch.Generator(device="cuda").manual_seed(si))
         C = torch.empty((M, N), dtype=torch.float32, device="cuda")
-        ws = torch.empty(Q.lib().qmm_nbits_workspace_bytes(M, K, Q.QMM_F32), dtype=torch.uint8,
+        ws = torch.empty(Q.lib().qmm_nbits_workspace_bytes(M, K, N, Q.QMM_F32), dtype=torch.uint8,
                          device="cuda")
         stream = torch.cuda.current_stream()
         for _ in range(2):
@@ -402,6 +468,8 @@ def main():
     }
     if "prefill" in legs:
         out["prefill"] = prefill_leg(args)
+    if "codebook" in legs:
+        out["codebook"] = codebook_leg(args)
     if "copycal" in legs:
         out["copy_calibration"] = copy_calibration()
     if "qmoe" in legs:

@@ -425,7 +425,7 @@ qmm_status check_nbits(const void* A, int a_type, int64_t M, int64_t K, int64_t 
     return QMM_E_ALIGN;
   if (bias && !aligned(bias, dtype_size(c_type))) return QMM_E_ALIGN;
   if (zp_kind == QMM_ZP_F16 && !aligned(zp, 2)) return QMM_E_ALIGN;
-  const size_t need = qmm_nbits_workspace_bytes(M, K, a_type);
+  const size_t need = qmm_nbits_workspace_bytes(M, K, N, a_type);
   if (need > 0 && (!workspace || workspace_bytes < need)) return QMM_E_WORKSPACE;
   if (need > 0 && !aligned(workspace, 16)) return QMM_E_ALIGN;
   return QMM_OK;
@@ -446,7 +446,7 @@ qmm_status check_codebook(const void* A, int a_type, int64_t M, int64_t K, int64
       !aligned(codebook, 4))
     return QMM_E_ALIGN;
   if (bias && !aligned(bias, dtype_size(c_type))) return QMM_E_ALIGN;
-  const size_t need = qmm_codebook4_workspace_bytes(M, K, a_type);
+  const size_t need = qmm_codebook4_workspace_bytes(M, K, N, a_type);
   if (need > 0 && (!workspace || workspace_bytes < need)) return QMM_E_WORKSPACE;
   return QMM_OK;
 }
@@ -554,18 +554,29 @@ hipError_t run_gemv_rows(int entry, GemvArgs g, hipStream_t st) {
 // ===========================================================================
 extern "C" {
 
-size_t qmm_nbits_workspace_bytes(int64_t M, int64_t K, int a_type) {
+size_t qmm_nbits_workspace_bytes(int64_t M, int64_t K, int64_t N, int a_type) {
   // the prefill path (M > 8) writes A once as fp16 rows of K rounded up to 64
-  // (zero padded) into the workspace, whatever the type of A
+  // (zero padded) into the workspace, whatever the type of A; when the output tiles
+  // do not fill the chip the reduction is split and fp32 partial sums follow A
   (void)a_type;
-  if (M <= kMaxGemvM || M <= 0 || K <= 0) return 0;
-  const size_t kp = (size_t)((K + 63) / 64) * 64;
-  return ((size_t)M * kp * 2 + 255) & ~size_t(255);
+  if (M <= kMaxGemvM || M <= 0 || K <= 0 || N <= 0) return 0;
+  const int64_t kp = (K + 63) / 64 * 64;
+  const size_t a16 = ((size_t)M * (size_t)kp * 2 + 255) & ~size_t(255);
+  const int splits = prefill_splits(M, N, kp);
+  const size_t part = splits > 1 ? (size_t)splits * (size_t)M * (size_t)N * 4 : 0;
+  return a16 + part;
 }
 
-size_t qmm_codebook4_workspace_bytes(int64_t M, int64_t K, int a_type) {
-  // M > 8 runs the matrix-core path, which writes A once as padded fp16 rows
-  return qmm_nbits_workspace_bytes(M, K, a_type);
+size_t qmm_codebook4_workspace_bytes(int64_t M, int64_t K, int64_t N, int a_type) {
+  // M > 8 runs the matrix-core path, with the workspace of qmm_nbits
+  return qmm_nbits_workspace_bytes(M, K, N, a_type);
+}
+
+// Start of the fp32 partial sums inside the prefill workspace.
+static float* prefill_partials(void* workspace, int64_t M, int64_t K) {
+  const int64_t kp = (K + 63) / 64 * 64;
+  const size_t a16 = ((size_t)M * (size_t)kp * 2 + 255) & ~size_t(255);
+  return (float*)((uint8_t*)workspace + a16);
 }
 
 qmm_status qmm_validate_nbits(const void* A, int a_type, int64_t M, int64_t K, int64_t N,
@@ -606,6 +617,7 @@ qmm_status qmm_nbits(const void* A, int a_type, int64_t M, int64_t K, int64_t N,
     p.K = K;
     p.Kp = Kp;
     p.ldc = N;
+    p.partials = prefill_partials(workspace, M, K);
     p.W = W;
     p.bits = bits;
     p.block = block;
@@ -658,6 +670,7 @@ qmm_status qmm_codebook4(const void* A, int a_type, int64_t M, int64_t K, int64_
     p.K = K;
     p.Kp = Kp;
     p.ldc = N;
+    p.partials = prefill_partials(workspace, M, K);
     p.W = W;
     p.bits = 4;
     p.block = block;

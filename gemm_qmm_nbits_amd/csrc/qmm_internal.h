@@ -99,8 +99,12 @@ struct PrefillArgs {
   void* C;
   int c_type;
   int ntiles, mtiles;
+  int tiles_grid;   // work-groups per split (XCD-padded tile grid)
+  int splits, spl;  // reduction splits and stages per split
+  float* partials;  // fp32 [splits][M][ldc] workspace (splits > 1), or NULL
 };
 hipError_t launch_prefill(PrefillArgs p, hipStream_t st);
+int prefill_splits(int64_t M, int64_t N, int64_t Kp);
 
 struct QmoeArgs {
   const uint16_t* X;

@@ -86,7 +86,10 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillArgs p) {
     if (threadIdx.x < 16) pf_cb[threadIdx.x] = p.codebook[threadIdx.x];
   }
   // tile order (work-groups are dealt round-robin over the 8 XCDs)
-  const int i = blockIdx.x;
+  // blockIdx.x = ks * tiles_grid + tile index; split ks covers stages
+  // [ks * spl, min((ks + 1) * spl, nsteps)) of the reduction
+  const int ks = (int)blockIdx.x / p.tiles_grid;
+  const int i = (int)blockIdx.x - ks * p.tiles_grid;
   const int x = i & 7, j = i >> 3;
   int nt, mt;
   if (p.mtiles == 8) {
@@ -108,6 +111,8 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillArgs p) {
   const int wm = wave >> 1, wn = wave & 1;  // 4 x 2 waves, 64 x 128 each
   const int Kp = (int)p.Kp;
   const int nsteps = Kp / BK;
+  const int s_begin = ks * p.spl;
+  const int nlocal = (s_begin + p.spl < nsteps ? s_begin + p.spl : nsteps) - s_begin;
   const int nblk = (int)p.nblk;
   const int blog = p.block_log2;
 
@@ -270,26 +275,44 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillArgs p) {
   // the weights of stage s + 1 (register set (s+1)%2) are dequantized into
   // pf_b[(s+1)%2].  Every load issued in a stage is waited for at its closing barrier.
   Stage<BITS> w0, w1;
-  load_a(0, pf_a0);
-  load_w(0, w0);
-  load_w(1, w1);
+  // stage indices below are local to the split: global stage = s_begin + local
+  load_a(s_begin, pf_a0);
+  load_w(s_begin, w0);
+  load_w(s_begin + 1, w1);
   __syncthreads();
 #pragma unroll
   for (int q = 0; q < 4; ++q) store_part(w0, pf_b0, q);
   __syncthreads();
   int s = 0;
-  for (; s + 2 <= nsteps; s += 2) {
-    load_a(s + 1, pf_a1);
-    load_w(s + 2, w0);
+  for (; s + 2 <= nlocal; s += 2) {
+    load_a(s_begin + s + 1, pf_a1);
+    load_w(s_begin + s + 2, w0);
     compute(pf_a0, pf_b0, w1, pf_b1, true);
     __syncthreads();
-    if (s + 2 < nsteps) load_a(s + 2, pf_a0);
-    load_w(s + 3, w1);
-    compute(pf_a1, pf_b1, w0, pf_b0, s + 2 < nsteps);
+    if (s + 2 < nlocal) load_a(s_begin + s + 2, pf_a0);
+    load_w(s_begin + s + 3, w1);
+    compute(pf_a1, pf_b1, w0, pf_b0, s + 2 < nlocal);
     __syncthreads();
   }
-  if (s < nsteps) compute(pf_a0, pf_b0, w1, pf_b1, false);  // odd number of stages
+  if (s < nlocal) compute(pf_a0, pf_b0, w1, pf_b1, false);  // odd number of stages
 
+  if (p.splits > 1) {
+    // split reduction: fp32 partial sums of this split, summed in split order (and the
+    // bias added) by reduce_splits_kernel
+    float* P = p.partials + (int64_t)ks * p.M * p.ldc;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int col = n0 + wn * 128 + b * 32 + (lane & 31);
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = m0 + wm * 64 + a * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+          if (col < p.N && row < p.M) P[(int64_t)row * p.ldc + col] = acc[a][b][v];
+        }
+    }
+    return;
+  }
   // epilogue: + bias, convert, store (rows/columns past the end are skipped)
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
@@ -307,6 +330,21 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillArgs p) {
   }
 }
 
+// C[m][n] = (((P[0] + P[1]) + ...) + P[S-1])[m][n] + bias[n], in the type of C.
+template <int CT>
+__global__ __launch_bounds__(256) void reduce_splits_kernel(const float* P, int S, int64_t M, int64_t N,
+                                                            int64_t ldc, const void* bias, void* C) {
+  const int64_t total = M * N;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t m = i / N, n = i - m * N;
+    float v = P[m * ldc + n];
+    for (int k = 1; k < S; ++k) v += P[(int64_t)k * M * ldc + m * ldc + n];
+    if (bias) v += load_bias<CT>(bias, n);
+    store_c<CT>(C, m * ldc + n, v);
+  }
+}
+
 template <int FMT, int BITS, int ZK, int CT>
 void launch_one(const PrefillArgs& p, dim3 grid, hipStream_t st) {
   hipLaunchKernelGGL((prefill_kernel<FMT, BITS, ZK, CT>), grid, dim3(NT), 0, st, p);
@@ -321,6 +359,31 @@ void launch_ct(const PrefillArgs& p, dim3 grid, hipStream_t st) {
 
 }  // namespace
 
+int prefill_splits(int64_t M, int64_t N, int64_t Kp) {
+  // Splits of the reduction when the 256 x 256 output tiles do not fill the chip.
+  // Cost in stage times (one 256 x 256 x 64 tile step, about 2.5 us): rounds of work
+  // groups over 256 slots (one 512-thread group per compute unit) times stages per
+  // split, plus the fp32 partial sums written and read back (8 bytes per output per
+  // split at about 4 TB/s) and one more launch.  The smallest split count of least
+  // cost wins (at most 64, at most one per stage).  A function of the shape only, so
+  // the summation order never depends on the device.
+  constexpr int64_t kSlots = 256;
+  const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  const int64_t nsteps = Kp / BK;
+  if (tiles >= kSlots) return 1;
+  int best = 1;
+  double best_cost = (double)((tiles + kSlots - 1) / kSlots) * (double)nsteps;
+  for (int s = 2; s <= 64 && s <= nsteps; ++s) {
+    const double cost = (double)((tiles * s + kSlots - 1) / kSlots) * (double)((nsteps + s - 1) / s) +
+                        (double)s * (double)M * (double)N * 8.0 / 1e7 + 1.0;
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = s;
+    }
+  }
+  return best;
+}
+
 hipError_t launch_prefill(PrefillArgs p, hipStream_t st) {
   // buffer offsets are 32-bit: split M and N so that every operand slice stays
   // below 2^31 bytes (one launch per slice)
@@ -329,6 +392,7 @@ hipError_t launch_prefill(PrefillArgs p, hipStream_t st) {
   int64_t nstep = std::max<int64_t>(BN, (lim / std::max<int64_t>(p.row_bytes, p.nblk * 4)) / BN * BN);
   const int zk = p.zp_kind == QMM_ZP_PACKED ? 1 : p.zp_kind == QMM_ZP_F16 ? 2 : 0;
   const size_t c_es = p.c_type == QMM_F32 ? 4 : 2;
+  const bool sliced = mstep < p.M || nstep < p.N;
   for (int64_t m0 = 0; m0 < p.M; m0 += mstep) {
     for (int64_t n0 = 0; n0 < p.N; n0 += nstep) {
       PrefillArgs q = p;
@@ -345,7 +409,11 @@ hipError_t launch_prefill(PrefillArgs p, hipStream_t st) {
       q.ntiles = (int)((q.N + BN - 1) / BN);
       q.mtiles = (int)((q.M + BM - 1) / BM);
       const int64_t groups = (q.ntiles + 7) / 8;
-      const dim3 grid((unsigned)(groups * 8 * q.mtiles));
+      q.tiles_grid = (int)(groups * 8 * q.mtiles);
+      q.splits = prefill_splits(q.M, q.N, q.Kp);
+      q.spl = (int)((q.Kp / BK + q.splits - 1) / q.splits);
+      if (q.splits > 1 && (!p.partials || sliced)) q.splits = 1, q.spl = (int)(q.Kp / BK);
+      const dim3 grid((unsigned)(q.tiles_grid * q.splits));
       if (q.fmt == GEMV_CODEBOOK) {
         launch_ct<GEMV_CODEBOOK, 4, 0>(q, grid, st);
       } else if (q.bits == 2) {
@@ -356,6 +424,19 @@ hipError_t launch_prefill(PrefillArgs p, hipStream_t st) {
         if (zk == 1) launch_ct<GEMV_AFFINE, 4, 1>(q, grid, st);
         else if (zk == 2) launch_ct<GEMV_AFFINE, 4, 2>(q, grid, st);
         else launch_ct<GEMV_AFFINE, 4, 0>(q, grid, st);
+      }
+      if (q.splits > 1) {
+        int64_t blocks = (q.M * q.N + 255) / 256;
+        if (blocks > 16384) blocks = 16384;
+        if (q.c_type == QMM_F32)
+          hipLaunchKernelGGL(reduce_splits_kernel<QMM_F32>, dim3((unsigned)blocks), dim3(256), 0, st,
+                             q.partials, q.splits, q.M, q.N, q.ldc, q.bias, q.C);
+        else if (q.c_type == QMM_F16)
+          hipLaunchKernelGGL(reduce_splits_kernel<QMM_F16>, dim3((unsigned)blocks), dim3(256), 0, st,
+                             q.partials, q.splits, q.M, q.N, q.ldc, q.bias, q.C);
+        else
+          hipLaunchKernelGGL(reduce_splits_kernel<QMM_BF16>, dim3((unsigned)blocks), dim3(256), 0, st,
+                             q.partials, q.splits, q.M, q.N, q.ldc, q.bias, q.C);
       }
     }
   }

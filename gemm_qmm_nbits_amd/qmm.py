@@ -40,14 +40,14 @@ _SIGS = {
     "qmm_nbits": (c_int, [c_void_p, c_int, c_int64, c_int64, c_int64, c_void_p, c_int, c_int,
                           c_void_p, c_void_p, c_int, c_float, c_void_p, c_void_p, c_int,
                           c_void_p, c_size_t, c_void_p]),
-    "qmm_nbits_workspace_bytes": (c_size_t, [c_int64, c_int64, c_int]),
+    "qmm_nbits_workspace_bytes": (c_size_t, [c_int64, c_int64, c_int64, c_int]),
     "qmm_validate_nbits": (c_int, [c_void_p, c_int, c_int64, c_int64, c_int64, c_void_p, c_int,
                                    c_int, c_void_p, c_void_p, c_int, c_void_p, c_void_p, c_int,
                                    c_void_p, c_size_t]),
     "qmm_codebook4": (c_int, [c_void_p, c_int, c_int64, c_int64, c_int64, c_void_p, c_int,
                               c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_void_p, c_size_t,
                               c_void_p]),
-    "qmm_codebook4_workspace_bytes": (c_size_t, [c_int64, c_int64, c_int]),
+    "qmm_codebook4_workspace_bytes": (c_size_t, [c_int64, c_int64, c_int64, c_int]),
     "qmm_validate_codebook4": (c_int, [c_void_p, c_int, c_int64, c_int64, c_int64, c_void_p, c_int,
                                        c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_void_p,
                                        c_size_t]),
@@ -151,7 +151,7 @@ def qmm_nbits(A, W, scales, K, bits, block, zp=None, zp_kind=QMM_ZP_NONE, unifor
     ctype = dtype_code(A) if out_dtype is None else dtype_code(torch.empty(0, dtype=out_dtype))
     if out is None:
         out = torch.empty((M, N), dtype=torch_dtype(ctype), device=A.device)
-    ws_bytes = lib().qmm_nbits_workspace_bytes(M, K, dtype_code(A))
+    ws_bytes = lib().qmm_nbits_workspace_bytes(M, K, N, dtype_code(A))
     if ws_bytes and workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=A.device)
     st = lib().qmm_nbits(_ptr(A), dtype_code(A), M, K, N, _ptr(W), bits, block, _ptr(scales),
@@ -172,7 +172,7 @@ def qmm_codebook4(A, W, absmax, codebook, K, block=64, bias=None, out=None, out_
     ctype = dtype_code(A) if out_dtype is None else dtype_code(torch.empty(0, dtype=out_dtype))
     if out is None:
         out = torch.empty((M, N), dtype=torch_dtype(ctype), device=A.device)
-    ws_bytes = lib().qmm_codebook4_workspace_bytes(M, K, dtype_code(A))
+    ws_bytes = lib().qmm_codebook4_workspace_bytes(M, K, N, dtype_code(A))
     if ws_bytes and workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=A.device)
     st = lib().qmm_codebook4(_ptr(A), dtype_code(A), M, K, N, _ptr(W), block, _ptr(absmax),

@@ -91,13 +91,15 @@ enum {
  *   bias     [N] of c_type, or NULL.
  *   C        [M][N] of c_type.
  *   workspace, workspace_bytes: device scratch of at least
- *            qmm_nbits_workspace_bytes(M, K, a_type) bytes (may be NULL when that is 0).
+ *            qmm_nbits_workspace_bytes(M, K, N, a_type) bytes (may be NULL when that is 0).
  * Paths: M <= 8 runs the weight-streaming GEMV, which reads A in its own type
  * and accumulates in fp32.  M > 8 runs the prefill path: A is rounded to fp16
  * once into the workspace (rows of K rounded up to a multiple of 64, padded with
- * zeros; qmm_nbits_workspace_bytes = M * that * 2 bytes for any a_type), W tiles
- * are dequantized to fp16 and multiplied on the fp16 matrix cores with fp32
- * accumulation.
+ * zeros, for any a_type), W tiles are dequantized to fp16 and multiplied on the
+ * fp16 matrix cores with fp32 accumulation.  When the 256 x 256 output tiles do
+ * not fill the chip, the reduction over K is split into a number of parts fixed
+ * by the shape; fp32 partial sums [parts][M][N] follow A in the workspace and are
+ * added in part order by a second kernel.
  * ------------------------------------------------------------------------- */
 qmm_status qmm_nbits(const void* A, int a_type, int64_t M, int64_t K, int64_t N,
                      const uint8_t* W, int bits, int block, const uint16_t* scales,
@@ -105,7 +107,7 @@ qmm_status qmm_nbits(const void* A, int a_type, int64_t M, int64_t K, int64_t N,
                      void* C, int c_type, void* workspace, size_t workspace_bytes,
                      void* stream);
 
-size_t qmm_nbits_workspace_bytes(int64_t M, int64_t K, int a_type);
+size_t qmm_nbits_workspace_bytes(int64_t M, int64_t K, int64_t N, int a_type);
 
 /* Host-only check of qmm_nbits arguments: returns the status qmm_nbits would
  * refuse with (or QMM_OK).  Never dereferences a pointer, needs no GPU. */
@@ -123,7 +125,7 @@ qmm_status qmm_validate_nbits(const void* A, int a_type, int64_t M, int64_t K, i
  *   codebook fp32 [16] (any values; NF4/FP4 tables are sorted in [-1, 1]).
  *   bias     [N] of c_type, or NULL.   C [M][N] of c_type.
  *   workspace, workspace_bytes: device scratch of at least
- *            qmm_codebook4_workspace_bytes(M, K, a_type) bytes (NULL when that is 0).
+ *            qmm_codebook4_workspace_bytes(M, K, N, a_type) bytes (NULL when that is 0).
  * Paths: M <= 8 weight-streaming GEMV (fp32 FMA, codebook staged in LDS);
  * larger M uses the matrix cores: A rounded to fp16 once into the workspace (as
  * for qmm_nbits), weights fp16(fp32(codebook[q] * absmax)) built tile by tile.
@@ -133,7 +135,7 @@ qmm_status qmm_codebook4(const void* A, int a_type, int64_t M, int64_t K, int64_
                          const float* codebook, const void* bias, void* C, int c_type,
                          void* workspace, size_t workspace_bytes, void* stream);
 
-size_t qmm_codebook4_workspace_bytes(int64_t M, int64_t K, int a_type);
+size_t qmm_codebook4_workspace_bytes(int64_t M, int64_t K, int64_t N, int a_type);
 
 qmm_status qmm_validate_codebook4(const void* A, int a_type, int64_t M, int64_t K, int64_t N,
                                   const uint8_t* W, int block, const float* absmax,

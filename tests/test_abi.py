@@ -66,11 +66,42 @@ def test_validate_nbits_codes():
     assert _v_nbits(A=FAKE + 2, a_type=Q.QMM_F16) == 0
     assert _v_nbits(M=0, A=None, W=None, C=None) == 0   # empty problem: nothing to do
     # the prefill path needs its workspace
-    need = Q.lib().qmm_nbits_workspace_bytes(2048, 5120, Q.QMM_F32)
-    if need:
-        assert _v_nbits(M=2048, K=5120) == -7
-        assert _v_nbits(M=2048, K=5120, ws=FAKE, wsb=need - 1) == -7
-        assert _v_nbits(M=2048, K=5120, ws=FAKE, wsb=need) == 0
+    need = Q.lib().qmm_nbits_workspace_bytes(2048, 5120, 128, Q.QMM_F32)
+    assert need > 0
+    assert _v_nbits(M=2048, K=5120) == -7
+    assert _v_nbits(M=2048, K=5120, ws=FAKE, wsb=need - 1) == -7
+    assert _v_nbits(M=2048, K=5120, ws=FAKE, wsb=need) == 0
+
+
+def _splits(M, N, kp):
+    """The reduction-split rule of the prefill path, restated: least (rounds of 256
+    slots x stages per split + partial-sum traffic + 1 launch), smallest count on ties."""
+    tiles = -(-M // 256) * -(-N // 256)
+    nsteps = kp // 64
+    if tiles >= 256:
+        return 1
+    best, best_cost = 1, float(-(-tiles // 256) * nsteps)
+    for s in range(2, min(64, nsteps) + 1):
+        cost = -(-tiles * s // 256) * -(-nsteps // s) + s * M * N * 8.0 / 1e7 + 1.0
+        if cost < best_cost:
+            best, best_cost = s, cost
+    return best
+
+
+@pytest.mark.parametrize("M,K,N", [(16, 4096, 14336), (64, 4096, 1024), (2048, 17920, 5120),
+                                   (2048, 5120, 7680), (2048, 5120, 100352), (9, 70, 33),
+                                   (8, 4096, 4096)])
+def test_workspace_sizes(M, K, N):
+    """Padded fp16 A plus the fp32 partial sums of a split reduction."""
+    need = Q.lib().qmm_nbits_workspace_bytes(M, K, N, Q.QMM_BF16)
+    assert need == Q.lib().qmm_codebook4_workspace_bytes(M, K, N, Q.QMM_BF16)
+    if M <= 8:
+        assert need == 0
+        return
+    kp = -(-K // 64) * 64
+    a16 = -(-M * kp * 2 // 256) * 256
+    s = _splits(M, N, kp)
+    assert need == a16 + (s * M * N * 4 if s > 1 else 0)
 
 
 def _v_cb(**kw):
