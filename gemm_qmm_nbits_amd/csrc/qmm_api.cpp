@@ -477,6 +477,7 @@ QmoeLayout qmoe_layout(int64_t T, int64_t H, int64_t I, int k, int mode) {
 }
 
 constexpr size_t kMaxLds = 64 * 1024;
+constexpr size_t kMaxFpLds = 160 * 1024;
 
 qmm_status check_qmoe(const uint16_t* X, int64_t T, int64_t H, int64_t I, int64_t E, int k,
                       const int32_t* ids, const float* w, qmoe_weights fc1, qmoe_weights fc2,
@@ -492,6 +493,10 @@ qmm_status check_qmoe(const uint16_t* X, int64_t T, int64_t H, int64_t I, int64_
     if (H % 32 != 0 || I % 32 != 0) return QMM_E_SHAPE;
     if ((size_t)H + (size_t)(H / 32) * 8 > kMaxLds) return QMM_E_SHAPE;
     if ((size_t)(k * I) + (size_t)(k * I / 32) * 8 > kMaxLds) return QMM_E_SHAPE;
+  } else {
+    // fp mode stages x (fc1) and the k rows of h (fc2) in LDS as fp32 plus chunk sums
+    if ((size_t)ceil_div(H, 32) * 33 * 4 > kMaxFpLds) return QMM_E_SHAPE;
+    if ((size_t)k * (size_t)ceil_div(I, 32) * 33 * 4 > kMaxFpLds) return QMM_E_SHAPE;
   }
   if (T == 0) return QMM_OK;
   if (!X || !ids || !w || !Y) return QMM_E_NULL;

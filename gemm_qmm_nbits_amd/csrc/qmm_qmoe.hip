@@ -130,235 +130,409 @@ __device__ void quantize_groups_lds(LoadFn load, int n, uint32_t* q_lds, float* 
   }
 }
 
+// ---- staged activations ------------------------------------------------------------
+//
+// fp mode: the activation vector in LDS as fp32 [nch * 32] (zero past the end) and
+// the fixed-order sum of each 32-value chunk (for the zero-point fold).
+// int8 mode: codes permuted per 8 as [0 2 4 6 | 1 3 5 7], one fp32 scale and one
+// int32 code sum per 32 values.
+
+// fp32 staging of `rows` vectors of n fp16 values each (row stride n, 16-byte aligned
+// rows): xf[r][nch * 32] (zero past n) and the chunk sums sa[r][nch], in one pass:
+// each thread converts 8 values, and the 4 threads of a chunk (one quad of lanes)
+// combine their sums of 8 through DPP in a fixed order.
+__device__ __forceinline__ void stage_f32(const uint16_t* src, int rows, int n, int nch, float* xf, float* sa) {
+  const int per_row = nch * 4;  // pieces of 8 values
+  const int total = rows * per_row;
+  for (int p = threadIdx.x; p < total; p += blockDim.x) {  // quads are all in or all out
+    const int r = p / per_row;
+    const int pp = p - r * per_row;
+    const int k0 = 8 * pp;
+    const uint16_t* row = src + (int64_t)r * n;
+    float v[8];
+    if (k0 + 8 <= n) {
+      const uint4 u = *(const uint4*)(row + k0);
+      h8_to_f32(u, v);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = k0 + q < n ? f16_to_f32(row[k0 + q]) : 0.0f;
+    }
+    f32x4* d = (f32x4*)(xf + (int64_t)r * nch * 32 + k0);
+    d[0] = f32x4{v[0], v[1], v[2], v[3]};
+    d[1] = f32x4{v[4], v[5], v[6], v[7]};
+    float s8 = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+    s8 += dpp_f<kDppXor1>(s8);
+    s8 += dpp_f<kDppXor2>(s8);
+    if ((pp & 3) == 0) sa[r * nch + (pp >> 2)] = s8;
+  }
+  __syncthreads();
+}
+
+// int8 staging from codes already quantized (natural order) and their scales.
+__device__ __forceinline__ void stage_i8(const int8_t* q, const float* sc, int n, uint32_t* q_lds,
+                                         float* s_lds, int* sum_lds) {
+  const int groups = n / 32;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    const int r = i & 7;
+    const int pos = (i & ~7) + ((r & 1) ? 4 + (r >> 1) : (r >> 1));
+    ((int8_t*)q_lds)[pos] = q[i];
+  }
+  for (int g = threadIdx.x; g < groups; g += blockDim.x) {
+    int v = 0;
+    for (int i = 0; i < 32; ++i) v += q[g * 32 + i];
+    s_lds[g] = sc[g];
+    sum_lds[g] = v;
+  }
+  __syncthreads();
+}
+
+// Raw loads of one item (one 16-byte chunk of NR weight rows) of one lane.
+template <int NR>
+struct MoeItem {
+  uint4 w[NR];
+  _Float16 s[NR];
+  uint32_t z[NR];  // packed zero-point byte (unshifted)
+};
+
+constexpr int kMoeThreads = 256;
+// items per lane whose loads are in flight (ring of register sets): fc1 items carry
+// 2 * RI rows (register-heavy), fc2 items one row per R
+constexpr int kFc1Depth = 2;
+constexpr int kFc2Depth = 4;
+
 // ---- fc1 + SwiGLU ---------------------------------------------------------------
 
+// Work-group (row tile, slot t*k + j): rows i of the tile, for each the g row i and the
+// u row I + i of W1_e; each lane walks its chunks of those 2*RI rows with the loads of
+// the next chunk in flight.
 template <int INT8, int RI>
-__global__ __launch_bounds__(256) void qmoe_fc1_kernel(QmoeArgs a) {
+__global__ __launch_bounds__(kMoeThreads) void qmoe_fc1_kernel(QmoeArgs a) {
+  constexpr int NR = 2 * RI;
   extern __shared__ uint32_t smem[];
   const int slot = blockIdx.y;  // t * k + j
   const int t = slot / a.k;
   const int e = a.ids[slot];
   const uint16_t* x = a.X + (int64_t)t * a.H;
-  const int64_t nchunks = a.fc1_chunks;  // chunks holding codes k < H
-  const int64_t nblk = a.fc1_nblk;
+  const int nch = (int)a.fc1_chunks;  // chunks holding codes k < H
+  const int nblk = (int)a.fc1_nblk;
 
-  // int8 mode: quantize x_t into LDS (work-group (0, slot t*k) keeps a copy)
-  uint32_t* xq = smem;
+  float* xf = (float*)smem;          // fp mode
+  float* sa = xf + nch * 32;
+  uint32_t* xq = smem;               // int8 mode
   float* xs = (float*)(smem + a.H / 4);
   int* xsum = (int*)(xs + a.H / 32);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int lpr_log2 = a.fc1_lpr_log2;
+  const int LPR = 1 << lpr_log2;
+  const int lp = lane & (LPR - 1);
+  const int sub = lane >> lpr_log2;
+  const int SUBS = 64 >> lpr_log2;
+  const int I = (int)a.I;
+  const int i0 = ((int)blockIdx.x * (kMoeThreads >> 6) + wave) * (SUBS * RI) + sub;
+
+  const uint8_t* W = a.fc1.W + (int64_t)e * 2 * a.I * a.fc1_row_bytes;
+  const _Float16* S = (const _Float16*)a.fc1.scales + (int64_t)e * 2 * a.I * nblk;
+  const uint8_t* Z = a.fc1.zp ? a.fc1.zp + (int64_t)e * 2 * a.I * a.fc1_zp_row_bytes : nullptr;
+
+  int rowc[NR];  // rows clamped into the expert (loads always valid)
+  bool valid[NR];
+#pragma unroll
+  for (int r = 0; r < RI; ++r) {
+    const int i = i0 + r * SUBS;
+    valid[2 * r] = valid[2 * r + 1] = i < I;
+    rowc[2 * r] = i < I ? i : 0;
+    rowc[2 * r + 1] = (i < I ? i : 0) + I;
+  }
+  const int iters = (nch + LPR - 1) >> lpr_log2;
+  const int blk_shift = __builtin_ctz((unsigned)a.block) - 5;  // chunks per block = block / 32
+
+  int fit = 0;
+  auto fetch = [&](MoeItem<NR>& b) {
+    int c = fit * LPR + lp;
+    c = c < nch ? c : nch - 1;
+    const int blk = c >> blk_shift;
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      b.w[r] = *(const uint4*)(W + (int64_t)rowc[r] * a.fc1_row_bytes + c * 16);
+      b.s[r] = S[(int64_t)rowc[r] * nblk + blk];
+      if (Z) b.z[r] = Z[(int64_t)rowc[r] * a.fc1_zp_row_bytes + (blk >> 1)];
+      else b.z[r] = 0x88u;
+    }
+    ++fit;
+  };
+
+  float acc[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) acc[r] = 0.0f;
+  int cit = 0;
+  auto step = [&](const MoeItem<NR>& cb, MoeItem<NR>& nxt) {
+    fetch(nxt);
+    const int c = cit * LPR + lp;
+    const bool cv = c < nch;
+    const int cc = cv ? c : nch - 1;
+    const int blk = cc >> blk_shift;
+    if constexpr (INT8) {
+      const uint4 q0 = *(const uint4*)(xq + cc * 8);
+      const uint4 q1 = *(const uint4*)(xq + cc * 8 + 4);
+      const uint32_t qq[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+      const float sx = xs[cc];
+      const int sum = xsum[cc];
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        const int dotv = dot_chunk_u4_i8(cb.w[r], qq);
+        const int zp = (int)((cb.z[r] >> ((blk & 1) * 4)) & 0xfu);
+        const float nv = fmaf((float)cb.s[r] * sx, (float)(dotv - zp * sum), acc[r]);
+        acc[r] = cv ? nv : acc[r];
+      }
+    } else {
+      float xa[32];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const f32x4 v = *(const f32x4*)(xf + cc * 32 + 4 * q);
+        xa[4 * q] = v.x; xa[4 * q + 1] = v.y; xa[4 * q + 2] = v.z; xa[4 * q + 3] = v.w;
+      }
+      const float sac = sa[cc];
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        const float pr = dot_chunk_u4(cb.w[r], xa);
+        const float zp = (float)((cb.z[r] >> ((blk & 1) * 4)) & 0xfu);
+        const float nv = fmaf((float)cb.s[r], fmaf(-zp, sac, 512.0f * pr), acc[r]);
+        acc[r] = cv ? nv : acc[r];
+      }
+    }
+    ++cit;
+  };
+  // the first loads go out before the activations are staged
+  MoeItem<NR> buf[kFc1Depth];
+#pragma unroll
+  for (int i = 0; i < kFc1Depth - 1; ++i) fetch(buf[i]);
   if constexpr (INT8) {
     const bool keep = blockIdx.x == 0 && (slot % a.k) == 0;
     quantize_groups_lds([&](int i) { return f16_to_f32(x[i]); }, (int)a.H, xq, xs, xsum,
                         keep ? a.xq_out + (int64_t)t * a.H : nullptr,
                         keep ? a.xs_out + (int64_t)t * (a.H / 32) : nullptr);
     __syncthreads();
+  } else {
+    stage_f32(x, 1, (int)a.H, nch, xf, sa);
   }
-
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int LPR = 1 << a.fc1_lpr_log2;
-  const int lp = lane & (LPR - 1);
-  const int sub = lane >> a.fc1_lpr_log2;
-  const int SUBS = 64 >> a.fc1_lpr_log2;
-  const int64_t i0 = ((int64_t)blockIdx.x * (blockDim.x >> 6) + wave) * (SUBS * RI) + sub;
-
-  const uint8_t* W = a.fc1.W + (int64_t)e * 2 * a.I * a.fc1_row_bytes;
-  const uint16_t* S = a.fc1.scales + (int64_t)e * 2 * a.I * nblk;
-  const uint8_t* Z = a.fc1.zp ? a.fc1.zp + (int64_t)e * 2 * a.I * a.fc1_zp_row_bytes : nullptr;
-
-  int64_t rows[2 * RI];
-  bool valid[2 * RI];
+  for (int base = 0; base < iters; base += kFc1Depth) {
 #pragma unroll
-  for (int r = 0; r < RI; ++r) {
-    const int64_t i = i0 + (int64_t)r * SUBS;
-    rows[2 * r] = i;          // g row
-    rows[2 * r + 1] = i + a.I;  // u row
-    valid[2 * r] = valid[2 * r + 1] = i < a.I;
-  }
-  float acc[2 * RI];
-#pragma unroll
-  for (int r = 0; r < 2 * RI; ++r) acc[r] = 0.0f;
-
-  for (int64_t c = lp; c < nchunks; c += LPR) {
-    uint4 w[2 * RI];
-#pragma unroll
-    for (int r = 0; r < 2 * RI; ++r)
-      w[r] = valid[r] ? *(const uint4*)(W + rows[r] * a.fc1_row_bytes + c * 16) : make_uint4(0, 0, 0, 0);
-    const int64_t k0 = c * 32;
-    const int b = (int)(k0 / a.block);
-    if constexpr (INT8) {
-      const uint4 q0 = *(const uint4*)(xq + c * 8);
-      const uint4 q1 = *(const uint4*)(xq + c * 8 + 4);
-      const uint32_t qq[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-      const float sx = xs[c];
-      const int sum = xsum[c];
-#pragma unroll
-      for (int r = 0; r < 2 * RI; ++r) {
-        if (!valid[r]) continue;
-        const int dotv = dot_chunk_u4_i8(w[r], qq);
-        const int zp = (int)u4_zero_point(Z, rows[r], a.fc1_zp_row_bytes, b);
-        const float sw = f16_to_f32(S[rows[r] * nblk + b]);
-        acc[r] = fmaf(sw * sx, (float)(dotv - zp * sum), acc[r]);
-      }
-    } else {
-      float xa[32];
-      const bool full = k0 + 32 <= a.H;
-      if (full) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) h8_to_f32(*(const uint4*)(x + k0 + 8 * q), xa + 8 * q);
-      } else {
-#pragma unroll
-        for (int q = 0; q < 32; ++q) xa[q] = (k0 + q < a.H) ? f16_to_f32(x[k0 + q]) : 0.0f;
-      }
-      float sa = 0.0f;
-#pragma unroll
-      for (int q = 0; q < 32; ++q) sa += xa[q];
-#pragma unroll
-      for (int r = 0; r < 2 * RI; ++r) {
-        if (!valid[r]) continue;
-        const float p = dot_chunk_u4(w[r], xa);
-        const float zp = u4_zero_point(Z, rows[r], a.fc1_zp_row_bytes, b);
-        const float sw = f16_to_f32(S[rows[r] * nblk + b]);
-        acc[r] = fmaf(sw, fmaf(-zp, sa, 512.0f * p), acc[r]);
-      }
-    }
+    for (int i = 0; i < kFc1Depth; ++i) step(buf[i], buf[(i + kFc1Depth - 1) % kFc1Depth]);
   }
 #pragma unroll
-  for (int r = 0; r < 2 * RI; ++r) acc[r] = group_sum(acc[r], LPR);
+  for (int r = 0; r < NR; ++r) acc[r] = group_sum(acc[r], LPR);
   if (lp == 0) {
 #pragma unroll
     for (int r = 0; r < RI; ++r) {
       if (!valid[2 * r]) continue;
-      const int64_t i = rows[2 * r];
+      const int i = i0 + r * SUBS;
       float g = acc[2 * r], u = acc[2 * r + 1];
       if (a.fc1.bias) {
         const uint16_t* bb = a.fc1.bias + (int64_t)e * 2 * a.I;
         g += f16_to_f32(bb[i]);
         u += f16_to_f32(bb[i + a.I]);
       }
-      const float h = g / (1.0f + expf(-g)) * u;
-      a.h[(int64_t)slot * a.I + i] = f32_to_f16(h);
+      const float hv = g / (1.0f + expf(-g)) * u;
+      a.h[(int64_t)slot * a.I + i] = f32_to_f16(hv);
     }
+  }
+}
+
+// ---- int8 mode: quantization of h once per call ------------------------------------
+
+// One half-wave per 32-value group of h [T*k][I]: codes (natural order) and scale
+// into the scratch that fc2 stages from.
+__global__ __launch_bounds__(256) void qmoe_quant_h_kernel(const uint16_t* h, int64_t groups, int8_t* q_out,
+                                                           float* s_out) {
+  const int lane = threadIdx.x & 63;
+  const int li = lane & 31;
+  const int64_t g = ((int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)) * 2 + (lane >> 5);
+  const bool ok = g < groups;
+  const float v = ok ? f16_to_f32(h[g * 32 + li]) : 0.0f;
+  float amax = fabsf(v);
+#pragma unroll
+  for (int off = 1; off < 32; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+  int q = 0;
+  float sc = 0.0f;
+  if (amax > 0.0f) {
+    const float inv = 127.0f / amax;
+    q = (int)rintf(__fmul_rn(v, inv));
+    q = q > 127 ? 127 : (q < -127 ? -127 : q);
+    sc = amax / 127.0f;
+  }
+  if (ok) {
+    q_out[g * 32 + li] = (int8_t)q;
+    if (li == 0) s_out[g] = sc;
   }
 }
 
 // ---- fc2 + weighted combine -----------------------------------------------------
 
+// Work-group (row tile, token t): output rows n of the tile; each lane walks the
+// chunks of row n of W2_e for the k slots of the token in slot order, with the loads
+// of the next item in flight across slot boundaries; at the end of slot j the lane
+// partials are combined (fixed butterfly) and y += w_j * (z_j + b2).
 template <int INT8, int R>
-__global__ __launch_bounds__(256) void qmoe_fc2_kernel(QmoeArgs a) {
+__global__ __launch_bounds__(kMoeThreads) void qmoe_fc2_kernel(QmoeArgs a) {
   extern __shared__ uint32_t smem[];
   const int t = blockIdx.y;
   const int k = a.k;
-  const int64_t nchunks = a.fc2_chunks;  // chunks holding codes k < I
-  const int64_t nblk = a.fc2_nblk;
+  const int nch = (int)a.fc2_chunks;  // chunks holding codes k < I
+  const int nblk = (int)a.fc2_nblk;
+  const int I = (int)a.I;
   const uint16_t* hT = a.h + (int64_t)t * k * a.I;  // [k][I] fp16
 
-  uint32_t* hq = smem;                                   // [k][I] permuted codes
-  float* hs = (float*)(smem + (int64_t)k * a.I / 4);     // [k][I/32]
-  int* hsum = (int*)(hs + (int64_t)k * a.I / 32);        // [k][I/32]
-  if constexpr (INT8) {
-    const bool keep = blockIdx.x == 0;
-    quantize_groups_lds([&](int i) { return f16_to_f32(hT[i]); }, (int)(k * a.I), hq, hs, hsum,
-                        keep ? a.hq_out + (int64_t)t * k * a.I : nullptr,
-                        keep ? a.hs_out + (int64_t)t * k * (a.I / 32) : nullptr);
-    __syncthreads();
-  }
+  float* hf = (float*)smem;                         // fp: [k][nch * 32]
+  float* sa = hf + (int64_t)k * nch * 32;           // fp: [k][nch]
+  uint32_t* hq = smem;                              // int8: [k][I] permuted codes
+  float* hs = (float*)(smem + (int64_t)k * a.I / 4);
+  int* hsum = (int*)(hs + (int64_t)k * a.I / 32);
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int LPR = 1 << a.fc2_lpr_log2;
+  const int lpr_log2 = a.fc2_lpr_log2;
+  const int LPR = 1 << lpr_log2;
   const int lp = lane & (LPR - 1);
-  const int sub = lane >> a.fc2_lpr_log2;
-  const int SUBS = 64 >> a.fc2_lpr_log2;
-  const int64_t n0 = ((int64_t)blockIdx.x * (blockDim.x >> 6) + wave) * (SUBS * R) + sub;
+  const int sub = lane >> lpr_log2;
+  const int SUBS = 64 >> lpr_log2;
+  const int H = (int)a.H;
+  const int n0 = ((int)blockIdx.x * (kMoeThreads >> 6) + wave) * (SUBS * R) + sub;
 
-  int64_t rows[R];
+  int rowc[R];
   bool valid[R];
-  float y[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    rows[r] = n0 + (int64_t)r * SUBS;
-    valid[r] = rows[r] < a.H;
-    y[r] = 0.0f;
+    const int n = n0 + r * SUBS;
+    valid[r] = n < H;
+    rowc[r] = n < H ? n : 0;
   }
+  const int iters = (nch + LPR - 1) >> lpr_log2;
+  const int total = k * iters;
+  const int blk_shift = __builtin_ctz((unsigned)a.block) - 5;
 
-  for (int j = 0; j < k; ++j) {
-    const int e = a.ids[t * k + j];
-    const float rw = a.rw[t * k + j];
+  // fetch cursor (slot fj, item fit)
+  int fj = 0, fit = 0;
+  auto fetch = [&](MoeItem<R>& b) {
+    const int jj = fj < k ? fj : k - 1;
+    const int e = a.ids[t * k + jj];
     const uint8_t* W = a.fc2.W + (int64_t)e * a.H * a.fc2_row_bytes;
-    const uint16_t* S = a.fc2.scales + (int64_t)e * a.H * nblk;
-    const uint8_t* Z = a.fc2.zp ? a.fc2.zp + (int64_t)e * a.H * a.fc2_zp_row_bytes : nullptr;
-    const uint16_t* hj = hT + (int64_t)j * a.I;
-    float acc[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) acc[r] = 0.0f;
-    for (int64_t c = lp; c < nchunks; c += LPR) {
-      uint4 w[R];
-#pragma unroll
-      for (int r = 0; r < R; ++r)
-        w[r] = valid[r] ? *(const uint4*)(W + rows[r] * a.fc2_row_bytes + c * 16) : make_uint4(0, 0, 0, 0);
-      const int64_t k0 = c * 32;
-      const int b = (int)(k0 / a.block);
-      if constexpr (INT8) {
-        const uint32_t* qg = hq + ((int64_t)j * a.I + k0) / 4;
-        const uint4 q0 = *(const uint4*)(qg);
-        const uint4 q1 = *(const uint4*)(qg + 4);
-        const uint32_t qq[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-        const int gi = (int)((j * a.I + k0) / 32);
-        const float sx = hs[gi];
-        const int sum = hsum[gi];
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-          if (!valid[r]) continue;
-          const int dotv = dot_chunk_u4_i8(w[r], qq);
-          const int zp = (int)u4_zero_point(Z, rows[r], a.fc2_zp_row_bytes, b);
-          const float sw = f16_to_f32(S[rows[r] * nblk + b]);
-          acc[r] = fmaf(sw * sx, (float)(dotv - zp * sum), acc[r]);
-        }
-      } else {
-        float xa[32];
-        const bool full = k0 + 32 <= a.I;
-        if (full) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) h8_to_f32(*(const uint4*)(hj + k0 + 8 * q), xa + 8 * q);
-        } else {
-#pragma unroll
-          for (int q = 0; q < 32; ++q) xa[q] = (k0 + q < a.I) ? f16_to_f32(hj[k0 + q]) : 0.0f;
-        }
-        float sa = 0.0f;
-#pragma unroll
-        for (int q = 0; q < 32; ++q) sa += xa[q];
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-          if (!valid[r]) continue;
-          const float p = dot_chunk_u4(w[r], xa);
-          const float zp = u4_zero_point(Z, rows[r], a.fc2_zp_row_bytes, b);
-          const float sw = f16_to_f32(S[rows[r] * nblk + b]);
-          acc[r] = fmaf(sw, fmaf(-zp, sa, 512.0f * p), acc[r]);
-        }
-      }
-    }
+    const _Float16* S = (const _Float16*)a.fc2.scales + (int64_t)e * a.H * nblk;
+    int c = fit * LPR + lp;
+    c = c < nch ? c : nch - 1;
+    const int blk = c >> blk_shift;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const float z = group_sum(acc[r], LPR) +
-                      ((a.fc2.bias && valid[r]) ? f16_to_f32(a.fc2.bias[(int64_t)e * a.H + rows[r]]) : 0.0f);
-      y[r] = fmaf(rw, z, y[r]);
+      b.w[r] = *(const uint4*)(W + (int64_t)rowc[r] * a.fc2_row_bytes + c * 16);
+      b.s[r] = S[(int64_t)rowc[r] * nblk + blk];
+      if (a.fc2.zp)
+        b.z[r] = a.fc2.zp[((int64_t)e * a.H + rowc[r]) * a.fc2_zp_row_bytes + (blk >> 1)];
+      else
+        b.z[r] = 0x88u;
     }
+    if (++fit == iters) {
+      fit = 0;
+      ++fj;
+    }
+  };
+
+  float acc[R], y[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = y[r] = 0.0f;
+  int cj = 0, cit = 0;
+  auto step = [&](const MoeItem<R>& cb, MoeItem<R>& nxt, bool live) {
+    fetch(nxt);
+    const int c = cit * LPR + lp;
+    const bool cv = live && c < nch;
+    const int cc = c < nch ? c : nch - 1;
+    const int jj = cj < k ? cj : k - 1;
+    const int blk = cc >> blk_shift;
+    if constexpr (INT8) {
+      const uint32_t* qg = hq + (jj * I + cc * 32) / 4;
+      const uint4 q0 = *(const uint4*)(qg);
+      const uint4 q1 = *(const uint4*)(qg + 4);
+      const uint32_t qq[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+      const int gi = (jj * I + cc * 32) / 32;
+      const float sx = hs[gi];
+      const int sum = hsum[gi];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int dotv = dot_chunk_u4_i8(cb.w[r], qq);
+        const int zp = (int)((cb.z[r] >> ((blk & 1) * 4)) & 0xfu);
+        const float nv = fmaf((float)cb.s[r] * sx, (float)(dotv - zp * sum), acc[r]);
+        acc[r] = cv ? nv : acc[r];
+      }
+    } else {
+      const float* xp = hf + ((int64_t)jj * nch + cc) * 32;
+      float xa[32];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const f32x4 v = *(const f32x4*)(xp + 4 * q);
+        xa[4 * q] = v.x; xa[4 * q + 1] = v.y; xa[4 * q + 2] = v.z; xa[4 * q + 3] = v.w;
+      }
+      const float sac = sa[jj * nch + cc];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float pr = dot_chunk_u4(cb.w[r], xa);
+        const float zp = (float)((cb.z[r] >> ((blk & 1) * 4)) & 0xfu);
+        const float nv = fmaf((float)cb.s[r], fmaf(-zp, sac, 512.0f * pr), acc[r]);
+        acc[r] = cv ? nv : acc[r];
+      }
+    }
+    if (live && cit == iters - 1) {
+      // slot cj complete: z = butterfly(acc) + b2, y += w * z (slot order)
+      const int e = a.ids[t * k + cj];
+      const float rw = a.rw[t * k + cj];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float z = group_sum(acc[r], LPR) +
+                        ((a.fc2.bias && valid[r]) ? f16_to_f32(a.fc2.bias[(int64_t)e * a.H + rowc[r]]) : 0.0f);
+        y[r] = fmaf(rw, z, y[r]);
+        acc[r] = 0.0f;
+      }
+    }
+    if (++cit == iters) {
+      cit = 0;
+      ++cj;
+    }
+  };
+  // the first loads go out before the activations are staged
+  MoeItem<R> buf[kFc2Depth];
+#pragma unroll
+  for (int i = 0; i < kFc2Depth - 1; ++i) fetch(buf[i]);
+  if constexpr (INT8) {
+    stage_i8(a.hq_out + (int64_t)t * k * a.I, a.hs_out + (int64_t)t * k * (a.I / 32), k * I, hq, hs, hsum);
+  } else {
+    stage_f32(hT, k, I, nch, hf, sa);
+  }
+  for (int base = 0; base < total; base += kFc2Depth) {
+#pragma unroll
+    for (int i = 0; i < kFc2Depth; ++i)
+      step(buf[i], buf[(i + kFc2Depth - 1) % kFc2Depth], base + i < total);
   }
   if (lp == 0) {
 #pragma unroll
     for (int r = 0; r < R; ++r)
-      if (valid[r]) a.Y[(int64_t)t * a.H + rows[r]] = f32_to_f16(y[r]);
+      if (valid[r]) a.Y[(int64_t)t * a.H + n0 + r * SUBS] = f32_to_f16(y[r]);
   }
 }
 
 // ---- launch ---------------------------------------------------------------------
 
 size_t qmoe_fc1_lds_bytes(const QmoeArgs& a) {
-  return a.mode == QMOE_INT8_ACT ? (size_t)a.H + (size_t)(a.H / 32) * 8 : 0;
+  if (a.mode == QMOE_INT8_ACT) return (size_t)a.H + (size_t)(a.H / 32) * 8;
+  return (size_t)a.fc1_chunks * 33 * sizeof(float);
 }
 size_t qmoe_fc2_lds_bytes(const QmoeArgs& a) {
-  return a.mode == QMOE_INT8_ACT ? (size_t)(a.k * a.I) + (size_t)(a.k * a.I / 32) * 8 : 0;
+  if (a.mode == QMOE_INT8_ACT) return (size_t)(a.k * a.I) + (size_t)(a.k * a.I / 32) * 8;
+  return (size_t)a.k * a.fc2_chunks * 33 * sizeof(float);
+}
+
+// Allow more than 64 KB of dynamic LDS for a kernel (once per kernel).
+template <typename Kern>
+static void allow_lds(Kern k, size_t lds) {
+  if (lds > 64 * 1024) (void)hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
 }
 
 hipError_t launch_qmoe_fc1(const QmoeArgs& a, int rows_per_lane, hipStream_t st) {
@@ -370,8 +544,10 @@ hipError_t launch_qmoe_fc1(const QmoeArgs& a, int rows_per_lane, hipStream_t st)
     if (rows_per_lane == 1) hipLaunchKernelGGL((qmoe_fc1_kernel<1, 1>), grid, dim3(256), lds, st, a);
     else hipLaunchKernelGGL((qmoe_fc1_kernel<1, 2>), grid, dim3(256), lds, st, a);
   } else {
-    if (rows_per_lane == 1) hipLaunchKernelGGL((qmoe_fc1_kernel<0, 1>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((qmoe_fc1_kernel<0, 2>), grid, dim3(256), 0, st, a);
+    allow_lds(qmoe_fc1_kernel<0, 1>, lds);
+    allow_lds(qmoe_fc1_kernel<0, 2>, lds);
+    if (rows_per_lane == 1) hipLaunchKernelGGL((qmoe_fc1_kernel<0, 1>), grid, dim3(256), lds, st, a);
+    else hipLaunchKernelGGL((qmoe_fc1_kernel<0, 2>), grid, dim3(256), lds, st, a);
   }
   return hipSuccess;
 }
@@ -382,11 +558,18 @@ hipError_t launch_qmoe_fc2(const QmoeArgs& a, int rows_per_lane, hipStream_t st)
   const dim3 grid((unsigned)((a.H + rows_per_wg - 1) / rows_per_wg), (unsigned)a.T);
   const size_t lds = qmoe_fc2_lds_bytes(a);
   if (a.mode == QMOE_INT8_ACT) {
+    // h -> int8 codes and scales once (into the scratch fc2 stages from)
+    const int64_t groups = a.T * a.k * a.I / 32;
+    const int64_t blocks = (groups + 7) / 8;
+    hipLaunchKernelGGL(qmoe_quant_h_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a.h, groups, a.hq_out,
+                       a.hs_out);
     if (rows_per_lane == 1) hipLaunchKernelGGL((qmoe_fc2_kernel<1, 1>), grid, dim3(256), lds, st, a);
     else hipLaunchKernelGGL((qmoe_fc2_kernel<1, 2>), grid, dim3(256), lds, st, a);
   } else {
-    if (rows_per_lane == 1) hipLaunchKernelGGL((qmoe_fc2_kernel<0, 1>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((qmoe_fc2_kernel<0, 2>), grid, dim3(256), 0, st, a);
+    allow_lds(qmoe_fc2_kernel<0, 1>, lds);
+    allow_lds(qmoe_fc2_kernel<0, 2>, lds);
+    if (rows_per_lane == 1) hipLaunchKernelGGL((qmoe_fc2_kernel<0, 1>), grid, dim3(256), lds, st, a);
+    else hipLaunchKernelGGL((qmoe_fc2_kernel<0, 2>), grid, dim3(256), lds, st, a);
   }
   return hipSuccess;
 }
