@@ -40,8 +40,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--legs", default="decode,prefill,qmoe,codebook",
-                    help="comma list of decode,prefill,qmoe,codebook (copycal: a plain copy for counter calibration)")
+    ap.add_argument("--legs", default="decode,stack,prefill,qmoe,codebook",
+                    help="comma list of decode,stack,prefill,qmoe,codebook "
+                         "(copycal: a plain copy for counter calibration)")
     ap.add_argument("--decode-shapes", default="qkv,gate_up,down,lm_head",
                     help="subset of the phi4 layers in the decode step (profiling runs)")
     return ap.parse_args()
@@ -155,6 +156,65 @@ def decode_leg(args):
     same = all(torch.equal(r, L["C"]) for r, L in zip(eager_ref, sets[0]))
     return {"step_bytes": step_bytes, "step_ms": step_ms, "wall_s": wall, "shapes": shapes_out,
             "copies": copies, "graph_replay_matches_eager": bool(same)}
+
+
+# ---------------------------------------------------------------------------
+# stack leg: the phi4-14B 2-bit decode stack, 40 x (qkv, gate_up, down) + lm_head
+# ---------------------------------------------------------------------------
+
+def stack_leg(args, layers=40, reps=10):
+    """One decode token through 40 layers of distinct phi4 2-bit weights (qkv, gate_up,
+    down) and the lm_head, M = 1, fp32 A/C, uniform zp 1.5, captured as one HIP graph
+    of 121 GEMV launches (3.68 GB of weights: every replay streams them cold)."""
+    import torch
+    from gemm_qmm_nbits_amd import inputs as gen
+    from gemm_qmm_nbits_amd import qmm as Q
+
+    g = torch.Generator(device="cuda")
+    g.manual_seed(4242)
+    shapes = [gen.PHI4_SHAPES[n] for n in ("qkv", "gate_up", "down")]
+    calls = []
+    total = 0
+    for li in range(layers + 1):
+        for (K, N) in (shapes if li < layers else [gen.PHI4_SHAPES["lm_head"]]):
+            nblk = (K + 63) // 64
+            W = torch.randint(0, 256, (N, nblk * 16), dtype=torch.uint8, device="cuda", generator=g)
+            S = (torch.rand((N, nblk), device="cuda", generator=g) * 0.04 + 0.01).half()
+            A = torch.randn((1, K), device="cuda", generator=g)
+            C = torch.empty((1, N), device="cuda")
+            calls.append((A, W, S, K, C))
+            total += weight_bytes_nbits(K, N)
+
+    def token():
+        for (A, W, S, K, C) in calls:
+            Q.qmm_nbits(A, W, S, K, 2, 64, None, Q.QMM_ZP_UNIFORM, 1.5, out=C)
+
+    token()
+    torch.cuda.synchronize()
+    cap = torch.cuda.Stream()
+    with torch.cuda.stream(cap):
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr, stream=cap):
+            token()
+    torch.cuda.synchronize()
+    gr.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        gr.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    gbs = total / (ms * 1e-3) / 1e9
+    del gr, calls
+    torch.cuda.empty_cache()
+    log(f"[stack] {layers} layers + lm_head: {ms:.3f} ms/token")
+    return {"layers": layers, "weight_GB_per_token": round(total / 1e9, 3), "ms_per_token": round(ms, 4),
+            "tok_per_s": round(1e3 / ms, 1), "weight_GBps": round(gbs, 1),
+            "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "launches_per_token": 3 * layers + 1}
 
 
 # ---------------------------------------------------------------------------
@@ -468,6 +528,8 @@ def main():
     }
     if "prefill" in legs:
         out["prefill"] = prefill_leg(args)
+    if "stack" in legs:
+        out["phi4_stack"] = stack_leg(args)
     if "codebook" in legs:
         out["codebook"] = codebook_leg(args)
     if "copycal" in legs:
