@@ -464,7 +464,7 @@ def roofline_entry(dec):
         return None
     lm = dec["shapes"]["lm_head"]
     achieved = lm["GBps"]
-    r = {"bound": "hbm", "kernel": "gemv_kernel<affine, u2, fp32 A, M=1> on lm_head 5120x100352",
+    r = {"bound": "hbm", "kernel": "gemv_ip_stream_kernel (u2, fp32 A, M=1) on lm_head 5120x100352",
          "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
          "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
          "algorithmic_bytes_per_launch": int(weight_bytes_nbits(5120, 100352)),
