@@ -422,29 +422,68 @@ def qmoe_leg(args, name, T, H, I, E, k, block, zp, bias, mode, calls=48):
 # CPU baseline: the oracle on a bounded sample of the decode workload
 # ---------------------------------------------------------------------------
 
-def cpu_baseline():
-    """The oracle, as it stands, on one full decode step (the four phi4 layers at M = 1)."""
-    from threadpoolctl import threadpool_limits
-
+def _oracle_samples():
+    """(name, weight bytes, callable) for the bounded oracle samples: one full decode step
+    of the four phi4 layers at M = 1, one codebook layer at M = 1, one MoE token."""
     from gemm_qmm_nbits_amd import inputs as gen
     from oracle import qmm_oracle as O
 
-    total_b = 0
-    total_s = 0.0
-    with threadpool_limits(limits=1):
+    def decode_step():
         for si, (name, (K, N)) in enumerate(gen.PHI4_SHAPES.items()):
             p = gen.nbits_problem(1, K, N, 2, 64, seed=gen.config_seed(1, si), zp="none",
                                   scale_range=(0.01, 0.05))
             t0 = time.perf_counter()
             O.qmm_nbits(p["A"], "f32", p["W"], 2, K, 64, p["scales"], None, O.ZP_UNIFORM,
                         uniform_zp=1.5)
-            total_s += time.perf_counter() - t0
-            total_b += weight_bytes_nbits(K, N)
+            yield time.perf_counter() - t0
             del p
-    return {"value": round(total_b / total_s / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
+
+    def codebook_up():
+        K, N = gen.CODEBOOK_SHAPES["up"]
+        p = gen.codebook_problem(1, K, N, seed=gen.config_seed(2, 2))
+        t0 = time.perf_counter()
+        O.qmm_codebook4(p["A"], "bf16", p["W"], K, 64, p["absmax"], p["codebook"])
+        yield time.perf_counter() - t0
+
+    def moe_token():
+        c = gen.QMOE_GPT_OSS
+        p = gen.qmoe_problem(1, c["H"], c["I"], c["E"], c["k"], 64, seed=gen.config_seed(3, 1))
+        t0 = time.perf_counter()
+        O.qmoe_decode(p["X"], p["ids"], p["rw"], p["fc1"], p["fc2"], c["H"], c["I"], 64)
+        yield time.perf_counter() - t0
+
+    c = gen.QMOE_GPT_OSS
+    moe_b = c["k"] * (weight_bytes_nbits(c["H"], 2 * c["I"], bits=4) +
+                      weight_bytes_nbits(c["I"], c["H"], bits=4))
+    Kc, Nc = gen.CODEBOOK_SHAPES["up"]
+    return [("decode step (qkv, gate_up, down, lm_head; u2, M=1)",
+             sum(weight_bytes_nbits(K, N) for K, N in gen.PHI4_SHAPES.values()), decode_step),
+            ("codebook up 4096x14336, M=1", Nc * (Kc // 2) + Nc * (Kc // 64) * 4, codebook_up),
+            ("GPT-OSS-20B MoE, one token, block 64 (4 experts)", moe_b, moe_token)]
+
+
+def cpu_baseline():
+    """The oracle, as it stands, on bounded samples of the workloads, with one thread and
+    with the host's cores (numpy's BLAS threads; capped at 16, one GPU's share of a host)."""
+    from threadpoolctl import threadpool_limits
+
+    all_cores = min(16, len(os.sched_getaffinity(0)))
+    runs = {}
+    for threads in (1, all_cores):
+        res = []
+        with threadpool_limits(limits=threads):
+            for name, nbytes, fn in _oracle_samples():
+                secs = sum(fn())
+                res.append({"sample": name, "weight_MB": round(nbytes / 1e6, 3),
+                            "s_per_call": round(secs, 4), "GBps": round(nbytes / secs / 1e9, 4)})
+        runs[threads] = res
+    head = runs[1][0]
+    return {"value": head["GBps"], "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"one full decode step (qkv, gate_up, down, lm_head at M=1): "
-                      f"{total_b / 1e6:.1f} MB of weights in {total_s:.1f} s, numpy fp64, 1 thread"}
+                      f"{head['weight_MB']:.1f} MB of weights in {head['s_per_call']:.1f} s, "
+                      f"numpy fp64, 1 thread",
+            "all_cores": {"cores": all_cores, "value": runs[all_cores][0]["GBps"], "unit": "GB/s"},
+            "samples": {"1_thread": runs[1], f"{all_cores}_threads": runs[all_cores]}}
 
 
 def copy_calibration(nbytes=256 << 20, calls=5):
