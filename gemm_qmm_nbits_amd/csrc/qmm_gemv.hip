@@ -130,7 +130,8 @@ void gemv_plan(GemvArgs& g, int num_cus) {
   if (iters < 1) iters = 1;
   if (iters > iters_all) iters = iters_all > 0 ? iters_all : 1;
   g.slice_chunks = (int)(iters * lpr);
-  // A slice + group records + codebook; the kernel adds its output buffer
+  // A slice + group records + 16 floats (the codebook kernel's table, the integer-plane
+  // kernels' trash line); the kernel adds its output buffer
   g.lds_bytes = (size_t)(iters * per_iter) + 16 * sizeof(float);
   const size_t total = g.lds_bytes + 4096 * sizeof(float);
   if (total > kMaxGemvLds) {

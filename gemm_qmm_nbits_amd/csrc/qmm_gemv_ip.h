@@ -27,6 +27,8 @@
 #pragma once
 #include "qmm_gemv_impl.h"
 
+#include <type_traits>
+
 namespace qmm {
 
 #ifndef QMM_IP_DEPTH
@@ -55,139 +57,260 @@ struct IpLayout {
   static constexpr int SLOT = 4 * PWD + 4;             // words per chunk slot (52 / 28)
 };
 
+// Nibble planes of eight 24-bit values: word p (p = 0..5) holds digit p (bits 4p..4p+3)
+// of value i in nibble i.  x holds byte k of values 0, 2, 4, 6 and y of values 1, 3,
+// 5, 7 (built by byte_gather), so the even digit 2k of value 2b is the low nibble
+// of byte b of x_k.
+__device__ __forceinline__ void byte_gather(uint32_t a, uint32_t b, uint32_t c, uint32_t d, uint32_t (&x)[3]) {
+  // x[k] = [byte k of a, byte k of b, byte k of c, byte k of d] (a in byte 0)
+  const uint32_t ab = __builtin_amdgcn_perm(b, a, 0x05010400u);  // a0 b0 a1 b1
+  const uint32_t cd = __builtin_amdgcn_perm(d, c, 0x05010400u);  // c0 d0 c1 d1
+  x[0] = __builtin_amdgcn_perm(cd, ab, 0x05040100u);
+  x[1] = __builtin_amdgcn_perm(cd, ab, 0x07060302u);
+  x[2] = __builtin_amdgcn_perm(b, a, 0x0c0c0602u) | __builtin_amdgcn_perm(d, c, 0x06020c0cu);
+}
+__device__ __forceinline__ void nibble_planes(const uint32_t (&x)[3], const uint32_t (&y)[3], uint32_t (&w)[6]) {
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    w[2 * k] = (x[k] & 0x0F0F0F0Fu) | ((y[k] << 4) & 0xF0F0F0F0u);
+    w[2 * k + 1] = ((x[k] >> 4) & 0x0F0F0F0Fu) | (y[k] & 0xF0F0F0F0u);
+  }
+}
+
 // Stage chunks [c0, c0 + SC) of every A row as planes; meta[(m*4+gi)*SC + slot] =
 // {2^(e-22), sum a} for scale group gi of the slot.  A group whose largest |a| is
 // not finite gets a NaN step, so the rows it meets come out NaN.
-template <int BITS, int AT, int G>
-__device__ __forceinline__ void stage_planes(const GemvArgs& g, uint32_t* planes, f32x2* meta, int c0,
-                                             int SC) {
+//
+// Each thread converts 16 consecutive activations (one 2-bit weight dword, two
+// 4-bit ones): the 12 plane words they fill are contiguous in the slot, so they
+// are built in registers and written as three 16-byte stores.  A scale group of G
+// codes spans G / 16 neighbouring lanes; its maximum and sum are DPP butterflies.
+// `issued` runs once (there is at least one piece), right after the loads of the
+// first batch are issued: a caller
+// that starts its own loads there (the first weights of its stream) lets them travel
+// while the activations are converted, and waiting for the activations, which are
+// issued first, does not wait for them (vector loads complete in order).
+// AVEC: rows of A allow 4-element vector loads.  Loads are branch-free, so all loads
+// of a batch are in flight together.  BUF (A below 2 GiB): raw buffer loads, with an
+// offset past the buffer's range for an element past the row or a piece past the
+// last, which returns 0 and fetches nothing.  Otherwise global loads, whose address
+// is replaced by the first element and whose value by a select.
+template <int BITS, int AT, int G, int MT, bool AVEC, bool BUF, typename Issued>
+__device__ __forceinline__ void stage_planes_impl(const GemvArgs& g, uint32_t* planes, f32x2* meta,
+                                                  uint32_t* trash, int c0, int SC, Issued&& issued) {
   using L = IpLayout<BITS>;
   constexpr int WPC = 128 / BITS;
-  constexpr int NB = 8;  // float4 pieces per thread whose loads are issued together
-  const int per_row = SC * (WPC / 4);  // float4 pieces per A row in the slice
+  constexpr int PPC = WPC / 16;  // 16-value pieces per chunk (4 or 2)
+  constexpr int NB = 2;          // pieces per thread whose loads are issued together
+  const int per_row = SC * PPC;
   const int total = (int)g.M * per_row;
   const int K = (int)g.K;
-  constexpr int gw = G / 4;  // threads per scale group (4, 8 or 16: aligned groups of lanes)
-  auto load = [&](int idx, float (&v)[4]) {
-    v[0] = v[1] = v[2] = v[3] = 0.0f;
-    if (idx >= total) return;
-    const int m = idx / per_row;
-    const int rem = idx - m * per_row;
-    const int k = (c0 * WPC) + 4 * rem;
-    const int64_t base = (int64_t)m * K + k;
-    if (g.a_vec && k + 3 < K) {
-      if constexpr (AT == QMM_F32) {
-        const f32x4 x = *(const f32x4*)((const float*)g.A + base);
-        v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
-      } else {
-        const uint2 u = *(const uint2*)((const uint16_t*)g.A + base);
-        const uint32_t w[2] = {u.x, u.y};
+  constexpr int gw = G / 16;  // threads per scale group (1, 2 or 4: aligned groups of lanes)
+  static_assert(gw == 1 || gw == 2 || gw == 4, "scale group of 16, 32 or 64 codes");
+  constexpr uint32_t ES = AT == QMM_F32 ? 4 : 2;
+  constexpr uint32_t kOut = 0x80000000u;  // past the buffer's range (< 2^31 bytes)
+  const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(g.A), (short)0, BUF ? (int)((uint32_t)g.M * (uint32_t)K * ES) : 0, 0x00020000);
+  const uint32_t trash_word = (uint32_t)(trash - planes);
+  const uint32_t meta_word = (uint32_t)((uint32_t*)meta - planes);
+  auto to_f32 = [](uint32_t w, int half) -> float {
+    const uint32_t h = half ? w >> 16 : w & 0xffffu;
+    if constexpr (AT == QMM_F16) return f16_to_f32((uint16_t)h);
+    else return __uint_as_float(h << 16);
+  };
+  // row m of piece idx (< MT rows) and its first piece, by compares: no division
+  auto row_of = [&](uint32_t idx, uint32_t& m, uint32_t& first) {
+    m = 0;
+    first = 0;
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          if constexpr (AT == QMM_F16) {
-            v[2 * e] = f16_to_f32((uint16_t)(w[e] & 0xffffu));
-            v[2 * e + 1] = f16_to_f32((uint16_t)(w[e] >> 16));
-          } else {
-            v[2 * e] = __uint_as_float(w[e] << 16);
-            v[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
-          }
-        }
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = (k + e < K) ? load_elem<AT>(g.A, base + e) : 0.0f;
+    for (int r = 1; r < MT; ++r) {
+      const bool ge = idx >= (uint32_t)(r * per_row);
+      m += ge ? 1u : 0u;
+      first = ge ? (uint32_t)(r * per_row) : first;
     }
   };
-  // NB rounds of pieces at a time: all loads first (one memory latency per batch),
-  // then the conversion; every lane takes part in the group butterflies
-  for (int base_idx = 0; base_idx < total; base_idx += NB * (int)blockDim.x) {
-    float vb[NB][4];
+  auto load = [&](int idx, float (&v)[16]) {
+    const bool okp = idx < total;
+    uint32_t m, first;
+    row_of(okp ? (uint32_t)idx : 0u, m, first);
+    const int k = c0 * WPC + 16 * (int)((okp ? (uint32_t)idx : 0u) - first);
+    const int64_t base = (int64_t)m * K + k;
 #pragma unroll
-    for (int j = 0; j < NB; ++j) load(base_idx + j * (int)blockDim.x + (int)threadIdx.x, vb[j]);
+    for (int q = 0; q < 4; ++q) {
+      const int kq = k + 4 * q;
+      if constexpr (BUF) {
+        if constexpr (AVEC) {
+          const uint32_t off = okp && kq < K ? (uint32_t)(base + 4 * q) * ES : kOut;
+          if constexpr (AT == QMM_F32) {
+            const auto t = __builtin_amdgcn_raw_buffer_load_b128(rA, (int)off, 0, 0);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[4 * q + e] = __uint_as_float(t[e]);
+          } else {
+            const auto t = __builtin_amdgcn_raw_buffer_load_b64(rA, (int)off, 0, 0);
+            v[4 * q] = to_f32(t[0], 0);
+            v[4 * q + 1] = to_f32(t[0], 1);
+            v[4 * q + 2] = to_f32(t[1], 0);
+            v[4 * q + 3] = to_f32(t[1], 1);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t off = okp && kq + e < K ? (uint32_t)(base + 4 * q + e) * ES : kOut;
+            if constexpr (AT == QMM_F32)
+              v[4 * q + e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rA, (int)off, 0, 0));
+            else
+              v[4 * q + e] = to_f32(__builtin_amdgcn_raw_buffer_load_b16(rA, (int)off, 0, 0), 0);
+          }
+        }
+      } else if constexpr (AVEC) {
+        const bool ok = okp && kq < K;  // K % 4 == 0: kq < K means all four are in the row
+        const int64_t off = ok ? base + 4 * q : 0;
+        float x[4];
+        if constexpr (AT == QMM_F32) {
+          const f32x4 t = *(const f32x4*)((const float*)g.A + off);
+          x[0] = t.x; x[1] = t.y; x[2] = t.z; x[3] = t.w;
+        } else {
+          const uint2 u = *(const uint2*)((const uint16_t*)g.A + off);
+          const uint32_t w[2] = {u.x, u.y};
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            if constexpr (AT == QMM_F16) {
+              x[2 * e] = f16_to_f32((uint16_t)(w[e] & 0xffffu));
+              x[2 * e + 1] = f16_to_f32((uint16_t)(w[e] >> 16));
+            } else {
+              x[2 * e] = __uint_as_float(w[e] << 16);
+              x[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+            }
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[4 * q + e] = ok ? x[e] : 0.0f;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool ok = okp && kq + e < K;
+          const float x = load_elem<AT>(g.A, ok ? base + 4 * q + e : 0);
+          v[4 * q + e] = ok ? x : 0.0f;
+        }
+      }
+    }
+  };
+  // NB pieces at a time: all loads first (one memory latency per batch), then the
+  // conversion; every lane takes part in the group butterflies
+  // the first batch is peeled so that the caller's loads are issued on every path
+  // (a conditional issue would make the compiler wait for them with the batch)
+  // first piece of this wave's lanes, as a scalar: a wave with no piece in a batch
+  // skips it (a branch on a scalar, so no lane of the wave waits at the join)
+  const int wave_base = __builtin_amdgcn_readfirstlane((int)(threadIdx.x & ~63u));
+  auto batch = [&](int base_idx, auto first) {
+    float vb[NB][16];
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+      if (base_idx + j * (int)blockDim.x + wave_base < total)
+        load(base_idx + j * (int)blockDim.x + (int)threadIdx.x, vb[j]);
+    if constexpr (decltype(first)::value) {
+      __builtin_amdgcn_sched_barrier(0);  // keep the caller's loads behind these
+      issued();
+    }
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
-      if (base_idx + j * (int)blockDim.x >= total) break;  // uniform over the work-group
+      if (base_idx + j * (int)blockDim.x + wave_base >= total) break;  // uniform over the wave
       const int idx = base_idx + j * (int)blockDim.x + (int)threadIdx.x;
       const bool ok = idx < total;
       const float* v = vb[j];
-      const int m = ok ? idx / per_row : 0;
-      const int rem = idx - m * per_row;
-      const int slot = rem / (WPC / 4);
-      const int j4 = rem - slot * (WPC / 4);  // float4 piece inside the chunk
-      // group maximum and group sum over the gw threads of the group (DPP exchanges)
-      float mx = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
-      float sm = ((v[0] + v[1]) + v[2]) + v[3];
-      mx = fmaxf(mx, dpp_f<kDppXor1>(mx));
-      sm += dpp_f<kDppXor1>(sm);
-      mx = fmaxf(mx, dpp_f<kDppXor2>(mx));
-      sm += dpp_f<kDppXor2>(sm);
-      if constexpr (gw >= 8) {
-        mx = fmaxf(mx, dpp_f<kDppHalfMirror>(mx));
-        sm += dpp_f<kDppHalfMirror>(sm);
+      // piece index = (m * SC + slot) * PPC + piece: chunk slot cs = m * SC + slot, and
+      // the 16-value piece inside the chunk (24-bit products: no 64-bit arithmetic)
+      const uint32_t uidx = ok ? (uint32_t)idx : 0u;
+      const uint32_t cs = uidx / (uint32_t)PPC;
+      const uint32_t piece = uidx % (uint32_t)PPC;
+      uint32_t m, first;
+      row_of(uidx, m, first);
+      float mx = 0.0f, sm = 0.0f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v[4 * q]), fabsf(v[4 * q + 1])),
+                             fmaxf(fabsf(v[4 * q + 2]), fabsf(v[4 * q + 3]))));
+        sm += ((v[4 * q] + v[4 * q + 1]) + v[4 * q + 2]) + v[4 * q + 3];
       }
-      if constexpr (gw >= 16) {
-        mx = fmaxf(mx, dpp_f<kDppMirror>(mx));
-        sm += dpp_f<kDppMirror>(sm);
+      if constexpr (gw >= 2) {
+        mx = fmaxf(mx, dpp_f<kDppXor1>(mx));
+        sm += dpp_f<kDppXor1>(sm);
+      }
+      if constexpr (gw >= 4) {
+        mx = fmaxf(mx, dpp_f<kDppXor2>(mx));
+        sm += dpp_f<kDppXor2>(sm);
       }
       int e = 0;
       (void)frexpf(mx, &e);  // mx < 2^e (mx = 0 gives e = 0)
-      if (!ok) continue;
-      uint32_t u[4];
+      uint32_t u[16];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) u[q] = (uint32_t)(int)rintf(ldexpf(v[q], 22 - e));
-      uint32_t* slot_w = planes + (m * SC + slot) * L::SLOT;
+      for (int q = 0; q < 16; ++q) u[q] = (uint32_t)(int)rintf(ldexpf(v[q], 22 - e));
+      uint32_t w[12];
       if constexpr (BITS == 2) {
-        // elements j0..j0+3 of a 16-code dword: j0, j0+2 even (nibbles j0/2, j0/2+1 of
-        // the E words), j0+1, j0+3 odd (same nibbles of the O words).  Digit p of two
-        // values goes to one byte: the low nibbles of bytes 0-2 of a value are its
-        // digits 0, 2, 4, the high nibbles its digits 1, 3, 5 (24-bit two's complement).
-        const int d = (4 * j4) >> 4;
-        const int qb = ((4 * j4) & 15) >> 2;  // byte of each plane word
-        uint8_t* wb = (uint8_t*)(slot_w + d * L::PWD) + qb;
-        const uint32_t ee = (u[0] & 0x0F0F0Fu) | ((u[2] << 4) & 0xF0F0F0u);  // E digits 0, 2, 4
-        const uint32_t eo = ((u[0] >> 4) & 0x0F0F0Fu) | (u[2] & 0xF0F0F0u);  // E digits 1, 3, 5
-        const uint32_t oe = (u[1] & 0x0F0F0Fu) | ((u[3] << 4) & 0xF0F0F0u);
-        const uint32_t oo = ((u[1] >> 4) & 0x0F0F0Fu) | (u[3] & 0xF0F0F0u);
+        // even values (nibble i of the E planes = value 2i), then odd values (O planes)
+        uint32_t ex[3], ey[3], ox[3], oy[3], ew[6], ow[6];
+        byte_gather(u[0], u[4], u[8], u[12], ex);
+        byte_gather(u[2], u[6], u[10], u[14], ey);
+        byte_gather(u[1], u[5], u[9], u[13], ox);
+        byte_gather(u[3], u[7], u[11], u[15], oy);
+        nibble_planes(ex, ey, ew);
+        nibble_planes(ox, oy, ow);
 #pragma unroll
-        for (int k = 0; k < 3; ++k) {
-          wb[(2 * (2 * k)) * 4] = (uint8_t)(ee >> (8 * k));
-          wb[(2 * (2 * k + 1)) * 4] = (uint8_t)(eo >> (8 * k));
-          wb[(2 * (2 * k) + 1) * 4] = (uint8_t)(oe >> (8 * k));
-          wb[(2 * (2 * k + 1) + 1) * 4] = (uint8_t)(oo >> (8 * k));
+        for (int p = 0; p < 6; ++p) {
+          w[2 * p] = ew[p];
+          w[2 * p + 1] = ow[p];
         }
       } else {
-        // elements j0..j0+3 of an 8-code dword are nibbles j0..j0+3 of each plane word
-        // (digits of a + 2^23): pair the values, then join the two pairs' bytes
-        const int d = (4 * j4) >> 3;
-        const int qh = ((4 * j4) & 7) >> 2;  // half-word of each plane word
-        uint16_t* wh = (uint16_t*)(slot_w + d * L::PWD) + qh;
+        // digits of a + 2^23; values 0..7 fill the six words of the first dword,
+        // values 8..15 those of the second
 #pragma unroll
-        for (int q = 0; q < 4; ++q) u[q] += 1u << 23;
-        const uint32_t x01 = (u[0] & 0x0F0F0Fu) | ((u[1] << 4) & 0xF0F0F0u);  // digits 0, 2, 4
-        const uint32_t y01 = ((u[0] >> 4) & 0x0F0F0Fu) | (u[1] & 0xF0F0F0u);  // digits 1, 3, 5
-        const uint32_t x23 = (u[2] & 0x0F0F0Fu) | ((u[3] << 4) & 0xF0F0F0u);
-        const uint32_t y23 = ((u[2] >> 4) & 0x0F0F0Fu) | (u[3] & 0xF0F0F0u);
-        // byte k of a pair word + byte k of the other pair word = the plane's half-word
-        const uint32_t p02 = __builtin_amdgcn_perm(x23, x01, 0x05010400u);  // digits 0 | 2
-        const uint32_t p13 = __builtin_amdgcn_perm(y23, y01, 0x05010400u);  // digits 1 | 3
-        const uint32_t p45 = __builtin_amdgcn_perm(y23, y01, 0x06020000u) & 0xffff0000u;
-        const uint32_t p4 = __builtin_amdgcn_perm(x23, x01, 0x00000602u) & 0xffffu;
-        wh[0 * 2] = (uint16_t)p02;
-        wh[2 * 2] = (uint16_t)(p02 >> 16);
-        wh[1 * 2] = (uint16_t)p13;
-        wh[3 * 2] = (uint16_t)(p13 >> 16);
-        wh[4 * 2] = (uint16_t)p4;
-        wh[5 * 2] = (uint16_t)(p45 >> 16);
+        for (int q = 0; q < 16; ++q) u[q] += 1u << 23;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          uint32_t x[3], y[3], pw[6];
+          byte_gather(u[8 * h], u[8 * h + 2], u[8 * h + 4], u[8 * h + 6], x);
+          byte_gather(u[8 * h + 1], u[8 * h + 3], u[8 * h + 5], u[8 * h + 7], y);
+          nibble_planes(x, y, pw);
+#pragma unroll
+          for (int p = 0; p < 6; ++p) w[6 * h + p] = pw[p];
+        }
       }
-      if ((j4 % gw) == 0) {
-        const int gi = j4 / gw;
-        f32x2 mt;
-        mt.x = mx <= 3.402823466e38f ? ldexpf(1.0f, e - 22) : __builtin_nanf("");
-        mt.y = sm;
-        meta[(m * 4 + gi) * SC + slot] = mt;
-      }
+      // lanes without a piece (and the meta record of all but the group's first lane)
+      // write to the trash line instead of branching around the stores
+      // (32-bit word offsets from the planes, so the choice is one select)
+      const uint32_t pw = ok ? __umul24(cs, (uint32_t)L::SLOT) + __umul24(piece, 12u) : trash_word;
+      uint4* dst = (uint4*)(planes + pw);
+      dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+      dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+      dst[2] = make_uint4(w[8], w[9], w[10], w[11]);
+      f32x2 mt;
+      mt.x = mx <= 3.402823466e38f ? ldexpf(1.0f, e - 22) : __builtin_nanf("");
+      mt.y = sm;
+      // record (m * 4 + gi) * SC + slot = cs + (3 m + gi) * SC, by selects
+      const uint32_t gi = piece / gw;
+      const uint32_t usc = (uint32_t)SC;
+      const uint32_t gsc = gi == 0 ? 0u : gi == 1 ? usc : gi == 2 ? 2u * usc : 3u * usc;
+      uint32_t m3 = 0;
+#pragma unroll
+      for (int r = 1; r < MT; ++r) m3 += m >= (uint32_t)r ? 3u * usc : 0u;
+      const uint32_t mw = ok && (piece % gw) == 0 ? meta_word + 2u * (cs + m3 + gsc) : trash_word;
+      *(f32x2*)(planes + mw) = mt;
     }
-  }
+  };
+  batch(0, std::true_type{});
+  for (int base_idx = NB * (int)blockDim.x; base_idx < total; base_idx += NB * (int)blockDim.x)
+    batch(base_idx, std::false_type{});
+}
+
+// trash: 64 bytes of LDS (16-byte aligned) that nothing reads.  BUF requires
+// M * K * element size < 2^31 - 64 (the streaming kernel's A fits in LDS).
+template <int BITS, int AT, int G, int MT, bool BUF, typename Issued>
+__device__ __forceinline__ void stage_planes(const GemvArgs& g, uint32_t* planes, f32x2* meta,
+                                             uint32_t* trash, int c0, int SC, Issued&& issued) {
+  if (g.a_vec)
+    stage_planes_impl<BITS, AT, G, MT, true, BUF>(g, planes, meta, trash, c0, SC, issued);
+  else
+    stage_planes_impl<BITS, AT, G, MT, false, BUF>(g, planes, meta, trash, c0, SC, issued);
 }
 
 // General form (A staged one K-slice at a time inside the item loop, row sums
@@ -205,7 +328,8 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_ip_kernel(GemvArgs g) {
   const int SC = g.slice_chunks;
   uint32_t* planes = (uint32_t*)lds;
   f32x2* meta = (f32x2*)(planes + MT * SC * L::SLOT);
-  float* out_lds = (float*)(meta + MT * 4 * SC);
+  uint32_t* trash = (uint32_t*)(meta + MT * 4 * SC);  // the 16 floats the plan adds after the records
+  float* out_lds = (float*)(trash + 16);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int lpr_log2 = g.lpr_log2;
@@ -319,7 +443,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_ip_kernel(GemvArgs g) {
   auto step = [&](IpBuf<R, NS>& cbuf, IpBuf<R, NS>& nxt, bool live) {
     if (live && cur.it == 0 && (nslices > 1 || !staged)) {
       __syncthreads();
-      stage_planes<BITS, AT, G>(g, planes, meta, cur.s * SC, SC);
+      stage_planes<BITS, AT, G, MT, false>(g, planes, meta, trash, cur.s * SC, SC, [] {});
       __syncthreads();
       staged = true;
     }

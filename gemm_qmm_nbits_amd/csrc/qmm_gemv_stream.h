@@ -37,7 +37,8 @@ __global__ __launch_bounds__(stream_threads(MT, R)) void gemv_ip_stream_kernel(G
   const int SC = g.slice_chunks;  // >= nchunks
   uint32_t* planes = (uint32_t*)lds;
   f32x2* meta = (f32x2*)(planes + MT * SC * L::SLOT);
-  float* out_lds = (float*)(meta + MT * 4 * SC);
+  uint32_t* trash = (uint32_t*)(meta + MT * 4 * SC);  // the 16 floats the plan adds after the records
+  float* out_lds = (float*)(trash + 16);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int lpr_log2 = g.lpr_log2;
@@ -120,10 +121,13 @@ __global__ __launch_bounds__(stream_threads(MT, R)) void gemv_ip_stream_kernel(G
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[r][m] = 0.0f;
 
+  // the activations' loads go out first, then the first weights of the stream, which
+  // travel while the activations are converted
   IpBuf<R, NS> buf[D];
+  stage_planes<BITS, AT, G, MT, true>(g, planes, meta, trash, 0, SC, [&] {
 #pragma unroll
-  for (int i = 0; i < D - 1; ++i) fetch(buf[i]);
-  stage_planes<BITS, AT, G>(g, planes, meta, 0, SC);
+    for (int i = 0; i < D - 1; ++i) fetch(buf[i]);
+  });
   __syncthreads();
 
   int cit = 0, ctile = t_begin;
@@ -264,6 +268,8 @@ __global__ __launch_bounds__(stream_threads(MT, R)) void gemv_ip_stream_kernel(G
 template <int BITS, int AT, int MT, int R, int DPG, int ZK>
 static hipError_t launch_ip_stream(const GemvArgs& g, hipStream_t st) {
   if (g.slice_chunks < g.nchunks) return hipErrorNotSupported;
+  // activations are read with 32-bit buffer offsets
+  if (g.M * g.K * (AT == QMM_F32 ? 4 : 2) >= (1LL << 31) - 64) return hipErrorNotSupported;
   // 32-bit buffer offsets: every byte offset (rows up to N + one tile) below 2^31
   const int subs = 64 >> g.lpr_log2;
   const int64_t rows_per_tile = (int64_t)(stream_threads(MT, R) / 64) * subs * R;
