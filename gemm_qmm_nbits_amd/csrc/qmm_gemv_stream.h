@@ -46,15 +46,18 @@ __global__ __launch_bounds__(stream_threads(MT, R)) void gemv_ip_stream_kernel(G
   const int lp = lane & (LPR - 1);
   const int sub = lane >> lpr_log2;
   const int SUBS = 64 >> lpr_log2;
-  const int rows_per_wave = SUBS * R;
-  const int rows_per_tile = NWAVES * rows_per_wave;
+  // Row groups (the rows one wave works on at once) are dealt out evenly: work-group
+  // b owns the contiguous groups [g_begin, g_end) (counts differ by at most one),
+  // and wave w of it takes groups g_begin + w, g_begin + w + NWAVES, ...
+  const int rpg = SUBS * R;  // rows per group
   const int N = (int)g.N;
   const int M = (int)g.M;
-  const int ntiles = (N + rows_per_tile - 1) / rows_per_tile;
-  const int tiles_lo = ntiles / gridDim.x, extra = ntiles % gridDim.x;
-  const int t_begin = blockIdx.x * tiles_lo + (blockIdx.x < extra ? blockIdx.x : extra);
-  const int t_end = t_begin + tiles_lo + (blockIdx.x < extra ? 1 : 0);
-  if (t_begin >= t_end) return;
+  const int ngroups = (N + rpg - 1) / rpg;
+  const int groups_lo = ngroups / gridDim.x, extra = ngroups % gridDim.x;
+  const int g_begin = blockIdx.x * groups_lo + (blockIdx.x < extra ? blockIdx.x : extra);
+  const int g_end = g_begin + groups_lo + (blockIdx.x < extra ? 1 : 0);
+  if (g_begin >= g_end) return;
+  const int wave_groups = g_end - g_begin > wave ? (g_end - g_begin - wave + NWAVES - 1) / NWAVES : 0;
   const int nchunks = (int)g.nchunks;
   const int iters = (nchunks + LPR - 1) >> lpr_log2;  // items per row group
   const int nblk = (int)g.nblk;
@@ -74,13 +77,13 @@ __global__ __launch_bounds__(stream_threads(MT, R)) void gemv_ip_stream_kernel(G
   if constexpr (ZK == 1) rZ = make_rsrc(g.zp, (uint32_t)(g.N * g.zp_row_bytes));
   if constexpr (ZK == 2) rZ = make_rsrc(g.zp, (uint32_t)(g.N * g.nblk * 2));
 
-  // fetch cursor: per-row byte offsets of item 0 of the current tile, and the item
+  // fetch cursor: per-row byte offsets of item 0 of the current group, and the item
   uint32_t fw[R], fs[R], fz[R];
-  int fit = 0, ftile = t_begin;
-  auto set_rows = [&](int tl) {
+  int fit = 0, fgrp = g_begin + wave;
+  auto set_rows = [&](int grp) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const uint32_t row = (uint32_t)(tl * rows_per_tile + wave * rows_per_wave + r * SUBS + sub);
+      const uint32_t row = (uint32_t)(grp * rpg + r * SUBS + sub);
       // rows past N give offsets past the end of every buffer (loads return 0)
       fw[r] = row * row_bytes + (uint32_t)lp * 16u;
       fs[r] = (row * (uint32_t)nblk + (uint32_t)lane_b) * 2u;
@@ -88,7 +91,7 @@ __global__ __launch_bounds__(stream_threads(MT, R)) void gemv_ip_stream_kernel(G
       if constexpr (ZK == 2) fz[r] = fs[r];
     }
   };
-  set_rows(t_begin);
+  set_rows(fgrp);
   auto fetch = [&](IpBuf<R, NS>& b) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -110,8 +113,8 @@ __global__ __launch_bounds__(stream_threads(MT, R)) void gemv_ip_stream_kernel(G
     }
     if (++fit == iters) {
       fit = 0;
-      ++ftile;
-      set_rows(ftile);
+      fgrp += NWAVES;
+      set_rows(fgrp);
     }
   };
 
@@ -130,8 +133,8 @@ __global__ __launch_bounds__(stream_threads(MT, R)) void gemv_ip_stream_kernel(G
   });
   __syncthreads();
 
-  int cit = 0, ctile = t_begin;
-  const int total = (t_end - t_begin) * iters;
+  int cit = 0, cgrp = g_begin + wave;
+  const int total = wave_groups * iters;
   const uint32_t* planes_lane = planes + lp * L::SLOT;
   const f32x2* meta_lane = meta + lp;
   auto step = [&](IpBuf<R, NS>& cbuf, IpBuf<R, NS>& nxt, bool live) {
@@ -221,10 +224,9 @@ __global__ __launch_bounds__(stream_threads(MT, R)) void gemv_ip_stream_kernel(G
 #pragma unroll
         for (int m = 0; m < MT; ++m) acc[r][m] = group_sum(acc[r][m], LPR);
       if (lp == 0) {
-        const int lt = ctile - t_begin;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-          const int lr = lt * rows_per_tile + wave * rows_per_wave + r * SUBS + sub;
+          const int lr = (cgrp - g_begin) * rpg + r * SUBS + sub;
 #pragma unroll
           for (int m = 0; m < MT; ++m) out_lds[lr * MT + m] = acc[r][m];
         }
@@ -236,7 +238,7 @@ __global__ __launch_bounds__(stream_threads(MT, R)) void gemv_ip_stream_kernel(G
     }
     if (++cit == iters) {
       cit = 0;
-      ++ctile;
+      cgrp += NWAVES;
     }
   };
 
@@ -245,10 +247,10 @@ __global__ __launch_bounds__(stream_threads(MT, R)) void gemv_ip_stream_kernel(G
     for (int i = 0; i < D; ++i) step(buf[i], buf[(i + D - 1) % D], base + i < total);
   }
 
-  // write the row sums (+ bias) of every tile of the work-group
+  // write the row sums (+ bias) of every group of the work-group
   __syncthreads();
-  const int nrows = (t_end - t_begin) * rows_per_tile;
-  const int row0 = t_begin * rows_per_tile;
+  const int nrows = (g_end - g_begin) * rpg;
+  const int row0 = g_begin * rpg;
   for (int i = threadIdx.x; i < nrows * M; i += blockDim.x) {
     const int m = i / nrows;
     const int lr = i - m * nrows;
@@ -261,30 +263,32 @@ __global__ __launch_bounds__(stream_threads(MT, R)) void gemv_ip_stream_kernel(G
   }
 }
 
-// Launch of the streaming form: one work-group per resident slot (or per tile when
-// there are fewer tiles), each with an output buffer sized to its rows.  Returns
-// hipErrorNotSupported when the shape does not suit it (the caller then uses
+// Launch of the streaming form: one work-group per resident slot (or per row group
+// when there are fewer groups), each with an output buffer sized to its rows.
+// Returns hipErrorNotSupported when the shape does not suit it (the caller then uses
 // gemv_ip_kernel).
 template <int BITS, int AT, int MT, int R, int DPG, int ZK>
 static hipError_t launch_ip_stream(const GemvArgs& g, hipStream_t st) {
   if (g.slice_chunks < g.nchunks) return hipErrorNotSupported;
   // activations are read with 32-bit buffer offsets
   if (g.M * g.K * (AT == QMM_F32 ? 4 : 2) >= (1LL << 31) - 64) return hipErrorNotSupported;
-  // 32-bit buffer offsets: every byte offset (rows up to N + one tile) below 2^31
-  const int subs = 64 >> g.lpr_log2;
-  const int64_t rows_per_tile = (int64_t)(stream_threads(MT, R) / 64) * subs * R;
-  const int64_t span = (g.N + rows_per_tile) * (g.row_bytes + 16 * (1LL << g.lpr_log2));
-  if (span >= (1LL << 31) || (g.N + rows_per_tile) * g.nblk * 2 >= (1LL << 31)) return hipErrorNotSupported;
-  const int64_t ntiles = (g.N + rows_per_tile - 1) / rows_per_tile;
+  // 32-bit buffer offsets: every byte offset below 2^31, for rows up to N plus the
+  // groups a wave's fetch may run ahead into (fewer than two work-groups' worth)
+  const int64_t rpg = (int64_t)(64 >> g.lpr_log2) * R;
+  const int64_t ahead = 2 * (int64_t)(stream_threads(MT, R) / 64) * rpg;
+  const int64_t span = (g.N + ahead) * (g.row_bytes + 16 * (1LL << g.lpr_log2));
+  if (span >= (1LL << 31) || (g.N + ahead) * g.nblk * 2 >= (1LL << 31)) return hipErrorNotSupported;
+  const int64_t ngroups = (g.N + rpg - 1) / rpg;
   auto kern = gemv_ip_stream_kernel<BITS, AT, MT, R, DPG, ZK>;
-  const size_t out_unit = (size_t)rows_per_tile * MT * sizeof(float);
-  int per_cu = resident_per_cu(kern, stream_threads(MT, R), g.lds_bytes + out_unit);
+  const size_t out_unit = (size_t)rpg * MT * sizeof(float);  // per group
+  int per_cu = resident_per_cu(kern, stream_threads(MT, R),
+                               g.lds_bytes + (size_t)(stream_threads(MT, R) / 64) * out_unit);
   int64_t per = 0, grid = 0;
   size_t lds = 0;
   for (int pass = 0; pass < 2; ++pass) {
     const int64_t slots = (int64_t)g.num_cus * per_cu;
-    per = (ntiles + slots - 1) / slots;
-    grid = slots < ntiles ? slots : ntiles;  // every resident slot; tiles differ by at most one
+    grid = slots < ngroups ? slots : ngroups;  // every resident slot
+    per = (ngroups + grid - 1) / grid;         // groups per work-group (at most)
     lds = g.lds_bytes + (size_t)per * out_unit;
     const int again = resident_per_cu(kern, stream_threads(MT, R), lds);
     if (again >= per_cu) break;
