@@ -265,10 +265,11 @@ int gemv_choice(int entry, const GemvArgs& g, hipStream_t st) {
   return kGemvCandidates[chosen];
 }
 
-// MoE decode candidates: rows per lane of the fc1 kernel (each row = a g row and
-// its u row) and of the fc2 kernel.
-constexpr int kQmoeCandidates[] = {1, 2};
-constexpr int kNumQmoeCandidates = 2;
+// MoE decode candidates, for fc1 and fc2 alike: rows per lane (low bits; an fc1 row
+// is a g row and its u row) and the form (kQmoePerSlot: one work-group per row tile
+// and slot; else the persistent form, fp mode only).  All give the same bits.
+constexpr int kQmoeCandidates[] = {1, 2, 1 | kQmoePerSlot, 2 | kQmoePerSlot};
+constexpr int kNumQmoeCandidates = 4;
 
 struct QmoeTimingBufs {
   int32_t* ids = nullptr;  // timing expert ids, [kSets][T][k]
@@ -389,9 +390,10 @@ void qmoe_choice(const QmoeArgs& a, hipStream_t st, int* r1, int* r2) {
           for (int c = 0; c < kNumQmoeCandidates; ++c) {
             double tot = 0;
             for (int r = 1; r < kRounds; ++r) tot += tv[r * kNumQmoeCandidates + c];
-            std::fprintf(stderr, " R=%d:%.2fus", kQmoeCandidates[c], tot / (kRounds - 1));
+            std::fprintf(stderr, " %s%d:%.2fus", (kQmoeCandidates[c] & kQmoePerSlot) ? "slot-R" : "R",
+                         kQmoeCandidates[c] & 15, tot / (kRounds - 1));
           }
-          std::fprintf(stderr, " pick R=%d\n", kQmoeCandidates[which == 0 ? c1 : c2]);
+          std::fprintf(stderr, " pick #%d\n", which == 0 ? c1 : c2);
         }
       }
     }
@@ -831,6 +833,7 @@ qmm_status qmoe_decode_fused(const uint16_t* X, int64_t T, int64_t H, int64_t I,
   a.fc2_zp_row_bytes = ceil_div(a.fc2_nblk, 2);
   a.fc2_chunks = ceil_div(I, 32);
   a.fc2_lpr_log2 = gemv_lanes_per_row_log2(a.fc2_chunks);
+  a.num_cus = device_cus();
   const QmoeLayout L = qmoe_layout(T, H, I, k, mode);
   uint8_t* sc = (uint8_t*)scratch;
   a.h = (uint16_t*)(sc + L.h);

@@ -102,6 +102,13 @@ __device__ __forceinline__ float swz_xor(float v) {
   return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x1f | (K << 10)));
 }
 
+// Raw buffer descriptor (32-bit data format) over `bytes` bytes at p: loads past the
+// range return 0 and fetch nothing.
+constexpr uint32_t kBufferWord3 = 0x00020000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, (int)kBufferWord3);
+}
+
 // Lane exchange inside rows of 16 lanes through DPP (no LDS traffic): xor 1 and
 // xor 2 inside quads, then the mirror of each half row (lane i <-> 7 - i) and of the
 // row (lane i <-> 15 - i).  Applied in that order with a commutative combine, every

@@ -16,14 +16,9 @@
 
 namespace qmm {
 
-constexpr uint32_t kBufferWord3 = 0x00020000u;  // raw buffer, 32-bit data format
 // Threads per work-group: 16 waves share one copy of the staged activations when
 // the kernel's registers allow it (<= 128 VGPRs), else 8.
 __host__ __device__ constexpr int stream_threads(int MT, int R) { return MT * R <= 2 ? 1024 : 512; }
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, (int)kBufferWord3);
-}
 
 template <int BITS, int AT, int MT, int R, int DPG, int ZK>
 __global__ __launch_bounds__(stream_threads(MT, R)) void gemv_ip_stream_kernel(GemvArgs g) {

@@ -125,10 +125,13 @@ struct QmoeArgs {
   int8_t* hq_out;   // int8 mode: [T][k][I] codes of h
   float* hs_out;    // int8 mode: [T][k][I/32] scales of h
   uint16_t* Y;
+  int num_cus;      // compute units of the device
 };
 size_t qmoe_fc1_lds_bytes(const QmoeArgs& a);
 size_t qmoe_fc2_lds_bytes(const QmoeArgs& a);
-hipError_t launch_qmoe_fc1(const QmoeArgs& a, int rows_per_lane, hipStream_t st);
-hipError_t launch_qmoe_fc2(const QmoeArgs& a, int rows_per_lane, hipStream_t st);
+// candidate: rows per lane (1 or 2), plus kQmoePerSlot for the per-slot form
+constexpr int kQmoePerSlot = 16;
+hipError_t launch_qmoe_fc1(const QmoeArgs& a, int candidate, hipStream_t st);
+hipError_t launch_qmoe_fc2(const QmoeArgs& a, int candidate, hipStream_t st);
 
 }  // namespace qmm

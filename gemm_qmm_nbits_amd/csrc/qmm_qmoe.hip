@@ -22,6 +22,10 @@
 #include "qmm_device.h"
 #include "qmm_internal.h"
 
+#include <map>
+#include <mutex>
+#include <type_traits>
+
 namespace qmm {
 
 // ---- shared pieces ------------------------------------------------------------
@@ -168,6 +172,64 @@ __device__ __forceinline__ void stage_f32(const uint16_t* src, int rows, int n, 
   __syncthreads();
 }
 
+// The same staging (same values and sums) with the loads of the first batch (NB
+// pieces per thread) issued before `issued` runs: a caller that starts its weight
+// loads there has them travel while the activations are converted, and waiting for
+// the activations, which were issued first, does not wait for them.
+template <typename Issued>
+__device__ __forceinline__ void stage_f32_first(const uint16_t* src, int rows, int n, int nch, float* xf,
+                                                float* sa, Issued&& issued) {
+  constexpr int NB = 4;
+  const int per_row = nch * 4;  // pieces of 8 values
+  const int total = rows * per_row;
+  const int wave_base = __builtin_amdgcn_readfirstlane((int)(threadIdx.x & ~63u));
+  // n % 8 == 0 (checked at the entry point): a piece is wholly inside the row or
+  // wholly past it, so the load is branch-free (address clamped, value selected)
+  auto load = [&](int p, float (&v)[8]) {
+    const bool okp = p < total;
+    const int pc = okp ? p : 0;
+    const int r = pc / per_row;
+    const int k0 = 8 * (pc - r * per_row);
+    const bool in = k0 < n;
+    const uint4 u = *(const uint4*)(src + (int64_t)r * n + (in ? k0 : 0));
+    h8_to_f32(u, v);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = in ? v[q] : 0.0f;
+  };
+  auto convert = [&](int p, const float (&v)[8]) {
+    const bool okp = p < total;
+    const int pc = okp ? p : 0;
+    const int r = pc / per_row;
+    const int pp = pc - r * per_row;
+    const int k0 = 8 * pp;
+    if (okp) {
+      f32x4* d = (f32x4*)(xf + (int64_t)r * nch * 32 + k0);
+      d[0] = f32x4{v[0], v[1], v[2], v[3]};
+      d[1] = f32x4{v[4], v[5], v[6], v[7]};
+    }
+    float s8 = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+    s8 += dpp_f<kDppXor1>(s8);
+    s8 += dpp_f<kDppXor2>(s8);
+    if (okp && (pp & 3) == 0) sa[r * nch + (pp >> 2)] = s8;
+  };
+  auto batch = [&](int base, auto first) {
+    float vb[NB][8];
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+      if (base + j * (int)blockDim.x + wave_base < total) load(base + j * (int)blockDim.x + (int)threadIdx.x, vb[j]);
+    if constexpr (decltype(first)::value) {
+      __builtin_amdgcn_sched_barrier(0);  // keep the caller's loads behind these
+      issued();
+    }
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+      if (base + j * (int)blockDim.x + wave_base < total) convert(base + j * (int)blockDim.x + (int)threadIdx.x, vb[j]);
+  };
+  batch(0, std::true_type{});
+  for (int base = NB * (int)blockDim.x; base < total; base += NB * (int)blockDim.x) batch(base, std::false_type{});
+  __syncthreads();
+}
+
 // int8 staging from codes already quantized (natural order) and their scales.
 __device__ __forceinline__ void stage_i8(const int8_t* q, const float* sc, int n, uint32_t* q_lds,
                                          float* s_lds, int* sum_lds) {
@@ -195,6 +257,12 @@ struct MoeItem {
 };
 
 constexpr int kMoeThreads = 256;
+constexpr int kMoeStreamThreads = 512;  // persistent forms
+
+// Expert ids outside [0, E) (a caller error) are clamped into it: never a fault.
+__device__ __forceinline__ int clamp_expert(int e, int64_t E) {
+  return e < 0 ? 0 : (e >= (int)E ? (int)E - 1 : e);
+}
 // items per lane whose loads are in flight (ring of register sets): fc1 items carry
 // 2 * RI rows (register-heavy), fc2 items one row per R
 constexpr int kFc1Depth = 2;
@@ -211,7 +279,7 @@ __global__ __launch_bounds__(kMoeThreads) void qmoe_fc1_kernel(QmoeArgs a) {
   extern __shared__ uint32_t smem[];
   const int slot = blockIdx.y;  // t * k + j
   const int t = slot / a.k;
-  const int e = a.ids[slot];
+  const int e = clamp_expert(a.ids[slot], a.E);
   const uint16_t* x = a.X + (int64_t)t * a.H;
   const int nch = (int)a.fc1_chunks;  // chunks holding codes k < H
   const int nblk = (int)a.fc1_nblk;
@@ -416,7 +484,7 @@ __global__ __launch_bounds__(kMoeThreads) void qmoe_fc2_kernel(QmoeArgs a) {
   int fj = 0, fit = 0;
   auto fetch = [&](MoeItem<R>& b) {
     const int jj = fj < k ? fj : k - 1;
-    const int e = a.ids[t * k + jj];
+    const int e = clamp_expert(a.ids[t * k + jj], a.E);
     const uint8_t* W = a.fc2.W + (int64_t)e * a.H * a.fc2_row_bytes;
     const _Float16* S = (const _Float16*)a.fc2.scales + (int64_t)e * a.H * nblk;
     int c = fit * LPR + lp;
@@ -482,7 +550,7 @@ __global__ __launch_bounds__(kMoeThreads) void qmoe_fc2_kernel(QmoeArgs a) {
     }
     if (live && cit == iters - 1) {
       // slot cj complete: z = butterfly(acc) + b2, y += w * z (slot order)
-      const int e = a.ids[t * k + cj];
+      const int e = clamp_expert(a.ids[t * k + cj], a.E);
       const float rw = a.rw[t * k + cj];
 #pragma unroll
       for (int r = 0; r < R; ++r) {
@@ -518,6 +586,340 @@ __global__ __launch_bounds__(kMoeThreads) void qmoe_fc2_kernel(QmoeArgs a) {
   }
 }
 
+// ---- persistent forms (fp mode) ------------------------------------------------------
+//
+// One work-group per resident slot.  The activations of every token (fc1: x; fc2: the
+// k rows of h of every token) are staged once per work-group, and the row groups (the
+// rows one wave works on at once, all of one slot, so of one expert) are dealt out
+// evenly: work-group b owns the contiguous groups [g_begin, g_end), wave w of it takes
+// groups g_begin + w, g_begin + w + waves, ...  A wave's weight loads run through one
+// register ring across its groups (and, in fc2, across the k slots of a group).  The
+// per-row arithmetic and its order are those of the kernels above, so both forms give
+// the same bits.  Row partial sums stay in LDS; bias, SwiGLU and the router-weighted
+// combine run at the write-out after the loop, so no load or store other than the
+// weight stream sits in the loop.  Expert ids are read with scalar loads (one per
+// group or slot) and clamped into [0, E).
+
+template <int RI, int ZK>
+__global__ __launch_bounds__(kMoeStreamThreads) void qmoe_fc1_stream_kernel(QmoeArgs a) {
+  constexpr int NR = 2 * RI;
+  constexpr int NW = kMoeStreamThreads / 64;
+  constexpr int D = RI == 1 ? 4 : 3;  // a wave's few items all in flight
+  extern __shared__ uint32_t smem[];
+  const int T = (int)a.T;
+  const int k = a.k;
+  const int I = (int)a.I;
+  const int nch = (int)a.fc1_chunks;
+  const int nblk = (int)a.fc1_nblk;
+  float* xf = (float*)smem;                    // [T][nch * 32]
+  float* sa = xf + (size_t)T * nch * 32;       // [T][nch]
+  float* outs = sa + (size_t)T * nch;          // [local rows][2]: g and u sums
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int lpr_log2 = a.fc1_lpr_log2;
+  const int LPR = 1 << lpr_log2;
+  const int lp = lane & (LPR - 1);
+  const int sub = lane >> lpr_log2;
+  const int SUBS = 64 >> lpr_log2;
+  const int rpg = SUBS * RI;              // rows i per group
+  const int GI = (I + rpg - 1) / rpg;     // groups per slot
+  const int ngroups = T * k * GI;
+  const int groups_lo = ngroups / (int)gridDim.x, extra = ngroups % (int)gridDim.x;
+  const int g_begin = (int)blockIdx.x * groups_lo + ((int)blockIdx.x < extra ? (int)blockIdx.x : extra);
+  const int g_end = g_begin + groups_lo + ((int)blockIdx.x < extra ? 1 : 0);
+  if (g_begin >= g_end) return;
+  const int wave_groups = g_end - g_begin > wave ? (g_end - g_begin - wave + NW - 1) / NW : 0;
+  const int iters = (nch + LPR - 1) >> lpr_log2;
+  const int blk_shift = __builtin_ctz((unsigned)a.block) - 5;
+  const uint32_t rb = (uint32_t)a.fc1_row_bytes;
+  const uint32_t zrb = (uint32_t)a.fc1_zp_row_bytes;
+  const uint32_t erows = 2u * (uint32_t)I;  // W1 rows per expert
+
+  // fetch cursor: group, item, and the expert's buffers and rows of that group
+  int fgrp = g_begin + wave, fit = 0;
+  __amdgpu_buffer_rsrc_t rW, rS, rZ;
+  uint32_t frow[NR];
+  auto set_group = [&](int grp) {
+    const int gg = grp < ngroups ? grp : ngroups - 1;  // past the end: the last group again
+    const int sl = gg / GI;
+    const int gi = gg - sl * GI;
+    const int e = clamp_expert(a.ids[sl], a.E);
+    rW = make_rsrc(a.fc1.W + (size_t)e * erows * rb, erows * rb);
+    rS = make_rsrc((const uint16_t*)a.fc1.scales + (size_t)e * erows * nblk, erows * (uint32_t)nblk * 2u);
+    if constexpr (ZK) rZ = make_rsrc(a.fc1.zp + (size_t)e * erows * zrb, erows * zrb);
+#pragma unroll
+    for (int r = 0; r < RI; ++r) {
+      const int i = gi * rpg + r * SUBS + sub;
+      const uint32_t ic = (uint32_t)(i < I ? i : I - 1);
+      frow[2 * r] = ic;
+      frow[2 * r + 1] = ic + (uint32_t)I;
+    }
+  };
+  auto fetch = [&](MoeItem<NR>& b) {
+    int c = fit * LPR + lp;
+    c = c < nch ? c : nch - 1;
+    const int blk = c >> blk_shift;
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rW, (int)(frow[r] * rb + (uint32_t)c * 16u), 0, 0);
+      b.w[r] = make_uint4(v[0], v[1], v[2], v[3]);
+      b.s[r] = __builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(
+                                                 rS, (int)((frow[r] * (uint32_t)nblk + (uint32_t)blk) * 2u), 0, 0));
+      if constexpr (ZK)
+        b.z[r] = __builtin_amdgcn_raw_buffer_load_b8(rZ, (int)(frow[r] * zrb + (uint32_t)(blk >> 1)), 0, 0);
+      else
+        b.z[r] = 0x88u;
+    }
+    if (++fit == iters) {
+      fit = 0;
+      fgrp += NW;
+      set_group(fgrp);
+    }
+  };
+  auto token_of = [&](int grp) { return ((grp < ngroups ? grp : ngroups - 1) / GI) / k; };
+
+  float acc[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) acc[r] = 0.0f;
+  int cgrp = g_begin + wave, cit = 0, ct = token_of(cgrp);
+  auto step = [&](const MoeItem<NR>& cb, MoeItem<NR>& nxt, bool live) {
+    fetch(nxt);
+    const int c = cit * LPR + lp;
+    const bool cv = live && c < nch;
+    const int cc = c < nch ? c : nch - 1;
+    const int blk = cc >> blk_shift;
+    const float* xp = xf + ((size_t)ct * nch + cc) * 32;
+    float xa[32];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const f32x4 v = *(const f32x4*)(xp + 4 * q);
+      xa[4 * q] = v.x; xa[4 * q + 1] = v.y; xa[4 * q + 2] = v.z; xa[4 * q + 3] = v.w;
+    }
+    const float sac = sa[ct * nch + cc];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const float pr = dot_chunk_u4(cb.w[r], xa);
+      const float zp = (float)((cb.z[r] >> ((blk & 1) * 4)) & 0xfu);
+      const float nv = fmaf((float)cb.s[r], fmaf(-zp, sac, 512.0f * pr), acc[r]);
+      acc[r] = cv ? nv : acc[r];
+    }
+    if (live && cit == iters - 1) {
+      // group complete: fixed-order combination of the LPR lane partials
+#pragma unroll
+      for (int r = 0; r < NR; ++r) acc[r] = group_sum(acc[r], LPR);
+      if (lp == 0) {
+#pragma unroll
+        for (int r = 0; r < RI; ++r) {
+          const int lr = (cgrp - g_begin) * rpg + r * SUBS + sub;
+          outs[2 * lr] = acc[2 * r];
+          outs[2 * lr + 1] = acc[2 * r + 1];
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < NR; ++r) acc[r] = 0.0f;
+    }
+    if (++cit == iters) {
+      cit = 0;
+      cgrp += NW;
+      ct = token_of(cgrp);
+    }
+  };
+
+  // the activations' loads go out first, then the first weights, which travel while
+  // the activations are converted
+  MoeItem<NR> buf[D];
+  set_group(fgrp);
+  stage_f32_first(a.X, T, (int)a.H, nch, xf, sa, [&] {
+#pragma unroll
+    for (int i = 0; i < D - 1; ++i) fetch(buf[i]);
+  });
+  const int total = wave_groups * iters;
+  for (int base = 0; base < total; base += D) {
+#pragma unroll
+    for (int i = 0; i < D; ++i) step(buf[i], buf[(i + D - 1) % D], base + i < total);
+  }
+  __syncthreads();
+  // bias and SwiGLU of every row of the work-group's groups
+  const int nloc = (g_end - g_begin) * rpg;
+  for (int q = threadIdx.x; q < nloc; q += blockDim.x) {
+    const int grp = g_begin + q / rpg;
+    const int sl = grp / GI;
+    const int i = (grp - sl * GI) * rpg + (q - (q / rpg) * rpg);
+    if (i >= I) continue;
+    float g = outs[2 * q], u = outs[2 * q + 1];
+    if (a.fc1.bias) {
+      const int e = clamp_expert(a.ids[sl], a.E);
+      const uint16_t* bb = a.fc1.bias + (int64_t)e * 2 * a.I;
+      g += f16_to_f32(bb[i]);
+      u += f16_to_f32(bb[i + a.I]);
+    }
+    const float hv = g / (1.0f + expf(-g)) * u;
+    a.h[(int64_t)sl * a.I + i] = f32_to_f16(hv);
+  }
+}
+
+template <int R, int ZK>
+__global__ __launch_bounds__(kMoeStreamThreads) void qmoe_fc2_stream_kernel(QmoeArgs a) {
+  constexpr int NW = kMoeStreamThreads / 64;
+  constexpr int D = kFc2Depth;
+  extern __shared__ uint32_t smem[];
+  const int T = (int)a.T;
+  const int k = a.k;
+  const int H = (int)a.H;
+  const int nch = (int)a.fc2_chunks;
+  const int nblk = (int)a.fc2_nblk;
+  float* hf = (float*)smem;                    // [T * k][nch * 32]
+  float* sa = hf + (size_t)T * k * nch * 32;   // [T * k][nch]
+  float* outs = sa + (size_t)T * k * nch;      // [local rows][k]: slot sums
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int lpr_log2 = a.fc2_lpr_log2;
+  const int LPR = 1 << lpr_log2;
+  const int lp = lane & (LPR - 1);
+  const int sub = lane >> lpr_log2;
+  const int SUBS = 64 >> lpr_log2;
+  const int rpg = SUBS * R;               // rows n per group
+  const int GN = (H + rpg - 1) / rpg;     // groups per token
+  const int ngroups = T * GN;
+  const int groups_lo = ngroups / (int)gridDim.x, extra = ngroups % (int)gridDim.x;
+  const int g_begin = (int)blockIdx.x * groups_lo + ((int)blockIdx.x < extra ? (int)blockIdx.x : extra);
+  const int g_end = g_begin + groups_lo + ((int)blockIdx.x < extra ? 1 : 0);
+  if (g_begin >= g_end) return;
+  // the work-group's units are (group, slot) pairs, unit u = (g_begin + u / k, u % k);
+  // wave w takes units w, w + NW, ... (the slot sums are combined at the write-out)
+  const int nunits = (g_end - g_begin) * k;
+  const int wave_units = nunits > wave ? (nunits - wave + NW - 1) / NW : 0;
+  const int iters = (nch + LPR - 1) >> lpr_log2;
+  const int blk_shift = __builtin_ctz((unsigned)a.block) - 5;
+  const uint32_t rb = (uint32_t)a.fc2_row_bytes;
+  const uint32_t zrb = (uint32_t)a.fc2_zp_row_bytes;
+  const uint32_t erows = (uint32_t)H;  // W2 rows per expert
+
+  // fetch cursor: unit and item, and the unit's expert buffers and rows
+  int fu = wave, fit = 0;
+  __amdgpu_buffer_rsrc_t rW, rS, rZ;
+  uint32_t frow[R];
+  auto set_unit = [&](int u) {
+    const int uu = u < nunits ? u : nunits - 1;  // past the end: the last unit again
+    const int grp = g_begin + uu / k;
+    const int j = uu - (uu / k) * k;
+    const int t = grp / GN;
+    const int gn = grp - t * GN;
+    const int e = clamp_expert(a.ids[t * k + j], a.E);
+    rW = make_rsrc(a.fc2.W + (size_t)e * erows * rb, erows * rb);
+    rS = make_rsrc((const uint16_t*)a.fc2.scales + (size_t)e * erows * nblk, erows * (uint32_t)nblk * 2u);
+    if constexpr (ZK) rZ = make_rsrc(a.fc2.zp + (size_t)e * erows * zrb, erows * zrb);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int n = gn * rpg + r * SUBS + sub;
+      frow[r] = (uint32_t)(n < H ? n : H - 1);
+    }
+  };
+  auto fetch = [&](MoeItem<R>& b) {
+    int c = fit * LPR + lp;
+    c = c < nch ? c : nch - 1;
+    const int blk = c >> blk_shift;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rW, (int)(frow[r] * rb + (uint32_t)c * 16u), 0, 0);
+      b.w[r] = make_uint4(v[0], v[1], v[2], v[3]);
+      b.s[r] = __builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(
+                                                 rS, (int)((frow[r] * (uint32_t)nblk + (uint32_t)blk) * 2u), 0, 0));
+      if constexpr (ZK)
+        b.z[r] = __builtin_amdgcn_raw_buffer_load_b8(rZ, (int)(frow[r] * zrb + (uint32_t)(blk >> 1)), 0, 0);
+      else
+        b.z[r] = 0x88u;
+    }
+    if (++fit == iters) {
+      fit = 0;
+      fu += NW;
+      set_unit(fu);
+    }
+  };
+  // compute cursor: unit cu (local row base and slot), item cit
+  int cu = wave, cit = 0, c_lr = 0, c_j = 0, c_hrow = 0;
+  auto set_cunit = [&](int u) {
+    const int uu = u < nunits ? u : nunits - 1;
+    const int grp = g_begin + uu / k;
+    c_j = uu - (uu / k) * k;
+    c_lr = (grp - g_begin) * rpg;
+    c_hrow = (grp / GN) * k + c_j;  // row t * k + j of the staged h
+  };
+  set_cunit(cu);
+
+  float acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+  auto step = [&](const MoeItem<R>& cb, MoeItem<R>& nxt, bool live) {
+    fetch(nxt);
+    const int c = cit * LPR + lp;
+    const bool cv = live && c < nch;
+    const int cc = c < nch ? c : nch - 1;
+    const int blk = cc >> blk_shift;
+    const float* xp = hf + ((size_t)c_hrow * nch + cc) * 32;
+    float xa[32];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const f32x4 v = *(const f32x4*)(xp + 4 * q);
+      xa[4 * q] = v.x; xa[4 * q + 1] = v.y; xa[4 * q + 2] = v.z; xa[4 * q + 3] = v.w;
+    }
+    const float sac = sa[c_hrow * nch + cc];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float pr = dot_chunk_u4(cb.w[r], xa);
+      const float zp = (float)((cb.z[r] >> ((blk & 1) * 4)) & 0xfu);
+      const float nv = fmaf((float)cb.s[r], fmaf(-zp, sac, 512.0f * pr), acc[r]);
+      acc[r] = cv ? nv : acc[r];
+    }
+    if (live && cit == iters - 1) {
+      // unit complete: fixed-order combination of the lane partials of its slot
+#pragma unroll
+      for (int r = 0; r < R; ++r) acc[r] = group_sum(acc[r], LPR);
+      if (lp == 0) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) outs[(c_lr + r * SUBS + sub) * k + c_j] = acc[r];
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+    }
+    if (++cit == iters) {
+      cit = 0;
+      cu += NW;
+      set_cunit(cu);
+    }
+  };
+
+  // the activations' loads go out first, then the first weights, which travel while
+  // the activations are converted
+  MoeItem<R> buf[D];
+  set_unit(fu);
+  stage_f32_first(a.h, T * k, (int)a.I, nch, hf, sa, [&] {
+#pragma unroll
+    for (int i = 0; i < D - 1; ++i) fetch(buf[i]);
+  });
+  const int total = wave_units * iters;
+  for (int base = 0; base < total; base += D) {
+#pragma unroll
+    for (int i = 0; i < D; ++i) step(buf[i], buf[(i + D - 1) % D], base + i < total);
+  }
+  __syncthreads();
+  // y = sum_j w_j * (z_j + b2) in slot order, one rounding to fp16
+  const int nloc = (g_end - g_begin) * rpg;
+  for (int q = threadIdx.x; q < nloc; q += blockDim.x) {
+    const int grp = g_begin + q / rpg;
+    const int t = grp / GN;
+    const int n = (grp - t * GN) * rpg + (q - (q / rpg) * rpg);
+    if (n >= H) continue;
+    float y = 0.0f;
+    for (int j = 0; j < k; ++j) {
+      const int e = clamp_expert(a.ids[t * k + j], a.E);
+      const float z = outs[q * k + j] + (a.fc2.bias ? f16_to_f32(a.fc2.bias[(int64_t)e * a.H + n]) : 0.0f);
+      y = fmaf(a.rw[t * k + j], z, y);
+    }
+    a.Y[(int64_t)t * a.H + n] = f32_to_f16(y);
+  }
+}
+
 // ---- launch ---------------------------------------------------------------------
 
 size_t qmoe_fc1_lds_bytes(const QmoeArgs& a) {
@@ -535,7 +937,90 @@ static void allow_lds(Kern k, size_t lds) {
   if (lds > 64 * 1024) (void)hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
 }
 
-hipError_t launch_qmoe_fc1(const QmoeArgs& a, int rows_per_lane, hipStream_t st) {
+// Work-groups of `kern` with `lds` bytes of dynamic LDS resident on one compute unit
+// (cached per kernel and size).
+template <typename Kern>
+static int moe_resident_per_cu(Kern kern, size_t lds) {
+  static std::mutex mu;
+  static std::map<std::pair<const void*, size_t>, int> cache;
+  const auto key = std::make_pair((const void*)kern, lds);
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  allow_lds(kern, lds);
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, kMoeStreamThreads, lds) != hipSuccess || n < 1) {
+    (void)hipGetLastError();
+    n = 1;
+  }
+  cache[key] = n;
+  return n;
+}
+
+// Grid and LDS of a persistent form: one work-group per resident slot (at most one
+// per group), `fixed` bytes of staged activations plus `per_group` bytes of row sums
+// for each group of the work-group.  Returns false when it does not fit in LDS.
+template <typename Kern>
+static bool moe_stream_plan(Kern kern, int64_t ngroups, size_t fixed, size_t per_group, int num_cus,
+                            int64_t* grid, size_t* lds) {
+  constexpr size_t kMaxStreamLds = 150 * 1024;
+  if (ngroups < 1 || fixed + per_group > kMaxStreamLds) return false;
+  int per_cu = moe_resident_per_cu(kern, fixed + per_group);
+  for (int pass = 0; pass < 2; ++pass) {
+    const int64_t slots = (int64_t)(num_cus > 0 ? num_cus : 256) * per_cu;
+    *grid = slots < ngroups ? slots : ngroups;
+    *lds = fixed + (size_t)((ngroups + *grid - 1) / *grid) * per_group;
+    if (*lds > kMaxStreamLds) return false;
+    const int again = moe_resident_per_cu(kern, *lds);
+    if (again >= per_cu) break;
+    per_cu = again;
+  }
+  return true;
+}
+
+template <int RI, int ZK>
+static bool launch_fc1_stream(const QmoeArgs& a, hipStream_t st) {
+  auto kern = qmoe_fc1_stream_kernel<RI, ZK>;
+  // one expert's W1, scales and zero points are addressed with 32-bit offsets
+  const int64_t erows = 2 * a.I;
+  if (erows * a.fc1_row_bytes >= (1LL << 31) || erows * a.fc1_nblk * 2 >= (1LL << 31)) return false;
+  const int64_t rpg = (64 >> a.fc1_lpr_log2) * RI;
+  const int64_t ngroups = a.T * a.k * ((a.I + rpg - 1) / rpg);
+  const size_t fixed = (size_t)a.T * a.fc1_chunks * 33 * sizeof(float);
+  int64_t grid = 0;
+  size_t lds = 0;
+  if (!moe_stream_plan(kern, ngroups, fixed, (size_t)rpg * 2 * sizeof(float), a.num_cus, &grid, &lds))
+    return false;
+  allow_lds(kern, lds);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kMoeStreamThreads), lds, st, a);
+  return true;
+}
+
+template <int R, int ZK>
+static bool launch_fc2_stream(const QmoeArgs& a, hipStream_t st) {
+  auto kern = qmoe_fc2_stream_kernel<R, ZK>;
+  if (a.H * a.fc2_row_bytes >= (1LL << 31) || a.H * a.fc2_nblk * 2 >= (1LL << 31)) return false;
+  const int64_t rpg = (64 >> a.fc2_lpr_log2) * R;
+  const int64_t ngroups = a.T * ((a.H + rpg - 1) / rpg);
+  const size_t fixed = (size_t)a.T * a.k * a.fc2_chunks * 33 * sizeof(float);
+  int64_t grid = 0;
+  size_t lds = 0;
+  if (!moe_stream_plan(kern, ngroups, fixed, (size_t)rpg * a.k * sizeof(float), a.num_cus, &grid, &lds))
+    return false;
+  allow_lds(kern, lds);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kMoeStreamThreads), lds, st, a);
+  return true;
+}
+
+hipError_t launch_qmoe_fc1(const QmoeArgs& a, int candidate, hipStream_t st) {
+  const int rows_per_lane = candidate & 15;
+  if (a.mode != QMOE_INT8_ACT && !(candidate & kQmoePerSlot)) {
+    const bool zk = a.fc1.zp != nullptr;
+    bool done;
+    if (rows_per_lane == 1) done = zk ? launch_fc1_stream<1, 1>(a, st) : launch_fc1_stream<1, 0>(a, st);
+    else done = zk ? launch_fc1_stream<2, 1>(a, st) : launch_fc1_stream<2, 0>(a, st);
+    if (done) return hipSuccess;
+  }
   const int subs = 64 >> a.fc1_lpr_log2;
   const int64_t rows_per_wg = 4LL * subs * rows_per_lane;
   const dim3 grid((unsigned)((a.I + rows_per_wg - 1) / rows_per_wg), (unsigned)(a.T * a.k));
@@ -552,7 +1037,15 @@ hipError_t launch_qmoe_fc1(const QmoeArgs& a, int rows_per_lane, hipStream_t st)
   return hipSuccess;
 }
 
-hipError_t launch_qmoe_fc2(const QmoeArgs& a, int rows_per_lane, hipStream_t st) {
+hipError_t launch_qmoe_fc2(const QmoeArgs& a, int candidate, hipStream_t st) {
+  const int rows_per_lane = candidate & 15;
+  if (a.mode != QMOE_INT8_ACT && !(candidate & kQmoePerSlot)) {
+    const bool zk = a.fc2.zp != nullptr;
+    bool done;
+    if (rows_per_lane == 1) done = zk ? launch_fc2_stream<1, 1>(a, st) : launch_fc2_stream<1, 0>(a, st);
+    else done = zk ? launch_fc2_stream<2, 1>(a, st) : launch_fc2_stream<2, 0>(a, st);
+    if (done) return hipSuccess;
+  }
   const int subs = 64 >> a.fc2_lpr_log2;
   const int64_t rows_per_wg = 4LL * subs * rows_per_lane;
   const dim3 grid((unsigned)((a.H + rows_per_wg - 1) / rows_per_wg), (unsigned)a.T);

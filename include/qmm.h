@@ -182,7 +182,7 @@ qmm_status qmm_dequantize_codebook4(const uint8_t* W, int block, const float* ab
  * and the products with (q - zp) are summed exactly in int32 per 32 values.
  *
  *   X          fp16 [T][H]            Y fp16 [T][H]
- *   expert_ids int32 [T][k], each in [0, E)  (precondition, not checked on device)
+ *   expert_ids int32 [T][k], each in [0, E)  (an id outside is clamped into it on device)
  *   expert_w   fp32 [T][k]
  *   fc1.W      uint8 [E][2I][nblk(H)][block/2]   fc1.scales fp16 [E][2I][nblk(H)]
  *   fc1.zp     uint8 [E][2I][ceil(nblk(H)/2)] packed u4, or NULL (zp = 8)
