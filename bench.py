@@ -375,7 +375,7 @@ def qmoe_leg(args, name, T, H, I, E, k, block, zp, bias, mode, calls=48):
         routes.append((to_dev(ids), to_dev(w)))
         n_unique.append(len(np.unique(ids)))
     Y = torch.empty((T, H), dtype=torch.float16, device="cuda")
-    scratch = torch.empty(Q.qmoe_decode_scratch_bytes(T, H, I, k, mode), dtype=torch.uint8,
+    scratch = torch.zeros(Q.qmoe_decode_scratch_bytes(T, H, I, k, mode), dtype=torch.uint8,
                           device="cuda")
 
     def call(i):

@@ -63,7 +63,8 @@ bool env_flag(const char* name) {
 // ---------------------------------------------------------------------------
 // Tuner state
 // ---------------------------------------------------------------------------
-enum { ENTRY_NBITS = 0, ENTRY_CODEBOOK = 1, ENTRY_QMOE_FC1 = 2, ENTRY_QMOE_FC2 = 3, ENTRY_COUNT = 4 };
+enum { ENTRY_NBITS = 0, ENTRY_CODEBOOK = 1, ENTRY_QMOE_FC1 = 2, ENTRY_QMOE_FC2 = 3, ENTRY_QMOE_FUSED = 4,
+       ENTRY_COUNT = 5 };
 
 // GEMV candidates: rows of W per lane.
 constexpr int kGemvCandidates[] = {1, 2, 4};
@@ -74,7 +75,7 @@ struct TunerState {
   int mode = -1;  // -1: not yet read from the environment
   int forced = 0;
   std::map<std::tuple<int, int64_t, int64_t, int64_t, int, int, int, int>, int> choice;
-  int last_choice[ENTRY_COUNT] = {-1, -1, -1, -1};
+  int last_choice[ENTRY_COUNT] = {-1, -1, -1, -1, -1};
   // cold-rotation pool (library-owned device memory, allocated on first tuning)
   uint8_t* pool = nullptr;
   size_t pool_bytes = 0;
@@ -405,6 +406,120 @@ void qmoe_choice(const QmoeArgs& a, hipStream_t st, int* r1, int* r2) {
   finish(c1, c2);
 }
 
+
+// Candidate of the single-launch MoE form for a shape, or -1 for the two-kernel form
+// with the tiling (r1, r2) already chosen by qmoe_choice.  The first uncaptured call of
+// a shape times every single-launch candidate and that two-kernel pair the same way as
+// qmoe_choice (one discarded round, then 8 timed rounds, every launch on a different
+// expert set, writing only the call's scratch and a library-owned output); the least
+// total wins.  Without timing the two-kernel form is used (the faster one measured on
+// MI355X for the configured shapes).  Forced tuning: indices >= kQmoeForcedFused select
+// candidate (index - kQmoeForcedFused) of the single-launch form, smaller ones the
+// two-kernel form.
+constexpr int kQmoeForcedFused = kNumQmoeCandidates * kNumQmoeCandidates;
+constexpr int kQmoeFusedDefault = 6;  // 4 row groups per wave, 1 work-group per CU
+
+int qmoe_fused_choice(QmoeArgs& a, hipStream_t st, int r1, int r2) {
+  TunerState& t = tuner();
+  std::lock_guard<std::mutex> lock(t.mu);
+  const int mode = tuning_mode_locked(t);
+  auto plan = [&](int c) { return qmoe_fused_plan(a, c); };
+  auto finish = [&](int c) {
+    t.last_choice[ENTRY_QMOE_FUSED] = c;
+    return c;
+  };
+  if (mode == 2) {
+    if (t.forced < kQmoeForcedFused) return finish(-1);
+    const int c = (t.forced - kQmoeForcedFused) % kNumQmoeFused;
+    return plan(c) ? finish(c) : finish(-1);
+  }
+  if (mode == 1 || !plan(kQmoeFusedDefault)) return finish(-1);
+  auto key = std::make_tuple((int)ENTRY_QMOE_FUSED, a.T * 1000 + a.k, a.H, a.I, a.block, a.mode, (int)a.E,
+                             (a.fc1.zp != nullptr ? 2 : 0) + (a.fc2.zp != nullptr ? 1 : 0));
+  auto it = t.choice.find(key);
+  if (it != t.choice.end()) return plan(it->second) ? finish(it->second) : finish(-1);
+  if (stream_capturing(st)) return finish(-1);
+  QmoeTimingBufs& b = qmoe_bufs();
+  constexpr int kRounds = 9;
+  constexpr int kCands = kNumQmoeFused + 1;  // the last one is the two-kernel pair
+  const int sets = kRounds * kCands;
+  const size_t ids_count = (size_t)sets * a.T * a.k;
+  const size_t y_bytes = (size_t)a.T * a.H * 2;
+  bool ok = true;
+  if (b.ids_count < ids_count) {
+    if (b.ids) (void)hipFree(b.ids);
+    b.ids = nullptr;
+    b.ids_count = 0;
+    ok = hipMalloc((void**)&b.ids, ids_count * 4) == hipSuccess;
+    if (ok) b.ids_count = ids_count;
+  }
+  if (ok && b.y_bytes < y_bytes) {
+    if (b.y) (void)hipFree(b.y);
+    b.y = nullptr;
+    b.y_bytes = 0;
+    ok = hipMalloc((void**)&b.y, y_bytes) == hipSuccess;
+    if (ok) b.y_bytes = y_bytes;
+  }
+  if (ok) {
+    std::vector<int32_t> hid(ids_count);
+    for (int s = 0; s < sets; ++s)
+      for (int64_t tt = 0; tt < a.T; ++tt)
+        for (int j = 0; j < a.k; ++j)
+          hid[((size_t)s * a.T + tt) * a.k + j] = (int32_t)(((int64_t)s * a.k * a.T + tt * a.k + j) % a.E);
+    ok = hipMemcpy(b.ids, hid.data(), ids_count * 4, hipMemcpyHostToDevice) == hipSuccess;
+  }
+  int best = kNumQmoeFused;
+  if (ok) {
+    hipEvent_t e0, e1;
+    ok = hipEventCreate(&e0) == hipSuccess && hipEventCreate(&e1) == hipSuccess;
+    std::vector<double> tv(kRounds * kCands, 1e30);
+    int set = 0;
+    for (int r = 0; ok && r < kRounds; ++r) {
+      for (int c = 0; ok && c < kCands; ++c) {
+        QmoeArgs ta = a;
+        ta.ids = b.ids + (size_t)(set++) * a.T * a.k;
+        ta.Y = b.y;
+        if (c < kNumQmoeFused && !qmoe_fused_plan(ta, c)) continue;
+        ok = hipEventRecord(e0, st) == hipSuccess;
+        if (c < kNumQmoeFused) {
+          ok = ok && launch_qmoe_fused(ta, st) == hipSuccess;
+        } else {
+          ok = ok && launch_qmoe_fc1(ta, r1, st) == hipSuccess && launch_qmoe_fc2(ta, r2, st) == hipSuccess;
+        }
+        ok = ok && hipPeekAtLastError() == hipSuccess;
+        ok = ok && hipEventRecord(e1, st) == hipSuccess && hipEventSynchronize(e1) == hipSuccess;
+        float ms = 0;
+        ok = ok && hipEventElapsedTime(&ms, e0, e1) == hipSuccess;
+        tv[r * kCands + c] = ms * 1000.0;
+      }
+    }
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    if (ok) {
+      best = pick_winner(tv.data(), kRounds, kCands);
+      t.choice[key] = best < kNumQmoeFused ? best : -1;
+      if (env_flag("QMM_LOG")) {
+        std::fprintf(stderr, "[qmm] tune qmoe fused T=%lld H=%lld I=%lld E=%lld k=%d block=%d ->", (long long)a.T,
+                     (long long)a.H, (long long)a.I, (long long)a.E, a.k, a.block);
+        for (int c = 0; c < kCands; ++c) {
+          double tot = 0;
+          for (int r = 1; r < kRounds; ++r) tot += tv[r * kCands + c];
+          if (c < kNumQmoeFused)
+            std::fprintf(stderr, " g%d/w%d:%.2fus", kQmoeFusedGpw[c / 3], kQmoeFusedWpc[c % 3], tot / (kRounds - 1));
+          else
+            std::fprintf(stderr, " two-kernel:%.2fus", tot / (kRounds - 1));
+        }
+        std::fprintf(stderr, " pick #%d\n", best);
+      }
+    }
+  }
+  if (!ok) {
+    (void)hipGetLastError();
+    best = kNumQmoeFused;
+  }
+  return (best < kNumQmoeFused && plan(best)) ? finish(best) : finish(-1);
+}
+
 // ---------------------------------------------------------------------------
 // argument checks
 // ---------------------------------------------------------------------------
@@ -456,7 +571,7 @@ qmm_status check_codebook(const void* A, int a_type, int64_t M, int64_t K, int64
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct QmoeLayout {
-  size_t h = 0, xq = 0, xs = 0, hq = 0, hs = 0, total = 0;
+  size_t h = 0, zpart = 0, sync = 0, xq = 0, xs = 0, hq = 0, hs = 0, total = 0;
 };
 
 QmoeLayout qmoe_layout(int64_t T, int64_t H, int64_t I, int k, int mode) {
@@ -464,6 +579,12 @@ QmoeLayout qmoe_layout(int64_t T, int64_t H, int64_t I, int k, int mode) {
   size_t off = 0;
   L.h = off;
   off += align256((size_t)(T * k * I) * 2);
+  if (mode == QMOE_FP) {
+    L.zpart = off;
+    off += align256((size_t)(T * k * H) * 4);
+    L.sync = off;
+    off += align256((size_t)qmoe_sync_words(T, H, k) * 4);
+  }
   if (mode == QMOE_INT8_ACT) {
     L.xq = off;
     off += align256((size_t)(T * H));
@@ -844,8 +965,17 @@ qmm_status qmoe_decode_fused(const uint16_t* X, int64_t T, int64_t H, int64_t I,
     a.hs_out = (float*)(sc + L.hs);
   }
   a.Y = Y;
+  if (mode == QMOE_FP) {
+    a.zpart = (float*)(sc + L.zpart);
+    a.sync = (uint32_t*)(sc + L.sync);
+  }
   int r1 = 1, r2 = 1;
   qmoe_choice(a, st, &r1, &r2);
+  if (mode == QMOE_FP && qmoe_fused_choice(a, st, r1, r2) >= 0) {
+    const hipError_t e = launch_qmoe_fused(a, st);
+    if (e != hipSuccess) return (qmm_status)e;
+    return (qmm_status)hipGetLastError();
+  }
   hipError_t e = launch_qmoe_fc1(a, r1, st);
   if (e == hipSuccess) e = launch_qmoe_fc2(a, r2, st);
   if (e != hipSuccess) return (qmm_status)e;
@@ -864,6 +994,7 @@ qmm_status qmm_set_tuning(int mode, int forced_index) {
 int qmm_num_candidates(int entry) {
   if (entry == ENTRY_NBITS || entry == ENTRY_CODEBOOK) return kNumGemvCandidates;
   if (entry == ENTRY_QMOE_FC1 || entry == ENTRY_QMOE_FC2) return kNumQmoeCandidates;
+  if (entry == ENTRY_QMOE_FUSED) return kNumQmoeFused;
   return 0;
 }
 

@@ -20,7 +20,7 @@ QMOE_FP, QMOE_INT8_ACT = 0, 1
 STATUS = {0: "QMM_OK", -1: "QMM_E_NULL", -2: "QMM_E_DTYPE", -3: "QMM_E_BITS", -4: "QMM_E_BLOCK",
           -5: "QMM_E_SHAPE", -6: "QMM_E_ALIGN", -7: "QMM_E_WORKSPACE", -8: "QMM_E_MODE",
           -9: "QMM_E_DEVICE"}
-ENTRY_NBITS, ENTRY_CODEBOOK, ENTRY_QMOE_FC1, ENTRY_QMOE_FC2 = 0, 1, 2, 3
+ENTRY_NBITS, ENTRY_CODEBOOK, ENTRY_QMOE_FC1, ENTRY_QMOE_FC2, ENTRY_QMOE_FUSED = 0, 1, 2, 3, 4
 
 
 class QmmError(RuntimeError):
@@ -247,7 +247,8 @@ def qmoe_decode_fused(X, expert_ids, expert_w, fc1, fc2, H, I, E, block, mode=QM
         out = torch.empty((T, H), dtype=torch.float16, device=X.device)
     sb = lib().qmoe_decode_scratch_bytes(T, H, I, k, mode)
     if scratch is None:
-        scratch = torch.empty(max(sb, 1), dtype=torch.uint8, device=X.device)
+        # zeroed: the single-launch form's sync words must start at zero (calls leave them so)
+        scratch = torch.zeros(max(sb, 1), dtype=torch.uint8, device=X.device)
     st = lib().qmoe_decode_fused(_ptr(X), T, H, I, E, k, _ptr(expert_ids), _ptr(expert_w), _qw(fc1),
                                  _qw(fc2), bits, block, mode, _ptr(out), _ptr(scratch),
                                  scratch.numel() * scratch.element_size(), _stream(stream))

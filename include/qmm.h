@@ -190,10 +190,25 @@ qmm_status qmm_dequantize_codebook4(const uint8_t* W, int block, const float* ab
  *   fc2.*      the same with [E][H][..] over K = I
  *   bits       4.  block in {32, 64, 128, 256} (int8 mode additionally needs
  *              H % 32 == 0 and I % 32 == 0).
- *   scratch    device buffer of at least qmoe_decode_scratch_bytes(T, H, I, k, mode).
- *              Layout: fp16 h [T][k][I] at offset 0; in int8 mode followed (at the
- *              next 256-byte boundary) by int8 x codes [T][H], fp32 x scales
- *              [T][H/32], int8 h codes [T][k][I], fp32 h scales [T][k][I/32].
+ *   scratch    device buffer of at least qmoe_decode_scratch_bytes(T, H, I, k, mode),
+ *              256-byte aligned.  Layout: fp16 h [T][k][I] at offset 0, then (each
+ *              region at the next 256-byte boundary) in fp mode fp32 slot sums
+ *              z [T][k][H] and the uint32 sync words of the single-launch form
+ *              (4 + T*k + T*ceil(H/4) words); in int8 mode int8 x codes [T][H], fp32
+ *              x scales [T][H/32], int8 h codes [T][k][I], fp32 h scales [T][k][I/32].
+ *              The sync words must be zero before the first call on a buffer (zero
+ *              the whole buffer once, e.g. hipMemset); every call leaves the first
+ *              two and the counters zero again.  The third word is an error flag
+ *              that a call sets, and leaves set, if a wait inside the launch gave up
+ *              after 1 s (a broken sync region); the output of that call is invalid.
+ *              Calls that share a scratch buffer must not overlap.
+ *   Launches   fp mode runs fc1, SwiGLU, fc2 and the combine in ONE launch: work
+ *              items (fc1 row runs, then fc2 row tiles) are taken in order from a
+ *              counter, an fc2 item waits only for the fc1 items of its own slot,
+ *              and the last of the k slot items of a row tile combines the slot sums
+ *              in slot order.  Items are only held by running work-groups, so no
+ *              wait depends on co-residency.  int8 mode runs fc1, the h quantizer
+ *              and fc2 as three launches.  Every form gives the same bits.
  *   E          num_experts: the first call of a shape times tiling candidates on
  *              other expert sets, writing only scratch.
  * ------------------------------------------------------------------------- */
@@ -223,8 +238,11 @@ qmm_status qmm_validate_qmoe(const uint16_t* X, int64_t T, int64_t H, int64_t I,
  *   1 = never time, always use the default tiling, 2 = force candidate
  *   `forced_index` (for tests: every candidate must give identical bits).
  * qmm_tuned_choice: the candidate index chosen for the last call of the given
- *   entry (0 = qmm_nbits GEMV, 1 = qmm_codebook4 GEMV, 2 = qmoe fc1, 3 = qmoe fc2),
- *   or -1 if none; qmm_num_candidates gives the candidate count per entry.
+ *   entry (0 = qmm_nbits GEMV, 1 = qmm_codebook4 GEMV, 2 = qmoe fc1, 3 = qmoe fc2,
+ *   4 = qmoe single-launch form, -1 when the last MoE call used two kernels), or -1
+ *   if none; qmm_num_candidates gives the candidate count per entry.  Forced MoE
+ *   indices below n(2) * n(3) pick the two-kernel form (fc1 = index % n(2),
+ *   fc2 = index / n(2)); index n(2) * n(3) + c picks candidate c of entry 4.
  * qmm_clear_tuning forgets every cached choice.
  * ------------------------------------------------------------------------- */
 qmm_status qmm_set_tuning(int mode, int forced_index);

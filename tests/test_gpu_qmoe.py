@@ -165,3 +165,125 @@ def test_zero_tokens_and_refusals():
     with pytest.raises(Q.QmmError) as e:
         Q.qmoe_decode_fused(d.X, d.ids, d.rw, d.fc["fc1"], d.fc["fc2"], 512, 256, 8, 64, scratch=small)
     assert e.value.status == -7
+
+
+# ---- single-launch form (fp mode) --------------------------------------------------
+
+def _fused_base():
+    return Q.num_candidates(Q.ENTRY_QMOE_FC1) * Q.num_candidates(Q.ENTRY_QMOE_FC2)
+
+
+def _sync_words(raw, T, H, I, k):
+    """The sync words of the fp-mode scratch layout (after h and the fp32 slot sums)."""
+    a256 = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    off = a256(T * k * I * 2) + a256(T * k * H * 4)
+    n = 4 + T * k + T * ((H + 3) // 4)
+    return raw[off:off + 4 * n].view(np.uint32)
+
+
+FUSED_CASES = [
+    # (T, H, I, E, k, block, zp, bias)
+    (1, 2880, 2880, 32, 4, 32, True, True),      # GPT-OSS-20B shape, 90 blocks per row
+    (1, 2880, 2880, 32, 4, 128, False, True),    # ragged last block (22.5 blocks)
+    (4, 2048, 768, 128, 8, 64, True, False),     # 128 experts, top-8, 4 tokens
+    (3, 1000, 520, 10, 3, 64, True, True),       # ragged rows, tiles and blocks
+]
+
+
+@pytest.mark.parametrize("case", FUSED_CASES, ids=[f"T{c[0]}-H{c[1]}-I{c[2]}-B{c[5]}" for c in FUSED_CASES])
+def test_single_launch_equals_two_kernel_forms(case):
+    """Every candidate of the single-launch form gives the bits of the two-kernel forms,
+    leaves its sync words at zero with no error, and stays within the oracle tolerance."""
+    t = torch()
+    T, H, I, E, k, block, zp, bias = case
+    say(f"qmoe single launch T={T} H={H} I={I} E={E} k={k} block={block} zp={zp} bias={bias}")
+    p = gen.qmoe_problem(T, H, I, E, k, block, seed=910 + T + block, zp=zp, bias=bias)
+    d = MoeDev(p)
+    base = _fused_base()
+    nbytes = Q.qmoe_decode_scratch_bytes(T, H, I, k, Q.QMOE_FP)
+    try:
+        Q.set_tuning(2, 0)
+        ref = host_bits(d.run(Q.QMOE_FP)).copy()
+        assert Q.tuned_choice(Q.ENTRY_QMOE_FUSED) == -1
+        for c in range(Q.num_candidates(Q.ENTRY_QMOE_FUSED)):
+            Q.set_tuning(2, base + c)
+            scratch = t.zeros(nbytes, dtype=t.uint8, device="cuda")
+            for rep in range(3):
+                y = d.run(Q.QMOE_FP, scratch=scratch)
+                assert Q.tuned_choice(Q.ENTRY_QMOE_FUSED) == c
+                assert np.array_equal(host_bits(y), ref), (c, rep)
+                words = _sync_words(scratch.cpu().numpy(), T, H, I, k)
+                assert not words.any(), (c, rep, np.nonzero(words)[0][:8])
+    finally:
+        Q.set_tuning(0, 0)
+    err = O.rel_l2(ref.view(np.float16).astype(np.float64), d.oracle(Q.QMOE_FP))
+    say(f"  relL2={err:.3e}")
+    assert err <= TOL["f16"]
+
+
+def test_single_launch_graph_replays():
+    """Calls of the single-launch form captured in a HIP graph and replayed several
+    times, with eager calls on the same scratch between the replays, give the eager bits
+    on every replay (its counters return to zero at the end of every launch)."""
+    Q.set_tuning(2, _fused_base() + 6)
+    try:
+        _graph_replays()
+    finally:
+        Q.set_tuning(0, 0)
+
+
+def _graph_replays():
+    t = torch()
+    T, H, I, E, k, block = 2, 2880, 2880, 32, 4, 64
+    p = gen.qmoe_problem(T, H, I, E, k, block, seed=921, zp=True, bias=True)
+    d = MoeDev(p)
+    rng = np.random.default_rng(922)
+    routes = []
+    for _ in range(3):
+        ids, w = gen.routing(rng, T, E, k)
+        routes.append((dev(ids), dev(w)))
+    scratch = t.zeros(Q.qmoe_decode_scratch_bytes(T, H, I, k, Q.QMOE_FP), dtype=t.uint8, device="cuda")
+    outs = [t.empty((T, H), dtype=t.float16, device="cuda") for _ in routes]
+    eager = []
+    for (ids, w), o in zip(routes, outs):
+        eager.append(host_bits(d.run(Q.QMOE_FP, ids=ids, rw=w, out=o, scratch=scratch)).copy())
+    assert Q.tuned_choice(Q.ENTRY_QMOE_FUSED) == 6
+    cap = t.cuda.Stream()
+    g = t.cuda.CUDAGraph()
+    with t.cuda.stream(cap):
+        with t.cuda.graph(g, stream=cap):
+            for (ids, w), o in zip(routes, outs):
+                d.run(Q.QMOE_FP, ids=ids, rw=w, out=o, scratch=scratch)
+    t.cuda.synchronize()
+    for rep in range(4):
+        for o in outs:
+            o.zero_()
+        g.replay()
+        t.cuda.synchronize()
+        for i, o in enumerate(outs):
+            assert np.array_equal(host_bits(o), eager[i]), (rep, i)
+        y = d.run(Q.QMOE_FP, ids=routes[rep % 3][0], rw=routes[rep % 3][1], scratch=scratch)
+        assert np.array_equal(host_bits(y), eager[rep % 3]), rep
+    assert not _sync_words(scratch.cpu().numpy(), T, H, I, k).any()
+
+
+@pytest.mark.parametrize("form", ["tuned", "single-launch"])
+def test_repeat_calls_bit_identical_fp(form):
+    """129 calls of the fp decode on one input give identical bits: the form the
+    up-front timing picks (a shape no other test uses, so the first call times), and
+    the single-launch form forced."""
+    p = gen.qmoe_problem(1, 1408, 704, 24, 6, 32, seed=923, zp=True, bias=True)
+    d = MoeDev(p)
+    if form == "single-launch":
+        Q.set_tuning(2, _fused_base() + 4)
+    try:
+        first = host_bits(d.run(Q.QMOE_FP)).copy()
+        if form == "single-launch":
+            assert Q.tuned_choice(Q.ENTRY_QMOE_FUSED) == 4
+        out = torch().empty_like(d.X[:, :1408])
+        for i in range(128):
+            d.run(Q.QMOE_FP, out=out)
+            assert np.array_equal(host_bits(out), first), i
+    finally:
+        Q.set_tuning(0, 0)
+    assert O.rel_l2(first.view(np.float16).astype(np.float64), d.oracle(Q.QMOE_FP)) <= TOL["f16"]
