@@ -24,6 +24,7 @@
 
 #include "qmm.h"
 #include "qmm_internal.h"
+#include "qmm_qmoe.h"
 
 using namespace qmm;
 
@@ -268,9 +269,11 @@ int gemv_choice(int entry, const GemvArgs& g, hipStream_t st) {
 
 // MoE decode candidates, for fc1 and fc2 alike: rows per lane (low bits; an fc1 row
 // is a g row and its u row) and the form (kQmoePerSlot: one work-group per row tile
-// and slot; else the persistent form, fp mode only).  All give the same bits.
-constexpr int kQmoeCandidates[] = {1, 2, 1 | kQmoePerSlot, 2 | kQmoePerSlot};
-constexpr int kNumQmoeCandidates = 4;
+// and slot; else the persistent form, fp mode only, with as many work-groups per
+// compute unit as fit, or one with kQmoeOnePerCu).  All give the same bits.
+constexpr int kQmoeCandidates[] = {1, 2, 1 | kQmoePerSlot, 2 | kQmoePerSlot, 1 | kQmoeOnePerCu,
+                                   2 | kQmoeOnePerCu};
+constexpr int kNumQmoeCandidates = 6;
 
 struct QmoeTimingBufs {
   int32_t* ids = nullptr;  // timing expert ids, [kSets][T][k]
@@ -391,7 +394,8 @@ void qmoe_choice(const QmoeArgs& a, hipStream_t st, int* r1, int* r2) {
           for (int c = 0; c < kNumQmoeCandidates; ++c) {
             double tot = 0;
             for (int r = 1; r < kRounds; ++r) tot += tv[r * kNumQmoeCandidates + c];
-            std::fprintf(stderr, " %s%d:%.2fus", (kQmoeCandidates[c] & kQmoePerSlot) ? "slot-R" : "R",
+            std::fprintf(stderr, " %s%d:%.2fus",
+                         (kQmoeCandidates[c] & kQmoePerSlot) ? "slot-R" : (kQmoeCandidates[c] & kQmoeOnePerCu) ? "cu1-R" : "R",
                          kQmoeCandidates[c] & 15, tot / (kRounds - 1));
           }
           std::fprintf(stderr, " pick #%d\n", which == 0 ? c1 : c2);

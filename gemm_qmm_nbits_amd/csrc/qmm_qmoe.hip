@@ -21,6 +21,7 @@
 // sum((q - zp) * xq) = sum(q * xq) - zp * sum(xq).
 #include "qmm_device.h"
 #include "qmm_internal.h"
+#include "qmm_qmoe.h"
 
 #include <map>
 #include <mutex>
@@ -1339,12 +1340,15 @@ static int moe_resident_per_cu(Kern kern, size_t lds) {
 // Grid and LDS of a persistent form: one work-group per resident slot (at most one
 // per group), `fixed` bytes of staged activations plus `per_group` bytes of row sums
 // for each group of the work-group.  Returns false when it does not fit in LDS.
+// `cap` limits the work-groups per compute unit (fewer, longer work-groups stage the
+// activations fewer times).
 template <typename Kern>
-static bool moe_stream_plan(Kern kern, int64_t ngroups, size_t fixed, size_t per_group, int num_cus,
+static bool moe_stream_plan(Kern kern, int64_t ngroups, size_t fixed, size_t per_group, int num_cus, int cap,
                             int64_t* grid, size_t* lds) {
   constexpr size_t kMaxStreamLds = 150 * 1024;
   if (ngroups < 1 || fixed + per_group > kMaxStreamLds) return false;
   int per_cu = moe_resident_per_cu(kern, fixed + per_group);
+  if (per_cu > cap) per_cu = cap;
   for (int pass = 0; pass < 2; ++pass) {
     const int64_t slots = (int64_t)(num_cus > 0 ? num_cus : 256) * per_cu;
     *grid = slots < ngroups ? slots : ngroups;
@@ -1358,7 +1362,7 @@ static bool moe_stream_plan(Kern kern, int64_t ngroups, size_t fixed, size_t per
 }
 
 template <int RI, int ZK>
-static bool launch_fc1_stream(const QmoeArgs& a, hipStream_t st) {
+static bool launch_fc1_stream(const QmoeArgs& a, int cap, hipStream_t st) {
   auto kern = qmoe_fc1_stream_kernel<RI, ZK>;
   // one expert's W1, scales and zero points are addressed with 32-bit offsets
   const int64_t erows = 2 * a.I;
@@ -1368,7 +1372,7 @@ static bool launch_fc1_stream(const QmoeArgs& a, hipStream_t st) {
   const size_t fixed = (size_t)a.T * a.fc1_chunks * 33 * sizeof(float);
   int64_t grid = 0;
   size_t lds = 0;
-  if (!moe_stream_plan(kern, ngroups, fixed, (size_t)rpg * 2 * sizeof(float), a.num_cus, &grid, &lds))
+  if (!moe_stream_plan(kern, ngroups, fixed, (size_t)rpg * 2 * sizeof(float), a.num_cus, cap, &grid, &lds))
     return false;
   allow_lds(kern, lds);
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kMoeStreamThreads), lds, st, a);
@@ -1376,7 +1380,7 @@ static bool launch_fc1_stream(const QmoeArgs& a, hipStream_t st) {
 }
 
 template <int R, int ZK>
-static bool launch_fc2_stream(const QmoeArgs& a, hipStream_t st) {
+static bool launch_fc2_stream(const QmoeArgs& a, int cap, hipStream_t st) {
   auto kern = qmoe_fc2_stream_kernel<R, ZK>;
   if (a.H * a.fc2_row_bytes >= (1LL << 31) || a.H * a.fc2_nblk * 2 >= (1LL << 31)) return false;
   const int64_t rpg = (64 >> a.fc2_lpr_log2) * R;
@@ -1384,7 +1388,7 @@ static bool launch_fc2_stream(const QmoeArgs& a, hipStream_t st) {
   const size_t fixed = (size_t)a.T * a.k * a.fc2_chunks * 33 * sizeof(float);
   int64_t grid = 0;
   size_t lds = 0;
-  if (!moe_stream_plan(kern, ngroups, fixed, (size_t)rpg * a.k * sizeof(float), a.num_cus, &grid, &lds))
+  if (!moe_stream_plan(kern, ngroups, fixed, (size_t)rpg * a.k * sizeof(float), a.num_cus, cap, &grid, &lds))
     return false;
   allow_lds(kern, lds);
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kMoeStreamThreads), lds, st, a);
@@ -1455,8 +1459,9 @@ hipError_t launch_qmoe_fc1(const QmoeArgs& a, int candidate, hipStream_t st) {
   if (a.mode != QMOE_INT8_ACT && !(candidate & kQmoePerSlot)) {
     const bool zk = a.fc1.zp != nullptr;
     bool done;
-    if (rows_per_lane == 1) done = zk ? launch_fc1_stream<1, 1>(a, st) : launch_fc1_stream<1, 0>(a, st);
-    else done = zk ? launch_fc1_stream<2, 1>(a, st) : launch_fc1_stream<2, 0>(a, st);
+    const int cap = (candidate & kQmoeOnePerCu) ? 1 : 1 << 20;
+    if (rows_per_lane == 1) done = zk ? launch_fc1_stream<1, 1>(a, cap, st) : launch_fc1_stream<1, 0>(a, cap, st);
+    else done = zk ? launch_fc1_stream<2, 1>(a, cap, st) : launch_fc1_stream<2, 0>(a, cap, st);
     if (done) return hipSuccess;
   }
   const int subs = 64 >> a.fc1_lpr_log2;
@@ -1480,8 +1485,9 @@ hipError_t launch_qmoe_fc2(const QmoeArgs& a, int candidate, hipStream_t st) {
   if (a.mode != QMOE_INT8_ACT && !(candidate & kQmoePerSlot)) {
     const bool zk = a.fc2.zp != nullptr;
     bool done;
-    if (rows_per_lane == 1) done = zk ? launch_fc2_stream<1, 1>(a, st) : launch_fc2_stream<1, 0>(a, st);
-    else done = zk ? launch_fc2_stream<2, 1>(a, st) : launch_fc2_stream<2, 0>(a, st);
+    const int cap = (candidate & kQmoeOnePerCu) ? 1 : 1 << 20;
+    if (rows_per_lane == 1) done = zk ? launch_fc2_stream<1, 1>(a, cap, st) : launch_fc2_stream<1, 0>(a, cap, st);
+    else done = zk ? launch_fc2_stream<2, 1>(a, cap, st) : launch_fc2_stream<2, 0>(a, cap, st);
     if (done) return hipSuccess;
   }
   const int subs = 64 >> a.fc2_lpr_log2;
