@@ -421,7 +421,6 @@ void qmoe_choice(const QmoeArgs& a, hipStream_t st, int* r1, int* r2) {
 // candidate (index - kQmoeForcedFused) of the single-launch form, smaller ones the
 // two-kernel form.
 constexpr int kQmoeForcedFused = kNumQmoeCandidates * kNumQmoeCandidates;
-constexpr int kQmoeFusedDefault = 6;  // 4 row groups per wave, 1 work-group per CU
 
 int qmoe_fused_choice(QmoeArgs& a, hipStream_t st, int r1, int r2) {
   TunerState& t = tuner();
@@ -437,12 +436,18 @@ int qmoe_fused_choice(QmoeArgs& a, hipStream_t st, int r1, int r2) {
     const int c = (t.forced - kQmoeForcedFused) % kNumQmoeFused;
     return plan(c) ? finish(c) : finish(-1);
   }
-  if (mode == 1 || !plan(kQmoeFusedDefault)) return finish(-1);
+  if (mode == 1) return finish(-1);
   auto key = std::make_tuple((int)ENTRY_QMOE_FUSED, a.T * 1000 + a.k, a.H, a.I, a.block, a.mode, (int)a.E,
                              (a.fc1.zp != nullptr ? 2 : 0) + (a.fc2.zp != nullptr ? 1 : 0));
   auto it = t.choice.find(key);
   if (it != t.choice.end()) return plan(it->second) ? finish(it->second) : finish(-1);
   if (stream_capturing(st)) return finish(-1);
+  bool any = false;
+  for (int c = 0; c < kNumQmoeFused; ++c) any = any || plan(c);
+  if (!any) {
+    t.choice[key] = -1;
+    return finish(-1);
+  }
   QmoeTimingBufs& b = qmoe_bufs();
   constexpr int kRounds = 9;
   constexpr int kCands = kNumQmoeFused + 1;  // the last one is the two-kernel pair
@@ -509,7 +514,7 @@ int qmoe_fused_choice(QmoeArgs& a, hipStream_t st, int r1, int r2) {
           double tot = 0;
           for (int r = 1; r < kRounds; ++r) tot += tv[r * kCands + c];
           if (c < kNumQmoeFused)
-            std::fprintf(stderr, " g%d/w%d:%.2fus", kQmoeFusedGpw[c / 3], kQmoeFusedWpc[c % 3], tot / (kRounds - 1));
+            std::fprintf(stderr, " fc2R%d/w%d:%.2fus", kQmoeFusedR2[c % 2], kQmoeFusedWpc[c / 2], tot / (kRounds - 1));
           else
             std::fprintf(stderr, " two-kernel:%.2fus", tot / (kRounds - 1));
         }
@@ -575,7 +580,7 @@ qmm_status check_codebook(const void* A, int a_type, int64_t M, int64_t K, int64
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct QmoeLayout {
-  size_t h = 0, zpart = 0, sync = 0, xq = 0, xs = 0, hq = 0, hs = 0, total = 0;
+  size_t h = 0, sync = 0, xq = 0, xs = 0, hq = 0, hs = 0, total = 0;
 };
 
 QmoeLayout qmoe_layout(int64_t T, int64_t H, int64_t I, int k, int mode) {
@@ -584,10 +589,8 @@ QmoeLayout qmoe_layout(int64_t T, int64_t H, int64_t I, int k, int mode) {
   L.h = off;
   off += align256((size_t)(T * k * I) * 2);
   if (mode == QMOE_FP) {
-    L.zpart = off;
-    off += align256((size_t)(T * k * H) * 4);
     L.sync = off;
-    off += align256((size_t)qmoe_sync_words(T, H, k) * 4);
+    off += align256((size_t)kQmoeSyncWords * 4);
   }
   if (mode == QMOE_INT8_ACT) {
     L.xq = off;
@@ -970,13 +973,12 @@ qmm_status qmoe_decode_fused(const uint16_t* X, int64_t T, int64_t H, int64_t I,
   }
   a.Y = Y;
   if (mode == QMOE_FP) {
-    a.zpart = (float*)(sc + L.zpart);
     a.sync = (uint32_t*)(sc + L.sync);
   }
   int r1 = 1, r2 = 1;
   qmoe_choice(a, st, &r1, &r2);
   if (mode == QMOE_FP && qmoe_fused_choice(a, st, r1, r2) >= 0) {
-    const hipError_t e = launch_qmoe_fused(a, st);
+    const hipError_t e = launch_qmoe_fused(a, st);  // the plan has checked that it fits
     if (e != hipSuccess) return (qmm_status)e;
     return (qmm_status)hipGetLastError();
   }

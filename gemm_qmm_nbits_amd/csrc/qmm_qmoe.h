@@ -29,30 +29,25 @@ struct QmoeArgs {
   float* hs_out;    // int8 mode: [T][k][I/32] scales of h
   uint16_t* Y;
   int num_cus;      // compute units of the device
-  // single-launch form (fp mode): groups per wave per work item, items per slot,
-  // fp32 slot sums [T*k][H] and the self-resetting sync words (see qmoe_sync_words)
-  int f_gpw1, f_gpw2;
-  int f_wpc;  // work-groups per compute unit in the grid (capped by occupancy)
-  int64_t f_n1s, f_n2s;
-  float* zpart;
+  // single-launch form (fp mode): fc2 rows per lane, work-groups per compute unit,
+  // and the self-resetting sync words in scratch (kQmoeSyncWords)
+  int f_r2;
+  int f_wpc;
   uint32_t* sync;
 };
-// Sync words of the single-launch form, in scratch: [0] next work item, [1] finished
-// work-groups, [2] error flag (a wait that timed out), [3] unused, then the finished
-// fc1 items of each slot [T*k], then the finished slots of each fc2 row tile [T][n2s].
-// They must be zero before the first call on a scratch buffer; every call leaves them
-// zero.
-constexpr int kSyncHead = 4;
-inline int64_t qmoe_sync_words(int64_t T, int64_t H, int k) {
-  return kSyncHead + T * k + T * ((H + 3) / 4);
-}
-// Geometry of the single-launch form for candidate c: row groups per wave per work
-// item kQmoeFusedGpw[c / 3], work-groups per compute unit kQmoeFusedWpc[c % 3]; false
-// when the form does not apply (int8 mode, 32-bit offsets, LDS).
-constexpr int kQmoeFusedGpw[] = {1, 2, 4};
-constexpr int kQmoeFusedWpc[] = {1, 2, 4};
-constexpr int kNumQmoeFused = 9;
+// Sync words of the single-launch form, in scratch: [0] work-groups arrived (fc1
+// share done), [1] work-groups finished, [2] error flag (a wait that timed out),
+// [3] unused.  They must be zero before the first call on a scratch buffer; every call
+// leaves [0] and [1] zero.
+constexpr int64_t kQmoeSyncWords = 4;
+// Single-launch candidates: candidate c runs fc2 with kQmoeFusedR2[c % 2] rows per lane
+// and kQmoeFusedWpc[c / 2] work-groups per compute unit (fewer when they do not fit).
+constexpr int kQmoeFusedR2[] = {1, 2};
+constexpr int kQmoeFusedWpc[] = {1, 2};
+constexpr int kNumQmoeFused = 4;
+// Fill the candidate's parameters; false when the form does not apply (int8 mode).
 bool qmoe_fused_plan(QmoeArgs& a, int candidate);
+// hipErrorNotSupported when the shape does not fit the form (LDS, 32-bit offsets).
 hipError_t launch_qmoe_fused(const QmoeArgs& a, hipStream_t st);
 size_t qmoe_fc1_lds_bytes(const QmoeArgs& a);
 size_t qmoe_fc2_lds_bytes(const QmoeArgs& a);

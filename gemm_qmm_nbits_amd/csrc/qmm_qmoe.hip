@@ -587,6 +587,36 @@ __global__ __launch_bounds__(kMoeThreads) void qmoe_fc2_kernel(QmoeArgs a) {
   }
 }
 
+// fp32 staging of `rows` fp16 rows of n values each (n % 8 == 0, row stride n) that
+// other work-groups of the same launch wrote: device-coherent 16-byte loads, the same
+// values and chunk sums as stage_f32 (xf[r][nch * 32], zero past n; sa[r][nch]).
+__device__ __forceinline__ void stage_h_coherent(const uint16_t* src, int rows, int n, int nch, float* xf,
+                                                 float* sa) {
+  constexpr int kDeviceCoherent = 16;  // cache-policy bit sc1: device scope
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(src, (uint32_t)rows * (uint32_t)n * 2u);
+  const int per_row = nch * 4;  // pieces of 8 values
+  const int total = rows * per_row;
+  for (int p = threadIdx.x; p < total; p += blockDim.x) {  // quads are all in or all out
+    const int rr = p / per_row;
+    const int pp = p - rr * per_row;
+    const int k0 = 8 * pp;
+    const bool in = k0 < n;  // a piece is wholly inside its row or wholly past it
+    const auto u = __builtin_amdgcn_raw_buffer_load_b128(r, (rr * n + (in ? k0 : 0)) * 2, 0, kDeviceCoherent);
+    float v[8];
+    h8_to_f32(make_uint4(u[0], u[1], u[2], u[3]), v);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = in ? v[q] : 0.0f;
+    f32x4* d = (f32x4*)(xf + (int64_t)rr * nch * 32 + k0);
+    d[0] = f32x4{v[0], v[1], v[2], v[3]};
+    d[1] = f32x4{v[4], v[5], v[6], v[7]};
+    float s8 = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+    s8 += dpp_f<kDppXor1>(s8);
+    s8 += dpp_f<kDppXor2>(s8);
+    if ((pp & 3) == 0) sa[rr * nch + (pp >> 2)] = s8;
+  }
+  __syncthreads();
+}
+
 // ---- persistent forms (fp mode) ------------------------------------------------------
 //
 // One work-group per resident slot.  The activations of every token (fc1: x; fc2: the
@@ -601,12 +631,13 @@ __global__ __launch_bounds__(kMoeThreads) void qmoe_fc2_kernel(QmoeArgs a) {
 // weight stream sits in the loop.  Expert ids are read with scalar loads (one per
 // group or slot) and clamped into [0, E).
 
-template <int RI, int ZK>
-__global__ __launch_bounds__(kMoeStreamThreads) void qmoe_fc1_stream_kernel(QmoeArgs a) {
+// COH: h is written with device-coherent stores (read by other work-groups of the
+// same launch in the single-launch form).
+template <int RI, int ZK, bool COH>
+__device__ __forceinline__ void fc1_stream_body(const QmoeArgs& a, int bid, int nb, uint32_t* smem) {
   constexpr int NR = 2 * RI;
   constexpr int NW = kMoeStreamThreads / 64;
   constexpr int D = RI == 1 ? 4 : 3;  // a wave's few items all in flight
-  extern __shared__ uint32_t smem[];
   const int T = (int)a.T;
   const int k = a.k;
   const int I = (int)a.I;
@@ -625,9 +656,9 @@ __global__ __launch_bounds__(kMoeStreamThreads) void qmoe_fc1_stream_kernel(Qmoe
   const int rpg = SUBS * RI;              // rows i per group
   const int GI = (I + rpg - 1) / rpg;     // groups per slot
   const int ngroups = T * k * GI;
-  const int groups_lo = ngroups / (int)gridDim.x, extra = ngroups % (int)gridDim.x;
-  const int g_begin = (int)blockIdx.x * groups_lo + ((int)blockIdx.x < extra ? (int)blockIdx.x : extra);
-  const int g_end = g_begin + groups_lo + ((int)blockIdx.x < extra ? 1 : 0);
+  const int groups_lo = ngroups / nb, extra = ngroups % nb;
+  const int g_begin = bid * groups_lo + (bid < extra ? bid : extra);
+  const int g_end = g_begin + groups_lo + (bid < extra ? 1 : 0);
   if (g_begin >= g_end) return;
   const int wave_groups = g_end - g_begin > wave ? (g_end - g_begin - wave + NW - 1) / NW : 0;
   const int iters = (nch + LPR - 1) >> lpr_log2;
@@ -755,15 +786,27 @@ __global__ __launch_bounds__(kMoeStreamThreads) void qmoe_fc1_stream_kernel(Qmoe
       u += f16_to_f32(bb[i + a.I]);
     }
     const float hv = g / (1.0f + expf(-g)) * u;
-    a.h[(int64_t)sl * a.I + i] = f32_to_f16(hv);
+    if constexpr (COH)
+      __hip_atomic_store(a.h + (int64_t)sl * a.I + i, f32_to_f16(hv), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+      a.h[(int64_t)sl * a.I + i] = f32_to_f16(hv);
   }
 }
 
-template <int R, int ZK>
-__global__ __launch_bounds__(kMoeStreamThreads) void qmoe_fc2_stream_kernel(QmoeArgs a) {
+template <int RI, int ZK>
+__global__ __launch_bounds__(kMoeStreamThreads) void qmoe_fc1_stream_kernel(QmoeArgs a) {
+  extern __shared__ uint32_t smem[];
+  fc1_stream_body<RI, ZK, false>(a, (int)blockIdx.x, (int)gridDim.x, smem);
+}
+
+
+// FUSED: h was written earlier in the same launch by other work-groups: the first
+// weight loads are issued, then `wait()` (every work-group's h is complete), then h is
+// staged with device-coherent loads.
+template <int R, int ZK, bool FUSED, typename Wait>
+__device__ __forceinline__ void fc2_stream_body(const QmoeArgs& a, int bid, int nb, uint32_t* smem, Wait&& wait) {
   constexpr int NW = kMoeStreamThreads / 64;
   constexpr int D = kFc2Depth;
-  extern __shared__ uint32_t smem[];
   const int T = (int)a.T;
   const int k = a.k;
   const int H = (int)a.H;
@@ -782,9 +825,9 @@ __global__ __launch_bounds__(kMoeStreamThreads) void qmoe_fc2_stream_kernel(Qmoe
   const int rpg = SUBS * R;               // rows n per group
   const int GN = (H + rpg - 1) / rpg;     // groups per token
   const int ngroups = T * GN;
-  const int groups_lo = ngroups / (int)gridDim.x, extra = ngroups % (int)gridDim.x;
-  const int g_begin = (int)blockIdx.x * groups_lo + ((int)blockIdx.x < extra ? (int)blockIdx.x : extra);
-  const int g_end = g_begin + groups_lo + ((int)blockIdx.x < extra ? 1 : 0);
+  const int groups_lo = ngroups / nb, extra = ngroups % nb;
+  const int g_begin = bid * groups_lo + (bid < extra ? bid : extra);
+  const int g_end = g_begin + groups_lo + (bid < extra ? 1 : 0);
   if (g_begin >= g_end) return;
   // the work-group's units are (group, slot) pairs, unit u = (g_begin + u / k, u % k);
   // wave w takes units w, w + NW, ... (the slot sums are combined at the write-out)
@@ -894,10 +937,17 @@ __global__ __launch_bounds__(kMoeStreamThreads) void qmoe_fc2_stream_kernel(Qmoe
   // the activations are converted
   MoeItem<R> buf[D];
   set_unit(fu);
-  stage_f32_first(a.h, T * k, (int)a.I, nch, hf, sa, [&] {
+  if constexpr (FUSED) {
 #pragma unroll
     for (int i = 0; i < D - 1; ++i) fetch(buf[i]);
-  });
+    wait();
+    stage_h_coherent(a.h, T * k, (int)a.I, nch, hf, sa);
+  } else {
+    stage_f32_first(a.h, T * k, (int)a.I, nch, hf, sa, [&] {
+#pragma unroll
+      for (int i = 0; i < D - 1; ++i) fetch(buf[i]);
+    });
+  }
   const int total = wave_units * iters;
   for (int base = 0; base < total; base += D) {
 #pragma unroll
@@ -921,28 +971,27 @@ __global__ __launch_bounds__(kMoeStreamThreads) void qmoe_fc2_stream_kernel(Qmoe
   }
 }
 
+template <int R, int ZK>
+__global__ __launch_bounds__(kMoeStreamThreads) void qmoe_fc2_stream_kernel(QmoeArgs a) {
+  extern __shared__ uint32_t smem[];
+  fc2_stream_body<R, ZK, false>(a, (int)blockIdx.x, (int)gridDim.x, smem, [] {});
+}
+
+
 // ---- single-launch form (fp mode) ------------------------------------------------------
 //
-// fc1, SwiGLU, fc2 and the combine in one launch.  The work is cut into items: first the
-// fc1 items (slot s, a run of row groups of rows i), then the fc2 items (slot s, a tile of
-// rows n).  Work-groups take items in order from a counter in scratch, so an item is only
-// ever held by a work-group that is already running.  An fc1 item writes its h rows and
-// then counts itself done for its slot.  An fc2 item of slot s first issues its weight
-// loads (they do not depend on h), then waits until every fc1 item of slot s is done.
-// Every such wait is on items held by running work-groups that never wait themselves,
-// so it ends whatever number of work-groups is resident.  An fc2 item writes its fp32
-// slot sums z to scratch; the work-group that finishes the last of the k slots of a row
-// tile forms y = sum_j w_j * (z_j + b2) in slot order.  The per-row arithmetic and its
-// order are those of the two-kernel forms above, so every form gives the same bits.
-// The last work-group to leave returns the counters to zero for the next call.
-// h and the slot sums cross work-groups (and so the separate L2 caches of the XCDs)
-// only through device-coherent stores and loads (relaxed agent-scope atomics, which
-// write through and read past the non-coherent cache lines); a producer waits for its
-// stores to complete before it moves a counter, a consumer reads only after it has seen
-// the counter.  No whole-cache write-back or invalidation is needed.
+// fc1, SwiGLU, fc2 and the combine in one launch of the persistent forms above: one
+// grid of work-groups, all resident at once (the grid is the occupancy of this kernel
+// times the compute units).  Each work-group runs its even share of the fc1 row
+// groups, writes its h rows with device-coherent stores, waits for them to complete
+// and counts itself arrived.  It then issues the first weight loads of its fc2 share,
+// waits until every work-group has arrived, stages h with device-coherent loads and
+// runs its fc2 share (all k slots of its rows, combined in slot order).  The per-row
+// arithmetic is that of the two-kernel forms, so every form gives the same bits.  h
+// crosses the separate L2 caches of the XCDs only through device-coherent stores and
+// loads, so no whole-cache write-back or invalidation is needed.  The last work-group
+// to leave returns the counters to zero for the next call.
 
-constexpr int kFusedThreads = 256;
-constexpr int kFusedDepth = 4;
 // a wait gives up after 1 s of the 100 MHz real-time counter and raises the error word
 constexpr uint64_t kSpinLimitTicks = 100000000ull;
 
@@ -956,347 +1005,38 @@ __device__ __forceinline__ void sync_store(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// fp32 staging of one fp16 row of n values (n % 8 == 0) written by other work-groups
-// in the same launch: device-coherent 16-byte loads (zero past n), fp32 into xf[nch*32]
-// and the fixed-order sum of each 32-value chunk into sa[nch] (the sums of stage_f32).
-__device__ __forceinline__ void stage_h_coherent(const uint16_t* src, int n, int nch, float* xf, float* sa) {
-  constexpr int kDeviceCoherent = 16;  // cache-policy bit sc1: device scope
-  const __amdgpu_buffer_rsrc_t r = make_rsrc(src, (uint32_t)n * 2u);
-  const int total = nch * 4;  // pieces of 8 values
-  for (int p = threadIdx.x; p < total; p += blockDim.x) {  // quads are all in or all out
-    const auto u = __builtin_amdgcn_raw_buffer_load_b128(r, p * 16, 0, kDeviceCoherent);
-    float v[8];
-    h8_to_f32(make_uint4(u[0], u[1], u[2], u[3]), v);
-    f32x4* d = (f32x4*)(xf + 8 * p);
-    d[0] = f32x4{v[0], v[1], v[2], v[3]};
-    d[1] = f32x4{v[4], v[5], v[6], v[7]};
-    float s8 = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
-    s8 += dpp_f<kDppXor1>(s8);
-    s8 += dpp_f<kDppXor2>(s8);
-    if ((p & 3) == 0) sa[p >> 2] = s8;
-  }
-  __syncthreads();
-}
-
-template <int ZK1, int ZK2>
-__global__ __launch_bounds__(kFusedThreads) void qmoe_fused_kernel(QmoeArgs a) {
-  constexpr int NW = kFusedThreads / 64;
-  constexpr int D = kFusedDepth;
+template <int RI, int R, int ZK1, int ZK2>
+__global__ __launch_bounds__(kMoeStreamThreads) void qmoe_fused_kernel(QmoeArgs a) {
   extern __shared__ uint32_t smem[];
-  __shared__ int s_item;
-  __shared__ int s_last;
-  const int T = (int)a.T;
-  const int k = a.k;
-  const int I = (int)a.I;
-  const int H = (int)a.H;
-  const int S = T * k;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   uint32_t* sync = a.sync;
-  uint32_t* slot_done = sync + kSyncHead;
-  uint32_t* tile_done = slot_done + S;
-  const int blk_shift = __builtin_ctz((unsigned)a.block) - 5;
-
-  // fc1: LPR1 lanes per row, SUBS1 rows i (each a g row and a u row) per wave and group
-  const int nch1 = (int)a.fc1_chunks;
-  const int nblk1 = (int)a.fc1_nblk;
-  const int l1 = a.fc1_lpr_log2;
-  const int LPR1 = 1 << l1;
-  const int SUBS1 = 64 >> l1;
-  const int lp1 = lane & (LPR1 - 1);
-  const int sub1 = lane >> l1;
-  const int iters1 = (nch1 + LPR1 - 1) >> l1;
-  const int GI = (I + SUBS1 - 1) / SUBS1;
-  const int gpw1 = a.f_gpw1;
-  const int n1s = (int)a.f_n1s;
-  const uint32_t rb1 = (uint32_t)a.fc1_row_bytes;
-  const uint32_t zrb1 = (uint32_t)a.fc1_zp_row_bytes;
-  // fc2: LPR2 lanes per row, SUBS2 rows n per wave and group
-  const int nch2 = (int)a.fc2_chunks;
-  const int nblk2 = (int)a.fc2_nblk;
-  const int l2 = a.fc2_lpr_log2;
-  const int LPR2 = 1 << l2;
-  const int SUBS2 = 64 >> l2;
-  const int lp2 = lane & (LPR2 - 1);
-  const int sub2 = lane >> l2;
-  const int iters2 = (nch2 + LPR2 - 1) >> l2;
-  const int GN = (H + SUBS2 - 1) / SUBS2;
-  const int gpw2 = a.f_gpw2;
-  const int n2s = (int)a.f_n2s;
-  const uint32_t rb2 = (uint32_t)a.fc2_row_bytes;
-  const uint32_t zrb2 = (uint32_t)a.fc2_zp_row_bytes;
-
-  const int n1 = S * n1s;
-  const int ntot = n1 + S * n2s;
-  const int nchm = nch1 > nch2 ? nch1 : nch2;
-  float* xf = (float*)smem;   // staged activations [nchm * 32]
-  float* sa = xf + nchm * 32; // their chunk sums [nchm]
-  float* outs = sa + nchm;    // row sums of the current item
-  int staged = -1;            // what xf holds: token t (x_t) or T + slot s (h of slot s)
-
-  if (threadIdx.x == 0) s_item = (int)sync_add(&sync[0], 1u);
+  const int nb = (int)gridDim.x;
+  const int bid = (int)blockIdx.x;
+  fc1_stream_body<RI, ZK1, true>(a, bid, nb, smem);
+  // every wave's h stores have completed before the work-group counts itself arrived
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  int item = s_item;
-  while (item < ntot) {
-    uint32_t next = 0;
-    if (threadIdx.x == 0) next = sync_add(&sync[0], 1u);  // used at the end of this item
-    if (item < n1) {
-      // ---- fc1 item: rows i of slot s, then bias, SwiGLU and fp16 h ----
-      const int s = item / n1s;
-      const int q = item - s * n1s;
-      const int t = s / k;
-      const int e = clamp_expert(a.ids[s], a.E);
-      const uint32_t erows = 2u * (uint32_t)I;
-      const __amdgpu_buffer_rsrc_t rW = make_rsrc(a.fc1.W + (size_t)e * erows * rb1, erows * rb1);
-      const __amdgpu_buffer_rsrc_t rS =
-          make_rsrc((const uint16_t*)a.fc1.scales + (size_t)e * erows * nblk1, erows * (uint32_t)nblk1 * 2u);
-      __amdgpu_buffer_rsrc_t rZ = rW;
-      if constexpr (ZK1) rZ = make_rsrc(a.fc1.zp + (size_t)e * erows * zrb1, erows * zrb1);
-      const int gbase = q * NW * gpw1 + wave;  // the wave's groups: gbase + NW * u
-      const int ng = gbase < GI ? min(gpw1, (GI - gbase + NW - 1) / NW) : 0;
-      const int total = ng * iters1;
-      int fu = 0, fit = 0;
-      uint32_t frow[2];
-      auto set_rows = [&](int u) {
-        const int uu = u < ng ? u : (ng > 0 ? ng - 1 : 0);
-        const int i = (gbase + NW * uu) * SUBS1 + sub1;
-        const uint32_t ic = (uint32_t)(i < I ? i : I - 1);
-        frow[0] = ic;
-        frow[1] = ic + (uint32_t)I;
-      };
-      auto fetch = [&](MoeItem<2>& b) {
-        int c = fit * LPR1 + lp1;
-        c = c < nch1 ? c : nch1 - 1;
-        const int blk = c >> blk_shift;
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-          const auto v = __builtin_amdgcn_raw_buffer_load_b128(rW, (int)(frow[r] * rb1 + (uint32_t)c * 16u), 0, 0);
-          b.w[r] = make_uint4(v[0], v[1], v[2], v[3]);
-          b.s[r] = __builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(
-                                                     rS, (int)((frow[r] * (uint32_t)nblk1 + (uint32_t)blk) * 2u), 0, 0));
-          if constexpr (ZK1)
-            b.z[r] = __builtin_amdgcn_raw_buffer_load_b8(rZ, (int)(frow[r] * zrb1 + (uint32_t)(blk >> 1)), 0, 0);
-          else
-            b.z[r] = 0x88u;
+  if (threadIdx.x == 0) (void)sync_add(&sync[0], 1u);
+  auto wait = [&] {
+    if (threadIdx.x == 0) {
+      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+      int polls = 0;
+      while (sync_load(&sync[0]) < (uint32_t)nb) {
+        if (polls < 4) __builtin_amdgcn_s_sleep(4);
+        else if (polls < 16) __builtin_amdgcn_s_sleep(16);
+        else __builtin_amdgcn_s_sleep(48);
+        ++polls;
+        if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinLimitTicks) {
+          sync_store(&sync[2], 1u);
+          break;
         }
-        if (++fit == iters1) {
-          fit = 0;
-          set_rows(++fu);
-        }
-      };
-      float acc[2] = {0.0f, 0.0f};
-      int cu = 0, cit = 0;
-      auto step = [&](const MoeItem<2>& cb, MoeItem<2>& nxt, bool live) {
-        fetch(nxt);
-        const int c = cit * LPR1 + lp1;
-        const bool cv = live && c < nch1;
-        const int cc = c < nch1 ? c : nch1 - 1;
-        const int blk = cc >> blk_shift;
-        const float* xp = xf + cc * 32;
-        float xa[32];
-#pragma unroll
-        for (int qv = 0; qv < 8; ++qv) {
-          const f32x4 v = *(const f32x4*)(xp + 4 * qv);
-          xa[4 * qv] = v.x; xa[4 * qv + 1] = v.y; xa[4 * qv + 2] = v.z; xa[4 * qv + 3] = v.w;
-        }
-        const float sac = sa[cc];
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-          const float pr = dot_chunk_u4(cb.w[r], xa);
-          const float zp = (float)((cb.z[r] >> ((blk & 1) * 4)) & 0xfu);
-          const float nv = fmaf((float)cb.s[r], fmaf(-zp, sac, 512.0f * pr), acc[r]);
-          acc[r] = cv ? nv : acc[r];
-        }
-        if (live && cit == iters1 - 1) {
-          acc[0] = group_sum(acc[0], LPR1);
-          acc[1] = group_sum(acc[1], LPR1);
-          if (lp1 == 0) {
-            const int lr = (wave + NW * cu) * SUBS1 + sub1;
-            outs[2 * lr] = acc[0];
-            outs[2 * lr + 1] = acc[1];
-          }
-          acc[0] = acc[1] = 0.0f;
-        }
-        if (++cit == iters1) {
-          cit = 0;
-          ++cu;
-        }
-      };
-      MoeItem<2> buf[D];
-      set_rows(0);
-      if (staged != t) {
-        stage_f32_first(a.X + (size_t)t * H, 1, H, nch1, xf, sa, [&] {
-#pragma unroll
-          for (int i = 0; i < D - 1; ++i) fetch(buf[i]);
-        });
-        staged = t;
-      } else {
-#pragma unroll
-        for (int i = 0; i < D - 1; ++i) fetch(buf[i]);
-      }
-      for (int base = 0; base < total; base += D) {
-#pragma unroll
-        for (int i = 0; i < D; ++i) step(buf[i], buf[(i + D - 1) % D], base + i < total);
-      }
-      __syncthreads();
-      const int row0 = q * NW * gpw1 * SUBS1;
-      const int nloc = NW * gpw1 * SUBS1;
-      for (int lr = threadIdx.x; lr < nloc; lr += blockDim.x) {
-        const int i = row0 + lr;
-        if (i >= I) continue;
-        float g = outs[2 * lr], u = outs[2 * lr + 1];
-        if (a.fc1.bias) {
-          const uint16_t* bb = a.fc1.bias + (int64_t)e * 2 * a.I;
-          g += f16_to_f32(bb[i]);
-          u += f16_to_f32(bb[i + a.I]);
-        }
-        const float hv = g / (1.0f + expf(-g)) * u;
-        __hip_atomic_store(a.h + (int64_t)s * a.I + i, f32_to_f16(hv), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      // publish: every wave's h stores (device-coherent, written through) have
-      // completed before the slot's count moves
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      if (threadIdx.x == 0) (void)sync_add(&slot_done[s], 1u);
-    } else {
-      // ---- fc2 item: rows n of slot s, z to scratch, combine by the last slot ----
-      const int q2 = item - n1;
-      const int s = q2 / n2s;
-      const int tile = q2 - s * n2s;
-      const int t = s / k;
-      const int e = clamp_expert(a.ids[s], a.E);
-      const uint32_t erows = (uint32_t)H;
-      const __amdgpu_buffer_rsrc_t rW = make_rsrc(a.fc2.W + (size_t)e * erows * rb2, erows * rb2);
-      const __amdgpu_buffer_rsrc_t rS =
-          make_rsrc((const uint16_t*)a.fc2.scales + (size_t)e * erows * nblk2, erows * (uint32_t)nblk2 * 2u);
-      __amdgpu_buffer_rsrc_t rZ = rW;
-      if constexpr (ZK2) rZ = make_rsrc(a.fc2.zp + (size_t)e * erows * zrb2, erows * zrb2);
-      const int gbase = tile * NW * gpw2 + wave;
-      const int ng = gbase < GN ? min(gpw2, (GN - gbase + NW - 1) / NW) : 0;
-      const int total = ng * iters2;
-      int fu = 0, fit = 0;
-      uint32_t frow = 0;
-      auto set_rows = [&](int u) {
-        const int uu = u < ng ? u : (ng > 0 ? ng - 1 : 0);
-        const int n = (gbase + NW * uu) * SUBS2 + sub2;
-        frow = (uint32_t)(n < H ? n : H - 1);
-      };
-      auto fetch = [&](MoeItem<1>& b) {
-        int c = fit * LPR2 + lp2;
-        c = c < nch2 ? c : nch2 - 1;
-        const int blk = c >> blk_shift;
-        const auto v = __builtin_amdgcn_raw_buffer_load_b128(rW, (int)(frow * rb2 + (uint32_t)c * 16u), 0, 0);
-        b.w[0] = make_uint4(v[0], v[1], v[2], v[3]);
-        b.s[0] = __builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(
-                                                   rS, (int)((frow * (uint32_t)nblk2 + (uint32_t)blk) * 2u), 0, 0));
-        if constexpr (ZK2)
-          b.z[0] = __builtin_amdgcn_raw_buffer_load_b8(rZ, (int)(frow * zrb2 + (uint32_t)(blk >> 1)), 0, 0);
-        else
-          b.z[0] = 0x88u;
-        if (++fit == iters2) {
-          fit = 0;
-          set_rows(++fu);
-        }
-      };
-      float acc = 0.0f;
-      int cu = 0, cit = 0;
-      auto step = [&](const MoeItem<1>& cb, MoeItem<1>& nxt, bool live) {
-        fetch(nxt);
-        const int c = cit * LPR2 + lp2;
-        const bool cv = live && c < nch2;
-        const int cc = c < nch2 ? c : nch2 - 1;
-        const int blk = cc >> blk_shift;
-        const float* xp = xf + cc * 32;
-        float xa[32];
-#pragma unroll
-        for (int qv = 0; qv < 8; ++qv) {
-          const f32x4 v = *(const f32x4*)(xp + 4 * qv);
-          xa[4 * qv] = v.x; xa[4 * qv + 1] = v.y; xa[4 * qv + 2] = v.z; xa[4 * qv + 3] = v.w;
-        }
-        const float sac = sa[cc];
-        const float pr = dot_chunk_u4(cb.w[0], xa);
-        const float zp = (float)((cb.z[0] >> ((blk & 1) * 4)) & 0xfu);
-        const float nv = fmaf((float)cb.s[0], fmaf(-zp, sac, 512.0f * pr), acc);
-        acc = cv ? nv : acc;
-        if (live && cit == iters2 - 1) {
-          acc = group_sum(acc, LPR2);
-          if (lp2 == 0) outs[(wave + NW * cu) * SUBS2 + sub2] = acc;
-          acc = 0.0f;
-        }
-        if (++cit == iters2) {
-          cit = 0;
-          ++cu;
-        }
-      };
-      MoeItem<1> buf[D];
-      set_rows(0);
-#pragma unroll
-      for (int i = 0; i < D - 1; ++i) fetch(buf[i]);
-      if (staged != T + s) {
-        // h of slot s: wait until every fc1 item of the slot is done (the weight loads
-        // above travel meanwhile), then stage it
-        if (threadIdx.x == 0) {
-          const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-          int polls = 0;
-          while (sync_load(&slot_done[s]) < (uint32_t)n1s) {
-            if (polls < 4) __builtin_amdgcn_s_sleep(4);
-            else if (polls < 16) __builtin_amdgcn_s_sleep(16);
-            else __builtin_amdgcn_s_sleep(48);
-            ++polls;
-            if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinLimitTicks) {
-              sync_store(&sync[2], 1u);
-              break;
-            }
-          }
-        }
-        __syncthreads();
-        stage_h_coherent(a.h + (size_t)s * I, I, nch2, xf, sa);
-        staged = T + s;
-      }
-      for (int base = 0; base < total; base += D) {
-#pragma unroll
-        for (int i = 0; i < D; ++i) step(buf[i], buf[(i + D - 1) % D], base + i < total);
-      }
-      __syncthreads();
-      const int row0 = tile * NW * gpw2 * SUBS2;
-      const int nloc = NW * gpw2 * SUBS2;
-      for (int lr = threadIdx.x; lr < nloc; lr += blockDim.x) {
-        const int n = row0 + lr;
-        if (n < H) __hip_atomic_store(a.zpart + (size_t)s * H + n, outs[lr], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      if (threadIdx.x == 0) s_last = sync_add(&tile_done[t * n2s + tile], 1u) == (uint32_t)(k - 1);
-      __syncthreads();
-      if (s_last) {
-        for (int lr = threadIdx.x; lr < nloc; lr += blockDim.x) {
-          const int n = row0 + lr;
-          if (n >= H) continue;
-          float y = 0.0f;
-          for (int j = 0; j < k; ++j) {
-            const int ej = clamp_expert(a.ids[t * k + j], a.E);
-            const float z = __hip_atomic_load(a.zpart + (size_t)(t * k + j) * H + n, __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_AGENT) +
-                            (a.fc2.bias ? f16_to_f32(a.fc2.bias[(int64_t)ej * a.H + n]) : 0.0f);
-            y = fmaf(a.rw[t * k + j], z, y);
-          }
-          a.Y[(int64_t)t * a.H + n] = f32_to_f16(y);
-        }
-        if (threadIdx.x == 0) sync_store(&tile_done[t * n2s + tile], 0u);
       }
     }
     __syncthreads();
-    if (threadIdx.x == 0) s_item = (int)next;
-    __syncthreads();
-    item = s_item;
-  }
-  // the last work-group out returns the counters to zero (the error word stays)
-  if (threadIdx.x == 0) {
-    if (sync_add(&sync[1], 1u) == gridDim.x - 1) {
-      sync_store(&sync[0], 0u);
-      sync_store(&sync[1], 0u);
-      for (int s = 0; s < S; ++s) sync_store(&slot_done[s], 0u);
-    }
+  };
+  fc2_stream_body<R, ZK2, true>(a, bid, nb, smem, wait);
+  if (threadIdx.x == 0 && sync_add(&sync[1], 1u) == (uint32_t)nb - 1u) {
+    sync_store(&sync[0], 0u);
+    sync_store(&sync[1], 0u);
   }
 }
 
@@ -1396,62 +1136,67 @@ static bool launch_fc2_stream(const QmoeArgs& a, int cap, hipStream_t st) {
 }
 
 
-static size_t fused_lds_bytes(const QmoeArgs& a) {
-  constexpr int NW = kFusedThreads / 64;
-  const int64_t nchm = a.fc1_chunks > a.fc2_chunks ? a.fc1_chunks : a.fc2_chunks;
-  const int64_t o1 = 2LL * NW * a.f_gpw1 * (64 >> a.fc1_lpr_log2);
-  const int64_t o2 = (int64_t)NW * a.f_gpw2 * (64 >> a.fc2_lpr_log2);
-  return (size_t)(nchm * 33 + (o1 > o2 ? o1 : o2)) * sizeof(float);
-}
-
-bool qmoe_fused_plan(QmoeArgs& a, int candidate) {
-  constexpr int NW = kFusedThreads / 64;
-  if (a.mode != QMOE_FP || candidate < 0 || candidate >= kNumQmoeFused) return false;
-  const int gpw = kQmoeFusedGpw[candidate / 3];
-  a.f_wpc = kQmoeFusedWpc[candidate % 3];
+template <int RI, int R, int ZK1, int ZK2>
+static bool launch_fused(const QmoeArgs& a, hipStream_t st) {
+  auto kern = qmoe_fused_kernel<RI, R, ZK1, ZK2>;
   // one expert's weights, scales and zero points are addressed with 32-bit offsets
   const int64_t r1 = 2 * a.I, r2 = a.H;
   if (r1 * a.fc1_row_bytes >= (1LL << 31) || r1 * a.fc1_nblk * 2 >= (1LL << 31)) return false;
   if (r2 * a.fc2_row_bytes >= (1LL << 31) || r2 * a.fc2_nblk * 2 >= (1LL << 31)) return false;
-  const int64_t subs1 = 64 >> a.fc1_lpr_log2, subs2 = 64 >> a.fc2_lpr_log2;
-  const int64_t gi = (a.I + subs1 - 1) / subs1, gn = (a.H + subs2 - 1) / subs2;
-  a.f_gpw1 = gpw;
-  a.f_gpw2 = gpw;
-  a.f_n1s = (gi + NW * gpw - 1) / (NW * gpw);
-  a.f_n2s = (gn + NW * gpw - 1) / (NW * gpw);
-  const int64_t items = a.T * a.k * (a.f_n1s + a.f_n2s);
-  if (items >= (1LL << 30) || a.f_n2s > (a.H + 3) / 4) return false;
-  return fused_lds_bytes(a) <= 64 * 1024;
+  const int64_t rpg1 = (64 >> a.fc1_lpr_log2) * RI, rpg2 = (64 >> a.fc2_lpr_log2) * R;
+  const int64_t ng1 = a.T * a.k * ((a.I + rpg1 - 1) / rpg1), ng2 = a.T * ((a.H + rpg2 - 1) / rpg2);
+  const size_t fixed1 = (size_t)a.T * a.fc1_chunks * 33 * sizeof(float);
+  const size_t fixed2 = (size_t)a.T * a.k * a.fc2_chunks * 33 * sizeof(float);
+  const size_t pg1 = (size_t)rpg1 * 2 * sizeof(float), pg2 = (size_t)rpg2 * a.k * sizeof(float);
+  constexpr size_t kMaxLds = 150 * 1024;
+  auto lds_for = [&](int64_t grid) {
+    const size_t l1 = fixed1 + (size_t)((ng1 + grid - 1) / grid) * pg1;
+    const size_t l2 = fixed2 + (size_t)((ng2 + grid - 1) / grid) * pg2;
+    return l1 > l2 ? l1 : l2;
+  };
+  const int cus = a.num_cus > 0 ? a.num_cus : 256;
+  // every work-group of the grid must be resident at once: the grid never exceeds the
+  // occupancy of the kernel with the LDS it is launched with
+  int per_cu = a.f_wpc;
+  size_t lds = 0;
+  for (; per_cu >= 1; --per_cu) {
+    lds = lds_for((int64_t)cus * per_cu);
+    if (lds > kMaxLds) return false;
+    if (moe_resident_per_cu(kern, lds) >= per_cu) break;
+  }
+  if (per_cu < 1) return false;
+  allow_lds(kern, lds);
+  hipLaunchKernelGGL(kern, dim3((unsigned)(cus * per_cu)), dim3(kMoeStreamThreads), lds, st, a);
+  return true;
+}
+
+bool qmoe_fused_plan(QmoeArgs& a, int candidate) {
+  if (a.mode != QMOE_FP || candidate < 0 || candidate >= kNumQmoeFused) return false;
+  a.f_r2 = kQmoeFusedR2[candidate % 2];
+  a.f_wpc = kQmoeFusedWpc[candidate / 2];
+  // the same limits launch_fused applies, at one work-group per compute unit (the most
+  // LDS per work-group)
+  const int64_t r1 = 2 * a.I, r2 = a.H;
+  if (r1 * a.fc1_row_bytes >= (1LL << 31) || r1 * a.fc1_nblk * 2 >= (1LL << 31)) return false;
+  if (r2 * a.fc2_row_bytes >= (1LL << 31) || r2 * a.fc2_nblk * 2 >= (1LL << 31)) return false;
+  const int64_t rpg1 = (64 >> a.fc1_lpr_log2) * 2, rpg2 = (64 >> a.fc2_lpr_log2) * a.f_r2;
+  const int64_t grid = a.num_cus > 0 ? a.num_cus : 256;
+  const int64_t ng1 = a.T * a.k * ((a.I + rpg1 - 1) / rpg1), ng2 = a.T * ((a.H + rpg2 - 1) / rpg2);
+  const int64_t l1 = a.T * a.fc1_chunks * 33 * 4 + ((ng1 + grid - 1) / grid) * rpg1 * 2 * 4;
+  const int64_t l2 = a.T * a.k * a.fc2_chunks * 33 * 4 + ((ng2 + grid - 1) / grid) * rpg2 * a.k * 4;
+  return (l1 > l2 ? l1 : l2) <= 150 * 1024;
 }
 
 hipError_t launch_qmoe_fused(const QmoeArgs& a, hipStream_t st) {
-  const size_t lds = fused_lds_bytes(a);
-  const bool zk1 = a.fc1.zp != nullptr, zk2 = a.fc2.zp != nullptr;
-  auto kern = zk1 ? (zk2 ? qmoe_fused_kernel<1, 1> : qmoe_fused_kernel<1, 0>)
-                  : (zk2 ? qmoe_fused_kernel<0, 1> : qmoe_fused_kernel<0, 0>);
-  static std::mutex mu;
-  static std::map<std::pair<const void*, size_t>, int> cache;
-  int per_cu = 0;
-  {
-    std::lock_guard<std::mutex> lock(mu);
-    const auto key = std::make_pair((const void*)kern, lds);
-    auto it = cache.find(key);
-    if (it != cache.end()) {
-      per_cu = it->second;
-    } else {
-      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kFusedThreads, lds) != hipSuccess ||
-          per_cu < 1) {
-        (void)hipGetLastError();
-        per_cu = 1;
-      }
-      cache[key] = per_cu;
-    }
-  }
-  const int64_t items = a.T * a.k * (a.f_n1s + a.f_n2s);
-  int64_t grid = (int64_t)(a.num_cus > 0 ? a.num_cus : 256) * (a.f_wpc < per_cu ? a.f_wpc : per_cu);
-  if (grid > items) grid = items;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kFusedThreads), lds, st, a);
-  return hipSuccess;
+  const bool z1 = a.fc1.zp != nullptr, z2 = a.fc2.zp != nullptr;
+  bool done;
+  if (a.f_r2 == 1)
+    done = z1 ? (z2 ? launch_fused<2, 1, 1, 1>(a, st) : launch_fused<2, 1, 1, 0>(a, st))
+              : (z2 ? launch_fused<2, 1, 0, 1>(a, st) : launch_fused<2, 1, 0, 0>(a, st));
+  else
+    done = z1 ? (z2 ? launch_fused<2, 2, 1, 1>(a, st) : launch_fused<2, 2, 1, 0>(a, st))
+              : (z2 ? launch_fused<2, 2, 0, 1>(a, st) : launch_fused<2, 2, 0, 0>(a, st));
+  return done ? hipSuccess : hipErrorNotSupported;
 }
 
 hipError_t launch_qmoe_fc1(const QmoeArgs& a, int candidate, hipStream_t st) {

@@ -192,23 +192,25 @@ qmm_status qmm_dequantize_codebook4(const uint8_t* W, int block, const float* ab
  *              H % 32 == 0 and I % 32 == 0).
  *   scratch    device buffer of at least qmoe_decode_scratch_bytes(T, H, I, k, mode),
  *              256-byte aligned.  Layout: fp16 h [T][k][I] at offset 0, then (each
- *              region at the next 256-byte boundary) in fp mode fp32 slot sums
- *              z [T][k][H] and the uint32 sync words of the single-launch form
- *              (4 + T*k + T*ceil(H/4) words); in int8 mode int8 x codes [T][H], fp32
- *              x scales [T][H/32], int8 h codes [T][k][I], fp32 h scales [T][k][I/32].
- *              The sync words must be zero before the first call on a buffer (zero
- *              the whole buffer once, e.g. hipMemset); every call leaves the first
- *              two and the counters zero again.  The third word is an error flag
- *              that a call sets, and leaves set, if a wait inside the launch gave up
- *              after 1 s (a broken sync region); the output of that call is invalid.
- *              Calls that share a scratch buffer must not overlap.
- *   Launches   fp mode runs fc1, SwiGLU, fc2 and the combine in ONE launch: work
- *              items (fc1 row runs, then fc2 row tiles) are taken in order from a
- *              counter, an fc2 item waits only for the fc1 items of its own slot,
- *              and the last of the k slot items of a row tile combines the slot sums
- *              in slot order.  Items are only held by running work-groups, so no
- *              wait depends on co-residency.  int8 mode runs fc1, the h quantizer
- *              and fc2 as three launches.  Every form gives the same bits.
+ *              region at the next 256-byte boundary) in fp mode four uint32 sync
+ *              words of the single-launch form; in int8 mode int8 x codes [T][H],
+ *              fp32 x scales [T][H/32], int8 h codes [T][k][I], fp32 h scales
+ *              [T][k][I/32].  The sync words must be zero before the first call on a
+ *              buffer (zero the whole buffer once, e.g. hipMemset); every call leaves
+ *              the first two zero again.  The third is an error flag that a call
+ *              sets, and leaves set, if its wait inside the launch gave up after 1 s
+ *              (its output is then invalid).  Calls that share a scratch buffer must
+ *              not overlap.
+ *   Launches   fp mode: two kernels (fc1 + SwiGLU, then fc2 + combine), or one launch
+ *              of both: a grid that is resident all at once (its size is the
+ *              kernel's occupancy times the compute units) runs its fc1 share,
+ *              publishes h, issues its first fc2 weight loads, waits for every
+ *              work-group's h and runs its fc2 share.  The up-front timing picks the
+ *              faster form per shape.  The one-launch form needs the compute units
+ *              to itself for that wait: a kernel on another stream that holds them
+ *              for more than 1 s makes the wait give up (error flag above).  int8
+ *              mode: fc1, the h quantizer and fc2 as three launches.  Every form
+ *              gives the same bits.
  *   E          num_experts: the first call of a shape times tiling candidates on
  *              other expert sets, writing only scratch.
  * ------------------------------------------------------------------------- */

@@ -178,9 +178,8 @@ def test_scratch_queries():
     fp = L.qmoe_decode_scratch_bytes(1, 2880, 2880, 4, Q.QMOE_FP)
     i8 = L.qmoe_decode_scratch_bytes(1, 2880, 2880, 4, Q.QMOE_INT8_ACT)
     a256 = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    # fp: h fp16 [T][k][I], slot sums fp32 [T][k][H], sync words 4 + T*k + T*ceil(H/4)
-    assert fp == a256(4 * 2880 * 2) + a256(4 * 2880 * 4) + a256(4 * (4 + 4 + 720))
+    # fp: h fp16 [T][k][I], then the four sync words of the single-launch form
+    assert fp == a256(4 * 2880 * 2) + a256(16)
     # int8: h, then x codes, x scales, h codes, h scales
     assert i8 == a256(4 * 2880 * 2) + a256(2880) + a256(90 * 4) + a256(4 * 2880) + a256(4 * 90 * 4)
-    assert L.qmoe_decode_scratch_bytes(8, 2048, 768, 8, Q.QMOE_FP) == (
-        a256(64 * 768 * 2) + a256(64 * 2048 * 4) + a256(4 * (4 + 64 + 8 * 512)))
+    assert L.qmoe_decode_scratch_bytes(8, 2048, 768, 8, Q.QMOE_FP) == a256(64 * 768 * 2) + a256(16)
