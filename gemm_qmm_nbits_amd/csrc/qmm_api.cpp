@@ -767,7 +767,9 @@ qmm_status qmm_nbits(const void* A, int a_type, int64_t M, int64_t K, int64_t N,
     p.bias = bias;
     p.C = C;
     p.c_type = c_type;
-    hipError_t e = launch_prefill(p, st);
+    // a few rows: the skinny kernel (16-row tiles, each weight dequantized once)
+    hipError_t e = skinny_applies(M, N, Kp, block, p.row_bytes, p.nblk) ? launch_skinny(p, st)
+                                                                        : launch_prefill(p, st);
     if (e != hipSuccess) return (qmm_status)e;
     return (qmm_status)hipGetLastError();
   }
@@ -819,7 +821,9 @@ qmm_status qmm_codebook4(const void* A, int a_type, int64_t M, int64_t K, int64_
     p.bias = bias;
     p.C = C;
     p.c_type = c_type;
-    hipError_t e = launch_prefill(p, st);
+    // a few rows: the skinny kernel (16-row tiles, each weight dequantized once)
+    hipError_t e = skinny_applies(M, N, Kp, block, p.row_bytes, p.nblk) ? launch_skinny(p, st)
+                                                                        : launch_prefill(p, st);
     if (e != hipSuccess) return (qmm_status)e;
     return (qmm_status)hipGetLastError();
   }

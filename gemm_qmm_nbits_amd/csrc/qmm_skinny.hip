@@ -1,0 +1,275 @@
+// Skinny matrix-core path of MatMulNBits and the 16-entry codebook for 8 < M <= 64
+// (activations of a few tokens: [P1] hip-ep PR 1318 "What", the prefill tiles on the
+// matrix cores with A cast to fp16 once; [P3] bitsandbytes PR 1979 "Technical
+// details", the codebook decoded inside the matrix product).
+//
+// C[M][N] = A16 . W16^T (+ bias) with the operand roundings of the prefill path:
+// A16 = fp16(A) (cast once into the caller's workspace, rows zero-padded to Kp, a
+// multiple of 64) and W16 = fp16 of the exact fp32 dequantized weight
+// (fp32(fp32(q - zp) * s) or fp32(codebook[q] * absmax)).  Unlike the 256 x 256 prefill
+// tiles, no matrix-core work is spent on padding rows beyond ceil(M / 16) * 16, and every
+// weight is loaded and dequantized once.
+//
+// Work-group: 8 waves and two 16-row strips of W (32 output columns).  The reduction
+// runs in steps of 128 codes; wave w takes steps w, w + 8, ...  In a step, lane l
+// (n = l % 16, q = l / 16) loads codes [32q, 32q + 32) of W row n of each strip (16 bytes
+// of u4, 8 of u2, inside one block since blocks are >= 32 codes), dequantizes them into
+// four groups of 8 fp16, and reads the matching 8 fp16 of A for each 16-row M tile
+// straight from the workspace (L2-resident).  v_mfma_f32_16x16x32_f16 then contracts the
+// 8-value groups: lane l supplies A row l % 16 and W row l % 16 over the same 8 k, so
+// the pairing is exact whatever order the instruction takes its k in; accumulator v of
+// lane l is row 4 * (l / 16) + v, column l % 16.  The eight waves' fp32 sums are added
+// in wave order through LDS, so the result depends only on the shape.
+#include "qmm_device.h"
+#include "qmm_internal.h"
+
+namespace qmm {
+
+namespace {
+
+constexpr int SK_WAVES = 8;
+constexpr int SK_THREADS = SK_WAVES * 64;
+constexpr int SK_NS = 2;       // 16-row strips of W per work-group
+constexpr int SK_STEP = 128;   // codes per reduction step
+constexpr uint32_t kSkWord3 = 0x00020000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t sk_rsrc(const void* p, int64_t bytes) {
+  const uint32_t n = bytes >= 0x7fffffff ? 0x7fffffffu : (uint32_t)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)n, (int)kSkWord3);
+}
+
+template <int CT>
+__device__ __forceinline__ void sk_store(void* C, int64_t i, float v) {
+  if constexpr (CT == QMM_F32) ((float*)C)[i] = v;
+  else if constexpr (CT == QMM_F16) ((uint16_t*)C)[i] = f32_to_f16(v);
+  else ((uint16_t*)C)[i] = f32_to_bf16(v);
+}
+
+template <int CT>
+__device__ __forceinline__ float sk_bias(const void* b, int64_t i) {
+  if constexpr (CT == QMM_F32) return ((const float*)b)[i];
+  else if constexpr (CT == QMM_F16) return f16_to_f32(((const uint16_t*)b)[i]);
+  else return bf16_to_f32(((const uint16_t*)b)[i]);
+}
+
+// 8 codes -> 8 fp16 weights (codes in order), exact fp32 dequant rounded to nearest
+// fp16.  BITS = 4: `xw` holds the 8 codes as nibbles; BITS = 2: in its low 16 bits.
+template <int FMT, int BITS>
+__device__ __forceinline__ f16x8 dequant8(uint32_t xw, float sc, float z, float am, const float* cb) {
+  uint32_t o[4];
+  if constexpr (FMT == GEMV_CODEBOOK) {
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      f32x2 w;
+      w.x = __fmul_rn(cb[(xw >> (8 * jj)) & 15u], am);
+      w.y = __fmul_rn(cb[(xw >> (8 * jj + 4)) & 15u], am);
+      o[jj] = __builtin_bit_cast(uint32_t, __builtin_convertvector(w, f16x2));
+    }
+  } else {
+    // codes as exact fp32 integers, two per conversion: 2-bit codes masked into e2m1
+    // nibbles are q/2 (scaled by 2), 4-bit codes masked into e4m3 bytes are q * 2^-9
+    // (scaled by 2^9)
+    float qv[8];
+    if constexpr (BITS == 2) {
+      const uint32_t ev = xw & 0x3333u, od = (xw >> 2) & 0x3333u;
+      const f32x2 e0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(ev, 2.0f, 0);
+      const f32x2 o0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(od, 2.0f, 0);
+      const f32x2 e1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(ev, 2.0f, 1);
+      const f32x2 o1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(od, 2.0f, 1);
+      qv[0] = e0.x; qv[2] = e0.y; qv[1] = o0.x; qv[3] = o0.y;
+      qv[4] = e1.x; qv[6] = e1.y; qv[5] = o1.x; qv[7] = o1.y;
+    } else {
+      const uint32_t lo = xw & 0x0F0F0F0Fu, hi = (xw >> 4) & 0x0F0F0F0Fu;
+      const f32x2 l0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(lo, 512.0f, false);
+      const f32x2 h0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hi, 512.0f, false);
+      const f32x2 l1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(lo, 512.0f, true);
+      const f32x2 h1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hi, 512.0f, true);
+      qv[0] = l0.x; qv[2] = l0.y; qv[4] = l1.x; qv[6] = l1.y;
+      qv[1] = h0.x; qv[3] = h0.y; qv[5] = h1.x; qv[7] = h1.y;
+    }
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      f32x2 w;
+      w.x = __fmul_rn(__fsub_rn(qv[2 * jj], z), sc);
+      w.y = __fmul_rn(__fsub_rn(qv[2 * jj + 1], z), sc);
+      o[jj] = __builtin_bit_cast(uint32_t, __builtin_convertvector(w, f16x2));  // nearest even
+    }
+  }
+  return __builtin_bit_cast(f16x8, make_uint4(o[0], o[1], o[2], o[3]));
+}
+
+// FMT: GEMV_AFFINE (w = (q - zp) * s) or GEMV_CODEBOOK (BITS = 4); MB: 16-row M tiles.
+template <int FMT, int BITS, int ZK, int CT, int MB>
+__global__ __launch_bounds__(SK_THREADS) void skinny_kernel(PrefillArgs p) {
+  __shared__ float cb[16];
+  extern __shared__ float red[];  // [SK_WAVES][MB * SK_NS * 4][64]
+  if constexpr (FMT == GEMV_CODEBOOK) {
+    if (threadIdx.x < 16) cb[threadIdx.x] = p.codebook[threadIdx.x];
+    __syncthreads();
+  }
+  const int wave = (int)(threadIdx.x >> 6);
+  const int lane = (int)(threadIdx.x & 63);
+  const int ln = lane & 15, lq = lane >> 4;
+  const int M = (int)p.M, N = (int)p.N, Kp = (int)p.Kp;
+  const int nsteps = (Kp + SK_STEP - 1) / SK_STEP;
+  const int nblk = (int)p.nblk, blog = p.block_log2;
+  const int n0 = (int)blockIdx.x * (SK_NS * 16);
+
+  const __amdgpu_buffer_rsrc_t rW = sk_rsrc(p.W, p.N * p.row_bytes);
+  const __amdgpu_buffer_rsrc_t rS = FMT == GEMV_CODEBOOK ? sk_rsrc(p.absmax, p.N * p.nblk * 4)
+                                                          : sk_rsrc(p.scales, p.N * p.nblk * 2);
+  __amdgpu_buffer_rsrc_t rZ = rS;
+  if constexpr (ZK == 1) rZ = sk_rsrc(p.zp, p.N * p.zp_row_bytes);
+  if constexpr (ZK == 2) rZ = sk_rsrc(p.zp, p.N * p.nblk * 2);
+  // A rows past M lie past the workspace rows and read as zero
+  const __amdgpu_buffer_rsrc_t rA = sk_rsrc(p.A16, (int64_t)p.M * p.Kp * 2);
+
+  // W rows of this lane (clamped: rows past N are computed and dropped)
+  uint32_t wrow[SK_NS];
+#pragma unroll
+  for (int s = 0; s < SK_NS; ++s) {
+    const int n = n0 + s * 16 + ln;
+    wrow[s] = (uint32_t)(n < N ? n : N - 1);
+  }
+
+  f32x4 acc[MB][SK_NS];
+#pragma unroll
+  for (int mt = 0; mt < MB; ++mt)
+#pragma unroll
+    for (int s = 0; s < SK_NS; ++s) acc[mt][s] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  for (int c = wave; c < nsteps; c += SK_WAVES) {
+    const int k0 = c * SK_STEP + lq * 32;  // this lane's 32 codes
+    const bool kin = k0 < Kp;             // Kp % 64 == 0: wholly inside or wholly past
+    // weights: 32 codes, scale (or absmax) and zero point of their block, per strip
+    uint32_t wv[SK_NS][BITS];
+    float sc[SK_NS], z[SK_NS], am[SK_NS];
+    int blk = k0 >> blog;
+    blk = blk < nblk - 1 ? blk : nblk - 1;  // codes past the row end meet zero A
+#pragma unroll
+    for (int s = 0; s < SK_NS; ++s) {
+      const uint32_t wo = wrow[s] * (uint32_t)p.row_bytes + (uint32_t)(k0 * BITS / 8);
+      if constexpr (BITS == 4) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(rW, (int)wo, 0, 0);
+        wv[s][0] = v[0]; wv[s][1] = v[1]; wv[s][2] = v[2]; wv[s][3] = v[3];
+      } else {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(rW, (int)wo, 0, 0);
+        wv[s][0] = v[0]; wv[s][1] = v[1];
+      }
+      const uint32_t sb = wrow[s] * (uint32_t)nblk + (uint32_t)blk;
+      sc[s] = 0.0f; z[s] = 0.0f; am[s] = 0.0f;
+      if constexpr (FMT == GEMV_CODEBOOK) {
+        am[s] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rS, (int)(4u * sb), 0, 0));
+      } else {
+        sc[s] = (float)__builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(rS, (int)(2u * sb), 0, 0));
+        if constexpr (ZK == 1) {
+          const int bit = blk * BITS;
+          const uint32_t zb = __builtin_amdgcn_raw_buffer_load_b8(
+              rZ, (int)(wrow[s] * (uint32_t)p.zp_row_bytes + (uint32_t)(bit >> 3)), 0, 0);
+          z[s] = (float)((zb >> (bit & 7)) & ((1u << BITS) - 1u));
+        } else if constexpr (ZK == 2) {
+          z[s] = (float)__builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(rZ, (int)(2u * sb), 0, 0));
+        } else {
+          z[s] = p.zconst;
+        }
+      }
+    }
+    // activations: 32 fp16 of row 16 mt + ln per M tile (zero past Kp and past M)
+    f16x8 af[MB][4];
+#pragma unroll
+    for (int mt = 0; mt < MB; ++mt) {
+      const uint32_t ao = ((uint32_t)(mt * 16 + ln) * (uint32_t)Kp + (uint32_t)(kin ? k0 : 0)) * 2u;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(rA, (int)(ao + 16u * j), 0, 0);
+        const uint4 u = kin ? make_uint4(v[0], v[1], v[2], v[3]) : make_uint4(0u, 0u, 0u, 0u);
+        af[mt][j] = __builtin_bit_cast(f16x8, u);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int s = 0; s < SK_NS; ++s) {
+        const uint32_t xw = BITS == 4 ? wv[s][j] : (wv[s][j >> 1] >> (16 * (j & 1)));
+        const f16x8 bf = dequant8<FMT, BITS>(xw, sc[s], z[s], am[s], cb);
+#pragma unroll
+        for (int mt = 0; mt < MB; ++mt)
+          acc[mt][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[mt][j], bf, acc[mt][s], 0, 0, 0);
+      }
+    }
+  }
+
+  // the eight waves' sums, added in wave order
+  constexpr int R = MB * SK_NS * 4;
+#pragma unroll
+  for (int mt = 0; mt < MB; ++mt)
+#pragma unroll
+    for (int s = 0; s < SK_NS; ++s)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) red[((wave * R) + (mt * SK_NS + s) * 4 + v) * 64 + lane] = acc[mt][s][v];
+  __syncthreads();
+  for (int e = (int)threadIdx.x; e < R * 64; e += SK_THREADS) {
+    const int r = e >> 6, l = e & 63;
+    const int mt = r / (SK_NS * 4), s = (r >> 2) % SK_NS, v = r & 3;
+    const int m = mt * 16 + 4 * (l >> 4) + v;
+    const int n = n0 + s * 16 + (l & 15);
+    if (m >= M || n >= N) continue;
+    float y = red[r * 64 + l];
+#pragma unroll
+    for (int w = 1; w < SK_WAVES; ++w) y += red[(w * R + r) * 64 + l];
+    if (p.bias) y += sk_bias<CT>(p.bias, n);
+    sk_store<CT>(p.C, (int64_t)m * p.ldc + n, y);
+  }
+}
+
+template <int FMT, int BITS, int ZK, int CT, int MB>
+void sk_launch(const PrefillArgs& p, hipStream_t st) {
+  auto kern = skinny_kernel<FMT, BITS, ZK, CT, MB>;
+  const size_t lds = (size_t)SK_WAVES * MB * SK_NS * 4 * 64 * sizeof(float);
+  if (lds > 64 * 1024) (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  const unsigned grid = (unsigned)((p.N + SK_NS * 16 - 1) / (SK_NS * 16));
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(SK_THREADS), lds, st, p);
+}
+
+template <int FMT, int BITS, int ZK, int CT>
+void sk_mb(const PrefillArgs& p, hipStream_t st) {
+  if (p.M <= 16) sk_launch<FMT, BITS, ZK, CT, 1>(p, st);
+  else if (p.M <= 32) sk_launch<FMT, BITS, ZK, CT, 2>(p, st);
+  else sk_launch<FMT, BITS, ZK, CT, 4>(p, st);
+}
+
+template <int FMT, int BITS, int ZK>
+void sk_ct(const PrefillArgs& p, hipStream_t st) {
+  if (p.c_type == QMM_F32) sk_mb<FMT, BITS, ZK, QMM_F32>(p, st);
+  else if (p.c_type == QMM_F16) sk_mb<FMT, BITS, ZK, QMM_F16>(p, st);
+  else sk_mb<FMT, BITS, ZK, QMM_BF16>(p, st);
+}
+
+}  // namespace
+
+bool skinny_applies(int64_t M, int64_t N, int64_t Kp, int block, int64_t row_bytes, int64_t nblk) {
+  // 32-bit buffer offsets for W, scales and the workspace rows
+  if (M > kSkinnyMaxM || block < 32) return false;
+  // (activation offsets are formed for all 16 * ceil(M / 16) <= 64 tile rows)
+  if (N * row_bytes >= (1LL << 31) || N * nblk * 4 >= (1LL << 31) || 64 * (Kp + 128) * 2 >= (1LL << 31))
+    return false;
+  return true;
+}
+
+hipError_t launch_skinny(const PrefillArgs& p, hipStream_t st) {
+  const int zk = p.zp_kind == QMM_ZP_PACKED ? 1 : p.zp_kind == QMM_ZP_F16 ? 2 : 0;
+  if (p.fmt == GEMV_CODEBOOK) {
+    sk_ct<GEMV_CODEBOOK, 4, 0>(p, st);
+  } else if (p.bits == 2) {
+    if (zk == 1) sk_ct<GEMV_AFFINE, 2, 1>(p, st);
+    else if (zk == 2) sk_ct<GEMV_AFFINE, 2, 2>(p, st);
+    else sk_ct<GEMV_AFFINE, 2, 0>(p, st);
+  } else {
+    if (zk == 1) sk_ct<GEMV_AFFINE, 4, 1>(p, st);
+    else if (zk == 2) sk_ct<GEMV_AFFINE, 4, 2>(p, st);
+    else sk_ct<GEMV_AFFINE, 4, 0>(p, st);
+  }
+  return hipSuccess;
+}
+
+}  // namespace qmm

@@ -246,6 +246,12 @@ def test_phi4_u2_prefill_full_size(name):
     (257, 1000, 64, 4, 32, "none", "bf16", "bf16"),
     (64, 70, 33, 2, 16, "f16", "f32", "f16"),
     (513, 4096, 300, 4, 256, "f16", "bf16", "f32"),
+    # 8 < M <= 64 with blocks >= 32: the skinny kernel (16-row M tiles)
+    (17, 320, 100, 2, 32, "packed", "f32", "f32"),          # last 128-code step half past Kp
+    (64, 1000, 70, 4, 64, "f16", "bf16", "bf16"),           # four M tiles, ragged K and N
+    (48, 4096, 4096, 4, 128, "none", "f16", "f32"),
+    (40, 5120, 7680, 2, 64, "f16_uniform", "f32", "f32"),   # phi4 qkv shape, a few tokens
+    (25, 2880, 33, 4, 32, "packed8", "f32", "f16"),
 ])
 def test_prefill_small_shapes(M, K, N, bits, block, zp, a, c):
     say(f"prefill M={M} K={K} N={N} bits={bits} block={block} zp={zp} a={a} c={c}")
@@ -279,6 +285,18 @@ def test_prefill_repeat_bit_identical():
     out = torch().empty_like(d.run(uniform=True))
     for i in range(16):
         d.run(uniform=True, out=out)
+        assert np.array_equal(host_bits(out), first), i
+
+
+def test_skinny_repeat_bit_identical():
+    """The skinny matrix-core path (8 < M <= 64) gives identical bits over repeated calls."""
+    p = gen.nbits_problem(64, 4096, 1024, 4, 64, seed=80, zp="packed")
+    d = NbitsDev(p)
+    first = host_bits(d.run()).copy()
+    _check_prefill(d, d.run(), label="M=64 skinny")
+    out = torch().empty_like(d.run())
+    for i in range(16):
+        d.run(out=out)
         assert np.array_equal(host_bits(out), first), i
 
 
