@@ -24,6 +24,7 @@
 
 #include "qmm.h"
 #include "qmm_internal.h"
+#include "qmm_skinny.h"
 #include "qmm_qmoe.h"
 
 using namespace qmm;

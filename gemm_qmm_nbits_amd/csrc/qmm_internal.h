@@ -106,11 +106,4 @@ struct PrefillArgs {
 hipError_t launch_prefill(PrefillArgs p, hipStream_t st);
 int prefill_splits(int64_t M, int64_t N, int64_t Kp);
 
-// Skinny matrix-core path for kMaxGemvM < M <= kSkinnyMaxM (blocks >= 32 codes): the
-// same operands as the prefill path (A16 in the workspace, W16 = fp16 of the exact
-// dequant), 16-row M tiles, one load and dequantization per weight.
-constexpr int64_t kSkinnyMaxM = 64;
-bool skinny_applies(int64_t M, int64_t N, int64_t Kp, int block, int64_t row_bytes, int64_t nblk);
-hipError_t launch_skinny(const PrefillArgs& p, hipStream_t st);
-
 }  // namespace qmm

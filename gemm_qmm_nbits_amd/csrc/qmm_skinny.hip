@@ -10,7 +10,7 @@
 // tiles, no matrix-core work is spent on padding rows beyond ceil(M / 16) * 16, and every
 // weight is loaded and dequantized once.
 //
-// Work-group: 8 waves and two 16-row strips of W (32 output columns).  The reduction
+// Work-group: 8 waves and one or two 16-row strips of W (16 or 32 output columns).  The reduction
 // runs in steps of 128 codes; wave w takes steps w, w + 8, ...  In a step, lane l
 // (n = l % 16, q = l / 16) loads codes [32q, 32q + 32) of W row n of each strip (16 bytes
 // of u4, 8 of u2, inside one block since blocks are >= 32 codes), dequantizes them into
@@ -22,6 +22,7 @@
 // in wave order through LDS, so the result depends only on the shape.
 #include "qmm_device.h"
 #include "qmm_internal.h"
+#include "qmm_skinny.h"
 
 namespace qmm {
 
@@ -29,7 +30,10 @@ namespace {
 
 constexpr int SK_WAVES = 8;
 constexpr int SK_THREADS = SK_WAVES * 64;
-constexpr int SK_NS = 2;       // 16-row strips of W per work-group
+// NS: 16-row strips of W per work-group.  Two let each activation fragment feed two
+// strips; one doubles the work-groups of a narrow output (used when N / 16 work-groups
+// fit on the compute units in one round, and only for a single M tile).  The strip
+// count never changes any output's summation order.
 constexpr int SK_STEP = 128;   // codes per reduction step
 constexpr uint32_t kSkWord3 = 0x00020000u;
 
@@ -99,7 +103,7 @@ __device__ __forceinline__ f16x8 dequant8(uint32_t xw, float sc, float z, float 
 }
 
 // FMT: GEMV_AFFINE (w = (q - zp) * s) or GEMV_CODEBOOK (BITS = 4); MB: 16-row M tiles.
-template <int FMT, int BITS, int ZK, int CT, int MB>
+template <int FMT, int BITS, int ZK, int CT, int MB, int SK_NS>
 __global__ __launch_bounds__(SK_THREADS) void skinny_kernel(PrefillArgs p) {
   __shared__ float cb[16];
   extern __shared__ float red[];  // [SK_WAVES][MB * SK_NS * 4][64]
@@ -222,9 +226,9 @@ __global__ __launch_bounds__(SK_THREADS) void skinny_kernel(PrefillArgs p) {
   }
 }
 
-template <int FMT, int BITS, int ZK, int CT, int MB>
+template <int FMT, int BITS, int ZK, int CT, int MB, int SK_NS>
 void sk_launch(const PrefillArgs& p, hipStream_t st) {
-  auto kern = skinny_kernel<FMT, BITS, ZK, CT, MB>;
+  auto kern = skinny_kernel<FMT, BITS, ZK, CT, MB, SK_NS>;
   const size_t lds = (size_t)SK_WAVES * MB * SK_NS * 4 * 64 * sizeof(float);
   if (lds > 64 * 1024) (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   const unsigned grid = (unsigned)((p.N + SK_NS * 16 - 1) / (SK_NS * 16));
@@ -233,9 +237,20 @@ void sk_launch(const PrefillArgs& p, hipStream_t st) {
 
 template <int FMT, int BITS, int ZK, int CT>
 void sk_mb(const PrefillArgs& p, hipStream_t st) {
-  if (p.M <= 16) sk_launch<FMT, BITS, ZK, CT, 1>(p, st);
-  else if (p.M <= 32) sk_launch<FMT, BITS, ZK, CT, 2>(p, st);
-  else sk_launch<FMT, BITS, ZK, CT, 4>(p, st);
+  int cus = 0, dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) {
+    (void)hipGetLastError();
+    cus = 256;
+  }
+  if (p.M <= 16) {
+    if ((p.N + 15) / 16 <= cus) sk_launch<FMT, BITS, ZK, CT, 1, 1>(p, st);
+    else sk_launch<FMT, BITS, ZK, CT, 1, 2>(p, st);
+  } else if (p.M <= 32) {
+    sk_launch<FMT, BITS, ZK, CT, 2, 2>(p, st);
+  } else {
+    sk_launch<FMT, BITS, ZK, CT, 4, 2>(p, st);
+  }
 }
 
 template <int FMT, int BITS, int ZK>
@@ -249,7 +264,7 @@ void sk_ct(const PrefillArgs& p, hipStream_t st) {
 
 bool skinny_applies(int64_t M, int64_t N, int64_t Kp, int block, int64_t row_bytes, int64_t nblk) {
   // 32-bit buffer offsets for W, scales and the workspace rows
-  if (M > kSkinnyMaxM || block < 32) return false;
+  if (M > kSkinnyMaxM || block < 32 || Kp <= 0) return false;
   // (activation offsets are formed for all 16 * ceil(M / 16) <= 64 tile rows)
   if (N * row_bytes >= (1LL << 31) || N * nblk * 4 >= (1LL << 31) || 64 * (Kp + 128) * 2 >= (1LL << 31))
     return false;
