@@ -10,7 +10,7 @@
 // tiles, no matrix-core work is spent on padding rows beyond ceil(M / 16) * 16, and every
 // weight is loaded and dequantized once.
 //
-// Work-group: 8 waves and one or two 16-row strips of W (16 or 32 output columns).  The reduction
+// Work-group: 8 waves and one, two or four 16-row strips of W (16 to 64 output columns).  The reduction
 // runs in steps of 128 codes; wave w takes steps w, w + 8, ...  In a step, lane l
 // (n = l % 16, q = l / 16) loads codes [32q, 32q + 32) of W row n of each strip (16 bytes
 // of u4, 8 of u2, inside one block since blocks are >= 32 codes), dequantizes them into
@@ -30,10 +30,13 @@ namespace {
 
 constexpr int SK_WAVES = 8;
 constexpr int SK_THREADS = SK_WAVES * 64;
-// NS: 16-row strips of W per work-group.  Two let each activation fragment feed two
-// strips; one doubles the work-groups of a narrow output (used when N / 16 work-groups
-// fit on the compute units in one round, and only for a single M tile).  The strip
-// count never changes any output's summation order.
+// NS: 16-row strips of W per work-group.  More strips let each activation fragment
+// feed more matrix-core steps; fewer give a narrow output more work-groups.  One M
+// tile: one strip when N / 16 work-groups fit on the compute units in one round, else
+// two.  Two or four M tiles: four strips when N / 64 work-groups still cover three
+// quarters of the compute units, else two.  (Measured on MI355X at the 16-entry
+// codebook shapes, M = 16 and 64.)  The strip count never changes any output's
+// summation order.
 constexpr int SK_STEP = 128;   // codes per reduction step
 constexpr uint32_t kSkWord3 = 0x00020000u;
 
@@ -246,10 +249,17 @@ void sk_mb(const PrefillArgs& p, hipStream_t st) {
   if (p.M <= 16) {
     if ((p.N + 15) / 16 <= cus) sk_launch<FMT, BITS, ZK, CT, 1, 1>(p, st);
     else sk_launch<FMT, BITS, ZK, CT, 1, 2>(p, st);
-  } else if (p.M <= 32) {
-    sk_launch<FMT, BITS, ZK, CT, 2, 2>(p, st);
   } else {
-    sk_launch<FMT, BITS, ZK, CT, 4, 2>(p, st);
+    // four strips (half the activation reads per matrix-core step) while that still
+    // leaves at least three quarters of the compute units a work-group
+    const bool wide = (p.N + 63) / 64 * 4 >= 3 * (int64_t)cus;
+    if (p.M <= 32) {
+      if (wide) sk_launch<FMT, BITS, ZK, CT, 2, 4>(p, st);
+      else sk_launch<FMT, BITS, ZK, CT, 2, 2>(p, st);
+    } else {
+      if (wide) sk_launch<FMT, BITS, ZK, CT, 4, 4>(p, st);
+      else sk_launch<FMT, BITS, ZK, CT, 4, 2>(p, st);
+    }
   }
 }
 
