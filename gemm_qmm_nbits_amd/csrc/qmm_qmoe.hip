@@ -633,7 +633,7 @@ __device__ __forceinline__ void stage_h_coherent(const uint16_t* src, int rows, 
 
 // COH: h is written with device-coherent stores (read by other work-groups of the
 // same launch in the single-launch form).
-template <int RI, int ZK, bool COH>
+template <int RI, int ZK, bool COH, bool INT8 = false>
 __device__ __forceinline__ void fc1_stream_body(const QmoeArgs& a, int bid, int nb, uint32_t* smem) {
   constexpr int NR = 2 * RI;
   constexpr int NW = kMoeStreamThreads / 64;
@@ -643,9 +643,13 @@ __device__ __forceinline__ void fc1_stream_body(const QmoeArgs& a, int bid, int 
   const int I = (int)a.I;
   const int nch = (int)a.fc1_chunks;
   const int nblk = (int)a.fc1_nblk;
-  float* xf = (float*)smem;                    // [T][nch * 32]
-  float* sa = xf + (size_t)T * nch * 32;       // [T][nch]
-  float* outs = sa + (size_t)T * nch;          // [local rows][2]: g and u sums
+  const int H = (int)a.H;
+  float* xf = (float*)smem;                    // fp: [T][nch * 32]
+  float* sa = xf + (size_t)T * nch * 32;       // fp: [T][nch]
+  uint32_t* xq = smem;                         // int8: [T][H / 4] permuted codes
+  float* xs = (float*)(smem + (size_t)T * H / 4);  // int8: [T][H / 32] scales
+  int* xsum = (int*)(xs + (size_t)T * H / 32);     // int8: [T][H / 32] code sums
+  float* outs = INT8 ? (float*)(xsum + (size_t)T * H / 32) : sa + (size_t)T * nch;  // [local rows][2]
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int lpr_log2 = a.fc1_lpr_log2;
@@ -720,20 +724,36 @@ __device__ __forceinline__ void fc1_stream_body(const QmoeArgs& a, int bid, int 
     const bool cv = live && c < nch;
     const int cc = c < nch ? c : nch - 1;
     const int blk = cc >> blk_shift;
-    const float* xp = xf + ((size_t)ct * nch + cc) * 32;
-    float xa[32];
+    if constexpr (INT8) {
+      const uint32_t* xqt = xq + (size_t)ct * (H / 4);
+      const uint4 q0 = *(const uint4*)(xqt + cc * 8);
+      const uint4 q1 = *(const uint4*)(xqt + cc * 8 + 4);
+      const uint32_t qq[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+      const float sx = xs[ct * (H / 32) + cc];
+      const int sum = xsum[ct * (H / 32) + cc];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const f32x4 v = *(const f32x4*)(xp + 4 * q);
-      xa[4 * q] = v.x; xa[4 * q + 1] = v.y; xa[4 * q + 2] = v.z; xa[4 * q + 3] = v.w;
-    }
-    const float sac = sa[ct * nch + cc];
+      for (int r = 0; r < NR; ++r) {
+        const int dotv = dot_chunk_u4_i8(cb.w[r], qq);
+        const int zp = (int)((cb.z[r] >> ((blk & 1) * 4)) & 0xfu);
+        const float nv = fmaf((float)cb.s[r] * sx, (float)(dotv - zp * sum), acc[r]);
+        acc[r] = cv ? nv : acc[r];
+      }
+    } else {
+      const float* xp = xf + ((size_t)ct * nch + cc) * 32;
+      float xa[32];
 #pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      const float pr = dot_chunk_u4(cb.w[r], xa);
-      const float zp = (float)((cb.z[r] >> ((blk & 1) * 4)) & 0xfu);
-      const float nv = fmaf((float)cb.s[r], fmaf(-zp, sac, 512.0f * pr), acc[r]);
-      acc[r] = cv ? nv : acc[r];
+      for (int q = 0; q < 8; ++q) {
+        const f32x4 v = *(const f32x4*)(xp + 4 * q);
+        xa[4 * q] = v.x; xa[4 * q + 1] = v.y; xa[4 * q + 2] = v.z; xa[4 * q + 3] = v.w;
+      }
+      const float sac = sa[ct * nch + cc];
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        const float pr = dot_chunk_u4(cb.w[r], xa);
+        const float zp = (float)((cb.z[r] >> ((blk & 1) * 4)) & 0xfu);
+        const float nv = fmaf((float)cb.s[r], fmaf(-zp, sac, 512.0f * pr), acc[r]);
+        acc[r] = cv ? nv : acc[r];
+      }
     }
     if (live && cit == iters - 1) {
       // group complete: fixed-order combination of the LPR lane partials
@@ -761,10 +781,24 @@ __device__ __forceinline__ void fc1_stream_body(const QmoeArgs& a, int bid, int 
   // the activations are converted
   MoeItem<NR> buf[D];
   set_group(fgrp);
-  stage_f32_first(a.X, T, (int)a.H, nch, xf, sa, [&] {
+  if constexpr (INT8) {
+    // every token's x quantized into LDS (work-group 0 keeps a copy in scratch)
 #pragma unroll
     for (int i = 0; i < D - 1; ++i) fetch(buf[i]);
-  });
+    for (int t = 0; t < T; ++t) {
+      const uint16_t* x = a.X + (size_t)t * H;
+      quantize_groups_lds([&](int i) { return f16_to_f32(x[i]); }, H, xq + (size_t)t * (H / 4),
+                          xs + (size_t)t * (H / 32), xsum + (size_t)t * (H / 32),
+                          bid == 0 ? a.xq_out + (size_t)t * H : nullptr,
+                          bid == 0 ? a.xs_out + (size_t)t * (H / 32) : nullptr);
+    }
+    __syncthreads();
+  } else {
+    stage_f32_first(a.X, T, (int)a.H, nch, xf, sa, [&] {
+#pragma unroll
+      for (int i = 0; i < D - 1; ++i) fetch(buf[i]);
+    });
+  }
   const int total = wave_groups * iters;
   for (int base = 0; base < total; base += D) {
 #pragma unroll
@@ -793,17 +827,17 @@ __device__ __forceinline__ void fc1_stream_body(const QmoeArgs& a, int bid, int 
   }
 }
 
-template <int RI, int ZK>
+template <int RI, int ZK, int INT8>
 __global__ __launch_bounds__(kMoeStreamThreads) void qmoe_fc1_stream_kernel(QmoeArgs a) {
   extern __shared__ uint32_t smem[];
-  fc1_stream_body<RI, ZK, false>(a, (int)blockIdx.x, (int)gridDim.x, smem);
+  fc1_stream_body<RI, ZK, false, INT8 != 0>(a, (int)blockIdx.x, (int)gridDim.x, smem);
 }
 
 
 // FUSED: h was written earlier in the same launch by other work-groups: the first
 // weight loads are issued, then `wait()` (every work-group's h is complete), then h is
 // staged with device-coherent loads.
-template <int R, int ZK, bool FUSED, typename Wait>
+template <int R, int ZK, bool FUSED, typename Wait, bool INT8 = false>
 __device__ __forceinline__ void fc2_stream_body(const QmoeArgs& a, int bid, int nb, uint32_t* smem, Wait&& wait) {
   constexpr int NW = kMoeStreamThreads / 64;
   constexpr int D = kFc2Depth;
@@ -812,9 +846,13 @@ __device__ __forceinline__ void fc2_stream_body(const QmoeArgs& a, int bid, int 
   const int H = (int)a.H;
   const int nch = (int)a.fc2_chunks;
   const int nblk = (int)a.fc2_nblk;
-  float* hf = (float*)smem;                    // [T * k][nch * 32]
-  float* sa = hf + (size_t)T * k * nch * 32;   // [T * k][nch]
-  float* outs = sa + (size_t)T * k * nch;      // [local rows][k]: slot sums
+  const int I = (int)a.I;
+  float* hf = (float*)smem;                    // fp: [T * k][nch * 32]
+  float* sa = hf + (size_t)T * k * nch * 32;   // fp: [T * k][nch]
+  uint32_t* hq = smem;                         // int8: [T * k][I / 4] permuted codes
+  float* hs = (float*)(smem + (size_t)T * k * I / 4);  // int8: [T * k][I / 32] scales
+  int* hsum = (int*)(hs + (size_t)T * k * I / 32);     // int8: [T * k][I / 32] code sums
+  float* outs = INT8 ? (float*)(hsum + (size_t)T * k * I / 32) : sa + (size_t)T * k * nch;  // [local rows][k]
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int lpr_log2 = a.fc2_lpr_log2;
@@ -900,20 +938,37 @@ __device__ __forceinline__ void fc2_stream_body(const QmoeArgs& a, int bid, int 
     const bool cv = live && c < nch;
     const int cc = c < nch ? c : nch - 1;
     const int blk = cc >> blk_shift;
-    const float* xp = hf + ((size_t)c_hrow * nch + cc) * 32;
-    float xa[32];
+    if constexpr (INT8) {
+      const uint32_t* qg = hq + ((size_t)c_hrow * I + cc * 32) / 4;
+      const uint4 q0 = *(const uint4*)(qg);
+      const uint4 q1 = *(const uint4*)(qg + 4);
+      const uint32_t qq[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+      const int gi = (c_hrow * I + cc * 32) / 32;
+      const float sx = hs[gi];
+      const int sum = hsum[gi];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const f32x4 v = *(const f32x4*)(xp + 4 * q);
-      xa[4 * q] = v.x; xa[4 * q + 1] = v.y; xa[4 * q + 2] = v.z; xa[4 * q + 3] = v.w;
-    }
-    const float sac = sa[c_hrow * nch + cc];
+      for (int r = 0; r < R; ++r) {
+        const int dotv = dot_chunk_u4_i8(cb.w[r], qq);
+        const int zp = (int)((cb.z[r] >> ((blk & 1) * 4)) & 0xfu);
+        const float nv = fmaf((float)cb.s[r] * sx, (float)(dotv - zp * sum), acc[r]);
+        acc[r] = cv ? nv : acc[r];
+      }
+    } else {
+      const float* xp = hf + ((size_t)c_hrow * nch + cc) * 32;
+      float xa[32];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const float pr = dot_chunk_u4(cb.w[r], xa);
-      const float zp = (float)((cb.z[r] >> ((blk & 1) * 4)) & 0xfu);
-      const float nv = fmaf((float)cb.s[r], fmaf(-zp, sac, 512.0f * pr), acc[r]);
-      acc[r] = cv ? nv : acc[r];
+      for (int q = 0; q < 8; ++q) {
+        const f32x4 v = *(const f32x4*)(xp + 4 * q);
+        xa[4 * q] = v.x; xa[4 * q + 1] = v.y; xa[4 * q + 2] = v.z; xa[4 * q + 3] = v.w;
+      }
+      const float sac = sa[c_hrow * nch + cc];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float pr = dot_chunk_u4(cb.w[r], xa);
+        const float zp = (float)((cb.z[r] >> ((blk & 1) * 4)) & 0xfu);
+        const float nv = fmaf((float)cb.s[r], fmaf(-zp, sac, 512.0f * pr), acc[r]);
+        acc[r] = cv ? nv : acc[r];
+      }
     }
     if (live && cit == iters - 1) {
       // unit complete: fixed-order combination of the lane partials of its slot
@@ -937,7 +992,12 @@ __device__ __forceinline__ void fc2_stream_body(const QmoeArgs& a, int bid, int 
   // the activations are converted
   MoeItem<R> buf[D];
   set_unit(fu);
-  if constexpr (FUSED) {
+  if constexpr (INT8) {
+    // the codes and scales of every slot's h (quantized once per call into scratch)
+#pragma unroll
+    for (int i = 0; i < D - 1; ++i) fetch(buf[i]);
+    stage_i8(a.hq_out, a.hs_out, T * k * I, hq, hs, hsum);
+  } else if constexpr (FUSED) {
 #pragma unroll
     for (int i = 0; i < D - 1; ++i) fetch(buf[i]);
     wait();
@@ -971,10 +1031,11 @@ __device__ __forceinline__ void fc2_stream_body(const QmoeArgs& a, int bid, int 
   }
 }
 
-template <int R, int ZK>
+template <int R, int ZK, int INT8>
 __global__ __launch_bounds__(kMoeStreamThreads) void qmoe_fc2_stream_kernel(QmoeArgs a) {
   extern __shared__ uint32_t smem[];
-  fc2_stream_body<R, ZK, false>(a, (int)blockIdx.x, (int)gridDim.x, smem, [] {});
+  auto no_wait = [] {};
+  fc2_stream_body<R, ZK, false, decltype(no_wait)&, INT8 != 0>(a, (int)blockIdx.x, (int)gridDim.x, smem, no_wait);
 }
 
 
@@ -1101,15 +1162,17 @@ static bool moe_stream_plan(Kern kern, int64_t ngroups, size_t fixed, size_t per
   return true;
 }
 
-template <int RI, int ZK>
+template <int RI, int ZK, int INT8>
 static bool launch_fc1_stream(const QmoeArgs& a, int cap, hipStream_t st) {
-  auto kern = qmoe_fc1_stream_kernel<RI, ZK>;
+  auto kern = qmoe_fc1_stream_kernel<RI, ZK, INT8>;
   // one expert's W1, scales and zero points are addressed with 32-bit offsets
   const int64_t erows = 2 * a.I;
   if (erows * a.fc1_row_bytes >= (1LL << 31) || erows * a.fc1_nblk * 2 >= (1LL << 31)) return false;
   const int64_t rpg = (64 >> a.fc1_lpr_log2) * RI;
   const int64_t ngroups = a.T * a.k * ((a.I + rpg - 1) / rpg);
-  const size_t fixed = (size_t)a.T * a.fc1_chunks * 33 * sizeof(float);
+  // staged activations: fp32 values and chunk sums, or int8 codes, scales and code sums
+  const size_t fixed = INT8 ? (size_t)a.T * ((size_t)a.H + (size_t)(a.H / 32) * 8)
+                            : (size_t)a.T * a.fc1_chunks * 33 * sizeof(float);
   int64_t grid = 0;
   size_t lds = 0;
   if (!moe_stream_plan(kern, ngroups, fixed, (size_t)rpg * 2 * sizeof(float), a.num_cus, cap, &grid, &lds))
@@ -1119,13 +1182,14 @@ static bool launch_fc1_stream(const QmoeArgs& a, int cap, hipStream_t st) {
   return true;
 }
 
-template <int R, int ZK>
+template <int R, int ZK, int INT8>
 static bool launch_fc2_stream(const QmoeArgs& a, int cap, hipStream_t st) {
-  auto kern = qmoe_fc2_stream_kernel<R, ZK>;
+  auto kern = qmoe_fc2_stream_kernel<R, ZK, INT8>;
   if (a.H * a.fc2_row_bytes >= (1LL << 31) || a.H * a.fc2_nblk * 2 >= (1LL << 31)) return false;
   const int64_t rpg = (64 >> a.fc2_lpr_log2) * R;
   const int64_t ngroups = a.T * ((a.H + rpg - 1) / rpg);
-  const size_t fixed = (size_t)a.T * a.k * a.fc2_chunks * 33 * sizeof(float);
+  const size_t fixed = INT8 ? (size_t)a.T * a.k * ((size_t)a.I + (size_t)(a.I / 32) * 8)
+                            : (size_t)a.T * a.k * a.fc2_chunks * 33 * sizeof(float);
   int64_t grid = 0;
   size_t lds = 0;
   if (!moe_stream_plan(kern, ngroups, fixed, (size_t)rpg * a.k * sizeof(float), a.num_cus, cap, &grid, &lds))
@@ -1201,12 +1265,17 @@ hipError_t launch_qmoe_fused(const QmoeArgs& a, hipStream_t st) {
 
 hipError_t launch_qmoe_fc1(const QmoeArgs& a, int candidate, hipStream_t st) {
   const int rows_per_lane = candidate & 15;
-  if (a.mode != QMOE_INT8_ACT && !(candidate & kQmoePerSlot)) {
+  if (!(candidate & kQmoePerSlot)) {
     const bool zk = a.fc1.zp != nullptr;
     bool done;
     const int cap = (candidate & kQmoeOnePerCu) ? 1 : 1 << 20;
-    if (rows_per_lane == 1) done = zk ? launch_fc1_stream<1, 1>(a, cap, st) : launch_fc1_stream<1, 0>(a, cap, st);
-    else done = zk ? launch_fc1_stream<2, 1>(a, cap, st) : launch_fc1_stream<2, 0>(a, cap, st);
+    if (a.mode == QMOE_INT8_ACT) {
+      if (rows_per_lane == 1) done = zk ? launch_fc1_stream<1, 1, 1>(a, cap, st) : launch_fc1_stream<1, 0, 1>(a, cap, st);
+      else done = zk ? launch_fc1_stream<2, 1, 1>(a, cap, st) : launch_fc1_stream<2, 0, 1>(a, cap, st);
+    } else {
+      if (rows_per_lane == 1) done = zk ? launch_fc1_stream<1, 1, 0>(a, cap, st) : launch_fc1_stream<1, 0, 0>(a, cap, st);
+      else done = zk ? launch_fc1_stream<2, 1, 0>(a, cap, st) : launch_fc1_stream<2, 0, 0>(a, cap, st);
+    }
     if (done) return hipSuccess;
   }
   const int subs = 64 >> a.fc1_lpr_log2;
@@ -1227,12 +1296,24 @@ hipError_t launch_qmoe_fc1(const QmoeArgs& a, int candidate, hipStream_t st) {
 
 hipError_t launch_qmoe_fc2(const QmoeArgs& a, int candidate, hipStream_t st) {
   const int rows_per_lane = candidate & 15;
-  if (a.mode != QMOE_INT8_ACT && !(candidate & kQmoePerSlot)) {
+  if (a.mode == QMOE_INT8_ACT) {
+    // h -> int8 codes and scales once (into the scratch fc2 stages from)
+    const int64_t groups = a.T * a.k * a.I / 32;
+    const int64_t blocks = (groups + 7) / 8;
+    hipLaunchKernelGGL(qmoe_quant_h_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a.h, groups, a.hq_out,
+                       a.hs_out);
+  }
+  if (!(candidate & kQmoePerSlot)) {
     const bool zk = a.fc2.zp != nullptr;
     bool done;
     const int cap = (candidate & kQmoeOnePerCu) ? 1 : 1 << 20;
-    if (rows_per_lane == 1) done = zk ? launch_fc2_stream<1, 1>(a, cap, st) : launch_fc2_stream<1, 0>(a, cap, st);
-    else done = zk ? launch_fc2_stream<2, 1>(a, cap, st) : launch_fc2_stream<2, 0>(a, cap, st);
+    if (a.mode == QMOE_INT8_ACT) {
+      if (rows_per_lane == 1) done = zk ? launch_fc2_stream<1, 1, 1>(a, cap, st) : launch_fc2_stream<1, 0, 1>(a, cap, st);
+      else done = zk ? launch_fc2_stream<2, 1, 1>(a, cap, st) : launch_fc2_stream<2, 0, 1>(a, cap, st);
+    } else {
+      if (rows_per_lane == 1) done = zk ? launch_fc2_stream<1, 1, 0>(a, cap, st) : launch_fc2_stream<1, 0, 0>(a, cap, st);
+      else done = zk ? launch_fc2_stream<2, 1, 0>(a, cap, st) : launch_fc2_stream<2, 0, 0>(a, cap, st);
+    }
     if (done) return hipSuccess;
   }
   const int subs = 64 >> a.fc2_lpr_log2;
@@ -1240,11 +1321,6 @@ hipError_t launch_qmoe_fc2(const QmoeArgs& a, int candidate, hipStream_t st) {
   const dim3 grid((unsigned)((a.H + rows_per_wg - 1) / rows_per_wg), (unsigned)a.T);
   const size_t lds = qmoe_fc2_lds_bytes(a);
   if (a.mode == QMOE_INT8_ACT) {
-    // h -> int8 codes and scales once (into the scratch fc2 stages from)
-    const int64_t groups = a.T * a.k * a.I / 32;
-    const int64_t blocks = (groups + 7) / 8;
-    hipLaunchKernelGGL(qmoe_quant_h_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a.h, groups, a.hq_out,
-                       a.hs_out);
     if (rows_per_lane == 1) hipLaunchKernelGGL((qmoe_fc2_kernel<1, 1>), grid, dim3(256), lds, st, a);
     else hipLaunchKernelGGL((qmoe_fc2_kernel<1, 2>), grid, dim3(256), lds, st, a);
   } else {
