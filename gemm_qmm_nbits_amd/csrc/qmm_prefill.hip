@@ -359,6 +359,20 @@ void launch_ct(const PrefillArgs& p, dim3 grid, hipStream_t st) {
 
 }  // namespace
 
+hipError_t launch_reduce_splits(const float* P, int S, int64_t M, int64_t N, int64_t ldc, const void* bias,
+                                void* C, int c_type, hipStream_t st) {
+  int64_t blocks = (M * N + 255) / 256;
+  if (blocks > 16384) blocks = 16384;
+  if (blocks < 1) blocks = 1;
+  if (c_type == QMM_F32)
+    hipLaunchKernelGGL(reduce_splits_kernel<QMM_F32>, dim3((unsigned)blocks), dim3(256), 0, st, P, S, M, N, ldc, bias, C);
+  else if (c_type == QMM_F16)
+    hipLaunchKernelGGL(reduce_splits_kernel<QMM_F16>, dim3((unsigned)blocks), dim3(256), 0, st, P, S, M, N, ldc, bias, C);
+  else
+    hipLaunchKernelGGL(reduce_splits_kernel<QMM_BF16>, dim3((unsigned)blocks), dim3(256), 0, st, P, S, M, N, ldc, bias, C);
+  return hipSuccess;
+}
+
 int prefill_splits(int64_t M, int64_t N, int64_t Kp) {
   // Splits of the reduction when the 256 x 256 output tiles do not fill the chip.
   // Cost in stage times (one 256 x 256 x 64 tile step, about 2.5 us): rounds of work

@@ -11,5 +11,11 @@ namespace qmm {
 constexpr int64_t kSkinnyMaxM = 64;
 bool skinny_applies(int64_t M, int64_t N, int64_t Kp, int block, int64_t row_bytes, int64_t nblk);
 hipError_t launch_skinny(const PrefillArgs& p, hipStream_t st);
+// Reduction splits of the skinny path (a function of the shape only; at most the
+// splits the workspace holds partial sums for).
+int skinny_splits(int64_t M, int64_t N, int64_t Kp);
+// C = (((P[0] + P[1]) + ...) + P[S-1]) + bias, in C's type (qmm_prefill.hip).
+hipError_t launch_reduce_splits(const float* P, int S, int64_t M, int64_t N, int64_t ldc, const void* bias,
+                                void* C, int c_type, hipStream_t st);
 
 }  // namespace qmm

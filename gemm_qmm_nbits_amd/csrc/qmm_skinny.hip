@@ -19,7 +19,9 @@
 // 8-value groups: lane l supplies A row l % 16 and W row l % 16 over the same 8 k, so
 // the pairing is exact whatever order the instruction takes its k in; accumulator v of
 // lane l is row 4 * (l / 16) + v, column l % 16.  The eight waves' fp32 sums are added
-// in wave order through LDS, so the result depends only on the shape.
+// in wave order through LDS.  When the grid would not fill the chip, the reduction is
+// split into contiguous step ranges whose fp32 partial sums the split reduction adds in
+// order.  The result depends only on the shape.
 #include "qmm_device.h"
 #include "qmm_internal.h"
 #include "qmm_skinny.h"
@@ -121,6 +123,10 @@ __global__ __launch_bounds__(SK_THREADS) void skinny_kernel(PrefillArgs p) {
   const int nsteps = (Kp + SK_STEP - 1) / SK_STEP;
   const int nblk = (int)p.nblk, blog = p.block_log2;
   const int n0 = (int)blockIdx.x * (SK_NS * 16);
+  // reduction split ks covers steps [ks * spl, (ks + 1) * spl)
+  const int ks = (int)blockIdx.y;
+  const int s_begin = ks * p.spl;
+  const int s_end = s_begin + p.spl < nsteps ? s_begin + p.spl : nsteps;
 
   const __amdgpu_buffer_rsrc_t rW = sk_rsrc(p.W, p.N * p.row_bytes);
   const __amdgpu_buffer_rsrc_t rS = FMT == GEMV_CODEBOOK ? sk_rsrc(p.absmax, p.N * p.nblk * 4)
@@ -145,7 +151,7 @@ __global__ __launch_bounds__(SK_THREADS) void skinny_kernel(PrefillArgs p) {
 #pragma unroll
     for (int s = 0; s < SK_NS; ++s) acc[mt][s] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  for (int c = wave; c < nsteps; c += SK_WAVES) {
+  for (int c = s_begin + wave; c < s_end; c += SK_WAVES) {
     const int k0 = c * SK_STEP + lq * 32;  // this lane's 32 codes
     const bool kin = k0 < Kp;             // Kp % 64 == 0: wholly inside or wholly past
     // weights: 32 codes, scale (or absmax) and zero point of their block, per strip
@@ -224,6 +230,11 @@ __global__ __launch_bounds__(SK_THREADS) void skinny_kernel(PrefillArgs p) {
     float y = red[r * 64 + l];
 #pragma unroll
     for (int w = 1; w < SK_WAVES; ++w) y += red[(w * R + r) * 64 + l];
+    if (p.splits > 1) {
+      // fp32 partial sum of this split; the split reduction adds the splits in order
+      p.partials[((int64_t)ks * M + m) * p.ldc + n] = y;
+      continue;
+    }
     if (p.bias) y += sk_bias<CT>(p.bias, n);
     sk_store<CT>(p.C, (int64_t)m * p.ldc + n, y);
   }
@@ -235,7 +246,7 @@ void sk_launch(const PrefillArgs& p, hipStream_t st) {
   const size_t lds = (size_t)SK_WAVES * MB * SK_NS * 4 * 64 * sizeof(float);
   if (lds > 64 * 1024) (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   const unsigned grid = (unsigned)((p.N + SK_NS * 16 - 1) / (SK_NS * 16));
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(SK_THREADS), lds, st, p);
+  hipLaunchKernelGGL(kern, dim3(grid, (unsigned)p.splits), dim3(SK_THREADS), lds, st, p);
 }
 
 template <int FMT, int BITS, int ZK, int CT>
@@ -281,7 +292,25 @@ bool skinny_applies(int64_t M, int64_t N, int64_t Kp, int block, int64_t row_byt
   return true;
 }
 
-hipError_t launch_skinny(const PrefillArgs& p, hipStream_t st) {
+int skinny_splits(int64_t M, int64_t N, int64_t Kp) {
+  // Split the reduction while the grid stays within one work-group per compute unit
+  // of a 256-CU device (work-groups counted as the launch deals strips: one per
+  // work-group for a single M tile when N / 16 <= 256, else two) and every wave of a
+  // split keeps at least one step; powers of two up to 8.  The partial sums go to the
+  // workspace, which holds prefill_splits(M, N, Kp) of them.
+  const int64_t wgs = (M <= 16 && (N + 15) / 16 <= 256) ? (N + 15) / 16 : (N + 31) / 32;
+  const int64_t nsteps = (Kp + SK_STEP - 1) / SK_STEP;
+  const int64_t cap = prefill_splits(M, N, Kp);
+  int s = 1;
+  while (s < 8 && wgs * s * 2 <= 256 && nsteps >= (int64_t)s * 2 * SK_WAVES && s * 2 <= cap) s *= 2;
+  return s;
+}
+
+hipError_t launch_skinny(const PrefillArgs& p0, hipStream_t st) {
+  PrefillArgs p = p0;
+  const int64_t nsteps = (p.Kp + SK_STEP - 1) / SK_STEP;
+  p.splits = p.partials ? skinny_splits(p.M, p.N, p.Kp) : 1;
+  p.spl = (int)((nsteps + p.splits - 1) / p.splits);
   const int zk = p.zp_kind == QMM_ZP_PACKED ? 1 : p.zp_kind == QMM_ZP_F16 ? 2 : 0;
   if (p.fmt == GEMV_CODEBOOK) {
     sk_ct<GEMV_CODEBOOK, 4, 0>(p, st);
@@ -294,6 +323,7 @@ hipError_t launch_skinny(const PrefillArgs& p, hipStream_t st) {
     else if (zk == 2) sk_ct<GEMV_AFFINE, 4, 2>(p, st);
     else sk_ct<GEMV_AFFINE, 4, 0>(p, st);
   }
+  if (p.splits > 1) return launch_reduce_splits(p.partials, p.splits, p.M, p.N, p.ldc, p.bias, p.C, p.c_type, st);
   return hipSuccess;
 }
 
