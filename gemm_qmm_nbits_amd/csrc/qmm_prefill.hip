@@ -67,8 +67,12 @@ __device__ __forceinline__ float load_bias(const void* b, int64_t i) {
 }
 
 // LDS tiles: 256 rows of 64 fp16 (128 bytes, no padding); the 16-byte piece p of row
-// r sits at piece position p ^ (r % 8), so the 16-byte operand reads of 8 consecutive
-// rows at one k hit 8 different bank groups.  A is double buffered and filled by
+// r sits at piece position p ^ ((r / 2) % 8).  The LDS serves 16 lanes (256 bytes) of a
+// 16-byte access per cycle, and a 256-byte line holds two rows: the 16 consecutive rows
+// that 16 lanes read at one k then fall on 16 different 16-byte bank groups (with the
+// position p ^ (r % 8), rows r and r + 8 met in one bank group on every operand read
+// and every dequantized-weight store: 43% of the LDS cycles were conflict stalls on
+// MI355X).  A is double buffered and filled by
 // direct global->LDS loads (no registers on the way); W16 is double buffered and
 // written by the dequantization.
 __shared__ __attribute__((aligned(16))) uint8_t pf_a0[BM * 128];
@@ -77,7 +81,9 @@ __shared__ __attribute__((aligned(16))) uint8_t pf_b0[BN * 128];
 __shared__ __attribute__((aligned(16))) uint8_t pf_b1[BN * 128];
 __shared__ float pf_cb[16];  // codebook (16 entries, one per bank)
 
-__device__ __forceinline__ uint32_t swz(int row, int piece) { return (uint32_t)row * 128u + (uint32_t)((piece ^ (row & 7)) << 4); }
+__device__ __forceinline__ uint32_t swz(int row, int piece) {
+  return (uint32_t)row * 128u + (uint32_t)((piece ^ ((row >> 1) & 7)) << 4);
+}
 
 // FMT: GEMV_AFFINE (w = (q - zp) * s) or GEMV_CODEBOOK (BITS = 4, w = codebook[q] * absmax).
 template <int FMT, int BITS, int ZK, int CT>
@@ -118,14 +124,14 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillArgs p) {
 
   // A rows of this thread's direct loads: wave w fills rows 32w .. 32w + 31 with four
   // 8-row loads; lane l takes row 32w + 8i + l/8 at piece position l % 8, i.e. global
-  // piece (l % 8) ^ (row % 8).  Rows past M read row M - 1 (results unused).
+  // piece (l % 8) ^ ((row / 2) % 8).  Rows past M read row M - 1 (results unused).
   const uint8_t* a_src[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int row = wave * 32 + q * 8 + (lane >> 3);
     int grow = m0 + row;
     grow = grow < (int)p.M ? grow : (int)p.M - 1;
-    const int piece = (lane & 7) ^ (row & 7);
+    const int piece = (lane & 7) ^ ((row >> 1) & 7);
     a_src[q] = (const uint8_t*)p.A16 + ((int64_t)grow * Kp) * 2 + piece * 16;
   }
   // plain global addresses (no range check): the stage index is clamped to the last
@@ -240,10 +246,10 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillArgs p) {
     for (int b = 0; b < 4; ++b) acc[a][b] = f32x16{};
 
   // operand rows of this lane: A rows wm*64 + 32a + lane%32, W rows wn*128 + 32b + lane%32;
-  // all have row % 8 == lane % 8
+  // all have (row / 2) % 8 == (lane / 2) % 8
   const uint32_t a_row0 = (uint32_t)(wm * 64 + (lane & 31)) * 128u;
   const uint32_t b_row0 = (uint32_t)(wn * 128 + (lane & 31)) * 128u;
-  const int hi = lane >> 5, l7 = lane & 7;
+  const int hi = lane >> 5, l7 = (lane >> 1) & 7;  // (row / 2) % 8 of the lane's operand rows
 
   // matrix-core work of one stage (tiles ab, bb); after each 16-deep k step, one part
   // of the next stage's weights (st) is dequantized into sdst
