@@ -93,10 +93,12 @@ enum {
  *   workspace, workspace_bytes: device scratch of at least
  *            qmm_nbits_workspace_bytes(M, K, N, a_type) bytes (may be NULL when that is 0).
  * Paths: M <= 8 runs the weight-streaming GEMV, which reads A in its own type
- * and accumulates in fp32.  M > 8 runs the prefill path: A is rounded to fp16
+ * and accumulates in fp32.  M > 8 runs a matrix-core path: A is rounded to fp16
  * once into the workspace (rows of K rounded up to a multiple of 64, padded with
- * zeros, for any a_type), W tiles are dequantized to fp16 and multiplied on the
- * fp16 matrix cores with fp32 accumulation.  When the 256 x 256 output tiles do
+ * zeros, for any a_type), each weight is dequantized exactly in fp32 and rounded
+ * to fp16, and the products are accumulated in fp32 on the fp16 matrix cores.
+ * For 8 < M <= 64 with block >= 32 a skinny kernel (16-row M tiles, each weight
+ * loaded once) runs; otherwise 256 x 256 output tiles.  When either grid would
  * not fill the chip, the reduction over K is split into a number of parts fixed
  * by the shape; fp32 partial sums [parts][M][N] follow A in the workspace and are
  * added in part order by a second kernel.
@@ -128,7 +130,8 @@ qmm_status qmm_validate_nbits(const void* A, int a_type, int64_t M, int64_t K, i
  *            qmm_codebook4_workspace_bytes(M, K, N, a_type) bytes (NULL when that is 0).
  * Paths: M <= 8 weight-streaming GEMV (fp32 FMA, codebook staged in LDS);
  * larger M uses the matrix cores: A rounded to fp16 once into the workspace (as
- * for qmm_nbits), weights fp16(fp32(codebook[q] * absmax)) built tile by tile.
+ * for qmm_nbits), weights fp16(fp32(codebook[q] * absmax)); the skinny kernel for
+ * 8 < M <= 64 with block >= 32, 256 x 256 tiles otherwise (as for qmm_nbits).
  * ------------------------------------------------------------------------- */
 qmm_status qmm_codebook4(const void* A, int a_type, int64_t M, int64_t K, int64_t N,
                          const uint8_t* W, int block, const float* absmax,
