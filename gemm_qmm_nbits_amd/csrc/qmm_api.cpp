@@ -273,8 +273,8 @@ int gemv_choice(int entry, const GemvArgs& g, hipStream_t st) {
 // and slot; else the persistent form, fp mode only, with as many work-groups per
 // compute unit as fit, or one with kQmoeOnePerCu).  All give the same bits.
 constexpr int kQmoeCandidates[] = {1, 2, 1 | kQmoePerSlot, 2 | kQmoePerSlot, 1 | kQmoeOnePerCu,
-                                   2 | kQmoeOnePerCu};
-constexpr int kNumQmoeCandidates = 6;
+                                   2 | kQmoeOnePerCu, 1 | kQmoeDedupe, 2 | kQmoeDedupe};
+constexpr int kNumQmoeCandidates = 8;
 
 struct QmoeTimingBufs {
   int32_t* ids = nullptr;  // timing expert ids, [kSets][T][k]
@@ -396,7 +396,10 @@ void qmoe_choice(const QmoeArgs& a, hipStream_t st, int* r1, int* r2) {
             double tot = 0;
             for (int r = 1; r < kRounds; ++r) tot += tv[r * kNumQmoeCandidates + c];
             std::fprintf(stderr, " %s%d:%.2fus",
-                         (kQmoeCandidates[c] & kQmoePerSlot) ? "slot-R" : (kQmoeCandidates[c] & kQmoeOnePerCu) ? "cu1-R" : "R",
+                         (kQmoeCandidates[c] & kQmoePerSlot)    ? "slot-R"
+                         : (kQmoeCandidates[c] & kQmoeOnePerCu) ? "cu1-R"
+                         : (kQmoeCandidates[c] & kQmoeDedupe)   ? "once-R"
+                                                                : "R",
                          kQmoeCandidates[c] & 15, tot / (kRounds - 1));
           }
           std::fprintf(stderr, " pick #%d\n", which == 0 ? c1 : c2);

@@ -51,10 +51,14 @@ bool qmoe_fused_plan(QmoeArgs& a, int candidate);
 hipError_t launch_qmoe_fused(const QmoeArgs& a, hipStream_t st);
 size_t qmoe_fc1_lds_bytes(const QmoeArgs& a);
 size_t qmoe_fc2_lds_bytes(const QmoeArgs& a);
-// candidate: rows per lane (1 or 2), plus kQmoePerSlot for the per-slot form, or
-// kQmoeOnePerCu for the persistent form with one work-group per compute unit
+// candidate: rows per lane (1 or 2), plus kQmoePerSlot for the per-slot form,
+// kQmoeOnePerCu for the persistent form with one work-group per compute unit, or
+// kQmoeDedupe (below)
 constexpr int kQmoePerSlot = 16;
 constexpr int kQmoeOnePerCu = 32;
+// fc1: each expert's rows read once per call for all its slots (fp mode, 1 < T <= 8);
+// otherwise, and for fc2, the persistent form with the same rows per lane
+constexpr int kQmoeDedupe = 64;
 hipError_t launch_qmoe_fc1(const QmoeArgs& a, int candidate, hipStream_t st);
 hipError_t launch_qmoe_fc2(const QmoeArgs& a, int candidate, hipStream_t st);
 

@@ -258,6 +258,8 @@ struct MoeItem {
 };
 
 constexpr int kMoeThreads = 256;
+// slots (T * k) up to which the fc1 form that reads each expert once per call applies
+constexpr int kMoeSortSlots = 64;
 constexpr int kMoeStreamThreads = 512;  // persistent forms
 
 // Expert ids outside [0, E) (a caller error) are clamped into it: never a fault.
@@ -1039,6 +1041,263 @@ __global__ __launch_bounds__(kMoeStreamThreads) void qmoe_fc2_stream_kernel(Qmoe
 }
 
 
+// ---- fc1 reading each expert's rows once per call (fp mode, 1 < T <= kDedupeMaxT) ------
+//
+// The slots routed to one expert share every load of its rows.  The row groups walk the
+// distinct experts of the call (in order of first use), each with the list of its slots
+// in slot order (split into units of at most kDedupeMaxT slots).  A lane loads each
+// chunk of its rows once and runs the per-slot chunk arithmetic of the stream form for
+// every slot of the unit, so every slot's h has the bits of the per-slot forms.
+constexpr int kDedupeMaxT = 8;                 // slots per expert at most (one per token)
+// LDS ints: expert and first use of each slot, the slot list, the start and expert of
+// each distinct expert, the start, count and expert of each unit, the unit count and
+// a split flag
+constexpr int kDedupeInts = 8 * kMoeSortSlots + 3;
+
+template <int RI, int ZK>
+__global__ __launch_bounds__(kMoeStreamThreads) void qmoe_fc1_dedupe_kernel(QmoeArgs a) {
+  constexpr int NR = 2 * RI;  // per row i: the g row and the u row
+  constexpr int NW = kMoeStreamThreads / 64;
+  constexpr int D = RI == 1 ? 4 : 3;
+  constexpr int MS = kDedupeMaxT;
+  extern __shared__ uint32_t smem[];
+  const int T = (int)a.T;
+  const int k = a.k;
+  const int I = (int)a.I;
+  const int S = T * k;
+  const int nch = (int)a.fc1_chunks;
+  const int nblk = (int)a.fc1_nblk;
+  float* xf = (float*)smem;                    // [T][nch * 32]
+  float* sa = xf + (size_t)T * nch * 32;       // [T][nch]
+  int* eid = (int*)(sa + (size_t)T * nch);     // [S] expert of each slot
+  int* first = eid + kMoeSortSlots;            // [S] first slot with the same expert
+  int* ulist = first + kMoeSortSlots;          // [S] slots grouped by expert
+  int* ustart = ulist + kMoeSortSlots;         // [U + 1] start of each expert's slots
+  int* uexp = ustart + kMoeSortSlots + 1;      // [U] the distinct experts
+  int* vstart = uexp + kMoeSortSlots;          // [V] units: start in the slot list,
+  int* vcnt = vstart + kMoeSortSlots;          //     slot count (<= MS),
+  int* vexp = vcnt + kMoeSortSlots;            //     expert
+  int* vnum = vexp + kMoeSortSlots;            // [2] V, and whether any expert needs splitting
+  float* outs = (float*)(eid + kDedupeInts);   // [local rows][MS][2]: g and u sums per slot
+
+  // distinct experts in order of first use and their slots, in three passes
+  for (int s = threadIdx.x; s < S; s += blockDim.x) eid[s] = clamp_expert(a.ids[s], a.E);
+  if (threadIdx.x == 0) vnum[0] = 0, vnum[1] = 0;
+  __syncthreads();
+  for (int s = threadIdx.x; s < S; s += blockDim.x) {
+    const int e = eid[s];
+    int f = s;
+#pragma unroll 16
+    for (int s2 = 0; s2 < S; ++s2) f = (s2 < f && eid[s2] == e) ? s2 : f;
+    first[s] = f;
+  }
+  __syncthreads();
+  for (int s = threadIdx.x; s < S; s += blockDim.x) {
+    const int f = first[s];
+    int pos = 0, u = 0, cnt = 0;
+#pragma unroll 16
+    for (int s2 = 0; s2 < S; ++s2) {
+      const int f2 = first[s2];
+      pos += (f2 < f || (f2 == f && s2 < s)) ? 1 : 0;
+      u += (s2 < f && f2 == s2) ? 1 : 0;
+      cnt += f2 == f ? 1 : 0;
+    }
+    ulist[pos] = s;
+    if (f == s) {
+      ustart[u] = pos;
+      uexp[u] = eid[s];
+      vstart[u] = pos;
+      vcnt[u] = cnt;
+      vexp[u] = eid[s];
+      atomicAdd(&vnum[0], 1);
+      if (cnt > MS) vnum[1] = 1;  // an expert repeated inside a token
+    }
+  }
+  __syncthreads();
+  // units of at most MS slots: normally one per distinct expert; a call that repeats
+  // an expert inside a token has that expert's slots split (one thread, rare)
+  if (vnum[1] != 0 && threadIdx.x == 0) {
+    const int U = vnum[0];
+    ustart[U] = S;
+    int V = 0;
+    for (int u = 0; u < U; ++u) {
+      const int cnt = ustart[u + 1] - ustart[u];
+      for (int off = 0; off < cnt; off += MS) {
+        vstart[V] = ustart[u] + off;
+        vcnt[V] = cnt - off < MS ? cnt - off : MS;
+        vexp[V] = uexp[u];
+        ++V;
+      }
+    }
+    vnum[0] = V;
+  }
+  __syncthreads();
+  const int V = vnum[0];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int lpr_log2 = a.fc1_lpr_log2;
+  const int LPR = 1 << lpr_log2;
+  const int lp = lane & (LPR - 1);
+  const int sub = lane >> lpr_log2;
+  const int SUBS = 64 >> lpr_log2;
+  const int rpg = SUBS * RI;              // rows i per group
+  const int GI = (I + rpg - 1) / rpg;     // groups per unit
+  const int ngroups = V * GI;
+  const int nb = (int)gridDim.x, bid = (int)blockIdx.x;
+  const int groups_lo = ngroups / nb, extra = ngroups % nb;
+  const int g_begin = bid * groups_lo + (bid < extra ? bid : extra);
+  const int g_end = g_begin + groups_lo + (bid < extra ? 1 : 0);
+  if (g_begin >= g_end) return;
+  const int wave_groups = g_end - g_begin > wave ? (g_end - g_begin - wave + NW - 1) / NW : 0;
+  const int iters = (nch + LPR - 1) >> lpr_log2;
+  const int blk_shift = __builtin_ctz((unsigned)a.block) - 5;
+  const uint32_t rb = (uint32_t)a.fc1_row_bytes;
+  const uint32_t zrb = (uint32_t)a.fc1_zp_row_bytes;
+  const uint32_t erows = 2u * (uint32_t)I;
+
+  int fgrp = g_begin + wave, fit = 0;
+  __amdgpu_buffer_rsrc_t rW, rS, rZ;
+  uint32_t frow[NR];
+  auto set_group = [&](int grp) {
+    const int gg = grp < ngroups ? grp : ngroups - 1;
+    const int v = gg / GI;
+    const int gi = gg - v * GI;
+    const int e = vexp[v];
+    rW = make_rsrc(a.fc1.W + (size_t)e * erows * rb, erows * rb);
+    rS = make_rsrc((const uint16_t*)a.fc1.scales + (size_t)e * erows * nblk, erows * (uint32_t)nblk * 2u);
+    if constexpr (ZK) rZ = make_rsrc(a.fc1.zp + (size_t)e * erows * zrb, erows * zrb);
+#pragma unroll
+    for (int r = 0; r < RI; ++r) {
+      const int i = gi * rpg + r * SUBS + sub;
+      const uint32_t ic = (uint32_t)(i < I ? i : I - 1);
+      frow[2 * r] = ic;
+      frow[2 * r + 1] = ic + (uint32_t)I;
+    }
+  };
+  auto fetch = [&](MoeItem<NR>& b) {
+    int c = fit * LPR + lp;
+    c = c < nch ? c : nch - 1;
+    const int blk = c >> blk_shift;
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rW, (int)(frow[r] * rb + (uint32_t)c * 16u), 0, 0);
+      b.w[r] = make_uint4(v[0], v[1], v[2], v[3]);
+      b.s[r] = __builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(
+                                                 rS, (int)((frow[r] * (uint32_t)nblk + (uint32_t)blk) * 2u), 0, 0));
+      if constexpr (ZK)
+        b.z[r] = __builtin_amdgcn_raw_buffer_load_b8(rZ, (int)(frow[r] * zrb + (uint32_t)(blk >> 1)), 0, 0);
+      else
+        b.z[r] = 0x88u;
+    }
+    if (++fit == iters) {
+      fit = 0;
+      fgrp += NW;
+      set_group(fgrp);
+    }
+  };
+
+  // compute cursor: group, item, and the tokens of the group's slots
+  int cgrp = g_begin + wave, cit = 0, ccnt = 0;
+  int ctok[MS];
+  auto set_cgroup = [&](int grp) {
+    const int gg = grp < ngroups ? grp : ngroups - 1;
+    const int v = gg / GI;
+    const int s0 = vstart[v];
+    ccnt = vcnt[v];
+#pragma unroll
+    for (int q = 0; q < MS; ++q) ctok[q] = ulist[s0 + (q < ccnt ? q : 0)] / k;
+  };
+  float acc[MS][NR];
+#pragma unroll
+  for (int q = 0; q < MS; ++q)
+#pragma unroll
+    for (int r = 0; r < NR; ++r) acc[q][r] = 0.0f;
+  auto step = [&](const MoeItem<NR>& cb, MoeItem<NR>& nxt, bool live) {
+    fetch(nxt);
+    const int c = cit * LPR + lp;
+    const bool cv = live && c < nch;
+    const int cc = c < nch ? c : nch - 1;
+    const int blk = cc >> blk_shift;
+#pragma unroll
+    for (int q = 0; q < MS; ++q) {
+      if (q < ccnt) {
+        const float* xp = xf + ((size_t)ctok[q] * nch + cc) * 32;
+        float xa[32];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const f32x4 v = *(const f32x4*)(xp + 4 * j);
+          xa[4 * j] = v.x; xa[4 * j + 1] = v.y; xa[4 * j + 2] = v.z; xa[4 * j + 3] = v.w;
+        }
+        const float sac = sa[ctok[q] * nch + cc];
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+          const float pr = dot_chunk_u4(cb.w[r], xa);
+          const float zp = (float)((cb.z[r] >> ((blk & 1) * 4)) & 0xfu);
+          const float nv = fmaf((float)cb.s[r], fmaf(-zp, sac, 512.0f * pr), acc[q][r]);
+          acc[q][r] = cv ? nv : acc[q][r];
+        }
+      }
+    }
+    if (live && cit == iters - 1) {
+#pragma unroll
+      for (int q = 0; q < MS; ++q) {
+        if (q < ccnt) {
+#pragma unroll
+          for (int r = 0; r < RI; ++r) {
+            const float g = group_sum(acc[q][2 * r], LPR);
+            const float u = group_sum(acc[q][2 * r + 1], LPR);
+            if (lp == 0) {
+              const int lr = (cgrp - g_begin) * rpg + r * SUBS + sub;
+              outs[(lr * MS + q) * 2] = g;
+              outs[(lr * MS + q) * 2 + 1] = u;
+            }
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < NR; ++r) acc[q][r] = 0.0f;
+      }
+    }
+    if (++cit == iters) {
+      cit = 0;
+      cgrp += NW;
+      set_cgroup(cgrp);
+    }
+  };
+
+  MoeItem<NR> buf[D];
+  set_group(fgrp);
+  set_cgroup(cgrp);
+  stage_f32_first(a.X, T, (int)a.H, nch, xf, sa, [&] {
+#pragma unroll
+    for (int i = 0; i < D - 1; ++i) fetch(buf[i]);
+  });
+  const int total = wave_groups * iters;
+  for (int base = 0; base < total; base += D) {
+#pragma unroll
+    for (int i = 0; i < D; ++i) step(buf[i], buf[(i + D - 1) % D], base + i < total);
+  }
+  __syncthreads();
+  // bias and SwiGLU for every slot of every row of the work-group's groups
+  const int nloc = (g_end - g_begin) * rpg;
+  for (int q2 = threadIdx.x; q2 < nloc * MS; q2 += blockDim.x) {
+    const int lr = q2 / MS, q = q2 - lr * MS;
+    const int grp = g_begin + lr / rpg;
+    const int v = grp / GI;
+    const int i = (grp - v * GI) * rpg + (lr - (lr / rpg) * rpg);
+    if (i >= I || q >= vcnt[v]) continue;
+    const int sl = ulist[vstart[v] + q];
+    float g = outs[(lr * MS + q) * 2], uu = outs[(lr * MS + q) * 2 + 1];
+    if (a.fc1.bias) {
+      const uint16_t* bb = a.fc1.bias + (int64_t)vexp[v] * 2 * a.I;
+      g += f16_to_f32(bb[i]);
+      uu += f16_to_f32(bb[i + a.I]);
+    }
+    const float hv = g / (1.0f + expf(-g)) * uu;
+    a.h[(int64_t)sl * a.I + i] = f32_to_f16(hv);
+  }
+}
+
 // ---- single-launch form (fp mode) ------------------------------------------------------
 //
 // fc1, SwiGLU, fc2 and the combine in one launch of the persistent forms above: one
@@ -1234,6 +1493,27 @@ static bool launch_fused(const QmoeArgs& a, hipStream_t st) {
   return true;
 }
 
+template <int RI, int ZK>
+static bool launch_fc1_dedupe(const QmoeArgs& a, hipStream_t st) {
+  auto kern = qmoe_fc1_dedupe_kernel<RI, ZK>;
+  if (a.mode != QMOE_FP || a.T < 2 || a.T > kDedupeMaxT || a.T * a.k > kMoeSortSlots) return false;
+  const int64_t erows = 2 * a.I;
+  if (erows * a.fc1_row_bytes >= (1LL << 31) || erows * a.fc1_nblk * 2 >= (1LL << 31)) return false;
+  const int64_t rpg = (64 >> a.fc1_lpr_log2) * RI;
+  // group count at its largest (every slot its own expert); the kernel deals the
+  // actual groups, never more
+  const int64_t ngroups = a.T * a.k * ((a.I + rpg - 1) / rpg);
+  const size_t fixed = (size_t)a.T * a.fc1_chunks * 33 * sizeof(float) + (size_t)kDedupeInts * sizeof(int);
+  int64_t grid = 0;
+  size_t lds = 0;
+  if (!moe_stream_plan(kern, ngroups, fixed, (size_t)rpg * kDedupeMaxT * 2 * sizeof(float), a.num_cus, 1,
+                       &grid, &lds))
+    return false;
+  allow_lds(kern, lds);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kMoeStreamThreads), lds, st, a);
+  return true;
+}
+
 bool qmoe_fused_plan(QmoeArgs& a, int candidate) {
   if (a.mode != QMOE_FP || candidate < 0 || candidate >= kNumQmoeFused) return false;
   a.f_r2 = kQmoeFusedR2[candidate % 2];
@@ -1265,6 +1545,12 @@ hipError_t launch_qmoe_fused(const QmoeArgs& a, hipStream_t st) {
 
 hipError_t launch_qmoe_fc1(const QmoeArgs& a, int candidate, hipStream_t st) {
   const int rows_per_lane = candidate & 15;
+  if (candidate & kQmoeDedupe) {
+    bool done;
+    if (rows_per_lane == 1) done = a.fc1.zp ? launch_fc1_dedupe<1, 1>(a, st) : launch_fc1_dedupe<1, 0>(a, st);
+    else done = a.fc1.zp ? launch_fc1_dedupe<2, 1>(a, st) : launch_fc1_dedupe<2, 0>(a, st);
+    if (done) return hipSuccess;
+  }
   if (!(candidate & kQmoePerSlot)) {
     const bool zk = a.fc1.zp != nullptr;
     bool done;

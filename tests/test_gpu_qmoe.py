@@ -286,3 +286,34 @@ def test_repeat_calls_bit_identical_fp(form):
     finally:
         Q.set_tuning(0, 0)
     assert O.rel_l2(first.view(np.float16).astype(np.float64), d.oracle(Q.QMOE_FP)) <= TOL["f16"]
+
+
+@pytest.mark.parametrize("routing", ["shared", "one-expert"])
+def test_experts_read_once_same_bits(routing):
+    """The fc1 form that reads each expert's rows once for all its slots gives the bits of
+    the per-slot forms: tokens that share all their experts, and every slot on one expert
+    (repeated inside a token, so its 32 slots are split into units of 8)."""
+    t = torch()
+    T, H, I, E, k = 8, 1024, 512, 16, 4
+    p = gen.qmoe_problem(T, H, I, E, k, 64, seed=930, zp=True, bias=True)
+    if routing == "shared":
+        p["ids"] = np.tile(np.array([[3, 9, 0, 14]], dtype=np.int32), (T, 1))
+    else:
+        p["ids"] = np.full((T, k), 5, dtype=np.int32)
+    d = MoeDev(p)
+    n1 = Q.num_candidates(Q.ENTRY_QMOE_FC1)
+    once = n1 - 1          # fc1 candidate: experts read once (the last one)
+    per_slot = 2           # per-slot form, one row per lane
+    outs = []
+    try:
+        for fc1, fc2 in ((per_slot, per_slot), (once, 0), (once, per_slot)):
+            Q.set_tuning(2, fc1 + n1 * fc2)
+            outs.append(host_bits(d.run(Q.QMOE_FP)).copy())
+    finally:
+        Q.set_tuning(0, 0)
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+    err = O.rel_l2(outs[0].view(np.float16).astype(np.float64), d.oracle(Q.QMOE_FP))
+    say(f"  {routing} relL2={err:.3e}")
+    assert err <= TOL["f16"]
+    t.cuda.synchronize()
