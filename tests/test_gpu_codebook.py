@@ -104,6 +104,8 @@ def test_codebook_repeat_bit_identical():
     (9, 1000, 300, 32, "bf16"),     # ragged K (last stage half padding), ragged N tile
     (33, 4096, 257, 64, "f16"),
     (300, 200, 64, 256, "bf16"),    # one block longer than K, two M tiles
+    (64, 96, 5, 32, "f16"),         # skinny path: ragged N, K of three blocks
+    (16, 4096, 1024, 64, "bf16"),   # skinny path with the reduction split
 ])
 def test_codebook_matrix_core_ragged(M, K, N, block, a_dtype):
     """M > 8 runs the matrix-core path; ragged M, N, K and a bias."""

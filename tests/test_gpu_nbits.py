@@ -252,6 +252,8 @@ def test_phi4_u2_prefill_full_size(name):
     (48, 4096, 4096, 4, 128, "none", "f16", "f32"),
     (40, 5120, 7680, 2, 64, "f16_uniform", "f32", "f32"),   # phi4 qkv shape, a few tokens
     (25, 2880, 33, 4, 32, "packed8", "f32", "f16"),
+    (9, 64, 1, 4, 32, "packed", "f32", "f32"),              # one column, one K step
+    (64, 33, 17, 2, 32, "none", "f16", "f16"),              # one-code last block
 ])
 def test_prefill_small_shapes(M, K, N, bits, block, zp, a, c):
     say(f"prefill M={M} K={K} N={N} bits={bits} block={block} zp={zp} a={a} c={c}")
