@@ -40,9 +40,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--legs", default="decode,stack,prefill,qmoe,codebook",
-                    help="comma list of decode,stack,prefill,qmoe,codebook "
-                         "(copycal: a plain copy for counter calibration)")
+    ap.add_argument("--legs", default="decode,stack,prefill,qmoe,codebook,ceilings",
+                    help="comma list of decode,stack,prefill,qmoe,codebook,ceilings "
+                         "(copycal: a plain copy for counter calibration; nsweep: the GEMV "
+                         "at N around the gate_up and lm_head widths)")
     ap.add_argument("--decode-shapes", default="qkv,gate_up,down,lm_head",
                     help="subset of the phi4 layers in the decode step (profiling runs)")
     return ap.parse_args()
@@ -486,6 +487,98 @@ def cpu_baseline():
             "samples": {"1_thread": runs[1], f"{all_cores}_threads": runs[all_cores]}}
 
 
+def ceilings_leg(reps=20):
+    """Achievable ceilings on this GPU, next to the spec peaks: a device copy and a
+    sum reduction (torch kernels) over the lm_head weight bytes, rotated over copies
+    that together exceed the last-level cache, and an fp16 matrix product through
+    torch.matmul (hipBLASLt) at the phi4 qkv and lm_head shapes, M = 2048."""
+    import torch
+    nbytes = int(weight_bytes_nbits(5120, 100352)) // 256 * 256
+    copies = 8
+    bufs = [torch.ones(nbytes, dtype=torch.uint8, device="cuda") for _ in range(copies)]
+    dsts = [torch.empty_like(b) for b in bufs]
+    out = {"bytes": nbytes}
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, n):
+        for i in range(copies):
+            fn(i)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(n):
+            fn(i % copies)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n  # us per call
+
+    us = timed(lambda i: dsts[i].copy_(bufs[i]), reps)
+    out["copy_read_plus_write_GBps"] = round(2 * nbytes / (us * 1e-6) / 1e9, 1)
+    views = [b.view(torch.int64) for b in bufs]
+    us = timed(lambda i: views[i].sum(), reps)
+    out["sum_read_GBps"] = round(nbytes / (us * 1e-6) / 1e9, 1)
+    del bufs, dsts, views
+    mm = {}
+    for name, (K, N) in (("qkv", (5120, 7680)), ("lm_head", (5120, 100352))):
+        a = torch.randn((2048, K), device="cuda", dtype=torch.float16)
+        b = torch.randn((K, N), device="cuda", dtype=torch.float16)
+        c = torch.empty((2048, N), device="cuda", dtype=torch.float16)
+        us = timed(lambda i: torch.matmul(a, b, out=c), 5)
+        mm[name] = {"M": 2048, "K": K, "N": N, "us": round(us, 1),
+                    "TFLOPs": round(2 * 2048 * K * N / (us * 1e-6) / 1e12, 1)}
+        del a, b, c
+    out["fp16_matmul_hipblaslt"] = mm
+    torch.cuda.empty_cache()
+    return out
+
+
+def n_sweep_leg(reps=5, copies=3):
+    """The 2-bit GEMV (M = 1, K = 5120) at N around the gate_up and lm_head widths, in
+    steps of 16 rows, to expose memory-channel outliers."""
+    import torch
+    from gemm_qmm_nbits_amd import qmm as Q
+    g = torch.Generator(device="cuda")
+    g.manual_seed(77)
+    res = []
+    stream = torch.cuda.current_stream()
+    for N0 in (35840, 100352):
+        for d in (-128, -64, -32, -16, 0, 16, 32, 64, 128):
+            N, K = N0 + d, 5120
+            sets = []
+            for _ in range(copies):
+                W = torch.randint(0, 256, (N, 80 * 16), dtype=torch.uint8, device="cuda", generator=g)
+                S = (torch.rand((N, 80), device="cuda", generator=g) * 0.04 + 0.01).half()
+                A = torch.randn((1, K), device="cuda", generator=g)
+                C = torch.empty((1, N), device="cuda")
+                sets.append((A, W, S, C))
+            for (A, W, S, C) in sets:   # first call of the shape: up-front tiling choice
+                Q.qmm_nbits(A, W, S, K, 2, 64, None, Q.QMM_ZP_UNIFORM, 1.5, out=C)
+            torch.cuda.synchronize()
+            cap = torch.cuda.Stream()
+            with torch.cuda.stream(cap):
+                gr = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(gr, stream=cap):
+                    for (A, W, S, C) in sets:
+                        Q.qmm_nbits(A, W, S, K, 2, 64, None, Q.QMM_ZP_UNIFORM, 1.5, out=C)
+            torch.cuda.synchronize()
+            gr.replay()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                gr.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / (reps * copies)
+            b = weight_bytes_nbits(K, N)
+            res.append({"N": N, "us": round(us, 2), "GBps": round(b / (us * 1e-6) / 1e9, 1)})
+            del sets, gr
+            torch.cuda.empty_cache()
+    return res
+
+
 def copy_calibration(nbytes=256 << 20, calls=5):
     """A plain device copy of known size, for scaling the HBM byte counters."""
     import torch
@@ -573,6 +666,10 @@ def main():
         out["codebook"] = codebook_leg(args)
     if "copycal" in legs:
         out["copy_calibration"] = copy_calibration()
+    if "ceilings" in legs:
+        out["ceilings"] = ceilings_leg()
+    if "nsweep" in legs:
+        out["n_sweep"] = n_sweep_leg()
     if "qmoe" in legs:
         q = []
         q.append(qmoe_leg(args, "gpt-oss-20b", 1, 2880, 2880, 32, 4, 64, False, False, Q.QMOE_FP))
