@@ -225,7 +225,7 @@ def stack_leg(args, layers=40, reps=10):
 def codebook_leg(args, reps=5):
     """Weight GB/s of qmm_codebook4 at the four codebook shapes for M = 1, 4, 16, 64:
     bf16 A and C, block 64, weights rotated over copies >= 1 GiB, each shape's calls
-    captured in one HIP graph (M <= 8: weight-streaming GEMV; M > 8: matrix cores)."""
+    captured in one HIP graph (M = 1: weight-streaming GEMV; M >= 4: matrix cores)."""
     import torch
     from gemm_qmm_nbits_amd import inputs as gen
     from gemm_qmm_nbits_amd import qmm as Q
@@ -275,7 +275,7 @@ def codebook_leg(args, reps=5):
             gbs = wbytes / (us * 1e-6) / 1e9
             out[f"{name} M={M}"] = {"K": K, "N": N, "M": M, "us": round(us, 2), "weight_GBps": round(gbs, 1),
                                     "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
-                                    "path": "gemv" if M <= 8 else "matrix cores"}
+                                    "path": "gemv" if M < 4 else "matrix cores"}
             del gr
         del Ws, ams
         torch.cuda.empty_cache()

@@ -39,6 +39,31 @@ size_t dtype_size(int t) { return t == QMM_F32 ? 4 : 2; }
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Codebook weights with a 16-bit output: from this M on, the skinny matrix-core kernel
+// beats the fp32 GEMV (it dequantizes each weight once for up to 16 rows), and its fp16
+// operand rounding stays far below the output's own rounding.
+constexpr int kCbSkinnyMinM = 4;
+
+// Workspace of the matrix-core paths: A as fp16 rows of K rounded up to 64, then the
+// fp32 partial sums of a split reduction.
+size_t matrix_workspace_bytes(int64_t M, int64_t K, int64_t N) {
+  const int64_t kp = (K + 63) / 64 * 64;
+  const size_t a16 = ((size_t)M * (size_t)kp * 2 + 255) & ~size_t(255);
+  const int splits = prefill_splits(M, N, kp);
+  const size_t part = splits > 1 ? (size_t)splits * (size_t)M * (size_t)N * 4 : 0;
+  return a16 + part;
+}
+
+// Whether qmm_codebook4 takes a matrix-core path (A rounded to fp16 in the workspace).
+bool codebook_on_matrix_cores(int64_t M, int64_t K, int64_t N, int block, int c_type) {
+  if (M <= 0 || K <= 0 || N <= 0) return false;
+  if (M > kMaxGemvM) return true;
+  if (M < kCbSkinnyMinM || c_type == QMM_F32) return false;
+  const int64_t Kp = (K + 63) / 64 * 64;
+  const int64_t nblk = ceil_div(K, block);
+  return skinny_applies(M, N, Kp, block, nblk * block / 2, nblk);
+}
+
 int device_cus() {
   static int cus[64] = {0};
   int dev = 0;
@@ -576,7 +601,9 @@ qmm_status check_codebook(const void* A, int a_type, int64_t M, int64_t K, int64
       !aligned(codebook, 4))
     return QMM_E_ALIGN;
   if (bias && !aligned(bias, dtype_size(c_type))) return QMM_E_ALIGN;
-  const size_t need = qmm_codebook4_workspace_bytes(M, K, N, a_type);
+  const size_t need = codebook_on_matrix_cores(M, K, N, block, c_type)
+                          ? qmm_codebook4_workspace_bytes(M, K, N, a_type)
+                          : 0;
   if (need > 0 && (!workspace || workspace_bytes < need)) return QMM_E_WORKSPACE;
   return QMM_OK;
 }
@@ -699,16 +726,15 @@ size_t qmm_nbits_workspace_bytes(int64_t M, int64_t K, int64_t N, int a_type) {
   // do not fill the chip the reduction is split and fp32 partial sums follow A
   (void)a_type;
   if (M <= kMaxGemvM || M <= 0 || K <= 0 || N <= 0) return 0;
-  const int64_t kp = (K + 63) / 64 * 64;
-  const size_t a16 = ((size_t)M * (size_t)kp * 2 + 255) & ~size_t(255);
-  const int splits = prefill_splits(M, N, kp);
-  const size_t part = splits > 1 ? (size_t)splits * (size_t)M * (size_t)N * 4 : 0;
-  return a16 + part;
+  return matrix_workspace_bytes(M, K, N);
 }
 
 size_t qmm_codebook4_workspace_bytes(int64_t M, int64_t K, int64_t N, int a_type) {
-  // M > 8 runs the matrix-core path, with the workspace of qmm_nbits
-  return qmm_nbits_workspace_bytes(M, K, N, a_type);
+  // the matrix-core paths take the workspace of qmm_nbits: M > 8, and 4 <= M <= 8 with
+  // a 16-bit output (the output type is not an argument, so the size covers that case)
+  (void)a_type;
+  if (M < kCbSkinnyMinM || K <= 0 || N <= 0) return 0;
+  return matrix_workspace_bytes(M, K, N);
 }
 
 // Start of the fp32 partial sums inside the prefill workspace.
@@ -799,7 +825,7 @@ qmm_status qmm_codebook4(const void* A, int a_type, int64_t M, int64_t K, int64_
   if (s != QMM_OK) return s;
   if (M == 0 || N == 0) return QMM_OK;
   hipStream_t st = (hipStream_t)stream;
-  if (M > kMaxGemvM && K > 0) {
+  if (codebook_on_matrix_cores(M, K, N, block, c_type)) {
     // matrix-core path: A -> padded fp16 once, W16 = fp16(codebook[q] * absmax) per tile
     PrefillArgs p{};
     const int64_t Kp = (K + 63) / 64 * 64;
@@ -855,9 +881,10 @@ qmm_status qmm_fp16_uniform_value(const uint16_t* zp, int64_t count, void* scrat
   if (scratch_bytes < qmm_uniform_scratch_bytes()) return QMM_E_WORKSPACE;
   if (!aligned(zp, 2) || !aligned(scratch, 4)) return QMM_E_ALIGN;
   hipStream_t st = (hipStream_t)stream;
-  launch_uniform_check(zp, count, (uint32_t*)scratch, st);
+  hipError_t e = launch_uniform_check(zp, count, (uint32_t*)scratch, st);
+  if (e != hipSuccess) return (qmm_status)e;
   uint32_t res[2] = {0, 0};
-  hipError_t e = hipMemcpyAsync(res, scratch, sizeof(res), hipMemcpyDeviceToHost, st);
+  e = hipMemcpyAsync(res, scratch, sizeof(res), hipMemcpyDeviceToHost, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   if (e != hipSuccess) return (qmm_status)e;
   *is_uniform = res[0] ? 1 : 0;
@@ -893,7 +920,8 @@ qmm_status qmm_dequantize_nbits(const uint8_t* W, int bits, int block, const uin
   d.zp_row_bytes = ceil_div(d.nblk * bits, 8);
   d.out = out;
   d.out_type = out_type;
-  launch_dequant(d, (hipStream_t)stream);
+  const hipError_t e = launch_dequant(d, (hipStream_t)stream);
+  if (e != hipSuccess) return (qmm_status)e;
   return (qmm_status)hipGetLastError();
 }
 
@@ -919,7 +947,8 @@ qmm_status qmm_dequantize_codebook4(const uint8_t* W, int block, const float* ab
   d.codebook = codebook;
   d.out = out;
   d.out_type = out_type;
-  launch_dequant(d, (hipStream_t)stream);
+  const hipError_t e = launch_dequant(d, (hipStream_t)stream);
+  if (e != hipSuccess) return (qmm_status)e;
   return (qmm_status)hipGetLastError();
 }
 

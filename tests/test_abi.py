@@ -90,18 +90,18 @@ def _splits(M, N, kp):
 
 @pytest.mark.parametrize("M,K,N", [(16, 4096, 14336), (64, 4096, 1024), (2048, 17920, 5120),
                                    (2048, 5120, 7680), (2048, 5120, 100352), (9, 70, 33),
-                                   (8, 4096, 4096)])
+                                   (8, 4096, 4096), (4, 4096, 14336), (3, 4096, 1024)])
 def test_workspace_sizes(M, K, N):
-    """Padded fp16 A plus the fp32 partial sums of a split reduction."""
+    """Padded fp16 A plus the fp32 partial sums of a split reduction: qmm_nbits from
+    M = 9 on, qmm_codebook4 from M = 4 on (its 16-bit outputs take the skinny kernel)."""
     need = Q.lib().qmm_nbits_workspace_bytes(M, K, N, Q.QMM_BF16)
-    assert need == Q.lib().qmm_codebook4_workspace_bytes(M, K, N, Q.QMM_BF16)
-    if M <= 8:
-        assert need == 0
-        return
+    need_cb = Q.lib().qmm_codebook4_workspace_bytes(M, K, N, Q.QMM_BF16)
     kp = -(-K // 64) * 64
     a16 = -(-M * kp * 2 // 256) * 256
     s = _splits(M, N, kp)
-    assert need == a16 + (s * M * N * 4 if s > 1 else 0)
+    full = a16 + (s * M * N * 4 if s > 1 else 0)
+    assert need == (0 if M <= 8 else full)
+    assert need_cb == (0 if M < 4 else full)
 
 
 def _v_cb(**kw):
@@ -120,6 +120,14 @@ def test_validate_codebook_codes():
     assert _v_cb(absmax=FAKE + 2) == -6
     assert _v_cb(a_type=5) == -2
     assert _v_cb(N=-3) == -5
+    # 4 <= M <= 8: the workspace is needed for a 16-bit output only
+    assert _v_cb(M=4) == -7
+    assert _v_cb(M=4, c_type=Q.QMM_F32) == 0
+    assert _v_cb(M=4, block=16) == 0
+    assert _v_cb(M=3) == 0
+    need = Q.lib().qmm_codebook4_workspace_bytes(4, 4096, 1024, Q.QMM_BF16)
+    assert _v_cb(M=4, ws=FAKE, wsb=need) == 0
+    assert _v_cb(M=4, ws=FAKE, wsb=need - 1) == -7
 
 
 def _v_moe(**kw):

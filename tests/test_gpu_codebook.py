@@ -11,6 +11,13 @@ from gpu_util import TOL, dev, dev_act, host_bits, host_f64, sample_rows, say, t
 pytestmark = pytest.mark.gpu
 
 
+def cb_matrix_path(M, block, out_dtype):
+    """Whether qmm_codebook4 takes a matrix-core path: M > 8, or 4 <= M <= 8 with a
+    16-bit output and blocks of at least 32 codes (the skinny kernel)."""
+    t = torch()
+    return M > 8 or (M >= 4 and block >= 32 and out_dtype in (t.float16, t.bfloat16))
+
+
 class CbDev:
     def __init__(self, p):
         t = torch()
@@ -35,14 +42,14 @@ class CbDev:
                                a_round=a_round)
 
     def check(self, y, rows=None, label=""):
-        """M <= 8: the GEMV against the exact oracle.  M > 8: the matrix-core path against
-        the oracle with its declared operand roundings (A and W to fp16); the error against
-        the exact oracle is printed for information."""
+        """GEMV path: against the exact oracle.  Matrix-core path: against the oracle
+        with its declared operand roundings (A and W to fp16); the error against the exact
+        oracle is printed for information."""
         got = host_f64(y)
         if rows is not None:
             got = got[:, rows]
         tol = TOL[self.p["a_dtype"]]
-        if self.p["A"].shape[0] > 8:
+        if cb_matrix_path(self.p["A"].shape[0], self.p["block"], y.dtype):
             err = O.rel_l2(got, self.oracle(rows=rows, a_round="f16", w_round="f16"))
             raw = O.rel_l2(got, self.oracle(rows=rows))
             say(f"  {label} relL2(mirrored)={err:.3e} relL2(exact)={raw:.3e}")
@@ -86,8 +93,30 @@ def test_codebook_config_shapes(name, M, a_dtype):
 def test_codebook_ragged_bias(M):
     p = gen.codebook_problem(M, 1000, 300, seed=55 + M, a_dtype="bf16", block=32, bias=True)
     d = CbDev(p)
-    err = O.rel_l2(host_f64(d.run()), d.oracle())
-    assert err <= TOL["bf16"], err
+    d.check(d.run(), label=f"M={M}")
+
+
+@pytest.mark.parametrize("M,out", [(4, "same"), (5, "same"), (7, "same"), (8, "same"),
+                                   (4, "f32"), (8, "f32")])
+def test_codebook_small_m_paths(M, out):
+    """4 <= M <= 8: a 16-bit output takes the skinny kernel (gate: the oracle with fp16
+    operands; the reduction is split at this width); an fp32 output keeps the GEMV
+    (gate: the exact oracle at the fp32 tolerance)."""
+    t = torch()
+    p = gen.codebook_problem(M, 4096, 1024, seed=58 + M, a_dtype="bf16", block=64,
+                             bias=(out == "same"))
+    d = CbDev(p)
+    if out == "f32":
+        y = Q.qmm_codebook4(d.A, d.W, d.absmax, d.cb, p["K"], p["block"], None,
+                            out_dtype=t.float32)
+        assert not cb_matrix_path(M, p["block"], y.dtype)
+        err = O.rel_l2(host_f64(y), d.oracle())
+        say(f"  M={M} fp32 out relL2={err:.3e}")
+        assert err <= TOL["f32"], err
+    else:
+        y = d.run()
+        assert cb_matrix_path(M, p["block"], y.dtype)
+        d.check(y, label=f"M={M} bf16 out")
 
 
 def test_codebook_repeat_bit_identical():
