@@ -4,17 +4,17 @@
 
 namespace qmm {
 
-template <int FMT, int BITS, int AT>
-hipError_t launch_at_type(const GemvArgs& g, int R, hipStream_t st);
+template <int AT>
+hipError_t launch_cb_at_type(const GemvArgs& g, int R, hipStream_t st);
 template <int BITS, int AT>
 hipError_t launch_ip_at_type(const GemvArgs& g, int R, hipStream_t st);
 
-// codebook weights: fp32 kernel with the LDS centroid table
+// codebook weights: fp32 kernels with the LDS centroid table
 static hipError_t launch_codebook(const GemvArgs& g, int R, hipStream_t st) {
   switch (g.a_type) {
-    case QMM_F32: return launch_at_type<GEMV_CODEBOOK, 4, QMM_F32>(g, R, st);
-    case QMM_F16: return launch_at_type<GEMV_CODEBOOK, 4, QMM_F16>(g, R, st);
-    default: return launch_at_type<GEMV_CODEBOOK, 4, QMM_BF16>(g, R, st);
+    case QMM_F32: return launch_cb_at_type<QMM_F32>(g, R, st);
+    case QMM_F16: return launch_cb_at_type<QMM_F16>(g, R, st);
+    default: return launch_cb_at_type<QMM_BF16>(g, R, st);
   }
 }
 

@@ -1,6 +1,6 @@
-// Instantiation of the GEMV kernels for one weight format and activation type.
-#include "qmm_gemv_impl.h"
+// Instantiation of the codebook GEMV kernels for one activation type.
+#include "qmm_gemv_cb_stream.h"
 
 namespace qmm {
-template hipError_t launch_at_type<GEMV_CODEBOOK, 4, QMM_BF16>(const GemvArgs& g, int R, hipStream_t st);
+template hipError_t launch_cb_at_type<QMM_BF16>(const GemvArgs& g, int R, hipStream_t st);
 }  // namespace qmm
