@@ -119,6 +119,29 @@ def test_codebook_small_m_paths(M, out):
         d.check(y, label=f"M={M} bf16 out")
 
 
+@pytest.mark.parametrize("M,K,N,block,out", [
+    (1, 20480, 300, 64, "same"),   # A does not fit in LDS: the general kernel, K in slices
+    (2, 20480, 77, 64, "f32"),     # the same with two A rows and an fp32 output
+    (4, 12288, 64, 64, "f32"),     # four A rows, six slices
+    (1, 2000, 129, 16, "same"),    # 16-code blocks: two absmax values per chunk (general kernel)
+    (1, 4096, 1, 64, "same"),      # streaming form, one output row
+    (1, 64, 5, 64, "same"),        # streaming form, K of two chunks (most lanes idle)
+    (3, 4096, 1000, 128, "f32"),   # streaming form, three A rows, 128-code blocks
+])
+def test_codebook_gemv_forms(M, K, N, block, out):
+    """M <= 8 GEMV paths the configuration shapes do not reach, against the exact oracle."""
+    t = torch()
+    p = gen.codebook_problem(M, K, N, seed=59 + K + N, a_dtype="bf16", block=block,
+                             bias=(out == "same"))
+    d = CbDev(p)
+    od = None if out == "same" else t.float32
+    y = Q.qmm_codebook4(d.A, d.W, d.absmax, d.cb, K, block, d.bias, out_dtype=od)
+    assert not cb_matrix_path(M, block, y.dtype)
+    err = O.rel_l2(host_f64(y), d.oracle())
+    say(f"  M={M} K={K} N={N} block={block} {out}: relL2={err:.3e}")
+    assert err <= (TOL["f32"] if out == "f32" else TOL["bf16"]), err
+
+
 def test_codebook_repeat_bit_identical():
     p = gen.codebook_problem(4, 4096, 4096, seed=56, a_dtype="f16")
     d = CbDev(p)
