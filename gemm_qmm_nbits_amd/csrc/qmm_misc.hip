@@ -99,11 +99,65 @@ __global__ __launch_bounds__(256) void cast_pad_f16_kernel(const void* src, int 
   }
 }
 
+// Same result for K a multiple of 8 and a 16-byte aligned source: a group of 8
+// destination elements then lies wholly inside the row or wholly in the padding, and
+// its source is one or two aligned 16-byte loads (vector loads, no per-element type
+// switch or bounds check).  The conversion is the one above.
+template <int AT>
+__global__ __launch_bounds__(256) void cast_pad_f16_vec_kernel(const void* src, int64_t M, int64_t K,
+                                                               int64_t Kp, uint16_t* dst) {
+  const int64_t per_row = Kp / 8;
+  const int64_t per_src = K / 8;
+  const int64_t total = M * per_row;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t m = i / per_row;
+    const int64_t c = i - m * per_row;
+    uint4 out = make_uint4(0u, 0u, 0u, 0u);
+    if (c < per_src) {
+      const int64_t base = m * K + c * 8;
+      float v[8];
+      if constexpr (AT == QMM_F32) {
+        const f32x4* p = (const f32x4*)((const float*)src + base);
+        const f32x4 a = p[0], b = p[1];
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+      } else {
+        const uint4 u = *(const uint4*)((const uint16_t*)src + base);
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint16_t lo = (uint16_t)(w[e] & 0xffffu), hi = (uint16_t)(w[e] >> 16);
+          v[2 * e] = AT == QMM_F16 ? f16_to_f32(lo) : bf16_to_f32(lo);
+          v[2 * e + 1] = AT == QMM_F16 ? f16_to_f32(hi) : bf16_to_f32(hi);
+        }
+      }
+      out.x = (uint32_t)f32_to_f16(v[0]) | ((uint32_t)f32_to_f16(v[1]) << 16);
+      out.y = (uint32_t)f32_to_f16(v[2]) | ((uint32_t)f32_to_f16(v[3]) << 16);
+      out.z = (uint32_t)f32_to_f16(v[4]) | ((uint32_t)f32_to_f16(v[5]) << 16);
+      out.w = (uint32_t)f32_to_f16(v[6]) | ((uint32_t)f32_to_f16(v[7]) << 16);
+    }
+    ((uint4*)dst)[i] = out;
+  }
+}
+
 hipError_t launch_cast_pad_f16(const void* src, int src_type, int64_t M, int64_t K, int64_t Kp,
                                uint16_t* dst, hipStream_t st) {
   int64_t blocks = (M * (Kp / 8) + 255) / 256;
   if (blocks > 16384) blocks = 16384;
   if (blocks < 1) blocks = 1;
+  if (K % 8 == 0 && (uintptr_t)src % 16 == 0) {
+    if (src_type == QMM_F32)
+      hipLaunchKernelGGL(cast_pad_f16_vec_kernel<QMM_F32>, dim3((unsigned)blocks), dim3(256), 0, st,
+                         src, M, K, Kp, dst);
+    else if (src_type == QMM_F16)
+      hipLaunchKernelGGL(cast_pad_f16_vec_kernel<QMM_F16>, dim3((unsigned)blocks), dim3(256), 0, st,
+                         src, M, K, Kp, dst);
+    else
+      hipLaunchKernelGGL(cast_pad_f16_vec_kernel<QMM_BF16>, dim3((unsigned)blocks), dim3(256), 0, st,
+                         src, M, K, Kp, dst);
+    return hipSuccess;
+  }
   hipLaunchKernelGGL(cast_pad_f16_kernel, dim3((unsigned)blocks), dim3(256), 0, st, src, src_type, M,
                      K, Kp, dst);
   return hipSuccess;
