@@ -302,6 +302,26 @@ def test_skinny_repeat_bit_identical():
         assert np.array_equal(host_bits(out), first), i
 
 
+@pytest.mark.parametrize("M,K,a", [(40, 320, "f32"), (100, 320, "f32"), (40, 512, "bf16"),
+                                   (130, 1024, "f16")])
+def test_prefill_misaligned_activations_same_bits(M, K, a):
+    """The A cast reads 16-byte vectors when A is 16-byte aligned and K is a multiple of
+    8, else element by element: an A that starts off a 16-byte boundary (skinny and tile
+    paths) gives the same bits as an aligned copy."""
+    t = torch()
+    p = gen.nbits_problem(M, K, 96, 4, 32, seed=81 + M, a_dtype=a, zp="packed")
+    d = NbitsDev(p)
+    ref = host_bits(d.run()).copy()
+    n = M * K
+    buf = t.empty(n + 8, dtype=d.A.dtype, device=d.A.device)
+    shifted = buf[1:1 + n].view(M, K)
+    shifted.copy_(d.A)
+    assert shifted.data_ptr() % 16 != 0
+    got = host_bits(d.run(A=shifted))
+    assert np.array_equal(got, ref)
+    _check_prefill(d, d.run(), label=f"M={M} K={K} {a}")
+
+
 def test_empty_and_degenerate():
     t = torch()
     p = gen.nbits_problem(3, 256, 8, 4, 64, seed=9, zp="packed8", bias=True)
