@@ -258,7 +258,11 @@ void sk_mb(const PrefillArgs& p, hipStream_t st) {
     cus = 256;
   }
   if (p.M <= 16) {
+    // one strip while the work-groups fit in one round; else four strips when that
+    // still leaves three quarters of the compute units a work-group (one round, where
+    // two strips would take nearly two), else two
     if ((p.N + 15) / 16 <= cus) sk_launch<FMT, BITS, ZK, CT, 1, 1>(p, st);
+    else if ((p.N + 63) / 64 * 4 >= 3 * (int64_t)cus) sk_launch<FMT, BITS, ZK, CT, 1, 4>(p, st);
     else sk_launch<FMT, BITS, ZK, CT, 1, 2>(p, st);
   } else {
     // four strips (half the activation reads per matrix-core step) while that still
