@@ -298,11 +298,13 @@ bool skinny_applies(int64_t M, int64_t N, int64_t Kp, int block, int64_t row_byt
 
 int skinny_splits(int64_t M, int64_t N, int64_t Kp) {
   // Split the reduction while the grid stays within one work-group per compute unit
-  // of a 256-CU device (work-groups counted as the launch deals strips: one per
-  // work-group for a single M tile when N / 16 <= 256, else two) and every wave of a
-  // split keeps at least one step; powers of two up to 8.  The partial sums go to the
-  // workspace, which holds prefill_splits(M, N, Kp) of them.
-  const int64_t wgs = (M <= 16 && (N + 15) / 16 <= 256) ? (N + 15) / 16 : (N + 31) / 32;
+  // of a 256-CU device (work-groups counted as the launch deals strips on such a
+  // device) and every wave of a split keeps at least one step; powers of two up to 8.
+  // The partial sums go to the workspace, which holds prefill_splits(M, N, Kp) of them.
+  const bool wide = (N + 63) / 64 * 4 >= 3 * 256;
+  const int64_t wgs = (M <= 16 && (N + 15) / 16 <= 256) ? (N + 15) / 16
+                      : wide                             ? (N + 63) / 64
+                                                         : (N + 31) / 32;
   const int64_t nsteps = (Kp + SK_STEP - 1) / SK_STEP;
   const int64_t cap = prefill_splits(M, N, Kp);
   int s = 1;
