@@ -266,13 +266,18 @@ void sk_mb(const PrefillArgs& p, hipStream_t st) {
     else sk_launch<FMT, BITS, ZK, CT, 1, 2>(p, st);
   } else {
     // four strips (half the activation reads per matrix-core step) while that still
-    // leaves at least three quarters of the compute units a work-group
+    // leaves at least three quarters of the compute units a work-group; one strip for
+    // narrow outputs (N / 16 work-groups within half the compute units), whose split
+    // reduction then fills the device; else two
     const bool wide = (p.N + 63) / 64 * 4 >= 3 * (int64_t)cus;
+    const bool narrow = (p.N + 15) / 16 * 2 <= (int64_t)cus;
     if (p.M <= 32) {
       if (wide) sk_launch<FMT, BITS, ZK, CT, 2, 4>(p, st);
+      else if (narrow) sk_launch<FMT, BITS, ZK, CT, 2, 1>(p, st);
       else sk_launch<FMT, BITS, ZK, CT, 2, 2>(p, st);
     } else {
       if (wide) sk_launch<FMT, BITS, ZK, CT, 4, 4>(p, st);
+      else if (narrow) sk_launch<FMT, BITS, ZK, CT, 4, 1>(p, st);
       else sk_launch<FMT, BITS, ZK, CT, 4, 2>(p, st);
     }
   }
@@ -302,8 +307,10 @@ int skinny_splits(int64_t M, int64_t N, int64_t Kp) {
   // device) and every wave of a split keeps at least one step; powers of two up to 8.
   // The partial sums go to the workspace, which holds prefill_splits(M, N, Kp) of them.
   const bool wide = (N + 63) / 64 * 4 >= 3 * 256;
+  const bool narrow = (N + 15) / 16 * 2 <= 256;
   const int64_t wgs = (M <= 16 && (N + 15) / 16 <= 256) ? (N + 15) / 16
                       : wide                             ? (N + 63) / 64
+                      : narrow                           ? (N + 15) / 16
                                                          : (N + 31) / 32;
   const int64_t nsteps = (Kp + SK_STEP - 1) / SK_STEP;
   const int64_t cap = prefill_splits(M, N, Kp);
