@@ -268,9 +268,12 @@ void sk_mb(const PrefillArgs& p, hipStream_t st) {
     // four strips (half the activation reads per matrix-core step) while that still
     // leaves at least three quarters of the compute units a work-group; one strip for
     // narrow outputs (N / 16 work-groups within half the compute units), whose split
-    // reduction then fills the device; else two
+    // reduction then fills the device, and for reductions too short to split when N / 16
+    // work-groups fit on the compute units; else two
     const bool wide = (p.N + 63) / 64 * 4 >= 3 * (int64_t)cus;
-    const bool narrow = (p.N + 15) / 16 * 2 <= (int64_t)cus;
+    const int64_t nsteps = (p.Kp + SK_STEP - 1) / SK_STEP;
+    const bool narrow = (p.N + 15) / 16 * 2 <= (int64_t)cus ||
+                        (nsteps < 2 * SK_WAVES && (p.N + 15) / 16 <= (int64_t)cus);
     if (p.M <= 32) {
       if (wide) sk_launch<FMT, BITS, ZK, CT, 2, 4>(p, st);
       else if (narrow) sk_launch<FMT, BITS, ZK, CT, 2, 1>(p, st);
@@ -307,12 +310,12 @@ int skinny_splits(int64_t M, int64_t N, int64_t Kp) {
   // device) and every wave of a split keeps at least one step; powers of two up to 8.
   // The partial sums go to the workspace, which holds prefill_splits(M, N, Kp) of them.
   const bool wide = (N + 63) / 64 * 4 >= 3 * 256;
-  const bool narrow = (N + 15) / 16 * 2 <= 256;
+  const int64_t nsteps = (Kp + SK_STEP - 1) / SK_STEP;
+  const bool narrow = (N + 15) / 16 * 2 <= 256 || (nsteps < 2 * SK_WAVES && (N + 15) / 16 <= 256);
   const int64_t wgs = (M <= 16 && (N + 15) / 16 <= 256) ? (N + 15) / 16
                       : wide                             ? (N + 63) / 64
                       : narrow                           ? (N + 15) / 16
                                                          : (N + 31) / 32;
-  const int64_t nsteps = (Kp + SK_STEP - 1) / SK_STEP;
   const int64_t cap = prefill_splits(M, N, Kp);
   int s = 1;
   while (s < 8 && wgs * s * 2 <= 256 && nsteps >= (int64_t)s * 2 * SK_WAVES && s * 2 <= cap) s *= 2;
