@@ -24,17 +24,27 @@ def sources():
     return sorted(glob.glob(os.path.join(csrc, "*.hip"))) + sorted(glob.glob(os.path.join(csrc, "*.cpp")))
 
 
-def build(verbose: bool = False, jobs: int = 0) -> str:
-    """Compile every source (in parallel) and link libqmm.so; returns its path."""
+def _headers():
+    return glob.glob(os.path.join(PKG, "csrc", "*.h")) + glob.glob(os.path.join(ROOT, "include", "*.h"))
+
+
+def build(verbose: bool = False, jobs: int = 0, incremental: bool = False) -> str:
+    """Compile every source (in parallel) and link libqmm.so; returns its path.
+
+    incremental: recompile only sources newer than their object (or older than any
+    header), for local iteration; the default rebuilds everything."""
     srcs = sources()
     objdir = os.path.join(ROOT, "_build")
     os.makedirs(objdir, exist_ok=True)
     inc = ["-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc")]
+    newest_header = max((os.path.getmtime(h) for h in _headers()), default=0.0)
     procs = []
     objs = []
     for s in srcs:
         o = os.path.join(objdir, os.path.basename(s) + ".o")
         objs.append(o)
+        if incremental and os.path.exists(o) and os.path.getmtime(o) >= max(os.path.getmtime(s), newest_header):
+            continue
         cmd = [HIPCC] + [f for f in FLAGS if f != "-shared"] + inc + ["-c", s, "-o", o]
         if verbose:
             print(" ".join(cmd), flush=True)
@@ -60,4 +70,4 @@ def build(verbose: bool = False, jobs: int = 0) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, incremental="--incremental" in sys.argv))

@@ -44,14 +44,44 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // operand rounding stays far below the output's own rounding.
 constexpr int kCbSkinnyMinM = 4;
 
-// Workspace of the matrix-core paths: A as fp16 rows of K rounded up to 64, then the
-// fp32 partial sums of a split reduction.
-size_t matrix_workspace_bytes(int64_t M, int64_t K, int64_t N) {
+// Workspace of the matrix-core paths: A as fp16 rows of K rounded up to 64, the
+// fp32 row scales of that cast, then the fp32 partial sums of a split reduction (each
+// region starts on a 256-byte boundary).
+struct MatrixWorkspace {
+  size_t a16 = 0, rs = 0, part = 0, total = 0;
+};
+
+MatrixWorkspace matrix_workspace(int64_t M, int64_t K, int64_t N) {
+  MatrixWorkspace w;
   const int64_t kp = (K + 63) / 64 * 64;
-  const size_t a16 = ((size_t)M * (size_t)kp * 2 + 255) & ~size_t(255);
+  w.a16 = 0;
+  w.rs = ((size_t)M * (size_t)kp * 2 + 255) & ~size_t(255);
+  w.part = w.rs + (((size_t)M * 4 + 255) & ~size_t(255));
   const int splits = prefill_splits(M, N, kp);
-  const size_t part = splits > 1 ? (size_t)splits * (size_t)M * (size_t)N * 4 : 0;
-  return a16 + part;
+  w.total = w.part + (splits > 1 ? (size_t)splits * (size_t)M * (size_t)N * 4 : 0);
+  return w;
+}
+
+size_t matrix_workspace_bytes(int64_t M, int64_t K, int64_t N) { return matrix_workspace(M, K, N).total; }
+
+// Matrix-core operands of A: fp16 A is read in place when its rows can be (16-byte
+// aligned, K a multiple of 8 for the skinny kernel, of 64 for the tile kernel);
+// otherwise A is cast into the workspace with the per-row pre-scale.
+hipError_t matrix_activations(PrefillArgs& p, const void* A, int a_type, bool skinny, void* workspace,
+                              hipStream_t st) {
+  const MatrixWorkspace w = matrix_workspace(p.M, p.K, p.N);
+  uint8_t* ws = (uint8_t*)workspace;
+  p.partials = (float*)(ws + w.part);
+  if (a_type == QMM_F16 && aligned(A, 16) && p.K % (skinny ? 8 : 64) == 0) {
+    p.A16 = (const uint16_t*)A;
+    p.lda = p.K;
+    p.row_scale = nullptr;
+    return hipSuccess;
+  }
+  p.A16 = (const uint16_t*)(ws + w.a16);
+  p.lda = p.Kp;
+  p.row_scale = (const float*)(ws + w.rs);
+  return launch_cast_pad_f16(A, a_type, p.M, p.K, p.Kp, (uint16_t*)(ws + w.a16), (float*)(ws + w.rs), st);
 }
 
 // Whether qmm_codebook4 takes a matrix-core path (A rounded to fp16 in the workspace).
@@ -185,6 +215,19 @@ bool ensure_pool(TunerState& t, size_t unit, size_t out_bytes) {
   return true;
 }
 
+// Give the rotation pool and the timing output back once a shape has been timed (the
+// next new shape allocates them again); the timing has synchronized the stream.
+void release_pool(TunerState& t) {
+  if (t.pool) (void)hipFree(t.pool);
+  if (t.out_scratch) (void)hipFree(t.out_scratch);
+  (void)hipGetLastError();
+  t.pool = nullptr;
+  t.pool_bytes = 0;
+  t.pool_cursor = 0;
+  t.out_scratch = nullptr;
+  t.out_scratch_bytes = 0;
+}
+
 // Next cold region of `unit` bytes in the pool (256-byte aligned).
 uint8_t* next_region(TunerState& t, size_t unit) {
   const size_t u = (unit + 255) & ~size_t(255);
@@ -289,6 +332,7 @@ int gemv_choice(int entry, const GemvArgs& g, hipStream_t st) {
     (void)hipEventDestroy(e0);
     (void)hipEventDestroy(e1);
   }
+  release_pool(t);
   t.last_choice[entry] = chosen;
   return kGemvCandidates[chosen];
 }
@@ -605,6 +649,7 @@ qmm_status check_codebook(const void* A, int a_type, int64_t M, int64_t K, int64
                           ? qmm_codebook4_workspace_bytes(M, K, N, a_type)
                           : 0;
   if (need > 0 && (!workspace || workspace_bytes < need)) return QMM_E_WORKSPACE;
+  if (need > 0 && !aligned(workspace, 16)) return QMM_E_ALIGN;
   return QMM_OK;
 }
 
@@ -737,13 +782,6 @@ size_t qmm_codebook4_workspace_bytes(int64_t M, int64_t K, int64_t N, int a_type
   return matrix_workspace_bytes(M, K, N);
 }
 
-// Start of the fp32 partial sums inside the prefill workspace.
-static float* prefill_partials(void* workspace, int64_t M, int64_t K) {
-  const int64_t kp = (K + 63) / 64 * 64;
-  const size_t a16 = ((size_t)M * (size_t)kp * 2 + 255) & ~size_t(255);
-  return (float*)((uint8_t*)workspace + a16);
-}
-
 qmm_status qmm_validate_nbits(const void* A, int a_type, int64_t M, int64_t K, int64_t N,
                               const uint8_t* W, int bits, int block, const uint16_t* scales,
                               const void* zp, int zp_kind, const void* bias, const void* C,
@@ -771,18 +809,14 @@ qmm_status qmm_nbits(const void* A, int a_type, int64_t M, int64_t K, int64_t N,
   if (M == 0 || N == 0) return QMM_OK;
   hipStream_t st = (hipStream_t)stream;
   if (M > kMaxGemvM && K > 0) {
-    // prefill: A -> fp16 once, then the matrix-core tile kernel
+    // prefill: A -> fp16 once (or fp16 A in place), then a matrix-core kernel
     PrefillArgs p{};
     const int64_t Kp = (K + 63) / 64 * 64;
-    hipError_t ce = launch_cast_pad_f16(A, a_type, M, K, Kp, (uint16_t*)workspace, st);
-    if (ce != hipSuccess) return (qmm_status)ce;
-    p.A16 = (const uint16_t*)workspace;
     p.M = M;
     p.N = N;
     p.K = K;
     p.Kp = Kp;
     p.ldc = N;
-    p.partials = prefill_partials(workspace, M, K);
     p.W = W;
     p.bits = bits;
     p.block = block;
@@ -798,8 +832,9 @@ qmm_status qmm_nbits(const void* A, int a_type, int64_t M, int64_t K, int64_t N,
     p.C = C;
     p.c_type = c_type;
     // a few rows: the skinny kernel (16-row tiles, each weight dequantized once)
-    hipError_t e = skinny_applies(M, N, Kp, block, p.row_bytes, p.nblk) ? launch_skinny(p, st)
-                                                                        : launch_prefill(p, st);
+    const bool skinny = skinny_applies(M, N, Kp, block, p.row_bytes, p.nblk);
+    hipError_t e = matrix_activations(p, A, a_type, skinny, workspace, st);
+    if (e == hipSuccess) e = skinny ? launch_skinny(p, st) : launch_prefill(p, st);
     if (e != hipSuccess) return (qmm_status)e;
     return (qmm_status)hipGetLastError();
   }
@@ -826,18 +861,15 @@ qmm_status qmm_codebook4(const void* A, int a_type, int64_t M, int64_t K, int64_
   if (M == 0 || N == 0) return QMM_OK;
   hipStream_t st = (hipStream_t)stream;
   if (codebook_on_matrix_cores(M, K, N, block, c_type)) {
-    // matrix-core path: A -> padded fp16 once, W16 = fp16(codebook[q] * absmax) per tile
+    // matrix-core path: A -> padded fp16 once (or fp16 A in place),
+    // W16 = fp16(codebook[q] * absmax) per tile
     PrefillArgs p{};
     const int64_t Kp = (K + 63) / 64 * 64;
-    hipError_t ce = launch_cast_pad_f16(A, a_type, M, K, Kp, (uint16_t*)workspace, st);
-    if (ce != hipSuccess) return (qmm_status)ce;
-    p.A16 = (const uint16_t*)workspace;
     p.M = M;
     p.N = N;
     p.K = K;
     p.Kp = Kp;
     p.ldc = N;
-    p.partials = prefill_partials(workspace, M, K);
     p.W = W;
     p.bits = 4;
     p.block = block;
@@ -852,8 +884,9 @@ qmm_status qmm_codebook4(const void* A, int a_type, int64_t M, int64_t K, int64_
     p.C = C;
     p.c_type = c_type;
     // a few rows: the skinny kernel (16-row tiles, each weight dequantized once)
-    hipError_t e = skinny_applies(M, N, Kp, block, p.row_bytes, p.nblk) ? launch_skinny(p, st)
-                                                                        : launch_prefill(p, st);
+    const bool skinny = skinny_applies(M, N, Kp, block, p.row_bytes, p.nblk);
+    hipError_t e = matrix_activations(p, A, a_type, skinny, workspace, st);
+    if (e == hipSuccess) e = skinny ? launch_skinny(p, st) : launch_prefill(p, st);
     if (e != hipSuccess) return (qmm_status)e;
     return (qmm_status)hipGetLastError();
   }
@@ -1025,6 +1058,140 @@ qmm_status qmoe_decode_fused(const uint16_t* X, int64_t T, int64_t H, int64_t I,
   return (qmm_status)hipGetLastError();
 }
 
+qmm_status qmoe_decode_status(void* scratch, size_t scratch_bytes, int64_t T, int64_t H, int64_t I, int k,
+                              int mode, int* timed_out, void* stream) {
+  (void)hipGetLastError();
+  if (!timed_out) return QMM_E_NULL;
+  *timed_out = 0;
+  if (mode != QMOE_FP && mode != QMOE_INT8_ACT) return QMM_E_MODE;
+  if (T < 0 || H < 0 || I < 0 || k < 0) return QMM_E_SHAPE;
+  if (mode != QMOE_FP || T == 0) return QMM_OK;  // only the fp single-launch form waits
+  const QmoeLayout L = qmoe_layout(T, H, I, k, mode);
+  if (!scratch) return QMM_E_NULL;
+  if (scratch_bytes < L.total) return QMM_E_WORKSPACE;
+  if (!aligned(scratch, 256)) return QMM_E_ALIGN;
+  hipStream_t st = (hipStream_t)stream;
+  uint32_t* flag = (uint32_t*)((uint8_t*)scratch + L.sync) + 2;
+  uint32_t v = 0;
+  hipError_t e = hipMemcpyAsync(&v, flag, 4, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e == hipSuccess && v != 0) {
+    e = hipMemsetAsync(flag, 0, 4, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+  }
+  if (e != hipSuccess) return (qmm_status)e;
+  *timed_out = v != 0 ? 1 : 0;
+  return QMM_OK;
+}
+
+// ---- activation quantization ops ---------------------------------------------
+static qmm_status check_qparams(qmm_qparams q, int bits) {
+  if (!(q.scale > 0.0f) || !(q.scale <= 3.402823466e38f)) return QMM_E_PARAM;
+  if (q.zero_point < 0 || q.zero_point > (1 << bits) - 1) return QMM_E_PARAM;
+  return QMM_OK;
+}
+
+static qmm_status check_qdq_common(int64_t n, int bits) {
+  if (bits != 8 && bits != 16) return QMM_E_BITS;
+  if (n < 0) return QMM_E_SHAPE;
+  return QMM_OK;
+}
+
+static bool codes_aligned(const void* p, int bits) { return aligned(p, bits == 16 ? 2 : 1); }
+
+qmm_status qmm_quantize_linear(const void* x, int x_type, int64_t n, qmm_qparams q, int bits, void* codes,
+                               void* stream) {
+  (void)hipGetLastError();
+  qmm_status s = check_qdq_common(n, bits);
+  if (s != QMM_OK) return s;
+  if (!valid_dtype(x_type)) return QMM_E_DTYPE;
+  if ((s = check_qparams(q, bits)) != QMM_OK) return s;
+  if (n == 0) return QMM_OK;
+  if (!x || !codes) return QMM_E_NULL;
+  if (!aligned(x, dtype_size(x_type)) || !codes_aligned(codes, bits)) return QMM_E_ALIGN;
+  const hipError_t e = launch_quantize_linear(x, x_type, n, q, bits, codes, (hipStream_t)stream);
+  if (e != hipSuccess) return (qmm_status)e;
+  return (qmm_status)hipGetLastError();
+}
+
+qmm_status qmm_dequantize_linear(const void* codes, int64_t n, qmm_qparams q, int bits, void* y, int y_type,
+                                 void* stream) {
+  (void)hipGetLastError();
+  qmm_status s = check_qdq_common(n, bits);
+  if (s != QMM_OK) return s;
+  if (!valid_dtype(y_type)) return QMM_E_DTYPE;
+  if ((s = check_qparams(q, bits)) != QMM_OK) return s;
+  if (n == 0) return QMM_OK;
+  if (!codes || !y) return QMM_E_NULL;
+  if (!aligned(y, dtype_size(y_type)) || !codes_aligned(codes, bits)) return QMM_E_ALIGN;
+  const hipError_t e = launch_dequantize_linear(codes, n, q, bits, y, y_type, (hipStream_t)stream);
+  if (e != hipSuccess) return (qmm_status)e;
+  return (qmm_status)hipGetLastError();
+}
+
+qmm_status qmm_fake_quantize(const void* x, int x_type, int64_t n, qmm_qparams q, int bits, void* y,
+                             void* stream) {
+  (void)hipGetLastError();
+  qmm_status s = check_qdq_common(n, bits);
+  if (s != QMM_OK) return s;
+  if (!valid_dtype(x_type)) return QMM_E_DTYPE;
+  if ((s = check_qparams(q, bits)) != QMM_OK) return s;
+  if (n == 0) return QMM_OK;
+  if (!x || !y) return QMM_E_NULL;
+  if (!aligned(x, dtype_size(x_type)) || !aligned(y, dtype_size(x_type))) return QMM_E_ALIGN;
+  const hipError_t e = launch_fake_quantize(x, x_type, n, q, bits, y, (hipStream_t)stream);
+  if (e != hipSuccess) return (qmm_status)e;
+  return (qmm_status)hipGetLastError();
+}
+
+qmm_status qmm_qsigmoid(const void* codes_in, int64_t n, qmm_qparams in, qmm_qparams out, int bits,
+                        void* codes_out, void* stream) {
+  (void)hipGetLastError();
+  qmm_status s = check_qdq_common(n, bits);
+  if (s != QMM_OK) return s;
+  if ((s = check_qparams(in, bits)) != QMM_OK || (s = check_qparams(out, bits)) != QMM_OK) return s;
+  if (n == 0) return QMM_OK;
+  if (!codes_in || !codes_out) return QMM_E_NULL;
+  if (!codes_aligned(codes_in, bits) || !codes_aligned(codes_out, bits)) return QMM_E_ALIGN;
+  const hipError_t e = launch_qsigmoid(codes_in, n, in, out, bits, codes_out, (hipStream_t)stream);
+  if (e != hipSuccess) return (qmm_status)e;
+  return (qmm_status)hipGetLastError();
+}
+
+qmm_status qmm_qmul(const void* a, qmm_qparams qa, const void* b, qmm_qparams qb, int64_t n, qmm_qparams qc,
+                    int bits, void* c, void* stream) {
+  (void)hipGetLastError();
+  qmm_status s = check_qdq_common(n, bits);
+  if (s != QMM_OK) return s;
+  if ((s = check_qparams(qa, bits)) != QMM_OK || (s = check_qparams(qb, bits)) != QMM_OK ||
+      (s = check_qparams(qc, bits)) != QMM_OK)
+    return s;
+  if (n == 0) return QMM_OK;
+  if (!a || !b || !c) return QMM_E_NULL;
+  if (!codes_aligned(a, bits) || !codes_aligned(b, bits) || !codes_aligned(c, bits)) return QMM_E_ALIGN;
+  const hipError_t e = launch_qmul(a, qa, b, qb, n, qc, bits, c, (hipStream_t)stream);
+  if (e != hipSuccess) return (qmm_status)e;
+  return (qmm_status)hipGetLastError();
+}
+
+qmm_status qmm_qswiglu(const void* gate, const void* up, int x_type, int64_t n, int bits, const qmm_qparams* q,
+                       void* y, void* stream) {
+  (void)hipGetLastError();
+  qmm_status s = check_qdq_common(n, bits);
+  if (s != QMM_OK) return s;
+  if (!valid_dtype(x_type)) return QMM_E_DTYPE;
+  if (!q) return QMM_E_NULL;
+  for (int i = 0; i < 5; ++i)
+    if ((s = check_qparams(q[i], bits)) != QMM_OK) return s;
+  if (n == 0) return QMM_OK;
+  if (!gate || !up || !y) return QMM_E_NULL;
+  const size_t es = dtype_size(x_type);
+  if (!aligned(gate, es) || !aligned(up, es) || !aligned(y, es)) return QMM_E_ALIGN;
+  const hipError_t e = launch_qswiglu(gate, up, x_type, n, bits, q, y, (hipStream_t)stream);
+  if (e != hipSuccess) return (qmm_status)e;
+  return (qmm_status)hipGetLastError();
+}
+
 qmm_status qmm_set_tuning(int mode, int forced_index) {
   if (mode < 0 || mode > 2) return QMM_E_MODE;
   TunerState& t = tuner();
@@ -1072,6 +1239,7 @@ const char* qmm_status_string(qmm_status s) {
     case QMM_E_WORKSPACE: return "workspace missing or too small";
     case QMM_E_MODE: return "unknown mode or zero-point kind";
     case QMM_E_DEVICE: return "no usable device";
+    case QMM_E_PARAM: return "quantization parameter out of range";
     default: return s > 0 ? hipGetErrorString((hipError_t)s) : "unknown status";
   }
 }

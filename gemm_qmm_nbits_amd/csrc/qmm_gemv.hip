@@ -118,11 +118,11 @@ void gemv_plan(GemvArgs& g, int num_cus) {
   g.num_cus = num_cus > 0 ? num_cus : 256;
   // LDS bytes per chunk slot per A row: codebook kernel = fp32 activations (WPC + 4
   // floats) + 4 group sums; integer-plane kernel = the planes (12 or 6 words per
-  // weight dword, 4 words of padding) + 4 group records of two floats
+  // weight dword, 4 words of padding) + 4 group records of four words
   int64_t cs_bytes;
   if (g.fmt == GEMV_CODEBOOK) cs_bytes = (int64_t)(32 + 4) * 4 + 4 * 4;
-  else if (g.bits == 2) cs_bytes = (int64_t)(4 * 12 + 4) * 4 + 4 * 8;
-  else cs_bytes = (int64_t)(4 * 6 + 4) * 4 + 4 * 8;
+  else if (g.bits == 2) cs_bytes = (int64_t)(4 * 12 + 4) * 4 + 4 * 16;
+  else cs_bytes = (int64_t)(4 * 6 + 4) * 4 + 4 * 16;
   const int64_t lpr = 1LL << g.lpr_log2;
   const int64_t per_iter = (int64_t)g.mt * lpr * cs_bytes;  // one chunk per lane, all A rows
   const int64_t iters_all = (g.nchunks + lpr - 1) / lpr;

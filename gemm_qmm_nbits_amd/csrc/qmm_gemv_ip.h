@@ -20,6 +20,14 @@
 // fp32 multiply-add), and the row partial gains  s * (P * 2^(e-22) - zp * sum_k a[k])
 // where sum_k a[k] is the fp32 group sum taken at staging.
 //
+// One dominant activation per group is taken out of the planes: when the largest
+// magnitude of a group is at least 32 times the second largest (an activation
+// outlier), that value is staged as zero and left out of the group sum, the exponent
+// e comes from the second largest, and its own term a_o * (q_o - zp) is added in fp32
+// to P * 2^(e-22).  The fixed-point error of the other values is then bounded by
+// 2^-23 of the second largest magnitude instead of the outlier's, and the zero-point
+// fold never subtracts two outlier-sized terms.
+//
 // The work decomposition (lanes per row, lane -> chunk map, per-lane chunk order,
 // fixed xor butterfly, tiles, prefetch ring, LDS output buffer) is that of the
 // fp32 kernel in qmm_gemv_impl.h, so the summation order again depends only on
@@ -78,8 +86,9 @@ __device__ __forceinline__ void nibble_planes(const uint32_t (&x)[3], const uint
 }
 
 // Stage chunks [c0, c0 + SC) of every A row as planes; meta[(m*4+gi)*SC + slot] =
-// {2^(e-22), sum a} for scale group gi of the slot.  A group whose largest |a| is
-// not finite gets a NaN step, so the rows it meets come out NaN.
+// {2^(e-22), sum a, a_o, index of a_o in the group (as bits)} for scale group gi of
+// the slot, a_o = 0 when no value is taken out.  A group whose largest |a| is not
+// finite, or that holds a NaN, gets a NaN step, so the rows it meets come out NaN.
 //
 // Each thread converts 16 consecutive activations (one 2-bit weight dword, two
 // 4-bit ones): the 12 plane words they fill are contiguous in the slot, so they
@@ -95,8 +104,26 @@ __device__ __forceinline__ void nibble_planes(const uint32_t (&x)[3], const uint
 // offset past the buffer's range for an element past the row or a piece past the
 // last, which returns 0 and fetches nothing.  Otherwise global loads, whose address
 // is replaced by the first element and whose value by a select.
+// Position of this lane's 16-value piece inside its scale group of GW pieces: the
+// pieces of a group are staged by GW consecutive lanes (batches start at multiples of
+// the work-group size).
+template <int GW>
+__device__ __forceinline__ int piece_of_lane() {
+  return (int)(threadIdx.x & (unsigned)(GW - 1));
+}
+
+// The product of a value taken out of a scale group with its code: the code sits in
+// dword gi * DPG + id / (32 / BITS) of the chunk, field id % (32 / BITS).
+template <int BITS, int DPG>
+__device__ __forceinline__ float outlier_code(const uint4& w, int gi, uint32_t id) {
+  constexpr uint32_t WPD = 32 / BITS;
+  const uint32_t di = (uint32_t)(gi * DPG) + id / WPD;
+  const uint32_t x = di == 0 ? w.x : di == 1 ? w.y : di == 2 ? w.z : w.w;
+  return (float)((x >> ((id % WPD) * BITS)) & ((1u << BITS) - 1u));
+}
+
 template <int BITS, int AT, int G, int MT, bool AVEC, bool BUF, typename Issued>
-__device__ __forceinline__ void stage_planes_impl(const GemvArgs& g, uint32_t* planes, f32x2* meta,
+__device__ __forceinline__ void stage_planes_impl(const GemvArgs& g, uint32_t* planes, f32x4* meta,
                                                   uint32_t* trash, int c0, int SC, Issued&& issued) {
   using L = IpLayout<BITS>;
   constexpr int WPC = 128 / BITS;
@@ -217,7 +244,7 @@ __device__ __forceinline__ void stage_planes_impl(const GemvArgs& g, uint32_t* p
       if (base_idx + j * (int)blockDim.x + wave_base >= total) break;  // uniform over the wave
       const int idx = base_idx + j * (int)blockDim.x + (int)threadIdx.x;
       const bool ok = idx < total;
-      const float* v = vb[j];
+      float* v = vb[j];
       // piece index = (m * SC + slot) * PPC + piece: chunk slot cs = m * SC + slot, and
       // the 16-value piece inside the chunk (24-bit products: no 64-bit arithmetic)
       const uint32_t uidx = ok ? (uint32_t)idx : 0u;
@@ -225,21 +252,51 @@ __device__ __forceinline__ void stage_planes_impl(const GemvArgs& g, uint32_t* p
       const uint32_t piece = uidx % (uint32_t)PPC;
       uint32_t m, first;
       row_of(uidx, m, first);
-      float mx = 0.0f, sm = 0.0f;
+      // largest magnitude m1 (its index in the group and its value), second largest m2
+      float m1 = 0.0f, m2 = 0.0f, vo = 0.0f;
+      uint32_t io = 0;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v[4 * q]), fabsf(v[4 * q + 1])),
-                             fmaxf(fabsf(v[4 * q + 2]), fabsf(v[4 * q + 3]))));
-        sm += ((v[4 * q] + v[4 * q + 1]) + v[4 * q + 2]) + v[4 * q + 3];
+      for (int q = 0; q < 16; ++q) {
+        const float a = fabsf(v[q]);
+        const bool top = a > m1;
+        m2 = top ? m1 : fmaxf(m2, a);
+        io = top ? (uint32_t)q : io;
+        vo = top ? v[q] : vo;
+        m1 = top ? a : m1;
       }
+      io += (uint32_t)(piece_of_lane<gw>() * 16);
+      // combine with the partner lane's record: the larger value wins (ties to the lower
+      // index), the loser's maximum competes for second place; partners agree bitwise
+      auto combine = [&](float om1, uint32_t oio, float om2, float ovo) {
+        const bool take = om1 > m1 || (om1 == m1 && oio < io);
+        m2 = take ? fmaxf(om2, m1) : fmaxf(m2, om1);
+        io = take ? oio : io;
+        vo = take ? ovo : vo;
+        m1 = take ? om1 : m1;
+      };
       if constexpr (gw >= 2) {
-        mx = fmaxf(mx, dpp_f<kDppXor1>(mx));
-        sm += dpp_f<kDppXor1>(sm);
+        const float om1 = dpp_f<kDppXor1>(m1), om2 = dpp_f<kDppXor1>(m2), ovo = dpp_f<kDppXor1>(vo);
+        const uint32_t oio = (uint32_t)__float_as_int(dpp_f<kDppXor1>(__int_as_float((int)io)));
+        combine(om1, oio, om2, ovo);
       }
       if constexpr (gw >= 4) {
-        mx = fmaxf(mx, dpp_f<kDppXor2>(mx));
-        sm += dpp_f<kDppXor2>(sm);
+        const float om1 = dpp_f<kDppXor2>(m1), om2 = dpp_f<kDppXor2>(m2), ovo = dpp_f<kDppXor2>(vo);
+        const uint32_t oio = (uint32_t)__float_as_int(dpp_f<kDppXor2>(__int_as_float((int)io)));
+        combine(om1, oio, om2, ovo);
       }
+      // a dominant value is taken out of the planes and of the group sum (finite,
+      // nonzero, at least 32 times every other magnitude); its product is added apart
+      const bool excl = m1 <= 3.402823466e38f && m1 > 0.0f && m1 >= 32.0f * m2;
+      const uint32_t own = excl && (io >> 4) == (uint32_t)piece_of_lane<gw>() ? (io & 15u) : 16u;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) v[q] = (uint32_t)q == own ? 0.0f : v[q];
+      float sm = 0.0f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) sm += ((v[4 * q] + v[4 * q + 1]) + v[4 * q + 2]) + v[4 * q + 3];
+      if constexpr (gw >= 2) sm += dpp_f<kDppXor1>(sm);
+      if constexpr (gw >= 4) sm += dpp_f<kDppXor2>(sm);
+      const bool finite = m1 <= 3.402823466e38f && sm == sm;
+      const float mx = excl ? m2 : m1;
       int e = 0;
       (void)frexpf(mx, &e);  // mx < 2^e (mx = 0 gives e = 0)
       uint32_t u[16];
@@ -283,9 +340,11 @@ __device__ __forceinline__ void stage_planes_impl(const GemvArgs& g, uint32_t* p
       dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
       dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
       dst[2] = make_uint4(w[8], w[9], w[10], w[11]);
-      f32x2 mt;
-      mt.x = mx <= 3.402823466e38f ? ldexpf(1.0f, e - 22) : __builtin_nanf("");
+      f32x4 mt;
+      mt.x = finite ? ldexpf(1.0f, e - 22) : __builtin_nanf("");
       mt.y = sm;
+      mt.z = excl ? vo : 0.0f;
+      mt.w = __uint_as_float(excl ? io : 0u);
       // record (m * 4 + gi) * SC + slot = cs + (3 m + gi) * SC, by selects
       const uint32_t gi = piece / gw;
       const uint32_t usc = (uint32_t)SC;
@@ -293,8 +352,8 @@ __device__ __forceinline__ void stage_planes_impl(const GemvArgs& g, uint32_t* p
       uint32_t m3 = 0;
 #pragma unroll
       for (int r = 1; r < MT; ++r) m3 += m >= (uint32_t)r ? 3u * usc : 0u;
-      const uint32_t mw = ok && (piece % gw) == 0 ? meta_word + 2u * (cs + m3 + gsc) : trash_word;
-      *(f32x2*)(planes + mw) = mt;
+      const uint32_t mw = ok && (piece % gw) == 0 ? meta_word + 4u * (cs + m3 + gsc) : trash_word;
+      *(f32x4*)(planes + mw) = mt;
     }
   };
   batch(0, std::true_type{});
@@ -305,7 +364,7 @@ __device__ __forceinline__ void stage_planes_impl(const GemvArgs& g, uint32_t* p
 // trash: 64 bytes of LDS (16-byte aligned) that nothing reads.  BUF requires
 // M * K * element size < 2^31 - 64 (the streaming kernel's A fits in LDS).
 template <int BITS, int AT, int G, int MT, bool BUF, typename Issued>
-__device__ __forceinline__ void stage_planes(const GemvArgs& g, uint32_t* planes, f32x2* meta,
+__device__ __forceinline__ void stage_planes(const GemvArgs& g, uint32_t* planes, f32x4* meta,
                                              uint32_t* trash, int c0, int SC, Issued&& issued) {
   if (g.a_vec)
     stage_planes_impl<BITS, AT, G, MT, true, BUF>(g, planes, meta, trash, c0, SC, issued);
@@ -327,7 +386,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_ip_kernel(GemvArgs g) {
   extern __shared__ float lds[];
   const int SC = g.slice_chunks;
   uint32_t* planes = (uint32_t*)lds;
-  f32x2* meta = (f32x2*)(planes + MT * SC * L::SLOT);
+  f32x4* meta = (f32x4*)(planes + MT * SC * L::SLOT);
   uint32_t* trash = (uint32_t*)(meta + MT * 4 * SC);  // the 16 floats the plan adds after the records
   float* out_lds = (float*)(trash + 16);
   const int lane = threadIdx.x & 63;
@@ -511,7 +570,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_ip_kernel(GemvArgs g) {
 #pragma unroll
           for (int m = 0; m < MT; ++m) {
             const int mm = m < M ? m : 0;
-            const f32x2 mt = meta[(mm * 4 + gi) * SC + slot];
+            const f32x4 mt = meta[(mm * 4 + gi) * SC + slot];
 #pragma unroll
             for (int r = 0; r < R; ++r) {
               int s5 = S[r][m][5];
@@ -525,9 +584,13 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_ip_kernel(GemvArgs g) {
               if constexpr (ZK == 1) z = (float)((cbuf.z[r][gi] >> cbuf.zsh[r][gi]) & ((1u << BITS) - 1u));
               else if constexpr (ZK == 2) z = (float)cbuf.zh[r][gi];
               else z = zconst;
+              float t = P * mt.x;
+              // a value taken out of the planes: a_o * (q_o - zp), q_o - zp exact
+              if (mt.z != 0.0f)
+                t = fmaf(mt.z, outlier_code<BITS, DPG>(cbuf.w[r], gi, __float_as_uint(mt.w)) - z, t);
               // same expression for every zero-point kind, so a uniform scalar and
               // a tensor holding that value give the same bits
-              const float nv = fmaf(scv, fmaf(-z, mt.y, P * mt.x), acc[r][m]);
+              const float nv = fmaf(scv, fmaf(-z, mt.y, t), acc[r][m]);
               acc[r][m] = valid ? nv : acc[r][m];
             }
           }

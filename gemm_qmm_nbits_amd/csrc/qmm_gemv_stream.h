@@ -31,7 +31,7 @@ __global__ __launch_bounds__(stream_threads(MT, R)) void gemv_ip_stream_kernel(G
   extern __shared__ float lds[];
   const int SC = g.slice_chunks;  // >= nchunks
   uint32_t* planes = (uint32_t*)lds;
-  f32x2* meta = (f32x2*)(planes + MT * SC * L::SLOT);
+  f32x4* meta = (f32x4*)(planes + MT * SC * L::SLOT);
   uint32_t* trash = (uint32_t*)(meta + MT * 4 * SC);  // the 16 floats the plan adds after the records
   float* out_lds = (float*)(trash + 16);
   const int lane = threadIdx.x & 63;
@@ -131,7 +131,7 @@ __global__ __launch_bounds__(stream_threads(MT, R)) void gemv_ip_stream_kernel(G
   int cit = 0, cgrp = g_begin + wave;
   const int total = wave_groups * iters;
   const uint32_t* planes_lane = planes + lp * L::SLOT;
-  const f32x2* meta_lane = meta + lp;
+  const f32x4* meta_lane = meta + lp;
   auto step = [&](IpBuf<R, NS>& cbuf, IpBuf<R, NS>& nxt, bool live) {
     fetch(nxt);
     const int slot = cit * LPR + lp;
@@ -193,7 +193,7 @@ __global__ __launch_bounds__(stream_threads(MT, R)) void gemv_ip_stream_kernel(G
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
           const int mm = m < M ? m : 0;
-          const f32x2 mt = meta_lane[(mm * 4 + gi) * SC + cit * LPR];
+          const f32x4 mt = meta_lane[(mm * 4 + gi) * SC + cit * LPR];
 #pragma unroll
           for (int r = 0; r < R; ++r) {
             int s5 = S[r][m][5];
@@ -206,7 +206,11 @@ __global__ __launch_bounds__(stream_threads(MT, R)) void gemv_ip_stream_kernel(G
             if constexpr (ZK == 1) z = (float)((cbuf.z[r][gi] >> cbuf.zsh[r][gi]) & ((1u << BITS) - 1u));
             else if constexpr (ZK == 2) z = (float)cbuf.zh[r][gi];
             else z = zconst;
-            const float nv = fmaf(scv, fmaf(-z, mt.y, P * mt.x), acc[r][m]);
+            float t = P * mt.x;
+            // a value taken out of the planes: a_o * (q_o - zp), q_o - zp exact
+            if (mt.z != 0.0f)
+              t = fmaf(mt.z, outlier_code<BITS, DPG>(cbuf.w[r], gi, __float_as_uint(mt.w)) - z, t);
+            const float nv = fmaf(scv, fmaf(-z, mt.y, t), acc[r][m]);
             acc[r][m] = valid ? nv : acc[r][m];
           }
         }

@@ -74,13 +74,17 @@ hipError_t launch_uniform_check(const uint16_t* zp, int64_t count, uint32_t* scr
                                 hipStream_t st);
 constexpr int kUniformPartials = 256;
 
-// A (fp32 / bf16) -> fp16, round to nearest even, count elements.
-// dst[m][k] = fp16(src[m][k]) for k < K, 0 for K <= k < Kp (rows of Kp elements).
+// A (fp32 / fp16 / bf16) -> fp16 rows of Kp elements with a per-row power-of-two
+// pre-scale: dst[m][k] = fp16(src[m][k] * 2^s_m) for k < K, 0 for K <= k < Kp, and
+// row_scale[m] = 2^-s_m (s_m puts the row's largest magnitude in [2^14, 2^15); 0 for
+// fp16 sources, zero rows and rows with a non-finite value).
 hipError_t launch_cast_pad_f16(const void* src, int src_type, int64_t M, int64_t K, int64_t Kp,
-                               uint16_t* dst, hipStream_t st);
+                               uint16_t* dst, float* row_scale, hipStream_t st);
 
 struct PrefillArgs {
-  const uint16_t* A16;  // fp16 [M][Kp], k >= K zero
+  const uint16_t* A16;  // fp16 [M][lda]: the cast workspace (lda = Kp, k >= K zero) or fp16 A itself
+  const float* row_scale;  // [M] factor of each row's sums (the cast's 2^-s_m), or NULL for 1
+  int64_t lda;  // row stride of A16 in elements (Kp, or K for fp16 A read in place)
   int64_t M, N, K;
   int64_t Kp;   // K rounded up to a multiple of 64
   int64_t ldc;  // row stride of C (elements)
@@ -105,5 +109,20 @@ struct PrefillArgs {
 };
 hipError_t launch_prefill(PrefillArgs p, hipStream_t st);
 int prefill_splits(int64_t M, int64_t N, int64_t Kp);
+
+// Activation quantization ops (qmm_qdq.hip); arguments checked by the caller.
+using QdqParams = qmm_qparams;
+hipError_t launch_quantize_linear(const void* x, int x_type, int64_t n, QdqParams q, int bits, void* codes,
+                                  hipStream_t st);
+hipError_t launch_dequantize_linear(const void* codes, int64_t n, QdqParams q, int bits, void* y, int y_type,
+                                    hipStream_t st);
+hipError_t launch_fake_quantize(const void* x, int x_type, int64_t n, QdqParams q, int bits, void* y,
+                                hipStream_t st);
+hipError_t launch_qsigmoid(const void* in, int64_t n, QdqParams qi, QdqParams qo, int bits, void* out,
+                           hipStream_t st);
+hipError_t launch_qmul(const void* a, QdqParams qa, const void* b, QdqParams qb, int64_t n, QdqParams qc, int bits,
+                       void* c, hipStream_t st);
+hipError_t launch_qswiglu(const void* gate, const void* up, int x_type, int64_t n, int bits, const QdqParams* q,
+                          void* y, hipStream_t st);
 
 }  // namespace qmm

@@ -77,89 +77,151 @@ hipError_t launch_uniform_check(const uint16_t* zp, int64_t count, uint32_t* scr
   return hipSuccess;
 }
 
-// ---- A cast to fp16 (prefill path; [P1] "What", commit 1: cast A once) --------
-// One thread per 8 consecutive elements of a destination row (one 16-byte store).
-__global__ __launch_bounds__(256) void cast_pad_f16_kernel(const void* src, int src_type, int64_t M,
-                                                           int64_t K, int64_t Kp, uint16_t* dst) {
-  const int64_t per_row = Kp / 8;
-  const int64_t total = M * per_row;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t m = i / per_row;
-    const int64_t k = (i - m * per_row) * 8;
-    const int64_t base = m * K + k;
-    uint32_t o[4];
+// ---- A cast to fp16 (matrix-core paths; [P1] "What", commit 1: cast A once) -----
+//
+// Row m of A becomes dst[m][0..Kp) = fp16(a[m][k] * 2^s_m) for k < K and 0 past K,
+// and rs[m] = 2^-s_m, the factor the epilogues apply to the row's sums.  The shift
+// puts the row's largest magnitude |a| = f * 2^E (f in [0.5, 1)) into [2^14, 2^15):
+// s_m = min(15 - E, 126), so no value overflows fp16 and small values keep their bits
+// (both scalings are exact powers of two).  A row that is all zero or whose largest
+// magnitude is not finite, and every row of fp16 activations (already in range), get
+// s_m = 0.  One work-group of 256 threads per row; each thread holds its 8-element
+// pieces in registers between the maximum and the conversion, so the row is read
+// once (rows longer than 256 * 8 * kCastPieces elements are read twice).
+constexpr int kCastThreads = 256;
+constexpr int kCastPieces = 16;
+
+__device__ __forceinline__ float cast_block_max(float v, float* red) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float v0 = (k + 2 * e < K) ? load_elem_rt(src, src_type, base + 2 * e) : 0.0f;
-      const float v1 = (k + 2 * e + 1 < K) ? load_elem_rt(src, src_type, base + 2 * e + 1) : 0.0f;
-      o[e] = (uint32_t)f32_to_f16(v0) | ((uint32_t)f32_to_f16(v1) << 16);
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int w = 1; w < kCastThreads / 64; ++w) r = fmaxf(r, red[w]);
+  return r;
+}
+
+__device__ __forceinline__ int cast_shift(float mx, int src_type) {
+  if (src_type == QMM_F16 || !(mx <= 3.402823466e38f) || mx == 0.0f) return 0;
+  int E = 0;
+  (void)frexpf(mx, &E);
+  const int s = 15 - E;
+  return s < 126 ? s : 126;
+}
+
+// 8 consecutive elements of row m starting at k (k < K); VEC: K % 8 == 0 and a
+// 16-byte aligned source, so the 8 lie in the row and come as aligned vectors.
+template <int AT, bool VEC>
+__device__ __forceinline__ void cast_load8(const void* src, int64_t m, int64_t K, int64_t k, float (&v)[8]) {
+  const int64_t base = m * K + k;
+  if constexpr (VEC) {
+    if constexpr (AT == QMM_F32) {
+      const f32x4* p = (const f32x4*)((const float*)src + base);
+      const f32x4 a = p[0], b = p[1];
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+      v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    } else {
+      const uint4 u = *(const uint4*)((const uint16_t*)src + base);
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint16_t lo = (uint16_t)(w[e] & 0xffffu), hi = (uint16_t)(w[e] >> 16);
+        v[2 * e] = AT == QMM_F16 ? f16_to_f32(lo) : bf16_to_f32(lo);
+        v[2 * e + 1] = AT == QMM_F16 ? f16_to_f32(hi) : bf16_to_f32(hi);
+      }
     }
-    ((uint4*)dst)[i] = make_uint4(o[0], o[1], o[2], o[3]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (k + e < K) ? load_elem<AT>(src, base + e) : 0.0f;
   }
 }
 
-// Same result for K a multiple of 8 and a 16-byte aligned source: a group of 8
-// destination elements then lies wholly inside the row or wholly in the padding, and
-// its source is one or two aligned 16-byte loads (vector loads, no per-element type
-// switch or bounds check).  The conversion is the one above.
-template <int AT>
-__global__ __launch_bounds__(256) void cast_pad_f16_vec_kernel(const void* src, int64_t M, int64_t K,
-                                                               int64_t Kp, uint16_t* dst) {
-  const int64_t per_row = Kp / 8;
-  const int64_t per_src = K / 8;
-  const int64_t total = M * per_row;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t m = i / per_row;
-    const int64_t c = i - m * per_row;
-    uint4 out = make_uint4(0u, 0u, 0u, 0u);
-    if (c < per_src) {
-      const int64_t base = m * K + c * 8;
-      float v[8];
-      if constexpr (AT == QMM_F32) {
-        const f32x4* p = (const f32x4*)((const float*)src + base);
-        const f32x4 a = p[0], b = p[1];
-        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-      } else {
-        const uint4 u = *(const uint4*)((const uint16_t*)src + base);
-        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+__device__ __forceinline__ uint4 cast_store8(const float (&v)[8], int s) {
+  uint32_t o[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint16_t lo = (uint16_t)(w[e] & 0xffffu), hi = (uint16_t)(w[e] >> 16);
-          v[2 * e] = AT == QMM_F16 ? f16_to_f32(lo) : bf16_to_f32(lo);
-          v[2 * e + 1] = AT == QMM_F16 ? f16_to_f32(hi) : bf16_to_f32(hi);
-        }
+  for (int e = 0; e < 4; ++e)
+    o[e] = (uint32_t)f32_to_f16(ldexpf(v[2 * e], s)) | ((uint32_t)f32_to_f16(ldexpf(v[2 * e + 1], s)) << 16);
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// CACHED: the row's pieces fit in registers (Kp <= 256 * 8 * kCastPieces).
+template <int AT, bool VEC, bool CACHED>
+__global__ __launch_bounds__(kCastThreads) void cast_rows_f16_kernel(const void* src, int64_t M, int64_t K,
+                                                                    int64_t Kp, uint16_t* dst, float* rs) {
+  __shared__ float red[kCastThreads / 64];
+  const int64_t m = blockIdx.x;
+  const int64_t pieces = Kp / 8;   // destination pieces of 8 elements
+  const int64_t src_pieces = (K + 7) / 8;
+  uint4* drow = (uint4*)(dst + m * Kp);
+  float mx = 0.0f;
+  if constexpr (CACHED) {
+    float v[kCastPieces][8];
+#pragma unroll
+    for (int j = 0; j < kCastPieces; ++j) {
+      const int64_t c = threadIdx.x + (int64_t)j * kCastThreads;
+      if (c < src_pieces) cast_load8<AT, VEC>(src, m, K, c * 8, v[j]);
+      else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[j][e] = 0.0f;
       }
-      out.x = (uint32_t)f32_to_f16(v[0]) | ((uint32_t)f32_to_f16(v[1]) << 16);
-      out.y = (uint32_t)f32_to_f16(v[2]) | ((uint32_t)f32_to_f16(v[3]) << 16);
-      out.z = (uint32_t)f32_to_f16(v[4]) | ((uint32_t)f32_to_f16(v[5]) << 16);
-      out.w = (uint32_t)f32_to_f16(v[6]) | ((uint32_t)f32_to_f16(v[7]) << 16);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(v[j][e]));
     }
-    ((uint4*)dst)[i] = out;
+    const int s = cast_shift(cast_block_max(mx, red), AT);
+#pragma unroll
+    for (int j = 0; j < kCastPieces; ++j) {
+      const int64_t c = threadIdx.x + (int64_t)j * kCastThreads;
+      if (c < pieces) drow[c] = cast_store8(v[j], s);
+    }
+    if (threadIdx.x == 0) rs[m] = ldexpf(1.0f, -s);
+  } else {
+    for (int64_t c = threadIdx.x; c < src_pieces; c += kCastThreads) {
+      float v[8];
+      cast_load8<AT, VEC>(src, m, K, c * 8, v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(v[e]));
+    }
+    const int s = cast_shift(cast_block_max(mx, red), AT);
+    for (int64_t c = threadIdx.x; c < pieces; c += kCastThreads) {
+      float v[8];
+      if (c < src_pieces) cast_load8<AT, VEC>(src, m, K, c * 8, v);
+      else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = 0.0f;
+      }
+      drow[c] = cast_store8(v, s);
+    }
+    if (threadIdx.x == 0) rs[m] = ldexpf(1.0f, -s);
   }
+}
+
+template <int AT, bool VEC>
+static void launch_cast_rows(const void* src, int64_t M, int64_t K, int64_t Kp, uint16_t* dst, float* rs,
+                             hipStream_t st) {
+  if (Kp <= (int64_t)kCastThreads * 8 * kCastPieces)
+    hipLaunchKernelGGL((cast_rows_f16_kernel<AT, VEC, true>), dim3((unsigned)M), dim3(kCastThreads), 0, st, src,
+                       M, K, Kp, dst, rs);
+  else
+    hipLaunchKernelGGL((cast_rows_f16_kernel<AT, VEC, false>), dim3((unsigned)M), dim3(kCastThreads), 0, st, src,
+                       M, K, Kp, dst, rs);
+}
+
+template <int AT>
+static void launch_cast_at(const void* src, int64_t M, int64_t K, int64_t Kp, uint16_t* dst, float* rs,
+                           bool vec, hipStream_t st) {
+  if (vec) launch_cast_rows<AT, true>(src, M, K, Kp, dst, rs, st);
+  else launch_cast_rows<AT, false>(src, M, K, Kp, dst, rs, st);
 }
 
 hipError_t launch_cast_pad_f16(const void* src, int src_type, int64_t M, int64_t K, int64_t Kp,
-                               uint16_t* dst, hipStream_t st) {
-  int64_t blocks = (M * (Kp / 8) + 255) / 256;
-  if (blocks > 16384) blocks = 16384;
-  if (blocks < 1) blocks = 1;
-  if (K % 8 == 0 && (uintptr_t)src % 16 == 0) {
-    if (src_type == QMM_F32)
-      hipLaunchKernelGGL(cast_pad_f16_vec_kernel<QMM_F32>, dim3((unsigned)blocks), dim3(256), 0, st,
-                         src, M, K, Kp, dst);
-    else if (src_type == QMM_F16)
-      hipLaunchKernelGGL(cast_pad_f16_vec_kernel<QMM_F16>, dim3((unsigned)blocks), dim3(256), 0, st,
-                         src, M, K, Kp, dst);
-    else
-      hipLaunchKernelGGL(cast_pad_f16_vec_kernel<QMM_BF16>, dim3((unsigned)blocks), dim3(256), 0, st,
-                         src, M, K, Kp, dst);
-    return hipSuccess;
-  }
-  hipLaunchKernelGGL(cast_pad_f16_kernel, dim3((unsigned)blocks), dim3(256), 0, st, src, src_type, M,
-                     K, Kp, dst);
+                               uint16_t* dst, float* row_scale, hipStream_t st) {
+  if (M <= 0) return hipSuccess;
+  const bool vec = K % 8 == 0 && (uintptr_t)src % 16 == 0;
+  if (src_type == QMM_F32) launch_cast_at<QMM_F32>(src, M, K, Kp, dst, row_scale, vec, st);
+  else if (src_type == QMM_F16) launch_cast_at<QMM_F16>(src, M, K, Kp, dst, row_scale, vec, st);
+  else launch_cast_at<QMM_BF16>(src, M, K, Kp, dst, row_scale, vec, st);
   return hipSuccess;
 }
 

@@ -23,6 +23,7 @@
 // + v%4, column l % 32.
 #include "qmm_device.h"
 #include "qmm_internal.h"
+#include "qmm_skinny.h"
 
 #include <algorithm>
 
@@ -132,7 +133,7 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillArgs p) {
     int grow = m0 + row;
     grow = grow < (int)p.M ? grow : (int)p.M - 1;
     const int piece = (lane & 7) ^ ((row >> 1) & 7);
-    a_src[q] = (const uint8_t*)p.A16 + ((int64_t)grow * Kp) * 2 + piece * 16;
+    a_src[q] = (const uint8_t*)p.A16 + ((int64_t)grow * p.lda) * 2 + piece * 16;
   }
   // plain global addresses (no range check): the stage index is clamped to the last
   // stage, so no load ever leaves the A16 rows
@@ -319,7 +320,16 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillArgs p) {
     }
     return;
   }
-  // epilogue: + bias, convert, store (rows/columns past the end are skipped)
+  // epilogue: x row scale of the activation cast, + bias, convert, store (rows and
+  // columns past the end are skipped)
+  float rsv[2][16];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int row = m0 + wm * 64 + a * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+      rsv[a][v] = (p.row_scale && row < p.M) ? p.row_scale[row] : 1.0f;
+    }
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
     const int col = n0 + wn * 128 + b * 32 + (lane & 31);
@@ -330,22 +340,24 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillArgs p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int row = m0 + wm * 64 + a * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if (col_ok && row < p.M) store_c<CT>(p.C, (int64_t)row * p.ldc + col, acc[a][b][v] + bv);
+        if (col_ok && row < p.M) store_c<CT>(p.C, (int64_t)row * p.ldc + col, acc[a][b][v] * rsv[a][v] + bv);
       }
     }
   }
 }
 
-// C[m][n] = (((P[0] + P[1]) + ...) + P[S-1])[m][n] + bias[n], in the type of C.
+// C[m][n] = (((P[0] + P[1]) + ...) + P[S-1])[m][n] * rs[m] + bias[n], in the type of C
+// (rs = the activation cast's row scales, or 1 when NULL).
 template <int CT>
 __global__ __launch_bounds__(256) void reduce_splits_kernel(const float* P, int S, int64_t M, int64_t N,
-                                                            int64_t ldc, const void* bias, void* C) {
+                                                            int64_t ldc, const float* rs, const void* bias, void* C) {
   const int64_t total = M * N;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
        i += (int64_t)gridDim.x * blockDim.x) {
     const int64_t m = i / N, n = i - m * N;
     float v = P[m * ldc + n];
     for (int k = 1; k < S; ++k) v += P[(int64_t)k * M * ldc + m * ldc + n];
+    if (rs) v *= rs[m];
     if (bias) v += load_bias<CT>(bias, n);
     store_c<CT>(C, m * ldc + n, v);
   }
@@ -365,17 +377,17 @@ void launch_ct(const PrefillArgs& p, dim3 grid, hipStream_t st) {
 
 }  // namespace
 
-hipError_t launch_reduce_splits(const float* P, int S, int64_t M, int64_t N, int64_t ldc, const void* bias,
-                                void* C, int c_type, hipStream_t st) {
+hipError_t launch_reduce_splits(const float* P, int S, int64_t M, int64_t N, int64_t ldc, const float* rs,
+                                const void* bias, void* C, int c_type, hipStream_t st) {
   int64_t blocks = (M * N + 255) / 256;
   if (blocks > 16384) blocks = 16384;
   if (blocks < 1) blocks = 1;
   if (c_type == QMM_F32)
-    hipLaunchKernelGGL(reduce_splits_kernel<QMM_F32>, dim3((unsigned)blocks), dim3(256), 0, st, P, S, M, N, ldc, bias, C);
+    hipLaunchKernelGGL(reduce_splits_kernel<QMM_F32>, dim3((unsigned)blocks), dim3(256), 0, st, P, S, M, N, ldc, rs, bias, C);
   else if (c_type == QMM_F16)
-    hipLaunchKernelGGL(reduce_splits_kernel<QMM_F16>, dim3((unsigned)blocks), dim3(256), 0, st, P, S, M, N, ldc, bias, C);
+    hipLaunchKernelGGL(reduce_splits_kernel<QMM_F16>, dim3((unsigned)blocks), dim3(256), 0, st, P, S, M, N, ldc, rs, bias, C);
   else
-    hipLaunchKernelGGL(reduce_splits_kernel<QMM_BF16>, dim3((unsigned)blocks), dim3(256), 0, st, P, S, M, N, ldc, bias, C);
+    hipLaunchKernelGGL(reduce_splits_kernel<QMM_BF16>, dim3((unsigned)blocks), dim3(256), 0, st, P, S, M, N, ldc, rs, bias, C);
   return hipSuccess;
 }
 
@@ -418,7 +430,8 @@ hipError_t launch_prefill(PrefillArgs p, hipStream_t st) {
       PrefillArgs q = p;
       q.M = std::min(mstep, p.M - m0);
       q.N = std::min(nstep, p.N - n0);
-      q.A16 = p.A16 + m0 * p.Kp;
+      q.A16 = p.A16 + m0 * p.lda;
+      if (p.row_scale) q.row_scale = p.row_scale + m0;
       q.W = p.W + n0 * p.row_bytes;
       if (p.scales) q.scales = p.scales + n0 * p.nblk;
       if (p.absmax) q.absmax = p.absmax + n0 * p.nblk;
@@ -445,19 +458,7 @@ hipError_t launch_prefill(PrefillArgs p, hipStream_t st) {
         else if (zk == 2) launch_ct<GEMV_AFFINE, 4, 2>(q, grid, st);
         else launch_ct<GEMV_AFFINE, 4, 0>(q, grid, st);
       }
-      if (q.splits > 1) {
-        int64_t blocks = (q.M * q.N + 255) / 256;
-        if (blocks > 16384) blocks = 16384;
-        if (q.c_type == QMM_F32)
-          hipLaunchKernelGGL(reduce_splits_kernel<QMM_F32>, dim3((unsigned)blocks), dim3(256), 0, st,
-                             q.partials, q.splits, q.M, q.N, q.ldc, q.bias, q.C);
-        else if (q.c_type == QMM_F16)
-          hipLaunchKernelGGL(reduce_splits_kernel<QMM_F16>, dim3((unsigned)blocks), dim3(256), 0, st,
-                             q.partials, q.splits, q.M, q.N, q.ldc, q.bias, q.C);
-        else
-          hipLaunchKernelGGL(reduce_splits_kernel<QMM_BF16>, dim3((unsigned)blocks), dim3(256), 0, st,
-                             q.partials, q.splits, q.M, q.N, q.ldc, q.bias, q.C);
-      }
+      if (q.splits > 1) launch_reduce_splits(q.partials, q.splits, q.M, q.N, q.ldc, q.row_scale, q.bias, q.C, q.c_type, st);
     }
   }
   return hipSuccess;

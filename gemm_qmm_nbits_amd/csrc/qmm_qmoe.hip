@@ -1318,6 +1318,11 @@ constexpr uint64_t kSpinLimitTicks = 100000000ull;
 __device__ __forceinline__ uint32_t sync_add(uint32_t* p, uint32_t v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// arrival: a release at agent scope, so every h store of the work-group (ordered before
+// it by the work-group barrier) is visible to a work-group that acquires the count
+__device__ __forceinline__ uint32_t sync_arrive(uint32_t* p) {
+  return __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
 __device__ __forceinline__ uint32_t sync_load(uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -1328,14 +1333,16 @@ __device__ __forceinline__ void sync_store(uint32_t* p, uint32_t v) {
 template <int RI, int R, int ZK1, int ZK2>
 __global__ __launch_bounds__(kMoeStreamThreads) void qmoe_fused_kernel(QmoeArgs a) {
   extern __shared__ uint32_t smem[];
+  __shared__ uint32_t gave_up;
   uint32_t* sync = a.sync;
   const int nb = (int)gridDim.x;
   const int bid = (int)blockIdx.x;
+  if (threadIdx.x == 0) gave_up = 0u;
   fc1_stream_body<RI, ZK1, true>(a, bid, nb, smem);
   // every wave's h stores have completed before the work-group counts itself arrived
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (threadIdx.x == 0) (void)sync_add(&sync[0], 1u);
+  if (threadIdx.x == 0) (void)sync_arrive(&sync[0]);
   auto wait = [&] {
     if (threadIdx.x == 0) {
       const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
@@ -1347,13 +1354,22 @@ __global__ __launch_bounds__(kMoeStreamThreads) void qmoe_fused_kernel(QmoeArgs 
         ++polls;
         if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinLimitTicks) {
           sync_store(&sync[2], 1u);
+          gave_up = 1u;
           break;
         }
       }
+      // acquire: pairs with every work-group's release of its arrival
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
     __syncthreads();
   };
   fc2_stream_body<R, ZK2, true>(a, bid, nb, smem, wait);
+  __syncthreads();
+  if (gave_up) {
+    // a wait that gave up leaves the output invalid: it is filled with fp16 NaN (after
+    // this work-group's own rows were written, so those rows are NaN at the end)
+    for (int64_t i = threadIdx.x; i < a.T * a.H; i += kMoeStreamThreads) a.Y[i] = 0x7E00u;
+  }
   if (threadIdx.x == 0 && sync_add(&sync[1], 1u) == (uint32_t)nb - 1u) {
     sync_store(&sync[0], 0u);
     sync_store(&sync[1], 0u);
@@ -1371,10 +1387,11 @@ size_t qmoe_fc2_lds_bytes(const QmoeArgs& a) {
   return (size_t)a.k * a.fc2_chunks * 33 * sizeof(float);
 }
 
-// Allow more than 64 KB of dynamic LDS for a kernel (once per kernel).
+// Allow more than 64 KB of dynamic LDS for a kernel: up to the 150 KB the launch plans
+// use, which leaves room for a kernel's few bytes of static LDS within the 160 KB.
 template <typename Kern>
 static void allow_lds(Kern k, size_t lds) {
-  if (lds > 64 * 1024) (void)hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  if (lds > 64 * 1024) (void)hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, 150 * 1024);
 }
 
 // Work-groups of `kern` with `lds` bytes of dynamic LDS resident on one compute unit

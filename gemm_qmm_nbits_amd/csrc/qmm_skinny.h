@@ -14,8 +14,9 @@ hipError_t launch_skinny(const PrefillArgs& p, hipStream_t st);
 // Reduction splits of the skinny path (a function of the shape only; at most the
 // splits the workspace holds partial sums for).
 int skinny_splits(int64_t M, int64_t N, int64_t Kp);
-// C = (((P[0] + P[1]) + ...) + P[S-1]) + bias, in C's type (qmm_prefill.hip).
-hipError_t launch_reduce_splits(const float* P, int S, int64_t M, int64_t N, int64_t ldc, const void* bias,
-                                void* C, int c_type, hipStream_t st);
+// C = (((P[0] + P[1]) + ...) + P[S-1]) * rs[row] + bias, in C's type (rs NULL: 1)
+// (qmm_prefill.hip).
+hipError_t launch_reduce_splits(const float* P, int S, int64_t M, int64_t N, int64_t ldc, const float* rs,
+                                const void* bias, void* C, int c_type, hipStream_t st);
 
 }  // namespace qmm

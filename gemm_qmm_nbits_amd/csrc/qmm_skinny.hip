@@ -134,8 +134,12 @@ __global__ __launch_bounds__(SK_THREADS) void skinny_kernel(PrefillArgs p) {
   __amdgpu_buffer_rsrc_t rZ = rS;
   if constexpr (ZK == 1) rZ = sk_rsrc(p.zp, p.N * p.zp_row_bytes);
   if constexpr (ZK == 2) rZ = sk_rsrc(p.zp, p.N * p.nblk * 2);
-  // A rows past M lie past the workspace rows and read as zero
-  const __amdgpu_buffer_rsrc_t rA = sk_rsrc(p.A16, (int64_t)p.M * p.Kp * 2);
+  // A rows past M lie past the buffer's range and read as zero
+  const __amdgpu_buffer_rsrc_t rA = sk_rsrc(p.A16, (int64_t)p.M * p.lda * 2);
+  const int lda = (int)p.lda;
+  // activations at k >= K8 (K rounded up to 8) read as zero: the cast workspace holds
+  // zeros there anyway; fp16 A read in place (K % 8 == 0) would hold the next row
+  const int K8 = (int)((p.K + 7) / 8 * 8);
 
   // W rows of this lane (clamped: rows past N are computed and dropped)
   uint32_t wrow[SK_NS];
@@ -187,15 +191,16 @@ __global__ __launch_bounds__(SK_THREADS) void skinny_kernel(PrefillArgs p) {
         }
       }
     }
-    // activations: 32 fp16 of row 16 mt + ln per M tile (zero past Kp and past M)
+    // activations: 32 fp16 of row 16 mt + ln per M tile (zero past K8 and past M)
     f16x8 af[MB][4];
 #pragma unroll
     for (int mt = 0; mt < MB; ++mt) {
-      const uint32_t ao = ((uint32_t)(mt * 16 + ln) * (uint32_t)Kp + (uint32_t)(kin ? k0 : 0)) * 2u;
+      const uint32_t ao = ((uint32_t)(mt * 16 + ln) * (uint32_t)lda + (uint32_t)(kin ? k0 : 0)) * 2u;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const auto v = __builtin_amdgcn_raw_buffer_load_b128(rA, (int)(ao + 16u * j), 0, 0);
-        const uint4 u = kin ? make_uint4(v[0], v[1], v[2], v[3]) : make_uint4(0u, 0u, 0u, 0u);
+        const bool kj = kin && k0 + 8 * j < K8;
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(rA, (int)(kj ? ao + 16u * j : 0u), 0, 0);
+        const uint4 u = kj ? make_uint4(v[0], v[1], v[2], v[3]) : make_uint4(0u, 0u, 0u, 0u);
         af[mt][j] = __builtin_bit_cast(f16x8, u);
       }
     }
@@ -235,6 +240,7 @@ __global__ __launch_bounds__(SK_THREADS) void skinny_kernel(PrefillArgs p) {
       p.partials[((int64_t)ks * M + m) * p.ldc + n] = y;
       continue;
     }
+    if (p.row_scale) y *= p.row_scale[m];
     if (p.bias) y += sk_bias<CT>(p.bias, n);
     sk_store<CT>(p.C, (int64_t)m * p.ldc + n, y);
   }
@@ -339,7 +345,8 @@ hipError_t launch_skinny(const PrefillArgs& p0, hipStream_t st) {
     else if (zk == 2) sk_ct<GEMV_AFFINE, 4, 2>(p, st);
     else sk_ct<GEMV_AFFINE, 4, 0>(p, st);
   }
-  if (p.splits > 1) return launch_reduce_splits(p.partials, p.splits, p.M, p.N, p.ldc, p.bias, p.C, p.c_type, st);
+  if (p.splits > 1)
+    return launch_reduce_splits(p.partials, p.splits, p.M, p.N, p.ldc, p.row_scale, p.bias, p.C, p.c_type, st);
   return hipSuccess;
 }
 

@@ -19,7 +19,7 @@ QMM_ZP_NONE, QMM_ZP_PACKED, QMM_ZP_F16, QMM_ZP_UNIFORM = 0, 1, 2, 3
 QMOE_FP, QMOE_INT8_ACT = 0, 1
 STATUS = {0: "QMM_OK", -1: "QMM_E_NULL", -2: "QMM_E_DTYPE", -3: "QMM_E_BITS", -4: "QMM_E_BLOCK",
           -5: "QMM_E_SHAPE", -6: "QMM_E_ALIGN", -7: "QMM_E_WORKSPACE", -8: "QMM_E_MODE",
-          -9: "QMM_E_DEVICE"}
+          -9: "QMM_E_DEVICE", -10: "QMM_E_PARAM"}
 ENTRY_NBITS, ENTRY_CODEBOOK, ENTRY_QMOE_FC1, ENTRY_QMOE_FC2, ENTRY_QMOE_FUSED = 0, 1, 2, 3, 4
 
 
@@ -32,6 +32,10 @@ class QmmError(RuntimeError):
 
 class qmoe_weights(Structure):
     _fields_ = [("W", c_void_p), ("scales", c_void_p), ("zp", c_void_p), ("bias", c_void_p)]
+
+
+class qmm_qparams(Structure):
+    _fields_ = [("scale", c_float), ("zero_point", ctypes.c_int32)]
 
 
 _lib = None
@@ -62,9 +66,19 @@ _SIGS = {
                                   c_void_p, qmoe_weights, qmoe_weights, c_int, c_int, c_int,
                                   c_void_p, c_void_p, c_size_t, c_void_p]),
     "qmoe_decode_scratch_bytes": (c_size_t, [c_int64, c_int64, c_int64, c_int, c_int]),
+    "qmoe_decode_status": (c_int, [c_void_p, c_size_t, c_int64, c_int64, c_int64, c_int, c_int,
+                                   POINTER(c_int), c_void_p]),
     "qmm_validate_qmoe": (c_int, [c_void_p, c_int64, c_int64, c_int64, c_int64, c_int, c_void_p,
                                   c_void_p, qmoe_weights, qmoe_weights, c_int, c_int, c_int,
                                   c_void_p, c_void_p, c_size_t]),
+    "qmm_quantize_linear": (c_int, [c_void_p, c_int, c_int64, qmm_qparams, c_int, c_void_p, c_void_p]),
+    "qmm_dequantize_linear": (c_int, [c_void_p, c_int64, qmm_qparams, c_int, c_void_p, c_int, c_void_p]),
+    "qmm_fake_quantize": (c_int, [c_void_p, c_int, c_int64, qmm_qparams, c_int, c_void_p, c_void_p]),
+    "qmm_qsigmoid": (c_int, [c_void_p, c_int64, qmm_qparams, qmm_qparams, c_int, c_void_p, c_void_p]),
+    "qmm_qmul": (c_int, [c_void_p, qmm_qparams, c_void_p, qmm_qparams, c_int64, qmm_qparams, c_int,
+                         c_void_p, c_void_p]),
+    "qmm_qswiglu": (c_int, [c_void_p, c_void_p, c_int, c_int64, c_int, POINTER(qmm_qparams), c_void_p,
+                            c_void_p]),
     "qmm_set_tuning": (c_int, [c_int, c_int]),
     "qmm_num_candidates": (c_int, [c_int]),
     "qmm_tuned_choice": (c_int, [c_int]),
@@ -253,6 +267,97 @@ def qmoe_decode_fused(X, expert_ids, expert_w, fc1, fc2, H, I, E, block, mode=QM
                                  _qw(fc2), bits, block, mode, _ptr(out), _ptr(scratch),
                                  scratch.numel() * scratch.element_size(), _stream(stream))
     _check("qmoe_decode_fused", st)
+    return out
+
+
+def qmoe_decode_status(scratch, T, H, I, k, mode=QMOE_FP, stream=None) -> bool:
+    """True if a single-launch decode on `scratch` gave up its wait (clears the flag)."""
+    flag = c_int(0)
+    st = lib().qmoe_decode_status(_ptr(scratch), scratch.numel() * scratch.element_size(), T, H, I, k,
+                                  mode, ctypes.byref(flag), _stream(stream))
+    _check("qmoe_decode_status", st)
+    return bool(flag.value)
+
+
+# ---------------------------------------------------------------------------
+# activation quantization ops
+# ---------------------------------------------------------------------------
+
+def _qp(q):
+    s, z = q
+    return qmm_qparams(float(s), int(z))
+
+
+def _code_dtype(bits):
+    torch = _torch()
+    return torch.uint8 if bits == 8 else torch.uint16
+
+
+def quantize_linear(x, q, bits, out=None, stream=None):
+    """uint8 / uint16 codes of x under the per-tensor (scale, zero_point) q."""
+    torch = _torch()
+    x = _contig(x, "x")
+    if out is None:
+        out = torch.empty(x.shape, dtype=_code_dtype(bits), device=x.device)
+    _check("qmm_quantize_linear", lib().qmm_quantize_linear(_ptr(x), dtype_code(x), x.numel(), _qp(q), bits,
+                                                            _ptr(out), _stream(stream)))
+    return out
+
+
+def dequantize_linear(codes, q, bits, out_dtype=None, out=None, stream=None):
+    torch = _torch()
+    codes = _contig(codes, "codes")
+    if out is None:
+        out = torch.empty(codes.shape, dtype=out_dtype or torch.float32, device=codes.device)
+    _check("qmm_dequantize_linear", lib().qmm_dequantize_linear(_ptr(codes), codes.numel(), _qp(q), bits,
+                                                                _ptr(out), dtype_code(out), _stream(stream)))
+    return out
+
+
+def fake_quantize(x, q, bits, out=None, stream=None):
+    torch = _torch()
+    x = _contig(x, "x")
+    if out is None:
+        out = torch.empty_like(x)
+    _check("qmm_fake_quantize", lib().qmm_fake_quantize(_ptr(x), dtype_code(x), x.numel(), _qp(q), bits,
+                                                        _ptr(out), _stream(stream)))
+    return out
+
+
+def qsigmoid(codes, q_in, q_out, bits, out=None, stream=None):
+    torch = _torch()
+    codes = _contig(codes, "codes")
+    if out is None:
+        out = torch.empty_like(codes)
+    _check("qmm_qsigmoid", lib().qmm_qsigmoid(_ptr(codes), codes.numel(), _qp(q_in), _qp(q_out), bits, _ptr(out),
+                                              _stream(stream)))
+    return out
+
+
+def qmul(a, qa, b, qb, qc, bits, out=None, stream=None):
+    torch = _torch()
+    a, b = _contig(a, "a"), _contig(b, "b")
+    if a.numel() != b.numel():
+        raise ValueError("a and b differ in size")
+    if out is None:
+        out = torch.empty_like(a)
+    _check("qmm_qmul", lib().qmm_qmul(_ptr(a), _qp(qa), _ptr(b), _qp(qb), a.numel(), _qp(qc), bits, _ptr(out),
+                                      _stream(stream)))
+    return out
+
+
+def qswiglu(gate, up, qparams, bits, out=None, stream=None):
+    """Fused quantized SwiGLU chain; qparams: five (scale, zero_point) pairs
+    (gate, sigmoid, silu, up, out)."""
+    torch = _torch()
+    gate, up = _contig(gate, "gate"), _contig(up, "up")
+    if gate.numel() != up.numel() or gate.dtype != up.dtype:
+        raise ValueError("gate and up differ in size or dtype")
+    if out is None:
+        out = torch.empty_like(gate)
+    arr = (qmm_qparams * 5)(*[_qp(q) for q in qparams])
+    _check("qmm_qswiglu", lib().qmm_qswiglu(_ptr(gate), _ptr(up), dtype_code(gate), gate.numel(), bits, arr,
+                                            _ptr(out), _stream(stream)))
     return out
 
 

@@ -78,7 +78,9 @@ enum {
   QMM_E_ALIGN = -6,      /* a pointer is not aligned as the kernels require             */
   QMM_E_WORKSPACE = -7,  /* workspace/scratch missing or smaller than the query says    */
   QMM_E_MODE = -8,       /* unknown zero-point kind or MoE mode                         */
-  QMM_E_DEVICE = -9      /* no usable gfx950 device / library not initialised           */
+  QMM_E_DEVICE = -9,     /* no usable gfx950 device / library not initialised           */
+  QMM_E_PARAM = -10      /* a quantization scale not finite and positive, or a zero
+                            point outside the code range                                */
 };
 
 /* ---------------------------------------------------------------------------
@@ -216,8 +218,9 @@ qmm_status qmm_dequantize_codebook4(const uint8_t* W, int block, const float* ab
  *              work-group's h and runs its fc2 share.  The up-front timing picks the
  *              faster form per shape.  The one-launch form needs the compute units
  *              to itself for that wait: a kernel on another stream that holds them
- *              for more than 1 s makes the wait give up (error flag above).  int8
- *              mode: fc1, the h quantizer and fc2 as three launches.  Every form
+ *              for more than 1 s makes the wait give up (error flag above; the
+ *              call's Y is then filled with fp16 NaN and qmoe_decode_status reports
+ *              it).  int8 mode: fc1, the h quantizer and fc2 as three launches.  Every form
  *              gives the same bits.
  *   E          num_experts: the first call of a shape times tiling candidates on
  *              other expert sets, writing only scratch.
@@ -237,10 +240,64 @@ qmm_status qmoe_decode_fused(const uint16_t* X, int64_t T, int64_t H, int64_t I,
 
 size_t qmoe_decode_scratch_bytes(int64_t T, int64_t H, int64_t I, int k, int mode);
 
+/* qmoe_decode_status -- whether a single-launch qmoe_decode_fused call on this scratch
+ * buffer gave up its wait ([P2] "What": a call must not report an error it did not
+ * cause, nor hide one it did).  Reads the error word of the scratch layout above into
+ * *timed_out (HOST pointer: 1 = some call gave up, its Y was filled with fp16 NaN;
+ * 0 = none), then clears it.  T, H, I, k, mode: those of the calls made on the buffer.
+ * Synchronizes `stream`; int8 mode never waits and always reports 0.  Returns
+ * QMM_E_NULL / QMM_E_WORKSPACE / QMM_E_ALIGN for a missing, short or misaligned buffer,
+ * or the hipError_t of the copy. */
+qmm_status qmoe_decode_status(void* scratch, size_t scratch_bytes, int64_t T, int64_t H, int64_t I,
+                              int k, int mode, int* timed_out, void* stream);
+
 qmm_status qmm_validate_qmoe(const uint16_t* X, int64_t T, int64_t H, int64_t I, int64_t E,
                              int k, const int32_t* expert_ids, const float* expert_w,
                              qmoe_weights fc1, qmoe_weights fc2, int bits, int block, int mode,
                              const uint16_t* Y, const void* scratch, size_t scratch_bytes);
+
+/* ---------------------------------------------------------------------------
+ * Activation quantize / dequantize and the fused quantized SwiGLU
+ *                       ([P1] "Why": the per-layer chain Q(gate) -> qsigmoid -> 2x qmul ->
+ *                        Q(up) -> DQ; "What", commit 4: fused Q -> DQ round trip and
+ *                        fused quantized SwiGLU, each exactly equal to the unfused chain)
+ *
+ * Per-tensor parameters (scale, zero_point); codes are uint8 (bits = 8) or uint16
+ * (bits = 16).  Element by element:
+ *   Q(x)    = min(max(rint(fp32(x / scale)) + zero_point, 0), 2^bits - 1)
+ *             (ties to even, the quotient correctly rounded; a NaN quotient gives 0)
+ *   DQ(q)   = fp32((q - zero_point) * scale)
+ *   sigmoid = the fp32 rounding of 1 / (1 + e^-v), evaluated in fp64
+ * x, y: [n] of x_type / y_type (QMM_F32, QMM_F16, QMM_BF16; 16-bit outputs are the
+ * nearest value of the fp32 result).  Device pointers, element-aligned; codes
+ * 2-byte aligned for bits = 16.  scale must be finite and > 0, zero_point in
+ * [0, 2^bits - 1] (else QMM_E_PARAM); bits other than 8 and 16 give QMM_E_BITS.
+ * n = 0 launches nothing.  The fused ops give the bits of the unfused chain.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  float scale;
+  int32_t zero_point;
+} qmm_qparams;
+
+qmm_status qmm_quantize_linear(const void* x, int x_type, int64_t n, qmm_qparams q, int bits,
+                               void* codes, void* stream);
+qmm_status qmm_dequantize_linear(const void* codes, int64_t n, qmm_qparams q, int bits, void* y,
+                                 int y_type, void* stream);
+/* y = DQ(Q(x)), y of x_type: one launch, no code tensor. */
+qmm_status qmm_fake_quantize(const void* x, int x_type, int64_t n, qmm_qparams q, int bits,
+                             void* y, void* stream);
+/* codes_out = Q(sigmoid(DQ(codes_in; in)); out). */
+qmm_status qmm_qsigmoid(const void* codes_in, int64_t n, qmm_qparams in, qmm_qparams out, int bits,
+                        void* codes_out, void* stream);
+/* c = Q(fp32(DQ(a; qa) * DQ(b; qb)); qc). */
+qmm_status qmm_qmul(const void* a, qmm_qparams qa, const void* b, qmm_qparams qb, int64_t n,
+                    qmm_qparams qc, int bits, void* c, void* stream);
+/* The quantized SwiGLU chain in one launch, y of x_type:
+ *   g = Q(gate; q[0]);  t = qsigmoid(g -> q[1]);  m = qmul(g, t -> q[2]);
+ *   u = Q(up; q[3]);    h = qmul(m, u -> q[4]);   y = DQ(h; q[4]).
+ * q: HOST array of five parameter pairs (gate, sigmoid, silu, up, out). */
+qmm_status qmm_qswiglu(const void* gate, const void* up, int x_type, int64_t n, int bits,
+                       const qmm_qparams* q, void* y, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Tuning control and introspection.

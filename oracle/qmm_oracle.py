@@ -180,14 +180,43 @@ def dequant_codebook4(W, K, block, absmax, codebook) -> np.ndarray:
 # Matmuls  ([P1] "What", commit 1; [P3] "Summary", "Technical details")
 # ---------------------------------------------------------------------------
 
+def row_prescale_exponents(a64) -> np.ndarray:
+    """Per-row power-of-two pre-scale of the matrix-core activation cast.
+
+    For row m with largest magnitude |a| = f * 2^E (f in [0.5, 1)), the row is
+    multiplied by 2^s with s = min(15 - E, 126) before its fp16 rounding, which
+    puts the largest magnitude in [2^14, 2^15) (the cap keeps 2^-s a normal fp32
+    for rows of tiny values): no value overflows fp16 and the small values keep
+    their bits.  A row that is all zero, or whose largest magnitude is not finite,
+    is not scaled (exponent 0).  Returns the exponents s as int64 [M].
+    """
+    a = np.asarray(a64, dtype=np.float64)
+    amax = np.max(np.abs(a), axis=-1) if a.shape[-1] > 0 else np.zeros(a.shape[:-1])
+    out = np.zeros(amax.shape, dtype=np.int64)
+    ok = np.isfinite(amax) & (amax > 0)
+    _, E = np.frexp(np.where(ok, amax, 1.0))
+    out[ok] = np.minimum(15 - E[ok], 126)
+    return out
+
+
 def _round_operand(x64, mode):
-    """Declared operand rounding of a path that feeds 16-bit matrix cores."""
+    """Declared operand rounding of a path that feeds 16-bit matrix cores.
+
+    "f16": nearest fp16 of each value.  "bf16": nearest bf16 of the fp32 value.
+    "f16_rows": the activation cast of the matrix-core paths: each row m is scaled
+    by 2^s_m (row_prescale_exponents), rounded to the nearest fp16 and scaled back,
+    a' = fp16(a * 2^s_m) * 2^-s_m (both scalings are exact).
+    """
     if mode is None:
         return x64
     if mode == "f16":
         return to_f16(x64).astype(np.float64)
     if mode == "bf16":
         return to_bf16_f64(to_f32(x64))
+    if mode == "f16_rows":
+        x = np.asarray(x64, dtype=np.float64)
+        s = row_prescale_exponents(x)[..., None].astype(np.int32)
+        return np.ldexp(to_f16(np.ldexp(x, s)).astype(np.float64), -s)
     raise ValueError(mode)
 
 
@@ -359,12 +388,30 @@ def qmoe_decode(X_f16, ids, rw, fc1, fc2, H, I, block, bits=4, mode="fp"):
 # exactly equal to the unfused Q -> DQ chain)
 # ---------------------------------------------------------------------------
 
+def div_f32(x, s) -> np.ndarray:
+    """IEEE fp32 division x / s, correctly rounded (numpy's float32 divide)."""
+    return np.asarray(x, dtype=np.float32) / np.asarray(s, dtype=np.float32)
+
+
+def code_dtype(bits: int):
+    return np.uint8 if bits <= 8 else np.uint16
+
+
 def quantize_linear(x_f32, scale_f32, zp, bits):
-    """Unfused Q: q = clamp(round-half-even(fp32(x / s) + zp), 0, 2^bits - 1)."""
-    x = np.asarray(x_f32, dtype=np.float32).astype(np.float64)
-    s = np.asarray(scale_f32, dtype=np.float32).astype(np.float64)
-    t = to_f32(x / s).astype(np.float64)
-    return np.clip(np.rint(t + zp), 0, (1 << bits) - 1).astype(np.uint8)
+    """Unfused Q (ONNX QuantizeLinear): q = saturate(round-half-even(fp32(x / s)) + zp)
+    into [0, 2^bits - 1] (the addition exact in fp64); a NaN quotient gives code 0.
+    Codes are uint8 for bits <= 8, else uint16."""
+    with np.errstate(invalid="ignore", divide="ignore", over="ignore"):
+        t = div_f32(x_f32, scale_f32).astype(np.float64)
+        r = np.rint(t) + float(zp)
+    r = np.where(np.isnan(r), 0.0, np.clip(r, 0.0, float((1 << bits) - 1)))
+    return r.astype(code_dtype(bits))
+
+
+def dequantize_linear(q, scale_f32, zp) -> np.ndarray:
+    """Unfused DQ (ONNX DequantizeLinear): x = fp32((q - zp) * s); q - zp is exact."""
+    d = np.asarray(q, dtype=np.float64) - float(zp)
+    return to_f32(d * np.asarray(scale_f32, dtype=np.float32).astype(np.float64))
 
 
 def pack_codes(q, bits: int, block: int) -> np.ndarray:
@@ -383,11 +430,57 @@ def pack_codes(q, bits: int, block: int) -> np.ndarray:
 
 
 def fake_quantize(x_f32, scale_f32, zp, bits):
-    """Fused Q -> DQ: x_hat = fp32(fp32(clamp(rint(fp32(x/s) + zp)) - zp) * s)."""
-    x = np.asarray(x_f32, dtype=np.float32).astype(np.float64)
+    """Fused Q -> DQ ([P1] "What", commit 4): x_hat = fp32((c - zp) * s) with
+    c = clamp(rint(fp32(x / s)) + zp, 0, 2^bits - 1) (a NaN quotient gives c = 0)."""
     s = np.asarray(scale_f32, dtype=np.float32).astype(np.float64)
-    code = np.clip(np.rint(to_f32(x / s).astype(np.float64) + zp), 0.0, float((1 << bits) - 1))
+    with np.errstate(invalid="ignore", divide="ignore", over="ignore"):
+        code = np.rint(div_f32(x_f32, scale_f32).astype(np.float64)) + float(zp)
+    code = np.where(np.isnan(code), 0.0, np.clip(code, 0.0, float((1 << bits) - 1)))
     return to_f32(to_f32(code - zp).astype(np.float64) * s)
+
+
+# ---------------------------------------------------------------------------
+# Quantized activation ops and the quantized SwiGLU chain  ([P1] "Why": the
+# per-layer chain Q(gate) -> qsigmoid -> 2x qmul -> Q(up) -> DQ; "What", commit 4:
+# a fused quantized SwiGLU exactly equal to the unfused chain)
+# ---------------------------------------------------------------------------
+
+def sigmoid_f32(v_f32) -> np.ndarray:
+    """Logistic function of fp32 inputs, computed in fp64 and rounded once to fp32."""
+    v = np.asarray(v_f32, dtype=np.float32).astype(np.float64)
+    with np.errstate(over="ignore"):
+        return to_f32(1.0 / (1.0 + np.exp(-v)))
+
+
+def qsigmoid(q_in, s_in, z_in, s_out, z_out, bits):
+    """Quantized sigmoid: Q(sigmoid(DQ(q_in)); s_out, z_out)."""
+    return quantize_linear(sigmoid_f32(dequantize_linear(q_in, s_in, z_in)), s_out, z_out, bits)
+
+
+def qmul(qa, sa, za, qb, sb, zb, sc, zc, bits):
+    """Quantized product: Q(fp32(DQ(qa) * DQ(qb)); sc, zc) (the fp32 product is one rounding)."""
+    p = to_f32(dequantize_linear(qa, sa, za).astype(np.float64) * dequantize_linear(qb, sb, zb).astype(np.float64))
+    return quantize_linear(p, sc, zc, bits)
+
+
+def qswiglu(gate_f32, up_f32, qp, bits):
+    """Quantized SwiGLU chain, in the order of the activation graph:
+
+        g = Q(gate; gate params)
+        t = qsigmoid(g -> sigmoid params)
+        m = qmul(g, t -> silu params)          (silu = gate * sigmoid(gate))
+        u = Q(up; up params)
+        h = qmul(m, u -> out params)
+        y = DQ(h; out params)                   (fp32)
+
+    qp: five (scale, zero_point) pairs: gate, sigmoid, silu, up, out."""
+    (sg, zg), (st, zt), (sm, zm), (su, zu), (sh, zh) = qp
+    g = quantize_linear(gate_f32, sg, zg, bits)
+    t = qsigmoid(g, sg, zg, st, zt, bits)
+    m = qmul(g, sg, zg, t, st, zt, sm, zm, bits)
+    u = quantize_linear(up_f32, su, zu, bits)
+    h = qmul(m, sm, zm, u, su, zu, sh, zh, bits)
+    return dequantize_linear(h, sh, zh)
 
 
 # ---------------------------------------------------------------------------

@@ -76,6 +76,70 @@ def zp_args(O, p):
     return dict(zp=None, zp_kind=O.ZP_NONE)
 
 
+def fr_round(x, mant_bits, emin):
+    """Nearest binary float with `mant_bits` significant bits and minimum normal
+    exponent `emin` (subnormals below it), ties to even, for a Fraction x.
+    Written from the definition: pick the spacing of x's binade, round the
+    quotient.  fp16: (11, -14); bf16: (8, -126)."""
+    if x == 0:
+        return Fr(0)
+    sign = -1 if x < 0 else 1
+    ax = abs(x)
+    # exponent e with 2^e <= ax < 2^(e+1)
+    e = ax.numerator.bit_length() - ax.denominator.bit_length()
+    if Fr(2) ** e > ax:
+        e -= 1
+    e = max(e, emin)
+    ulp = Fr(2) ** (e - mant_bits + 1)
+    q = ax / ulp
+    n = q.numerator // q.denominator
+    r = q - n
+    if r > Fr(1, 2) or (r == Fr(1, 2) and n % 2 == 1):
+        n += 1
+    return sign * n * ulp
+
+
+def row_shift(row_values):
+    """Exponent s with 2^14 <= max|a| * 2^s < 2^15, at most 126 (0 for a zero row)."""
+    mx = max(abs(v) for v in row_values)
+    if mx == 0:
+        return 0
+    s = 0
+    while mx * Fr(2) ** s >= 2 ** 15:
+        s -= 1
+    while mx * Fr(2) ** s < 2 ** 14:
+        s += 1
+    return min(s, 126)
+
+
+def fr_rint(t):
+    """Round a Fraction to the nearest integer, ties to even."""
+    r = t.numerator // t.denominator
+    frac = t - r
+    return r + 1 if frac > Fr(1, 2) or (frac == Fr(1, 2) and r % 2 == 1) else r
+
+
+def ref_quantize(x, s, zp, bits):
+    """QuantizeLinear from its definition: the quotient rounded to fp32 (24 significant
+    bits), then to an integer (ties to even), plus the zero point, saturated."""
+    xf, sf = float(np.float32(x)), float(np.float32(s))
+    if math.isnan(xf):
+        return 0
+    if math.isinf(xf):
+        return (1 << bits) - 1 if (xf > 0) == (sf > 0) else 0
+    t = fr_round(Fr(xf) / Fr(sf), 24, -126)
+    return min(max(fr_rint(t) + zp, 0), (1 << bits) - 1)
+
+
+def ref_dequantize(q, s, zp):
+    return fr_round((Fr(int(q)) - zp) * Fr(float(np.float32(s))), 24, -126)
+
+
+def ref_sigmoid(v):
+    """fp32 rounding of 1 / (1 + e^-v) with e^-v from math.exp."""
+    return fr_round(1 / (1 + Fr(math.exp(-float(v)))), 24, -126)
+
+
 # ---------------------------------------------------------------------------
 # pins
 # ---------------------------------------------------------------------------
@@ -230,13 +294,10 @@ def pin_fake_quant_chain(O, seed=19):
         packed = O.pack_codes(q, bits, block)
         chain = O.dequant_nbits(packed, bits, K, block, s16.view(np.uint16), None, O.ZP_NONE)
         assert np.array_equal(fused.view(np.uint32), chain.view(np.uint32)), bits
-        # integer zero point: Q is saturate(round-half-even(x / s) + zp) (QuantizeLinear)
+        # integer zero point: Q is saturate(round-half-even(x / s) + zp) (QuantizeLinear),
+        # with x / s the correctly rounded fp32 quotient
         for i in range(64):
-            t = float(np.float32(float(x[1, i]) / float(s_full[1, i])))
-            r = math.floor(t)
-            frac = t - r
-            rr = r + 1 if frac > 0.5 or (frac == 0.5 and r % 2 == 1) else r
-            assert int(q[1, i]) == min(max(rr + zp_int, 0), (1 << bits) - 1)
+            assert int(q[1, i]) == ref_quantize(x[1, i], s_full[1, i], zp_int, bits)
 
 
 def pin_bf16_rounding(O, seed=23):
@@ -426,7 +487,155 @@ def pin_qmoe_composition(O, seed=41):
     assert np.allclose(got[0], want, rtol=1e-14, atol=0)
 
 
+def pin_round_operand(O, seed=43):
+    """Declared operand roundings of the matrix-core paths vs exact rationals.
+
+    A' is the per-row pre-scaled fp16 rounding (f16_rows), W' the fp16 rounding of
+    the exact dequantized weight; each is checked alone and together, on rows whose
+    largest value overflows fp16, rows of tiny values and ordinary rows.  Integer
+    activations up to 2^11 make the activation rounding the identity."""
+    rng = np.random.default_rng(seed)
+    K, N, block = 40, 3, 16
+    p = gen.nbits_problem(4, K, N, 4, block, seed=seed, zp="packed", scale_range=(0.01, 0.05))
+    A = rng.standard_normal((4, K))
+    A[1] *= 3e5            # largest values past the fp16 range
+    A[2] *= 1e-7           # every value below the smallest normal fp16
+    A[3, 5] = 7e4          # one large value in a row of ordinary ones
+    A = A.astype(np.float32)
+    w = O.dequant_nbits(p["W"], 4, K, block, p["scales"], p["zp"], O.ZP_PACKED)
+    a_fr = [[fr32(A[m, k]) for k in range(K)] for m in range(4)]
+    w_fr = [[Fr(float(w[n, k])) for k in range(K)] for n in range(N)]
+    a16 = []
+    for m in range(4):
+        s = row_shift(a_fr[m])
+        assert s == int(O.row_prescale_exponents(A.astype(np.float64))[m]), ("shift", m)
+        a16.append([fr_round(v * Fr(2) ** s, 11, -14) / Fr(2) ** s for v in a_fr[m]])
+    w16 = [[fr_round(v, 11, -14) for v in row] for row in w_fr]
+    for a_round, w_round, aa, ww in ((None, None, a_fr, w_fr), ("f16_rows", None, a16, w_fr),
+                                     (None, "f16", a_fr, w16), ("f16_rows", "f16", a16, w16)):
+        y = O.qmm_nbits(A, "f32", p["W"], 4, K, block, p["scales"], p["zp"], O.ZP_PACKED,
+                        a_round=a_round, w_round=w_round)
+        for m in range(4):
+            for n in range(N):
+                exact = sum(aa[m][k] * ww[n][k] for k in range(K))
+                mag = sum(abs(float(aa[m][k] * ww[n][k])) for k in range(K)) + 1e-300
+                err = abs(float(Fr(float(y[m, n])) - exact)) / mag
+                assert err < 1e-13, (a_round, w_round, m, n, err)
+    # the pre-scaled rounding keeps every row finite and the tiny row's bits
+    r = O._round_operand(A.astype(np.float64), "f16_rows")
+    assert np.all(np.isfinite(r))
+    assert np.max(np.abs(r[2] / A[2].astype(np.float64) - 1)) < 2.0 ** -11
+    # integer activations |a| <= 2^11: the rounding is the identity
+    Ai = rng.integers(-2048, 2049, size=(3, K)).astype(np.float64)
+    assert np.array_equal(O._round_operand(Ai, "f16_rows"), Ai)
+    # bf16 of fp32 values vs the rational rounding to 8 significant bits
+    v = (rng.standard_normal(200) * 10.0 ** rng.integers(-3, 4, size=200)).astype(np.float32)
+    got = O._round_operand(v.astype(np.float64), "bf16")
+    for i in range(len(v)):
+        assert Fr(float(got[i])) == fr_round(fr32(v[i]), 8, -126), i
+    # the codebook entry applies the same roundings
+    pc = gen.codebook_problem(2, K, N, seed=seed + 1, a_dtype="f32", block=block)
+    pc["A"] = A[:2].copy()
+    wc = O.dequant_codebook4(pc["W"], K, block, pc["absmax"], pc["codebook"])
+    yc = O.qmm_codebook4(pc["A"], "f32", pc["W"], K, block, pc["absmax"], pc["codebook"],
+                         a_round="f16_rows", w_round="f16")
+    for m in range(2):
+        for n in range(N):
+            exact = sum(a16[m][k] * fr_round(Fr(float(wc[n, k])), 11, -14) for k in range(K))
+            mag = sum(abs(float(a16[m][k] * Fr(float(wc[n, k])))) for k in range(K)) + 1e-300
+            assert abs(float(Fr(float(yc[m, n])) - exact)) / mag < 1e-13, (m, n)
+
+
+def pin_rel_l2(O):
+    """Relative L2 on closed-form vectors."""
+    ref = np.array([3.0, 4.0])
+    assert O.rel_l2(ref, ref) == 0.0
+    assert O.rel_l2(np.array([3.0, 4.5]), ref) == 0.1                 # 0.5 / 5
+    assert O.rel_l2(np.array([0.0, 0.0]), ref) == 1.0
+    assert O.rel_l2(np.array([6.0, 8.0]), ref) == 1.0
+    m = np.array([[1.0, 2.0], [2.0, 4.0]])                             # norm 5
+    assert O.rel_l2(m + np.array([[0.0, 0.0], [0.0, 1.0]]), m) == 0.2  # whole array, not per row
+    assert O.rel_l2(np.array([3.0, 4.0]), np.zeros(2)) == 5.0          # absolute when ref = 0
+    v = np.array([1.0, -2.0, 2.0])                                     # norm 3
+    assert abs(O.rel_l2(v + np.array([0.3, 0.0, 0.0]), v) - 0.1) < 1e-15
+    assert abs(O.rel_l2(1e3 * (v + 0.1), 1e3 * v) - O.rel_l2(v + 0.1, v)) < 1e-15
+
+
+def pin_quantized_ops(O, seed=47):
+    """QuantizeLinear / DequantizeLinear, the quantized sigmoid and product, and the
+    quantized SwiGLU chain against their definitions in exact rational arithmetic (fp32
+    quotients and products rounded from the exact value, ties to even), on random values,
+    exact ties, saturation, NaN and infinities; plus closed forms (a zero gate gives 0)."""
+    rng = np.random.default_rng(seed)
+    for bits in (8, 16):
+        qmax = (1 << bits) - 1
+        s = np.float32(2.0 ** -6 if bits == 8 else 2.0 ** -12)
+        zp = 1 << (bits - 1)
+        x = (rng.standard_normal(300) * 1.5).astype(np.float32)
+        ties = ((rng.integers(-100, 100, size=40) + 0.5) * float(s)).astype(np.float32)
+        specials = np.array([0.0, -0.0, 1e30, -1e30, np.inf, -np.inf, np.nan, float(s) * (qmax + 5)],
+                            dtype=np.float32)
+        xs = np.concatenate([x, ties, specials])
+        q = O.quantize_linear(xs, s, zp, bits)
+        assert q.dtype == (np.uint8 if bits == 8 else np.uint16)
+        for i, v in enumerate(xs):
+            assert int(q[i]) == ref_quantize(v, s, zp, bits), ("Q", bits, i, v)
+        # a scale that is not a power of two: the fp32 quotient decides, most visibly for
+        # values next to a rounding tie ((k + 1/2) * s rounded to fp32)
+        s2 = np.float32(0.0123)
+        near = ((rng.integers(-60, 60, size=200) + 0.5) * np.float64(s2)).astype(np.float32)
+        # and their fp32 neighbours, a few ulps either side of the tie
+        nb = near.view(np.int32)[:, None] + np.arange(-3, 4, dtype=np.int32)[None, :]
+        xn = np.concatenate([x, nb.ravel().view(np.float32)])
+        q2 = O.quantize_linear(xn, s2, 3, bits)
+        for i, v in enumerate(xn):
+            assert int(q2[i]) == ref_quantize(v, s2, 3, bits), ("Q s2", bits, i)
+        codes = rng.integers(0, qmax + 1, size=200)
+        d = O.dequantize_linear(codes, s2, 77)
+        for i, c in enumerate(codes):
+            assert Fr(float(d[i])) == ref_dequantize(c, s2, 77), ("DQ", bits, i)
+        # fused Q -> DQ is the chain
+        fq = O.fake_quantize(xs, s2, 5, bits)
+        ch = O.dequantize_linear(O.quantize_linear(xs, s2, 5, bits), s2, 5)
+        assert np.array_equal(fq.view(np.uint32), ch.view(np.uint32))
+        # quantized sigmoid and product, one code at a time
+        sin, zin = np.float32(8.0 / qmax), zp
+        sout, zout = np.float32(1.0 / qmax), 0
+        qi = rng.integers(0, qmax + 1, size=200)
+        qs = O.qsigmoid(qi, sin, zin, sout, zout, bits)
+        for i, c in enumerate(qi):
+            t = fr_round(Fr(float(ref_dequantize(c, sin, zin))), 24, -126)
+            y = ref_sigmoid(float(t))
+            assert int(qs[i]) == min(max(fr_rint(fr_round(y / Fr(float(sout)), 24, -126)) + zout, 0), qmax), i
+        assert np.all(np.diff(O.qsigmoid(np.arange(qmax + 1), sin, zin, sout, zout, bits).astype(np.int64)) >= 0)
+        qa = rng.integers(0, qmax + 1, size=200)
+        qb = rng.integers(0, qmax + 1, size=200)
+        sa, sb, sc = np.float32(0.031), np.float32(0.017), np.float32(0.0093)
+        qc = O.qmul(qa, sa, 100, qb, sb, 9, sc, 40, bits)
+        for i in range(200):
+            prod = fr_round(ref_dequantize(qa[i], sa, 100) * ref_dequantize(qb[i], sb, 9), 24, -126)
+            assert int(qc[i]) == min(max(fr_rint(fr_round(prod / Fr(float(sc)), 24, -126)) + 40, 0), qmax), i
+        # the SwiGLU chain, element by element
+        qp = [(np.float32(6.0 / qmax), zp), (np.float32(1.0 / qmax), 0), (np.float32(7.0 / qmax), zp),
+              (np.float32(6.0 / qmax), zp), (np.float32(9.0 / qmax), zp)]
+        gate = (rng.standard_normal(150) * 1.2).astype(np.float32)
+        up = (rng.standard_normal(150) * 1.2).astype(np.float32)
+        gate[:3] = [0.0, 100.0, -100.0]
+        y = O.qswiglu(gate, up, qp, bits)
+        for i in range(150):
+            g = ref_quantize(gate[i], qp[0][0], qp[0][1], bits)
+            gd = ref_dequantize(g, *qp[0])
+            t = min(max(fr_rint(fr_round(ref_sigmoid(float(gd)) / Fr(float(qp[1][0])), 24, -126)) + qp[1][1], 0), qmax)
+            m_ = fr_round(gd * ref_dequantize(t, *qp[1]), 24, -126)
+            m = min(max(fr_rint(fr_round(m_ / Fr(float(qp[2][0])), 24, -126)) + qp[2][1], 0), qmax)
+            u = ref_quantize(up[i], qp[3][0], qp[3][1], bits)
+            h_ = fr_round(ref_dequantize(m, *qp[2]) * ref_dequantize(u, *qp[3]), 24, -126)
+            h = min(max(fr_rint(fr_round(h_ / Fr(float(qp[4][0])), 24, -126)) + qp[4][1], 0), qmax)
+            assert Fr(float(y[i])) == ref_dequantize(h, *qp[4]), ("swiglu", bits, i)
+        assert y[0] == 0.0   # a zero gate gives silu 0 and an output of 0
+
+
 ALL_PINS = [pin_unpack_exhaustive, pin_nbits_bruteforce, pin_nbits_closed_forms,
             pin_codebook_bruteforce, pin_codebook_linear_equals_affine, pin_fake_quant_chain,
             pin_bf16_rounding, pin_f16_rounding, pin_swiglu, pin_int8_quantizer, pin_uniform_zp,
-            pin_qmoe_bruteforce, pin_qmoe_composition]
+            pin_qmoe_bruteforce, pin_qmoe_composition, pin_round_operand, pin_rel_l2, pin_quantized_ops]

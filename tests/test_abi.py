@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     L = Q.lib()
-    for code in range(-9, 1):
+    for code in range(-10, 1):
         assert L.qmm_status_string(code)
 
 
@@ -92,14 +92,16 @@ def _splits(M, N, kp):
                                    (2048, 5120, 7680), (2048, 5120, 100352), (9, 70, 33),
                                    (8, 4096, 4096), (4, 4096, 14336), (3, 4096, 1024)])
 def test_workspace_sizes(M, K, N):
-    """Padded fp16 A plus the fp32 partial sums of a split reduction: qmm_nbits from
-    M = 9 on, qmm_codebook4 from M = 4 on (its 16-bit outputs take the skinny kernel)."""
+    """Padded fp16 A, the fp32 row scales of its cast and the fp32 partial sums of a split
+    reduction (each from a 256-byte boundary): qmm_nbits from M = 9 on, qmm_codebook4 from
+    M = 4 on (its 16-bit outputs take the skinny kernel)."""
     need = Q.lib().qmm_nbits_workspace_bytes(M, K, N, Q.QMM_BF16)
     need_cb = Q.lib().qmm_codebook4_workspace_bytes(M, K, N, Q.QMM_BF16)
     kp = -(-K // 64) * 64
     a16 = -(-M * kp * 2 // 256) * 256
+    rs = -(-M * 4 // 256) * 256
     s = _splits(M, N, kp)
-    full = a16 + (s * M * N * 4 if s > 1 else 0)
+    full = a16 + rs + (s * M * N * 4 if s > 1 else 0)
     assert need == (0 if M <= 8 else full)
     assert need_cb == (0 if M < 4 else full)
 
@@ -128,6 +130,8 @@ def test_validate_codebook_codes():
     need = Q.lib().qmm_codebook4_workspace_bytes(4, 4096, 1024, Q.QMM_BF16)
     assert _v_cb(M=4, ws=FAKE, wsb=need) == 0
     assert _v_cb(M=4, ws=FAKE, wsb=need - 1) == -7
+    assert _v_cb(M=4, ws=FAKE + 8, wsb=need) == -6    # the workspace must be 16-byte aligned
+    assert _v_cb(M=16, ws=FAKE + 4, wsb=need * 4) == -6
 
 
 def _v_moe(**kw):
@@ -191,3 +195,17 @@ def test_scratch_queries():
     # int8: h, then x codes, x scales, h codes, h scales
     assert i8 == a256(4 * 2880 * 2) + a256(2880) + a256(90 * 4) + a256(4 * 2880) + a256(4 * 90 * 4)
     assert L.qmoe_decode_scratch_bytes(8, 2048, 768, 8, Q.QMOE_FP) == a256(64 * 768 * 2) + a256(16)
+
+
+def test_decode_status_refusals():
+    """Host-side refusals of qmoe_decode_status (no GPU work is reached)."""
+    L = Q.lib()
+    flag = ctypes.c_int(7)
+    assert L.qmoe_decode_status(FAKE, 1 << 20, 1, 2880, 2880, 4, Q.QMOE_FP, None, None) == -1
+    assert L.qmoe_decode_status(FAKE, 1 << 20, 1, 2880, 2880, 4, 5, ctypes.byref(flag), None) == -8
+    assert L.qmoe_decode_status(None, 1 << 20, 1, 2880, 2880, 4, Q.QMOE_FP, ctypes.byref(flag), None) == -1
+    assert L.qmoe_decode_status(FAKE, 16, 1, 2880, 2880, 4, Q.QMOE_FP, ctypes.byref(flag), None) == -7
+    assert L.qmoe_decode_status(FAKE + 16, 1 << 20, 1, 2880, 2880, 4, Q.QMOE_FP, ctypes.byref(flag), None) == -6
+    # int8 mode never waits: 0 without touching the buffer
+    assert L.qmoe_decode_status(None, 0, 1, 2880, 2880, 4, Q.QMOE_INT8_ACT, ctypes.byref(flag), None) == 0
+    assert flag.value == 0

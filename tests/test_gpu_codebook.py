@@ -6,7 +6,7 @@ from gemm_qmm_nbits_amd import inputs as gen
 from gemm_qmm_nbits_amd import qmm as Q
 from oracle import qmm_oracle as O
 
-from gpu_util import TOL, dev, dev_act, host_bits, host_f64, sample_rows, say, torch
+from gpu_util import TOL, assert_elementwise, column_chunks, dev, dev_act, gamma, host_bits, host_f64, say, torch
 
 pytestmark = pytest.mark.gpu
 
@@ -41,22 +41,52 @@ class CbDev:
                                p["codebook"], bias=p["bias"], rows=rows, w_round=w_round,
                                a_round=a_round)
 
-    def check(self, y, rows=None, label=""):
-        """GEMV path: against the exact oracle.  Matrix-core path: against the oracle
-        with its declared operand roundings (A and W to fp16); the error against the exact
-        oracle is printed for information."""
+    def reference(self, a_round=None, w_round=None):
+        """Whole-width oracle, one column chunk at a time: (exact, mirrored, sum |a'||w'|)."""
+        p = self.p
+        a = O.activations_f64(p["A"], p["a_dtype"])
+        am = O._round_operand(a, a_round) if a_round else a
+        b = None if p["bias"] is None else O.activations_f64(p["bias"], p["a_dtype"])
+        N = p["N"]
+        exact = np.zeros((a.shape[0], N))
+        mirr = np.zeros((a.shape[0], N))
+        absdot = np.zeros((a.shape[0], N))
+        for cols in column_chunks(N):
+            w = O.dequant_codebook4(np.asarray(p["W"])[cols], p["K"], p["block"],
+                                    np.asarray(p["absmax"])[cols], p["codebook"]).astype(np.float64)
+            wm = O._round_operand(w, w_round) if w_round else w
+            bc = None if b is None else b[cols]
+            exact[:, cols] = O.matmul_f64(a, w, bc)
+            mirr[:, cols] = O.matmul_f64(am, wm, bc)
+            absdot[:, cols] = np.abs(am) @ np.abs(wm).T
+        return exact, mirr, absdot
+
+    def check(self, y, label=""):
+        """Every output column.  GEMV path: against the exact oracle, every element within
+        the bound of fp32 accumulation.  Matrix-core path: against the oracle with its
+        declared operand roundings (A: per-row pre-scaled fp16 unless already fp16, W: fp16),
+        every element within the bound of fp32 accumulation of those products, and for a
+        16-bit output also against the unrounded oracle at the same tolerance."""
         got = host_f64(y)
-        if rows is not None:
-            got = got[:, rows]
-        tol = TOL[self.p["a_dtype"]]
+        out_dt = {torch().float32: "f32", torch().float16: "f16", torch().bfloat16: "bf16"}[y.dtype]
+        tol = TOL[out_dt]
+        K = self.p["K"]
         if cb_matrix_path(self.p["A"].shape[0], self.p["block"], y.dtype):
-            err = O.rel_l2(got, self.oracle(rows=rows, a_round="f16", w_round="f16"))
-            raw = O.rel_l2(got, self.oracle(rows=rows))
+            a_round = None if self.p["a_dtype"] == "f16" else "f16_rows"
+            exact, mirr, absdot = self.reference(a_round=a_round, w_round="f16")
+            err = O.rel_l2(got, mirr)
+            raw = O.rel_l2(got, exact)
             say(f"  {label} relL2(mirrored)={err:.3e} relL2(exact)={raw:.3e}")
+            assert err <= tol, (label, err)
+            if out_dt != "f32":
+                assert raw <= tol, (label, raw)
+            assert_elementwise(got, mirr, gamma(K + 2) * absdot, out_dt, label)
         else:
-            err = O.rel_l2(got, self.oracle(rows=rows))
+            exact, _, absdot = self.reference()
+            err = O.rel_l2(got, exact)
             say(f"  {label} relL2={err:.3e}")
-        assert err <= tol, (label, err)
+            assert err <= tol, (label, err)
+            assert_elementwise(got, exact, gamma(K + 4) * absdot, out_dt, label)
 
 
 @pytest.mark.parametrize("out", ["f32", "f16"])
@@ -85,8 +115,7 @@ def test_codebook_config_shapes(name, M, a_dtype):
     p = gen.codebook_problem(M, K, N, seed=gen.config_seed(2, 10 * idx + M), a_dtype=a_dtype)
     d = CbDev(p)
     y = d.run()
-    rows = sample_rows(N, 2048, seed=N + M)
-    d.check(y, rows=rows, label=f"{name} M={M}")
+    d.check(y, label=f"{name} M={M}")
 
 
 @pytest.mark.parametrize("M", [1, 3, 8])
@@ -107,12 +136,10 @@ def test_codebook_small_m_paths(M, out):
                              bias=(out == "same"))
     d = CbDev(p)
     if out == "f32":
-        y = Q.qmm_codebook4(d.A, d.W, d.absmax, d.cb, p["K"], p["block"], None,
+        y = Q.qmm_codebook4(d.A, d.W, d.absmax, d.cb, p["K"], p["block"], d.bias,
                             out_dtype=t.float32)
         assert not cb_matrix_path(M, p["block"], y.dtype)
-        err = O.rel_l2(host_f64(y), d.oracle())
-        say(f"  M={M} fp32 out relL2={err:.3e}")
-        assert err <= TOL["f32"], err
+        d.check(y, label=f"M={M} fp32 out")
     else:
         y = d.run()
         assert cb_matrix_path(M, p["block"], y.dtype)
@@ -137,9 +164,7 @@ def test_codebook_gemv_forms(M, K, N, block, out):
     od = None if out == "same" else t.float32
     y = Q.qmm_codebook4(d.A, d.W, d.absmax, d.cb, K, block, d.bias, out_dtype=od)
     assert not cb_matrix_path(M, block, y.dtype)
-    err = O.rel_l2(host_f64(y), d.oracle())
-    say(f"  M={M} K={K} N={N} block={block} {out}: relL2={err:.3e}")
-    assert err <= (TOL["f32"] if out == "f32" else TOL["bf16"]), err
+    d.check(y, label=f"M={M} K={K} N={N} block={block} {out}")
 
 
 def test_codebook_repeat_bit_identical():

@@ -6,7 +6,8 @@ from gemm_qmm_nbits_amd import inputs as gen
 from gemm_qmm_nbits_amd import qmm as Q
 from oracle import qmm_oracle as O
 
-from gpu_util import TOL, NbitsDev, dev, host_bits, host_f64, oracle_zp_kind, sample_rows, say, torch
+from gpu_util import (TOL, NbitsDev, assert_elementwise, dev, dev_act, gamma, host_bits, host_f64, nbits_reference,
+                      oracle_zp_kind, say, torch)
 
 pytestmark = pytest.mark.gpu
 
@@ -76,14 +77,29 @@ def test_dequant_matches_fake_quant():
 
 # --- GEMV path (M <= 8) -------------------------------------------------------
 
-def _check(d, got, rows=None, label=""):
-    ref = d.oracle(O, rows=rows)
+def _bias_args(d):
+    """Bias as the oracle takes it: fp32 values, or the stored 16-bit patterns."""
+    bias = d.p["bias"]
+    if bias is not None and d.c_dtype != "f32":
+        return host_bits(d.bias).view(np.uint16), d.c_dtype
+    return bias, "f32"
+
+
+def _check(d, got, label=""):
+    """GEMV path: every output column against the exact oracle (relative L2 gate) and
+    every element within the bound of the GEMV's arithmetic: fp32 roundings over the
+    products and the zero-point fold, plus the 23-bit block fixed point of A."""
+    bias, bdt = _bias_args(d)
+    r = nbits_reference(O, d.p, bias=bias, bias_dtype=bdt)
     y = host_f64(got)
-    if rows is not None:
-        y = y[:, rows]
-    err = O.rel_l2(y, ref)
+    err = O.rel_l2(y, r["exact"])
     say(f"  {label} relL2={err:.3e} (tol {TOL[d.c_dtype]:.0e})")
     assert err <= TOL[d.c_dtype], (label, err)
+    a = O.activations_f64(d.p["A"], d.p["a_dtype"])
+    K = d.p["K"]
+    bound = gamma(2 * K + 8) * (r["absdot"] + r["zsdot"]) + 2.0 ** -22 * np.abs(a).max(axis=1)[:, None] * r["wsum"][None, :]
+    assert_elementwise(y, r["exact"], bound, d.c_dtype, label)
+    return err
 
 
 def test_tiny_u4_config():
@@ -106,8 +122,7 @@ def test_phi4_u2_decode_full_size(name):
     torch().cuda.synchronize()
     # the uniform-scalar path and the fp16-tensor path give the same bits
     assert np.array_equal(host_bits(got_u), host_bits(got_t))
-    rows = None if N <= 8192 else sample_rows(N, 1024, seed=N)
-    _check(d, got_u, rows=rows, label=name)
+    _check(d, got_u, label=name)
 
 
 @pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 11])
@@ -118,6 +133,9 @@ def test_phi4_u2_decode_full_size(name):
     (2, 16, 512, 130, "f16", "f32", "f16"),
     (2, 16, 70, 33, "packed", "f32", "f32"),     # 20-byte rows: generic kernel
     (4, 256, 1536, 64, "f16", "bf16", "f32"),
+    (2, 64, 5120, 300, "f16_uniform", "f16", "f16"),   # u2 planes from fp16 activations
+    (2, 64, 1000, 260, "packed", "bf16", "f32"),       # u2 planes from bf16 activations
+    (2, 32, 2048, 129, "none", "f16", "f32"),
 ])
 def test_gemv_small_shapes(M, bits, block, K, N, zp, a, c):
     say(f"gemv M={M} bits={bits} block={block} K={K} N={N} zp={zp} a={a} c={c}")
@@ -207,23 +225,48 @@ def test_refused_arguments_on_device():
 
 # --- prefill path (M > 8): A rounded to fp16 once, fp16 weights, fp32 accumulation ---
 
-def _check_prefill(d, got, rows=None, label=""):
-    """Gate against the oracle with the path's declared operand roundings (A and W
-    to fp16); the error against the unrounded oracle is printed for information."""
+def _a_mirror(a_dtype):
+    """Declared activation rounding of the matrix-core paths: fp32 and bf16 A are cast with
+    the per-row power-of-two pre-scale; fp16 A is used as it is."""
+    return None if a_dtype == "f16" else "f16_rows"
+
+
+def _check_prefill(d, got, mrows=None, label=""):
+    """Matrix-core paths: every output column against the oracle with the path's declared
+    operand roundings (A: per-row pre-scaled fp16, W: fp16), every element within the
+    bound of fp32 accumulation of those exact products, and, for a 16-bit output, the
+    unrounded oracle at the same tolerance.  mrows: the output rows compared (all when
+    None)."""
+    bias, bdt = _bias_args(d)
+    A = d.p["A"] if mrows is None else np.asarray(d.p["A"])[mrows]
+    r = nbits_reference(O, d.p, A=A, bias=bias, bias_dtype=bdt, a_mirror=_a_mirror(d.p["a_dtype"]),
+                        w_mirror="f16")
     y = host_f64(got)
-    if rows is not None:
-        y = y[:, rows]
-    ref = d.oracle(O, rows=rows, a_round="f16", w_round="f16")
-    err = O.rel_l2(y, ref)
-    raw = O.rel_l2(y, d.oracle(O, rows=rows))
+    if mrows is not None:
+        y = y[mrows]
+    err = O.rel_l2(y, r["mirrored"])
+    raw = O.rel_l2(y, r["exact"])
     say(f"  {label} relL2(mirrored)={err:.3e} relL2(unrounded)={raw:.3e}")
     assert err <= TOL[d.c_dtype], (label, err)
+    if d.c_dtype != "f32":
+        assert raw <= TOL[d.c_dtype], (label, raw)
+    assert_elementwise(y, r["mirrored"], gamma(d.p["K"] + 2) * r["absdot"], d.c_dtype, label)
     return err
+
+
+def _tile_rows(M, tile=256):
+    """Output rows that meet every M tile: the first two and last two rows of each."""
+    rows = set()
+    for t0 in range(0, M, tile):
+        t1 = min(M, t0 + tile)
+        rows.update({t0, t0 + 1, t1 - 2, t1 - 1})
+    return np.array(sorted(r for r in rows if 0 <= r < M))
 
 
 @pytest.mark.parametrize("name", list(gen.PHI4_SHAPES))
 def test_phi4_u2_prefill_full_size(name):
-    """phi4-14B 2-bit shapes at M = 2048 (full size; oracle on sampled output columns)."""
+    """phi4-14B 2-bit shapes at M = 2048: every output column, for rows that meet every
+    256-row tile."""
     K, N = gen.PHI4_SHAPES[name]
     say(f"phi4 prefill {name} K={K} N={N}")
     p = gen.nbits_problem(2048, K, N, 2, 64, seed=gen.config_seed(1, 10 + list(gen.PHI4_SHAPES).index(name)),
@@ -231,8 +274,7 @@ def test_phi4_u2_prefill_full_size(name):
     d = NbitsDev(p)
     got = d.run(uniform=True)
     torch().cuda.synchronize()
-    rows = sample_rows(N, 192, seed=N + 1)
-    _check_prefill(d, got, rows=rows, label=name)
+    _check_prefill(d, got, mrows=_tile_rows(2048), label=name)
     # the fp16 zero-point tensor path gives the same bits as the scalar path
     got_t = d.run(uniform=False)
     assert np.array_equal(host_bits(got), host_bits(got_t))
@@ -338,5 +380,108 @@ def test_empty_and_degenerate():
     # M = 20 with K = 1 on the prefill path
     p2 = gen.nbits_problem(20, 1, 8, 2, 16, seed=11, zp="packed")
     d2 = NbitsDev(p2)
-    assert O.rel_l2(host_f64(d2.run()), d2.oracle(O, a_round="f16", w_round="f16")) <= TOL["f32"]
+    assert O.rel_l2(host_f64(d2.run()), d2.oracle(O, a_round="f16_rows", w_round="f16")) <= TOL["f32"]
     t.cuda.synchronize()
+
+
+# --- activation outliers and range ----------------------------------------------
+
+def _store_act(x64, a_dtype):
+    """fp64 activations -> the storage of a_dtype (fp32 array or 16-bit patterns)."""
+    t = torch()
+    if a_dtype == "f32":
+        return x64.astype(np.float32)
+    if a_dtype == "f16":
+        return x64.astype(np.float16).view(np.uint16)
+    return t.from_numpy(x64.astype(np.float32)).to(t.bfloat16).view(t.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("M", [1, 3])
+@pytest.mark.parametrize("bits,zp,a,at_zp", [
+    (2, "packed", "f32", True), (4, "packed", "f32", True), (2, "none", "bf16", True),
+    (4, "none", "f16", True), (2, "f16_uniform", "f32", False), (4, "packed", "f32", False),
+])
+def test_gemv_activation_outliers(M, bits, zp, a, at_zp):
+    """One activation of magnitude 1e3..1e4 in every 64-value group ("massive
+    activations"), at the 1e-5 gate of an fp32 output.  at_zp: the weight code at each
+    outlier equals its block's zero point, so the outliers contribute nothing and the
+    output is made of the ordinary activations alone."""
+    K, N, block = 5120, 384, 64
+    say(f"gemv outliers M={M} bits={bits} zp={zp} a={a} at_zp={at_zp}")
+    p = gen.nbits_problem(M, K, N, bits, block, seed=300 + 7 * bits + M + at_zp, zp=zp, uniform_zp=1.5,
+                          scale_range=(0.01, 0.05))
+    rng = np.random.default_rng(301 + M)
+    x = rng.standard_normal((M, K))
+    pos = np.arange(0, K, 64) + rng.integers(0, 64, size=K // 64)
+    x[:, pos] = rng.uniform(1e3, 1e4, size=(M, len(pos))) * rng.choice([-1.0, 1.0], size=(M, len(pos)))
+    p["A"] = _store_act(x, a)
+    p["a_dtype"] = a
+    if at_zp:
+        q = O.unpack_codes(p["W"], bits, K, block).astype(np.int64)
+        nblk = gen.nblocks(K, block)
+        z = O.zero_points_f64(p["zp"], {"packed": O.ZP_PACKED, "none": O.ZP_NONE}[zp], bits, N, nblk)
+        q[:, pos] = z[:, pos // block].astype(np.int64)
+        p["W"] = O.pack_codes(q.astype(np.uint8), bits, block)
+    d = NbitsDev(p, c_dtype="f32")
+    _check(d, d.run(uniform=(zp == "f16_uniform")), label=f"outliers M={M}")
+
+
+@pytest.mark.parametrize("M,K,N,a,c", [
+    (16, 4096, 512, "bf16", "bf16"),   # skinny kernel
+    (40, 1000, 200, "f32", "f32"),     # skinny kernel, K not a multiple of 64
+    (200, 2048, 300, "bf16", "f32"),   # 256 x 256 tiles
+    (300, 640, 256, "f32", "f32"),
+])
+def test_matrix_core_activation_range(M, K, N, a, c):
+    """Rows whose values pass the fp16 range (1e5) or lie below its normal range (1e-6,
+    3e-9), and a row with one value past it: the per-row power-of-two pre-scale of the
+    activation cast keeps every row finite and near its unrounded result."""
+    say(f"activation range M={M} K={K} N={N} a={a}")
+    p = gen.nbits_problem(M, K, N, 4, 64, seed=310 + M, zp="packed", a_dtype="f32", bias=True)
+    x = np.asarray(p["A"], dtype=np.float64)
+    x[0] *= 1e5
+    x[1] *= 1e-6
+    x[2] *= 3e-9
+    x[3, 7] = 7e4
+    p["A"] = _store_act(x, a)
+    p["a_dtype"] = a
+    d = NbitsDev(p, c_dtype=c)
+    y = d.run()
+    torch().cuda.synchronize()
+    got = host_f64(y)
+    assert np.all(np.isfinite(got))
+    _check_prefill(d, y, label=f"range M={M}")
+    bias, bdt = _bias_args(d)
+    r = nbits_reference(O, d.p, bias=bias, bias_dtype=bdt)
+    for m in range(4):
+        err = O.rel_l2(got[m], r["exact"][m])
+        say(f"  row {m}: relL2(unrounded)={err:.3e}")
+        assert err <= 2e-3, (m, err)
+
+
+def test_first_call_of_new_shape_under_capture():
+    """The first call of a shape no other test uses, made while the stream is captured:
+    nothing is timed (the capture would fail on the timing's synchronization), the
+    default tiling runs, and every replay and the later timed eager call give the same
+    bits."""
+    t = torch()
+    p = gen.nbits_problem(2, 3072, 777, 4, 64, seed=320, zp="packed", bias=True)
+    d = NbitsDev(p)
+    out = t.empty((2, 777), dtype=t.float32, device="cuda")
+    t.cuda.synchronize()
+    cap = t.cuda.Stream()
+    g = t.cuda.CUDAGraph()
+    with t.cuda.stream(cap):
+        with t.cuda.graph(g, stream=cap):
+            d.run(out=out)
+    t.cuda.synchronize()
+    reps = []
+    for _ in range(3):
+        out.zero_()
+        g.replay()
+        t.cuda.synchronize()
+        reps.append(host_bits(out).copy())
+    eager = host_bits(d.run()).copy()   # first uncaptured call: times the candidates
+    for r_ in reps:
+        assert np.array_equal(r_, eager)
+    _check(d, d.run(), label="after capture")

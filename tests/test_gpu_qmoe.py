@@ -317,3 +317,80 @@ def test_experts_read_once_same_bits(routing):
     say(f"  {routing} relL2={err:.3e}")
     assert err <= TOL["f16"]
     t.cuda.synchronize()
+
+
+# ---- error state, capture and the wait's status ---------------------------------------
+
+@pytest.mark.parametrize("mode", MODES, ids=["fp", "int8"])
+def test_first_call_over_pending_error(mode):
+    """The first call of a shape no other test uses, made while an unrelated HIP error is
+    pending, succeeds and is within tolerance: the error state is cleared on entry, so
+    neither the up-front timing nor the call reports it."""
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so.7")  # the runtime already loaded by torch
+    hip.hipSetDevice.argtypes = [ctypes.c_int]
+    t = torch()
+    p = gen.qmoe_problem(1, 1536, 512, 12, 3, 64, seed=940 + mode, zp=True, bias=True)
+    d = MoeDev(p)
+    # output and scratch come first: torch checks the error state after its own launches
+    out = t.empty((1, 1536), dtype=t.float16, device="cuda")
+    scratch = t.zeros(Q.qmoe_decode_scratch_bytes(1, 1536, 512, 3, mode), dtype=t.uint8, device="cuda")
+    t.cuda.synchronize()
+    # hipSetDevice on an invalid ordinal records hipErrorInvalidDevice without touching the GPU
+    assert hip.hipSetDevice(9999) != 0
+    y = d.run(mode, out=out, scratch=scratch)
+    err = O.rel_l2(host_f64(y), d.oracle(mode))
+    say(f"  pending error mode={mode} relL2={err:.3e}")
+    assert err <= TOL["f16"], err
+
+
+@pytest.mark.parametrize("mode", MODES, ids=["fp", "int8"])
+def test_first_call_under_capture(mode):
+    """The first call of an untimed shape inside a stream capture: nothing is timed (the
+    timing's synchronization would break the capture), and every replay, with eager calls
+    in between, gives the bits of the later timed eager call."""
+    t = torch()
+    T, H, I, E, k = 2, 1280, 640, 20, 4
+    p = gen.qmoe_problem(T, H, I, E, k, 64, seed=950 + mode, zp=True, bias=False)
+    d = MoeDev(p)
+    scratch = t.zeros(Q.qmoe_decode_scratch_bytes(T, H, I, k, mode), dtype=t.uint8, device="cuda")
+    out = t.empty((T, H), dtype=t.float16, device="cuda")
+    t.cuda.synchronize()
+    cap = t.cuda.Stream()
+    g = t.cuda.CUDAGraph()
+    with t.cuda.stream(cap):
+        with t.cuda.graph(g, stream=cap):
+            d.run(mode, out=out, scratch=scratch)
+    t.cuda.synchronize()
+    eager = host_bits(d.run(mode, scratch=scratch)).copy()   # first uncaptured call: times
+    for rep in range(3):
+        out.zero_()
+        g.replay()
+        t.cuda.synchronize()
+        assert np.array_equal(host_bits(out), eager), rep
+        assert np.array_equal(host_bits(d.run(mode, scratch=scratch)), eager), rep
+    err = O.rel_l2(eager.view(np.float16).astype(np.float64), d.oracle(mode))
+    assert err <= TOL["f16"], err
+    assert not Q.qmoe_decode_status(scratch, T, H, I, k, mode)
+
+
+def test_decode_status_clear_after_single_launch_calls():
+    """qmoe_decode_status reports no wait that gave up after calls of the single-launch
+    form, and refuses a scratch buffer smaller than the layout."""
+    t = torch()
+    T, H, I, E, k = 1, 2880, 2880, 32, 4
+    p = gen.qmoe_problem(T, H, I, E, k, 64, seed=960, zp=False, bias=False)
+    d = MoeDev(p)
+    scratch = t.zeros(Q.qmoe_decode_scratch_bytes(T, H, I, k, Q.QMOE_FP), dtype=t.uint8, device="cuda")
+    Q.set_tuning(2, _fused_base() + 0)
+    try:
+        for _ in range(5):
+            y = d.run(Q.QMOE_FP, scratch=scratch)
+        assert Q.tuned_choice(Q.ENTRY_QMOE_FUSED) == 0
+    finally:
+        Q.set_tuning(0, 0)
+    assert np.all(np.isfinite(host_f64(y)))
+    assert Q.qmoe_decode_status(scratch, T, H, I, k, Q.QMOE_FP) is False
+    with pytest.raises(Q.QmmError) as e:
+        Q.qmoe_decode_status(scratch[:64], T, H, I, k, Q.QMOE_FP)
+    assert e.value.status == -7

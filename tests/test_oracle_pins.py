@@ -94,6 +94,54 @@ def _mutants():
     m = _fresh_oracle_copy()
     m.f32_to_bf16_bits = lambda x: (np.asarray(x, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
     muts["bf16_truncation"] = m
+
+    m = _fresh_oracle_copy()
+    orig_ro = m._round_operand
+    m._round_operand = lambda x, mode: orig_ro(x, "bf16" if mode in ("f16", "f16_rows") else mode)
+    muts["bf16_for_f16_operands"] = m
+
+    m = _fresh_oracle_copy()
+    orig_ro2 = m._round_operand
+    m._round_operand = lambda x, mode: orig_ro2(x, "f16" if mode == "f16_rows" else mode)
+    muts["no_row_prescale"] = m
+
+    m = _fresh_oracle_copy()
+    orig_ro3 = m._round_operand
+    m._round_operand = lambda x, mode: x if mode == "f16" else orig_ro3(x, mode)
+    muts["weight_operand_not_rounded"] = m
+
+    m = _fresh_oracle_copy()
+    orig_l2 = m.rel_l2
+    m.rel_l2 = lambda y, ref: orig_l2(y, ref) ** 2  # squared norm ratio
+    muts["rel_l2_squared"] = m
+
+    m = _fresh_oracle_copy()
+    m.rel_l2 = lambda y, ref: float(np.max(np.abs(np.asarray(y) - np.asarray(ref))) /
+                                    max(np.max(np.abs(np.asarray(ref))), 1e-300))
+    muts["rel_l2_max_norm"] = m
+
+    m = _fresh_oracle_copy()
+    m.qsigmoid = lambda q, si, zi, so, zo, bits: m.quantize_linear(
+        m.dequantize_linear(q, si, zi) * 0.25 + 0.5, so, zo, bits)   # linearised sigmoid
+    muts["qsigmoid_linearised"] = m
+
+    m = _fresh_oracle_copy()
+    orig_sw = m.qswiglu
+
+    def sw_no_requant(gate, up, qp, bits):   # the chain without the sigmoid's requantize
+        (sg, zg), (st, zt), (sm, zm), (su, zu), (sh, zh) = qp
+        g = m.quantize_linear(gate, sg, zg, bits)
+        gd = m.dequantize_linear(g, sg, zg)
+        mm = m.quantize_linear(m.to_f32(gd.astype(np.float64) * m.sigmoid_f32(gd)), sm, zm, bits)
+        u = m.quantize_linear(up, su, zu, bits)
+        return m.dequantize_linear(m.qmul(mm, sm, zm, u, su, zu, sh, zh, bits), sh, zh)
+    m.qswiglu = sw_no_requant
+    muts["qswiglu_sigmoid_not_requantized"] = m
+
+    m = _fresh_oracle_copy()
+    m.div_f32 = lambda x, s: m.to_f32(np.asarray(x, dtype=np.float32).astype(np.float64) *
+                                      m.to_f32(1.0 / np.asarray(s, dtype=np.float32).astype(np.float64)))
+    muts["quotient_by_reciprocal"] = m
     return muts
 
 
