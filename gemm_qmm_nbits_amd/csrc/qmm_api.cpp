@@ -361,7 +361,7 @@ QmoeTimingBufs& qmoe_bufs() {
 // a shape times each candidate of each kernel: one discarded round, then 8 timed
 // rounds, every timed launch on a different set of k experts (so the weights are
 // read cold), writing only the call's scratch and a library-owned output.
-void qmoe_choice(const QmoeArgs& a, hipStream_t st, int* r1, int* r2) {
+void qmoe_choice(const QmoeArgs& a, hipStream_t st, bool may_time, int* r1, int* r2) {
   TunerState& t = tuner();
   std::lock_guard<std::mutex> lock(t.mu);
   const int mode = tuning_mode_locked(t);
@@ -390,7 +390,7 @@ void qmoe_choice(const QmoeArgs& a, hipStream_t st, int* r1, int* r2) {
     finish(i1->second, i2->second);
     return;
   }
-  if (stream_capturing(st)) {
+  if (!may_time || stream_capturing(st)) {
     finish(0, 0);
     return;
   }
@@ -495,7 +495,7 @@ void qmoe_choice(const QmoeArgs& a, hipStream_t st, int* r1, int* r2) {
 // two-kernel form.
 constexpr int kQmoeForcedFused = kNumQmoeCandidates * kNumQmoeCandidates;
 
-int qmoe_fused_choice(QmoeArgs& a, hipStream_t st, int r1, int r2) {
+int qmoe_fused_choice(QmoeArgs& a, hipStream_t st, bool may_time, int r1, int r2) {
   TunerState& t = tuner();
   std::lock_guard<std::mutex> lock(t.mu);
   const int mode = tuning_mode_locked(t);
@@ -514,7 +514,7 @@ int qmoe_fused_choice(QmoeArgs& a, hipStream_t st, int r1, int r2) {
                              (a.fc1.zp != nullptr ? 2 : 0) + (a.fc2.zp != nullptr ? 1 : 0));
   auto it = t.choice.find(key);
   if (it != t.choice.end()) return plan(it->second) ? finish(it->second) : finish(-1);
-  if (stream_capturing(st)) return finish(-1);
+  if (!may_time || stream_capturing(st)) return finish(-1);
   bool any = false;
   for (int c = 0; c < kNumQmoeFused; ++c) any = any || plan(c);
   if (!any) {
@@ -1003,6 +1003,18 @@ qmm_status qmoe_decode_fused(const uint16_t* X, int64_t T, int64_t H, int64_t I,
                              qmoe_weights fc2, int bits, int block, int mode, uint16_t* Y,
                              void* scratch, size_t scratch_bytes, void* stream) {
   (void)hipGetLastError();
+  return qmm::qmoe_decode_run(X, T, H, I, E, k, expert_ids, expert_w, fc1, fc2, bits, block, mode, Y, scratch,
+                              scratch_bytes, stream, true);
+}
+
+}  // extern "C"
+
+// The MoE decode behind both entry points: may_time = false never times candidates
+// (the cached choice of the shape or the default tiling), so the call allocates nothing.
+qmm_status qmm::qmoe_decode_run(const uint16_t* X, int64_t T, int64_t H, int64_t I, int64_t E, int k,
+                                const int32_t* expert_ids, const float* expert_w, qmoe_weights fc1,
+                                qmoe_weights fc2, int bits, int block, int mode, uint16_t* Y, void* scratch,
+                                size_t scratch_bytes, void* stream, bool may_time) {
   const qmm_status s = check_qmoe(X, T, H, I, E, k, expert_ids, expert_w, fc1, fc2, bits, block,
                                   mode, Y, scratch, scratch_bytes);
   if (s != QMM_OK) return s;
@@ -1046,8 +1058,8 @@ qmm_status qmoe_decode_fused(const uint16_t* X, int64_t T, int64_t H, int64_t I,
     a.sync = (uint32_t*)(sc + L.sync);
   }
   int r1 = 1, r2 = 1;
-  qmoe_choice(a, st, &r1, &r2);
-  if (mode == QMOE_FP && qmoe_fused_choice(a, st, r1, r2) >= 0) {
+  qmoe_choice(a, st, may_time, &r1, &r2);
+  if (mode == QMOE_FP && qmoe_fused_choice(a, st, may_time, r1, r2) >= 0) {
     const hipError_t e = launch_qmoe_fused(a, st);  // the plan has checked that it fits
     if (e != hipSuccess) return (qmm_status)e;
     return (qmm_status)hipGetLastError();
@@ -1057,6 +1069,8 @@ qmm_status qmoe_decode_fused(const uint16_t* X, int64_t T, int64_t H, int64_t I,
   if (e != hipSuccess) return (qmm_status)e;
   return (qmm_status)hipGetLastError();
 }
+
+extern "C" {
 
 qmm_status qmoe_decode_status(void* scratch, size_t scratch_bytes, int64_t T, int64_t H, int64_t I, int k,
                               int mode, int* timed_out, void* stream) {

@@ -62,4 +62,11 @@ constexpr int kQmoeDedupe = 64;
 hipError_t launch_qmoe_fc1(const QmoeArgs& a, int candidate, hipStream_t st);
 hipError_t launch_qmoe_fc2(const QmoeArgs& a, int candidate, hipStream_t st);
 
+// The whole MoE decode call (checks, tiling choice, launches) on a given scratch
+// buffer; may_time = false never times candidates (and so never allocates).
+qmm_status qmoe_decode_run(const uint16_t* X, int64_t T, int64_t H, int64_t I, int64_t E, int k,
+                           const int32_t* expert_ids, const float* expert_w, qmoe_weights fc1, qmoe_weights fc2,
+                           int bits, int block, int mode, uint16_t* Y, void* scratch, size_t scratch_bytes,
+                           void* stream, bool may_time);
+
 }  // namespace qmm

@@ -68,6 +68,9 @@ _SIGS = {
     "qmoe_decode_scratch_bytes": (c_size_t, [c_int64, c_int64, c_int64, c_int, c_int]),
     "qmoe_decode_status": (c_int, [c_void_p, c_size_t, c_int64, c_int64, c_int64, c_int, c_int,
                                    POINTER(c_int), c_void_p]),
+    "qmoe_decode_fused_noalloc": (c_int, [c_void_p, c_int64, c_int64, c_int64, c_int64, c_int, c_void_p,
+                                          c_void_p, qmoe_weights, qmoe_weights, c_int, c_int, c_int,
+                                          c_void_p, c_void_p]),
     "qmm_validate_qmoe": (c_int, [c_void_p, c_int64, c_int64, c_int64, c_int64, c_int, c_void_p,
                                   c_void_p, qmoe_weights, qmoe_weights, c_int, c_int, c_int,
                                   c_void_p, c_void_p, c_size_t]),
@@ -267,6 +270,22 @@ def qmoe_decode_fused(X, expert_ids, expert_w, fc1, fc2, H, I, E, block, mode=QM
                                  _qw(fc2), bits, block, mode, _ptr(out), _ptr(scratch),
                                  scratch.numel() * scratch.element_size(), _stream(stream))
     _check("qmoe_decode_fused", st)
+    return out
+
+
+QMOE_NOALLOC_SCRATCH_BYTES = 8 << 20
+
+
+def qmoe_decode_fused_noalloc(X, expert_ids, expert_w, fc1, fc2, H, I, E, block, out, mode=QMOE_FP, bits=4,
+                              stream=None):
+    """The MoE decode on the library's static scratch: no allocation in the library
+    (the caller passes the output)."""
+    X = _contig(X, "X")
+    T = X.shape[0]
+    k = expert_ids.shape[1]
+    st = lib().qmoe_decode_fused_noalloc(_ptr(X), T, H, I, E, k, _ptr(expert_ids), _ptr(expert_w), _qw(fc1),
+                                         _qw(fc2), bits, block, mode, _ptr(out), _stream(stream))
+    _check("qmoe_decode_fused_noalloc", st)
     return out
 
 

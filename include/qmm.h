@@ -240,6 +240,22 @@ qmm_status qmoe_decode_fused(const uint16_t* X, int64_t T, int64_t H, int64_t I,
 
 size_t qmoe_decode_scratch_bytes(int64_t T, int64_t H, int64_t I, int k, int mode);
 
+/* qmoe_decode_fused_noalloc -- qmoe_decode_fused for callers that cannot allocate
+ * (code under stream capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Same arguments and results as qmoe_decode_fused, without scratch: the scratch is a
+ * static device array of QMOE_NOALLOC_SCRATCH_BYTES inside the library, one per
+ * device, held until the process ends.  A shape that needs more
+ * (qmoe_decode_scratch_bytes) is refused with QMM_E_WORKSPACE.  The call never times
+ * tiling candidates: it uses the choice an earlier qmoe_decode_fused call made for the
+ * shape, else the default tiling, and so calls no allocating routine.  All calls on
+ * one device share the array: calls that overlap on one device (other streams, other
+ * threads) race and must not be made. */
+#define QMOE_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+qmm_status qmoe_decode_fused_noalloc(const uint16_t* X, int64_t T, int64_t H, int64_t I, int64_t E,
+                                     int k, const int32_t* expert_ids, const float* expert_w,
+                                     qmoe_weights fc1, qmoe_weights fc2, int bits, int block, int mode,
+                                     uint16_t* Y, void* stream);
+
 /* qmoe_decode_status -- whether a single-launch qmoe_decode_fused call on this scratch
  * buffer gave up its wait ([P2] "What": a call must not report an error it did not
  * cause, nor hide one it did).  Reads the error word of the scratch layout above into
