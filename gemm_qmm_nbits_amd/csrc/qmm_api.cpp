@@ -34,6 +34,8 @@ namespace {
 constexpr int kMaxGemvM = 8;  // M above this takes the prefill (matrix-core) path
 
 bool is_pow2_block(int b) { return b >= 16 && b <= 256 && (b & (b - 1)) == 0; }
+// zero point when none is given: the middle code of unsigned codes, 0 for signed int8
+float default_zp(int bits) { return bits == 8 ? 0.0f : (float)(1 << (bits - 1)); }
 bool valid_dtype(int t) { return t == QMM_F32 || t == QMM_F16 || t == QMM_BF16; }
 size_t dtype_size(int t) { return t == QMM_F32 ? 4 : 2; }
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -611,8 +613,8 @@ qmm_status check_nbits(const void* A, int a_type, int64_t M, int64_t K, int64_t 
                        size_t workspace_bytes) {
   (void)bias;
   if (!valid_dtype(a_type) || !valid_dtype(c_type)) return QMM_E_DTYPE;
-  if (bits != 2 && bits != 4) return QMM_E_BITS;
-  if (!is_pow2_block(block)) return QMM_E_BLOCK;
+  if (bits != 2 && bits != 3 && bits != 4 && bits != 8) return QMM_E_BITS;
+  if (!is_pow2_block(block) || (bits == 3 && block < 32)) return QMM_E_BLOCK;
   if (M < 0 || K < 0 || N < 0 || M > (1LL << 30) || K > (1LL << 30) || N > (1LL << 30))
     return QMM_E_SHAPE;
   if (zp_kind < QMM_ZP_NONE || zp_kind > QMM_ZP_UNIFORM) return QMM_E_MODE;
@@ -731,11 +733,12 @@ GemvArgs make_gemv(const void* A, int a_type, int64_t M, int64_t K, int64_t N, c
   g.block_log2 = __builtin_ctz((unsigned)block);
   g.nblk = ceil_div(K, block);
   g.row_bytes = g.nblk * block * bits / 8;
-  g.nchunks = g.row_bytes / 16;
+  const int64_t chb = bits == 3 ? 12 : 16;  // bytes of a lane's weight chunk (32 3-bit codes)
+  g.nchunks = g.row_bytes / chb;
   g.bias = bias;
   g.C = C;
   g.c_type = c_type;
-  g.chunked = (g.row_bytes % 16 == 0) && aligned(W, 16);
+  g.chunked = (g.row_bytes % chb == 0) && aligned(W, 16);
   g.lpr_log2 = gemv_row_lanes_log2(g.nchunks, N);
   g.a_vec = aligned(A, 16) && (K % 4 == 0);
   return g;
@@ -826,7 +829,7 @@ qmm_status qmm_nbits(const void* A, int a_type, int64_t M, int64_t K, int64_t N,
     p.scales = scales;
     p.zp = zp;
     p.zp_kind = zp_kind;
-    p.zconst = zp_kind == QMM_ZP_UNIFORM ? uniform_zp : (float)(1 << (bits - 1));
+    p.zconst = zp_kind == QMM_ZP_UNIFORM ? uniform_zp : default_zp(bits);
     p.zp_row_bytes = ceil_div(p.nblk * bits, 8);
     p.bias = bias;
     p.C = C;
@@ -929,8 +932,8 @@ qmm_status qmm_dequantize_nbits(const uint8_t* W, int bits, int block, const uin
                                 const void* zp, int zp_kind, float uniform_zp, int64_t N, int64_t K,
                                 void* out, int out_type, void* stream) {
   (void)hipGetLastError();
-  if (bits != 2 && bits != 4) return QMM_E_BITS;
-  if (!is_pow2_block(block)) return QMM_E_BLOCK;
+  if (bits != 2 && bits != 3 && bits != 4 && bits != 8) return QMM_E_BITS;
+  if (!is_pow2_block(block) || (bits == 3 && block < 32)) return QMM_E_BLOCK;
   if (N < 0 || K < 0) return QMM_E_SHAPE;
   if (out_type != QMM_F32 && out_type != QMM_F16) return QMM_E_DTYPE;
   if (zp_kind < QMM_ZP_NONE || zp_kind > QMM_ZP_UNIFORM) return QMM_E_MODE;

@@ -63,35 +63,51 @@ __device__ __forceinline__ void store_elem_rt(void* p, int t, int64_t i, float v
 
 // ---- code extraction -------------------------------------------------------
 
-// Unsigned `bits`-wide code of element j (0-based) of a packed block.
-__device__ __forceinline__ uint32_t code_at(const uint8_t* blk, int j, int bits) {
+// Code of element j (0-based) of a packed block: bits = 2, 3, 4 give the unsigned field
+// at bit j * bits of the block's little-endian bit stream (a 3-bit field may continue
+// into the next byte, which is read only then); bits = 8 gives the signed byte.
+__device__ __forceinline__ int32_t code_at(const uint8_t* blk, int j, int bits) {
+  if (bits == 8) return (int32_t)(int8_t)blk[j];
   const int bit = j * bits;
-  return (blk[bit >> 3] >> (bit & 7)) & ((1u << bits) - 1u);
+  uint32_t v = blk[bit >> 3];
+  if ((bit & 7) + bits > 8) v |= (uint32_t)blk[(bit >> 3) + 1] << 8;
+  return (int32_t)((v >> (bit & 7)) & ((1u << bits) - 1u));
 }
 
-// Zero point of (row n, block b) as fp32 for each zero-point kind.
+// Zero point when none is given: the middle code of unsigned codes, 0 for signed int8.
+__host__ __device__ __forceinline__ float default_zero_point(int bits) {
+  return bits == 8 ? 0.0f : (float)(1 << (bits - 1));
+}
+
+// Zero point of (row n, block b) as fp32 for each zero-point kind (packed zero points use
+// the weights' field layout: block b is field b of the row's bit stream).
 __device__ __forceinline__ float zero_point(const void* zp, int zp_kind, float uniform_zp,
                                             int bits, int64_t n, int b, int64_t zp_row_bytes,
                                             int64_t nblk) {
   switch (zp_kind) {
-    case QMM_ZP_PACKED: {
-      const uint8_t* row = (const uint8_t*)zp + n * zp_row_bytes;
-      const int bit = b * bits;
-      return (float)((row[bit >> 3] >> (bit & 7)) & ((1u << bits) - 1u));
-    }
+    case QMM_ZP_PACKED:
+      return (float)code_at((const uint8_t*)zp + n * zp_row_bytes, b, bits);
     case QMM_ZP_F16:
       return f16_to_f32(((const uint16_t*)zp)[n * nblk + b]);
     case QMM_ZP_UNIFORM:
       return uniform_zp;
     default:
-      return (float)(1 << (bits - 1));
+      return default_zero_point(bits);
   }
 }
 
 // Bit-exact affine dequant: fp32(fp32(q - zp) * s), two separate roundings.
-__device__ __forceinline__ float dequant_affine(uint32_t q, float zp, float s) {
+__device__ __forceinline__ float dequant_affine(int32_t q, float zp, float s) {
   float d = __fsub_rn((float)q, zp);
   return __fmul_rn(d, s);
+}
+
+// The fp32 value as a register a following conversion reads: keeps the compiler from
+// merging the operation that produced it with a conversion to a 16-bit type (a mixed-
+// precision operation would round the exact result once, not the fp32 value).
+__device__ __forceinline__ float materialize(float v) {
+  asm volatile("" : "+v"(v));
+  return v;
 }
 
 // ---- wave-level helpers ------------------------------------------------------

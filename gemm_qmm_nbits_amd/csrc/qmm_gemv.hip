@@ -8,6 +8,18 @@ template <int AT>
 hipError_t launch_cb_at_type(const GemvArgs& g, int R, hipStream_t st);
 template <int BITS, int AT>
 hipError_t launch_ip_at_type(const GemvArgs& g, int R, hipStream_t st);
+template <int FMT, int BITS, int AT>
+hipError_t launch_at_type(const GemvArgs& g, int R, hipStream_t st);
+
+// 3-bit and signed 8-bit affine weights: the fp32 kernel (codes decoded to fp32)
+template <int BITS>
+static hipError_t launch_affine_fp32(const GemvArgs& g, int R, hipStream_t st) {
+  switch (g.a_type) {
+    case QMM_F32: return launch_at_type<GEMV_AFFINE, BITS, QMM_F32>(g, R, st);
+    case QMM_F16: return launch_at_type<GEMV_AFFINE, BITS, QMM_F16>(g, R, st);
+    default: return launch_at_type<GEMV_AFFINE, BITS, QMM_BF16>(g, R, st);
+  }
+}
 
 // codebook weights: fp32 kernels with the LDS centroid table
 static hipError_t launch_codebook(const GemvArgs& g, int R, hipStream_t st) {
@@ -39,11 +51,11 @@ __global__ __launch_bounds__(256) void gemv_generic_kernel(GemvArgs g) {
 #pragma unroll
   for (int m = 0; m < 8; ++m) acc[m] = 0.0f;
   const int bits = g.fmt == GEMV_CODEBOOK ? 4 : g.bits;
-  const int blob = g.block * bits / 8;
+  const int blob = g.block * bits / 8;   // bytes per block
   for (int64_t k = lane; k < g.K; k += 64) {
     const int b = (int)(k / g.block);
     const int j = (int)(k % g.block);
-    const uint32_t q = code_at(g.W + n * g.row_bytes + (int64_t)b * blob, j, bits);
+    const int32_t q = code_at(g.W + n * g.row_bytes + (int64_t)b * blob, j, bits);
     float w;
     if (g.fmt == GEMV_CODEBOOK) {
       w = __fmul_rn(g.codebook[q], g.absmax[n * g.nblk + b]);
@@ -121,6 +133,8 @@ void gemv_plan(GemvArgs& g, int num_cus) {
   // weight dword, 4 words of padding) + 4 group records of four words
   int64_t cs_bytes;
   if (g.fmt == GEMV_CODEBOOK) cs_bytes = (int64_t)(32 + 4) * 4 + 4 * 4;
+  else if (g.bits == 3) cs_bytes = (int64_t)(32 + 4) * 4 + 4 * 4;   // fp32 kernel, 32 codes per chunk
+  else if (g.bits == 8) cs_bytes = (int64_t)(16 + 4) * 4 + 4 * 4;   // fp32 kernel, 16 codes per chunk
   else if (g.bits == 2) cs_bytes = (int64_t)(4 * 12 + 4) * 4 + 4 * 16;
   else cs_bytes = (int64_t)(4 * 6 + 4) * 4 + 4 * 16;
   const int64_t lpr = 1LL << g.lpr_log2;
@@ -152,6 +166,8 @@ hipError_t launch_gemv(GemvArgs g, int rows_per_lane, hipStream_t st) {
   }
   if (g.fmt == GEMV_CODEBOOK) return launch_codebook(g, rows_per_lane, st);
   if (g.bits == 2) return launch_affine<2>(g, rows_per_lane, st);
+  if (g.bits == 3) return launch_affine_fp32<3>(g, rows_per_lane, st);
+  if (g.bits == 8) return launch_affine_fp32<8>(g, rows_per_lane, st);
   return launch_affine<4>(g, rows_per_lane, st);
 }
 

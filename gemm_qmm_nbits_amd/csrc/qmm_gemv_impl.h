@@ -63,10 +63,53 @@ __device__ __forceinline__ void decode_dword_affine(uint32_t x, float (&q)[32 / 
   }
 }
 
-// Factor that turns the decoded values above into the codes themselves.
+// Factor that turns the decoded values above into the codes themselves (3- and 8-bit
+// codes are decoded as the codes).
 template <int BITS>
 __device__ __forceinline__ constexpr float affine_decode_factor() {
-  return BITS == 2 ? 2.0f : 512.0f;
+  return BITS == 2 ? 2.0f : BITS == 4 ? 512.0f : 1.0f;
+}
+
+// Bytes of one weight chunk of a lane: 16 (64 u2, 32 u4, 16 i8 codes) or 12 for 3-bit
+// codes (32 codes: a 16-byte chunk would split a code).
+template <int BITS>
+__host__ __device__ __forceinline__ constexpr int chunk_bytes() {
+  return BITS == 3 ? 12 : 16;
+}
+
+// Codes [8d, 8d + 8) of a 12-byte chunk of 3-bit codes (24 bits at bit 24d), as floats.
+__device__ __forceinline__ void decode_group_u3(const uint4& w, int d, float (&q)[8]) {
+  const uint32_t x = d == 0 ? w.x : d == 1 ? __builtin_amdgcn_alignbit(w.y, w.x, 24)
+                   : d == 2 ? __builtin_amdgcn_alignbit(w.z, w.y, 16) : (w.z >> 8);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) q[i] = (float)__builtin_amdgcn_ubfe(x, 3 * i, 3);
+}
+
+// The four signed 8-bit codes of a dword, as floats.
+__device__ __forceinline__ void decode_dword_i8(uint32_t x, float (&q)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) q[i] = (float)(int)__builtin_amdgcn_sbfe((int)x, 8 * i, 8);
+}
+
+// The weight chunk of one lane: 16 bytes, or 12 for 3-bit codes (w.w unused).
+template <int BITS>
+__device__ __forceinline__ uint4 load_chunk(const uint8_t* p) {
+  if constexpr (BITS == 3) {
+    const uint32_t* q = (const uint32_t*)p;
+    return make_uint4(q[0], q[1], q[2], 0u);
+  } else {
+    return *(const uint4*)p;
+  }
+}
+
+// Packed zero-point code `idx` of a row (the weights' field layout; signed for 8 bits).
+template <int BITS>
+__device__ __forceinline__ float packed_zp_code(const uint8_t* row, int idx) {
+  if constexpr (BITS == 8) return (float)(int8_t)row[idx];
+  const int bit = idx * BITS;
+  uint32_t v = row[bit >> 3];
+  if ((bit & 7) + BITS > 8) v |= (uint32_t)row[(bit >> 3) + 1] << 8;
+  return (float)((v >> (bit & 7)) & ((1u << BITS) - 1u));
 }
 
 // Codebook lookup of the eight 4-bit codes of a dword from the LDS table.
@@ -168,9 +211,10 @@ struct ItemPos {
 // tensor.  MULTI: a chunk spans several blocks (block < codes per chunk).
 template <int FMT, int BITS, int AT, int MT, int R, int MULTI, int ZK>
 __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs g) {
-  constexpr int WPC = 128 / BITS;  // codes per 16-byte chunk
-  constexpr int WPD = 32 / BITS;   // codes per dword
-  constexpr int CS = WPC + 4;      // LDS floats per chunk slot
+  constexpr int CHB = chunk_bytes<BITS>();
+  constexpr int WPC = CHB * 8 / BITS;  // codes per chunk
+  constexpr int WPD = WPC / 4;         // codes per decode step (a dword, or 24 bits of u3)
+  constexpr int CS = WPC + 4;          // LDS floats per chunk slot
   constexpr int NS = MULTI ? 4 : 1;
   constexpr int D = kGemvDepth;
   constexpr int NWAVES = kGemvThreads / 64;
@@ -209,7 +253,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs g) {
   const int DPG = G / WPD;                       // dwords per group: 1, 2 or 4
   const int64_t row_bytes = g.row_bytes;
   constexpr float FAC = (FMT == GEMV_AFFINE) ? affine_decode_factor<BITS>() : 1.0f;
-  const float zconst = g.zp_kind == QMM_ZP_UNIFORM ? g.uniform_zp : (float)(1 << (BITS - 1));
+  const float zconst = g.zp_kind == QMM_ZP_UNIFORM ? g.uniform_zp : default_zero_point(BITS);
   const int zrow_bytes = (int)g.zp_row_bytes;
   // output buffer: tiles per flush
   int out_tiles = kGemvOutFloats / (rows_per_tile * MT);
@@ -251,7 +295,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs g) {
     const int cc = (fpos.tile < t_end && fchunk < nchunks) ? fchunk : nchunks - 1;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      b.w[r] = *(const uint4*)(fw[r] + cc * 16);
+      b.w[r] = load_chunk<BITS>(fw[r] + cc * CHB);
 #pragma unroll
       for (int i = 0; i < NS; ++i) {
         const int gi = i < GPC ? i : GPC - 1;
@@ -259,8 +303,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs g) {
         if constexpr (FMT == GEMV_AFFINE) {
           b.s[r][i] = f16_to_f32(fsa[r][bidx]);
           if constexpr (ZK == 1) {
-            const int bit = bidx * BITS;
-            b.z[r][i] = (float)((fzp[r][bit >> 3] >> (bit & 7)) & ((1u << BITS) - 1u));
+            b.z[r][i] = packed_zp_code<BITS>(fzp[r], bidx);
           } else if constexpr (ZK == 2) {
             b.z[r][i] = f16_to_f32(fzh[r][bidx]);
           } else {
@@ -347,8 +390,10 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs g) {
         for (int r = 0; r < R; ++r) {
           const uint32_t x = d == 0 ? cbuf.w[r].x : d == 1 ? cbuf.w[r].y : d == 2 ? cbuf.w[r].z : cbuf.w[r].w;
           float q[WPD];
-          if constexpr (FMT == GEMV_AFFINE) decode_dword_affine<BITS>(x, q);
-          else decode_dword_codebook(x, cb_lds, q);
+          if constexpr (FMT == GEMV_CODEBOOK) decode_dword_codebook(x, cb_lds, q);
+          else if constexpr (BITS == 3) decode_group_u3(cbuf.w[r], d, q);
+          else if constexpr (BITS == 8) decode_dword_i8(x, q);
+          else decode_dword_affine<BITS>(x, q);
 #pragma unroll
           for (int m = 0; m < MT; ++m)
 #pragma unroll
@@ -498,7 +543,7 @@ static hipError_t launch_mr(const GemvArgs& g, int R, hipStream_t st) {
 
 template <int FMT, int BITS, int AT>
 hipError_t launch_at_type(const GemvArgs& g, int R, hipStream_t st) {
-  constexpr int WPC = 128 / BITS;
+  constexpr int WPC = chunk_bytes<BITS>() * 8 / BITS;
   const bool multi = g.block < WPC;
   if constexpr (FMT == GEMV_CODEBOOK) {
     return multi ? launch_mr<FMT, BITS, AT, 1, 0>(g, R, st) : launch_mr<FMT, BITS, AT, 0, 0>(g, R, st);

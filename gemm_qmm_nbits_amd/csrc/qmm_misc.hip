@@ -17,7 +17,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs d) {
     const int64_t k = i - n * d.K;
     const int b = (int)(k / d.block);
     const int j = (int)(k - (int64_t)b * d.block);
-    const uint32_t q = code_at(d.W + n * d.row_bytes + (int64_t)b * blob, j, d.bits);
+    const int32_t q = code_at(d.W + n * d.row_bytes + (int64_t)b * blob, j, d.bits);
     float w;
     if (d.fmt == GEMV_CODEBOOK) {
       w = __fmul_rn(d.codebook[q], d.absmax[n * d.nblk + b]);
@@ -26,7 +26,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs d) {
       const float z = zero_point(d.zp, d.zp_kind, d.uniform_zp, d.bits, n, b, d.zp_row_bytes, d.nblk);
       w = dequant_affine(q, z, s);
     }
-    if (d.out_type == QMM_F16) ((uint16_t*)d.out)[i] = f32_to_f16(w);
+    if (d.out_type == QMM_F16) ((uint16_t*)d.out)[i] = f32_to_f16(materialize(w));
     else ((float*)d.out)[i] = w;
   }
 }

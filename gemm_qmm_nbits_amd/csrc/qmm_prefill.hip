@@ -46,7 +46,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, int64_t by
 // with the scale and zero point of each 16.
 template <int BITS>
 struct Stage {
-  uint32_t w[BITS];  // 32 codes: 2-bit -> 2 dwords, 4-bit -> 4 dwords
+  uint32_t w[BITS];  // 32 codes: BITS dwords (2-bit -> 2, 3-bit -> 3, 4-bit -> 4, 8-bit -> 8)
   _Float16 sc[2];    // affine scale
   _Float16 zh[2];
   uint32_t zb[2];
@@ -176,7 +176,11 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillArgs p) {
       st.sc[g] = __builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(rS, (int)(s_off + 2u * blk), 0, 0));
       if constexpr (ZK == 1) {
         const int bit = blk * BITS;
-        st.zb[g] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rZ, (int)(z_off + (uint32_t)(bit >> 3)), 0, 0) >> (bit & 7);
+        const uint32_t zo = z_off + (uint32_t)(bit >> 3);
+        uint32_t zb = __builtin_amdgcn_raw_buffer_load_b8(rZ, (int)zo, 0, 0);
+        // a 3-bit field may continue into the next byte (past the buffer it reads 0)
+        if constexpr (BITS == 3) zb |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rZ, (int)(zo + 1u), 0, 0) << 8;
+        st.zb[g] = BITS == 8 ? zb : zb >> (bit & 7);
       } else if constexpr (ZK == 2) {
         st.zh[g] = __builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(rZ, (int)(s_off + 2u * blk), 0, 0));
       }
@@ -203,14 +207,26 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillArgs p) {
     }
     const float sc = (float)st.sc[g];
     float z;
-    if constexpr (ZK == 1) z = (float)(st.zb[g] & ((1u << BITS) - 1u));
+    if constexpr (ZK == 1) z = BITS == 8 ? (float)(int8_t)st.zb[g] : (float)(st.zb[g] & ((1u << BITS) - 1u));
     else if constexpr (ZK == 2) z = (float)st.zh[g];
     else z = p.zconst;
     // codes as exact fp32 integers, two per conversion: 2-bit codes masked into e2m1
     // nibbles are q/2 (scaled by 2), 4-bit codes masked into e4m3 bytes are q * 2^-9
-    // (scaled by 2^9)
+    // (scaled by 2^9); 3-bit and signed 8-bit codes are extracted one by one
     float qv[8];
-    if constexpr (BITS == 2) {
+    if constexpr (BITS == 3) {
+      // codes 8q .. 8q+7: the 24-bit field at bit 24 q of this thread's 96 bits
+      const uint32_t xw = q == 0 ? st.w[0] : q == 1 ? __builtin_amdgcn_alignbit(st.w[1], st.w[0], 24)
+                        : q == 2 ? __builtin_amdgcn_alignbit(st.w[2], st.w[1], 16) : (st.w[2] >> 8);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qv[i] = (float)__builtin_amdgcn_ubfe(xw, 3 * i, 3);
+    } else if constexpr (BITS == 8) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        qv[i] = (float)(int)__builtin_amdgcn_sbfe((int)st.w[2 * q], 8 * i, 8);
+        qv[4 + i] = (float)(int)__builtin_amdgcn_sbfe((int)st.w[2 * q + 1], 8 * i, 8);
+      }
+    } else if constexpr (BITS == 2) {
       const uint32_t xw = st.w[q >> 1] >> (16 * (q & 1));  // 8 codes in the low 16 bits
       const uint32_t ev = xw & 0x3333u, od = (xw >> 2) & 0x3333u;
       const f32x2 e0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(ev, 2.0f, 0);
@@ -453,6 +469,14 @@ hipError_t launch_prefill(PrefillArgs p, hipStream_t st) {
         if (zk == 1) launch_ct<GEMV_AFFINE, 2, 1>(q, grid, st);
         else if (zk == 2) launch_ct<GEMV_AFFINE, 2, 2>(q, grid, st);
         else launch_ct<GEMV_AFFINE, 2, 0>(q, grid, st);
+      } else if (q.bits == 3) {
+        if (zk == 1) launch_ct<GEMV_AFFINE, 3, 1>(q, grid, st);
+        else if (zk == 2) launch_ct<GEMV_AFFINE, 3, 2>(q, grid, st);
+        else launch_ct<GEMV_AFFINE, 3, 0>(q, grid, st);
+      } else if (q.bits == 8) {
+        if (zk == 1) launch_ct<GEMV_AFFINE, 8, 1>(q, grid, st);
+        else if (zk == 2) launch_ct<GEMV_AFFINE, 8, 2>(q, grid, st);
+        else launch_ct<GEMV_AFFINE, 8, 0>(q, grid, st);
       } else {
         if (zk == 1) launch_ct<GEMV_AFFINE, 4, 1>(q, grid, st);
         else if (zk == 2) launch_ct<GEMV_AFFINE, 4, 2>(q, grid, st);

@@ -12,8 +12,9 @@
 //
 // Work-group: 8 waves and one, two or four 16-row strips of W (16 to 64 output columns).  The reduction
 // runs in steps of 128 codes; wave w takes steps w, w + 8, ...  In a step, lane l
-// (n = l % 16, q = l / 16) loads codes [32q, 32q + 32) of W row n of each strip (16 bytes
-// of u4, 8 of u2, inside one block since blocks are >= 32 codes), dequantizes them into
+// (n = l % 16, q = l / 16) loads codes [32q, 32q + 32) of W row n of each strip (8 bytes
+// of u2, 12 of u3, 16 of u4, 32 of i8, inside one block since blocks are >= 32 codes),
+// dequantizes them into
 // four groups of 8 fp16, and reads the matching 8 fp16 of A for each 16-row M tile
 // straight from the workspace (L2-resident).  v_mfma_f32_16x16x32_f16 then contracts the
 // 8-value groups: lane l supplies A row l % 16 and W row l % 16 over the same 8 k, so
@@ -62,9 +63,11 @@ __device__ __forceinline__ float sk_bias(const void* b, int64_t i) {
 }
 
 // 8 codes -> 8 fp16 weights (codes in order), exact fp32 dequant rounded to nearest
-// fp16.  BITS = 4: `xw` holds the 8 codes as nibbles; BITS = 2: in its low 16 bits.
+// fp16.  BITS = 4: `xw` holds the 8 codes as nibbles; BITS = 2: in its low 16 bits;
+// BITS = 3: in its low 24 bits; BITS = 8: four signed bytes in xw, four in xw2.
 template <int FMT, int BITS>
-__device__ __forceinline__ f16x8 dequant8(uint32_t xw, float sc, float z, float am, const float* cb) {
+__device__ __forceinline__ f16x8 dequant8(uint32_t xw, uint32_t xw2, float sc, float z, float am,
+                                          const float* cb) {
   uint32_t o[4];
   if constexpr (FMT == GEMV_CODEBOOK) {
 #pragma unroll
@@ -79,7 +82,16 @@ __device__ __forceinline__ f16x8 dequant8(uint32_t xw, float sc, float z, float 
     // nibbles are q/2 (scaled by 2), 4-bit codes masked into e4m3 bytes are q * 2^-9
     // (scaled by 2^9)
     float qv[8];
-    if constexpr (BITS == 2) {
+    if constexpr (BITS == 3) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qv[i] = (float)__builtin_amdgcn_ubfe(xw, 3 * i, 3);
+    } else if constexpr (BITS == 8) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        qv[i] = (float)(int)__builtin_amdgcn_sbfe((int)xw, 8 * i, 8);
+        qv[4 + i] = (float)(int)__builtin_amdgcn_sbfe((int)xw2, 8 * i, 8);
+      }
+    } else if constexpr (BITS == 2) {
       const uint32_t ev = xw & 0x3333u, od = (xw >> 2) & 0x3333u;
       const f32x2 e0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(ev, 2.0f, 0);
       const f32x2 o0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(od, 2.0f, 0);
@@ -166,9 +178,17 @@ __global__ __launch_bounds__(SK_THREADS) void skinny_kernel(PrefillArgs p) {
 #pragma unroll
     for (int s = 0; s < SK_NS; ++s) {
       const uint32_t wo = wrow[s] * (uint32_t)p.row_bytes + (uint32_t)(k0 * BITS / 8);
-      if constexpr (BITS == 4) {
+      if constexpr (BITS == 8) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(rW, (int)wo, 0, 0);
+        const auto u = __builtin_amdgcn_raw_buffer_load_b128(rW, (int)(wo + 16u), 0, 0);
+        wv[s][0] = v[0]; wv[s][1] = v[1]; wv[s][2] = v[2]; wv[s][3] = v[3];
+        wv[s][4] = u[0]; wv[s][5] = u[1]; wv[s][6] = u[2]; wv[s][7] = u[3];
+      } else if constexpr (BITS == 4) {
         const auto v = __builtin_amdgcn_raw_buffer_load_b128(rW, (int)wo, 0, 0);
         wv[s][0] = v[0]; wv[s][1] = v[1]; wv[s][2] = v[2]; wv[s][3] = v[3];
+      } else if constexpr (BITS == 3) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b96(rW, (int)wo, 0, 0);
+        wv[s][0] = v[0]; wv[s][1] = v[1]; wv[s][2] = v[2];
       } else {
         const auto v = __builtin_amdgcn_raw_buffer_load_b64(rW, (int)wo, 0, 0);
         wv[s][0] = v[0]; wv[s][1] = v[1];
@@ -181,9 +201,15 @@ __global__ __launch_bounds__(SK_THREADS) void skinny_kernel(PrefillArgs p) {
         sc[s] = (float)__builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(rS, (int)(2u * sb), 0, 0));
         if constexpr (ZK == 1) {
           const int bit = blk * BITS;
-          const uint32_t zb = __builtin_amdgcn_raw_buffer_load_b8(
-              rZ, (int)(wrow[s] * (uint32_t)p.zp_row_bytes + (uint32_t)(bit >> 3)), 0, 0);
-          z[s] = (float)((zb >> (bit & 7)) & ((1u << BITS) - 1u));
+          const uint32_t zo = wrow[s] * (uint32_t)p.zp_row_bytes + (uint32_t)(bit >> 3);
+          uint32_t zb = __builtin_amdgcn_raw_buffer_load_b8(rZ, (int)zo, 0, 0);
+          if constexpr (BITS == 8) {
+            z[s] = (float)(int8_t)zb;
+          } else {
+            // a 3-bit field may continue into the next byte (past the buffer it reads 0)
+            if constexpr (BITS == 3) zb |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rZ, (int)(zo + 1u), 0, 0) << 8;
+            z[s] = (float)((zb >> (bit & 7)) & ((1u << BITS) - 1u));
+          }
         } else if constexpr (ZK == 2) {
           z[s] = (float)__builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(rZ, (int)(2u * sb), 0, 0));
         } else {
@@ -208,8 +234,14 @@ __global__ __launch_bounds__(SK_THREADS) void skinny_kernel(PrefillArgs p) {
     for (int j = 0; j < 4; ++j) {
 #pragma unroll
       for (int s = 0; s < SK_NS; ++s) {
-        const uint32_t xw = BITS == 4 ? wv[s][j] : (wv[s][j >> 1] >> (16 * (j & 1)));
-        const f16x8 bf = dequant8<FMT, BITS>(xw, sc[s], z[s], am[s], cb);
+        uint32_t xw, xw2 = 0u;
+        if constexpr (BITS == 4) xw = wv[s][j];
+        else if constexpr (BITS == 2) xw = wv[s][j >> 1] >> (16 * (j & 1));
+        else if constexpr (BITS == 8) xw = wv[s][2 * j], xw2 = wv[s][2 * j + 1];
+        else  // 3 bits: the 24-bit field at bit 24 j of the 96-bit group
+          xw = j == 0 ? wv[s][0] : j == 1 ? __builtin_amdgcn_alignbit(wv[s][1], wv[s][0], 24)
+             : j == 2 ? __builtin_amdgcn_alignbit(wv[s][2], wv[s][1], 16) : (wv[s][2] >> 8);
+        const f16x8 bf = dequant8<FMT, BITS>(xw, xw2, sc[s], z[s], am[s], cb);
 #pragma unroll
         for (int mt = 0; mt < MB; ++mt)
           acc[mt][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[mt][j], bf, acc[mt][s], 0, 0, 0);
@@ -340,6 +372,14 @@ hipError_t launch_skinny(const PrefillArgs& p0, hipStream_t st) {
     if (zk == 1) sk_ct<GEMV_AFFINE, 2, 1>(p, st);
     else if (zk == 2) sk_ct<GEMV_AFFINE, 2, 2>(p, st);
     else sk_ct<GEMV_AFFINE, 2, 0>(p, st);
+  } else if (p.bits == 3) {
+    if (zk == 1) sk_ct<GEMV_AFFINE, 3, 1>(p, st);
+    else if (zk == 2) sk_ct<GEMV_AFFINE, 3, 2>(p, st);
+    else sk_ct<GEMV_AFFINE, 3, 0>(p, st);
+  } else if (p.bits == 8) {
+    if (zk == 1) sk_ct<GEMV_AFFINE, 8, 1>(p, st);
+    else if (zk == 2) sk_ct<GEMV_AFFINE, 8, 2>(p, st);
+    else sk_ct<GEMV_AFFINE, 8, 0>(p, st);
   } else {
     if (zk == 1) sk_ct<GEMV_AFFINE, 4, 1>(p, st);
     else if (zk == 2) sk_ct<GEMV_AFFINE, 4, 2>(p, st);

@@ -81,10 +81,13 @@ def packed_zero_points(rng, N: int, nblk: int, bits: int, fill: int | None = Non
     shape = tuple(lead) + (N, nbytes)
     if fill is None:
         return rng.integers(0, 256, size=shape, dtype=np.uint8)
-    byte = 0
-    for f in range(8 // bits):
-        byte |= (fill & ((1 << bits) - 1)) << (f * bits)
-    return np.full(shape, byte, dtype=np.uint8)
+    # the code `fill` in every field of a row's little-endian bit stream
+    bits_row = np.zeros(nbytes * 8 + 8, dtype=np.uint8)
+    for b in range(nblk):
+        for i in range(bits):
+            bits_row[b * bits + i] = (fill >> i) & 1
+    row = np.packbits(bits_row[: nbytes * 8].reshape(nbytes, 8), axis=1, bitorder="little").ravel()
+    return np.broadcast_to(row, shape).copy()
 
 
 def fp16_fill(shape, value: float) -> np.ndarray:
@@ -137,7 +140,7 @@ def nbits_problem(M, K, N, bits, block, *, seed, a_dtype=F32, scale_range=(0.005
 
     zp: "packed8" (packed code 2^(bits-1) everywhere), "packed" (random codes),
         "f16_uniform" (fp16 tensor filled with `uniform_zp`), "f16" (random fp16
-        in [0, 2^bits - 1]) or "none".
+        in [0, 2^bits - 1], or [-8, 8] for signed 8-bit codes) or "none".
     Draw order: A, codes, scales, zero points, bias.
     """
     rng = make_rng(seed)
@@ -155,7 +158,8 @@ def nbits_problem(M, K, N, bits, block, *, seed, a_dtype=F32, scale_range=(0.005
         p["zp"] = fp16_fill((N, nblk), uniform_zp)
         p["uniform_zp"] = float(np.float16(uniform_zp))
     elif zp == "f16":
-        p["zp"] = fp16_uniform(rng, (N, nblk), 0.0, float((1 << bits) - 1))
+        lo, hi = (-8.0, 8.0) if bits == 8 else (0.0, float((1 << bits) - 1))
+        p["zp"] = fp16_uniform(rng, (N, nblk), lo, hi)
     elif zp == "none":
         p["zp"] = None
     else:

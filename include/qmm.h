@@ -31,9 +31,11 @@
  *   - Matrices are dense and row-major: A[M][K] (row stride K), C[M][N].
  *   - Packed weights: W[N][nblk][block*bits/8] bytes, nblk = ceil(K/block).
  *     Element k of row n lives in block b = k/block at position j = k%block, as
- *     the `bits`-wide field starting at bit (j*bits)%8 of byte (j*bits)/8 of that
- *     block (least significant field first). Codes past K in the last block are
- *     padding and are never read.
+ *     the `bits`-wide field starting at bit j*bits of the block's little-endian
+ *     bit stream (bit i of byte m is stream bit 8m + i; least significant field
+ *     first, so a 3-bit field may continue into the next byte).  Codes of 2, 3 and
+ *     4 bits are unsigned; 8-bit codes are signed bytes (two's complement). Codes
+ *     past K in the last block are padding and are never read.
  *   - Dequantized weight (affine): w = fp32(fp32(q - zp) * fp32(scale)).
  *     Dequantized weight (codebook): w = fp32(codebook[q] * absmax).
  *   - Outputs are accumulated in fp32 and rounded once to the output dtype.
@@ -58,8 +60,9 @@ enum { QMM_F32 = 0, QMM_F16 = 1, QMM_BF16 = 2 };
 
 /* zero-point kinds ([P1] "What", commit 1) */
 enum {
-  QMM_ZP_NONE = 0,     /* zp = 2^(bits-1) for every block                             */
-  QMM_ZP_PACKED = 1,   /* uint8 [N][ceil(nblk*bits/8)]: unsigned codes, same field order as W */
+  QMM_ZP_NONE = 0,     /* zp = 2^(bits-1) for every block (0 for signed 8-bit codes)  */
+  QMM_ZP_PACKED = 1,   /* uint8 [N][ceil(nblk*bits/8)]: codes in W's field layout (signed
+                          bytes for 8-bit weights)                                      */
   QMM_ZP_F16 = 2,      /* fp16 [N][nblk]                                              */
   QMM_ZP_UNIFORM = 3   /* the scalar `uniform_zp`; the zp pointer is never read       */
 };
@@ -72,8 +75,9 @@ enum {
   QMM_OK = 0,
   QMM_E_NULL = -1,       /* a required pointer is NULL                                  */
   QMM_E_DTYPE = -2,      /* unsupported element type                                    */
-  QMM_E_BITS = -3,       /* bits not in {2, 4} (MoE: 4)                                 */
-  QMM_E_BLOCK = -4,      /* block not a power of two in [16, 256] (int8 MoE: >= 32)     */
+  QMM_E_BITS = -3,       /* bits not in {2, 3, 4, 8} (MoE: 4; activation ops: 8, 16)    */
+  QMM_E_BLOCK = -4,      /* block not a power of two in [16, 256] (3-bit weights and
+                            MoE: >= 32)                                                 */
   QMM_E_SHAPE = -5,      /* a size is negative or out of range                          */
   QMM_E_ALIGN = -6,      /* a pointer is not aligned as the kernels require             */
   QMM_E_WORKSPACE = -7,  /* workspace/scratch missing or smaller than the query says    */
@@ -87,7 +91,8 @@ enum {
  * qmm_nbits -- C[M][N] = A[M][K] . dequant(W)^T (+ bias)       ([P1] "What", commit 1)
  *
  *   A        [M][K] of a_type (QMM_F32, QMM_F16, QMM_BF16), contiguous, 16-byte aligned.
- *   W        packed codes, bits in {2, 4}, block in {16, 32, 64, 128, 256}.
+ *   W        packed codes, bits in {2, 3, 4, 8} ([P1] kernel unit-test leaves Wu2, Wu3,
+ *            Wu4, Wi8; 8 = signed), block in {16, 32, 64, 128, 256} (3 bits: >= 32).
  *   scales   fp16 [N][nblk].
  *   zp       per zp_kind (see above); uniform_zp used only for QMM_ZP_UNIFORM.
  *   bias     [N] of c_type, or NULL.

@@ -101,43 +101,67 @@ def activations_f64(A, a_dtype: str) -> np.ndarray:
 # Unpacking and dequantization  ([P1] "What", commit 1; [P3] "Summary")
 # ---------------------------------------------------------------------------
 
-def unpack_codes(W, bits: int, K: int, block: int) -> np.ndarray:
-    """Unsigned codes q[n, k] from packed W[N][nblk][block*bits/8].
+def _field(lo, hi, shift, bits: int) -> np.ndarray:
+    """The `bits`-wide field at bit `shift` of the 16-bit little-endian pair (lo, hi)."""
+    v = lo.astype(np.uint16) | (hi.astype(np.uint16) << np.uint16(8))
+    return ((v >> np.asarray(shift, dtype=np.uint16)) & np.uint16((1 << bits) - 1)).astype(np.uint8)
 
-    Element k sits in block b = k // block at position j = k % block; its code is
-    the `bits`-wide field starting at bit (j*bits) % 8 of byte (j*bits) // 8 of
-    that block (least significant field first).  Codes past K are not read.
+
+def unpack_codes(W, bits: int, K: int, block: int) -> np.ndarray:
+    """Codes q[n, k] from packed W[N][nblk][block*bits/8].
+
+    Element k sits in block b = k // block at position j = k % block; its code is the
+    `bits`-wide field starting at bit j*bits of the block's little-endian bit stream
+    (bit i of byte n of the block is stream bit 8n + i; least significant field first,
+    so a 3-bit field may continue into the next byte).  bits = 2, 3, 4: unsigned codes.
+    bits = 8: the byte is a signed two's-complement code in [-128, 127].  Codes past K
+    are not read.
     """
     W = np.asarray(W, dtype=np.uint8)
     k = np.arange(K)
     b = k // block
     j = k % block
-    byte_index = (j * bits) // 8
-    shift = ((j * bits) % 8).astype(np.uint8)
-    mask = np.uint8((1 << bits) - 1)
-    return (W[..., b, byte_index] >> shift) & mask
+    if bits == 8:
+        return W[..., b, j].view(np.int8)
+    nbytes = W.shape[-1]
+    pos = j * bits
+    byte = pos // 8
+    lo = W[..., b, byte]
+    hi = np.where(byte + 1 < nbytes, W[..., b, np.minimum(byte + 1, nbytes - 1)], 0)
+    return _field(lo, hi, pos % 8, bits)
 
 
 def unpack_zero_points(zp_packed, bits: int, nblk: int) -> np.ndarray:
-    """Packed per-block zero-point codes zp[n][ceil(nblk*bits/8)] -> [N, nblk].
+    """Packed per-block zero points zp[n][ceil(nblk*bits/8)] -> [N, nblk].
 
-    Same field order as the weights: block b is field b, least significant first.
-    """
+    Same field order as the weights: block b is the field at bit b*bits of the row's
+    bit stream.  bits = 8: signed bytes."""
     zp_packed = np.asarray(zp_packed, dtype=np.uint8)
     b = np.arange(nblk)
-    shift = ((b * bits) % 8).astype(np.uint8)
-    return (zp_packed[..., (b * bits) // 8] >> shift) & np.uint8((1 << bits) - 1)
+    if bits == 8:
+        return zp_packed[..., b].view(np.int8)
+    nbytes = zp_packed.shape[-1]
+    pos = b * bits
+    byte = pos // 8
+    lo = zp_packed[..., byte]
+    hi = np.where(byte + 1 < nbytes, zp_packed[..., np.minimum(byte + 1, nbytes - 1)], 0)
+    return _field(lo, hi, pos % 8, bits)
+
+
+def default_zero_point(bits: int) -> float:
+    """Zero point when none is given: 2^(bits-1) for unsigned codes, 0 for signed int8."""
+    return 0.0 if bits == 8 else float(1 << (bits - 1))
 
 
 def zero_points_f64(zp, zp_kind: str, bits: int, N: int, nblk: int,
                     uniform_zp: float = 0.0) -> np.ndarray:
     """Per-(row, block) zero point as fp64 [N, nblk] for each zero-point kind.
 
-    none -> 2^(bits-1); packed -> unsigned code; f16 -> the fp16 value;
-    uniform -> the scalar (given as fp32).
+    none -> default_zero_point(bits); packed -> the code (signed for bits = 8);
+    f16 -> the fp16 value; uniform -> the scalar (given as fp32).
     """
     if zp_kind == ZP_NONE:
-        return np.full((N, nblk), float(1 << (bits - 1)))
+        return np.full((N, nblk), default_zero_point(bits))
     if zp_kind == ZP_PACKED:
         return unpack_zero_points(zp, bits, nblk).astype(np.float64)
     if zp_kind == ZP_F16:
@@ -415,18 +439,25 @@ def dequantize_linear(q, scale_f32, zp) -> np.ndarray:
 
 
 def pack_codes(q, bits: int, block: int) -> np.ndarray:
-    """Pack codes q[N, K] into [N][nblk][block*bits/8], LSB-first, zero padding."""
-    q = np.asarray(q, dtype=np.uint8)
-    N, K = q.shape
+    """Pack codes q[N, K] into [N][nblk][block*bits/8], LSB-first bit streams, zero
+    padding (bits = 8: signed codes stored as their two's-complement bytes)."""
+    if bits == 8:
+        q8 = np.asarray(q).astype(np.int64).astype(np.int8).view(np.uint8)
+    else:
+        q8 = np.asarray(q).astype(np.uint8)
+    N, K = q8.shape
     nblk = (K + block - 1) // block
-    qp = np.zeros((N, nblk * block), dtype=np.uint8)
-    qp[:, :K] = q
-    per = 8 // bits
-    fields = qp.reshape(N, nblk, block // per, per)
-    out = np.zeros((N, nblk, block // per), dtype=np.uint8)
-    for f in range(per):
-        out |= (fields[..., f] << np.uint8(f * bits)).astype(np.uint8)
-    return out
+    qp = np.zeros((N, nblk * block), dtype=np.uint16)
+    qp[:, :K] = q8
+    qp = qp.reshape(N, nblk, block)
+    nbytes = block * bits // 8
+    out = np.zeros((N, nblk, nbytes + 1), dtype=np.uint16)
+    for j in range(block):
+        pos = j * bits
+        v = qp[..., j] << np.uint16(pos % 8)
+        out[..., pos // 8] |= v & np.uint16(0xFF)
+        out[..., pos // 8 + 1] |= v >> np.uint16(8)
+    return out[..., :nbytes].astype(np.uint8)
 
 
 def fake_quantize(x_f32, scale_f32, zp, bits):

@@ -47,8 +47,12 @@ def _v_nbits(**kw):
 
 def test_validate_nbits_codes():
     assert _v_nbits() == 0
-    assert _v_nbits(bits=3) == -3
-    assert _v_nbits(bits=8) == -3
+    assert _v_nbits(bits=3) == 0                # 3-bit codes, blocks of at least 32
+    assert _v_nbits(bits=3, block=16) == -4
+    assert _v_nbits(bits=8) == 0                # signed 8-bit codes
+    assert _v_nbits(bits=8, block=16) == 0
+    for b in (1, 5, 6, 16):
+        assert _v_nbits(bits=b) == -3, b
     for b in (8, 48, 96, 512, 0, -64):
         assert _v_nbits(block=b) == -4, b
     for b in (16, 32, 64, 128, 256):

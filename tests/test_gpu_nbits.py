@@ -212,7 +212,7 @@ def test_refused_arguments_on_device():
     p = gen.nbits_problem(1, 256, 16, 4, 64, seed=4, zp="packed8")
     d = NbitsDev(p)
     with pytest.raises(Q.QmmError) as e:
-        Q.qmm_nbits(d.A, d.W, d.scales, 256, 3, 64, d.zp, Q.QMM_ZP_PACKED)
+        Q.qmm_nbits(d.A, d.W, d.scales, 256, 5, 64, d.zp, Q.QMM_ZP_PACKED)
     assert e.value.status == -3
     with pytest.raises(Q.QmmError) as e:
         Q.qmm_nbits(d.A, d.W, d.scales, 256, 4, 48, d.zp, Q.QMM_ZP_PACKED)
@@ -485,3 +485,63 @@ def test_first_call_of_new_shape_under_capture():
     for r_ in reps:
         assert np.array_equal(r_, eager)
     _check(d, d.run(), label="after capture")
+
+
+# --- 3-bit and signed 8-bit weights ([P1] kernel unit-test leaves Wu3, Wi8) ------
+
+@pytest.mark.parametrize("bits,block,K,zp", [
+    (3, 32, 200, "packed"), (3, 64, 5120, "f16"), (3, 128, 300, "none"), (3, 256, 1000, "packed8"),
+    (8, 16, 70, "packed"), (8, 32, 2880, "none"), (8, 64, 512, "f16"), (8, 128, 300, "f16_uniform"),
+])
+@pytest.mark.parametrize("out", ["f32", "f16"])
+def test_dequant_wide_codes_bit_exact(bits, block, K, zp, out):
+    say(f"dequant bits={bits} block={block} K={K} zp={zp} out={out}")
+    t = torch()
+    p = gen.nbits_problem(1, K, 96, bits, block, seed=500 + K + bits, zp=zp)
+    d = NbitsDev(p)
+    got = Q.qmm_dequantize_nbits(d.W, d.scales, K, bits, block, d.zp, gpu_kind(zp),
+                                 out_dtype=t.float32 if out == "f32" else t.float16)
+    w = O.dequant_nbits(p["W"], bits, K, block, p["scales"], p["zp"], oracle_zp_kind(O, zp))
+    if out == "f32":
+        assert np.array_equal(host_bits(got).view(np.uint32), w.view(np.uint32))
+    else:
+        assert np.array_equal(host_bits(got).view(np.uint16), O.to_f16(w).view(np.uint16))
+
+
+WIDE_SHAPES = [(1000, 300, 32, "packed"), (2880, 257, 64, "f16"), (4096, 520, 128, "none")]
+
+
+@pytest.mark.parametrize("shape", range(len(WIDE_SHAPES)))
+@pytest.mark.parametrize("M", [1, 5, 33, 300])
+@pytest.mark.parametrize("bits", [3, 8])
+@pytest.mark.parametrize("leaf", ["f16", "f32"])
+def test_wide_codes_leaf_grid(leaf, bits, M, shape):
+    """The page's leaves X{fp16, fp32} x W{u3, i8} with the output in the activation type:
+    GEMV (M <= 8), skinny matrix-core kernel (8 < M <= 64) and 256 x 256 tiles."""
+    K, N, block, zp = WIDE_SHAPES[shape]
+    say(f"leaf X{leaf} W{'u3' if bits == 3 else 'i8'} M={M} K={K} N={N} block={block} zp={zp}")
+    p = gen.nbits_problem(M, K, N, bits, block, seed=510 + 7 * M + K + bits, zp=zp, a_dtype=leaf,
+                          bias=(M % 2 == 1))
+    d = NbitsDev(p, c_dtype=leaf)
+    y = d.run()
+    if M > 8:
+        _check_prefill(d, y, label=f"M={M}")
+    else:
+        _check(d, y, label=f"M={M}")
+
+
+def test_wide_codes_repeat_and_candidates():
+    """3-bit GEMV: every tiling candidate gives the same bits, and repeated calls too."""
+    p = gen.nbits_problem(3, 4096, 1000, 3, 64, seed=530, zp="packed")
+    d = NbitsDev(p)
+    outs = []
+    try:
+        for c in range(Q.num_candidates(Q.ENTRY_NBITS)):
+            Q.set_tuning(2, c)
+            outs.append(host_bits(d.run()).copy())
+    finally:
+        Q.set_tuning(0, 0)
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+    for _ in range(8):
+        assert np.array_equal(host_bits(d.run()), outs[0])
