@@ -1075,6 +1075,46 @@ qmm_status qmm::qmoe_decode_run(const uint16_t* X, int64_t T, int64_t H, int64_t
 
 extern "C" {
 
+qmm_status qmoe_ragged_mm(const uint16_t* X, int64_t R, int64_t K, int64_t N, int64_t E,
+                          const int32_t* row_offsets, qmoe_weights w, int bits, int block, uint16_t* Y,
+                          void* stream) {
+  (void)hipGetLastError();
+  if (bits != 4) return QMM_E_BITS;
+  if (!is_pow2_block(block) || block < 32) return QMM_E_BLOCK;
+  if (R < 0 || K <= 0 || N <= 0 || E < 1 || E > (1LL << 20) || K % 8 != 0) return QMM_E_SHAPE;
+  const int64_t nblk = ceil_div(K, block);
+  const int64_t row_bytes = nblk * block / 2;
+  // 32-bit buffer offsets: X, and one expert's weights and scales
+  if (R * K * 2 >= (1LL << 31) || N * row_bytes >= (1LL << 31) || N * nblk * 2 >= (1LL << 31) ||
+      R >= (1LL << 31) - 64)
+    return QMM_E_SHAPE;
+  if (R == 0) return QMM_OK;
+  if (!X || !row_offsets || !w.W || !w.scales || !Y) return QMM_E_NULL;
+  if (!aligned(X, 16) || !aligned(Y, 2) || !aligned(row_offsets, 4) || !aligned(w.W, 16) ||
+      !aligned(w.scales, 2) || !aligned(w.bias, 2))
+    return QMM_E_ALIGN;
+  RaggedArgs p{};
+  p.X = X;
+  p.R = R;
+  p.K = K;
+  p.N = N;
+  p.E = E;
+  p.offsets = row_offsets;
+  p.W = w.W;
+  p.scales = w.scales;
+  p.zp = w.zp;
+  p.bias = w.bias;
+  p.block = block;
+  p.block_log2 = __builtin_ctz((unsigned)block);
+  p.nblk = nblk;
+  p.row_bytes = row_bytes;
+  p.zp_row_bytes = ceil_div(nblk, 2);
+  p.Y = Y;
+  const hipError_t e = launch_ragged(p, (hipStream_t)stream);
+  if (e != hipSuccess) return (qmm_status)e;
+  return (qmm_status)hipGetLastError();
+}
+
 qmm_status qmoe_decode_status(void* scratch, size_t scratch_bytes, int64_t T, int64_t H, int64_t I, int k,
                               int mode, int* timed_out, void* stream) {
   (void)hipGetLastError();

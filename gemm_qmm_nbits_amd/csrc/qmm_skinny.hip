@@ -331,7 +331,199 @@ void sk_ct(const PrefillArgs& p, hipStream_t st) {
   else sk_mb<FMT, BITS, ZK, QMM_BF16>(p, st);
 }
 
+
+// ---- ragged multi-token MoE matmul -------------------------------------------------
+//
+// Rows of X are grouped by expert (expert e owns rows offsets[e] .. offsets[e+1]-1), and
+// Y[r] = fp16(X[r] . W16_e^T + b_e) with the operands of the skinny kernel: fp16 X as
+// given and W16 = fp16 of the exact fp32 dequant.  Work-group slot y is the y-th tile of
+// 16 * MB rows in expert order (each expert's rows split into tiles, empty experts none);
+// wave 0 finds the slot's expert by a prefix sum of the experts' tile counts, and slots
+// past the last tile exit.  Within a tile the work is the skinny kernel's: 8 waves take
+// 128-code steps, lane l loads 32 codes of W_e row n0 + 16 s + l % 16 per strip s and 8
+// fp16 of X row l % 16 of each 16-row M tile (rows of the next expert and k >= K read
+// as zero), v_mfma_f32_16x16x32_f16 accumulates, and the waves' sums are added in wave
+// order.  The summation order depends only on K.
+template <int ZK, int MB, int NS>
+__global__ __launch_bounds__(SK_THREADS) void ragged_kernel(RaggedArgs p) {
+  extern __shared__ float red[];  // [SK_WAVES][MB * NS * 4][64]
+  __shared__ int slot_expert, slot_tile;
+  const int wave = (int)(threadIdx.x >> 6);
+  const int lane = (int)(threadIdx.x & 63);
+  const int ln = lane & 15, lq = lane >> 4;
+  const int R = (int)p.R, E = (int)p.E, N = (int)p.N, K = (int)p.K;
+  constexpr int kTileRows = 16 * MB;
+  // offsets are clamped into [0, R] and made nondecreasing, so every row index stays in X
+  auto off = [&](int e) {
+    const int o = p.offsets[e];
+    return o < 0 ? 0 : o > R ? R : o;
+  };
+  if (wave == 0) {
+    const int slot = (int)blockIdx.y;
+    int found_e = -1, found_t = 0, base = 0;
+    for (int c = 0; c < E && found_e < 0; c += 64) {  // uniform over the wave
+      const int e = c + lane;
+      int tiles = 0;
+      if (e < E) {
+        const int o0 = off(e), o1 = off(e + 1);
+        tiles = o1 > o0 ? (o1 - o0 + kTileRows - 1) / kTileRows : 0;
+      }
+      int incl = tiles;  // inclusive prefix over the lanes
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int v = __shfl_up(incl, d, 64);
+        incl += lane >= d ? v : 0;
+      }
+      const int excl = incl - tiles;
+      const bool mine = e < E && slot >= base + excl && slot < base + incl;
+      const unsigned long long m = __ballot(mine);
+      if (m) {
+        const int src = __ffsll((long long)m) - 1;
+        found_e = c + src;
+        found_t = slot - base - __shfl(excl, src, 64);
+      }
+      base += __shfl(incl, 63, 64);
+    }
+    if (lane == 0) {
+      slot_expert = found_e;
+      slot_tile = found_t;
+    }
+  }
+  __syncthreads();
+  const int e = slot_expert;
+  if (e < 0) return;  // past the last tile (uniform over the work-group)
+  const int o0 = off(e), o1e = off(e + 1);
+  const int o1 = o1e > o0 ? o1e : o0;
+  const int r_begin = o0 + slot_tile * kTileRows;
+  const int r_end = r_begin + kTileRows < o1 ? r_begin + kTileRows : o1;
+
+  const int nblk = (int)p.nblk, blog = p.block_log2;
+  const int nsteps = (K + SK_STEP - 1) / SK_STEP;
+  const int n0 = (int)blockIdx.x * (NS * 16);
+  const int64_t ew = (int64_t)e * p.N;  // first W row of expert e
+  const __amdgpu_buffer_rsrc_t rW = sk_rsrc(p.W + ew * p.row_bytes, p.N * p.row_bytes);
+  const __amdgpu_buffer_rsrc_t rS = sk_rsrc(p.scales + ew * nblk, p.N * p.nblk * 2);
+  __amdgpu_buffer_rsrc_t rZ = rS;
+  if constexpr (ZK == 1) rZ = sk_rsrc(p.zp + ew * p.zp_row_bytes, p.N * p.zp_row_bytes);
+  const __amdgpu_buffer_rsrc_t rA = sk_rsrc(p.X, p.R * p.K * 2);
+
+  uint32_t wrow[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int n = n0 + s * 16 + ln;
+    wrow[s] = (uint32_t)(n < N ? n : N - 1);
+  }
+  // X rows of this lane per M tile, or -1 past the tile's rows
+  int arow[MB];
+#pragma unroll
+  for (int mt = 0; mt < MB; ++mt) {
+    const int r = r_begin + mt * 16 + ln;
+    arow[mt] = r < r_end ? r : -1;
+  }
+
+  f32x4 acc[MB][NS];
+#pragma unroll
+  for (int mt = 0; mt < MB; ++mt)
+#pragma unroll
+    for (int s = 0; s < NS; ++s) acc[mt][s] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  for (int c = wave; c < nsteps; c += SK_WAVES) {
+    const int k0 = c * SK_STEP + lq * 32;  // this lane's 32 codes
+    uint32_t wv[NS][4];
+    float sc[NS], z[NS];
+    int blk = k0 >> blog;
+    blk = blk < nblk - 1 ? blk : nblk - 1;  // codes past the row end meet zero X
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const uint32_t wo = wrow[s] * (uint32_t)p.row_bytes + (uint32_t)(k0 / 2);
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rW, (int)wo, 0, 0);
+      wv[s][0] = v[0]; wv[s][1] = v[1]; wv[s][2] = v[2]; wv[s][3] = v[3];
+      const uint32_t sb = wrow[s] * (uint32_t)nblk + (uint32_t)blk;
+      sc[s] = (float)__builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(rS, (int)(2u * sb), 0, 0));
+      if constexpr (ZK == 1) {
+        const uint32_t zb = __builtin_amdgcn_raw_buffer_load_b8(
+            rZ, (int)(wrow[s] * (uint32_t)p.zp_row_bytes + (uint32_t)(blk >> 1)), 0, 0);
+        z[s] = (float)((zb >> (4 * (blk & 1))) & 15u);
+      } else {
+        z[s] = 8.0f;
+      }
+    }
+    f16x8 af[MB][4];
+#pragma unroll
+    for (int mt = 0; mt < MB; ++mt) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool ok = arow[mt] >= 0 && k0 + 8 * j < K;
+        const uint32_t ao = ok ? ((uint32_t)arow[mt] * (uint32_t)K + (uint32_t)(k0 + 8 * j)) * 2u : 0u;
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(rA, (int)ao, 0, 0);
+        const uint4 u = ok ? make_uint4(v[0], v[1], v[2], v[3]) : make_uint4(0u, 0u, 0u, 0u);
+        af[mt][j] = __builtin_bit_cast(f16x8, u);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const f16x8 bf = dequant8<GEMV_AFFINE, 4>(wv[s][j], 0u, sc[s], z[s], 0.0f, nullptr);
+#pragma unroll
+        for (int mt = 0; mt < MB; ++mt)
+          acc[mt][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[mt][j], bf, acc[mt][s], 0, 0, 0);
+      }
+    }
+  }
+
+  constexpr int RR = MB * NS * 4;
+#pragma unroll
+  for (int mt = 0; mt < MB; ++mt)
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) red[((wave * RR) + (mt * NS + s) * 4 + v) * 64 + lane] = acc[mt][s][v];
+  __syncthreads();
+  const uint16_t* bias = p.bias ? p.bias + ew : nullptr;
+  for (int i = (int)threadIdx.x; i < RR * 64; i += SK_THREADS) {
+    const int r = i >> 6, l = i & 63;
+    const int mt = r / (NS * 4), s = (r >> 2) % NS, v = r & 3;
+    const int row = r_begin + mt * 16 + 4 * (l >> 4) + v;
+    const int n = n0 + s * 16 + (l & 15);
+    if (row >= r_end || n >= N) continue;
+    float y = red[r * 64 + l];
+#pragma unroll
+    for (int w = 1; w < SK_WAVES; ++w) y += red[(w * RR + r) * 64 + l];
+    if (bias) y += f16_to_f32(bias[n]);
+    p.Y[(int64_t)row * N + n] = f32_to_f16(y);
+  }
+}
+
+template <int ZK, int MB, int NS>
+void ragged_launch(const RaggedArgs& p, hipStream_t st) {
+  auto kern = ragged_kernel<ZK, MB, NS>;
+  const size_t lds = (size_t)SK_WAVES * MB * NS * 4 * 64 * sizeof(float);
+  if (lds > 64 * 1024) (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  const unsigned gx = (unsigned)((p.N + NS * 16 - 1) / (NS * 16));
+  // every expert's tiles, at most ceil(R / rows) + E slots
+  const unsigned gy = (unsigned)((p.R + 16 * MB - 1) / (16 * MB) + p.E);
+  hipLaunchKernelGGL(kern, dim3(gx, gy), dim3(SK_THREADS), lds, st, p);
+}
+
+template <int ZK>
+void ragged_mb(const RaggedArgs& p, hipStream_t st) {
+  // tile height from the mean rows per expert: one 16-row tile for sparse bursts, up to
+  // four when experts hold many rows (each weight strip then feeds more MFMA steps)
+  const int64_t mean = p.E > 0 ? (p.R + p.E - 1) / p.E : p.R;
+  const bool wide = p.N >= 2048;
+  if (mean <= 16) wide ? ragged_launch<ZK, 1, 2>(p, st) : ragged_launch<ZK, 1, 1>(p, st);
+  else if (mean <= 32) wide ? ragged_launch<ZK, 2, 2>(p, st) : ragged_launch<ZK, 2, 1>(p, st);
+  else wide ? ragged_launch<ZK, 4, 2>(p, st) : ragged_launch<ZK, 4, 1>(p, st);
+}
+
 }  // namespace
+
+hipError_t launch_ragged(const RaggedArgs& p, hipStream_t st) {
+  if (p.zp) ragged_mb<1>(p, st);
+  else ragged_mb<0>(p, st);
+  return hipSuccess;
+}
 
 bool skinny_applies(int64_t M, int64_t N, int64_t Kp, int block, int64_t row_bytes, int64_t nblk) {
   // 32-bit buffer offsets for W, scales and the workspace rows

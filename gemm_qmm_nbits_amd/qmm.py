@@ -68,6 +68,8 @@ _SIGS = {
     "qmoe_decode_scratch_bytes": (c_size_t, [c_int64, c_int64, c_int64, c_int, c_int]),
     "qmoe_decode_status": (c_int, [c_void_p, c_size_t, c_int64, c_int64, c_int64, c_int, c_int,
                                    POINTER(c_int), c_void_p]),
+    "qmoe_ragged_mm": (c_int, [c_void_p, c_int64, c_int64, c_int64, c_int64, c_void_p, qmoe_weights, c_int,
+                               c_int, c_void_p, c_void_p]),
     "qmoe_decode_fused_noalloc": (c_int, [c_void_p, c_int64, c_int64, c_int64, c_int64, c_int, c_void_p,
                                           c_void_p, qmoe_weights, qmoe_weights, c_int, c_int, c_int,
                                           c_void_p, c_void_p]),
@@ -270,6 +272,20 @@ def qmoe_decode_fused(X, expert_ids, expert_w, fc1, fc2, H, I, E, block, mode=QM
                                  _qw(fc2), bits, block, mode, _ptr(out), _ptr(scratch),
                                  scratch.numel() * scratch.element_size(), _stream(stream))
     _check("qmoe_decode_fused", st)
+    return out
+
+
+def qmoe_ragged_mm(X, row_offsets, w, N, E, block, bits=4, out=None, stream=None):
+    """Y[R, N] fp16: rows of X grouped by expert (row_offsets [E+1] int32 on the device),
+    each row times its expert's dequantized u4 weights (w: dict W, scales, zp, bias)."""
+    torch = _torch()
+    X = _contig(X, "X")
+    R, K = X.shape
+    if out is None:
+        out = torch.empty((R, N), dtype=torch.float16, device=X.device)
+    st = lib().qmoe_ragged_mm(_ptr(X), R, K, N, E, _ptr(row_offsets), _qw(w), bits, block, _ptr(out),
+                              _stream(stream))
+    _check("qmoe_ragged_mm", st)
     return out
 
 

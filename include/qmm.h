@@ -245,6 +245,28 @@ qmm_status qmoe_decode_fused(const uint16_t* X, int64_t T, int64_t H, int64_t I,
 
 size_t qmoe_decode_scratch_bytes(int64_t T, int64_t H, int64_t I, int k, int mode);
 
+/* ---------------------------------------------------------------------------
+ * qmoe_ragged_mm -- the expert matmul of a multi-token MoE burst ([P1]/[P2] "Kernel Unit
+ * Test Results": qmoe_ragged_mm, leaf Xfp16_Wu4_Yfp16; [P2] "Related issue or design":
+ * T-token bursts through the QMoE layer).
+ *   Rows of X are grouped by expert: expert e owns rows row_offsets[e] ..
+ *   row_offsets[e+1] - 1 (row_offsets [E+1] int32 on the device, nondecreasing,
+ *   row_offsets[0] = 0, row_offsets[E] = R; values are clamped into [0, R] on the
+ *   device, and rows no expert owns are not written).  For each such row r
+ *     Y[r] = fp16( X[r] . W16_e^T + bias_e )
+ *   with W16_e = fp16 of the exact dequantized u4 weight (w = fp32(fp32(q - zp) * s),
+ *   zp 8 when w.zp is NULL) and the products accumulated in fp32 on the fp16 matrix
+ *   cores (the operand rounding of the matrix-core paths of qmm_nbits).
+ *   X      fp16 [R][K], 16-byte aligned, K a multiple of 8.
+ *   w      W [E][N][nblk][block/2], scales fp16 [E][N][nblk], zp packed u4
+ *          [E][N][ceil(nblk/2)] or NULL, bias fp16 [E][N] or NULL.
+ *   bits   4.  block: power of two in [32, 256].   Y fp16 [R][N].
+ *   One launch; tiles of 16 to 64 rows of one expert per work-group.
+ * ------------------------------------------------------------------------- */
+qmm_status qmoe_ragged_mm(const uint16_t* X, int64_t R, int64_t K, int64_t N, int64_t E,
+                          const int32_t* row_offsets, qmoe_weights w, int bits, int block,
+                          uint16_t* Y, void* stream);
+
 /* qmoe_decode_fused_noalloc -- qmoe_decode_fused for callers that cannot allocate
  * (code under stream capture, tight serving loops, harnesses that forbid hipMalloc).
  * Same arguments and results as qmoe_decode_fused, without scratch: the scratch is a

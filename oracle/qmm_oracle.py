@@ -408,6 +408,48 @@ def qmoe_decode(X_f16, ids, rw, fc1, fc2, H, I, block, bits=4, mode="fp"):
 
 
 # ---------------------------------------------------------------------------
+# Ragged multi-token MoE matmul  ([P1]/[P2] "Kernel Unit Test Results": the
+# qmoe_ragged_mm leaf Xfp16_Wu4_Yfp16; [P2] "Related issue or design": bursts of
+# T tokens through the QMoE layer)
+# ---------------------------------------------------------------------------
+
+def group_by_expert(ids, E: int):
+    """Rows of a ragged expert batch from top-k routing ids [T, k]: the (token, slot)
+    pairs ordered by expert, and within an expert by token then slot (a stable sort of
+    the flattened ids).  Returns (order [T*k] of flat slot indices t*k + j, offsets
+    [E+1]: expert e owns rows offsets[e] .. offsets[e+1]-1)."""
+    flat = np.asarray(ids, dtype=np.int64).ravel()
+    order = np.argsort(flat, kind="stable")
+    counts = np.bincount(flat, minlength=E)
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(counts)
+    return order, offsets
+
+
+def qmoe_ragged_mm(X_f16, offsets, fc, K, N, block, bits=4, w_round=None) -> np.ndarray:
+    """Grouped matmul over experts: rows r in [offsets[e], offsets[e+1]) use expert e,
+
+        y[r] = x[r] . dequant(W_e)^T + b_e      (fp64, unrounded; empty experts skipped)
+
+    X fp16 bits [R, K]; fc = {"W" [E][N][nblk][B/2], "scales" [E][N][nblk], "zp" packed
+    or None, "bias" fp16 [E][N] or None}.  w_round names the declared rounding of the
+    dequantized weights (e.g. "f16" for the matrix-core operand)."""
+    X = f16_bits_to_f64(X_f16)
+    R = X.shape[0]
+    y = np.zeros((R, N))
+    offsets = np.asarray(offsets, dtype=np.int64)
+    for e in range(len(offsets) - 1):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 <= r0:
+            continue
+        w = _round_operand(_expert_dequant(fc, e, bits, K, block, N).astype(np.float64), w_round)
+        y[r0:r1] = X[r0:r1] @ w.T
+        if fc.get("bias") is not None:
+            y[r0:r1] += f16_bits_to_f64(np.asarray(fc["bias"])[e])[None, :]
+    return y
+
+
+# ---------------------------------------------------------------------------
 # Quantize -> dequantize round trip  ([P1] "What", commit 4: fake_quantize
 # exactly equal to the unfused Q -> DQ chain)
 # ---------------------------------------------------------------------------

@@ -659,7 +659,40 @@ def pin_quantized_ops(O, seed=47):
         assert y[0] == 0.0   # a zero gate gives silu 0 and an output of 0
 
 
+def pin_ragged_mm(O, seed=53):
+    """Ragged expert matmul vs exact rationals (ragged last block, zero points, bias, an
+    empty expert, a one-row expert); the grouping is a stable sort by expert."""
+    rng = np.random.default_rng(seed)
+    E, K, N, block = 4, 40, 3, 32
+    ids = np.array([[2, 0], [2, 3], [0, 2], [3, 2]], dtype=np.int32)   # expert 1 unused
+    order, offsets = O.group_by_expert(ids, E)
+    assert list(offsets) == [0, 2, 2, 6, 8]
+    assert list(order) == [1, 4, 0, 2, 5, 7, 3, 6]
+    p = gen.qmoe_problem(1, K, N // 2, E, 1, block, seed=seed, zp=True, bias=True)
+    fc = p["fc1"]   # [E][N][...] with N = 2 * (N // 2) rows ... use the first N rows
+    Nn = fc["W"].shape[1]
+    X = gen.activations(rng, (8, K), "f16")
+    y = O.qmoe_ragged_mm(X, offsets, fc, K, Nn, block)
+    nblk = gen.nblocks(K, block)
+    for e in range(E):
+        q = bitstring_codes(fc["W"][e], 4, K, block)
+        z = bitstring_zp(fc["zp"][e], 4, nblk)
+        for r in range(int(offsets[e]), int(offsets[e + 1])):
+            for n in range(Nn):
+                acc = sum(fr16(X[r, k]) * (Fr(int(q[n, k])) - int(z[n, k // block])) *
+                          fr16(fc["scales"][e, n, k // block]) for k in range(K))
+                acc += fr16(fc["bias"][e, n])
+                assert abs(float(Fr(float(y[r, n])) - acc)) <= 1e-12 * (1 + abs(float(acc))), (e, r, n)
+    # every row of one expert: the plain MatMulNBits of that expert
+    one = np.array([0, 0, 8, 8, 8], dtype=np.int64)
+    y1 = O.qmoe_ragged_mm(X, one, fc, K, Nn, block)
+    want = O.qmm_nbits(X, "f16", fc["W"][1], 4, K, block, fc["scales"][1], fc["zp"][1], O.ZP_PACKED,
+                       bias=fc["bias"][1], bias_dtype="f16")
+    assert np.allclose(y1, want, rtol=1e-13, atol=1e-13)
+
+
 ALL_PINS = [pin_unpack_exhaustive, pin_nbits_bruteforce, pin_nbits_closed_forms,
             pin_codebook_bruteforce, pin_codebook_linear_equals_affine, pin_fake_quant_chain,
             pin_bf16_rounding, pin_f16_rounding, pin_swiglu, pin_int8_quantizer, pin_uniform_zp,
-            pin_qmoe_bruteforce, pin_qmoe_composition, pin_round_operand, pin_rel_l2, pin_quantized_ops]
+            pin_qmoe_bruteforce, pin_qmoe_composition, pin_round_operand, pin_rel_l2, pin_quantized_ops,
+            pin_ragged_mm]
