@@ -902,6 +902,64 @@ qmm_status qmm_codebook4(const void* A, int a_type, int64_t M, int64_t K, int64_
   return (qmm_status)hipGetLastError();
 }
 
+static qmm_status check_nested(const qmm_nested_absmax* a) {
+  if (!a) return QMM_E_NULL;
+  if (a->group < 1) return QMM_E_SHAPE;
+  if (!a->codes || !a->table || !a->scales) return QMM_E_NULL;
+  if (!aligned(a->table, 4) || !aligned(a->scales, 4)) return QMM_E_ALIGN;
+  return QMM_OK;
+}
+
+qmm_status qmm_dequantize_absmax_nested(const qmm_nested_absmax* absmax, int64_t count, float* out, void* stream) {
+  (void)hipGetLastError();
+  if (count < 0) return QMM_E_SHAPE;
+  if (count == 0) return QMM_OK;
+  const qmm_status s = check_nested(absmax);
+  if (s != QMM_OK) return s;
+  if (!out) return QMM_E_NULL;
+  if (!aligned(out, 4)) return QMM_E_ALIGN;
+  const hipError_t e = launch_nested_absmax(absmax->codes, absmax->table, absmax->scales, absmax->offset,
+                                            absmax->group, count, out, (hipStream_t)stream);
+  if (e != hipSuccess) return (qmm_status)e;
+  return (qmm_status)hipGetLastError();
+}
+
+size_t qmm_codebook4_nested_workspace_bytes(int64_t M, int64_t K, int64_t N, int a_type, int block) {
+  if (M <= 0 || K <= 0 || N <= 0 || !is_pow2_block(block)) return 0;
+  const size_t am = ((size_t)N * (size_t)ceil_div(K, block) * 4 + 255) & ~size_t(255);
+  return am + qmm_codebook4_workspace_bytes(M, K, N, a_type);
+}
+
+qmm_status qmm_codebook4_nested(const void* A, int a_type, int64_t M, int64_t K, int64_t N, const uint8_t* W,
+                                int block, const qmm_nested_absmax* absmax, const float* codebook,
+                                const void* bias, void* C, int c_type, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  (void)hipGetLastError();
+  if (!is_pow2_block(block)) return QMM_E_BLOCK;
+  if (M < 0 || K < 0 || N < 0 || M > (1LL << 30) || K > (1LL << 30) || N > (1LL << 30)) return QMM_E_SHAPE;
+  if (M == 0 || N == 0) return QMM_OK;
+  qmm_status s = K > 0 ? check_nested(absmax) : QMM_OK;
+  if (s != QMM_OK) return s;
+  const size_t need = qmm_codebook4_nested_workspace_bytes(M, K, N, a_type, block);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return QMM_E_WORKSPACE;
+  if (need > 0 && !aligned(workspace, 256)) return QMM_E_ALIGN;
+  const size_t am_bytes = K > 0 ? (((size_t)N * (size_t)ceil_div(K, block) * 4 + 255) & ~size_t(255)) : 0;
+  float* am = (float*)workspace;
+  // the regular entry's own checks, with the decoded absmax in place of a caller's
+  s = check_codebook(A, a_type, M, K, N, W, block, K > 0 ? am : nullptr, codebook, bias, C, c_type,
+                     (uint8_t*)workspace + am_bytes, workspace_bytes - am_bytes);
+  if (s != QMM_OK) return s;
+  if (K > 0) {
+    const hipError_t e = launch_nested_absmax(absmax->codes, absmax->table, absmax->scales, absmax->offset,
+                                              absmax->group, N * ceil_div(K, block), am, (hipStream_t)stream);
+    if (e != hipSuccess) return (qmm_status)e;
+    const hipError_t le = hipGetLastError();
+    if (le != hipSuccess) return (qmm_status)le;
+  }
+  return qmm_codebook4(A, a_type, M, K, N, W, block, am, codebook, bias, C, c_type, (uint8_t*)workspace + am_bytes,
+                       workspace_bytes - am_bytes, stream);
+}
+
 size_t qmm_uniform_scratch_bytes(void) { return (2 + kUniformPartials) * sizeof(uint32_t); }
 
 qmm_status qmm_fp16_uniform_value(const uint16_t* zp, int64_t count, void* scratch,

@@ -72,6 +72,8 @@ hipError_t launch_dequant(const DequantArgs& d, hipStream_t st);
 
 hipError_t launch_uniform_check(const uint16_t* zp, int64_t count, uint32_t* scratch,
                                 hipStream_t st);
+hipError_t launch_nested_absmax(const uint8_t* codes, const float* table, const float* scales, float offset,
+                                int group, int64_t count, float* out, hipStream_t st);
 constexpr int kUniformPartials = 256;
 
 // A (fp32 / fp16 / bf16) -> fp16 rows of Kp elements with a per-row power-of-two

@@ -40,6 +40,29 @@ hipError_t launch_dequant(const DequantArgs& d, hipStream_t st) {
   return hipSuccess;
 }
 
+// ---- nested absmax ([P3] "Testing plan": nested absmax) ------------------------
+// out[i] = fp32(fp32(table[codes[i]] * scales[i / group]) + offset), each operation
+// rounded once (no contraction).
+__global__ __launch_bounds__(256) void nested_absmax_kernel(const uint8_t* codes, const float* table,
+                                                            const float* scales, float offset, int group,
+                                                            int64_t count, float* out) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const float prod = __fmul_rn(table[codes[i]], scales[i / group]);
+    out[i] = __fadd_rn(materialize(prod), offset);
+  }
+}
+
+hipError_t launch_nested_absmax(const uint8_t* codes, const float* table, const float* scales, float offset,
+                                int group, int64_t count, float* out, hipStream_t st) {
+  int64_t blocks = (count + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(nested_absmax_kernel, dim3((unsigned)blocks), dim3(256), 0, st, codes, table, scales, offset,
+                     group, count, out);
+  return hipSuccess;
+}
+
 // ---- uniform zero point ([P1] "What", commit 1) ------------------------------
 // Pass 1: partial p of kUniformPartials records whether its slice holds any fp16
 // bit pattern different from zp[0].  Pass 2: one work-group folds the partials

@@ -112,6 +112,23 @@ def fp32_uniform(rng, shape, lo: float, hi: float) -> np.ndarray:
     return rng.uniform(lo, hi, size=shape).astype(np.float32)
 
 
+def nested_absmax_inputs(rng, N: int, nblk: int, group: int = 256):
+    """Double-quantized absmax storage: uint8 codes [N][nblk] (uniform), a sorted
+    256-entry fp32 table in [-1, 1] holding -1, 0 and 1 (the other entries i.i.d.
+    U(-1, 1), no repeats), fp32 scales U[0.01, 0.04] per `group` blocks and an fp32
+    offset 0.055 (so the decoded absmax lies in [0.015, 0.095])."""
+    codes = rng.integers(0, 256, size=(N, nblk), dtype=np.uint8)
+    vals = {np.float32(-1.0), np.float32(0.0), np.float32(1.0)}
+    while len(vals) < 256:
+        v = np.float32(rng.uniform(-1.0, 1.0))
+        if v != 0.0:
+            vals.add(v)
+    table = np.array(sorted(vals), dtype=np.float32)
+    ngroups = (N * nblk + group - 1) // group
+    scales = rng.uniform(0.01, 0.04, size=ngroups).astype(np.float32)
+    return {"codes": codes, "table": table, "scales": scales, "offset": np.float32(0.055), "group": group}
+
+
 def routing(rng, T: int, E: int, k: int):
     """Top-k routing from N(0,1) logits: ids [T,k] int32, weights [T,k] fp32.
 

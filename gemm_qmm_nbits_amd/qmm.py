@@ -38,6 +38,11 @@ class qmm_qparams(Structure):
     _fields_ = [("scale", c_float), ("zero_point", ctypes.c_int32)]
 
 
+class qmm_nested_absmax(Structure):
+    _fields_ = [("codes", c_void_p), ("table", c_void_p), ("scales", c_void_p), ("offset", c_float),
+                ("group", c_int)]
+
+
 _lib = None
 
 _SIGS = {
@@ -55,6 +60,11 @@ _SIGS = {
     "qmm_validate_codebook4": (c_int, [c_void_p, c_int, c_int64, c_int64, c_int64, c_void_p, c_int,
                                        c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_void_p,
                                        c_size_t]),
+    "qmm_dequantize_absmax_nested": (c_int, [POINTER(qmm_nested_absmax), c_int64, c_void_p, c_void_p]),
+    "qmm_codebook4_nested": (c_int, [c_void_p, c_int, c_int64, c_int64, c_int64, c_void_p, c_int,
+                                     POINTER(qmm_nested_absmax), c_void_p, c_void_p, c_void_p, c_int, c_void_p,
+                                     c_size_t, c_void_p]),
+    "qmm_codebook4_nested_workspace_bytes": (c_size_t, [c_int64, c_int64, c_int64, c_int, c_int]),
     "qmm_fp16_uniform_value": (c_int, [c_void_p, c_int64, c_void_p, c_size_t, POINTER(c_int),
                                        POINTER(c_float), c_void_p]),
     "qmm_uniform_scratch_bytes": (c_size_t, []),
@@ -200,6 +210,42 @@ def qmm_codebook4(A, W, absmax, codebook, K, block=64, bias=None, out=None, out_
                              0 if workspace is None else workspace.numel() * workspace.element_size(),
                              _stream(stream))
     _check("qmm_codebook4", st)
+    return out
+
+
+def _nested(na):
+    """na: dict of device tensors codes, table, scales and python offset, group."""
+    return qmm_nested_absmax(na["codes"].data_ptr(), na["table"].data_ptr(), na["scales"].data_ptr(),
+                             float(na["offset"]), int(na["group"]))
+
+
+def qmm_dequantize_absmax_nested(na, count, stream=None):
+    torch = _torch()
+    out = torch.empty(count, dtype=torch.float32, device=na["codes"].device)
+    desc = _nested(na)
+    _check("qmm_dequantize_absmax_nested", lib().qmm_dequantize_absmax_nested(ctypes.byref(desc), count, _ptr(out),
+                                                                              _stream(stream)))
+    return out
+
+
+def qmm_codebook4_nested(A, W, na, codebook, K, block=64, bias=None, out=None, out_dtype=None, workspace=None,
+                         stream=None):
+    torch = _torch()
+    A = _contig(A, "A")
+    M = A.shape[0]
+    N = W.shape[0]
+    ctype = dtype_code(A) if out_dtype is None else dtype_code(torch.empty(0, dtype=out_dtype))
+    if out is None:
+        out = torch.empty((M, N), dtype=torch_dtype(ctype), device=A.device)
+    ws_bytes = lib().qmm_codebook4_nested_workspace_bytes(M, K, N, dtype_code(A), block)
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=A.device)
+    desc = _nested(na)
+    st = lib().qmm_codebook4_nested(_ptr(A), dtype_code(A), M, K, N, _ptr(W), block, ctypes.byref(desc),
+                                    _ptr(codebook), _ptr(bias), _ptr(out), dtype_code(out), _ptr(workspace),
+                                    0 if workspace is None else workspace.numel() * workspace.element_size(),
+                                    _stream(stream))
+    _check("qmm_codebook4_nested", st)
     return out
 
 

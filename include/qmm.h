@@ -158,6 +158,37 @@ qmm_status qmm_validate_codebook4(const void* A, int a_type, int64_t M, int64_t 
                                   int c_type, const void* workspace, size_t workspace_bytes);
 
 /* ---------------------------------------------------------------------------
+ * Nested (double-quantized) absmax for the codebook format ([P3] "Testing plan":
+ * nested and non-nested absmax).  Block i (flat index n * nblk + b) stores an 8-bit
+ * code into a 256-entry fp32 table; `group` consecutive blocks share one fp32 scale,
+ * and one fp32 offset is added back:
+ *   absmax_i = fp32(fp32(table[codes[i]] * scales[i / group]) + offset)
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  const uint8_t* codes;  /* uint8 [N][nblk] (device)                          */
+  const float* table;    /* fp32 [256] (device)                               */
+  const float* scales;   /* fp32 [ceil(N * nblk / group)] (device)            */
+  float offset;
+  int group;             /* blocks per scale, >= 1 (bitsandbytes uses 256)    */
+} qmm_nested_absmax;
+
+/* out[i] = absmax_i for i < count (fp32, device); `absmax` is a HOST pointer to the
+ * descriptor.  Bit-exact with the definition above. */
+qmm_status qmm_dequantize_absmax_nested(const qmm_nested_absmax* absmax, int64_t count, float* out,
+                                        void* stream);
+
+/* qmm_codebook4 with nested absmax: the absmax of the N * nblk blocks is decoded once
+ * into the workspace (one small launch), then qmm_codebook4 runs on it, so results
+ * are those of qmm_codebook4 on the decoded values.  workspace: at least
+ * qmm_codebook4_nested_workspace_bytes(M, K, N, a_type, block) bytes, 256-byte
+ * aligned (the decoded absmax first, then qmm_codebook4's workspace). */
+qmm_status qmm_codebook4_nested(const void* A, int a_type, int64_t M, int64_t K, int64_t N,
+                                const uint8_t* W, int block, const qmm_nested_absmax* absmax,
+                                const float* codebook, const void* bias, void* C, int c_type,
+                                void* workspace, size_t workspace_bytes, void* stream);
+size_t qmm_codebook4_nested_workspace_bytes(int64_t M, int64_t K, int64_t N, int a_type, int block);
+
+/* ---------------------------------------------------------------------------
  * qmm_fp16_uniform_value -- is every fp16 zero point bitwise equal?
  *                                     ([P1] "What", commit 1: detected once per buffer)
  *   zp       fp16 [count] (device).

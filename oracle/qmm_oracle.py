@@ -189,6 +189,23 @@ def dequant_nbits(W, bits, K, block, scales_f16, zp=None, zp_kind=ZP_NONE,
     return to_f32(d * s[:, blk])
 
 
+def nested_absmax(codes, table, scales, offset, group: int) -> np.ndarray:
+    """Per-block absmax stored double-quantized ([P3] "Testing plan": nested absmax):
+    block i (the flat index n * nblk + b) has an 8-bit code c_i into a 256-entry fp32
+    table, one fp32 scale per `group` consecutive blocks, and one fp32 offset:
+
+        absmax_i = fp32(fp32(table[c_i] * scales[i // group]) + offset)
+
+    (each operation one fp32 rounding of its exact result).  Returns fp32 with the
+    shape of `codes`."""
+    c = np.asarray(codes, dtype=np.uint8)
+    t = np.asarray(table, dtype=np.float32).astype(np.float64)
+    sc = np.asarray(scales, dtype=np.float32).astype(np.float64)
+    i = np.arange(c.size).reshape(c.shape)
+    prod = to_f32(t[c] * sc[i // group]).astype(np.float64)
+    return to_f32(prod + float(np.float32(offset)))
+
+
 def dequant_codebook4(W, K, block, absmax, codebook) -> np.ndarray:
     """Dequantized fp32 weights [N, K]: w = fp32(codebook[q] * absmax[n, block])."""
     q = unpack_codes(W, 4, K, block)

@@ -691,8 +691,35 @@ def pin_ragged_mm(O, seed=53):
     assert np.allclose(y1, want, rtol=1e-13, atol=1e-13)
 
 
+def pin_nested_absmax(O, seed=59):
+    """Double-quantized absmax vs exact rationals; a table and scales that make every
+    step exact give the plain values; with the offset 0 and scale 1 the table itself."""
+    rng = np.random.default_rng(seed)
+    na = gen.nested_absmax_inputs(rng, 5, 70, group=64)
+    got = O.nested_absmax(na["codes"], na["table"], na["scales"], na["offset"], 64)
+    flat = na["codes"].ravel()
+    for i in range(flat.size):
+        prod = fr_round(fr32(na["table"][flat[i]]) * fr32(na["scales"][i // 64]), 24, -126)
+        want = fr_round(prod + fr32(na["offset"]), 24, -126)
+        assert Fr(float(got.ravel()[i])) == want, i
+    ident = O.nested_absmax(np.arange(256, dtype=np.uint8).reshape(4, 64), na["table"],
+                            np.ones(4, dtype=np.float32), 0.0, 64)
+    assert np.array_equal(ident.ravel().view(np.uint32), na["table"].view(np.uint32))
+    # the codebook matmul on decoded absmax equals the one on the same fp32 values
+    p = gen.codebook_problem(2, 200, 5, seed=seed, a_dtype="f32", block=64)
+    nb = gen.nested_absmax_inputs(rng, 5, 4, group=8)
+    am = O.nested_absmax(nb["codes"], nb["table"], nb["scales"], nb["offset"], 8)
+    y = O.qmm_codebook4(p["A"], "f32", p["W"], 200, 64, am, p["codebook"])
+    q = bitstring_codes(p["W"], 4, 200, 64)
+    for m in range(2):
+        for n in range(5):
+            acc = sum(fr32(p["A"][m, k]) * fr_round(fr32(p["codebook"][q[n, k]]) * fr32(am[n, k // 64]), 24, -126)
+                      for k in range(200))
+            assert abs(float(Fr(float(y[m, n])) - acc)) < 1e-12, (m, n)
+
+
 ALL_PINS = [pin_unpack_exhaustive, pin_nbits_bruteforce, pin_nbits_closed_forms,
             pin_codebook_bruteforce, pin_codebook_linear_equals_affine, pin_fake_quant_chain,
             pin_bf16_rounding, pin_f16_rounding, pin_swiglu, pin_int8_quantizer, pin_uniform_zp,
             pin_qmoe_bruteforce, pin_qmoe_composition, pin_round_operand, pin_rel_l2, pin_quantized_ops,
-            pin_ragged_mm]
+            pin_ragged_mm, pin_nested_absmax]

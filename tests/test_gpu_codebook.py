@@ -189,3 +189,39 @@ def test_codebook_matrix_core_ragged(M, K, N, block, a_dtype):
     p = gen.codebook_problem(M, K, N, seed=57 + M, a_dtype=a_dtype, block=block, bias=True)
     d = CbDev(p)
     d.check(d.run(), label=f"M={M} K={K} N={N}")
+
+
+# --- nested (double-quantized) absmax ----------------------------------------------
+
+def _nested_dev(na):
+    t = torch()
+    return {"codes": dev(na["codes"]), "table": dev(na["table"]), "scales": dev(na["scales"]),
+            "offset": float(na["offset"]), "group": na["group"]}
+
+
+@pytest.mark.parametrize("group", [256, 64, 1])
+def test_nested_absmax_decode_bit_exact(group):
+    rng = np.random.default_rng(700 + group)
+    na = gen.nested_absmax_inputs(rng, 4096, 64, group=group)
+    got = Q.qmm_dequantize_absmax_nested(_nested_dev(na), 4096 * 64)
+    want = O.nested_absmax(na["codes"], na["table"], na["scales"], na["offset"], group)
+    assert np.array_equal(host_bits(got).view(np.uint32), want.ravel().view(np.uint32))
+
+
+@pytest.mark.parametrize("M", [1, 4, 16, 64])
+@pytest.mark.parametrize("name", ["square", "moe_down"])
+def test_codebook_nested_absmax(name, M):
+    """The codebook matmul with nested absmax equals, bit for bit, the plain entry on the
+    decoded absmax, and the oracle on the oracle's decoded absmax within the gate."""
+    K, N = gen.CODEBOOK_SHAPES[name]
+    say(f"codebook nested {name} M={M}")
+    p = gen.codebook_problem(M, K, N, seed=710 + M, a_dtype="bf16")
+    rng = np.random.default_rng(711 + M)
+    na = gen.nested_absmax_inputs(rng, N, K // 64)
+    am = O.nested_absmax(na["codes"], na["table"], na["scales"], na["offset"], na["group"])
+    p["absmax"] = am
+    d = CbDev(p)
+    y = Q.qmm_codebook4_nested(d.A, d.W, _nested_dev(na), d.cb, K, 64)
+    plain = d.run()
+    assert np.array_equal(host_bits(y), host_bits(plain))
+    d.check(y, label=f"nested {name} M={M}")
