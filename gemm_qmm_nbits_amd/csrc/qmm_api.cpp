@@ -1342,6 +1342,73 @@ int qmm_tuner_pick(const double* times_us, int rounds, int ncand) {
   return pick_winner(times_us, rounds, ncand);
 }
 
+qmm_status qmm_hbm_read_probe(const void* buf, int64_t bytes, uint32_t* sink, int groups, void* stream) {
+  (void)hipGetLastError();
+  if (bytes < 0 || bytes % 16 != 0 || groups < 1 || groups > (1 << 20)) return QMM_E_SHAPE;
+  if (bytes == 0) return QMM_OK;
+  if (!buf || !sink) return QMM_E_NULL;
+  if (!aligned(buf, 16) || !aligned(sink, 4)) return QMM_E_ALIGN;
+  const hipError_t e = launch_hbm_read(buf, bytes, sink, groups, (hipStream_t)stream);
+  if (e != hipSuccess) return (qmm_status)e;
+  return (qmm_status)hipGetLastError();
+}
+
+qmm_status qmm_launch_timing_begin(int n) {
+  LaunchTiming& t = g_launch_timing;
+  if (t.on) return QMM_E_MODE;
+  if (n < 1 || n > 65536) return QMM_E_SHAPE;
+  t.start = new hipEvent_t[n];
+  t.stop = new hipEvent_t[n];
+  int made = 0;
+  hipError_t e = hipSuccess;
+  for (; made < n; ++made) {
+    if ((e = hipEventCreate(&t.start[made])) != hipSuccess) break;
+    if ((e = hipEventCreate(&t.stop[made])) != hipSuccess) {
+      (void)hipEventDestroy(t.start[made]);
+      break;
+    }
+  }
+  if (e != hipSuccess) {
+    for (int i = 0; i < made; ++i) {
+      (void)hipEventDestroy(t.start[i]);
+      (void)hipEventDestroy(t.stop[i]);
+    }
+    delete[] t.start;
+    delete[] t.stop;
+    t = LaunchTiming{};
+    return (qmm_status)e;
+  }
+  t.cap = n;
+  t.next = 0;
+  t.on = 1;
+  return QMM_OK;
+}
+
+qmm_status qmm_launch_timing_end(float* us, int n_max, int* count) {
+  LaunchTiming& t = g_launch_timing;
+  if (!count) return QMM_E_NULL;
+  *count = 0;
+  if (!t.on) return QMM_OK;
+  hipError_t first = hipSuccess;
+  const int used = t.next;
+  for (int i = 0; i < used; ++i) {
+    float ms = 0.0f;
+    hipError_t e = hipEventSynchronize(t.stop[i]);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, t.start[i], t.stop[i]);
+    if (e != hipSuccess && first == hipSuccess) first = e;
+    if (us && i < n_max) us[i] = ms * 1000.0f;
+  }
+  for (int i = 0; i < t.cap; ++i) {
+    (void)hipEventDestroy(t.start[i]);
+    (void)hipEventDestroy(t.stop[i]);
+  }
+  delete[] t.start;
+  delete[] t.stop;
+  t = LaunchTiming{};
+  *count = used;
+  return (qmm_status)first;
+}
+
 const char* qmm_status_string(qmm_status s) {
   switch (s) {
     case QMM_OK: return "ok";

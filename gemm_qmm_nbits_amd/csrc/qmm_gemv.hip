@@ -161,7 +161,7 @@ void gemv_plan(GemvArgs& g, int num_cus) {
 hipError_t launch_gemv(GemvArgs g, int rows_per_lane, hipStream_t st) {
   if (!g.chunked) {
     const dim3 grid((unsigned)((g.N + 3) / 4));
-    hipLaunchKernelGGL(gemv_generic_kernel, grid, dim3(256), 0, st, g);
+    launch(gemv_generic_kernel, grid, dim3(256), 0, st, g);
     return hipSuccess;
   }
   if (g.fmt == GEMV_CODEBOOK) return launch_codebook(g, rows_per_lane, st);

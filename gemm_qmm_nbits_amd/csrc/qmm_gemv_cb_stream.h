@@ -270,7 +270,7 @@ static hipError_t launch_cb_stream(const GemvArgs& g, hipStream_t st) {
   }
   if (lds + kCbStaticLds > kMaxGemvLds) return hipErrorNotSupported;
   allow_cb_lds(kern, lds);
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(stream_threads(MT, R)), lds, st, g);
+  launch(kern, dim3((unsigned)grid), dim3(stream_threads(MT, R)), lds, st, g);
   return hipSuccess;
 }
 

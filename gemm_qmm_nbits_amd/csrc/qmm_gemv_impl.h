@@ -519,7 +519,7 @@ static hipError_t launch_one(const GemvArgs& g, hipStream_t st) {
   const size_t lds = g.lds_bytes + kGemvOutFloats * sizeof(float);
   auto kern = gemv_kernel<FMT, BITS, AT, MT, R, MULTI, ZK>;
   allow_large_lds(kern, lds);
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kGemvThreads), lds, st, g);
+  launch(kern, dim3((unsigned)grid), dim3(kGemvThreads), lds, st, g);
   return hipSuccess;
 }
 

@@ -295,7 +295,7 @@ static hipError_t launch_ip_stream(const GemvArgs& g, hipStream_t st) {
   }
   if (lds > kMaxGemvLds) return hipErrorNotSupported;
   allow_large_lds(kern, lds);
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(stream_threads(MT, R)), lds, st, g);
+  launch(kern, dim3((unsigned)grid), dim3(stream_threads(MT, R)), lds, st, g);
   return hipSuccess;
 }
 
@@ -313,7 +313,7 @@ static hipError_t launch_ip_one(const GemvArgs& g, hipStream_t st) {
   const size_t lds = g.lds_bytes + kGemvOutFloats * sizeof(float);
   auto kern = gemv_ip_kernel<BITS, AT, MT, R, DPG, ZK>;
   allow_large_lds(kern, lds);
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kGemvThreads), lds, st, g);
+  launch(kern, dim3((unsigned)grid), dim3(kGemvThreads), lds, st, g);
   return hipSuccess;
 }
 

@@ -1,12 +1,39 @@
 // Internal interfaces between the host runtime (qmm_api.cpp) and the kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "qmm.h"
 
 namespace qmm {
+
+// Launch timing, a measurement aid: while the calling host thread has it switched on
+// (qmm_launch_timing_begin), each kernel the library launches from that thread records
+// the start and the end of its execution on the device into the next pair of a fixed
+// set of HIP events; launches past the set, and every launch while it is off, go out
+// as plain launches.
+struct LaunchTiming {
+  int on = 0;
+  int next = 0;
+  int cap = 0;
+  hipEvent_t* start = nullptr;
+  hipEvent_t* stop = nullptr;
+};
+inline thread_local LaunchTiming g_launch_timing;
+
+// Every kernel launch of the library goes through here.
+template <typename F, typename... Args>
+inline void launch(F kernel, dim3 grid, dim3 block, uint32_t lds, hipStream_t st, Args... args) {
+  LaunchTiming& t = g_launch_timing;
+  if (t.on && t.next < t.cap) {
+    const int i = t.next++;
+    hipExtLaunchKernelGGL(kernel, grid, block, lds, st, t.start[i], t.stop[i], 0u, args...);
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, lds, st, args...);
+  }
+}
 
 enum { GEMV_AFFINE = 0, GEMV_CODEBOOK = 1 };
 
@@ -111,6 +138,9 @@ struct PrefillArgs {
 };
 hipError_t launch_prefill(PrefillArgs p, hipStream_t st);
 int prefill_splits(int64_t M, int64_t N, int64_t Kp);
+
+// Streaming read of `bytes` (a multiple of 16) by `groups` work-groups (qmm_probe.hip).
+hipError_t launch_hbm_read(const void* buf, int64_t bytes, uint32_t* sink, int groups, hipStream_t st);
 
 // Activation quantization ops (qmm_qdq.hip); arguments checked by the caller.
 using QdqParams = qmm_qparams;

@@ -36,7 +36,7 @@ hipError_t launch_dequant(const DequantArgs& d, hipStream_t st) {
   int64_t blocks = (total + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL(dequant_kernel, dim3((unsigned)blocks), dim3(256), 0, st, d);
+  launch(dequant_kernel, dim3((unsigned)blocks), dim3(256), 0, st, d);
   return hipSuccess;
 }
 
@@ -58,7 +58,7 @@ hipError_t launch_nested_absmax(const uint8_t* codes, const float* table, const 
   int64_t blocks = (count + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL(nested_absmax_kernel, dim3((unsigned)blocks), dim3(256), 0, st, codes, table, scales, offset,
+  launch(nested_absmax_kernel, dim3((unsigned)blocks), dim3(256), 0, st, codes, table, scales, offset,
                      group, count, out);
   return hipSuccess;
 }
@@ -94,9 +94,9 @@ __global__ __launch_bounds__(256) void uniform_final_kernel(const uint16_t* zp, 
 
 hipError_t launch_uniform_check(const uint16_t* zp, int64_t count, uint32_t* scratch,
                                 hipStream_t st) {
-  hipLaunchKernelGGL(uniform_partial_kernel, dim3(kUniformPartials), dim3(256), 0, st, zp, count,
+  launch(uniform_partial_kernel, dim3(kUniformPartials), dim3(256), 0, st, zp, count,
                      scratch + 2);
-  hipLaunchKernelGGL(uniform_final_kernel, dim3(1), dim3(256), 0, st, zp, scratch + 2, scratch);
+  launch(uniform_final_kernel, dim3(1), dim3(256), 0, st, zp, scratch + 2, scratch);
   return hipSuccess;
 }
 
@@ -224,10 +224,10 @@ template <int AT, bool VEC>
 static void launch_cast_rows(const void* src, int64_t M, int64_t K, int64_t Kp, uint16_t* dst, float* rs,
                              hipStream_t st) {
   if (Kp <= (int64_t)kCastThreads * 8 * kCastPieces)
-    hipLaunchKernelGGL((cast_rows_f16_kernel<AT, VEC, true>), dim3((unsigned)M), dim3(kCastThreads), 0, st, src,
+    launch((cast_rows_f16_kernel<AT, VEC, true>), dim3((unsigned)M), dim3(kCastThreads), 0, st, src,
                        M, K, Kp, dst, rs);
   else
-    hipLaunchKernelGGL((cast_rows_f16_kernel<AT, VEC, false>), dim3((unsigned)M), dim3(kCastThreads), 0, st, src,
+    launch((cast_rows_f16_kernel<AT, VEC, false>), dim3((unsigned)M), dim3(kCastThreads), 0, st, src,
                        M, K, Kp, dst, rs);
 }
 

@@ -381,7 +381,7 @@ __global__ __launch_bounds__(256) void reduce_splits_kernel(const float* P, int 
 
 template <int FMT, int BITS, int ZK, int CT>
 void launch_one(const PrefillArgs& p, dim3 grid, hipStream_t st) {
-  hipLaunchKernelGGL((prefill_kernel<FMT, BITS, ZK, CT>), grid, dim3(NT), 0, st, p);
+  launch((prefill_kernel<FMT, BITS, ZK, CT>), grid, dim3(NT), 0, st, p);
 }
 
 template <int FMT, int BITS, int ZK>
@@ -399,11 +399,11 @@ hipError_t launch_reduce_splits(const float* P, int S, int64_t M, int64_t N, int
   if (blocks > 16384) blocks = 16384;
   if (blocks < 1) blocks = 1;
   if (c_type == QMM_F32)
-    hipLaunchKernelGGL(reduce_splits_kernel<QMM_F32>, dim3((unsigned)blocks), dim3(256), 0, st, P, S, M, N, ldc, rs, bias, C);
+    launch(reduce_splits_kernel<QMM_F32>, dim3((unsigned)blocks), dim3(256), 0, st, P, S, M, N, ldc, rs, bias, C);
   else if (c_type == QMM_F16)
-    hipLaunchKernelGGL(reduce_splits_kernel<QMM_F16>, dim3((unsigned)blocks), dim3(256), 0, st, P, S, M, N, ldc, rs, bias, C);
+    launch(reduce_splits_kernel<QMM_F16>, dim3((unsigned)blocks), dim3(256), 0, st, P, S, M, N, ldc, rs, bias, C);
   else
-    hipLaunchKernelGGL(reduce_splits_kernel<QMM_BF16>, dim3((unsigned)blocks), dim3(256), 0, st, P, S, M, N, ldc, rs, bias, C);
+    launch(reduce_splits_kernel<QMM_BF16>, dim3((unsigned)blocks), dim3(256), 0, st, P, S, M, N, ldc, rs, bias, C);
   return hipSuccess;
 }
 

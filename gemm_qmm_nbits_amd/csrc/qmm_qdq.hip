@@ -148,14 +148,14 @@ QP qp_of(const QdqParams& p, int bits) { return QP{p.scale, (float)p.zero_point,
 
 template <int XT>
 void q_at(const void* x, int64_t n, QP q, int bits, void* codes, hipStream_t st_) {
-  if (bits == 8) hipLaunchKernelGGL((quantize_kernel<XT, 8>), qdq_grid(n), dim3(kQdqThreads), 0, st_, x, n, q, codes);
-  else hipLaunchKernelGGL((quantize_kernel<XT, 16>), qdq_grid(n), dim3(kQdqThreads), 0, st_, x, n, q, codes);
+  if (bits == 8) launch((quantize_kernel<XT, 8>), qdq_grid(n), dim3(kQdqThreads), 0, st_, x, n, q, codes);
+  else launch((quantize_kernel<XT, 16>), qdq_grid(n), dim3(kQdqThreads), 0, st_, x, n, q, codes);
 }
 
 template <int YT>
 void dq_at(const void* codes, int64_t n, QP q, int bits, void* y, hipStream_t st_) {
-  if (bits == 8) hipLaunchKernelGGL((dequantize_kernel<8, YT>), qdq_grid(n), dim3(kQdqThreads), 0, st_, codes, n, q, y);
-  else hipLaunchKernelGGL((dequantize_kernel<16, YT>), qdq_grid(n), dim3(kQdqThreads), 0, st_, codes, n, q, y);
+  if (bits == 8) launch((dequantize_kernel<8, YT>), qdq_grid(n), dim3(kQdqThreads), 0, st_, codes, n, q, y);
+  else launch((dequantize_kernel<16, YT>), qdq_grid(n), dim3(kQdqThreads), 0, st_, codes, n, q, y);
 }
 
 template <int XT>
@@ -163,9 +163,9 @@ void swiglu_at(const void* gate, const void* up, int64_t n, int bits, const QdqP
   const QP a = qp_of(p[0], bits), b = qp_of(p[1], bits), c = qp_of(p[2], bits), d = qp_of(p[3], bits),
            e = qp_of(p[4], bits);
   if (bits == 8)
-    hipLaunchKernelGGL((qswiglu_kernel<XT, 8>), qdq_grid(n), dim3(kQdqThreads), 0, st_, gate, up, n, a, b, c, d, e, y);
+    launch((qswiglu_kernel<XT, 8>), qdq_grid(n), dim3(kQdqThreads), 0, st_, gate, up, n, a, b, c, d, e, y);
   else
-    hipLaunchKernelGGL((qswiglu_kernel<XT, 16>), qdq_grid(n), dim3(kQdqThreads), 0, st_, gate, up, n, a, b, c, d, e, y);
+    launch((qswiglu_kernel<XT, 16>), qdq_grid(n), dim3(kQdqThreads), 0, st_, gate, up, n, a, b, c, d, e, y);
 }
 
 }  // namespace
@@ -192,19 +192,19 @@ hipError_t launch_fake_quantize(const void* x, int x_type, int64_t n, QdqParams 
                                 hipStream_t st_) {
   const QP p = qp_of(q, bits);
   if (x_type == QMM_F32)
-    hipLaunchKernelGGL((fake_quantize_kernel<QMM_F32>), qdq_grid(n), dim3(kQdqThreads), 0, st_, x, n, p, y);
+    launch((fake_quantize_kernel<QMM_F32>), qdq_grid(n), dim3(kQdqThreads), 0, st_, x, n, p, y);
   else if (x_type == QMM_F16)
-    hipLaunchKernelGGL((fake_quantize_kernel<QMM_F16>), qdq_grid(n), dim3(kQdqThreads), 0, st_, x, n, p, y);
+    launch((fake_quantize_kernel<QMM_F16>), qdq_grid(n), dim3(kQdqThreads), 0, st_, x, n, p, y);
   else
-    hipLaunchKernelGGL((fake_quantize_kernel<QMM_BF16>), qdq_grid(n), dim3(kQdqThreads), 0, st_, x, n, p, y);
+    launch((fake_quantize_kernel<QMM_BF16>), qdq_grid(n), dim3(kQdqThreads), 0, st_, x, n, p, y);
   return hipSuccess;
 }
 
 hipError_t launch_qsigmoid(const void* in, int64_t n, QdqParams qi, QdqParams qo, int bits, void* out,
                            hipStream_t st_) {
   const QP a = qp_of(qi, bits), b = qp_of(qo, bits);
-  if (bits == 8) hipLaunchKernelGGL((qsigmoid_kernel<8>), qdq_grid(n), dim3(kQdqThreads), 0, st_, in, n, a, b, out);
-  else hipLaunchKernelGGL((qsigmoid_kernel<16>), qdq_grid(n), dim3(kQdqThreads), 0, st_, in, n, a, b, out);
+  if (bits == 8) launch((qsigmoid_kernel<8>), qdq_grid(n), dim3(kQdqThreads), 0, st_, in, n, a, b, out);
+  else launch((qsigmoid_kernel<16>), qdq_grid(n), dim3(kQdqThreads), 0, st_, in, n, a, b, out);
   return hipSuccess;
 }
 
@@ -212,9 +212,9 @@ hipError_t launch_qmul(const void* a, QdqParams qa, const void* b, QdqParams qb,
                        void* c, hipStream_t st_) {
   const QP pa = qp_of(qa, bits), pb = qp_of(qb, bits), pc = qp_of(qc, bits);
   if (bits == 8)
-    hipLaunchKernelGGL((qmul_kernel<8>), qdq_grid(n), dim3(kQdqThreads), 0, st_, a, pa, b, pb, n, pc, c);
+    launch((qmul_kernel<8>), qdq_grid(n), dim3(kQdqThreads), 0, st_, a, pa, b, pb, n, pc, c);
   else
-    hipLaunchKernelGGL((qmul_kernel<16>), qdq_grid(n), dim3(kQdqThreads), 0, st_, a, pa, b, pb, n, pc, c);
+    launch((qmul_kernel<16>), qdq_grid(n), dim3(kQdqThreads), 0, st_, a, pa, b, pb, n, pc, c);
   return hipSuccess;
 }
 

@@ -1454,7 +1454,7 @@ static bool launch_fc1_stream(const QmoeArgs& a, int cap, hipStream_t st) {
   if (!moe_stream_plan(kern, ngroups, fixed, (size_t)rpg * 2 * sizeof(float), a.num_cus, cap, &grid, &lds))
     return false;
   allow_lds(kern, lds);
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kMoeStreamThreads), lds, st, a);
+  launch(kern, dim3((unsigned)grid), dim3(kMoeStreamThreads), lds, st, a);
   return true;
 }
 
@@ -1471,7 +1471,7 @@ static bool launch_fc2_stream(const QmoeArgs& a, int cap, hipStream_t st) {
   if (!moe_stream_plan(kern, ngroups, fixed, (size_t)rpg * a.k * sizeof(float), a.num_cus, cap, &grid, &lds))
     return false;
   allow_lds(kern, lds);
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kMoeStreamThreads), lds, st, a);
+  launch(kern, dim3((unsigned)grid), dim3(kMoeStreamThreads), lds, st, a);
   return true;
 }
 
@@ -1506,7 +1506,7 @@ static bool launch_fused(const QmoeArgs& a, hipStream_t st) {
   }
   if (per_cu < 1) return false;
   allow_lds(kern, lds);
-  hipLaunchKernelGGL(kern, dim3((unsigned)(cus * per_cu)), dim3(kMoeStreamThreads), lds, st, a);
+  launch(kern, dim3((unsigned)(cus * per_cu)), dim3(kMoeStreamThreads), lds, st, a);
   return true;
 }
 
@@ -1527,7 +1527,7 @@ static bool launch_fc1_dedupe(const QmoeArgs& a, hipStream_t st) {
                        &grid, &lds))
     return false;
   allow_lds(kern, lds);
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kMoeStreamThreads), lds, st, a);
+  launch(kern, dim3((unsigned)grid), dim3(kMoeStreamThreads), lds, st, a);
   return true;
 }
 
@@ -1586,13 +1586,13 @@ hipError_t launch_qmoe_fc1(const QmoeArgs& a, int candidate, hipStream_t st) {
   const dim3 grid((unsigned)((a.I + rows_per_wg - 1) / rows_per_wg), (unsigned)(a.T * a.k));
   const size_t lds = qmoe_fc1_lds_bytes(a);
   if (a.mode == QMOE_INT8_ACT) {
-    if (rows_per_lane == 1) hipLaunchKernelGGL((qmoe_fc1_kernel<1, 1>), grid, dim3(256), lds, st, a);
-    else hipLaunchKernelGGL((qmoe_fc1_kernel<1, 2>), grid, dim3(256), lds, st, a);
+    if (rows_per_lane == 1) launch((qmoe_fc1_kernel<1, 1>), grid, dim3(256), lds, st, a);
+    else launch((qmoe_fc1_kernel<1, 2>), grid, dim3(256), lds, st, a);
   } else {
     allow_lds(qmoe_fc1_kernel<0, 1>, lds);
     allow_lds(qmoe_fc1_kernel<0, 2>, lds);
-    if (rows_per_lane == 1) hipLaunchKernelGGL((qmoe_fc1_kernel<0, 1>), grid, dim3(256), lds, st, a);
-    else hipLaunchKernelGGL((qmoe_fc1_kernel<0, 2>), grid, dim3(256), lds, st, a);
+    if (rows_per_lane == 1) launch((qmoe_fc1_kernel<0, 1>), grid, dim3(256), lds, st, a);
+    else launch((qmoe_fc1_kernel<0, 2>), grid, dim3(256), lds, st, a);
   }
   return hipSuccess;
 }
@@ -1603,7 +1603,7 @@ hipError_t launch_qmoe_fc2(const QmoeArgs& a, int candidate, hipStream_t st) {
     // h -> int8 codes and scales once (into the scratch fc2 stages from)
     const int64_t groups = a.T * a.k * a.I / 32;
     const int64_t blocks = (groups + 7) / 8;
-    hipLaunchKernelGGL(qmoe_quant_h_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a.h, groups, a.hq_out,
+    launch(qmoe_quant_h_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a.h, groups, a.hq_out,
                        a.hs_out);
   }
   if (!(candidate & kQmoePerSlot)) {
@@ -1624,13 +1624,13 @@ hipError_t launch_qmoe_fc2(const QmoeArgs& a, int candidate, hipStream_t st) {
   const dim3 grid((unsigned)((a.H + rows_per_wg - 1) / rows_per_wg), (unsigned)a.T);
   const size_t lds = qmoe_fc2_lds_bytes(a);
   if (a.mode == QMOE_INT8_ACT) {
-    if (rows_per_lane == 1) hipLaunchKernelGGL((qmoe_fc2_kernel<1, 1>), grid, dim3(256), lds, st, a);
-    else hipLaunchKernelGGL((qmoe_fc2_kernel<1, 2>), grid, dim3(256), lds, st, a);
+    if (rows_per_lane == 1) launch((qmoe_fc2_kernel<1, 1>), grid, dim3(256), lds, st, a);
+    else launch((qmoe_fc2_kernel<1, 2>), grid, dim3(256), lds, st, a);
   } else {
     allow_lds(qmoe_fc2_kernel<0, 1>, lds);
     allow_lds(qmoe_fc2_kernel<0, 2>, lds);
-    if (rows_per_lane == 1) hipLaunchKernelGGL((qmoe_fc2_kernel<0, 1>), grid, dim3(256), lds, st, a);
-    else hipLaunchKernelGGL((qmoe_fc2_kernel<0, 2>), grid, dim3(256), lds, st, a);
+    if (rows_per_lane == 1) launch((qmoe_fc2_kernel<0, 1>), grid, dim3(256), lds, st, a);
+    else launch((qmoe_fc2_kernel<0, 2>), grid, dim3(256), lds, st, a);
   }
   return hipSuccess;
 }

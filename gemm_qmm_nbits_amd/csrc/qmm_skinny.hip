@@ -284,7 +284,7 @@ void sk_launch(const PrefillArgs& p, hipStream_t st) {
   const size_t lds = (size_t)SK_WAVES * MB * SK_NS * 4 * 64 * sizeof(float);
   if (lds > 64 * 1024) (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   const unsigned grid = (unsigned)((p.N + SK_NS * 16 - 1) / (SK_NS * 16));
-  hipLaunchKernelGGL(kern, dim3(grid, (unsigned)p.splits), dim3(SK_THREADS), lds, st, p);
+  launch(kern, dim3(grid, (unsigned)p.splits), dim3(SK_THREADS), lds, st, p);
 }
 
 template <int FMT, int BITS, int ZK, int CT>
@@ -503,7 +503,7 @@ void ragged_launch(const RaggedArgs& p, hipStream_t st) {
   const unsigned gx = (unsigned)((p.N + NS * 16 - 1) / (NS * 16));
   // every expert's tiles, at most ceil(R / rows) + E slots
   const unsigned gy = (unsigned)((p.R + 16 * MB - 1) / (16 * MB) + p.E);
-  hipLaunchKernelGGL(kern, dim3(gx, gy), dim3(SK_THREADS), lds, st, p);
+  launch(kern, dim3(gx, gy), dim3(SK_THREADS), lds, st, p);
 }
 
 template <int ZK>

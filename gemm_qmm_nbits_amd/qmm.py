@@ -94,6 +94,9 @@ _SIGS = {
                          c_void_p, c_void_p]),
     "qmm_qswiglu": (c_int, [c_void_p, c_void_p, c_int, c_int64, c_int, POINTER(qmm_qparams), c_void_p,
                             c_void_p]),
+    "qmm_hbm_read_probe": (c_int, [c_void_p, c_int64, c_void_p, c_int, c_void_p]),
+    "qmm_launch_timing_begin": (c_int, [c_int]),
+    "qmm_launch_timing_end": (c_int, [c_void_p, c_int, c_void_p]),
     "qmm_set_tuning": (c_int, [c_int, c_int]),
     "qmm_num_candidates": (c_int, [c_int]),
     "qmm_tuned_choice": (c_int, [c_int]),
@@ -440,6 +443,25 @@ def qswiglu(gate, up, qparams, bits, out=None, stream=None):
     _check("qmm_qswiglu", lib().qmm_qswiglu(_ptr(gate), _ptr(up), dtype_code(gate), gate.numel(), bits, arr,
                                             _ptr(out), _stream(stream)))
     return out
+
+
+def hbm_read_probe(buf, sink, groups, stream=None):
+    """Read every byte of `buf` once with 128-bit loads (measurement helper)."""
+    _check("qmm_hbm_read_probe", lib().qmm_hbm_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                                          groups, _stream(stream)))
+
+
+def launch_timing_begin(n: int):
+    """Time the next n kernel launches the library makes from this thread."""
+    _check("qmm_launch_timing_begin", lib().qmm_launch_timing_begin(n))
+
+
+def launch_timing_end(n_max: int = 65536):
+    """Stop launch timing; the execution time in us of each timed launch, in order."""
+    buf = (c_float * n_max)()
+    count = c_int(0)
+    _check("qmm_launch_timing_end", lib().qmm_launch_timing_end(buf, n_max, ctypes.byref(count)))
+    return [float(buf[i]) for i in range(min(count.value, n_max))]
 
 
 def set_tuning(mode: int, forced_index: int = 0):

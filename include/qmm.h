@@ -397,6 +397,29 @@ void qmm_clear_tuning(void);
  * Returns -1 for bad arguments. */
 int qmm_tuner_pick(const double* times_us, int rounds, int ncand);
 
+/* ---------------------------------------------------------------------------
+ * Measurement helper (not part of the computation): reads `bytes` of device memory
+ * (16-byte aligned, a multiple of 16) once with 128-bit loads, `groups` work-groups of
+ * 256 threads each reading one contiguous range, and writes the xor of what each
+ * work-group read to sink[group] (uint32 [groups], device).  Timing it gives the HBM
+ * read rate a plain streaming kernel reaches, the practical ceiling of the weight-
+ * streaming kernels.  groups in [1, 2^20].
+ * ------------------------------------------------------------------------- */
+qmm_status qmm_hbm_read_probe(const void* buf, int64_t bytes, uint32_t* sink, int groups, void* stream);
+
+/* Measurement helpers (not part of the computation): kernel execution times.
+ * qmm_launch_timing_begin(n): from now on, the first n kernel launches that the library
+ * makes from the calling host thread each record the start and the end of their execution
+ * on the device (hipExtLaunchKernel with a pair of HIP events, created here on the current
+ * device); the launches themselves are unchanged.  n in [1, 65536]; QMM_E_MODE if timing
+ * is already on for this thread.  Do not switch it on around stream capture.
+ * qmm_launch_timing_end(us, n_max, count): switches it off, waits for the recorded
+ * launches, writes the duration in microseconds of each (launch order) to us[0..] (HOST
+ * array, at most n_max values), the number of timed launches to *count (HOST), and frees
+ * the events.  With timing off it writes *count = 0. */
+qmm_status qmm_launch_timing_begin(int n);
+qmm_status qmm_launch_timing_end(float* us, int n_max, int* count);
+
 /* Human-readable name of a status code (static storage). */
 const char* qmm_status_string(qmm_status s);
 

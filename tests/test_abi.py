@@ -213,3 +213,24 @@ def test_decode_status_refusals():
     # int8 mode never waits: 0 without touching the buffer
     assert L.qmoe_decode_status(None, 0, 1, 2880, 2880, 4, Q.QMOE_INT8_ACT, ctypes.byref(flag), None) == 0
     assert flag.value == 0
+
+
+def test_hbm_read_probe_refusals():
+    """Host-side refusals of the streaming-read measurement helper."""
+    L = Q.lib()
+    assert L.qmm_hbm_read_probe(FAKE, 100, FAKE, 16, None) == -5      # not a multiple of 16
+    assert L.qmm_hbm_read_probe(FAKE, 1 << 20, FAKE, 0, None) == -5
+    assert L.qmm_hbm_read_probe(FAKE, 1 << 20, FAKE, (1 << 20) + 1, None) == -5
+    assert L.qmm_hbm_read_probe(None, 1 << 20, FAKE, 16, None) == -1
+    assert L.qmm_hbm_read_probe(FAKE + 8, 1 << 20, FAKE, 16, None) == -6
+    assert L.qmm_hbm_read_probe(None, 0, None, 16, None) == 0
+
+
+def test_launch_timing_host_paths():
+    """Launch timing: refusals and the switched-off end (no GPU work)."""
+    L = Q.lib()
+    count = ctypes.c_int(5)
+    assert L.qmm_launch_timing_end(None, 0, ctypes.byref(count)) == 0 and count.value == 0
+    assert L.qmm_launch_timing_end(None, 0, None) == -1
+    assert L.qmm_launch_timing_begin(0) == -5
+    assert L.qmm_launch_timing_begin(65537) == -5
