@@ -793,6 +793,22 @@ def ceilings_leg(T):
     best = max(sweep, key=sweep.get)
     out["stream_read_128b"] = {"bytes": 4 << 30, "GBps_by_workgroups": sweep, "best_GBps": sweep[best],
                                "best_frac_hbm": round(sweep[best] / HBM_PEAK_GBS, 4)}
+    # the same read at the sizes of the decode layers and MoE calls: the fixed cost of a
+    # launch that streams a few MB, buffers rotated through the 4 GiB so every read is cold
+    by_size = {}
+    for mb in (2, 4, 11, 20, 26, 53, 145, 512):
+        nb = mb * 1000000 // 4096 * 4096
+        nbuf = (4 << 30) // nb
+        best = None
+        for groups in (256, 512, 1024, 2048, 4096):
+            views = [big[i * nb:(i + 1) * nb] for i in range(min(nbuf, 64))]
+            ku = T.kernel_us([lambda i=i: Q.hbm_read_probe(views[i % len(views)], sink, groups)
+                              for i in range(max(16, min(len(views), 64)))])
+            if best is None or ku["kernel_us"] < best[1]:
+                best = (groups, ku["kernel_us"])
+        by_size[mb] = {"workgroups": best[0], "kernel_us": round(best[1], 2),
+                       "GBps": round(nb / best[1] / 1e3, 1)}
+    out["stream_read_128b"]["by_size_MB"] = by_size
     del big
     torch.cuda.empty_cache()
     nbytes = int(weight_bytes_nbits(5120, 100352)) // 256 * 256

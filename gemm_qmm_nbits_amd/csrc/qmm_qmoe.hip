@@ -41,29 +41,39 @@ __device__ __forceinline__ void h8_to_f32(uint4 v, float* o) {
   }
 }
 
-// fp dot of one 16-byte chunk of u4 codes (32 codes) with 32 fp32 activations,
-// unscaled: sum a[i] * q[i].  Codes are decoded two at a time through the fp8
-// conversion (bytes 0..15 -> q * 2^-9), the factor 512 is applied by the caller.
-__device__ __forceinline__ float dot_chunk_u4(uint4 w, const float* a) {
+// Staged fp activations are fp16 pairs: each 8 values x0..x7 are held as the four
+// dwords (x0,x2) (x4,x6) (x1,x3) (x5,x7), the order in which the code decoding below
+// yields the codes (low nibbles give codes 0,2,4,6, high nibbles 1,3,5,7).
+__device__ __forceinline__ uint4 h8_pairs(uint4 v) {
+  const uint32_t p02 = __builtin_amdgcn_perm(v.y, v.x, 0x05040100u);
+  const uint32_t p46 = __builtin_amdgcn_perm(v.w, v.z, 0x05040100u);
+  const uint32_t p13 = __builtin_amdgcn_perm(v.y, v.x, 0x07060302u);
+  const uint32_t p57 = __builtin_amdgcn_perm(v.w, v.z, 0x07060302u);
+  return make_uint4(p02, p46, p13, p57);
+}
+
+// fp dot of one 16-byte chunk of u4 codes (32 codes) with its 32 staged activations
+// (16 dwords of fp16 pairs), unscaled: sum q[i] * a[i].  Each byte holding a code is
+// read as an fp8 E4M3 value (codes 0..15 are q * 2^-9) and converted to fp16 with the
+// scale 2^9, which gives q exactly; the pairs go through the fp16 dot into the fp32
+// sum (products of fp16 values are exact in fp32), in a fixed order.
+typedef _Float16 moe_h2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dot_chunk_u4(uint4 w, const uint32_t* a) {
   const uint32_t d[4] = {w.x, w.y, w.z, w.w};
   float s = 0.0f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint32_t lo = d[i] & 0x0f0f0f0fu;
-    const uint32_t hi = (d[i] >> 4) & 0x0f0f0f0fu;
-    const f32x2 l0 = __builtin_amdgcn_cvt_pk_f32_fp8(lo, false);
-    const f32x2 l1 = __builtin_amdgcn_cvt_pk_f32_fp8(lo, true);
-    const f32x2 h0 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
-    const f32x2 h1 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
-    const float* ai = a + 8 * i;
-    s = fmaf(ai[0], l0.x, s);
-    s = fmaf(ai[1], h0.x, s);
-    s = fmaf(ai[2], l0.y, s);
-    s = fmaf(ai[3], h0.y, s);
-    s = fmaf(ai[4], l1.x, s);
-    s = fmaf(ai[5], h1.x, s);
-    s = fmaf(ai[6], l1.y, s);
-    s = fmaf(ai[7], h1.y, s);
+    const uint32_t lo = d[i] & 0x0f0f0f0fu;         // codes 0,2,4,6 of these 8
+    const uint32_t hi = (d[i] >> 4) & 0x0f0f0f0fu;  // codes 1,3,5,7
+    const moe_h2 q02 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 512.0f, false);
+    const moe_h2 q46 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 512.0f, true);
+    const moe_h2 q13 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 512.0f, false);
+    const moe_h2 q57 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 512.0f, true);
+    const uint32_t* ai = a + 4 * i;
+    s = __builtin_amdgcn_fdot2(q02, __builtin_bit_cast(moe_h2, ai[0]), s, false);
+    s = __builtin_amdgcn_fdot2(q46, __builtin_bit_cast(moe_h2, ai[1]), s, false);
+    s = __builtin_amdgcn_fdot2(q13, __builtin_bit_cast(moe_h2, ai[2]), s, false);
+    s = __builtin_amdgcn_fdot2(q57, __builtin_bit_cast(moe_h2, ai[3]), s, false);
   }
   return s;
 }
@@ -137,16 +147,17 @@ __device__ void quantize_groups_lds(LoadFn load, int n, uint32_t* q_lds, float* 
 
 // ---- staged activations ------------------------------------------------------------
 //
-// fp mode: the activation vector in LDS as fp32 [nch * 32] (zero past the end) and
-// the fixed-order sum of each 32-value chunk (for the zero-point fold).
+// fp mode: the activation vector in LDS as fp16 pairs [nch * 16] (h8_pairs order, zero
+// past the end) and the fixed-order fp32 sum of each 32-value chunk (for the zero-point
+// fold).
 // int8 mode: codes permuted per 8 as [0 2 4 6 | 1 3 5 7], one fp32 scale and one
 // int32 code sum per 32 values.
 
-// fp32 staging of `rows` vectors of n fp16 values each (row stride n, 16-byte aligned
-// rows): xf[r][nch * 32] (zero past n) and the chunk sums sa[r][nch], in one pass:
-// each thread converts 8 values, and the 4 threads of a chunk (one quad of lanes)
-// combine their sums of 8 through DPP in a fixed order.
-__device__ __forceinline__ void stage_f32(const uint16_t* src, int rows, int n, int nch, float* xf, float* sa) {
+// Staging of `rows` vectors of n fp16 values each (row stride n, 16-byte aligned
+// rows): xh[r][nch * 16] (fp16 pairs, zero past n) and the chunk sums sa[r][nch], in
+// one pass: each thread takes 8 values, and the 4 threads of a chunk (one quad of
+// lanes) combine their fp32 sums of 8 through DPP in a fixed order.
+__device__ __forceinline__ void stage_h16(const uint16_t* src, int rows, int n, int nch, uint32_t* xh, float* sa) {
   const int per_row = nch * 4;  // pieces of 8 values
   const int total = rows * per_row;
   for (int p = threadIdx.x; p < total; p += blockDim.x) {  // quads are all in or all out
@@ -154,17 +165,19 @@ __device__ __forceinline__ void stage_f32(const uint16_t* src, int rows, int n, 
     const int pp = p - r * per_row;
     const int k0 = 8 * pp;
     const uint16_t* row = src + (int64_t)r * n;
-    float v[8];
+    uint4 u;
     if (k0 + 8 <= n) {
-      const uint4 u = *(const uint4*)(row + k0);
-      h8_to_f32(u, v);
+      u = *(const uint4*)(row + k0);
     } else {
+      uint16_t h[8];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) v[q] = k0 + q < n ? f16_to_f32(row[k0 + q]) : 0.0f;
+      for (int q = 0; q < 8; ++q) h[q] = k0 + q < n ? row[k0 + q] : (uint16_t)0;
+      u = make_uint4(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16), h[4] | ((uint32_t)h[5] << 16),
+                     h[6] | ((uint32_t)h[7] << 16));
     }
-    f32x4* d = (f32x4*)(xf + (int64_t)r * nch * 32 + k0);
-    d[0] = f32x4{v[0], v[1], v[2], v[3]};
-    d[1] = f32x4{v[4], v[5], v[6], v[7]};
+    float v[8];
+    h8_to_f32(u, v);
+    *(uint4*)(xh + (int64_t)r * nch * 16 + k0 / 2) = h8_pairs(u);
     float s8 = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
     s8 += dpp_f<kDppXor1>(s8);
     s8 += dpp_f<kDppXor2>(s8);
@@ -178,7 +191,7 @@ __device__ __forceinline__ void stage_f32(const uint16_t* src, int rows, int n, 
 // loads there has them travel while the activations are converted, and waiting for
 // the activations, which were issued first, does not wait for them.
 template <typename Issued>
-__device__ __forceinline__ void stage_f32_first(const uint16_t* src, int rows, int n, int nch, float* xf,
+__device__ __forceinline__ void stage_h16_first(const uint16_t* src, int rows, int n, int nch, uint32_t* xh,
                                                 float* sa, Issued&& issued) {
   constexpr int NB = 4;
   const int per_row = nch * 4;  // pieces of 8 values
@@ -186,35 +199,31 @@ __device__ __forceinline__ void stage_f32_first(const uint16_t* src, int rows, i
   const int wave_base = __builtin_amdgcn_readfirstlane((int)(threadIdx.x & ~63u));
   // n % 8 == 0 (checked at the entry point): a piece is wholly inside the row or
   // wholly past it, so the load is branch-free (address clamped, value selected)
-  auto load = [&](int p, float (&v)[8]) {
+  auto load = [&](int p, uint4& u) {
     const bool okp = p < total;
     const int pc = okp ? p : 0;
     const int r = pc / per_row;
     const int k0 = 8 * (pc - r * per_row);
     const bool in = k0 < n;
-    const uint4 u = *(const uint4*)(src + (int64_t)r * n + (in ? k0 : 0));
-    h8_to_f32(u, v);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) v[q] = in ? v[q] : 0.0f;
+    u = *(const uint4*)(src + (int64_t)r * n + (in ? k0 : 0));
+    if (!in) u = make_uint4(0u, 0u, 0u, 0u);
   };
-  auto convert = [&](int p, const float (&v)[8]) {
+  auto convert = [&](int p, const uint4& u) {
     const bool okp = p < total;
     const int pc = okp ? p : 0;
     const int r = pc / per_row;
     const int pp = pc - r * per_row;
     const int k0 = 8 * pp;
-    if (okp) {
-      f32x4* d = (f32x4*)(xf + (int64_t)r * nch * 32 + k0);
-      d[0] = f32x4{v[0], v[1], v[2], v[3]};
-      d[1] = f32x4{v[4], v[5], v[6], v[7]};
-    }
+    if (okp) *(uint4*)(xh + (int64_t)r * nch * 16 + k0 / 2) = h8_pairs(u);
+    float v[8];
+    h8_to_f32(u, v);
     float s8 = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
     s8 += dpp_f<kDppXor1>(s8);
     s8 += dpp_f<kDppXor2>(s8);
     if (okp && (pp & 3) == 0) sa[r * nch + (pp >> 2)] = s8;
   };
   auto batch = [&](int base, auto first) {
-    float vb[NB][8];
+    uint4 vb[NB];
 #pragma unroll
     for (int j = 0; j < NB; ++j)
       if (base + j * (int)blockDim.x + wave_base < total) load(base + j * (int)blockDim.x + (int)threadIdx.x, vb[j]);
@@ -258,6 +267,8 @@ struct MoeItem {
 };
 
 constexpr int kMoeThreads = 256;
+// LDS dwords per staged 32-value chunk in fp mode: 16 of fp16 pairs and the chunk sum
+constexpr int kStagedWords = 17;
 // slots (T * k) up to which the fc1 form that reads each expert once per call applies
 constexpr int kMoeSortSlots = 64;
 constexpr int kMoeStreamThreads = 512;  // persistent forms
@@ -287,8 +298,8 @@ __global__ __launch_bounds__(kMoeThreads) void qmoe_fc1_kernel(QmoeArgs a) {
   const int nch = (int)a.fc1_chunks;  // chunks holding codes k < H
   const int nblk = (int)a.fc1_nblk;
 
-  float* xf = (float*)smem;          // fp mode
-  float* sa = xf + nch * 32;
+  uint32_t* xh = smem;               // fp mode
+  float* sa = (float*)(xh + nch * 16);
   uint32_t* xq = smem;               // int8 mode
   float* xs = (float*)(smem + a.H / 4);
   int* xsum = (int*)(xs + a.H / 32);
@@ -358,10 +369,10 @@ __global__ __launch_bounds__(kMoeThreads) void qmoe_fc1_kernel(QmoeArgs a) {
         acc[r] = cv ? nv : acc[r];
       }
     } else {
-      float xa[32];
+      uint32_t xa[16];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const f32x4 v = *(const f32x4*)(xf + cc * 32 + 4 * q);
+      for (int q = 0; q < 4; ++q) {
+        const uint4 v = *(const uint4*)(xh + cc * 16 + 4 * q);
         xa[4 * q] = v.x; xa[4 * q + 1] = v.y; xa[4 * q + 2] = v.z; xa[4 * q + 3] = v.w;
       }
       const float sac = sa[cc];
@@ -369,7 +380,7 @@ __global__ __launch_bounds__(kMoeThreads) void qmoe_fc1_kernel(QmoeArgs a) {
       for (int r = 0; r < NR; ++r) {
         const float pr = dot_chunk_u4(cb.w[r], xa);
         const float zp = (float)((cb.z[r] >> ((blk & 1) * 4)) & 0xfu);
-        const float nv = fmaf((float)cb.s[r], fmaf(-zp, sac, 512.0f * pr), acc[r]);
+        const float nv = fmaf((float)cb.s[r], fmaf(-zp, sac, pr), acc[r]);
         acc[r] = cv ? nv : acc[r];
       }
     }
@@ -386,7 +397,7 @@ __global__ __launch_bounds__(kMoeThreads) void qmoe_fc1_kernel(QmoeArgs a) {
                         keep ? a.xs_out + (int64_t)t * (a.H / 32) : nullptr);
     __syncthreads();
   } else {
-    stage_f32(x, 1, (int)a.H, nch, xf, sa);
+    stage_h16(x, 1, (int)a.H, nch, xh, sa);
   }
   for (int base = 0; base < iters; base += kFc1Depth) {
 #pragma unroll
@@ -455,8 +466,8 @@ __global__ __launch_bounds__(kMoeThreads) void qmoe_fc2_kernel(QmoeArgs a) {
   const int I = (int)a.I;
   const uint16_t* hT = a.h + (int64_t)t * k * a.I;  // [k][I] fp16
 
-  float* hf = (float*)smem;                         // fp: [k][nch * 32]
-  float* sa = hf + (int64_t)k * nch * 32;           // fp: [k][nch]
+  uint32_t* hh = smem;                              // fp: [k][nch * 16] fp16 pairs
+  float* sa = (float*)(hh + (int64_t)k * nch * 16); // fp: [k][nch]
   uint32_t* hq = smem;                              // int8: [k][I] permuted codes
   float* hs = (float*)(smem + (int64_t)k * a.I / 4);
   int* hsum = (int*)(hs + (int64_t)k * a.I / 32);
@@ -535,11 +546,11 @@ __global__ __launch_bounds__(kMoeThreads) void qmoe_fc2_kernel(QmoeArgs a) {
         acc[r] = cv ? nv : acc[r];
       }
     } else {
-      const float* xp = hf + ((int64_t)jj * nch + cc) * 32;
-      float xa[32];
+      const uint32_t* xp = hh + ((int64_t)jj * nch + cc) * 16;
+      uint32_t xa[16];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const f32x4 v = *(const f32x4*)(xp + 4 * q);
+      for (int q = 0; q < 4; ++q) {
+        const uint4 v = *(const uint4*)(xp + 4 * q);
         xa[4 * q] = v.x; xa[4 * q + 1] = v.y; xa[4 * q + 2] = v.z; xa[4 * q + 3] = v.w;
       }
       const float sac = sa[jj * nch + cc];
@@ -547,7 +558,7 @@ __global__ __launch_bounds__(kMoeThreads) void qmoe_fc2_kernel(QmoeArgs a) {
       for (int r = 0; r < R; ++r) {
         const float pr = dot_chunk_u4(cb.w[r], xa);
         const float zp = (float)((cb.z[r] >> ((blk & 1) * 4)) & 0xfu);
-        const float nv = fmaf((float)cb.s[r], fmaf(-zp, sac, 512.0f * pr), acc[r]);
+        const float nv = fmaf((float)cb.s[r], fmaf(-zp, sac, pr), acc[r]);
         acc[r] = cv ? nv : acc[r];
       }
     }
@@ -575,7 +586,7 @@ __global__ __launch_bounds__(kMoeThreads) void qmoe_fc2_kernel(QmoeArgs a) {
   if constexpr (INT8) {
     stage_i8(a.hq_out + (int64_t)t * k * a.I, a.hs_out + (int64_t)t * k * (a.I / 32), k * I, hq, hs, hsum);
   } else {
-    stage_f32(hT, k, I, nch, hf, sa);
+    stage_h16(hT, k, I, nch, hh, sa);
   }
   for (int base = 0; base < total; base += kFc2Depth) {
 #pragma unroll
@@ -589,10 +600,10 @@ __global__ __launch_bounds__(kMoeThreads) void qmoe_fc2_kernel(QmoeArgs a) {
   }
 }
 
-// fp32 staging of `rows` fp16 rows of n values each (n % 8 == 0, row stride n) that
-// other work-groups of the same launch wrote: device-coherent 16-byte loads, the same
-// values and chunk sums as stage_f32 (xf[r][nch * 32], zero past n; sa[r][nch]).
-__device__ __forceinline__ void stage_h_coherent(const uint16_t* src, int rows, int n, int nch, float* xf,
+// Staging of `rows` fp16 rows of n values each (n % 8 == 0, row stride n) that other
+// work-groups of the same launch wrote: device-coherent 16-byte loads, the same pairs
+// and chunk sums as stage_h16 (xh[r][nch * 16], zero past n; sa[r][nch]).
+__device__ __forceinline__ void stage_h_coherent(const uint16_t* src, int rows, int n, int nch, uint32_t* xh,
                                                  float* sa) {
   constexpr int kDeviceCoherent = 16;  // cache-policy bit sc1: device scope
   const __amdgpu_buffer_rsrc_t r = make_rsrc(src, (uint32_t)rows * (uint32_t)n * 2u);
@@ -603,14 +614,11 @@ __device__ __forceinline__ void stage_h_coherent(const uint16_t* src, int rows, 
     const int pp = p - rr * per_row;
     const int k0 = 8 * pp;
     const bool in = k0 < n;  // a piece is wholly inside its row or wholly past it
-    const auto u = __builtin_amdgcn_raw_buffer_load_b128(r, (rr * n + (in ? k0 : 0)) * 2, 0, kDeviceCoherent);
+    const auto l = __builtin_amdgcn_raw_buffer_load_b128(r, (rr * n + (in ? k0 : 0)) * 2, 0, kDeviceCoherent);
+    const uint4 u = in ? make_uint4(l[0], l[1], l[2], l[3]) : make_uint4(0u, 0u, 0u, 0u);
     float v[8];
-    h8_to_f32(make_uint4(u[0], u[1], u[2], u[3]), v);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) v[q] = in ? v[q] : 0.0f;
-    f32x4* d = (f32x4*)(xf + (int64_t)rr * nch * 32 + k0);
-    d[0] = f32x4{v[0], v[1], v[2], v[3]};
-    d[1] = f32x4{v[4], v[5], v[6], v[7]};
+    h8_to_f32(u, v);
+    *(uint4*)(xh + (int64_t)rr * nch * 16 + k0 / 2) = h8_pairs(u);
     float s8 = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
     s8 += dpp_f<kDppXor1>(s8);
     s8 += dpp_f<kDppXor2>(s8);
@@ -646,8 +654,8 @@ __device__ __forceinline__ void fc1_stream_body(const QmoeArgs& a, int bid, int 
   const int nch = (int)a.fc1_chunks;
   const int nblk = (int)a.fc1_nblk;
   const int H = (int)a.H;
-  float* xf = (float*)smem;                    // fp: [T][nch * 32]
-  float* sa = xf + (size_t)T * nch * 32;       // fp: [T][nch]
+  uint32_t* xh = smem;                         // fp: [T][nch * 16] fp16 pairs
+  float* sa = (float*)(xh + (size_t)T * nch * 16);  // fp: [T][nch]
   uint32_t* xq = smem;                         // int8: [T][H / 4] permuted codes
   float* xs = (float*)(smem + (size_t)T * H / 4);  // int8: [T][H / 32] scales
   int* xsum = (int*)(xs + (size_t)T * H / 32);     // int8: [T][H / 32] code sums
@@ -741,11 +749,11 @@ __device__ __forceinline__ void fc1_stream_body(const QmoeArgs& a, int bid, int 
         acc[r] = cv ? nv : acc[r];
       }
     } else {
-      const float* xp = xf + ((size_t)ct * nch + cc) * 32;
-      float xa[32];
+      const uint32_t* xp = xh + ((size_t)ct * nch + cc) * 16;
+      uint32_t xa[16];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const f32x4 v = *(const f32x4*)(xp + 4 * q);
+      for (int q = 0; q < 4; ++q) {
+        const uint4 v = *(const uint4*)(xp + 4 * q);
         xa[4 * q] = v.x; xa[4 * q + 1] = v.y; xa[4 * q + 2] = v.z; xa[4 * q + 3] = v.w;
       }
       const float sac = sa[ct * nch + cc];
@@ -753,7 +761,7 @@ __device__ __forceinline__ void fc1_stream_body(const QmoeArgs& a, int bid, int 
       for (int r = 0; r < NR; ++r) {
         const float pr = dot_chunk_u4(cb.w[r], xa);
         const float zp = (float)((cb.z[r] >> ((blk & 1) * 4)) & 0xfu);
-        const float nv = fmaf((float)cb.s[r], fmaf(-zp, sac, 512.0f * pr), acc[r]);
+        const float nv = fmaf((float)cb.s[r], fmaf(-zp, sac, pr), acc[r]);
         acc[r] = cv ? nv : acc[r];
       }
     }
@@ -796,7 +804,7 @@ __device__ __forceinline__ void fc1_stream_body(const QmoeArgs& a, int bid, int 
     }
     __syncthreads();
   } else {
-    stage_f32_first(a.X, T, (int)a.H, nch, xf, sa, [&] {
+    stage_h16_first(a.X, T, (int)a.H, nch, xh, sa, [&] {
 #pragma unroll
       for (int i = 0; i < D - 1; ++i) fetch(buf[i]);
     });
@@ -849,8 +857,8 @@ __device__ __forceinline__ void fc2_stream_body(const QmoeArgs& a, int bid, int 
   const int nch = (int)a.fc2_chunks;
   const int nblk = (int)a.fc2_nblk;
   const int I = (int)a.I;
-  float* hf = (float*)smem;                    // fp: [T * k][nch * 32]
-  float* sa = hf + (size_t)T * k * nch * 32;   // fp: [T * k][nch]
+  uint32_t* hh = smem;                         // fp: [T * k][nch * 16] fp16 pairs
+  float* sa = (float*)(hh + (size_t)T * k * nch * 16);  // fp: [T * k][nch]
   uint32_t* hq = smem;                         // int8: [T * k][I / 4] permuted codes
   float* hs = (float*)(smem + (size_t)T * k * I / 4);  // int8: [T * k][I / 32] scales
   int* hsum = (int*)(hs + (size_t)T * k * I / 32);     // int8: [T * k][I / 32] code sums
@@ -956,11 +964,11 @@ __device__ __forceinline__ void fc2_stream_body(const QmoeArgs& a, int bid, int 
         acc[r] = cv ? nv : acc[r];
       }
     } else {
-      const float* xp = hf + ((size_t)c_hrow * nch + cc) * 32;
-      float xa[32];
+      const uint32_t* xp = hh + ((size_t)c_hrow * nch + cc) * 16;
+      uint32_t xa[16];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const f32x4 v = *(const f32x4*)(xp + 4 * q);
+      for (int q = 0; q < 4; ++q) {
+        const uint4 v = *(const uint4*)(xp + 4 * q);
         xa[4 * q] = v.x; xa[4 * q + 1] = v.y; xa[4 * q + 2] = v.z; xa[4 * q + 3] = v.w;
       }
       const float sac = sa[c_hrow * nch + cc];
@@ -968,7 +976,7 @@ __device__ __forceinline__ void fc2_stream_body(const QmoeArgs& a, int bid, int 
       for (int r = 0; r < R; ++r) {
         const float pr = dot_chunk_u4(cb.w[r], xa);
         const float zp = (float)((cb.z[r] >> ((blk & 1) * 4)) & 0xfu);
-        const float nv = fmaf((float)cb.s[r], fmaf(-zp, sac, 512.0f * pr), acc[r]);
+        const float nv = fmaf((float)cb.s[r], fmaf(-zp, sac, pr), acc[r]);
         acc[r] = cv ? nv : acc[r];
       }
     }
@@ -1003,9 +1011,9 @@ __device__ __forceinline__ void fc2_stream_body(const QmoeArgs& a, int bid, int 
 #pragma unroll
     for (int i = 0; i < D - 1; ++i) fetch(buf[i]);
     wait();
-    stage_h_coherent(a.h, T * k, (int)a.I, nch, hf, sa);
+    stage_h_coherent(a.h, T * k, (int)a.I, nch, hh, sa);
   } else {
-    stage_f32_first(a.h, T * k, (int)a.I, nch, hf, sa, [&] {
+    stage_h16_first(a.h, T * k, (int)a.I, nch, hh, sa, [&] {
 #pragma unroll
       for (int i = 0; i < D - 1; ++i) fetch(buf[i]);
     });
@@ -1067,8 +1075,8 @@ __global__ __launch_bounds__(kMoeStreamThreads) void qmoe_fc1_dedupe_kernel(Qmoe
   const int S = T * k;
   const int nch = (int)a.fc1_chunks;
   const int nblk = (int)a.fc1_nblk;
-  float* xf = (float*)smem;                    // [T][nch * 32]
-  float* sa = xf + (size_t)T * nch * 32;       // [T][nch]
+  uint32_t* xh = smem;                         // [T][nch * 16] fp16 pairs
+  float* sa = (float*)(xh + (size_t)T * nch * 16);  // [T][nch]
   int* eid = (int*)(sa + (size_t)T * nch);     // [S] expert of each slot
   int* first = eid + kMoeSortSlots;            // [S] first slot with the same expert
   int* ulist = first + kMoeSortSlots;          // [S] slots grouped by expert
@@ -1222,11 +1230,11 @@ __global__ __launch_bounds__(kMoeStreamThreads) void qmoe_fc1_dedupe_kernel(Qmoe
 #pragma unroll
     for (int q = 0; q < MS; ++q) {
       if (q < ccnt) {
-        const float* xp = xf + ((size_t)ctok[q] * nch + cc) * 32;
-        float xa[32];
+        const uint32_t* xp = xh + ((size_t)ctok[q] * nch + cc) * 16;
+        uint32_t xa[16];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const f32x4 v = *(const f32x4*)(xp + 4 * j);
+        for (int j = 0; j < 4; ++j) {
+          const uint4 v = *(const uint4*)(xp + 4 * j);
           xa[4 * j] = v.x; xa[4 * j + 1] = v.y; xa[4 * j + 2] = v.z; xa[4 * j + 3] = v.w;
         }
         const float sac = sa[ctok[q] * nch + cc];
@@ -1234,7 +1242,7 @@ __global__ __launch_bounds__(kMoeStreamThreads) void qmoe_fc1_dedupe_kernel(Qmoe
         for (int r = 0; r < NR; ++r) {
           const float pr = dot_chunk_u4(cb.w[r], xa);
           const float zp = (float)((cb.z[r] >> ((blk & 1) * 4)) & 0xfu);
-          const float nv = fmaf((float)cb.s[r], fmaf(-zp, sac, 512.0f * pr), acc[q][r]);
+          const float nv = fmaf((float)cb.s[r], fmaf(-zp, sac, pr), acc[q][r]);
           acc[q][r] = cv ? nv : acc[q][r];
         }
       }
@@ -1268,7 +1276,7 @@ __global__ __launch_bounds__(kMoeStreamThreads) void qmoe_fc1_dedupe_kernel(Qmoe
   MoeItem<NR> buf[D];
   set_group(fgrp);
   set_cgroup(cgrp);
-  stage_f32_first(a.X, T, (int)a.H, nch, xf, sa, [&] {
+  stage_h16_first(a.X, T, (int)a.H, nch, xh, sa, [&] {
 #pragma unroll
     for (int i = 0; i < D - 1; ++i) fetch(buf[i]);
   });
@@ -1307,10 +1315,18 @@ __global__ __launch_bounds__(kMoeStreamThreads) void qmoe_fc1_dedupe_kernel(Qmoe
 // and counts itself arrived.  It then issues the first weight loads of its fc2 share,
 // waits until every work-group has arrived, stages h with device-coherent loads and
 // runs its fc2 share (all k slots of its rows, combined in slot order).  The per-row
-// arithmetic is that of the two-kernel forms, so every form gives the same bits.  h
-// crosses the separate L2 caches of the XCDs only through device-coherent stores and
-// loads, so no whole-cache write-back or invalidation is needed.  The last work-group
-// to leave returns the counters to zero for the next call.
+// arithmetic is that of the two-kernel forms, so every form gives the same bits.  The
+// last work-group to leave returns the counters to zero for the next call.
+//
+// Ordering across the XCDs (each with its own L2) without whole-cache operations: the
+// h stores are agent-scope atomic stores, which write through the L2; the work-group
+// waits until every one of them is acknowledged (s_waitcnt) before its agent-scope
+// arrival add, so an arrival count that includes it implies its h is in memory.  A
+// waiting work-group reads the count with agent-scope loads (which miss the L2) and
+// only after it has seen every arrival issues its h loads, which are device-coherent
+// (they also miss the L2) and are ordered after the poll by the work-group barrier.  A
+// release/acquire pair would add an L2 write-back per arrival and an L2 invalidation
+// per waiter, several microseconds per call, to order data that never enters the L2.
 
 // a wait gives up after 1 s of the 100 MHz real-time counter and raises the error word
 constexpr uint64_t kSpinLimitTicks = 100000000ull;
@@ -1318,10 +1334,10 @@ constexpr uint64_t kSpinLimitTicks = 100000000ull;
 __device__ __forceinline__ uint32_t sync_add(uint32_t* p, uint32_t v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// arrival: a release at agent scope, so every h store of the work-group (ordered before
-// it by the work-group barrier) is visible to a work-group that acquires the count
+// arrival: the caller has waited for every h store of the work-group (write-through
+// agent-scope stores) to be acknowledged
 __device__ __forceinline__ uint32_t sync_arrive(uint32_t* p) {
-  return __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  return __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint32_t sync_load(uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1346,20 +1362,14 @@ __global__ __launch_bounds__(kMoeStreamThreads) void qmoe_fused_kernel(QmoeArgs 
   auto wait = [&] {
     if (threadIdx.x == 0) {
       const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-      int polls = 0;
       while (sync_load(&sync[0]) < (uint32_t)nb) {
-        if (polls < 4) __builtin_amdgcn_s_sleep(4);
-        else if (polls < 16) __builtin_amdgcn_s_sleep(16);
-        else __builtin_amdgcn_s_sleep(48);
-        ++polls;
+        __builtin_amdgcn_s_sleep(2);
         if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinLimitTicks) {
           sync_store(&sync[2], 1u);
           gave_up = 1u;
           break;
         }
       }
-      // acquire: pairs with every work-group's release of its arrival
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
     __syncthreads();
   };
@@ -1380,11 +1390,11 @@ __global__ __launch_bounds__(kMoeStreamThreads) void qmoe_fused_kernel(QmoeArgs 
 
 size_t qmoe_fc1_lds_bytes(const QmoeArgs& a) {
   if (a.mode == QMOE_INT8_ACT) return (size_t)a.H + (size_t)(a.H / 32) * 8;
-  return (size_t)a.fc1_chunks * 33 * sizeof(float);
+  return (size_t)a.fc1_chunks * kStagedWords * sizeof(uint32_t);
 }
 size_t qmoe_fc2_lds_bytes(const QmoeArgs& a) {
   if (a.mode == QMOE_INT8_ACT) return (size_t)(a.k * a.I) + (size_t)(a.k * a.I / 32) * 8;
-  return (size_t)a.k * a.fc2_chunks * 33 * sizeof(float);
+  return (size_t)a.k * a.fc2_chunks * kStagedWords * sizeof(uint32_t);
 }
 
 // Allow more than 64 KB of dynamic LDS for a kernel: up to the 150 KB the launch plans
@@ -1448,7 +1458,7 @@ static bool launch_fc1_stream(const QmoeArgs& a, int cap, hipStream_t st) {
   const int64_t ngroups = a.T * a.k * ((a.I + rpg - 1) / rpg);
   // staged activations: fp32 values and chunk sums, or int8 codes, scales and code sums
   const size_t fixed = INT8 ? (size_t)a.T * ((size_t)a.H + (size_t)(a.H / 32) * 8)
-                            : (size_t)a.T * a.fc1_chunks * 33 * sizeof(float);
+                            : (size_t)a.T * a.fc1_chunks * kStagedWords * sizeof(uint32_t);
   int64_t grid = 0;
   size_t lds = 0;
   if (!moe_stream_plan(kern, ngroups, fixed, (size_t)rpg * 2 * sizeof(float), a.num_cus, cap, &grid, &lds))
@@ -1465,7 +1475,7 @@ static bool launch_fc2_stream(const QmoeArgs& a, int cap, hipStream_t st) {
   const int64_t rpg = (64 >> a.fc2_lpr_log2) * R;
   const int64_t ngroups = a.T * ((a.H + rpg - 1) / rpg);
   const size_t fixed = INT8 ? (size_t)a.T * a.k * ((size_t)a.I + (size_t)(a.I / 32) * 8)
-                            : (size_t)a.T * a.k * a.fc2_chunks * 33 * sizeof(float);
+                            : (size_t)a.T * a.k * a.fc2_chunks * kStagedWords * sizeof(uint32_t);
   int64_t grid = 0;
   size_t lds = 0;
   if (!moe_stream_plan(kern, ngroups, fixed, (size_t)rpg * a.k * sizeof(float), a.num_cus, cap, &grid, &lds))
@@ -1485,8 +1495,8 @@ static bool launch_fused(const QmoeArgs& a, hipStream_t st) {
   if (r2 * a.fc2_row_bytes >= (1LL << 31) || r2 * a.fc2_nblk * 2 >= (1LL << 31)) return false;
   const int64_t rpg1 = (64 >> a.fc1_lpr_log2) * RI, rpg2 = (64 >> a.fc2_lpr_log2) * R;
   const int64_t ng1 = a.T * a.k * ((a.I + rpg1 - 1) / rpg1), ng2 = a.T * ((a.H + rpg2 - 1) / rpg2);
-  const size_t fixed1 = (size_t)a.T * a.fc1_chunks * 33 * sizeof(float);
-  const size_t fixed2 = (size_t)a.T * a.k * a.fc2_chunks * 33 * sizeof(float);
+  const size_t fixed1 = (size_t)a.T * a.fc1_chunks * kStagedWords * sizeof(uint32_t);
+  const size_t fixed2 = (size_t)a.T * a.k * a.fc2_chunks * kStagedWords * sizeof(uint32_t);
   const size_t pg1 = (size_t)rpg1 * 2 * sizeof(float), pg2 = (size_t)rpg2 * a.k * sizeof(float);
   constexpr size_t kMaxLds = 150 * 1024;
   auto lds_for = [&](int64_t grid) {
@@ -1520,7 +1530,7 @@ static bool launch_fc1_dedupe(const QmoeArgs& a, hipStream_t st) {
   // group count at its largest (every slot its own expert); the kernel deals the
   // actual groups, never more
   const int64_t ngroups = a.T * a.k * ((a.I + rpg - 1) / rpg);
-  const size_t fixed = (size_t)a.T * a.fc1_chunks * 33 * sizeof(float) + (size_t)kDedupeInts * sizeof(int);
+  const size_t fixed = (size_t)a.T * a.fc1_chunks * kStagedWords * sizeof(uint32_t) + (size_t)kDedupeInts * sizeof(int);
   int64_t grid = 0;
   size_t lds = 0;
   if (!moe_stream_plan(kern, ngroups, fixed, (size_t)rpg * kDedupeMaxT * 2 * sizeof(float), a.num_cus, 1,
@@ -1543,8 +1553,8 @@ bool qmoe_fused_plan(QmoeArgs& a, int candidate) {
   const int64_t rpg1 = (64 >> a.fc1_lpr_log2) * 2, rpg2 = (64 >> a.fc2_lpr_log2) * a.f_r2;
   const int64_t grid = a.num_cus > 0 ? a.num_cus : 256;
   const int64_t ng1 = a.T * a.k * ((a.I + rpg1 - 1) / rpg1), ng2 = a.T * ((a.H + rpg2 - 1) / rpg2);
-  const int64_t l1 = a.T * a.fc1_chunks * 33 * 4 + ((ng1 + grid - 1) / grid) * rpg1 * 2 * 4;
-  const int64_t l2 = a.T * a.k * a.fc2_chunks * 33 * 4 + ((ng2 + grid - 1) / grid) * rpg2 * a.k * 4;
+  const int64_t l1 = a.T * a.fc1_chunks * kStagedWords * 4 + ((ng1 + grid - 1) / grid) * rpg1 * 2 * 4;
+  const int64_t l2 = a.T * a.k * a.fc2_chunks * kStagedWords * 4 + ((ng2 + grid - 1) / grid) * rpg2 * a.k * 4;
   return (l1 > l2 ? l1 : l2) <= 150 * 1024;
 }
 
