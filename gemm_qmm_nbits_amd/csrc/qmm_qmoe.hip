@@ -147,14 +147,26 @@ __device__ void quantize_groups_lds(LoadFn load, int n, uint32_t* q_lds, float* 
 
 // ---- staged activations ------------------------------------------------------------
 //
-// fp mode: the activation vector in LDS as fp16 pairs [nch * 16] (h8_pairs order, zero
-// past the end) and the fixed-order fp32 sum of each 32-value chunk (for the zero-point
-// fold).
+// fp mode: the activation vector in LDS as fp16 pairs, 16 dwords per 32-value chunk
+// (h8_pairs order, zero past the end) at a stride of kPairStride dwords, and the
+// fixed-order fp32 sum of each chunk (for the zero-point fold).
 // int8 mode: codes permuted per 8 as [0 2 4 6 | 1 3 5 7], one fp32 scale and one
 // int32 code sum per 32 values.
 
+// Staged chunks lie kPairStride dwords apart: the pad dword puts the chunks that
+// consecutive lanes read in different LDS banks (at 16 dwords every fourth lane would
+// share a bank).
+constexpr int kPairStride = 17;
+__device__ __forceinline__ void store_pairs(uint32_t* p, uint4 v) {
+  p[0] = v.x;
+  p[1] = v.y;
+  p[2] = v.z;
+  p[3] = v.w;
+}
+__device__ __forceinline__ uint4 load_pairs(const uint32_t* p) { return make_uint4(p[0], p[1], p[2], p[3]); }
+
 // Staging of `rows` vectors of n fp16 values each (row stride n, 16-byte aligned
-// rows): xh[r][nch * 16] (fp16 pairs, zero past n) and the chunk sums sa[r][nch], in
+// rows): xh[r][nch][kPairStride] (fp16 pairs, zero past n) and the chunk sums sa[r][nch], in
 // one pass: each thread takes 8 values, and the 4 threads of a chunk (one quad of
 // lanes) combine their fp32 sums of 8 through DPP in a fixed order.
 __device__ __forceinline__ void stage_h16(const uint16_t* src, int rows, int n, int nch, uint32_t* xh, float* sa) {
@@ -177,7 +189,7 @@ __device__ __forceinline__ void stage_h16(const uint16_t* src, int rows, int n, 
     }
     float v[8];
     h8_to_f32(u, v);
-    *(uint4*)(xh + (int64_t)r * nch * 16 + k0 / 2) = h8_pairs(u);
+    store_pairs(xh + ((int64_t)r * nch + (k0 >> 5)) * kPairStride + ((k0 & 31) >> 1), h8_pairs(u));
     float s8 = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
     s8 += dpp_f<kDppXor1>(s8);
     s8 += dpp_f<kDppXor2>(s8);
@@ -214,7 +226,7 @@ __device__ __forceinline__ void stage_h16_first(const uint16_t* src, int rows, i
     const int r = pc / per_row;
     const int pp = pc - r * per_row;
     const int k0 = 8 * pp;
-    if (okp) *(uint4*)(xh + (int64_t)r * nch * 16 + k0 / 2) = h8_pairs(u);
+    if (okp) store_pairs(xh + ((int64_t)r * nch + (k0 >> 5)) * kPairStride + ((k0 & 31) >> 1), h8_pairs(u));
     float v[8];
     h8_to_f32(u, v);
     float s8 = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
@@ -267,8 +279,9 @@ struct MoeItem {
 };
 
 constexpr int kMoeThreads = 256;
-// LDS dwords per staged 32-value chunk in fp mode: 16 of fp16 pairs and the chunk sum
-constexpr int kStagedWords = 17;
+// LDS dwords per staged 32-value chunk in fp mode: kPairStride of fp16 pairs (one pad)
+// and the chunk sum
+constexpr int kStagedWords = kPairStride + 1;
 // slots (T * k) up to which the fc1 form that reads each expert once per call applies
 constexpr int kMoeSortSlots = 64;
 constexpr int kMoeStreamThreads = 512;  // persistent forms
@@ -299,7 +312,7 @@ __global__ __launch_bounds__(kMoeThreads) void qmoe_fc1_kernel(QmoeArgs a) {
   const int nblk = (int)a.fc1_nblk;
 
   uint32_t* xh = smem;               // fp mode
-  float* sa = (float*)(xh + nch * 16);
+  float* sa = (float*)(xh + nch * kPairStride);
   uint32_t* xq = smem;               // int8 mode
   float* xs = (float*)(smem + a.H / 4);
   int* xsum = (int*)(xs + a.H / 32);
@@ -372,7 +385,7 @@ __global__ __launch_bounds__(kMoeThreads) void qmoe_fc1_kernel(QmoeArgs a) {
       uint32_t xa[16];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const uint4 v = *(const uint4*)(xh + cc * 16 + 4 * q);
+        const uint4 v = load_pairs(xh + cc * kPairStride + 4 * q);
         xa[4 * q] = v.x; xa[4 * q + 1] = v.y; xa[4 * q + 2] = v.z; xa[4 * q + 3] = v.w;
       }
       const float sac = sa[cc];
@@ -466,8 +479,8 @@ __global__ __launch_bounds__(kMoeThreads) void qmoe_fc2_kernel(QmoeArgs a) {
   const int I = (int)a.I;
   const uint16_t* hT = a.h + (int64_t)t * k * a.I;  // [k][I] fp16
 
-  uint32_t* hh = smem;                              // fp: [k][nch * 16] fp16 pairs
-  float* sa = (float*)(hh + (int64_t)k * nch * 16); // fp: [k][nch]
+  uint32_t* hh = smem;                              // fp: [k][nch][kPairStride] fp16 pairs
+  float* sa = (float*)(hh + (int64_t)k * nch * kPairStride);  // fp: [k][nch]
   uint32_t* hq = smem;                              // int8: [k][I] permuted codes
   float* hs = (float*)(smem + (int64_t)k * a.I / 4);
   int* hsum = (int*)(hs + (int64_t)k * a.I / 32);
@@ -546,11 +559,11 @@ __global__ __launch_bounds__(kMoeThreads) void qmoe_fc2_kernel(QmoeArgs a) {
         acc[r] = cv ? nv : acc[r];
       }
     } else {
-      const uint32_t* xp = hh + ((int64_t)jj * nch + cc) * 16;
+      const uint32_t* xp = hh + ((int64_t)jj * nch + cc) * kPairStride;
       uint32_t xa[16];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const uint4 v = *(const uint4*)(xp + 4 * q);
+        const uint4 v = load_pairs(xp + 4 * q);
         xa[4 * q] = v.x; xa[4 * q + 1] = v.y; xa[4 * q + 2] = v.z; xa[4 * q + 3] = v.w;
       }
       const float sac = sa[jj * nch + cc];
@@ -602,7 +615,7 @@ __global__ __launch_bounds__(kMoeThreads) void qmoe_fc2_kernel(QmoeArgs a) {
 
 // Staging of `rows` fp16 rows of n values each (n % 8 == 0, row stride n) that other
 // work-groups of the same launch wrote: device-coherent 16-byte loads, the same pairs
-// and chunk sums as stage_h16 (xh[r][nch * 16], zero past n; sa[r][nch]).
+// and chunk sums as stage_h16 (xh[r][nch][kPairStride], zero past n; sa[r][nch]).
 __device__ __forceinline__ void stage_h_coherent(const uint16_t* src, int rows, int n, int nch, uint32_t* xh,
                                                  float* sa) {
   constexpr int kDeviceCoherent = 16;  // cache-policy bit sc1: device scope
@@ -618,7 +631,7 @@ __device__ __forceinline__ void stage_h_coherent(const uint16_t* src, int rows, 
     const uint4 u = in ? make_uint4(l[0], l[1], l[2], l[3]) : make_uint4(0u, 0u, 0u, 0u);
     float v[8];
     h8_to_f32(u, v);
-    *(uint4*)(xh + (int64_t)rr * nch * 16 + k0 / 2) = h8_pairs(u);
+    store_pairs(xh + ((int64_t)rr * nch + (k0 >> 5)) * kPairStride + ((k0 & 31) >> 1), h8_pairs(u));
     float s8 = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
     s8 += dpp_f<kDppXor1>(s8);
     s8 += dpp_f<kDppXor2>(s8);
@@ -654,8 +667,8 @@ __device__ __forceinline__ void fc1_stream_body(const QmoeArgs& a, int bid, int 
   const int nch = (int)a.fc1_chunks;
   const int nblk = (int)a.fc1_nblk;
   const int H = (int)a.H;
-  uint32_t* xh = smem;                         // fp: [T][nch * 16] fp16 pairs
-  float* sa = (float*)(xh + (size_t)T * nch * 16);  // fp: [T][nch]
+  uint32_t* xh = smem;                         // fp: [T][nch][kPairStride] fp16 pairs
+  float* sa = (float*)(xh + (size_t)T * nch * kPairStride);  // fp: [T][nch]
   uint32_t* xq = smem;                         // int8: [T][H / 4] permuted codes
   float* xs = (float*)(smem + (size_t)T * H / 4);  // int8: [T][H / 32] scales
   int* xsum = (int*)(xs + (size_t)T * H / 32);     // int8: [T][H / 32] code sums
@@ -749,11 +762,11 @@ __device__ __forceinline__ void fc1_stream_body(const QmoeArgs& a, int bid, int 
         acc[r] = cv ? nv : acc[r];
       }
     } else {
-      const uint32_t* xp = xh + ((size_t)ct * nch + cc) * 16;
+      const uint32_t* xp = xh + ((size_t)ct * nch + cc) * kPairStride;
       uint32_t xa[16];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const uint4 v = *(const uint4*)(xp + 4 * q);
+        const uint4 v = load_pairs(xp + 4 * q);
         xa[4 * q] = v.x; xa[4 * q + 1] = v.y; xa[4 * q + 2] = v.z; xa[4 * q + 3] = v.w;
       }
       const float sac = sa[ct * nch + cc];
@@ -857,8 +870,8 @@ __device__ __forceinline__ void fc2_stream_body(const QmoeArgs& a, int bid, int 
   const int nch = (int)a.fc2_chunks;
   const int nblk = (int)a.fc2_nblk;
   const int I = (int)a.I;
-  uint32_t* hh = smem;                         // fp: [T * k][nch * 16] fp16 pairs
-  float* sa = (float*)(hh + (size_t)T * k * nch * 16);  // fp: [T * k][nch]
+  uint32_t* hh = smem;                         // fp: [T * k][nch][kPairStride] fp16 pairs
+  float* sa = (float*)(hh + (size_t)T * k * nch * kPairStride);  // fp: [T * k][nch]
   uint32_t* hq = smem;                         // int8: [T * k][I / 4] permuted codes
   float* hs = (float*)(smem + (size_t)T * k * I / 4);  // int8: [T * k][I / 32] scales
   int* hsum = (int*)(hs + (size_t)T * k * I / 32);     // int8: [T * k][I / 32] code sums
@@ -964,11 +977,11 @@ __device__ __forceinline__ void fc2_stream_body(const QmoeArgs& a, int bid, int 
         acc[r] = cv ? nv : acc[r];
       }
     } else {
-      const uint32_t* xp = hh + ((size_t)c_hrow * nch + cc) * 16;
+      const uint32_t* xp = hh + ((size_t)c_hrow * nch + cc) * kPairStride;
       uint32_t xa[16];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const uint4 v = *(const uint4*)(xp + 4 * q);
+        const uint4 v = load_pairs(xp + 4 * q);
         xa[4 * q] = v.x; xa[4 * q + 1] = v.y; xa[4 * q + 2] = v.z; xa[4 * q + 3] = v.w;
       }
       const float sac = sa[c_hrow * nch + cc];
@@ -1075,8 +1088,8 @@ __global__ __launch_bounds__(kMoeStreamThreads) void qmoe_fc1_dedupe_kernel(Qmoe
   const int S = T * k;
   const int nch = (int)a.fc1_chunks;
   const int nblk = (int)a.fc1_nblk;
-  uint32_t* xh = smem;                         // [T][nch * 16] fp16 pairs
-  float* sa = (float*)(xh + (size_t)T * nch * 16);  // [T][nch]
+  uint32_t* xh = smem;                         // [T][nch][kPairStride] fp16 pairs
+  float* sa = (float*)(xh + (size_t)T * nch * kPairStride);  // [T][nch]
   int* eid = (int*)(sa + (size_t)T * nch);     // [S] expert of each slot
   int* first = eid + kMoeSortSlots;            // [S] first slot with the same expert
   int* ulist = first + kMoeSortSlots;          // [S] slots grouped by expert
@@ -1230,11 +1243,11 @@ __global__ __launch_bounds__(kMoeStreamThreads) void qmoe_fc1_dedupe_kernel(Qmoe
 #pragma unroll
     for (int q = 0; q < MS; ++q) {
       if (q < ccnt) {
-        const uint32_t* xp = xh + ((size_t)ctok[q] * nch + cc) * 16;
+        const uint32_t* xp = xh + ((size_t)ctok[q] * nch + cc) * kPairStride;
         uint32_t xa[16];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const uint4 v = *(const uint4*)(xp + 4 * j);
+          const uint4 v = load_pairs(xp + 4 * j);
           xa[4 * j] = v.x; xa[4 * j + 1] = v.y; xa[4 * j + 2] = v.z; xa[4 * j + 3] = v.w;
         }
         const float sac = sa[ctok[q] * nch + cc];
