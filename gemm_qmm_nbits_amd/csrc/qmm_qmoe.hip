@@ -210,15 +210,19 @@ __device__ __forceinline__ void stage_h16_first(const uint16_t* src, int rows, i
   const int total = rows * per_row;
   const int wave_base = __builtin_amdgcn_readfirstlane((int)(threadIdx.x & ~63u));
   // n % 8 == 0 (checked at the entry point): a piece is wholly inside the row or
-  // wholly past it, so the load is branch-free (address clamped, value selected)
+  // wholly past it.  Every lane issues its loads unconditionally: a piece past the row
+  // or past the batch loads from beyond the descriptor's range, which returns zero and
+  // moves no data (a load inside a branch would make the compiler wait for it at the
+  // branch's end, before the caller's loads are issued).
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, (uint32_t)rows * (uint32_t)n * 2u);
   auto load = [&](int p, uint4& u) {
     const bool okp = p < total;
     const int pc = okp ? p : 0;
     const int r = pc / per_row;
     const int k0 = 8 * (pc - r * per_row);
-    const bool in = k0 < n;
-    u = *(const uint4*)(src + (int64_t)r * n + (in ? k0 : 0));
-    if (!in) u = make_uint4(0u, 0u, 0u, 0u);
+    const uint32_t off = okp && k0 < n ? ((uint32_t)r * (uint32_t)n + (uint32_t)k0) * 2u : 0x80000000u;
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0);
+    u = make_uint4(v[0], v[1], v[2], v[3]);
   };
   auto convert = [&](int p, const uint4& u) {
     const bool okp = p < total;
@@ -237,8 +241,7 @@ __device__ __forceinline__ void stage_h16_first(const uint16_t* src, int rows, i
   auto batch = [&](int base, auto first) {
     uint4 vb[NB];
 #pragma unroll
-    for (int j = 0; j < NB; ++j)
-      if (base + j * (int)blockDim.x + wave_base < total) load(base + j * (int)blockDim.x + (int)threadIdx.x, vb[j]);
+    for (int j = 0; j < NB; ++j) load(base + j * (int)blockDim.x + (int)threadIdx.x, vb[j]);
     if constexpr (decltype(first)::value) {
       __builtin_amdgcn_sched_barrier(0);  // keep the caller's loads behind these
       issued();
