@@ -73,10 +73,12 @@ __global__ __launch_bounds__(stream_threads(MT, R)) void gemv_cb_stream_kernel(G
   uint32_t fw[R], fs[R];
   int fit = 0, fgrp = g_begin + wave;
   auto set_rows = [&](int grp) {
+    // past the wave's own groups the cursor moves to group `ngroups`, whose rows lie
+    // past N: offsets past the end of both buffers, loads that return 0 and move no data
+    const int gq = grp < g_end ? grp : ngroups;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const uint32_t row = (uint32_t)(grp * rpg + r * SUBS + sub);
-      // rows past N give offsets past the end of both buffers (loads return 0)
+      const uint32_t row = (uint32_t)(gq * rpg + r * SUBS + sub);
       fw[r] = row * row_bytes + (uint32_t)lp * 16u;
       fs[r] = (row * (uint32_t)nblk + (uint32_t)lane_b) * 4u;
     }

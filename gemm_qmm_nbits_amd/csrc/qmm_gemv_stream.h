@@ -76,10 +76,15 @@ __global__ __launch_bounds__(stream_threads(MT, R)) void gemv_ip_stream_kernel(G
   uint32_t fw[R], fs[R], fz[R];
   int fit = 0, fgrp = g_begin + wave;
   auto set_rows = [&](int grp) {
+    // Past the wave's own groups (the ring's run-ahead at the end of its work) the
+    // cursor moves to group `ngroups`, whose rows all lie past N: rows past N give
+    // offsets past the end of every buffer, so those loads return 0 and move no data
+    // (the groups that follow belong to the next work-group, whose rows another
+    // XCD's L2 reads).
+    const int gq = grp < g_end ? grp : ngroups;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const uint32_t row = (uint32_t)(grp * rpg + r * SUBS + sub);
-      // rows past N give offsets past the end of every buffer (loads return 0)
+      const uint32_t row = (uint32_t)(gq * rpg + r * SUBS + sub);
       fw[r] = row * row_bytes + (uint32_t)lp * 16u;
       fs[r] = (row * (uint32_t)nblk + (uint32_t)lane_b) * 2u;
       if constexpr (ZK == 1) fz[r] = row * zrow_bytes;

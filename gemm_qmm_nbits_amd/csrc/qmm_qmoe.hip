@@ -702,13 +702,17 @@ __device__ __forceinline__ void fc1_stream_body(const QmoeArgs& a, int bid, int 
   __amdgpu_buffer_rsrc_t rW, rS, rZ;
   uint32_t frow[NR];
   auto set_group = [&](int grp) {
-    const int gg = grp < ngroups ? grp : ngroups - 1;  // past the end: the last group again
+    // Past the wave's own groups (the ring's run-ahead at the end of its work, or a
+    // wave with none) the buffers get range 0: those loads return 0 and move no data.
+    // (The groups that follow belong to the next work-group, on another XCD.)
+    const uint32_t on = grp < g_end ? 1u : 0u;
+    const int gg = grp < ngroups ? grp : ngroups - 1;
     const int sl = gg / GI;
     const int gi = gg - sl * GI;
     const int e = clamp_expert(a.ids[sl], a.E);
-    rW = make_rsrc(a.fc1.W + (size_t)e * erows * rb, erows * rb);
-    rS = make_rsrc((const uint16_t*)a.fc1.scales + (size_t)e * erows * nblk, erows * (uint32_t)nblk * 2u);
-    if constexpr (ZK) rZ = make_rsrc(a.fc1.zp + (size_t)e * erows * zrb, erows * zrb);
+    rW = make_rsrc(a.fc1.W + (size_t)e * erows * rb, on * erows * rb);
+    rS = make_rsrc((const uint16_t*)a.fc1.scales + (size_t)e * erows * nblk, on * erows * (uint32_t)nblk * 2u);
+    if constexpr (ZK) rZ = make_rsrc(a.fc1.zp + (size_t)e * erows * zrb, on * erows * zrb);
 #pragma unroll
     for (int r = 0; r < RI; ++r) {
       const int i = gi * rpg + r * SUBS + sub;
@@ -908,15 +912,17 @@ __device__ __forceinline__ void fc2_stream_body(const QmoeArgs& a, int bid, int 
   __amdgpu_buffer_rsrc_t rW, rS, rZ;
   uint32_t frow[R];
   auto set_unit = [&](int u) {
-    const int uu = u < nunits ? u : nunits - 1;  // past the end: the last unit again
+    // past the wave's own units the buffers get range 0 (loads return 0, move no data)
+    const uint32_t on = u < nunits ? 1u : 0u;
+    const int uu = u < nunits ? u : nunits - 1;
     const int grp = g_begin + uu / k;
     const int j = uu - (uu / k) * k;
     const int t = grp / GN;
     const int gn = grp - t * GN;
     const int e = clamp_expert(a.ids[t * k + j], a.E);
-    rW = make_rsrc(a.fc2.W + (size_t)e * erows * rb, erows * rb);
-    rS = make_rsrc((const uint16_t*)a.fc2.scales + (size_t)e * erows * nblk, erows * (uint32_t)nblk * 2u);
-    if constexpr (ZK) rZ = make_rsrc(a.fc2.zp + (size_t)e * erows * zrb, erows * zrb);
+    rW = make_rsrc(a.fc2.W + (size_t)e * erows * rb, on * erows * rb);
+    rS = make_rsrc((const uint16_t*)a.fc2.scales + (size_t)e * erows * nblk, on * erows * (uint32_t)nblk * 2u);
+    if constexpr (ZK) rZ = make_rsrc(a.fc2.zp + (size_t)e * erows * zrb, on * erows * zrb);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int n = gn * rpg + r * SUBS + sub;
@@ -1184,13 +1190,15 @@ __global__ __launch_bounds__(kMoeStreamThreads) void qmoe_fc1_dedupe_kernel(Qmoe
   __amdgpu_buffer_rsrc_t rW, rS, rZ;
   uint32_t frow[NR];
   auto set_group = [&](int grp) {
+    // past the wave's own groups the buffers get range 0 (loads return 0, move no data)
+    const uint32_t on = grp < g_end ? 1u : 0u;
     const int gg = grp < ngroups ? grp : ngroups - 1;
     const int v = gg / GI;
     const int gi = gg - v * GI;
     const int e = vexp[v];
-    rW = make_rsrc(a.fc1.W + (size_t)e * erows * rb, erows * rb);
-    rS = make_rsrc((const uint16_t*)a.fc1.scales + (size_t)e * erows * nblk, erows * (uint32_t)nblk * 2u);
-    if constexpr (ZK) rZ = make_rsrc(a.fc1.zp + (size_t)e * erows * zrb, erows * zrb);
+    rW = make_rsrc(a.fc1.W + (size_t)e * erows * rb, on * erows * rb);
+    rS = make_rsrc((const uint16_t*)a.fc1.scales + (size_t)e * erows * nblk, on * erows * (uint32_t)nblk * 2u);
+    if constexpr (ZK) rZ = make_rsrc(a.fc1.zp + (size_t)e * erows * zrb, on * erows * zrb);
 #pragma unroll
     for (int r = 0; r < RI; ++r) {
       const int i = gi * rpg + r * SUBS + sub;
