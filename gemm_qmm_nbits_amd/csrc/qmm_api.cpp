@@ -661,15 +661,16 @@ struct QmoeLayout {
   size_t h = 0, sync = 0, xq = 0, xs = 0, hq = 0, hs = 0, total = 0;
 };
 
+// The sync words sit at offset 0 for every shape and mode, so calls of different
+// shapes on one buffer (the no-allocation entry's static array) never find another
+// shape's h or codes where their sync words are.
 QmoeLayout qmoe_layout(int64_t T, int64_t H, int64_t I, int k, int mode) {
   QmoeLayout L;
   size_t off = 0;
+  L.sync = off;
+  off += align256((size_t)kQmoeSyncWords * 4);
   L.h = off;
   off += align256((size_t)(T * k * I) * 2);
-  if (mode == QMOE_FP) {
-    L.sync = off;
-    off += align256((size_t)kQmoeSyncWords * 4);
-  }
   if (mode == QMOE_INT8_ACT) {
     L.xq = off;
     off += align256((size_t)(T * H));
@@ -1115,12 +1116,10 @@ qmm_status qmm::qmoe_decode_run(const uint16_t* X, int64_t T, int64_t H, int64_t
     a.hs_out = (float*)(sc + L.hs);
   }
   a.Y = Y;
-  if (mode == QMOE_FP) {
-    a.sync = (uint32_t*)(sc + L.sync);
-  }
+  a.sync = (uint32_t*)(sc + L.sync);
   int r1 = 1, r2 = 1;
   qmoe_choice(a, st, may_time, &r1, &r2);
-  if (mode == QMOE_FP && qmoe_fused_choice(a, st, may_time, r1, r2) >= 0) {
+  if (qmoe_fused_choice(a, st, may_time, r1, r2) >= 0) {
     const hipError_t e = launch_qmoe_fused(a, st);  // the plan has checked that it fits
     if (e != hipSuccess) return (qmm_status)e;
     return (qmm_status)hipGetLastError();
@@ -1180,7 +1179,7 @@ qmm_status qmoe_decode_status(void* scratch, size_t scratch_bytes, int64_t T, in
   *timed_out = 0;
   if (mode != QMOE_FP && mode != QMOE_INT8_ACT) return QMM_E_MODE;
   if (T < 0 || H < 0 || I < 0 || k < 0) return QMM_E_SHAPE;
-  if (mode != QMOE_FP || T == 0) return QMM_OK;  // only the fp single-launch form waits
+  if (T == 0) return QMM_OK;
   const QmoeLayout L = qmoe_layout(T, H, I, k, mode);
   if (!scratch) return QMM_E_NULL;
   if (scratch_bytes < L.total) return QMM_E_WORKSPACE;

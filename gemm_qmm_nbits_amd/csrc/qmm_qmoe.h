@@ -29,23 +29,24 @@ struct QmoeArgs {
   float* hs_out;    // int8 mode: [T][k][I/32] scales of h
   uint16_t* Y;
   int num_cus;      // compute units of the device
-  // single-launch form (fp mode): fc2 rows per lane, work-groups per compute unit,
-  // and the self-resetting sync words in scratch (kQmoeSyncWords)
+  // single-launch form: fc2 rows per lane, work-groups per compute unit, and the
+  // self-resetting sync words in scratch (kQmoeSyncWords)
   int f_r2;
   int f_wpc;
   uint32_t* sync;
 };
-// Sync words of the single-launch form, in scratch: [0] work-groups arrived (fc1
-// share done), [1] work-groups finished, [2] error flag (a wait that timed out),
-// [3] unused.  They must be zero before the first call on a scratch buffer; every call
-// leaves [0] and [1] zero.
+// Sync words of the single-launch form, at offset 0 of scratch: [0] work-groups
+// arrived (fc1 share done), [1] phase (flipped once per call by the last arrival), [2]
+// error flag (a wait that timed out), [3] unused.  They must be zero before the first
+// call on a scratch buffer; every call leaves [0] zero and [1] at 0 or 1.
 constexpr int64_t kQmoeSyncWords = 4;
 // Single-launch candidates: candidate c runs fc2 with kQmoeFusedR2[c % 2] rows per lane
 // and kQmoeFusedWpc[c / 2] work-groups per compute unit (fewer when they do not fit).
 constexpr int kQmoeFusedR2[] = {1, 2};
 constexpr int kQmoeFusedWpc[] = {1, 2};
 constexpr int kNumQmoeFused = 4;
-// Fill the candidate's parameters; false when the form does not apply (int8 mode).
+// Fill the candidate's parameters; false when the shape does not suit it (LDS, 32-bit
+// offsets).
 bool qmoe_fused_plan(QmoeArgs& a, int candidate);
 // hipErrorNotSupported when the shape does not fit the form (LDS, 32-bit offsets).
 hipError_t launch_qmoe_fused(const QmoeArgs& a, hipStream_t st);

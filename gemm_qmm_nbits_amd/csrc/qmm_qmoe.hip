@@ -157,6 +157,9 @@ __device__ void quantize_groups_lds(LoadFn load, int n, uint32_t* q_lds, float* 
 // consecutive lanes read in different LDS banks (at 16 dwords every fourth lane would
 // share a bank).
 constexpr int kPairStride = 17;
+// cache-policy bit sc1 of a load: device scope (misses the L2, so it sees what other
+// work-groups of the same launch wrote through theirs)
+constexpr int kDeviceCoherent = 16;
 __device__ __forceinline__ void store_pairs(uint32_t* p, uint4 v) {
   p[0] = v.x;
   p[1] = v.y;
@@ -201,8 +204,10 @@ __device__ __forceinline__ void stage_h16(const uint16_t* src, int rows, int n, 
 // The same staging (same values and sums) with the loads of the first batch (NB
 // pieces per thread) issued before `issued` runs: a caller that starts its weight
 // loads there has them travel while the activations are converted, and waiting for
-// the activations, which were issued first, does not wait for them.
-template <typename Issued>
+// the activations, which were issued first, does not wait for them.  Every batch has
+// all its loads in flight at once.  AUX: the loads' cache-policy bits (device-coherent
+// loads for values other work-groups of the same launch wrote).
+template <int AUX = 0, typename Issued>
 __device__ __forceinline__ void stage_h16_first(const uint16_t* src, int rows, int n, int nch, uint32_t* xh,
                                                 float* sa, Issued&& issued) {
   constexpr int NB = 4;
@@ -221,7 +226,7 @@ __device__ __forceinline__ void stage_h16_first(const uint16_t* src, int rows, i
     const int r = pc / per_row;
     const int k0 = 8 * (pc - r * per_row);
     const uint32_t off = okp && k0 < n ? ((uint32_t)r * (uint32_t)n + (uint32_t)k0) * 2u : 0x80000000u;
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0);
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, AUX);
     u = make_uint4(v[0], v[1], v[2], v[3]);
   };
   auto convert = [&](int p, const uint4& u) {
@@ -616,33 +621,6 @@ __global__ __launch_bounds__(kMoeThreads) void qmoe_fc2_kernel(QmoeArgs a) {
   }
 }
 
-// Staging of `rows` fp16 rows of n values each (n % 8 == 0, row stride n) that other
-// work-groups of the same launch wrote: device-coherent 16-byte loads, the same pairs
-// and chunk sums as stage_h16 (xh[r][nch][kPairStride], zero past n; sa[r][nch]).
-__device__ __forceinline__ void stage_h_coherent(const uint16_t* src, int rows, int n, int nch, uint32_t* xh,
-                                                 float* sa) {
-  constexpr int kDeviceCoherent = 16;  // cache-policy bit sc1: device scope
-  const __amdgpu_buffer_rsrc_t r = make_rsrc(src, (uint32_t)rows * (uint32_t)n * 2u);
-  const int per_row = nch * 4;  // pieces of 8 values
-  const int total = rows * per_row;
-  for (int p = threadIdx.x; p < total; p += blockDim.x) {  // quads are all in or all out
-    const int rr = p / per_row;
-    const int pp = p - rr * per_row;
-    const int k0 = 8 * pp;
-    const bool in = k0 < n;  // a piece is wholly inside its row or wholly past it
-    const auto l = __builtin_amdgcn_raw_buffer_load_b128(r, (rr * n + (in ? k0 : 0)) * 2, 0, kDeviceCoherent);
-    const uint4 u = in ? make_uint4(l[0], l[1], l[2], l[3]) : make_uint4(0u, 0u, 0u, 0u);
-    float v[8];
-    h8_to_f32(u, v);
-    store_pairs(xh + ((int64_t)rr * nch + (k0 >> 5)) * kPairStride + ((k0 & 31) >> 1), h8_pairs(u));
-    float s8 = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
-    s8 += dpp_f<kDppXor1>(s8);
-    s8 += dpp_f<kDppXor2>(s8);
-    if ((pp & 3) == 0) sa[rr * nch + (pp >> 2)] = s8;
-  }
-  __syncthreads();
-}
-
 // ---- persistent forms (fp mode) ------------------------------------------------------
 //
 // One work-group per resident slot.  The activations of every token (fc1: x; fc2: the
@@ -658,9 +636,12 @@ __device__ __forceinline__ void stage_h_coherent(const uint16_t* src, int rows, 
 // group or slot) and clamped into [0, E).
 
 // COH: h is written with device-coherent stores (read by other work-groups of the
-// same launch in the single-launch form).
-template <int RI, int ZK, bool COH, bool INT8 = false>
-__device__ __forceinline__ void fc1_stream_body(const QmoeArgs& a, int bid, int nb, uint32_t* smem) {
+// same launch in the single-launch form).  `issued` runs once the activations' loads
+// and the first weight loads are out (the single-launch form issues its fc2 weight
+// copies there).
+template <int RI, int ZK, bool COH, bool INT8, typename Issued>
+__device__ __forceinline__ void fc1_stream_body(const QmoeArgs& a, int bid, int nb, uint32_t* smem,
+                                                Issued&& issued) {
   constexpr int NR = 2 * RI;
   constexpr int NW = kMoeStreamThreads / 64;
   constexpr int D = RI == 1 ? 4 : 3;  // a wave's few items all in flight
@@ -689,7 +670,10 @@ __device__ __forceinline__ void fc1_stream_body(const QmoeArgs& a, int bid, int 
   const int groups_lo = ngroups / nb, extra = ngroups % nb;
   const int g_begin = bid * groups_lo + (bid < extra ? bid : extra);
   const int g_end = g_begin + groups_lo + (bid < extra ? 1 : 0);
-  if (g_begin >= g_end) return;
+  if (g_begin >= g_end) {
+    issued();
+    return;
+  }
   const int wave_groups = g_end - g_begin > wave ? (g_end - g_begin - wave + NW - 1) / NW : 0;
   const int iters = (nch + LPR - 1) >> lpr_log2;
   const int blk_shift = __builtin_ctz((unsigned)a.block) - 5;
@@ -813,20 +797,16 @@ __device__ __forceinline__ void fc1_stream_body(const QmoeArgs& a, int bid, int 
   set_group(fgrp);
   if constexpr (INT8) {
     // every token's x quantized into LDS (work-group 0 keeps a copy in scratch)
+    stage_i8_first<0>(a.X, T * H, xq, xs, xsum, bid == 0 ? a.xq_out : nullptr, bid == 0 ? a.xs_out : nullptr, [&] {
 #pragma unroll
-    for (int i = 0; i < D - 1; ++i) fetch(buf[i]);
-    for (int t = 0; t < T; ++t) {
-      const uint16_t* x = a.X + (size_t)t * H;
-      quantize_groups_lds([&](int i) { return f16_to_f32(x[i]); }, H, xq + (size_t)t * (H / 4),
-                          xs + (size_t)t * (H / 32), xsum + (size_t)t * (H / 32),
-                          bid == 0 ? a.xq_out + (size_t)t * H : nullptr,
-                          bid == 0 ? a.xs_out + (size_t)t * (H / 32) : nullptr);
-    }
-    __syncthreads();
+      for (int i = 0; i < D - 1; ++i) fetch(buf[i]);
+      issued();
+    });
   } else {
     stage_h16_first(a.X, T, (int)a.H, nch, xh, sa, [&] {
 #pragma unroll
       for (int i = 0; i < D - 1; ++i) fetch(buf[i]);
+      issued();
     });
   }
   const int total = wave_groups * iters;
@@ -860,9 +840,113 @@ __device__ __forceinline__ void fc1_stream_body(const QmoeArgs& a, int bid, int 
 template <int RI, int ZK, int INT8>
 __global__ __launch_bounds__(kMoeStreamThreads) void qmoe_fc1_stream_kernel(QmoeArgs a) {
   extern __shared__ uint32_t smem[];
-  fc1_stream_body<RI, ZK, false, INT8 != 0>(a, (int)blockIdx.x, (int)gridDim.x, smem);
+  fc1_stream_body<RI, ZK, false, INT8 != 0>(a, (int)blockIdx.x, (int)gridDim.x, smem, [] {});
 }
 
+
+// fc2 write-out: y = sum_j w_j * (z_j + b2) in slot order, one rounding to fp16, for
+// every row of the work-group's groups [g_begin, g_end) (outs[local row][k]: the row
+// sums z_j without bias).
+__device__ __forceinline__ void fc2_write_out(const QmoeArgs& a, int g_begin, int g_end, int rpg, int GN,
+                                              const float* outs) {
+  __syncthreads();
+  const int k = a.k;
+  const int H = (int)a.H;
+  const int nloc = (g_end - g_begin) * rpg;
+  for (int q = threadIdx.x; q < nloc; q += blockDim.x) {
+    const int grp = g_begin + q / rpg;
+    const int t = grp / GN;
+    const int n = (grp - t * GN) * rpg + (q - (q / rpg) * rpg);
+    if (n >= H) continue;
+    float y = 0.0f;
+    for (int j = 0; j < k; ++j) {
+      const int e = clamp_expert(a.ids[t * k + j], a.E);
+      const float z = outs[q * k + j] + (a.fc2.bias ? f16_to_f32(a.fc2.bias[(int64_t)e * a.H + n]) : 0.0f);
+      y = fmaf(a.rw[t * k + j], z, y);
+    }
+    a.Y[(int64_t)t * a.H + n] = f32_to_f16(y);
+  }
+}
+
+// int8 staging of the n fp16 values at src (n % 32 == 0, 16-byte aligned; rows back to
+// back, each a multiple of 32 values): 16-byte loads of 8 values per lane, so the 4
+// lanes of a quad hold one 32-value group, NB per thread in flight at once; the group
+// is quantized as the oracle's quantizer does it (amax over the 32 values, codes
+// rint(v * fp32(127/amax)) clamped to +-127, scale fp32(amax/127); all zero when amax
+// is 0), the codes go to LDS permuted per 8 as [0 2 4 6 | 1 3 5 7], with the scale and
+// the code sum per group.  q_out / s_out (may be null): the codes in natural order and
+// the scales, in memory.  The first batch's loads are issued before `issued` runs (as
+// in stage_h16_first).  AUX: the loads' cache-policy bits.
+template <int AUX, typename Issued>
+__device__ __forceinline__ void stage_i8_first(const uint16_t* src, int n, uint32_t* q_lds, float* s_lds,
+                                               int* sum_lds, int8_t* q_out, float* s_out, Issued&& issued) {
+  constexpr int NB = 4;
+  const int total = n / 8;  // pieces of 8 values, a multiple of 4: quads are all in or all out
+  const int wave_base = __builtin_amdgcn_readfirstlane((int)(threadIdx.x & ~63u));
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, (uint32_t)n * 2u);
+  auto load = [&](int p, uint4& u) {
+    const uint32_t off = p < total ? (uint32_t)p * 16u : 0x80000000u;  // past the range: 0, no data
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, AUX);
+    u = make_uint4(v[0], v[1], v[2], v[3]);
+  };
+  auto pack = [](int a0, int a1, int a2, int a3) {
+    return (uint32_t)(a0 & 0xff) | ((uint32_t)(a1 & 0xff) << 8) | ((uint32_t)(a2 & 0xff) << 16) |
+           ((uint32_t)(a3 & 0xff) << 24);
+  };
+  auto convert = [&](int p, const uint4& u) {
+    float v[8];
+    h8_to_f32(u, v);
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    amax = fmaxf(amax, dpp_f<kDppXor1>(amax));
+    amax = fmaxf(amax, dpp_f<kDppXor2>(amax));
+    int q[8];
+    float sc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = 0;
+    if (amax > 0.0f) {
+      const float inv = 127.0f / amax;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int c = (int)rintf(__fmul_rn(v[i], inv));
+        q[i] = c > 127 ? 127 : (c < -127 ? -127 : c);
+      }
+      sc = amax / 127.0f;
+    }
+    int sum = ((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7]));
+    sum += __float_as_int(dpp_f<kDppXor1>(__int_as_float(sum)));
+    sum += __float_as_int(dpp_f<kDppXor2>(__int_as_float(sum)));
+    if (p < total) {
+      const int g = p >> 2, m = p & 3;
+      q_lds[g * 8 + 2 * m] = pack(q[0], q[2], q[4], q[6]);
+      q_lds[g * 8 + 2 * m + 1] = pack(q[1], q[3], q[5], q[7]);
+      if (m == 0) {
+        s_lds[g] = sc;
+        sum_lds[g] = sum;
+      }
+      if (q_out) {
+        *(uint2*)(q_out + (int64_t)p * 8) = make_uint2(pack(q[0], q[1], q[2], q[3]), pack(q[4], q[5], q[6], q[7]));
+        if (m == 0) s_out[g] = sc;
+      }
+    }
+  };
+  auto batch = [&](int base, auto first) {
+    uint4 vb[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) load(base + j * (int)blockDim.x + (int)threadIdx.x, vb[j]);
+    if constexpr (decltype(first)::value) {
+      __builtin_amdgcn_sched_barrier(0);  // keep the caller's loads behind these
+      issued();
+    }
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+      if (base + j * (int)blockDim.x + wave_base < total) convert(base + j * (int)blockDim.x + (int)threadIdx.x, vb[j]);
+  };
+  batch(0, std::true_type{});
+  for (int base = NB * (int)blockDim.x; base < total; base += NB * (int)blockDim.x) batch(base, std::false_type{});
+  __syncthreads();
+}
 
 // FUSED: h was written earlier in the same launch by other work-groups: the first
 // weight loads are issued, then `wait()` (every work-group's h is complete), then h is
@@ -1024,16 +1108,20 @@ __device__ __forceinline__ void fc2_stream_body(const QmoeArgs& a, int bid, int 
   // the activations are converted
   MoeItem<R> buf[D];
   set_unit(fu);
-  if constexpr (INT8) {
+  if constexpr (FUSED) {
+#pragma unroll
+    for (int i = 0; i < D - 1; ++i) fetch(buf[i]);
+    wait();
+    if constexpr (INT8)
+      stage_i8_first<kDeviceCoherent>(a.h, T * k * I, hq, hs, hsum, bid == 0 ? a.hq_out : nullptr,
+                                      bid == 0 ? a.hs_out : nullptr, [] {});
+    else
+      stage_h16_first<kDeviceCoherent>(a.h, T * k, (int)a.I, nch, hh, sa, [] {});
+  } else if constexpr (INT8) {
     // the codes and scales of every slot's h (quantized once per call into scratch)
 #pragma unroll
     for (int i = 0; i < D - 1; ++i) fetch(buf[i]);
     stage_i8(a.hq_out, a.hs_out, T * k * I, hq, hs, hsum);
-  } else if constexpr (FUSED) {
-#pragma unroll
-    for (int i = 0; i < D - 1; ++i) fetch(buf[i]);
-    wait();
-    stage_h_coherent(a.h, T * k, (int)a.I, nch, hh, sa);
   } else {
     stage_h16_first(a.h, T * k, (int)a.I, nch, hh, sa, [&] {
 #pragma unroll
@@ -1045,22 +1133,7 @@ __device__ __forceinline__ void fc2_stream_body(const QmoeArgs& a, int bid, int 
 #pragma unroll
     for (int i = 0; i < D; ++i) step(buf[i], buf[(i + D - 1) % D], base + i < total);
   }
-  __syncthreads();
-  // y = sum_j w_j * (z_j + b2) in slot order, one rounding to fp16
-  const int nloc = (g_end - g_begin) * rpg;
-  for (int q = threadIdx.x; q < nloc; q += blockDim.x) {
-    const int grp = g_begin + q / rpg;
-    const int t = grp / GN;
-    const int n = (grp - t * GN) * rpg + (q - (q / rpg) * rpg);
-    if (n >= H) continue;
-    float y = 0.0f;
-    for (int j = 0; j < k; ++j) {
-      const int e = clamp_expert(a.ids[t * k + j], a.E);
-      const float z = outs[q * k + j] + (a.fc2.bias ? f16_to_f32(a.fc2.bias[(int64_t)e * a.H + n]) : 0.0f);
-      y = fmaf(a.rw[t * k + j], z, y);
-    }
-    a.Y[(int64_t)t * a.H + n] = f32_to_f16(y);
-  }
+  fc2_write_out(a, g_begin, g_end, rpg, GN, outs);
 }
 
 template <int R, int ZK, int INT8>
@@ -1330,36 +1403,40 @@ __global__ __launch_bounds__(kMoeStreamThreads) void qmoe_fc1_dedupe_kernel(Qmoe
   }
 }
 
-// ---- single-launch form (fp mode) ------------------------------------------------------
+// ---- single-launch form ------------------------------------------------------------
 //
 // fc1, SwiGLU, fc2 and the combine in one launch of the persistent forms above: one
 // grid of work-groups, all resident at once (the grid is the occupancy of this kernel
 // times the compute units).  Each work-group runs its even share of the fc1 row
 // groups, writes its h rows with device-coherent stores, waits for them to complete
 // and counts itself arrived.  It then issues the first weight loads of its fc2 share,
-// waits until every work-group has arrived, stages h with device-coherent loads and
-// runs its fc2 share (all k slots of its rows, combined in slot order).  The per-row
-// arithmetic is that of the two-kernel forms, so every form gives the same bits.  The
-// last work-group to leave returns the counters to zero for the next call.
+// waits until every work-group has arrived, stages h with device-coherent loads (int8
+// mode: and quantizes it) and runs its fc2 share (all k slots of its rows, combined in
+// slot order).  The per-row arithmetic is that of the two-kernel forms, so every form
+// gives the same bits.
+//
+// The wait is sense-reversing: each work-group reads the phase word when it starts; the
+// arrival add returns the count before it, so the last work-group to arrive knows it is
+// last, returns the count to zero and flips the phase, and the others wait for the
+// phase to change.  Nothing is left to do at exit, and the next call finds the count at
+// zero.
 //
 // Ordering across the XCDs (each with its own L2) without whole-cache operations: the
 // h stores are agent-scope atomic stores, which write through the L2; the work-group
 // waits until every one of them is acknowledged (s_waitcnt) before its agent-scope
-// arrival add, so an arrival count that includes it implies its h is in memory.  A
-// waiting work-group reads the count with agent-scope loads (which miss the L2) and
-// only after it has seen every arrival issues its h loads, which are device-coherent
-// (they also miss the L2) and are ordered after the poll by the work-group barrier.  A
-// release/acquire pair would add an L2 write-back per arrival and an L2 invalidation
-// per waiter, several microseconds per call, to order data that never enters the L2.
+// arrival add, so a count that includes it implies its h is in memory, and the last
+// arrival's add returns only once every earlier add is performed.  A waiting
+// work-group reads the phase with agent-scope loads (which miss the L2) and only after
+// it has seen the flip issues its h loads, which are device-coherent (they also miss
+// the L2) and are ordered after the poll by the work-group barrier.  A release/acquire
+// pair would add an L2 write-back per arrival and an L2 invalidation per waiter,
+// several microseconds per call, to order data that never enters the L2.
 
 // a wait gives up after 1 s of the 100 MHz real-time counter and raises the error word
 constexpr uint64_t kSpinLimitTicks = 100000000ull;
 
-__device__ __forceinline__ uint32_t sync_add(uint32_t* p, uint32_t v) {
-  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 // arrival: the caller has waited for every h store of the work-group (write-through
-// agent-scope stores) to be acknowledged
+// agent-scope stores) to be acknowledged; returns the count before this arrival
 __device__ __forceinline__ uint32_t sync_arrive(uint32_t* p) {
   return __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -1370,7 +1447,7 @@ __device__ __forceinline__ void sync_store(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int RI, int R, int ZK1, int ZK2>
+template <int RI, int R, int ZK1, int ZK2, int INT8>
 __global__ __launch_bounds__(kMoeStreamThreads) void qmoe_fused_kernel(QmoeArgs a) {
   extern __shared__ uint32_t smem[];
   __shared__ uint32_t gave_up;
@@ -1378,15 +1455,23 @@ __global__ __launch_bounds__(kMoeStreamThreads) void qmoe_fused_kernel(QmoeArgs 
   const int nb = (int)gridDim.x;
   const int bid = (int)blockIdx.x;
   if (threadIdx.x == 0) gave_up = 0u;
-  fc1_stream_body<RI, ZK1, true>(a, bid, nb, smem);
-  // every wave's h stores have completed before the work-group counts itself arrived
+  // the phase before this call (the flip needs every work-group's arrival, this one's too)
+  const uint32_t phase = threadIdx.x == 0 ? sync_load(&sync[1]) : 0u;
+  fc1_stream_body<RI, ZK1, true, INT8 != 0>(a, bid, nb, smem, [] {});
+  // every wave's h stores (and the phase load) have completed before the work-group
+  // counts itself arrived
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (threadIdx.x == 0) (void)sync_arrive(&sync[0]);
+  bool last = false;
+  if (threadIdx.x == 0 && sync_arrive(&sync[0]) == (uint32_t)nb - 1u) {
+    last = true;
+    sync_store(&sync[0], 0u);
+    sync_store(&sync[1], phase ^ 1u);
+  }
   auto wait = [&] {
-    if (threadIdx.x == 0) {
+    if (threadIdx.x == 0 && !last) {
       const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-      while (sync_load(&sync[0]) < (uint32_t)nb) {
+      while (sync_load(&sync[1]) == phase) {
         __builtin_amdgcn_s_sleep(2);
         if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinLimitTicks) {
           sync_store(&sync[2], 1u);
@@ -1397,16 +1482,12 @@ __global__ __launch_bounds__(kMoeStreamThreads) void qmoe_fused_kernel(QmoeArgs 
     }
     __syncthreads();
   };
-  fc2_stream_body<R, ZK2, true>(a, bid, nb, smem, wait);
+  fc2_stream_body<R, ZK2, true, decltype(wait)&, INT8 != 0>(a, bid, nb, smem, wait);
   __syncthreads();
   if (gave_up) {
     // a wait that gave up leaves the output invalid: it is filled with fp16 NaN (after
     // this work-group's own rows were written, so those rows are NaN at the end)
     for (int64_t i = threadIdx.x; i < a.T * a.H; i += kMoeStreamThreads) a.Y[i] = 0x7E00u;
-  }
-  if (threadIdx.x == 0 && sync_add(&sync[1], 1u) == (uint32_t)nb - 1u) {
-    sync_store(&sync[0], 0u);
-    sync_store(&sync[1], 0u);
   }
 }
 
@@ -1510,32 +1591,39 @@ static bool launch_fc2_stream(const QmoeArgs& a, int cap, hipStream_t st) {
 }
 
 
-template <int RI, int R, int ZK1, int ZK2>
-static bool launch_fused(const QmoeArgs& a, hipStream_t st) {
-  auto kern = qmoe_fused_kernel<RI, R, ZK1, ZK2>;
-  // one expert's weights, scales and zero points are addressed with 32-bit offsets
+// LDS of the single-launch form at `grid` work-groups: the larger of the fc1 and fc2
+// phases' staged activations and row sums.  0 when the shape does not suit the form
+// (32-bit offsets).
+static size_t fused_lds(const QmoeArgs& a, int R2, int64_t grid) {
+  const bool i8 = a.mode == QMOE_INT8_ACT;
   const int64_t r1 = 2 * a.I, r2 = a.H;
-  if (r1 * a.fc1_row_bytes >= (1LL << 31) || r1 * a.fc1_nblk * 2 >= (1LL << 31)) return false;
-  if (r2 * a.fc2_row_bytes >= (1LL << 31) || r2 * a.fc2_nblk * 2 >= (1LL << 31)) return false;
-  const int64_t rpg1 = (64 >> a.fc1_lpr_log2) * RI, rpg2 = (64 >> a.fc2_lpr_log2) * R;
+  // one expert's weights, scales and zero points are addressed with 32-bit offsets
+  if (r1 * a.fc1_row_bytes >= (1LL << 31) || r1 * a.fc1_nblk * 2 >= (1LL << 31)) return 0;
+  if (r2 * a.fc2_row_bytes >= (1LL << 31) || r2 * a.fc2_nblk * 2 >= (1LL << 31)) return 0;
+  const int64_t rpg1 = (64 >> a.fc1_lpr_log2) * 2, rpg2 = (64 >> a.fc2_lpr_log2) * R2;
   const int64_t ng1 = a.T * a.k * ((a.I + rpg1 - 1) / rpg1), ng2 = a.T * ((a.H + rpg2 - 1) / rpg2);
-  const size_t fixed1 = (size_t)a.T * a.fc1_chunks * kStagedWords * sizeof(uint32_t);
-  const size_t fixed2 = (size_t)a.T * a.k * a.fc2_chunks * kStagedWords * sizeof(uint32_t);
-  const size_t pg1 = (size_t)rpg1 * 2 * sizeof(float), pg2 = (size_t)rpg2 * a.k * sizeof(float);
-  constexpr size_t kMaxLds = 150 * 1024;
-  auto lds_for = [&](int64_t grid) {
-    const size_t l1 = fixed1 + (size_t)((ng1 + grid - 1) / grid) * pg1;
-    const size_t l2 = fixed2 + (size_t)((ng2 + grid - 1) / grid) * pg2;
-    return l1 > l2 ? l1 : l2;
-  };
+  const size_t fixed1 = i8 ? (size_t)a.T * ((size_t)a.H + (size_t)(a.H / 32) * 8)
+                           : (size_t)a.T * a.fc1_chunks * kStagedWords * sizeof(uint32_t);
+  const size_t fixed2 = i8 ? (size_t)a.T * a.k * ((size_t)a.I + (size_t)(a.I / 32) * 8)
+                           : (size_t)a.T * a.k * a.fc2_chunks * kStagedWords * sizeof(uint32_t);
+  const size_t l1 = fixed1 + (size_t)((ng1 + grid - 1) / grid) * rpg1 * 2 * sizeof(float);
+  const size_t l2 = fixed2 + (size_t)((ng2 + grid - 1) / grid) * rpg2 * a.k * sizeof(float);
+  return l1 > l2 ? l1 : l2;
+}
+
+constexpr size_t kMaxFusedLds = 150 * 1024;
+
+template <int RI, int R, int ZK1, int ZK2, int INT8>
+static bool launch_fused(const QmoeArgs& a, hipStream_t st) {
+  auto kern = qmoe_fused_kernel<RI, R, ZK1, ZK2, INT8>;
   const int cus = a.num_cus > 0 ? a.num_cus : 256;
   // every work-group of the grid must be resident at once: the grid never exceeds the
   // occupancy of the kernel with the LDS it is launched with
   int per_cu = a.f_wpc;
   size_t lds = 0;
   for (; per_cu >= 1; --per_cu) {
-    lds = lds_for((int64_t)cus * per_cu);
-    if (lds > kMaxLds) return false;
+    lds = fused_lds(a, R, (int64_t)cus * per_cu);
+    if (lds == 0 || lds > kMaxFusedLds) return false;
     if (moe_resident_per_cu(kern, lds) >= per_cu) break;
   }
   if (per_cu < 1) return false;
@@ -1566,31 +1654,27 @@ static bool launch_fc1_dedupe(const QmoeArgs& a, hipStream_t st) {
 }
 
 bool qmoe_fused_plan(QmoeArgs& a, int candidate) {
-  if (a.mode != QMOE_FP || candidate < 0 || candidate >= kNumQmoeFused) return false;
+  if (candidate < 0 || candidate >= kNumQmoeFused) return false;
   a.f_r2 = kQmoeFusedR2[candidate % 2];
   a.f_wpc = kQmoeFusedWpc[candidate / 2];
-  // the same limits launch_fused applies, at one work-group per compute unit (the most
-  // LDS per work-group)
-  const int64_t r1 = 2 * a.I, r2 = a.H;
-  if (r1 * a.fc1_row_bytes >= (1LL << 31) || r1 * a.fc1_nblk * 2 >= (1LL << 31)) return false;
-  if (r2 * a.fc2_row_bytes >= (1LL << 31) || r2 * a.fc2_nblk * 2 >= (1LL << 31)) return false;
-  const int64_t rpg1 = (64 >> a.fc1_lpr_log2) * 2, rpg2 = (64 >> a.fc2_lpr_log2) * a.f_r2;
-  const int64_t grid = a.num_cus > 0 ? a.num_cus : 256;
-  const int64_t ng1 = a.T * a.k * ((a.I + rpg1 - 1) / rpg1), ng2 = a.T * ((a.H + rpg2 - 1) / rpg2);
-  const int64_t l1 = a.T * a.fc1_chunks * kStagedWords * 4 + ((ng1 + grid - 1) / grid) * rpg1 * 2 * 4;
-  const int64_t l2 = a.T * a.k * a.fc2_chunks * kStagedWords * 4 + ((ng2 + grid - 1) / grid) * rpg2 * a.k * 4;
-  return (l1 > l2 ? l1 : l2) <= 150 * 1024;
+  // the limits launch_fused applies, at one work-group per compute unit (the most LDS
+  // per work-group)
+  const size_t lds = fused_lds(a, a.f_r2, a.num_cus > 0 ? a.num_cus : 256);
+  return lds != 0 && lds <= kMaxFusedLds;
+}
+
+template <int INT8>
+static bool launch_fused_zk(const QmoeArgs& a, hipStream_t st) {
+  const bool z1 = a.fc1.zp != nullptr, z2 = a.fc2.zp != nullptr;
+  if (a.f_r2 == 1)
+    return z1 ? (z2 ? launch_fused<2, 1, 1, 1, INT8>(a, st) : launch_fused<2, 1, 1, 0, INT8>(a, st))
+              : (z2 ? launch_fused<2, 1, 0, 1, INT8>(a, st) : launch_fused<2, 1, 0, 0, INT8>(a, st));
+  return z1 ? (z2 ? launch_fused<2, 2, 1, 1, INT8>(a, st) : launch_fused<2, 2, 1, 0, INT8>(a, st))
+            : (z2 ? launch_fused<2, 2, 0, 1, INT8>(a, st) : launch_fused<2, 2, 0, 0, INT8>(a, st));
 }
 
 hipError_t launch_qmoe_fused(const QmoeArgs& a, hipStream_t st) {
-  const bool z1 = a.fc1.zp != nullptr, z2 = a.fc2.zp != nullptr;
-  bool done;
-  if (a.f_r2 == 1)
-    done = z1 ? (z2 ? launch_fused<2, 1, 1, 1>(a, st) : launch_fused<2, 1, 1, 0>(a, st))
-              : (z2 ? launch_fused<2, 1, 0, 1>(a, st) : launch_fused<2, 1, 0, 0>(a, st));
-  else
-    done = z1 ? (z2 ? launch_fused<2, 2, 1, 1>(a, st) : launch_fused<2, 2, 1, 0>(a, st))
-              : (z2 ? launch_fused<2, 2, 0, 1>(a, st) : launch_fused<2, 2, 0, 0>(a, st));
+  const bool done = a.mode == QMOE_INT8_ACT ? launch_fused_zk<1>(a, st) : launch_fused_zk<0>(a, st);
   return done ? hipSuccess : hipErrorNotSupported;
 }
 

@@ -237,27 +237,28 @@ qmm_status qmm_dequantize_codebook4(const uint8_t* W, int block, const float* ab
  *   bits       4.  block in {32, 64, 128, 256} (int8 mode additionally needs
  *              H % 32 == 0 and I % 32 == 0).
  *   scratch    device buffer of at least qmoe_decode_scratch_bytes(T, H, I, k, mode),
- *              256-byte aligned.  Layout: fp16 h [T][k][I] at offset 0, then (each
- *              region at the next 256-byte boundary) in fp mode four uint32 sync
- *              words of the single-launch form; in int8 mode int8 x codes [T][H],
- *              fp32 x scales [T][H/32], int8 h codes [T][k][I], fp32 h scales
- *              [T][k][I/32].  The sync words must be zero before the first call on a
- *              buffer (zero the whole buffer once, e.g. hipMemset); every call leaves
- *              the first two zero again.  The third is an error flag that a call
- *              sets, and leaves set, if its wait inside the launch gave up after 1 s
- *              (its output is then invalid).  Calls that share a scratch buffer must
- *              not overlap.
- *   Launches   fp mode: two kernels (fc1 + SwiGLU, then fc2 + combine), or one launch
- *              of both: a grid that is resident all at once (its size is the
- *              kernel's occupancy times the compute units) runs its fc1 share,
- *              publishes h, issues its first fc2 weight loads, waits for every
- *              work-group's h and runs its fc2 share.  The up-front timing picks the
- *              faster form per shape.  The one-launch form needs the compute units
- *              to itself for that wait: a kernel on another stream that holds them
- *              for more than 1 s makes the wait give up (error flag above; the
- *              call's Y is then filled with fp16 NaN and qmoe_decode_status reports
- *              it).  int8 mode: fc1, the h quantizer and fc2 as three launches.  Every form
- *              gives the same bits.
+ *              256-byte aligned.  Layout (each region at a 256-byte boundary): four
+ *              uint32 sync words of the single-launch form at offset 0 (the same place
+ *              for every shape and mode), fp16 h [T][k][I] at offset 256, then in int8
+ *              mode int8 x codes [T][H], fp32 x scales [T][H/32], int8 h codes
+ *              [T][k][I], fp32 h scales [T][k][I/32].  The sync words must be zero
+ *              before the first call on a buffer (zero the whole buffer once, e.g.
+ *              hipMemset); every call leaves the first zero again and the second (a
+ *              phase) at 0 or 1.  The third is an error flag that a call sets, and leaves set, if its wait inside the
+ *              launch gave up after 1 s (its output is then invalid).  Calls that share
+ *              a scratch buffer must not overlap.
+ *   Launches   two kernels (fc1 + SwiGLU, then fc2 + combine; int8 mode adds the h
+ *              quantizer between them), or one launch of all of it: a grid that is
+ *              resident all at once (its size is the kernel's occupancy times the
+ *              compute units) runs its fc1 share, publishes h, waits for every
+ *              work-group's h and runs its fc2 share, whose weights it either streams
+ *              after the wait (first loads issued before it) or has copied into LDS
+ *              while fc1 ran (int8 mode: each work-group quantizes h itself).  The
+ *              up-front timing picks the faster form per shape.  The one-launch form
+ *              needs the compute units to itself for that wait: a kernel on another
+ *              stream that holds them for more than 1 s makes the wait give up (error
+ *              flag above; the call's Y is then filled with fp16 NaN and
+ *              qmoe_decode_status reports it).  Every form gives the same bits.
  *   E          num_experts: the first call of a shape times tiling candidates on
  *              other expert sets, writing only scratch.
  * ------------------------------------------------------------------------- */
@@ -319,7 +320,7 @@ qmm_status qmoe_decode_fused_noalloc(const uint16_t* X, int64_t T, int64_t H, in
  * cause, nor hide one it did).  Reads the error word of the scratch layout above into
  * *timed_out (HOST pointer: 1 = some call gave up, its Y was filled with fp16 NaN;
  * 0 = none), then clears it.  T, H, I, k, mode: those of the calls made on the buffer.
- * Synchronizes `stream`; int8 mode never waits and always reports 0.  Returns
+ * Synchronizes `stream`.  Returns
  * QMM_E_NULL / QMM_E_WORKSPACE / QMM_E_ALIGN for a missing, short or misaligned buffer,
  * or the hipError_t of the copy. */
 qmm_status qmoe_decode_status(void* scratch, size_t scratch_bytes, int64_t T, int64_t H, int64_t I,

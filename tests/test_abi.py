@@ -194,11 +194,11 @@ def test_scratch_queries():
     fp = L.qmoe_decode_scratch_bytes(1, 2880, 2880, 4, Q.QMOE_FP)
     i8 = L.qmoe_decode_scratch_bytes(1, 2880, 2880, 4, Q.QMOE_INT8_ACT)
     a256 = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    # fp: h fp16 [T][k][I], then the four sync words of the single-launch form
-    assert fp == a256(4 * 2880 * 2) + a256(16)
-    # int8: h, then x codes, x scales, h codes, h scales
-    assert i8 == a256(4 * 2880 * 2) + a256(2880) + a256(90 * 4) + a256(4 * 2880) + a256(4 * 90 * 4)
-    assert L.qmoe_decode_scratch_bytes(8, 2048, 768, 8, Q.QMOE_FP) == a256(64 * 768 * 2) + a256(16)
+    # fp: the four sync words of the single-launch form, then h fp16 [T][k][I]
+    assert fp == a256(16) + a256(4 * 2880 * 2)
+    # int8: sync words, h, then x codes, x scales, h codes, h scales
+    assert i8 == a256(16) + a256(4 * 2880 * 2) + a256(2880) + a256(90 * 4) + a256(4 * 2880) + a256(4 * 90 * 4)
+    assert L.qmoe_decode_scratch_bytes(8, 2048, 768, 8, Q.QMOE_FP) == a256(16) + a256(64 * 768 * 2)
 
 
 def test_decode_status_refusals():
@@ -210,8 +210,11 @@ def test_decode_status_refusals():
     assert L.qmoe_decode_status(None, 1 << 20, 1, 2880, 2880, 4, Q.QMOE_FP, ctypes.byref(flag), None) == -1
     assert L.qmoe_decode_status(FAKE, 16, 1, 2880, 2880, 4, Q.QMOE_FP, ctypes.byref(flag), None) == -7
     assert L.qmoe_decode_status(FAKE + 16, 1 << 20, 1, 2880, 2880, 4, Q.QMOE_FP, ctypes.byref(flag), None) == -6
-    # int8 mode never waits: 0 without touching the buffer
-    assert L.qmoe_decode_status(None, 0, 1, 2880, 2880, 4, Q.QMOE_INT8_ACT, ctypes.byref(flag), None) == 0
+    # int8 mode has a single-launch form too: the same checks
+    assert L.qmoe_decode_status(None, 1 << 20, 1, 2880, 2880, 4, Q.QMOE_INT8_ACT, ctypes.byref(flag), None) == -1
+    assert L.qmoe_decode_status(FAKE, 16, 1, 2880, 2880, 4, Q.QMOE_INT8_ACT, ctypes.byref(flag), None) == -7
+    # T = 0: nothing ran, 0 without touching the buffer
+    assert L.qmoe_decode_status(None, 0, 0, 2880, 2880, 4, Q.QMOE_INT8_ACT, ctypes.byref(flag), None) == 0
     assert flag.value == 0
 
 

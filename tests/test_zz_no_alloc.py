@@ -42,6 +42,37 @@ def test_noalloc_equals_allocating_entry(mode):
         assert np.array_equal(host_bits(y2), host_bits(ref))
 
 
+@pytest.mark.parametrize("mode", [Q.QMOE_FP, Q.QMOE_INT8_ACT], ids=["fp", "int8"])
+def test_noalloc_single_launch_across_shapes(mode):
+    """The single-launch form (forced) on the static scratch, alternating a larger and a
+    smaller shape: every call finds its arrival count at zero (the sync words sit at the
+    same place for every shape, never under another shape's h or codes) and matches the
+    allocating entry."""
+    t = torch()
+    n1 = Q.num_candidates(Q.ENTRY_QMOE_FC1) * Q.num_candidates(Q.ENTRY_QMOE_FC2)
+    shapes = ((4, 2048, 768, 128, 8, 64), (1, 1024, 512, 16, 4, 32))
+    probs = []
+    for T, H, I, E, k, block in shapes:
+        p = gen.qmoe_problem(T, H, I, E, k, block, seed=980 + T + mode, zp=True, bias=True)
+        probs.append(((T, H, I, E, k, block), _dev_problem(p)))
+    Q.set_tuning(2, n1 + 1)   # single-launch candidate 1: fc2 streamed, one work-group per CU
+    try:
+        refs = []
+        for (T, H, I, E, k, block), (X, ids, rw, fc) in probs:
+            refs.append(host_bits(Q.qmoe_decode_fused(X, ids, rw, fc["fc1"], fc["fc2"], H, I, E, block,
+                                                      mode=mode)).copy())
+            assert Q.tuned_choice(Q.ENTRY_QMOE_FUSED) == 1
+        for rep in range(3):
+            for i, ((T, H, I, E, k, block), (X, ids, rw, fc)) in enumerate(probs):
+                say(f"noalloc single launch mode={mode} rep={rep} T={T} H={H}")
+                out = t.full((T, H), float("nan"), dtype=t.float16, device="cuda")
+                y = Q.qmoe_decode_fused_noalloc(X, ids, rw, fc["fc1"], fc["fc2"], H, I, E, block, out, mode=mode)
+                assert Q.tuned_choice(Q.ENTRY_QMOE_FUSED) == 1
+                assert np.array_equal(host_bits(y), refs[i]), (rep, i)
+    finally:
+        Q.set_tuning(0, 0)
+
+
 def test_noalloc_refuses_scratch_beyond_the_array():
     """A shape whose scratch exceeds the static array is refused before any launch."""
     t = torch()
