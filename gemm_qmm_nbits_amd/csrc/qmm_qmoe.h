@@ -35,11 +35,16 @@ struct QmoeArgs {
   int f_wpc;
   uint32_t* sync;
 };
-// Sync words of the single-launch form, at offset 0 of scratch: [0] work-groups
-// arrived (fc1 share done), [1] phase (flipped once per call by the last arrival), [2]
-// error flag (a wait that timed out), [3] unused.  They must be zero before the first
-// call on a scratch buffer; every call leaves [0] zero and [1] at 0 or 1.
-constexpr int64_t kQmoeSyncWords = 4;
+// Sync words of the single-launch form, at offset 0 of scratch, in slots of 256 bytes:
+// slot 0 holds [0] the top arrival count (slots complete), [1] unused, [2] the error
+// flag (a wait that timed out), [3] unused; slots 1 .. kQmoeSyncSubs hold [0] a
+// sub-counter (work-groups b with b % kQmoeSyncSubs == slot - 1 arrived) and [1] a
+// copy of the phase (flipped once per call by the last arrival).  All must be zero
+// before the first call on a scratch buffer; every call leaves the counters zero and
+// the phases equal, at 0 or 1.
+constexpr int kQmoeSyncSubs = 32;
+constexpr int kQmoeSyncSlotWords = 64;
+constexpr int64_t kQmoeSyncWords = (1 + kQmoeSyncSubs) * kQmoeSyncSlotWords;
 // Single-launch candidates: candidate c runs fc2 with kQmoeFusedR2[c % 2] rows per lane
 // and kQmoeFusedWpc[c / 2] work-groups per compute unit (fewer when they do not fit).
 constexpr int kQmoeFusedR2[] = {1, 2};

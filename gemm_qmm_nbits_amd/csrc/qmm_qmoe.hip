@@ -1415,17 +1415,22 @@ __global__ __launch_bounds__(kMoeStreamThreads) void qmoe_fc1_dedupe_kernel(Qmoe
 // slot order).  The per-row arithmetic is that of the two-kernel forms, so every form
 // gives the same bits.
 //
-// The wait is sense-reversing: each work-group reads the phase word when it starts; the
-// arrival add returns the count before it, so the last work-group to arrive knows it is
-// last, returns the count to zero and flips the phase, and the others wait for the
-// phase to change.  Nothing is left to do at exit, and the next call finds the count at
-// zero.
+// The wait is sense-reversing and counts in two levels, spread over slots of 256 bytes
+// so that arrivals and polls do not queue on one address: work-group b belongs to slot
+// 1 + b % kQmoeSyncSubs, which holds a sub-counter and a copy of the phase.  Each
+// work-group reads its slot's phase when it starts and adds its arrival to its slot's
+// sub-counter; the add returns the count before it, so the last arrival of a slot knows
+// it is last, returns the sub-counter to zero and adds one to the top counter (slot 0);
+// the last of those returns the top counter to zero and flips every slot's phase, and
+// every other work-group waits for its slot's phase to change.  Nothing is left to do
+// at exit, and the next call finds every counter at zero and every phase equal.
 //
 // Ordering across the XCDs (each with its own L2) without whole-cache operations: the
 // h stores are agent-scope atomic stores, which write through the L2; the work-group
 // waits until every one of them is acknowledged (s_waitcnt) before its agent-scope
-// arrival add, so a count that includes it implies its h is in memory, and the last
-// arrival's add returns only once every earlier add is performed.  A waiting
+// arrival add, so a count that includes it implies its h is in memory; a counter's
+// last add returns only once every earlier add to it is performed, and the top add of
+// a sub-counter's last arrival is issued only after its sub-counter add returned.  A waiting
 // work-group reads the phase with agent-scope loads (which miss the L2) and only after
 // it has seen the flip issues its h loads, which are device-coherent (they also miss
 // the L2) and are ordered after the poll by the work-group barrier.  A release/acquire
@@ -1455,23 +1460,33 @@ __global__ __launch_bounds__(kMoeStreamThreads) void qmoe_fused_kernel(QmoeArgs 
   const int nb = (int)gridDim.x;
   const int bid = (int)blockIdx.x;
   if (threadIdx.x == 0) gave_up = 0u;
-  // the phase before this call (the flip needs every work-group's arrival, this one's too)
-  const uint32_t phase = threadIdx.x == 0 ? sync_load(&sync[1]) : 0u;
+  // this work-group's sync slot and the phase before this call (the flip needs every
+  // work-group's arrival, this one's too)
+  uint32_t* slot = sync + (size_t)(1 + bid % kQmoeSyncSubs) * kQmoeSyncSlotWords;
+  const uint32_t phase = threadIdx.x == 0 ? sync_load(&slot[1]) : 0u;
   fc1_stream_body<RI, ZK1, true, INT8 != 0>(a, bid, nb, smem, [] {});
   // every wave's h stores (and the phase load) have completed before the work-group
   // counts itself arrived
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   bool last = false;
-  if (threadIdx.x == 0 && sync_arrive(&sync[0]) == (uint32_t)nb - 1u) {
-    last = true;
-    sync_store(&sync[0], 0u);
-    sync_store(&sync[1], phase ^ 1u);
+  if (threadIdx.x == 0) {
+    const int sub = bid % kQmoeSyncSubs;
+    const int nsub = nb < kQmoeSyncSubs ? nb : kQmoeSyncSubs;  // slots in use
+    const uint32_t in_sub = (uint32_t)(nb / kQmoeSyncSubs + (sub < nb % kQmoeSyncSubs ? 1 : 0));
+    if (sync_arrive(&slot[0]) == in_sub - 1u) {
+      sync_store(&slot[0], 0u);
+      if (sync_arrive(&sync[0]) == (uint32_t)nsub - 1u) {
+        last = true;
+        sync_store(&sync[0], 0u);
+        for (int i = 1; i <= kQmoeSyncSubs; ++i) sync_store(&sync[(size_t)i * kQmoeSyncSlotWords + 1], phase ^ 1u);
+      }
+    }
   }
   auto wait = [&] {
     if (threadIdx.x == 0 && !last) {
       const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-      while (sync_load(&sync[1]) == phase) {
+      while (sync_load(&slot[1]) == phase) {
         __builtin_amdgcn_s_sleep(2);
         if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinLimitTicks) {
           sync_store(&sync[2], 1u);

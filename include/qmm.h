@@ -237,16 +237,18 @@ qmm_status qmm_dequantize_codebook4(const uint8_t* W, int block, const float* ab
  *   bits       4.  block in {32, 64, 128, 256} (int8 mode additionally needs
  *              H % 32 == 0 and I % 32 == 0).
  *   scratch    device buffer of at least qmoe_decode_scratch_bytes(T, H, I, k, mode),
- *              256-byte aligned.  Layout (each region at a 256-byte boundary): four
- *              uint32 sync words of the single-launch form at offset 0 (the same place
- *              for every shape and mode), fp16 h [T][k][I] at offset 256, then in int8
- *              mode int8 x codes [T][H], fp32 x scales [T][H/32], int8 h codes
+ *              256-byte aligned.  Layout (each region at a 256-byte boundary): the
+ *              sync words of the single-launch form in the first 8448 bytes (the same
+ *              place for every shape and mode): uint32 [0] top arrival count, [2] error
+ *              flag, then in each of the next 32 256-byte slots an arrival sub-counter
+ *              and a phase word; then fp16 h [T][k][I] at offset 8448, then in
+ *              int8 mode int8 x codes [T][H], fp32 x scales [T][H/32], int8 h codes
  *              [T][k][I], fp32 h scales [T][k][I/32].  The sync words must be zero
  *              before the first call on a buffer (zero the whole buffer once, e.g.
- *              hipMemset); every call leaves the first zero again and the second (a
- *              phase) at 0 or 1.  The third is an error flag that a call sets, and leaves set, if its wait inside the
- *              launch gave up after 1 s (its output is then invalid).  Calls that share
- *              a scratch buffer must not overlap.
+ *              hipMemset); every call leaves the counters zero again and the phases
+ *              equal, at 0 or 1.  The error flag is set, and left set, by a call whose wait inside
+ *              the launch gave up after 1 s (its output is then invalid).  Calls that
+ *              share a scratch buffer must not overlap.
  *   Launches   two kernels (fc1 + SwiGLU, then fc2 + combine; int8 mode adds the h
  *              quantizer between them), or one launch of all of it: a grid that is
  *              resident all at once (its size is the kernel's occupancy times the

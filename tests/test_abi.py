@@ -194,11 +194,12 @@ def test_scratch_queries():
     fp = L.qmoe_decode_scratch_bytes(1, 2880, 2880, 4, Q.QMOE_FP)
     i8 = L.qmoe_decode_scratch_bytes(1, 2880, 2880, 4, Q.QMOE_INT8_ACT)
     a256 = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    # fp: the four sync words of the single-launch form, then h fp16 [T][k][I]
-    assert fp == a256(16) + a256(4 * 2880 * 2)
-    # int8: sync words, h, then x codes, x scales, h codes, h scales
-    assert i8 == a256(16) + a256(4 * 2880 * 2) + a256(2880) + a256(90 * 4) + a256(4 * 2880) + a256(4 * 90 * 4)
-    assert L.qmoe_decode_scratch_bytes(8, 2048, 768, 8, Q.QMOE_FP) == a256(16) + a256(64 * 768 * 2)
+    sync = 33 * 256  # the single-launch form's sync slots: top count / flag, 32 sub-counter + phase
+    # fp: the sync slots, then h fp16 [T][k][I]
+    assert fp == sync + a256(4 * 2880 * 2)
+    # int8: sync slots, h, then x codes, x scales, h codes, h scales
+    assert i8 == sync + a256(4 * 2880 * 2) + a256(2880) + a256(90 * 4) + a256(4 * 2880) + a256(4 * 90 * 4)
+    assert L.qmoe_decode_scratch_bytes(8, 2048, 768, 8, Q.QMOE_FP) == sync + a256(64 * 768 * 2)
 
 
 def test_decode_status_refusals():

@@ -132,7 +132,7 @@ def test_int8_activation_codes_bit_exact():
 
     def a256(x):
         return (x + 255) // 256 * 256
-    off_h = 256                      # after the sync words
+    off_h = 33 * 256                 # after the sync words
     off_xq = off_h + a256(T * k * I * 2)
     off_xs = off_xq + a256(T * H)
     off_hq = off_xs + a256(T * (H // 32) * 4)
@@ -173,13 +173,17 @@ def _fused_base():
     return Q.num_candidates(Q.ENTRY_QMOE_FC1) * Q.num_candidates(Q.ENTRY_QMOE_FC2)
 
 
+SYNC_BYTES = 33 * 256   # slot 0 (top count, error flag) + 32 slots (sub-counter, phase)
+
+
 def _sync_words(raw, T, H, I, k):
-    """The sync words of the single-launch form (offset 0 of the scratch layout) that
-    must be zero after a call: the arrival count, the error flag and the unused word
-    (the phase word between them alternates between 0 and 1)."""
-    w = raw[0:16].view(np.uint32)
-    assert w[1] in (0, 1), w
-    return w[[0, 2, 3]]
+    """The sync words of the single-launch form (the first slots of the scratch layout)
+    that must be zero after a call: slot 0 (top arrival count, error flag, unused words)
+    and the 32 arrival sub-counters; the 32 phase copies must all be equal, 0 or 1."""
+    w = raw[0:SYNC_BYTES].view(np.uint32)
+    phases = w[65::64]
+    assert phases.min() == phases.max() and phases[0] in (0, 1), phases
+    return np.concatenate([w[:4], w[64::64]])
 
 
 FUSED_CASES = [
