@@ -99,52 +99,6 @@ __device__ __forceinline__ float u4_zero_point(const uint8_t* zp, int64_t row, i
   return (float)((zp[row * zp_row_bytes + (b >> 1)] >> ((b & 1) * 4)) & 0xfu);
 }
 
-// Symmetric int8 quantization of `n` fp32 values (n % 32 == 0) held by the whole
-// work-group, into LDS: codes permuted per 8 as [0 2 4 6 | 1 3 5 7], one fp32
-// scale and one int32 code sum per 32 values.  Optional natural-order copy to
-// global memory (codes int8, scales fp32) for inspection.
-template <typename LoadFn>
-__device__ void quantize_groups_lds(LoadFn load, int n, uint32_t* q_lds, float* s_lds, int* sum_lds,
-                                    int8_t* q_out, float* s_out) {
-  const int groups = n / 32;
-  const int lane = threadIdx.x & 63;
-  const int nwaves = blockDim.x >> 6;
-  const int half = lane >> 5;        // two groups per wave pass
-  const int li = lane & 31;
-  for (int g0 = (threadIdx.x >> 6) * 2; g0 < groups; g0 += nwaves * 2) {
-    const int g = g0 + half;
-    const bool ok = g < groups;
-    const float v = ok ? load(g * 32 + li) : 0.0f;
-    float amax = fabsf(v);
-#pragma unroll
-    for (int off = 1; off < 32; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
-    int q = 0;
-    float s = 0.0f;
-    if (amax > 0.0f) {
-      const float inv = 127.0f / amax;
-      const float t = __fmul_rn(v, inv);
-      q = (int)rintf(t);
-      q = q > 127 ? 127 : (q < -127 ? -127 : q);
-      s = amax / 127.0f;
-    }
-    int qs = q;
-#pragma unroll
-    for (int off = 1; off < 32; off <<= 1) qs += __shfl_xor(qs, off, 64);
-    if (ok) {
-      // permuted position: within each run of 8, even indices first
-      const int r = li & 7;
-      const int pos = (li & ~7) + ((r & 1) ? 4 + (r >> 1) : (r >> 1));
-      ((int8_t*)q_lds)[g * 32 + pos] = (int8_t)q;
-      if (q_out) q_out[g * 32 + li] = (int8_t)q;
-      if (li == 0) {
-        s_lds[g] = s;
-        sum_lds[g] = qs;
-        if (s_out) s_out[g] = s;
-      }
-    }
-  }
-}
-
 // ---- staged activations ------------------------------------------------------------
 //
 // fp mode: the activation vector in LDS as fp16 pairs, 16 dwords per 32-value chunk
@@ -242,6 +196,86 @@ __device__ __forceinline__ void stage_h16_first(const uint16_t* src, int rows, i
     s8 += dpp_f<kDppXor1>(s8);
     s8 += dpp_f<kDppXor2>(s8);
     if (okp && (pp & 3) == 0) sa[r * nch + (pp >> 2)] = s8;
+  };
+  auto batch = [&](int base, auto first) {
+    uint4 vb[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) load(base + j * (int)blockDim.x + (int)threadIdx.x, vb[j]);
+    if constexpr (decltype(first)::value) {
+      __builtin_amdgcn_sched_barrier(0);  // keep the caller's loads behind these
+      issued();
+    }
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+      if (base + j * (int)blockDim.x + wave_base < total) convert(base + j * (int)blockDim.x + (int)threadIdx.x, vb[j]);
+  };
+  batch(0, std::true_type{});
+  for (int base = NB * (int)blockDim.x; base < total; base += NB * (int)blockDim.x) batch(base, std::false_type{});
+  __syncthreads();
+}
+
+// int8 staging of the n fp16 values at src (n % 32 == 0, 16-byte aligned; rows back to
+// back, each a multiple of 32 values): 16-byte loads of 8 values per lane, so the 4
+// lanes of a quad hold one 32-value group, NB per thread in flight at once; the group
+// is quantized as the oracle's quantizer does it (amax over the 32 values, codes
+// rint(v * fp32(127/amax)) clamped to +-127, scale fp32(amax/127); all zero when amax
+// is 0), the codes go to LDS permuted per 8 as [0 2 4 6 | 1 3 5 7], with the scale and
+// the code sum per group.  q_out / s_out (may be null): the codes in natural order and
+// the scales, in memory.  The first batch's loads are issued before `issued` runs (as
+// in stage_h16_first).  AUX: the loads' cache-policy bits.
+template <int AUX, typename Issued>
+__device__ __forceinline__ void stage_i8_first(const uint16_t* src, int n, uint32_t* q_lds, float* s_lds,
+                                               int* sum_lds, int8_t* q_out, float* s_out, Issued&& issued) {
+  constexpr int NB = 4;
+  const int total = n / 8;  // pieces of 8 values, a multiple of 4: quads are all in or all out
+  const int wave_base = __builtin_amdgcn_readfirstlane((int)(threadIdx.x & ~63u));
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, (uint32_t)n * 2u);
+  auto load = [&](int p, uint4& u) {
+    const uint32_t off = p < total ? (uint32_t)p * 16u : 0x80000000u;  // past the range: 0, no data
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, AUX);
+    u = make_uint4(v[0], v[1], v[2], v[3]);
+  };
+  auto pack = [](int a0, int a1, int a2, int a3) {
+    return (uint32_t)(a0 & 0xff) | ((uint32_t)(a1 & 0xff) << 8) | ((uint32_t)(a2 & 0xff) << 16) |
+           ((uint32_t)(a3 & 0xff) << 24);
+  };
+  auto convert = [&](int p, const uint4& u) {
+    float v[8];
+    h8_to_f32(u, v);
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    amax = fmaxf(amax, dpp_f<kDppXor1>(amax));
+    amax = fmaxf(amax, dpp_f<kDppXor2>(amax));
+    int q[8];
+    float sc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = 0;
+    if (amax > 0.0f) {
+      const float inv = 127.0f / amax;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int c = (int)rintf(__fmul_rn(v[i], inv));
+        q[i] = c > 127 ? 127 : (c < -127 ? -127 : c);
+      }
+      sc = amax / 127.0f;
+    }
+    int sum = ((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7]));
+    sum += __float_as_int(dpp_f<kDppXor1>(__int_as_float(sum)));
+    sum += __float_as_int(dpp_f<kDppXor2>(__int_as_float(sum)));
+    if (p < total) {
+      const int g = p >> 2, m = p & 3;
+      q_lds[g * 8 + 2 * m] = pack(q[0], q[2], q[4], q[6]);
+      q_lds[g * 8 + 2 * m + 1] = pack(q[1], q[3], q[5], q[7]);
+      if (m == 0) {
+        s_lds[g] = sc;
+        sum_lds[g] = sum;
+      }
+      if (q_out) {
+        *(uint2*)(q_out + (int64_t)p * 8) = make_uint2(pack(q[0], q[1], q[2], q[3]), pack(q[4], q[5], q[6], q[7]));
+        if (m == 0) s_out[g] = sc;
+      }
+    }
   };
   auto batch = [&](int base, auto first) {
     uint4 vb[NB];
@@ -413,10 +447,8 @@ __global__ __launch_bounds__(kMoeThreads) void qmoe_fc1_kernel(QmoeArgs a) {
   for (int i = 0; i < kFc1Depth - 1; ++i) fetch(buf[i]);
   if constexpr (INT8) {
     const bool keep = blockIdx.x == 0 && (slot % a.k) == 0;
-    quantize_groups_lds([&](int i) { return f16_to_f32(x[i]); }, (int)a.H, xq, xs, xsum,
-                        keep ? a.xq_out + (int64_t)t * a.H : nullptr,
-                        keep ? a.xs_out + (int64_t)t * (a.H / 32) : nullptr);
-    __syncthreads();
+    stage_i8_first<0>(x, (int)a.H, xq, xs, xsum, keep ? a.xq_out + (int64_t)t * a.H : nullptr,
+                      keep ? a.xs_out + (int64_t)t * (a.H / 32) : nullptr, [] {});
   } else {
     stage_h16(x, 1, (int)a.H, nch, xh, sa);
   }
@@ -866,86 +898,6 @@ __device__ __forceinline__ void fc2_write_out(const QmoeArgs& a, int g_begin, in
     }
     a.Y[(int64_t)t * a.H + n] = f32_to_f16(y);
   }
-}
-
-// int8 staging of the n fp16 values at src (n % 32 == 0, 16-byte aligned; rows back to
-// back, each a multiple of 32 values): 16-byte loads of 8 values per lane, so the 4
-// lanes of a quad hold one 32-value group, NB per thread in flight at once; the group
-// is quantized as the oracle's quantizer does it (amax over the 32 values, codes
-// rint(v * fp32(127/amax)) clamped to +-127, scale fp32(amax/127); all zero when amax
-// is 0), the codes go to LDS permuted per 8 as [0 2 4 6 | 1 3 5 7], with the scale and
-// the code sum per group.  q_out / s_out (may be null): the codes in natural order and
-// the scales, in memory.  The first batch's loads are issued before `issued` runs (as
-// in stage_h16_first).  AUX: the loads' cache-policy bits.
-template <int AUX, typename Issued>
-__device__ __forceinline__ void stage_i8_first(const uint16_t* src, int n, uint32_t* q_lds, float* s_lds,
-                                               int* sum_lds, int8_t* q_out, float* s_out, Issued&& issued) {
-  constexpr int NB = 4;
-  const int total = n / 8;  // pieces of 8 values, a multiple of 4: quads are all in or all out
-  const int wave_base = __builtin_amdgcn_readfirstlane((int)(threadIdx.x & ~63u));
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, (uint32_t)n * 2u);
-  auto load = [&](int p, uint4& u) {
-    const uint32_t off = p < total ? (uint32_t)p * 16u : 0x80000000u;  // past the range: 0, no data
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, AUX);
-    u = make_uint4(v[0], v[1], v[2], v[3]);
-  };
-  auto pack = [](int a0, int a1, int a2, int a3) {
-    return (uint32_t)(a0 & 0xff) | ((uint32_t)(a1 & 0xff) << 8) | ((uint32_t)(a2 & 0xff) << 16) |
-           ((uint32_t)(a3 & 0xff) << 24);
-  };
-  auto convert = [&](int p, const uint4& u) {
-    float v[8];
-    h8_to_f32(u, v);
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
-    amax = fmaxf(amax, dpp_f<kDppXor1>(amax));
-    amax = fmaxf(amax, dpp_f<kDppXor2>(amax));
-    int q[8];
-    float sc = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) q[i] = 0;
-    if (amax > 0.0f) {
-      const float inv = 127.0f / amax;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int c = (int)rintf(__fmul_rn(v[i], inv));
-        q[i] = c > 127 ? 127 : (c < -127 ? -127 : c);
-      }
-      sc = amax / 127.0f;
-    }
-    int sum = ((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7]));
-    sum += __float_as_int(dpp_f<kDppXor1>(__int_as_float(sum)));
-    sum += __float_as_int(dpp_f<kDppXor2>(__int_as_float(sum)));
-    if (p < total) {
-      const int g = p >> 2, m = p & 3;
-      q_lds[g * 8 + 2 * m] = pack(q[0], q[2], q[4], q[6]);
-      q_lds[g * 8 + 2 * m + 1] = pack(q[1], q[3], q[5], q[7]);
-      if (m == 0) {
-        s_lds[g] = sc;
-        sum_lds[g] = sum;
-      }
-      if (q_out) {
-        *(uint2*)(q_out + (int64_t)p * 8) = make_uint2(pack(q[0], q[1], q[2], q[3]), pack(q[4], q[5], q[6], q[7]));
-        if (m == 0) s_out[g] = sc;
-      }
-    }
-  };
-  auto batch = [&](int base, auto first) {
-    uint4 vb[NB];
-#pragma unroll
-    for (int j = 0; j < NB; ++j) load(base + j * (int)blockDim.x + (int)threadIdx.x, vb[j]);
-    if constexpr (decltype(first)::value) {
-      __builtin_amdgcn_sched_barrier(0);  // keep the caller's loads behind these
-      issued();
-    }
-#pragma unroll
-    for (int j = 0; j < NB; ++j)
-      if (base + j * (int)blockDim.x + wave_base < total) convert(base + j * (int)blockDim.x + (int)threadIdx.x, vb[j]);
-  };
-  batch(0, std::true_type{});
-  for (int base = NB * (int)blockDim.x; base < total; base += NB * (int)blockDim.x) batch(base, std::false_type{});
-  __syncthreads();
 }
 
 // FUSED: h was written earlier in the same launch by other work-groups: the first
