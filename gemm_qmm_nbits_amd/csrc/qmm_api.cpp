@@ -831,6 +831,7 @@ qmm_status qmm_nbits(const void* A, int a_type, int64_t M, int64_t K, int64_t N,
     p.zp = zp;
     p.zp_kind = zp_kind;
     p.zconst = zp_kind == QMM_ZP_UNIFORM ? uniform_zp : default_zp(bits);
+    p.zconst_fma = zconst_fma_exact(p.zconst) ? 1 : 0;
     p.zp_row_bytes = ceil_div(p.nblk * bits, 8);
     p.bias = bias;
     p.C = C;

@@ -110,6 +110,20 @@ constexpr int kUniformPartials = 256;
 hipError_t launch_cast_pad_f16(const void* src, int src_type, int64_t M, int64_t K, int64_t Kp,
                                uint16_t* dst, float* row_scale, hipStream_t st);
 
+// A zero point z for which fp32((q - z) * s) == fma(q, s, -(z * s)) for every code q
+// in 0..255 (or -128..127) and every fp16 scale s: q - z is exact in fp32 (|z| < 2^8,
+// lowest set bit at 2^-15 or above) and z * s is exact (z has at most 13 significant
+// bits, s has 11), so the one rounding of the fma is the rounding of the product.
+inline bool zconst_fma_exact(float z) {
+  if (!(z > -256.0f && z < 256.0f)) return false;
+  const float t = z * 32768.0f;  // exact: a power of two
+  if (t != (float)(int32_t)t) return false;
+  uint32_t u = (uint32_t)(t < 0 ? -t : t);
+  if (u == 0) return true;
+  while (!(u & 1u)) u >>= 1;
+  return u < (1u << 13);
+}
+
 struct PrefillArgs {
   const uint16_t* A16;  // fp16 [M][lda]: the cast workspace (lda = Kp, k >= K zero) or fp16 A itself
   const float* row_scale;  // [M] factor of each row's sums (the cast's 2^-s_m), or NULL for 1
@@ -127,6 +141,7 @@ struct PrefillArgs {
   const void* zp;
   int zp_kind;
   float zconst;  // zero point for QMM_ZP_NONE / QMM_ZP_UNIFORM
+  int zconst_fma;  // zconst_fma_exact(zconst): the dequantization may use one fma per code
   int64_t zp_row_bytes;
   const void* bias;
   void* C;

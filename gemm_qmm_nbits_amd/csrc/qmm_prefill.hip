@@ -246,12 +246,25 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillArgs p) {
       qv[1] = h0.x; qv[3] = h0.y; qv[5] = h1.x; qv[7] = h1.y;
     }
     uint32_t o[4];
+    if (ZK == 1 || (ZK == 0 && p.zconst_fma)) {
+      // q - z is exact for every code and z * s is exact (packed integer zero points, or
+      // a constant that passed zconst_fma_exact), so one fma gives fp32((q - z) * s)
+      const float nzs = -(z * sc);
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      f32x2 w;
-      w.x = __fmul_rn(__fsub_rn(qv[2 * jj], z), sc);
-      w.y = __fmul_rn(__fsub_rn(qv[2 * jj + 1], z), sc);
-      o[jj] = __builtin_bit_cast(uint32_t, __builtin_convertvector(w, f16x2));  // round to nearest even
+      for (int jj = 0; jj < 4; ++jj) {
+        f32x2 w;
+        w.x = __fmaf_rn(qv[2 * jj], sc, nzs);
+        w.y = __fmaf_rn(qv[2 * jj + 1], sc, nzs);
+        o[jj] = __builtin_bit_cast(uint32_t, __builtin_convertvector(w, f16x2));  // round to nearest even
+      }
+    } else {
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        f32x2 w;
+        w.x = __fmul_rn(__fsub_rn(qv[2 * jj], z), sc);
+        w.y = __fmul_rn(__fsub_rn(qv[2 * jj + 1], z), sc);
+        o[jj] = __builtin_bit_cast(uint32_t, __builtin_convertvector(w, f16x2));  // round to nearest even
+      }
     }
     *(uint4*)(dst + swz(r2, 4 * h + q)) = make_uint4(o[0], o[1], o[2], o[3]);
   };

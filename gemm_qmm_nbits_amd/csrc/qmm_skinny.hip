@@ -65,9 +65,11 @@ __device__ __forceinline__ float sk_bias(const void* b, int64_t i) {
 // 8 codes -> 8 fp16 weights (codes in order), exact fp32 dequant rounded to nearest
 // fp16.  BITS = 4: `xw` holds the 8 codes as nibbles; BITS = 2: in its low 16 bits;
 // BITS = 3: in its low 24 bits; BITS = 8: four signed bytes in xw, four in xw2.
+// fz: q - z is exact for every code and z * sc is exact (integer zero points, or a
+// constant that passed zconst_fma_exact), so fp32((q - z) * sc) is one fma.
 template <int FMT, int BITS>
 __device__ __forceinline__ f16x8 dequant8(uint32_t xw, uint32_t xw2, float sc, float z, float am,
-                                          const float* cb) {
+                                          const float* cb, bool fz) {
   uint32_t o[4];
   if constexpr (FMT == GEMV_CODEBOOK) {
 #pragma unroll
@@ -108,12 +110,23 @@ __device__ __forceinline__ f16x8 dequant8(uint32_t xw, uint32_t xw2, float sc, f
       qv[0] = l0.x; qv[2] = l0.y; qv[4] = l1.x; qv[6] = l1.y;
       qv[1] = h0.x; qv[3] = h0.y; qv[5] = h1.x; qv[7] = h1.y;
     }
+    if (fz) {
+      const float nzs = -(z * sc);
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      f32x2 w;
-      w.x = __fmul_rn(__fsub_rn(qv[2 * jj], z), sc);
-      w.y = __fmul_rn(__fsub_rn(qv[2 * jj + 1], z), sc);
-      o[jj] = __builtin_bit_cast(uint32_t, __builtin_convertvector(w, f16x2));  // nearest even
+      for (int jj = 0; jj < 4; ++jj) {
+        f32x2 w;
+        w.x = __fmaf_rn(qv[2 * jj], sc, nzs);
+        w.y = __fmaf_rn(qv[2 * jj + 1], sc, nzs);
+        o[jj] = __builtin_bit_cast(uint32_t, __builtin_convertvector(w, f16x2));  // nearest even
+      }
+    } else {
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        f32x2 w;
+        w.x = __fmul_rn(__fsub_rn(qv[2 * jj], z), sc);
+        w.y = __fmul_rn(__fsub_rn(qv[2 * jj + 1], z), sc);
+        o[jj] = __builtin_bit_cast(uint32_t, __builtin_convertvector(w, f16x2));  // nearest even
+      }
     }
   }
   return __builtin_bit_cast(f16x8, make_uint4(o[0], o[1], o[2], o[3]));
@@ -241,7 +254,7 @@ __global__ __launch_bounds__(SK_THREADS) void skinny_kernel(PrefillArgs p) {
         else  // 3 bits: the 24-bit field at bit 24 j of the 96-bit group
           xw = j == 0 ? wv[s][0] : j == 1 ? __builtin_amdgcn_alignbit(wv[s][1], wv[s][0], 24)
              : j == 2 ? __builtin_amdgcn_alignbit(wv[s][2], wv[s][1], 16) : (wv[s][2] >> 8);
-        const f16x8 bf = dequant8<FMT, BITS>(xw, xw2, sc[s], z[s], am[s], cb);
+        const f16x8 bf = dequant8<FMT, BITS>(xw, xw2, sc[s], z[s], am[s], cb, ZK == 1 || (ZK == 0 && p.zconst_fma));
 #pragma unroll
         for (int mt = 0; mt < MB; ++mt)
           acc[mt][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[mt][j], bf, acc[mt][s], 0, 0, 0);
@@ -464,7 +477,7 @@ __global__ __launch_bounds__(SK_THREADS) void ragged_kernel(RaggedArgs p) {
     for (int j = 0; j < 4; ++j) {
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        const f16x8 bf = dequant8<GEMV_AFFINE, 4>(wv[s][j], 0u, sc[s], z[s], 0.0f, nullptr);
+        const f16x8 bf = dequant8<GEMV_AFFINE, 4>(wv[s][j], 0u, sc[s], z[s], 0.0f, nullptr, true);
 #pragma unroll
         for (int mt = 0; mt < MB; ++mt)
           acc[mt][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[mt][j], bf, acc[mt][s], 0, 0, 0);
