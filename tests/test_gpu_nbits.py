@@ -322,6 +322,35 @@ def test_prefill_exact_arithmetic_bitwise():
     t.cuda.synchronize()
 
 
+@pytest.mark.parametrize("M", [32, 128], ids=["skinny", "tiles"])
+@pytest.mark.parametrize("bits,zp,zval,uniform", [
+    (4, "f16_uniform", 1.5, True),          # one fma per code
+    (2, "f16_uniform", 0.25, True),
+    (4, "f16_uniform", 100.5, True),
+    (4, "f16_uniform", 300.0, True),        # |z| >= 2^8: subtract and multiply
+    (4, "f16_uniform", 2.0 ** -20, True),   # a bit below 2^-15: subtract and multiply
+    (4, "packed", None, False),             # integer codes: one fma per code
+    (2, "f16", None, False),                # fp16 tensor: subtract and multiply
+])
+def test_matrix_core_weights_bit_exact(M, bits, zp, zval, uniform):
+    """One-hot activation rows read the matrix-core paths' fp16 weights out exactly:
+    C[m][n] = fp16(fp32((q - z) * s)) of W row n at k = m, bit for bit, whether the
+    dequantization computes the product as one fma (where q - z and z * s are exact) or
+    as a subtract and a multiply."""
+    K, N, block = 256, 96, 32
+    kw = {"uniform_zp": zval} if zval is not None else {}
+    p = gen.nbits_problem(M, K, N, bits, block, seed=990 + bits + M, zp=zp, scale_range=(0.01, 0.5), **kw)
+    A = np.zeros((M, K), dtype=np.float32)
+    A[np.arange(M), np.arange(M)] = 1.0
+    p["A"] = A
+    d = NbitsDev(p)
+    got = host_f64(d.run(uniform=uniform))
+    torch().cuda.synchronize()
+    w = O.dequant_nbits(p["W"], bits, K, block, p["scales"], p["zp"], oracle_zp_kind(O, zp)).astype(np.float64)
+    want = O._round_operand(w, "f16")[:, :M].T
+    assert np.array_equal(got, want), (M, bits, zp, zval, np.argwhere(got != want)[:4])
+
+
 def test_prefill_repeat_bit_identical():
     p = gen.nbits_problem(512, 5120, 1024, 2, 64, seed=79, zp="f16_uniform", scale_range=(0.01, 0.05))
     d = NbitsDev(p)
