@@ -184,6 +184,31 @@ int pick_winner(const double* t, int rounds, int ncand) {
   return best;
 }
 
+// The single-launch MoE forms (candidates 0 .. ncand - 2) against the two-kernel pair
+// (candidate ncand - 1): the fastest single launch is kept unless the pair's total is
+// more than kQmoePairMargin below it.  A second launch costs the host one more issue
+// and the stream one more dependency, which the device-side timing does not see.
+constexpr double kQmoePairMargin = 0.05;
+int pick_single_launch(const double* t, int rounds, int ncand) {
+  auto total = [&](int c) {
+    double tot = 0;
+    for (int r = 1; r < rounds; ++r) tot += t[r * ncand + c];
+    return tot;
+  };
+  const int pair = ncand - 1;
+  int best = -1;
+  double best_total = 0;
+  for (int c = 0; c < pair; ++c) {
+    const double tot = total(c);
+    if (best < 0 || tot < best_total) {
+      best = c;
+      best_total = tot;
+    }
+  }
+  if (best < 0) return pair;
+  return best_total <= total(pair) * (1.0 + kQmoePairMargin) ? best : pair;
+}
+
 // Ensure the rotation pool holds at least 4x the last-level cache (256 MB) and at
 // least 4 copies of `unit` bytes.  Returns false when memory is not available.
 bool ensure_pool(TunerState& t, size_t unit, size_t out_bytes) {
@@ -580,7 +605,7 @@ int qmoe_fused_choice(QmoeArgs& a, hipStream_t st, bool may_time, int r1, int r2
     (void)hipEventDestroy(e0);
     (void)hipEventDestroy(e1);
     if (ok) {
-      best = pick_winner(tv.data(), kRounds, kCands);
+      best = pick_single_launch(tv.data(), kRounds, kCands);
       t.choice[key] = best < kNumQmoeFused ? best : -1;
       if (env_flag("QMM_LOG")) {
         std::fprintf(stderr, "[qmm] tune qmoe fused T=%lld H=%lld I=%lld E=%lld k=%d block=%d ->", (long long)a.T,
@@ -1340,6 +1365,11 @@ void qmm_clear_tuning(void) {
 int qmm_tuner_pick(const double* times_us, int rounds, int ncand) {
   if (!times_us || rounds < 2 || ncand < 1) return -1;
   return pick_winner(times_us, rounds, ncand);
+}
+
+int qmm_tuner_pick_single_launch(const double* times_us, int rounds, int ncand) {
+  if (!times_us || rounds < 2 || ncand < 2) return -1;
+  return pick_single_launch(times_us, rounds, ncand);
 }
 
 qmm_status qmm_hbm_read_probe(const void* buf, int64_t bytes, uint32_t* sink, int groups, void* stream) {

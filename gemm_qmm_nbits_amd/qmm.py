@@ -102,6 +102,7 @@ _SIGS = {
     "qmm_tuned_choice": (c_int, [c_int]),
     "qmm_clear_tuning": (None, []),
     "qmm_tuner_pick": (c_int, [POINTER(c_double), c_int, c_int]),
+    "qmm_tuner_pick_single_launch": (c_int, [POINTER(c_double), c_int, c_int]),
     "qmm_status_string": (ctypes.c_char_p, [c_int]),
 }
 
@@ -483,3 +484,8 @@ def clear_tuning():
 def tuner_pick(times_us, rounds, ncand):
     arr = (c_double * len(times_us))(*times_us)
     return lib().qmm_tuner_pick(arr, rounds, ncand)
+
+
+def tuner_pick_single_launch(times_us, rounds, ncand):
+    arr = (c_double * len(times_us))(*times_us)
+    return lib().qmm_tuner_pick_single_launch(arr, rounds, ncand)

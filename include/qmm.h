@@ -400,6 +400,13 @@ void qmm_clear_tuning(void);
  * Returns -1 for bad arguments. */
 int qmm_tuner_pick(const double* times_us, int rounds, int ncand);
 
+/* The MoE decode's choice between its single-launch forms and the two-kernel pair,
+ * exposed for host-only checks: candidates 0 .. ncand-2 are single-launch forms and
+ * candidate ncand-1 the pair, totals as in qmm_tuner_pick.  The fastest single launch
+ * is chosen unless the pair's total is more than 5% below it (ties to the lower
+ * index).  Returns -1 for bad arguments (ncand < 2 or rounds < 2). */
+int qmm_tuner_pick_single_launch(const double* times_us, int rounds, int ncand);
+
 /* ---------------------------------------------------------------------------
  * Measurement helper (not part of the computation): reads `bytes` of device memory
  * (16-byte aligned, a multiple of 16) once with 128-bit loads, `groups` work-groups of

@@ -188,6 +188,21 @@ def test_tuner_selection_rule():
     assert Q.tuner_pick([1.0], 1, 1) == -1
 
 
+def test_single_launch_preference_rule():
+    """MoE decode: candidates 0..n-2 are single-launch forms, n-1 the two-kernel pair;
+    the fastest single launch stays unless the pair is more than 5% faster."""
+    # 3 rounds (round 0 discarded) x (2 single-launch forms + the pair)
+    def times(s0, s1, pair):
+        return [50.0, 50.0, 50.0, s0, s1, pair, s0, s1, pair]
+    assert Q.tuner_pick_single_launch(times(21.0, 22.0, 20.0), 3, 3) == 0   # 5% slower: single
+    assert Q.tuner_pick_single_launch(times(22.0, 21.5, 20.0), 3, 3) == 2   # 7.5% slower: pair
+    assert Q.tuner_pick_single_launch(times(19.0, 18.0, 20.0), 3, 3) == 1   # faster: the faster single
+    assert Q.tuner_pick_single_launch(times(1e30, 1e30, 20.0), 3, 3) == 2   # no single-launch plan
+    assert Q.tuner_pick_single_launch(times(20.0, 20.0, 20.0), 3, 3) == 0   # ties: lower index
+    assert Q.tuner_pick_single_launch([1.0, 2.0], 1, 2) == -1
+    assert Q.tuner_pick_single_launch([1.0, 2.0], 2, 1) == -1
+
+
 def test_scratch_queries():
     L = Q.lib()
     assert L.qmm_uniform_scratch_bytes() >= 8
