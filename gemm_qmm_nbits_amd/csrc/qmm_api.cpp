@@ -515,12 +515,14 @@ void qmoe_choice(const QmoeArgs& a, hipStream_t st, bool may_time, int* r1, int*
 // with the tiling (r1, r2) already chosen by qmoe_choice.  The first uncaptured call of
 // a shape times every single-launch candidate and that two-kernel pair the same way as
 // qmoe_choice (one discarded round, then 8 timed rounds, every launch on a different
-// expert set, writing only the call's scratch and a library-owned output); the least
-// total wins.  Without timing the two-kernel form is used (the faster one measured on
-// MI355X for the configured shapes).  Forced tuning: indices >= kQmoeForcedFused select
-// candidate (index - kQmoeForcedFused) of the single-launch form, smaller ones the
-// two-kernel form.
+// expert set, writing only the call's scratch and a library-owned output), and
+// pick_single_launch decides.  Without timing (tuning off, a first call under capture,
+// the allocation-free entry) the single launch is used: candidate kQmoeDefaultFused
+// (fc2 streamed, one work-group per compute unit) where its plan fits, else the
+// two-kernel form.  Forced tuning: indices >= kQmoeForcedFused select candidate
+// (index - kQmoeForcedFused) of the single-launch form, smaller ones the two-kernel form.
 constexpr int kQmoeForcedFused = kNumQmoeCandidates * kNumQmoeCandidates;
+constexpr int kQmoeDefaultFused = 1;
 
 int qmoe_fused_choice(QmoeArgs& a, hipStream_t st, bool may_time, int r1, int r2) {
   TunerState& t = tuner();
@@ -536,12 +538,13 @@ int qmoe_fused_choice(QmoeArgs& a, hipStream_t st, bool may_time, int r1, int r2
     const int c = (t.forced - kQmoeForcedFused) % kNumQmoeFused;
     return plan(c) ? finish(c) : finish(-1);
   }
-  if (mode == 1) return finish(-1);
+  auto untimed = [&] { return plan(kQmoeDefaultFused) ? finish(kQmoeDefaultFused) : finish(-1); };
+  if (mode == 1) return untimed();
   auto key = std::make_tuple((int)ENTRY_QMOE_FUSED, a.T * 1000 + a.k, a.H, a.I, a.block, a.mode, (int)a.E,
                              (a.fc1.zp != nullptr ? 2 : 0) + (a.fc2.zp != nullptr ? 1 : 0));
   auto it = t.choice.find(key);
   if (it != t.choice.end()) return plan(it->second) ? finish(it->second) : finish(-1);
-  if (!may_time || stream_capturing(st)) return finish(-1);
+  if (!may_time || stream_capturing(st)) return untimed();
   bool any = false;
   for (int c = 0; c < kNumQmoeFused; ++c) any = any || plan(c);
   if (!any) {

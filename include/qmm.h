@@ -249,14 +249,14 @@ qmm_status qmm_dequantize_codebook4(const uint8_t* W, int block, const float* ab
  *              equal, at 0 or 1.  The error flag is set, and left set, by a call whose wait inside
  *              the launch gave up after 1 s (its output is then invalid).  Calls that
  *              share a scratch buffer must not overlap.
- *   Launches   two kernels (fc1 + SwiGLU, then fc2 + combine; int8 mode adds the h
- *              quantizer between them), or one launch of all of it: a grid that is
- *              resident all at once (its size is the kernel's occupancy times the
- *              compute units) runs its fc1 share, publishes h, waits for every
- *              work-group's h and runs its fc2 share, whose weights it either streams
- *              after the wait (first loads issued before it) or has copied into LDS
- *              while fc1 ran (int8 mode: each work-group quantizes h itself).  The
- *              up-front timing picks the faster form per shape.  The one-launch form
+ *   Launches   one launch of all of it by default: a grid that is resident all at
+ *              once (its size is the kernel's occupancy times the compute units) runs
+ *              its fc1 share, publishes h, waits for every work-group's h and streams
+ *              its fc2 share (first loads issued before the wait; int8 mode: each
+ *              work-group quantizes h itself).  The two-kernel form (fc1 + SwiGLU,
+ *              then fc2 + combine; int8 mode adds the h quantizer between them) runs
+ *              instead where the up-front timing finds it more than 5% faster, or
+ *              where no single-launch plan fits.  The one-launch form
  *              needs the compute units to itself for that wait: a kernel on another
  *              stream that holds them for more than 1 s makes the wait give up (error
  *              flag above; the call's Y is then filled with fp16 NaN and
