@@ -364,8 +364,8 @@ def stack_leg(args, layers=40, reps=10):
 
 def codebook_leg(T):
     """Weight GB/s of qmm_codebook4 at the four codebook shapes for M = 1, 4, 16, 64:
-    bf16 A and C, block 64, weight copies >= 1 GiB per shape (M = 1: weight-streaming
-    GEMV; M >= 4: matrix cores).  Also the nested-absmax form (uint8 absmax codes through
+    bf16 A and C, block 64, weight copies >= 1 GiB per shape (M = 1, and M = 4 on at
+    most 2^24 codes: weight-streaming GEMV; otherwise matrix cores).  Also the nested-absmax form (uint8 absmax codes through
     a 256-entry table and per-256-block scales) at M = 1."""
     import torch
     from gemm_qmm_nbits_amd import inputs as gen
@@ -402,7 +402,7 @@ def codebook_leg(T):
                 "K": K, "N": N, "M": M, "graph_us": round(gus, 2), "kernel_us": round(ku["kernel_us"], 2),
                 "weight_GBps": round(wbytes / ku["kernel_us"] / 1e3, 1),
                 "frac_hbm": round(wbytes / ku["kernel_us"] / 1e3 / HBM_PEAK_GBS, 4),
-                "path": "gemv" if M < 4 else "matrix cores"}
+                "path": "gemv" if M < 4 or (M == 4 and N * K <= 1 << 24) else "matrix cores"}
         # nested absmax at M = 1: codes 1 B per block + table + scales per 256 blocks
         nbytes = N * nblk * (32 + 1) + 256 * 4 + ((N * nblk + 255) // 256) * 4
         na = gen.nested_absmax_inputs(np.random.default_rng(900 + si), N, nblk)

@@ -43,8 +43,14 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Codebook weights with a 16-bit output: from this M on, the skinny matrix-core kernel
 // beats the fp32 GEMV (it dequantizes each weight once for up to 16 rows), and its fp16
-// operand rounding stays far below the output's own rounding.
+// operand rounding stays far below the output's own rounding.  The exception is M = 4
+// on at most kCbGemvM4Codes codes, where the GEMV's four-row form wins (measured on
+// MI355X: 4096 x 1024 8.6 against 12.7 us, 4096 x 2048 9.3 against 14.1, 4096 x 4096
+// 11.4 against 12.1; 4096 x 14336 25.6 against 22.4).  A rule of the shape only, so a
+// shape's path, and its bits, never depend on the device.
 constexpr int kCbSkinnyMinM = 4;
+constexpr int64_t kCbGemvM4Codes = int64_t(1) << 24;
+bool codebook_gemv_m4(int64_t M, int64_t K, int64_t N) { return M == 4 && N * K <= kCbGemvM4Codes; }
 
 // Workspace of the matrix-core paths: A as fp16 rows of K rounded up to 64, the
 // fp32 row scales of that cast, then the fp32 partial sums of a split reduction (each
@@ -90,7 +96,7 @@ hipError_t matrix_activations(PrefillArgs& p, const void* A, int a_type, bool sk
 bool codebook_on_matrix_cores(int64_t M, int64_t K, int64_t N, int block, int c_type) {
   if (M <= 0 || K <= 0 || N <= 0) return false;
   if (M > kMaxGemvM) return true;
-  if (M < kCbSkinnyMinM || c_type == QMM_F32) return false;
+  if (M < kCbSkinnyMinM || c_type == QMM_F32 || codebook_gemv_m4(M, K, N)) return false;
   const int64_t Kp = (K + 63) / 64 * 64;
   const int64_t nblk = ceil_div(K, block);
   return skinny_applies(M, N, Kp, block, nblk * block / 2, nblk);
@@ -809,8 +815,9 @@ size_t qmm_nbits_workspace_bytes(int64_t M, int64_t K, int64_t N, int a_type) {
 size_t qmm_codebook4_workspace_bytes(int64_t M, int64_t K, int64_t N, int a_type) {
   // the matrix-core paths take the workspace of qmm_nbits: M > 8, and 4 <= M <= 8 with
   // a 16-bit output (the output type is not an argument, so the size covers that case)
+  // except M = 4 on a shape the GEMV keeps
   (void)a_type;
-  if (M < kCbSkinnyMinM || K <= 0 || N <= 0) return 0;
+  if (M < kCbSkinnyMinM || K <= 0 || N <= 0 || codebook_gemv_m4(M, K, N)) return 0;
   return matrix_workspace_bytes(M, K, N);
 }
 

@@ -135,12 +135,15 @@ qmm_status qmm_validate_nbits(const void* A, int a_type, int64_t M, int64_t K, i
  *   bias     [N] of c_type, or NULL.   C [M][N] of c_type.
  *   workspace, workspace_bytes: device scratch of at least
  *            qmm_codebook4_workspace_bytes(M, K, N, a_type) bytes (NULL when that is 0).
- *            That size is nonzero from M = 4 on.  It is needed for M > 8, and for
- *            4 <= M <= 8 with a 16-bit c_type (the size does not depend on c_type).
+ *            That size is nonzero from M = 4 on (except M = 4 with N * K <= 2^24).
+ *            It is needed for M > 8, and for 4 <= M <= 8 with a 16-bit c_type (the
+ *            size does not depend on c_type).
  * Paths: M <= 8 weight-streaming GEMV (fp32 FMA, codebook staged in LDS), except
  * 4 <= M <= 8 with a QMM_F16 or QMM_BF16 output and block >= 32, which takes the
  * skinny kernel below (the GEMV's work grows with M, the skinny kernel's does not up
- * to 16 rows; the fp16 operand rounding is well below the 16-bit output's).
+ * to 16 rows; the fp16 operand rounding is well below the 16-bit output's).  M = 4
+ * with N * K <= 2^24 stays on the GEMV (its four-row form is the faster there); the
+ * path is a function of the shape and output type only.
  * The matrix-core paths round A to fp16 once into the workspace (as for qmm_nbits)
  * and use weights fp16(fp32(codebook[q] * absmax)): the skinny kernel for M <= 64
  * with block >= 32, 256 x 256 tiles otherwise (as for qmm_nbits).

@@ -94,11 +94,13 @@ def _splits(M, N, kp):
 
 @pytest.mark.parametrize("M,K,N", [(16, 4096, 14336), (64, 4096, 1024), (2048, 17920, 5120),
                                    (2048, 5120, 7680), (2048, 5120, 100352), (9, 70, 33),
-                                   (8, 4096, 4096), (4, 4096, 14336), (3, 4096, 1024)])
+                                   (8, 4096, 4096), (4, 4096, 14336), (3, 4096, 1024), (4, 4096, 4096),
+                                   (4, 4096, 4097), (5, 4096, 1024)])
 def test_workspace_sizes(M, K, N):
     """Padded fp16 A, the fp32 row scales of its cast and the fp32 partial sums of a split
     reduction (each from a 256-byte boundary): qmm_nbits from M = 9 on, qmm_codebook4 from
-    M = 4 on (its 16-bit outputs take the skinny kernel)."""
+    M = 4 on (its 16-bit outputs take the skinny kernel), except M = 4 on at most 2^24
+    codes, which the GEMV keeps."""
     need = Q.lib().qmm_nbits_workspace_bytes(M, K, N, Q.QMM_BF16)
     need_cb = Q.lib().qmm_codebook4_workspace_bytes(M, K, N, Q.QMM_BF16)
     kp = -(-K // 64) * 64
@@ -107,7 +109,7 @@ def test_workspace_sizes(M, K, N):
     s = _splits(M, N, kp)
     full = a16 + rs + (s * M * N * 4 if s > 1 else 0)
     assert need == (0 if M <= 8 else full)
-    assert need_cb == (0 if M < 4 else full)
+    assert need_cb == (0 if M < 4 or (M == 4 and N * K <= 1 << 24) else full)
 
 
 def _v_cb(**kw):
@@ -126,15 +128,18 @@ def test_validate_codebook_codes():
     assert _v_cb(absmax=FAKE + 2) == -6
     assert _v_cb(a_type=5) == -2
     assert _v_cb(N=-3) == -5
-    # 4 <= M <= 8: the workspace is needed for a 16-bit output only
-    assert _v_cb(M=4) == -7
-    assert _v_cb(M=4, c_type=Q.QMM_F32) == 0
-    assert _v_cb(M=4, block=16) == 0
+    # 4 <= M <= 8: the workspace is needed for a 16-bit output only, and at M = 4 only
+    # above 2^24 codes (the GEMV keeps the smaller shapes)
+    assert _v_cb(M=5) == -7
+    assert _v_cb(M=4, N=14336) == -7
+    assert _v_cb(M=4) == 0
+    assert _v_cb(M=4, c_type=Q.QMM_F32, N=14336) == 0
+    assert _v_cb(M=4, block=16, N=14336) == 0
     assert _v_cb(M=3) == 0
-    need = Q.lib().qmm_codebook4_workspace_bytes(4, 4096, 1024, Q.QMM_BF16)
-    assert _v_cb(M=4, ws=FAKE, wsb=need) == 0
-    assert _v_cb(M=4, ws=FAKE, wsb=need - 1) == -7
-    assert _v_cb(M=4, ws=FAKE + 8, wsb=need) == -6    # the workspace must be 16-byte aligned
+    need = Q.lib().qmm_codebook4_workspace_bytes(5, 4096, 1024, Q.QMM_BF16)
+    assert _v_cb(M=5, ws=FAKE, wsb=need) == 0
+    assert _v_cb(M=5, ws=FAKE, wsb=need - 1) == -7
+    assert _v_cb(M=5, ws=FAKE + 8, wsb=need) == -6    # the workspace must be 16-byte aligned
     assert _v_cb(M=16, ws=FAKE + 4, wsb=need * 4) == -6
 
 

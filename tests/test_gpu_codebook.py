@@ -11,10 +11,13 @@ from gpu_util import TOL, assert_elementwise, column_chunks, dev, dev_act, gamma
 pytestmark = pytest.mark.gpu
 
 
-def cb_matrix_path(M, block, out_dtype):
+def cb_matrix_path(M, K, N, block, out_dtype):
     """Whether qmm_codebook4 takes a matrix-core path: M > 8, or 4 <= M <= 8 with a
-    16-bit output and blocks of at least 32 codes (the skinny kernel)."""
+    16-bit output and blocks of at least 32 codes (the skinny kernel), except M = 4 on
+    at most 2^24 codes (the GEMV's four-row form)."""
     t = torch()
+    if M == 4 and N * K <= 1 << 24:
+        return False
     return M > 8 or (M >= 4 and block >= 32 and out_dtype in (t.float16, t.bfloat16))
 
 
@@ -71,7 +74,7 @@ class CbDev:
         out_dt = {torch().float32: "f32", torch().float16: "f16", torch().bfloat16: "bf16"}[y.dtype]
         tol = TOL[out_dt]
         K = self.p["K"]
-        if cb_matrix_path(self.p["A"].shape[0], self.p["block"], y.dtype):
+        if cb_matrix_path(self.p["A"].shape[0], self.p["K"], self.p["N"], self.p["block"], y.dtype):
             a_round = None if self.p["a_dtype"] == "f16" else "f16_rows"
             exact, mirr, absdot = self.reference(a_round=a_round, w_round="f16")
             err = O.rel_l2(got, mirr)
@@ -125,25 +128,27 @@ def test_codebook_ragged_bias(M):
     d.check(d.run(), label=f"M={M}")
 
 
-@pytest.mark.parametrize("M,out", [(4, "same"), (5, "same"), (7, "same"), (8, "same"),
-                                   (4, "f32"), (8, "f32")])
-def test_codebook_small_m_paths(M, out):
+@pytest.mark.parametrize("M,N,out", [(4, 1024, "same"), (4, 4160, "same"), (5, 1024, "same"),
+                                     (7, 1024, "same"), (8, 1024, "same"), (4, 4160, "f32"),
+                                     (8, 1024, "f32")])
+def test_codebook_small_m_paths(M, N, out):
     """4 <= M <= 8: a 16-bit output takes the skinny kernel (gate: the oracle with fp16
-    operands; the reduction is split at this width); an fp32 output keeps the GEMV
-    (gate: the exact oracle at the fp32 tolerance)."""
+    operands; the reduction is split at this width), except M = 4 on at most 2^24 codes,
+    which the GEMV keeps; an fp32 output keeps the GEMV (gate: the exact oracle at the
+    fp32 tolerance)."""
     t = torch()
-    p = gen.codebook_problem(M, 4096, 1024, seed=58 + M, a_dtype="bf16", block=64,
+    p = gen.codebook_problem(M, 4096, N, seed=58 + M + N, a_dtype="bf16", block=64,
                              bias=(out == "same"))
     d = CbDev(p)
     if out == "f32":
         y = Q.qmm_codebook4(d.A, d.W, d.absmax, d.cb, p["K"], p["block"], d.bias,
                             out_dtype=t.float32)
-        assert not cb_matrix_path(M, p["block"], y.dtype)
-        d.check(y, label=f"M={M} fp32 out")
+        assert not cb_matrix_path(M, p["K"], N, p["block"], y.dtype)
+        d.check(y, label=f"M={M} N={N} fp32 out")
     else:
         y = d.run()
-        assert cb_matrix_path(M, p["block"], y.dtype)
-        d.check(y, label=f"M={M} bf16 out")
+        assert cb_matrix_path(M, p["K"], N, p["block"], y.dtype) == (M > 4 or N * p["K"] > 1 << 24)
+        d.check(y, label=f"M={M} N={N} bf16 out")
 
 
 @pytest.mark.parametrize("M,K,N,block,out", [
@@ -163,7 +168,7 @@ def test_codebook_gemv_forms(M, K, N, block, out):
     d = CbDev(p)
     od = None if out == "same" else t.float32
     y = Q.qmm_codebook4(d.A, d.W, d.absmax, d.cb, K, block, d.bias, out_dtype=od)
-    assert not cb_matrix_path(M, block, y.dtype)
+    assert not cb_matrix_path(M, K, N, block, y.dtype)
     d.check(y, label=f"M={M} K={K} N={N} block={block} {out}")
 
 
