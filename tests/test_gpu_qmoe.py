@@ -399,6 +399,26 @@ def test_first_call_under_capture(mode):
     assert not Q.qmoe_decode_status(scratch, T, H, I, k, mode)
 
 
+@pytest.mark.parametrize("mode", MODES, ids=["fp", "int8"])
+def test_untimed_default_is_single_launch(mode):
+    """With tuning off nothing is timed and the decode runs as one launch (the
+    single-launch candidate with fc2 streamed, one work-group per CU) where its plan
+    fits; its bits equal the two-kernel form's."""
+    T, H, I, E, k = 1, 2880, 2880, 32, 4
+    p = gen.qmoe_problem(T, H, I, E, k, 64, seed=965 + mode, zp=True, bias=True)
+    d = MoeDev(p)
+    try:
+        Q.set_tuning(1, 0)
+        one = host_bits(d.run(mode)).copy()
+        assert Q.tuned_choice(Q.ENTRY_QMOE_FUSED) == 1
+        Q.set_tuning(2, 0)  # the two-kernel form
+        two = host_bits(d.run(mode)).copy()
+        assert Q.tuned_choice(Q.ENTRY_QMOE_FUSED) == -1
+    finally:
+        Q.set_tuning(0, 0)
+    assert np.array_equal(one, two)
+
+
 def test_decode_status_clear_after_single_launch_calls():
     """qmoe_decode_status reports no wait that gave up after calls of the single-launch
     form, and refuses a scratch buffer smaller than the layout."""
