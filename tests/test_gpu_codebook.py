@@ -128,7 +128,7 @@ def test_codebook_ragged_bias(M):
     d.check(d.run(), label=f"M={M}")
 
 
-@pytest.mark.parametrize("M,N,out", [(4, 1024, "same"), (4, 4160, "same"), (5, 1024, "same"),
+@pytest.mark.parametrize("M,N,out", [(4, 1024, "same"), (4, 4096, "same"), (4, 4160, "same"), (5, 1024, "same"),
                                      (7, 1024, "same"), (8, 1024, "same"), (4, 4160, "f32"),
                                      (8, 1024, "f32")])
 def test_codebook_small_m_paths(M, N, out):
