@@ -131,9 +131,11 @@ bool env_flag(const char* name) {
 enum { ENTRY_NBITS = 0, ENTRY_CODEBOOK = 1, ENTRY_QMOE_FC1 = 2, ENTRY_QMOE_FC2 = 3, ENTRY_QMOE_FUSED = 4,
        ENTRY_COUNT = 5 };
 
-// GEMV candidates: rows of W per lane.
-constexpr int kGemvCandidates[] = {1, 2, 4};
-constexpr int kNumGemvCandidates = 3;
+// GEMV candidates: rows of W per lane (v_dot8 and fp32 kernels), then the matrix-core
+// form of the 2-bit GEMV (one group of 16 rows per wave).
+constexpr int kGemvCandidates[] = {1, 2, 4, kGemvMxBase + 1};
+constexpr int kNumGemvCandidates = 4;
+constexpr int kNumGemvRowCandidates = 3;  // the rows-per-lane candidates come first
 
 struct TunerState {
   std::mutex mu;
@@ -278,7 +280,7 @@ int gemv_choice(int entry, const GemvArgs& g, hipStream_t st) {
   // default: the largest R that still gives >= 2 work-groups per compute unit
   auto default_idx = [&]() {
     const int subs = 64 >> g.lpr_log2;
-    for (int i = kNumGemvCandidates - 1; i > 0; --i) {
+    for (int i = kNumGemvRowCandidates - 1; i > 0; --i) {
       const int64_t tiles = ceil_div(g.N, 8LL * subs * kGemvCandidates[i]);
       if (tiles >= 2LL * g.num_cus) return i;
     }
@@ -325,6 +327,10 @@ int gemv_choice(int entry, const GemvArgs& g, hipStream_t st) {
     bool ok = hipEventCreate(&e0) == hipSuccess && hipEventCreate(&e1) == hipSuccess;
     for (int r = 0; ok && r < kRounds; ++r) {
       for (int c = 0; ok && c < kNumGemvCandidates; ++c) {
+        if (kGemvCandidates[c] > kGemvMxBase && !gemv_mx_supported(g)) {
+          times[r * kNumGemvCandidates + c] = 1e30;  // not a form of this shape
+          continue;
+        }
         ok = hipEventRecord(e0, st) == hipSuccess;
         for (int b = 0; ok && b < kBurst; ++b) {
           GemvArgs tg = g;
@@ -1349,6 +1355,14 @@ qmm_status qmm_set_tuning(int mode, int forced_index) {
   t.mode = mode;
   t.forced = forced_index;
   return QMM_OK;
+}
+
+int qmm_nbits_gemv_matrix_core_form(int64_t M, int64_t K, int64_t N, int bits, int block) {
+  if (M != 1 || K <= 0 || N <= 0 || bits != 2 || block < 16 || (block & (block - 1)) != 0) return 0;
+  GemvArgs g = make_gemv((const void*)(uintptr_t)256, QMM_F32, M, K, N, (const uint8_t*)(uintptr_t)256, bits,
+                         block, nullptr, nullptr, QMM_F32);
+  gemv_plan(g, 256);
+  return gemv_mx_supported(g) ? 1 : 0;
 }
 
 int qmm_num_candidates(int entry) {

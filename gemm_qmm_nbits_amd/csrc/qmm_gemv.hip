@@ -1,6 +1,7 @@
 // Dispatch of the weight-streaming GEMV kernels (instantiated in qmm_gemv_*.hip).
 #include "qmm_device.h"
 #include "qmm_internal.h"
+#include "qmm_gemv_mx.h"
 
 namespace qmm {
 
@@ -10,6 +11,8 @@ template <int BITS, int AT>
 hipError_t launch_ip_at_type(const GemvArgs& g, int R, hipStream_t st);
 template <int FMT, int BITS, int AT>
 hipError_t launch_at_type(const GemvArgs& g, int R, hipStream_t st);
+template <int AT>
+hipError_t launch_mx_at_type(const GemvArgs& g, int R, hipStream_t st);
 
 // 3-bit and signed 8-bit affine weights: the fp32 kernel (codes decoded to fp32)
 template <int BITS>
@@ -39,6 +42,18 @@ static hipError_t launch_affine(const GemvArgs& g, int R, hipStream_t st) {
     default: return launch_ip_at_type<BITS, QMM_BF16>(g, R, st);
   }
 }
+
+// 2-bit affine weights at M = 1: matrix-core form (hipErrorNotSupported where the
+// shape does not suit it)
+static hipError_t launch_affine_mx(const GemvArgs& g, int R, hipStream_t st) {
+  switch (g.a_type) {
+    case QMM_F32: return launch_mx_at_type<QMM_F32>(g, R, st);
+    case QMM_F16: return launch_mx_at_type<QMM_F16>(g, R, st);
+    default: return launch_mx_at_type<QMM_BF16>(g, R, st);
+  }
+}
+
+bool gemv_mx_supported(const GemvArgs& g) { return gemv_mx_pairs(g) > 0 && ((uintptr_t)g.scales & 15u) == 0; }
 
 // Generic path for layouts the chunked kernel cannot read (row length not a
 // multiple of 16 bytes, or unaligned pointers): one wave per output column n,
@@ -163,6 +178,12 @@ hipError_t launch_gemv(GemvArgs g, int rows_per_lane, hipStream_t st) {
     const dim3 grid((unsigned)((g.N + 3) / 4));
     launch(gemv_generic_kernel, grid, dim3(256), 0, st, g);
     return hipSuccess;
+  }
+  if (rows_per_lane > kGemvMxBase) {
+    const hipError_t e = gemv_mx_supported(g) ? launch_affine_mx(g, rows_per_lane - kGemvMxBase, st)
+                                              : hipErrorNotSupported;
+    if (e != hipErrorNotSupported) return e;
+    rows_per_lane = 2;
   }
   if (g.fmt == GEMV_CODEBOOK) return launch_codebook(g, rows_per_lane, st);
   if (g.bits == 2) return launch_affine<2>(g, rows_per_lane, st);

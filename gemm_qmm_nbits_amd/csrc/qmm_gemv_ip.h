@@ -122,7 +122,7 @@ __device__ __forceinline__ float outlier_code(const uint4& w, int gi, uint32_t i
   return (float)((x >> ((id % WPD) * BITS)) & ((1u << BITS) - 1u));
 }
 
-template <int BITS, int AT, int G, int MT, bool AVEC, bool BUF, typename Issued>
+template <int BITS, int AT, int G, int MT, bool AVEC, bool BUF, bool MX, typename Issued>
 __device__ __forceinline__ void stage_planes_impl(const GemvArgs& g, uint32_t* planes, f32x4* meta,
                                                   uint32_t* trash, int c0, int SC, Issued&& issued) {
   using L = IpLayout<BITS>;
@@ -303,7 +303,33 @@ __device__ __forceinline__ void stage_planes_impl(const GemvArgs& g, uint32_t* p
 #pragma unroll
       for (int q = 0; q < 16; ++q) u[q] = (uint32_t)(int)rintf(ldexpf(v[q], 22 - e));
       uint32_t w[12];
-      if constexpr (BITS == 2) {
+      if constexpr (MX) {
+        // matrix-core operand (2-bit codes, one group per chunk, one A row): chunk cs is
+        // chunk j = cs % 4 of pair u = cs / 4; digit p of the piece's 16 values goes as 16
+        // e4m3 bytes (the even values first) to operand region 2 * (j / 2) + piece / 2 of
+        // the pair, lane slot 16 * (2 * (j % 2) + piece % 2) + row(p), with row(p) =
+        // 8 * (j % 2) + 4 * (p / 3) + p % 3 (the six planes as two triples)
+        static_assert(BITS == 2 && G == 64 && MT == 1, "matrix-core staging: 2-bit, one group per chunk, M = 1");
+        const uint32_t j = cs & 3u;
+        const uint32_t base = __umul24(cs >> 2, 1024u) + (2u * (j >> 1) + (piece >> 1)) * 256u +
+                              (16u * (2u * (j & 1u) + (piece & 1u))) * 4u;
+#pragma unroll
+        for (int p = 0; p < 6; ++p) {
+          auto digit = [&](uint32_t x) -> float {
+            return p < 5 ? (float)(int)((x >> (4 * p)) & 15u) : (float)(((int)(x << 8)) >> 28);
+          };
+          uint32_t pk[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const int i0 = k < 2 ? 8 * k : 8 * (k - 2) + 1;
+            int x = __builtin_amdgcn_cvt_pk_fp8_f32(digit(u[i0]), digit(u[i0 + 2]), 0, false);
+            x = __builtin_amdgcn_cvt_pk_fp8_f32(digit(u[i0 + 4]), digit(u[i0 + 6]), x, true);
+            pk[k] = (uint32_t)x;
+          }
+          const uint32_t row = (j & 1u) * 8u + 4u * (uint32_t)(p / 3) + (uint32_t)(p % 3);
+          *(uint4*)(planes + (ok ? base + row * 4u : trash_word)) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+        }
+      } else if constexpr (BITS == 2) {
         // even values (nibble i of the E planes = value 2i), then odd values (O planes)
         uint32_t ex[3], ey[3], ox[3], oy[3], ew[6], ow[6];
         byte_gather(u[0], u[4], u[8], u[12], ex);
@@ -335,11 +361,13 @@ __device__ __forceinline__ void stage_planes_impl(const GemvArgs& g, uint32_t* p
       // lanes without a piece (and the meta record of all but the group's first lane)
       // write to the trash line instead of branching around the stores
       // (32-bit word offsets from the planes, so the choice is one select)
-      const uint32_t pw = ok ? __umul24(cs, (uint32_t)L::SLOT) + __umul24(piece, 12u) : trash_word;
-      uint4* dst = (uint4*)(planes + pw);
-      dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
-      dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
-      dst[2] = make_uint4(w[8], w[9], w[10], w[11]);
+      if constexpr (!MX) {
+        const uint32_t pw = ok ? __umul24(cs, (uint32_t)L::SLOT) + __umul24(piece, 12u) : trash_word;
+        uint4* dst = (uint4*)(planes + pw);
+        dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+        dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+        dst[2] = make_uint4(w[8], w[9], w[10], w[11]);
+      }
       f32x4 mt;
       mt.x = finite ? ldexpf(1.0f, e - 22) : __builtin_nanf("");
       mt.y = sm;
@@ -367,9 +395,9 @@ template <int BITS, int AT, int G, int MT, bool BUF, typename Issued>
 __device__ __forceinline__ void stage_planes(const GemvArgs& g, uint32_t* planes, f32x4* meta,
                                              uint32_t* trash, int c0, int SC, Issued&& issued) {
   if (g.a_vec)
-    stage_planes_impl<BITS, AT, G, MT, true, BUF>(g, planes, meta, trash, c0, SC, issued);
+    stage_planes_impl<BITS, AT, G, MT, true, BUF, false>(g, planes, meta, trash, c0, SC, issued);
   else
-    stage_planes_impl<BITS, AT, G, MT, false, BUF>(g, planes, meta, trash, c0, SC, issued);
+    stage_planes_impl<BITS, AT, G, MT, false, BUF, false>(g, planes, meta, trash, c0, SC, issued);
 }
 
 // General form (A staged one K-slice at a time inside the item loop, row sums

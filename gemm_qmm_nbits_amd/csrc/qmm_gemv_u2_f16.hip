@@ -1,6 +1,8 @@
-// Instantiation of the integer-plane GEMV for 2-bit affine weights and f16 activations.
+// Instantiation of the integer-plane GEMV (v_dot8 and matrix-core forms) for 2-bit affine weights and f16 activations.
+#include "qmm_gemv_mx.h"
 #include "qmm_gemv_stream.h"
 
 namespace qmm {
 template hipError_t launch_ip_at_type<2, QMM_F16>(const GemvArgs& g, int R, hipStream_t st);
+template hipError_t launch_mx_at_type<QMM_F16>(const GemvArgs& g, int R, hipStream_t st);
 }  // namespace qmm

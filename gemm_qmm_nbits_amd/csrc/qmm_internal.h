@@ -77,7 +77,13 @@ void gemv_plan(GemvArgs& g, int num_cus);
 
 int gemv_lanes_per_row_log2(int64_t nchunks);
 int gemv_row_lanes_log2(int64_t nchunks, int64_t N);
+// rows_per_lane above kGemvMxBase selects the matrix-core form of the 2-bit GEMV with
+// rows_per_lane - kGemvMxBase groups of 16 rows per wave (where the shape suits it;
+// elsewhere the v_dot8 kernel with 2 rows per lane, which gives the same bits).
+constexpr int kGemvMxBase = 16;
 hipError_t launch_gemv(GemvArgs g, int rows_per_lane, hipStream_t st);
+// Whether the matrix-core form serves this planned shape.
+bool gemv_mx_supported(const GemvArgs& g);
 
 struct DequantArgs {
   const uint8_t* W;

@@ -99,6 +99,7 @@ _SIGS = {
     "qmm_launch_timing_end": (c_int, [c_void_p, c_int, c_void_p]),
     "qmm_set_tuning": (c_int, [c_int, c_int]),
     "qmm_num_candidates": (c_int, [c_int]),
+    "qmm_nbits_gemv_matrix_core_form": (c_int, [c_int64, c_int64, c_int64, c_int, c_int]),
     "qmm_tuned_choice": (c_int, [c_int]),
     "qmm_clear_tuning": (None, []),
     "qmm_tuner_pick": (c_int, [POINTER(c_double), c_int, c_int]),
@@ -471,6 +472,10 @@ def set_tuning(mode: int, forced_index: int = 0):
 
 def num_candidates(entry: int) -> int:
     return lib().qmm_num_candidates(entry)
+
+
+def nbits_gemv_matrix_core_form(M: int, K: int, N: int, bits: int, block: int) -> bool:
+    return bool(lib().qmm_nbits_gemv_matrix_core_form(M, K, N, bits, block))
 
 
 def tuned_choice(entry: int) -> int:

@@ -397,6 +397,19 @@ int qmm_num_candidates(int entry);
 int qmm_tuned_choice(int entry);
 void qmm_clear_tuning(void);
 
+/* GEMV candidates of entries 0 and 1: indices 0, 1, 2 are the v_dot8 / fp32 kernels
+ * with 1, 2, 4 weight rows per lane; 3 is the matrix-core form of the 2-bit GEMV
+ * (v_mfma_scale_f32_16x16x128_f8f6f4: the activation digit planes as e4m3 rows, the
+ * codes as e2m1 nibbles, every product and sum exact; 16 weight rows per wave).  All
+ * four give the same bits.  Where the matrix-core form does not serve a shape, index 3
+ * runs the v_dot8 kernel with 2 rows per lane and the up-front timing skips it.
+ * qmm_nbits_gemv_matrix_core_form: 1 when qmm_nbits at this shape (16-byte aligned
+ * W, A and scales) has the matrix-core form among its candidates: bits = 2, M = 1,
+ * block = 64 with ceil(K / 64) a multiple of 8, the activations' operand (4 KiB per
+ * 256 codes) within LDS, and the lanes-per-row split of the v_dot8 kernel (fixed by K
+ * and N) of 16 or 32 lanes, with ceil(K / 256) a multiple of a quarter of it; else 0. */
+int qmm_nbits_gemv_matrix_core_form(int64_t M, int64_t K, int64_t N, int bits, int block);
+
 /* The selection rule of the up-front timing, exposed for host-only checks:
  * times_us[r * ncand + c] is round r of candidate c; round 0 is discarded, the
  * least total over rounds 1..rounds-1 wins, ties go to the lower index.

@@ -258,3 +258,17 @@ def test_launch_timing_host_paths():
     assert L.qmm_launch_timing_end(None, 0, None) == -1
     assert L.qmm_launch_timing_begin(0) == -5
     assert L.qmm_launch_timing_begin(65537) == -5
+
+
+def test_matrix_core_form_rule():
+    """Shapes the form serves and shapes it leaves to the v_dot8 kernel."""
+    assert Q.nbits_gemv_matrix_core_form(1, 5120, 100352, 2, 64)
+    assert Q.nbits_gemv_matrix_core_form(1, 5120, 35840, 2, 64)
+    assert not Q.nbits_gemv_matrix_core_form(2, 5120, 100352, 2, 64)    # M = 2
+    assert not Q.nbits_gemv_matrix_core_form(1, 5120, 100352, 4, 64)    # 4-bit
+    assert not Q.nbits_gemv_matrix_core_form(1, 5120, 100352, 2, 32)    # two groups per chunk
+    assert not Q.nbits_gemv_matrix_core_form(1, 5120, 7680, 2, 64)      # 32 lanes, 20 pairs
+    assert not Q.nbits_gemv_matrix_core_form(1, 5120, 100352, 2, 128)   # block 128
+    assert not Q.nbits_gemv_matrix_core_form(1, 5056, 100352, 2, 64)    # 79 blocks per row
+    assert not Q.nbits_gemv_matrix_core_form(1, 17920, 5120, 2, 64)     # operand past LDS
+    assert not Q.nbits_gemv_matrix_core_form(1, 4096, 100352, 2, 64)    # 64 lanes per row
