@@ -10,11 +10,11 @@
 //     every sum (at most 64 * 15 * 3) is an exact integer in fp32;
 //   * B columns are 16 weight rows; a pair of steps covers four 64-code chunks, lane
 //     group g loading chunk g (16 bytes) and the two steps taking its two halves;
-//   * two accumulations per pair, each over two chunks: the A operand rows
-//     8c + 4h + v carry digit plane 3h + v of chunk c of the accumulation at that
-//     chunk's k positions (the other half of the operand is zero), so lane group
-//     2c + h of the result holds, per column, the three sums of one half (lo = planes
-//     0..2, hi = planes 3..5) of chunk c;
+//   * two accumulations per pair, each over two chunks: A operand rows 8c + 4h + v
+//     carry digit plane 3h + v of chunk c (k < 64) and of chunk 2 + c (k >= 64) of
+//     the pair, and the first accumulation's B keeps only the k < 64 lane groups, the
+//     second's only the others, so lane group 2c + h of the result holds, per column,
+//     the three sums of one half (lo = planes 0..2, hi = planes 3..5) of one chunk;
 //   * lo + 16 S + 256 S' is exact, a row swap pairs lo with hi, and
 //     P = fma(hi, 4096, lo), the outlier term, the zero-point fold and the scale follow
 //     as in the v_dot8 kernel;
@@ -79,6 +79,9 @@ __global__ __launch_bounds__(kMxThreads) void gemv_mx_kernel(GemvArgs g, int T2)
   const int col = lane & 15;
   const int sig = lg >> 1;   // parity of the chunks whose epilogue this lane runs
   const uint32_t ssh = 16u * (uint32_t)sig;
+  constexpr uint32_t kM = 0x33333333u;
+  const uint32_t m1 = lg < 2 ? kM : 0u;  // B of the first accumulation: chunks 4u, 4u + 1
+  const uint32_t m2 = lg < 2 ? 0u : kM;  // of the second: chunks 4u + 2, 4u + 3
   const int rpg = 16 * R;
   const int N = (int)g.N;
   const int ngroups = (N + rpg - 1) / rpg;
@@ -87,8 +90,7 @@ __global__ __launch_bounds__(kMxThreads) void gemv_mx_kernel(GemvArgs g, int T2)
   const int g_end = g_begin + groups_lo + (blockIdx.x < extra ? 1 : 0);
   if (g_begin >= g_end) return;
   const int wave_groups = g_end - g_begin > wave ? (g_end - g_begin - wave + NW - 1) / NW : 0;
-  const int nchunks = (int)g.nchunks;
-  const int nblk = (int)g.nblk;
+  const int nblk = (int)g.nblk;  // a multiple of 8: every chunk of a pair lies in the row
   const uint32_t row_bytes = (uint32_t)g.row_bytes;
   const float zconst = g.zp_kind == QMM_ZP_UNIFORM ? g.uniform_zp : 2.0f;
   const uint32_t zrow_bytes = (uint32_t)g.zp_row_bytes;
@@ -176,7 +178,6 @@ __global__ __launch_bounds__(kMxThreads) void gemv_mx_kernel(GemvArgs g, int T2)
   int cit = 0, cgrp = g_begin + wave;
   const int total = wave_groups * T2;
   const mx_f32x4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
-  constexpr uint32_t kM = 0x33333333u;
   auto pair = [&](MxBuf<R>& cb, MxBuf<R>& nx, int i) {
     if (i == 0) {
       // the round's scales: lane groups 2k and 2k + 1 exchange their halves
@@ -197,31 +198,43 @@ __global__ __launch_bounds__(kMxThreads) void gemv_mx_kernel(GemvArgs g, int T2)
     fetch(nx);
     const uint4* ap = (const uint4*)(aop + cit * 1024);
     const uint4 xa = ap[lane], xb = ap[64 + lane], ya = ap[128 + lane], yb = ap[192 + lane];
-    const mx_i32x8 A1a = {(int)xa.x, (int)xa.y, (int)xa.z, (int)xa.w, 0, 0, 0, 0};
-    const mx_i32x8 A1b = {(int)xb.x, (int)xb.y, (int)xb.z, (int)xb.w, 0, 0, 0, 0};
-    const mx_i32x8 A2a = {0, 0, 0, 0, (int)ya.x, (int)ya.y, (int)ya.z, (int)ya.w};
-    const mx_i32x8 A2b = {0, 0, 0, 0, (int)yb.x, (int)yb.y, (int)yb.z, (int)yb.w};
+    // one operand per step: chunks 4u, 4u + 1 in the low half (k < 64), 4u + 2, 4u + 3 in
+    // the high half; B keeps one half per accumulation (the other lane groups zero)
+    const mx_i32x8 Aa = {(int)xa.x, (int)xa.y, (int)xa.z, (int)xa.w, (int)ya.x, (int)ya.y, (int)ya.z, (int)ya.w};
+    const mx_i32x8 Ab = {(int)xb.x, (int)xb.y, (int)xb.z, (int)xb.w, (int)yb.x, (int)yb.y, (int)yb.z, (int)yb.w};
     f32x4 mt[2];
-    bool valid[2];
 #pragma unroll
-    for (int d = 0; d < 2; ++d) {
-      const int ch = 4 * cit + 2 * d + sig;
-      mt[d] = meta[ch];
-      valid[d] = ch < nchunks;
-    }
+    for (int d = 0; d < 2; ++d) mt[d] = meta[4 * cit + 2 * d + sig];
     const bool any_out = __builtin_amdgcn_ballot_w64(mt[0].z != 0.0f || mt[1].z != 0.0f) != 0;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const uint4 x = cb.w[r];
-      const mx_i32x8 Ba = {(int)(x.x & kM), (int)((x.x >> 2) & kM), (int)(x.y & kM), (int)((x.y >> 2) & kM), 0, 0, 0, 0};
-      const mx_i32x8 Bb = {(int)(x.z & kM), (int)((x.z >> 2) & kM), (int)(x.w & kM), (int)((x.w >> 2) & kM), 0, 0, 0, 0};
+      const uint32_t e0 = x.x >> 2, e1 = x.y >> 2, e2 = x.z >> 2, e3 = x.w >> 2;
+      const mx_i32x8 B1a = {(int)(x.x & m1), (int)(e0 & m1), (int)(x.y & m1), (int)(e1 & m1), 0, 0, 0, 0};
+      const mx_i32x8 B1b = {(int)(x.z & m1), (int)(e2 & m1), (int)(x.w & m1), (int)(e3 & m1), 0, 0, 0, 0};
+      const mx_i32x8 B2a = {(int)(x.x & m2), (int)(e0 & m2), (int)(x.y & m2), (int)(e1 & m2), 0, 0, 0, 0};
+      const mx_i32x8 B2b = {(int)(x.z & m2), (int)(e2 & m2), (int)(x.w & m2), (int)(e3 & m2), 0, 0, 0, 0};
       // A e4m3 (cbsz 0), B e2m1 (blgp 4); scales 2^0 and 2^1
       mx_f32x4 acc2[2];
-      acc2[0] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A1a, Ba, zero4, 0, 4, 0, 0x7f7f7f7f, 0, (int)0x80808080);
-      acc2[1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A2a, Ba, zero4, 0, 4, 0, 0x7f7f7f7f, 0, (int)0x80808080);
-      acc2[0] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A1b, Bb, acc2[0], 0, 4, 0, 0x7f7f7f7f, 0, (int)0x80808080);
-      acc2[1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A2b, Bb, acc2[1], 0, 4, 0, 0x7f7f7f7f, 0, (int)0x80808080);
-      uint32_t code[2] = {0u, 0u};
+      acc2[0] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Aa, B1a, zero4, 0, 4, 0, 0x7f7f7f7f, 0, (int)0x80808080);
+      acc2[1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Aa, B2a, zero4, 0, 4, 0, 0x7f7f7f7f, 0, (int)0x80808080);
+      acc2[0] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Ab, B1b, acc2[0], 0, 4, 0, 0x7f7f7f7f, 0, (int)0x80808080);
+      acc2[1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Ab, B2b, acc2[1], 0, 4, 0, 0x7f7f7f7f, 0, (int)0x80808080);
+      float P[2], scv[2], z[2];
+#pragma unroll
+      for (int d = 0; d < 2; ++d) {
+        const int slot = 2 * (i % PR) + d;
+        const mx_f32x4 dd = acc2[d];
+        const float h3 = fmaf(dd[2], 256.0f, fmaf(dd[1], 16.0f, dd[0]));
+        // lane groups 0 / 2 hold lo (planes 0..2), 1 / 3 hi (planes 3..5)
+        const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(h3), __float_as_uint(h3), false, false);
+        P[d] = fmaf(__uint_as_float(sw[1]), 4096.0f, __uint_as_float(sw[0]));
+        const uint32_t sbits = __builtin_amdgcn_ubfe(sc[r][slot / 8][slot % 8], ssh, 16u);
+        scv[d] = (float)__builtin_bit_cast(_Float16, (uint16_t)sbits);
+        if constexpr (ZK == 1) z[d] = (float)((cb.z[r][d] >> cb.zsh[r][d]) & 3u);
+        else if constexpr (ZK == 2) z[d] = (float)cb.zh[r][d];
+        else z[d] = zconst;
+      }
       if (any_out) {
         // the code of a value taken out of the planes: this lane's own chunk 4u + lg
         // holds it at dword id / 16; lane group 2d + g / 2 owns chunk 4u + 2d + g / 2
@@ -230,27 +243,20 @@ __global__ __launch_bounds__(kMxThreads) void gemv_mx_kernel(GemvArgs g, int T2)
         const uint32_t xv = di == 0 ? x.x : di == 1 ? x.y : di == 2 ? x.z : x.w;
         const int own = (int)((xv >> ((id & 15u) * 2u)) & 3u);
 #pragma unroll
-        for (int d = 0; d < 2; ++d)
-          code[d] = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * (16 * (2 * d + sig) + col), own);
-      }
+        for (int d = 0; d < 2; ++d) {
+          const int slot = 2 * (i % PR) + d;
+          const uint32_t code = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * (16 * (2 * d + sig) + col), own);
+          float t = P[d] * mt[d].x;
+          if (mt[d].z != 0.0f) t = fmaf(mt[d].z, (float)code - z[d], t);
+          acc[r][slot] = fmaf(scv[d], fmaf(-z[d], mt[d].y, t), acc[r][slot]);
+        }
+      } else {
 #pragma unroll
-      for (int d = 0; d < 2; ++d) {
-        const int slot = 2 * (i % PR) + d;
-        const mx_f32x4 dd = acc2[d];
-        const float h3 = fmaf(dd[2], 256.0f, fmaf(dd[1], 16.0f, dd[0]));
-        // lane groups 0 / 2 hold lo (planes 0..2), 1 / 3 hi (planes 3..5)
-        const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(h3), __float_as_uint(h3), false, false);
-        const float P = fmaf(__uint_as_float(sw[1]), 4096.0f, __uint_as_float(sw[0]));
-        const uint32_t sbits = __builtin_amdgcn_ubfe(sc[r][slot / 8][slot % 8], ssh, 16u);
-        const float scv = (float)__builtin_bit_cast(_Float16, (uint16_t)sbits);
-        float z;
-        if constexpr (ZK == 1) z = (float)((cb.z[r][d] >> cb.zsh[r][d]) & 3u);
-        else if constexpr (ZK == 2) z = (float)cb.zh[r][d];
-        else z = zconst;
-        float t = P * mt[d].x;
-        if (any_out && mt[d].z != 0.0f) t = fmaf(mt[d].z, (float)code[d] - z, t);
-        const float nv = fmaf(scv, fmaf(-z, mt[d].y, t), acc[r][slot]);
-        acc[r][slot] = valid[d] ? nv : acc[r][slot];
+        for (int d = 0; d < 2; ++d) {
+          const int slot = 2 * (i % PR) + d;
+          const float t = P[d] * mt[d].x;
+          acc[r][slot] = fmaf(scv[d], fmaf(-z[d], mt[d].y, t), acc[r][slot]);
+        }
       }
     }
     if (cit == T2 - 1) {

@@ -22,8 +22,10 @@ MX_CANDIDATES = (3,)
     (5120, 16400, 64, "packed", "f16", "f16", True, True),
     # fp16 zero-point tensor, bf16 activations, 32 lanes per row (one round of 8 pairs)
     (2048, 20000, 64, "f16", "bf16", "bf16", False, False),
-    # 12 pairs, packed zero point 2, bias
-    (3072, 20000, 64, "packed8", "f32", "f32", True, False),
+    # packed zero point 2, bias, rows a multiple of 16
+    (5120, 20000, 64, "packed8", "f32", "f32", True, False),
+    # 12 pairs (three rounds), uniform zero point, fp16 activations, fp32 output
+    (3072, 20000, 64, "f16_uniform", "f16", "f32", False, False),
     # 32 lanes per row, three rounds, outliers, no zero point
     (6144, 9000, 64, "none", "f32", "f32", False, True),
     # the lm_head shape, uniform zero point
