@@ -272,3 +272,6 @@ def test_matrix_core_form_rule():
     assert not Q.nbits_gemv_matrix_core_form(1, 5056, 100352, 2, 64)    # 79 blocks per row
     assert not Q.nbits_gemv_matrix_core_form(1, 17920, 5120, 2, 64)     # operand past LDS
     assert not Q.nbits_gemv_matrix_core_form(1, 4096, 100352, 2, 64)    # 64 lanes per row
+    for args in ((1, 0, 100352, 2, 64), (1, 5120, 0, 2, 64), (1, -5120, 100352, 2, 64),
+                 (1, 5120, 100352, 2, 48), (1, 5120, 100352, 2, 0), (0, 5120, 100352, 2, 64)):
+        assert not Q.nbits_gemv_matrix_core_form(*args), args

@@ -71,3 +71,37 @@ def test_matrix_core_gemv_same_bits(K, N, block, zp, a, c, bias, outliers):
     assert err <= TOL[c]
     torch().cuda.synchronize()
 
+
+
+def test_matrix_core_gemv_in_graph_replays():
+    """The matrix-core form captured in a HIP graph: every replay (with eager work and
+    synchronizations between them) gives the eager call's bits, and the same bits as the
+    v_dot8 kernel."""
+    t = torch()
+    K, N = 5120, 16400
+    assert Q.nbits_gemv_matrix_core_form(1, K, N, 2, 64)
+    p = gen.nbits_problem(1, K, N, 2, 64, seed=905, zp="packed", bias=True)
+    d = NbitsDev(p, c_dtype="f32")
+    out = t.empty((1, N), dtype=t.float32, device="cuda")
+    try:
+        Q.set_tuning(2, 0)
+        ref = host_bits(d.run()).copy()
+        Q.set_tuning(2, MX_CANDIDATES[0])
+        eager = host_bits(d.run()).copy()
+        t.cuda.synchronize()
+        cap = t.cuda.Stream()
+        g = t.cuda.CUDAGraph()
+        with t.cuda.stream(cap):
+            with t.cuda.graph(g, stream=cap):
+                d.run(out=out)
+        t.cuda.synchronize()
+        for rep in range(4):
+            out.zero_()
+            g.replay()
+            t.cuda.synchronize()
+            assert np.array_equal(host_bits(out), eager), rep
+            d.run()  # eager work between replays
+            t.cuda.synchronize()
+    finally:
+        Q.set_tuning(0, 0)
+    assert np.array_equal(eager, ref)
